@@ -1,0 +1,225 @@
+"""CPU oracle for block-quantized MUL_MAT (ctypes wrapper over qmm_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import this package.  The GPU
+library never imports, links or calls it, and it shares no code with the GPU
+path: the arithmetic lives in plain C (``qmm_oracle.c``), this module only
+marshals numpy arrays.
+
+What it computes (the pages it follows are cited in ``qmm_oracle.h``):
+  * IEEE binary16 / bfloat16 conversions written from the format definitions;
+  * Q8_0 / Q4_0 block quantization of fp32 rows and the row-planar packing;
+  * the exact dequantized weights W';
+  * MUL_MAT y[n][m] = sum_k W'[m][k] x[n][k] accumulated in binary64, with
+    the magnitude sum a[n][m] = sum_k |W'[m][k] x[n][k]| used by tolerances.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qmm_oracle.c")
+_SO = os.environ.get("QMM_ORACLE_LIB") or os.path.join(_HERE, "libqmm_oracle.so")
+
+# Own type numbering (mirrors qmm_oracle.h, not the GPU library's enum).
+F32, F16, BF16, Q8_0, Q4_0 = 0, 1, 2, 3, 4
+
+CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+          "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+
+def build(out: str = _SO) -> str:
+    """Compile the oracle with gcc (plain -O2, contraction off, no fast-math)."""
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(_SO):
+            build()
+        h = ctypes.CDLL(_SO)
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        vp = ctypes.c_void_p
+        sz = ctypes.c_size_t
+        i64 = ctypes.c_int64
+        ci = ctypes.c_int
+        h.orc_f32_to_f16_n.argtypes = [f32p, u16p, sz]
+        h.orc_f16_to_f32_n.argtypes = [u16p, f32p, sz]
+        h.orc_f32_to_bf16_n.argtypes = [f32p, u16p, sz]
+        h.orc_bf16_to_f32_n.argtypes = [u16p, f32p, sz]
+        for name in ("orc_f32_to_f16_n", "orc_f16_to_f32_n",
+                     "orc_f32_to_bf16_n", "orc_bf16_to_f32_n"):
+            getattr(h, name).restype = None
+        h.orc_quantize_block_q8_0.argtypes = [f32p, u16p, ctypes.POINTER(ctypes.c_int8)]
+        h.orc_quantize_block_q8_0.restype = None
+        h.orc_quantize_block_q4_0.argtypes = [f32p, u16p, u8p]
+        h.orc_quantize_block_q4_0.restype = None
+        h.orc_row_size.argtypes = [ci, i64]
+        h.orc_row_size.restype = sz
+        h.orc_quantize_rows.argtypes = [ci, f32p, i64, i64, u8p, sz]
+        h.orc_quantize_rows.restype = ci
+        h.orc_dequantize_rows.argtypes = [ci, u8p, sz, i64, i64, f32p]
+        h.orc_dequantize_rows.restype = ci
+        h.orc_mul_mat_rows.argtypes = [ci, u8p, sz, i64, i64, vp, ci, i64, ci,
+                                       i64, i64, f64p, f64p]
+        h.orc_mul_mat_rows.restype = ci
+        h.orc_mul_mat_pairs.argtypes = [ci, u8p, sz, i64, i64, vp, ci, i64, ci,
+                                        i64p, i64p, i64, f64p, f64p]
+        h.orc_mul_mat_pairs.restype = ci
+        _lib_handle = h
+    return _lib_handle
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _c(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---- conversions --------------------------------------------------------
+
+def f32_to_f16_bits(x) -> np.ndarray:
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().orc_f32_to_f16_n(_ptr(x, ctypes.c_float), _ptr(out, ctypes.c_uint16), x.size)
+    return out
+
+
+def f16_bits_to_f32(h) -> np.ndarray:
+    h = _c(h, np.uint16)
+    out = np.empty(h.shape, np.float32)
+    lib().orc_f16_to_f32_n(_ptr(h, ctypes.c_uint16), _ptr(out, ctypes.c_float), h.size)
+    return out
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    x = _c(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    lib().orc_f32_to_bf16_n(_ptr(x, ctypes.c_float), _ptr(out, ctypes.c_uint16), x.size)
+    return out
+
+
+def bf16_bits_to_f32(h) -> np.ndarray:
+    h = _c(h, np.uint16)
+    out = np.empty(h.shape, np.float32)
+    lib().orc_bf16_to_f32_n(_ptr(h, ctypes.c_uint16), _ptr(out, ctypes.c_float), h.size)
+    return out
+
+
+# ---- blocks and rows ------------------------------------------------------
+
+def quantize_block(type_: int, w32) -> tuple[int, np.ndarray]:
+    """One 32-weight block -> (fp16 scale bits, codes).  Q8_0 codes are int8
+    in [-127, 127]; Q4_0 codes are the stored nibbles in [0, 15]."""
+    w = _c(w32, np.float32).reshape(32)
+    sb = np.zeros(1, np.uint16)
+    if type_ == Q8_0:
+        q = np.zeros(32, np.int8)
+        lib().orc_quantize_block_q8_0(_ptr(w, ctypes.c_float), _ptr(sb, ctypes.c_uint16),
+                                      _ptr(q, ctypes.c_int8))
+    elif type_ == Q4_0:
+        q = np.zeros(32, np.uint8)
+        lib().orc_quantize_block_q4_0(_ptr(w, ctypes.c_float), _ptr(sb, ctypes.c_uint16),
+                                      _ptr(q, ctypes.c_uint8))
+    else:
+        raise ValueError("quantize_block: type must be Q8_0 or Q4_0")
+    return int(sb[0]), q
+
+
+def row_size(type_: int, K: int) -> int:
+    return int(lib().orc_row_size(type_, K))
+
+
+def quantize(type_: int, w, pitch: int | None = None) -> np.ndarray:
+    """Quantize fp32 rows w (M x K) into packed rows: uint8 array (M, pitch)."""
+    w = _c(w, np.float32)
+    M, K = w.shape
+    pitch = row_size(type_, K) if pitch is None else pitch
+    out = np.zeros((M, pitch), np.uint8)
+    rc = lib().orc_quantize_rows(type_, _ptr(w, ctypes.c_float), K, M,
+                                 _ptr(out, ctypes.c_uint8), pitch)
+    if rc != 0:
+        raise ValueError("orc_quantize_rows rejected its arguments")
+    return out
+
+
+def dequantize(type_: int, packed, K: int) -> np.ndarray:
+    """Packed rows (M, pitch) uint8 (or dense rows viewed as bytes) -> W' (M, K) f32."""
+    packed = _c(packed, np.uint8)
+    M, pitch = packed.shape
+    out = np.zeros((M, K), np.float32)
+    rc = lib().orc_dequantize_rows(type_, _ptr(packed, ctypes.c_uint8), pitch, K, M,
+                                   _ptr(out, ctypes.c_float))
+    if rc != 0:
+        raise ValueError("orc_dequantize_rows rejected its arguments")
+    return out
+
+
+def _x_args(x, x_bf16_bits: bool):
+    if x_bf16_bits:
+        xa = _c(x, np.uint16)
+        return xa, BF16
+    xa = _c(x, np.float32)
+    return xa, F32
+
+
+def mul_mat(type_: int, packed, K: int, x, *, x_bf16_bits: bool = False,
+            w_to_bf16: bool = False, rows: tuple[int, int] | None = None):
+    """y[n][m] = sum_k W'[m][k] x[n][k] in binary64, and a = sum |W' x|.
+
+    packed: (M, pitch) uint8 rows of the weight type; x: (N, K) float32, or
+    (N, K) uint16 bf16 bits when x_bf16_bits.  Returns (y, a), each (N, M)
+    float64; only rows [m0, m1) are filled when ``rows`` is given (rest 0)."""
+    packed = _c(packed, np.uint8)
+    M, pitch = packed.shape
+    xa, xt = _x_args(x, x_bf16_bits)
+    N = xa.shape[0]
+    assert xa.shape[1] == K
+    m0, m1 = (0, M) if rows is None else rows
+    y = np.zeros((N, M), np.float64)
+    a = np.zeros((N, M), np.float64)
+    rc = lib().orc_mul_mat_rows(type_, _ptr(packed, ctypes.c_uint8), pitch, K, M,
+                                xa.ctypes.data_as(ctypes.c_void_p), xt, N,
+                                1 if w_to_bf16 else 0, m0, m1,
+                                _ptr(y, ctypes.c_double), _ptr(a, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("orc_mul_mat_rows rejected its arguments")
+    return y, a
+
+
+def mul_mat_pairs(type_: int, packed, K: int, x, ms, ns, *, x_bf16_bits: bool = False,
+                  w_to_bf16: bool = False):
+    """The same sums for the (m, n) pairs only; returns (y, a) of shape (count,)."""
+    packed = _c(packed, np.uint8)
+    M, pitch = packed.shape
+    xa, xt = _x_args(x, x_bf16_bits)
+    N = xa.shape[0]
+    ms = _c(ms, np.int64)
+    ns = _c(ns, np.int64)
+    y = np.zeros(ms.shape, np.float64)
+    a = np.zeros(ms.shape, np.float64)
+    rc = lib().orc_mul_mat_pairs(type_, _ptr(packed, ctypes.c_uint8), pitch, K, M,
+                                 xa.ctypes.data_as(ctypes.c_void_p), xt, N,
+                                 1 if w_to_bf16 else 0,
+                                 _ptr(ms, ctypes.c_int64), _ptr(ns, ctypes.c_int64), ms.size,
+                                 _ptr(y, ctypes.c_double), _ptr(a, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("orc_mul_mat_pairs rejected its arguments")
+    return y, a

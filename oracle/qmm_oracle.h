@@ -1,0 +1,98 @@
+/*
+ * qmm_oracle.h -- plain, slow CPU reference for block-quantized MUL_MAT.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This is the oracle that the GPU library is
+ * checked against.  Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg may load it.  It shares no code, header, table or constant
+ * with the GPU library (it does not include include/qmm.h) and the GPU library
+ * never calls it.
+ *
+ * Everything here is scalar C with IEEE binary32 arithmetic where the method
+ * fixes binary32 (the quantizer) and binary64 accumulation for every dot
+ * product.  Built with -O2 -ffp-contract=off and no fast-math.
+ *
+ * Sources (the pages this follows):
+ *  - "No Python! Building an AI Inference Engine Exclusively in C++",
+ *    §4 (tensor ne/nb strides) and §6 (the GEMM definition C_ij = sum_k A_ik B_kj).
+ *  - "Development Guide for Small AI Models (TinyLLaMA, etc.) Using C++",
+ *    §6.1 (Q4_0 block: 32 values, one FP16 scale, 32 four-bit values) and
+ *    §6.2 (load, unpack, multiply by the scale, multiply-add with activations).
+ *  - "A Complete Guide to llama.cpp and Customization with C++", §2.2
+ *    (w_i ~= Delta * q_i per block, Delta from the block's max |w|).
+ */
+#ifndef QMM_ORACLE_H
+#define QMM_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight encodings the oracle knows.  Own numbering (not the library's). */
+enum {
+    ORC_F32 = 0,   /* dense binary32 rows                                   */
+    ORC_F16 = 1,   /* dense binary16 rows (bits)                            */
+    ORC_BF16 = 2,  /* dense bfloat16 rows (bits)                            */
+    ORC_Q8_0 = 3,  /* 32-blocks: fp16 scale + 32 int8 codes                 */
+    ORC_Q4_0 = 4   /* 32-blocks: fp16 scale + 32 offset-binary 4-bit codes  */
+};
+
+/* ---- IEEE conversions, written from the format definitions ---------- */
+uint16_t orc_f32_to_f16(float f);        /* round to nearest, ties to even */
+float    orc_f16_to_f32(uint16_t h);     /* exact                          */
+uint16_t orc_f32_to_bf16(float f);       /* round to nearest, ties to even */
+float    orc_bf16_to_f32(uint16_t h);    /* exact                          */
+
+void orc_f32_to_f16_n(const float *src, uint16_t *dst, size_t n);
+void orc_f16_to_f32_n(const uint16_t *src, float *dst, size_t n);
+void orc_f32_to_bf16_n(const float *src, uint16_t *dst, size_t n);
+void orc_bf16_to_f32_n(const uint16_t *src, float *dst, size_t n);
+
+/* ---- one 32-weight block ------------------------------------------- */
+/* Q8_0: scale_bits = fp16(amax/127); q_i = clamp(roundf(w_i/scale), -127, 127). */
+void orc_quantize_block_q8_0(const float w[32], uint16_t *scale_bits, int8_t q[32]);
+/* Q4_0: scale_bits = fp16(amax/8); nib_i = clamp(roundf(w_i/scale) + 8, 0, 15). */
+void orc_quantize_block_q4_0(const float w[32], uint16_t *scale_bits, uint8_t nib[32]);
+
+/* ---- packed rows ------------------------------------------------------
+ * Row-planar packing of one row of K weights (K % 32 == 0):
+ *   bytes [0, 2*K/32)            fp16 scale of block b at offset 2b (little endian)
+ *   zero padding up to qoff = align16(K/16)
+ *   Q8_0: bytes [qoff + 32b, +32) the int8 codes of block b
+ *   Q4_0: bytes [qoff + 16b, +16) block b, byte j = nib_j | nib_{j+16} << 4
+ *   zero padding up to the row size (a multiple of 16).
+ * orc_row_size returns that size (dense types: K * element size).          */
+size_t orc_row_size(int type, int64_t K);
+
+/* Quantize M rows of K floats (row m at w + m*K) into dst (row m at
+ * dst + m*pitch, pitch >= orc_row_size).  Returns 0, or -1 on bad args.     */
+int orc_quantize_rows(int type, const float *w, int64_t K, int64_t M,
+                      uint8_t *dst, size_t pitch);
+
+/* Expand rows of any weight type to exact binary32 values (M x K, dense).  */
+int orc_dequantize_rows(int type, const uint8_t *src, size_t pitch,
+                        int64_t K, int64_t M, float *dst);
+
+/* ---- MUL_MAT ----------------------------------------------------------
+ * y[n][m] = sum_k W'[m][k] * x[n][k], W' the exactly dequantized weights,
+ * accumulated sequentially in binary64; a[n][m] = sum_k |W'[m][k] x[n][k]|.
+ * x_type is ORC_F32 (x as floats, row n at x + n*K) or ORC_BF16 (x as bf16
+ * bits, row n at x + n*K).  w_to_bf16 != 0 first rounds every W' to bf16
+ * (diagnostic variant of the bf16 matrix-core path).  Only rows
+ * [m0, m1) are computed; y and a are N x M (row n at + n*M).             */
+int orc_mul_mat_rows(int type, const uint8_t *w, size_t pitch, int64_t K, int64_t M,
+                     const void *x, int x_type, int64_t N, int w_to_bf16,
+                     int64_t m0, int64_t m1, double *y, double *a);
+
+/* Same sum for a list of (m, n) pairs only: y[i], a[i] for pair i.         */
+int orc_mul_mat_pairs(int type, const uint8_t *w, size_t pitch, int64_t K, int64_t M,
+                      const void *x, int x_type, int64_t N, int w_to_bf16,
+                      const int64_t *ms, const int64_t *ns, int64_t count,
+                      double *y, double *a);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMM_ORACLE_H */
