@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Throughput of block-quantized MUL_MAT on one MI355X (gfx950).
+
+One step = one decode token of a TinyLLaMA-shaped model through libqmm:
+22 decoder layers of Q4_0 weights (Wq, Wk, Wv, Wo, Wgate, Wup, Wdown: seven
+GEMVs per layer, each layer with its own weights, 548 MB in all, more than
+twice the 256 MB Infinity Cache) followed by the 32000 x 2048 Q8_0 LM head.
+The step is captured once into a HIP graph and replayed, the way a decode
+loop is driven.  `value` is the step's algorithmic bytes (packed weights +
+activations + outputs) per second.
+
+Also reported on the same JSON line:
+  * prefill: the Q4_0 x bf16 GEMM 5632 x 2048 x 512 in TFLOP/s;
+  * breakdown: the 512 x 512 Q8_0 GEMV, the fp16 5632 x 2048 GEMV and the
+    Q8_0 LM head with 1, 2, 4 and 8 tokens (GB/s, rotating weight copies);
+  * roofline: the dominant kernel (the Q4_0 FFN gate/up GEMV, 5632 x 2048)
+    timed per launch with HIP events;
+  * cpu_baseline: the CPU oracle on a bounded sample of the same decode step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import threading
+import time
+
+METRIC = "quantized mul_mat GB/s (decode GEMV) & TFLOP/s (prefill), % of roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip prefill/breakdown legs")
+    return ap.parse_args()
+
+
+class Graph:
+    """A captured sequence of library calls, replayed on the current stream."""
+
+    def __init__(self, fn):
+        import torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()                               # warm the path outside capture
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.g):
+            fn()
+        torch.cuda.synchronize()
+
+    def __call__(self):
+        self.g.replay()
+
+
+def timed(fn, steps, warmup):
+    """ms per call of fn over exactly `steps` calls, synchronized on both sides."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall = time.perf_counter()
+    t0.record()
+    for _ in range(steps):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall
+    return t0.elapsed_time(t1) / steps, wall
+
+
+def per_launch_ms(launches):
+    """Average GPU duration of each launch in `launches` (callables that
+    enqueue one kernel on the current stream), measured with an event pair
+    around each launch.  A spin kernel holds the queue first so that the
+    host enqueues everything before the GPU starts: the events then bracket
+    the kernel alone, not the host's launch latency."""
+    import torch
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in launches]
+    torch.cuda._sleep(int(2.4e9 * 0.05))      # ~50 ms at 2.4 GHz
+    for (a, b), fn in zip(evs, launches):
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the library has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import quantized_matmul_ggml_amd as Q
+    from quantized_matmul_ggml_amd import workloads as WL
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} {getattr(props, 'gcnArchName', '')} CUs={props.multi_processor_count}")
+
+    # ------------------------------------------------------------ decode step
+    log("quantizing 22 Q4_0 decoder layers and the Q8_0 LM head on the GPU")
+    layers = []
+    for l in range(WL.LAYERS):
+        mats = {}
+        for t, (name, M, K, _) in enumerate(WL.LAYER):
+            w = WL.weights_device(WL.seed(3, t, l), M, K, dev)
+            mats[name] = Q.quantize(w, Q.Q4_0)
+            del w
+        layers.append(mats)
+    xs = [WL.activations_device(WL.seed(3, 7 + s), 1, k, dev) for s, k in enumerate(WL.LAYER_X_K)]
+    ys = {name: torch.empty((1, M), device=dev) for name, M, _, _ in WL.LAYER}
+    lm = Q.quantize(WL.weights_device(WL.seed(4, 0), WL.VOCAB, WL.HIDDEN, dev), Q.Q8_0)
+    x_lm = WL.activations_device(WL.seed(4, 1), 1, WL.HIDDEN, dev)
+    y_lm = torch.empty((1, WL.VOCAB), device=dev)
+    torch.cuda.synchronize()
+
+    def gemv_bytes(w, n):
+        return w.M * Q.row_size(w.type, w.K) + 4 * n * w.K + 4 * n * w.M
+
+    layer_bytes = sum(gemv_bytes(layers[0][name], 1) for name, *_ in WL.LAYER)
+    step_bytes = WL.LAYERS * layer_bytes + gemv_bytes(lm, 1)
+
+    def decode_step():
+        for L in layers:
+            for name, _, _, slot in WL.LAYER:
+                Q.gemv(L[name], xs[slot], out=ys[name])
+        Q.gemv(lm, x_lm, out=y_lm)
+
+    log("capturing the decode step into a HIP graph")
+    graph = Graph(decode_step)
+    log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
+    ms, wall = timed(graph, args.steps, args.warmup)
+    value = step_bytes / (ms * 1e-3) / 1e9
+    log(f"decode step {ms * 1e3:.1f} us  {value:.0f} GB/s  ({step_bytes / 1e6:.1f} MB/step)")
+
+    # dominant kernel: the gate/up GEMV (two per layer, 26 % of the bytes)
+    gate_launches = []
+    for L in layers:
+        for name in ("wgate", "wup"):
+            gate_launches.append(lambda w=L[name]: Q.gemv(w, xs[2], out=ys["wgate"]))
+    durs = []
+    for _ in range(max(1, args.steps // 4)):
+        durs += per_launch_ms(gate_launches)
+    kern_ms = sum(durs) / len(durs)
+    kern_bytes = gemv_bytes(layers[0]["wgate"], 1)
+    achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
+    log(f"gate/up GEMV {kern_ms * 1e3:.2f} us/launch  {achieved:.0f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "tinyllama_decode_token: 22 x Q4_0 layer (2048/256/256/2048/5632/5632 x 2048, "
+                        "2048 x 5632) + Q8_0 LM head 32000 x 2048, batch 1",
+            "layers": WL.LAYERS, "bytes_per_step": step_bytes, "launches_per_step": 7 * WL.LAYERS + 1,
+            "driver": "hip graph replay",
+            "decode_tokens_per_s": round(1e3 / ms, 1),
+            "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+            "wall_s_timed_region": round(wall, 4),
+        },
+        "roofline": {
+            "kernel": "Q4_0 GEMV 5632 x 2048 (FFN gate/up), batch 1",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "avg_launch_us": round(kern_ms * 1e3, 3), "bytes_per_launch": kern_bytes,
+        },
+    }
+
+    if not args.no_extras:
+        result["prefill"] = prefill_leg(Q, WL, dev, args)
+        result["breakdown"] = breakdown_leg(Q, WL, dev, args, gemv_bytes)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_leg(WL, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def prefill_leg(Q, WL, dev, args):
+    import torch
+    M, K, N = WL.FFN, WL.HIDDEN, 512
+    w = Q.quantize(WL.weights_device(WL.seed(5, 0), M, K, dev), Q.Q4_0)
+    x = WL.activations_device(WL.seed(5, 1), N, K, dev).to(torch.bfloat16)
+    y = torch.empty((N, M), device=dev)
+    reps = 10
+    graph = Graph(lambda: [Q.gemm(w, x, out=y) for _ in range(reps)])
+    ms, _ = timed(graph, max(2, args.steps // 2), 2)
+    per = ms / reps
+    flops = 2.0 * M * K * N
+    tf = flops / (per * 1e-3) / 1e12
+    durs = per_launch_ms([lambda: Q.gemm(w, x, out=y)] * 20)
+    kern = sum(durs) / len(durs)
+    log(f"prefill GEMM {per * 1e3:.1f} us  {tf:.0f} TFLOP/s (per-launch events {kern * 1e3:.1f} us)")
+    return {"workload": "Q4_0 5632 x 2048 x bf16 2048 x 512 -> f32", "us": round(per * 1e3, 2),
+            "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+            "avg_launch_us": round(kern * 1e3, 2), "flops": flops}
+
+
+def breakdown_leg(Q, WL, dev, args, gemv_bytes):
+    import torch
+    out = {}
+
+    def rotate(ws, x, y, n_per_graph):
+        calls = [ws[i % len(ws)] for i in range(n_per_graph)]
+        g = Graph(lambda: [Q.gemv(w, x, out=y) for w in calls])
+        ms, _ = timed(g, max(2, args.steps // 2), 2)
+        return ms / n_per_graph
+
+    # 512 x 512 Q8_0, one token (latency bound: 0.28 MB per call)
+    w1 = [Q.quantize(WL.weights_device(WL.seed(1, 0, r), 512, 512, dev), Q.Q8_0) for r in range(64)]
+    x1 = WL.activations_device(WL.seed(1, 1), 1, 512, dev)
+    y1 = torch.empty((1, 512), device=dev)
+    per = rotate(w1, x1, y1, 256)
+    b = gemv_bytes(w1[0], 1)
+    out["q8_0_gemv_512x512_n1"] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1)}
+    del w1
+
+    # fp16 5632 x 2048, one token: 48 copies (1.1 GB) so HBM is read
+    w2 = []
+    for r in range(48):
+        h = WL.weights_device(WL.seed(2, 0, r), WL.FFN, WL.HIDDEN, dev).to(torch.float16)
+        w2.append(Q.f16_weight(h))
+    x2 = WL.activations_device(WL.seed(2, 1), 1, WL.HIDDEN, dev)
+    y2 = torch.empty((1, WL.FFN), device=dev)
+    per = rotate(w2, x2, y2, 96)
+    b = gemv_bytes(w2[0], 1)
+    out["f16_gemv_5632x2048_n1"] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1),
+                                    "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
+    del w2
+
+    # Q8_0 LM head, 16 copies (1.1 GB), N = 1, 2, 4, 8
+    w4 = [Q.quantize(WL.weights_device(WL.seed(4, 0, r), WL.VOCAB, WL.HIDDEN, dev), Q.Q8_0)
+          for r in range(16)]
+    for n in (1, 2, 4, 8):
+        x4 = WL.activations_device(WL.seed(4, 1), n, WL.HIDDEN, dev)
+        y4 = torch.empty((n, WL.VOCAB), device=dev)
+        per = rotate(w4, x4, y4, 32)
+        b = gemv_bytes(w4[0], n)
+        out[f"q8_0_lm_head_32000x2048_n{n}"] = {
+            "us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1),
+            "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
+    del w4
+    for k, v in out.items():
+        log(f"{k}: {v}")
+    return out
+
+
+def cpu_baseline_leg(WL, seconds):
+    """The oracle (plain C, binary64) on the host cores, on a bounded sample
+    of the decode step: whole decoder layers (same shapes, seeded weights
+    quantized by the oracle itself), repeated until about `seconds` of CPU
+    time, rows split evenly over the threads.  Reported in the step's unit:
+    algorithmic bytes of the sample per second."""
+    import numpy as np
+    import oracle as orc
+    cores = max(1, min(16, os.cpu_count() or 1))
+    xs = [WL.activations(WL.seed(3, 7 + s), 1, k) for s, k in enumerate(WL.LAYER_X_K)]
+    layer = []
+    for t, (name, M, K, slot) in enumerate(WL.LAYER):
+        layer.append((orc.quantize(orc.Q4_0, WL.weights(WL.seed(3, t), M, K)), M, K, slot))
+    layer_bytes = sum(M * orc.row_size(orc.Q4_0, K) + 4 * K + 4 * M for _, M, K, _ in layer)
+
+    def run_layer():
+        jobs = []
+        for packed, M, K, slot in layer:
+            for c in range(cores):
+                jobs.append((packed, K, xs[slot], M * c // cores, M * (c + 1) // cores))
+        chunks = [jobs[i::cores] for i in range(cores)]
+
+        def worker(chunk):
+            for packed, K, x, m0, m1 in chunk:
+                orc.mul_mat(orc.Q4_0, packed, K, x, rows=(m0, m1))
+        th = [threading.Thread(target=worker, args=(c,)) for c in chunks]
+        for t in th:
+            t.start()
+        for t in th:
+            t.join()
+
+    n_layers, t0 = 0, time.perf_counter()
+    while True:
+        run_layer()
+        n_layers += 1
+        el = time.perf_counter() - t0
+        if el * cores >= seconds:
+            break
+    gbs = n_layers * layer_bytes / el / 1e9
+    log(f"cpu oracle: {n_layers} layer(s) in {el:.2f} s on {cores} threads -> {gbs:.3f} GB/s")
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_layers} Q4_0 decoder layers (7 GEMVs each, batch 1; the step has 22 "
+                      f"plus the LM head), binary64 oracle, {el:.2f} s wall"}
+
+
+if __name__ == "__main__":
+    main()

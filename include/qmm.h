@@ -1,0 +1,153 @@
+/*
+ * qmm.h -- C ABI of libqmm: block-quantized MUL_MAT on AMD Instinct MI355X
+ * (gfx950), in its two forms: the decode GEMV (one to eight tokens, fp32
+ * activations) and the prefill GEMM (many tokens, bf16 activations).
+ *
+ * The operation is the weight-by-activation matrix product that the pages
+ * single out as the bulk of LLM inference time ("No Python! Building an AI
+ * Inference Engine Exclusively in C++", §6; "A Complete Guide to llama.cpp and
+ * Customization with C++", §2.1: with one token per step it is a GEMV), over
+ * block-quantized weights ("Development Guide for Small AI Models (TinyLLaMA,
+ * etc.) Using C++", §6.1-§6.2; "A Complete Guide to llama.cpp ...", §2.2).
+ *
+ * Tensors follow the pages' ne / nb convention ("No Python! ...", §4):
+ * ne[i] is the number of elements along dimension i, nb[i] the distance in
+ * BYTES between neighbours along dimension i, and ne[0] is the contiguous
+ * dimension.  A matrix with ne = [K, M] therefore holds M rows of K elements,
+ * row r starting at data + r * nb[1].
+ *
+ * MUL_MAT semantics (every entry point below):
+ *     W  ne = [K, M]   weights, one row per output feature
+ *     x  ne = [K, N]   activations, one row of K per token
+ *     y  ne = [M, N]   F32 result, one row of M per token
+ *     y[n][m] = sum_k W'[m][k] * x[n][k]
+ * where W' is the dequantized weight: Delta_b * code for the 32-weight block b
+ * that holds k.  The contraction runs over ne[0] of both operands (the second
+ * operand is the "transposed" one of the pages' tensor_mul_mat, §5 of
+ * "No Python! ...").
+ *
+ * Quantized row layout ("row-planar"; the pages fix the block contents but
+ * not the byte order, see the Development Guide §6.1):
+ *     bytes [0, 2*K/32)       fp16 scale Delta_b of block b at offset 2b (LE)
+ *     zero padding up to qoff = align16(K/16)
+ *     Q8_0: bytes [qoff + 32b, +32)  the 32 int8 codes of block b
+ *     Q4_0: bytes [qoff + 16b, +16)  block b, byte j = code_j | code_{j+16} << 4,
+ *                                    stored codes 0..15 meaning code - 8
+ *     zero padding up to qmm_row_size() (a multiple of 16 bytes).
+ * The row keeps the 34 (Q8_0) or 18 (Q4_0) bytes per 32 weights of the block
+ * records; when K is a multiple of 256 there is no padding at all.
+ *
+ * Ownership and errors (all entry points):
+ *  - Every buffer is caller-owned DEVICE memory; the library allocates
+ *    nothing, keeps no pointer after returning and holds no global state.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *    Work is enqueued asynchronously; nothing synchronizes.
+ *  - Arguments are validated on the host before anything is enqueued.  A
+ *    non-zero (negative) return means nothing was enqueued and every output
+ *    is untouched.  A launch failure returns QMM_ERR_DEVICE; faults during
+ *    execution surface at the caller's next synchronization of `stream`.
+ *  - Tensors with zero rows or zero tokens are valid and enqueue nothing.
+ *    K = 0 yields y = 0.
+ *  - Entry points are thread-safe.
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define QMM_API __attribute__((visibility("default")))
+#else
+#define QMM_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element / block types.  F16 and BF16 are IEEE binary16 and bfloat16. */
+typedef enum {
+    QMM_TYPE_F32  = 0,
+    QMM_TYPE_F16  = 1,
+    QMM_TYPE_BF16 = 2,
+    QMM_TYPE_Q8_0 = 3,  /* 32-blocks: fp16 Delta + 32 int8 codes in [-127, 127]   */
+    QMM_TYPE_Q4_0 = 4   /* 32-blocks: fp16 Delta + 32 four-bit codes (value - 8)  */
+} qmm_type;
+
+typedef enum {
+    QMM_OK              = 0,
+    QMM_ERR_NULL        = -1,  /* a descriptor or a needed data pointer is NULL      */
+    QMM_ERR_TYPE        = -2,  /* type not accepted by this entry point              */
+    QMM_ERR_SHAPE       = -3,  /* ne mismatch between operands, K % 32 != 0, N range */
+    QMM_ERR_LAYOUT      = -4,  /* nb / alignment not supported                       */
+    QMM_ERR_ALIAS       = -5,  /* the output overlaps an input                       */
+    QMM_ERR_UNSUPPORTED = -6,  /* n_dims > 2, ne[2] or ne[3] != 1, or K*N too large */
+    QMM_ERR_DEVICE      = -7   /* the HIP runtime refused the launch                 */
+} qmm_status;
+
+/* Tensor descriptor ("No Python! ...", §4: Tensor {n_dims, ne[4], nb[4],
+ * type, data}).  Layout rules checked by every entry point:
+ *  - n_dims is 1 or 2, ne[2] = ne[3] = 1 (higher dims: QMM_ERR_UNSUPPORTED);
+ *  - dense types: nb[0] = element size;  quantized types: nb[0] = 0;
+ *  - nb[1] >= qmm_row_size(type, ne[0]); for quantized weights nb[1] % 16 == 0
+ *    and data % 16 == 0; F16 weights need nb[1] % 16 == 0 and data % 16 == 0;
+ *    F32 activations and outputs need 4-byte alignment of data and nb[1];
+ *    BF16 activations of qmm_gemm need 16-byte alignment of data and nb[1];
+ *  - quantized ne[0] must be a multiple of 32 (else QMM_ERR_SHAPE). */
+typedef struct qmm_tensor {
+    int32_t  type;     /* qmm_type                          */
+    int32_t  n_dims;   /* 1 or 2                            */
+    int64_t  ne[4];    /* elements per dimension            */
+    uint64_t nb[4];    /* byte stride per dimension         */
+    void    *data;     /* device pointer                    */
+} qmm_tensor;
+
+/* Bytes of one packed (or dense) row of ne0 elements; 0 for an unknown type
+ * or an invalid ne0 (negative, or not a multiple of 32 for Q8_0 / Q4_0).
+ * Q8_0: align16(ne0/16) + align16(ne0);  Q4_0: align16(ne0/16) + align16(ne0/2). */
+QMM_API size_t qmm_row_size(int32_t type, int64_t ne0);
+
+/* Quantize F32 rows into Q8_0 or Q4_0 rows (load time, once per weight).
+ * src: F32 ne = [K, M];  dst: Q8_0 or Q4_0 ne = [K, M], K % 32 == 0.
+ * Per block of 32 ("A Complete Guide to llama.cpp ...", §2.2; Development
+ * Guide §6.1): amax = max|w|; Delta = fp16(amax / 127) for Q8_0 or
+ * fp16(amax / 8) for Q4_0 (round to nearest even); code = round(w / Delta)
+ * half away from zero, one IEEE binary32 division by the stored Delta;
+ * Q8_0 clamps to [-127, 127], Q4_0 stores code + 8 clamped to [0, 15];
+ * Delta = 0 gives all-zero codes.  Bit-exact and deterministic.  Inputs must
+ * be finite with amax / 127 (Q8_0) or amax / 8 (Q4_0) below 65520. */
+QMM_API int qmm_quantize(const qmm_tensor *src_f32, qmm_tensor *dst_q, void *stream);
+
+/* Expand Q8_0 / Q4_0 / F16 rows to F32 (W' = Delta * code, exact in binary32;
+ * "Development Guide ...", §6.2 step "Dequantization").
+ * src ne = [K, M];  dst: F32 ne = [K, M].  Bit-exact. */
+QMM_API int qmm_dequantize(const qmm_tensor *src, qmm_tensor *dst_f32, void *stream);
+
+/* Decode GEMV / skinny GEMM ("A Complete Guide to llama.cpp ...", §2.1: one
+ * token per step makes every projection a GEMV).
+ * w: Q8_0, Q4_0 or F16, ne = [K, M];  x: F32 ne = [K, N], 1 <= N <= 8
+ * (N > 8: QMM_ERR_SHAPE);  y: F32 ne = [M, N], must not overlap w or x.
+ * Each lane keeps its slice of x in registers, which bounds the size: the
+ * call returns QMM_ERR_UNSUPPORTED when K * N exceeds 32768 (Q4_0), 16384
+ * (Q8_0) or 8192 (F16), counting N rounded up to 1, 2, 4 or 8.
+ * Weights are read once from HBM and dequantized in registers; binary32
+ * multiply-add; the accumulation order is unspecified (results agree with
+ * the exact sum within 1e-4 * sum_k |W'[m][k] x[n][k]| + 1e-6). */
+QMM_API int qmm_gemv(const qmm_tensor *w, const qmm_tensor *x_f32, qmm_tensor *y_f32, void *stream);
+
+/* Prefill GEMM ("No Python! ...", §6: C_ij = sum_k A_ik B_kj, with many tokens
+ * per step).  w: Q4_0 or Q8_0, ne = [K, M];  x: BF16 ne = [K, N], any N >= 0;
+ * y: F32 ne = [M, N], must not overlap w or x.  Weight tiles are dequantized
+ * to bfloat16 (round to nearest even) and multiplied on the bf16 matrix cores
+ * with binary32 accumulation (results agree with the exact sum of the
+ * dequantized weights within 1e-2 * sum_k |W'[m][k] x[n][k]| + 1e-5). */
+QMM_API int qmm_gemm(const qmm_tensor *w, const qmm_tensor *x_bf16, qmm_tensor *y_f32, void *stream);
+
+/* Static text for a qmm_status value (never NULL). */
+QMM_API const char *qmm_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMM_H */

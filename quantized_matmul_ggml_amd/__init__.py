@@ -1,0 +1,12 @@
+"""libqmm: block-quantized MUL_MAT (decode GEMV, prefill GEMM) on MI355X.
+
+The compute lives in hand-written HIP kernels (csrc/, built into libqmm.so by
+``python -m quantized_matmul_ggml_amd.build``); ``binding`` is a thin ctypes
+layer over the C ABI of include/qmm.h, with torch supplying device memory and
+streams.
+"""
+from .binding import (BF16, F16, F32, Q4_0, Q8_0, QmmError, Weight, dequantize, f16_weight,
+                      gemm, gemv, quantize, row_size, strerror)
+
+__all__ = ["BF16", "F16", "F32", "Q4_0", "Q8_0", "QmmError", "Weight", "dequantize",
+           "f16_weight", "gemm", "gemv", "quantize", "row_size", "strerror"]

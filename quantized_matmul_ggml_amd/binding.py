@@ -1,0 +1,199 @@
+"""ctypes binding of libqmm (include/qmm.h): argument marshalling only.
+
+Every computation runs in the HIP kernels of libqmm.so; this module only
+builds ``qmm_tensor`` descriptors from torch tensors (device memory and the
+current stream come from torch) and turns non-zero status codes into
+exceptions.  There is no CPU fallback: if the library is missing or a tensor
+is not on the GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqmm.so")
+
+# qmm_type
+F32, F16, BF16, Q8_0, Q4_0 = 0, 1, 2, 3, 4
+TYPE_NAMES = {F32: "F32", F16: "F16", BF16: "BF16", Q8_0: "Q8_0", Q4_0: "Q4_0"}
+
+# qmm_status
+OK, ERR_NULL, ERR_TYPE, ERR_SHAPE, ERR_LAYOUT, ERR_ALIAS, ERR_UNSUPPORTED, ERR_DEVICE = \
+    0, -1, -2, -3, -4, -5, -6, -7
+
+EXPORTS = ("qmm_row_size", "qmm_quantize", "qmm_dequantize", "qmm_gemv", "qmm_gemm",
+           "qmm_strerror")
+
+
+class QmmTensor(ctypes.Structure):
+    """Mirror of ``qmm_tensor`` (ne/nb convention: ne[0] contiguous, nb in bytes)."""
+    _fields_ = [("type", ctypes.c_int32), ("n_dims", ctypes.c_int32),
+                ("ne", ctypes.c_int64 * 4), ("nb", ctypes.c_uint64 * 4),
+                ("data", ctypes.c_void_p)]
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqmm.so from the package directory (build it with build.py)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m quantized_matmul_ggml_amd.build` "
+                "(hipcc, gfx950); there is no fallback implementation")
+        h = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(QmmTensor)
+        h.qmm_row_size.argtypes = [ctypes.c_int32, ctypes.c_int64]
+        h.qmm_row_size.restype = ctypes.c_size_t
+        h.qmm_quantize.argtypes = [P, P, ctypes.c_void_p]
+        h.qmm_dequantize.argtypes = [P, P, ctypes.c_void_p]
+        h.qmm_gemv.argtypes = [P, P, P, ctypes.c_void_p]
+        h.qmm_gemm.argtypes = [P, P, P, ctypes.c_void_p]
+        for f in ("qmm_quantize", "qmm_dequantize", "qmm_gemv", "qmm_gemm"):
+            getattr(h, f).restype = ctypes.c_int
+        h.qmm_strerror.argtypes = [ctypes.c_int]
+        h.qmm_strerror.restype = ctypes.c_char_p
+        _lib = h
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().qmm_strerror(status).decode()
+
+
+def row_size(type_: int, K: int) -> int:
+    return int(lib().qmm_row_size(type_, K))
+
+
+def make_desc(type_: int, ne0: int, ne1: int, nb1: int, data_ptr: int, n_dims: int = 2,
+              nb0: int | None = None) -> QmmTensor:
+    """A raw descriptor (used directly by the boundary tests)."""
+    t = QmmTensor()
+    t.type = type_
+    t.n_dims = n_dims
+    t.ne[0], t.ne[1], t.ne[2], t.ne[3] = ne0, ne1, 1, 1
+    if nb0 is None:
+        nb0 = {F32: 4, F16: 2, BF16: 2}.get(type_, 0)
+    t.nb[0], t.nb[1] = nb0, nb1
+    t.nb[2] = t.nb[3] = nb1 * max(ne1, 1)
+    t.data = data_ptr
+    return t
+
+
+@dataclass
+class Weight:
+    """A weight matrix W (ne = [K, M]): M rows of K weights on the GPU.
+
+    data is uint8 (M, pitch) for Q8_0 / Q4_0 rows in the row-planar layout of
+    include/qmm.h, or float16 (M, >= K) for F16 rows."""
+    data: torch.Tensor
+    type: int
+    K: int
+    M: int
+
+    @property
+    def pitch(self) -> int:
+        return self.data.stride(0) * self.data.element_size()
+
+    def desc(self) -> QmmTensor:
+        return make_desc(self.type, self.K, self.M, self.pitch, self.data.data_ptr())
+
+    def rows(self, r0: int, r1: int) -> "Weight":
+        """Row-range view [r0, r1): no copy, same pitch."""
+        return Weight(self.data[r0:r1], self.type, self.K, r1 - r0)
+
+
+def _need_gpu(*ts: torch.Tensor):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("libqmm operates on GPU tensors only")
+
+
+def _dense_desc(t: torch.Tensor, type_: int) -> QmmTensor:
+    """2-D row-major torch tensor (rows, cols) -> ne = [cols, rows]."""
+    assert t.dim() == 2 and t.stride(1) == 1
+    es = t.element_size()
+    return make_desc(type_, t.shape[1], t.shape[0], t.stride(0) * es, t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise QmmError(status, where)
+
+
+def quantize(w: torch.Tensor, type_: int, *, pitch: int | None = None, stream=None) -> Weight:
+    """Quantize fp32 rows w (M, K) on the GPU into Q8_0 / Q4_0 rows."""
+    _need_gpu(w)
+    M, K = w.shape
+    rs = row_size(type_, K)
+    pitch = rs if pitch is None else pitch
+    out = torch.empty((M, pitch), dtype=torch.uint8, device=w.device)
+    if pitch > rs:
+        out[:, rs:].zero_()
+    wt = Weight(out, type_, K, M)
+    src, dst = _dense_desc(w, F32), wt.desc()
+    _check(lib().qmm_quantize(ctypes.byref(src), ctypes.byref(dst), _stream(stream)), "qmm_quantize")
+    return wt
+
+
+def dequantize(w: Weight, *, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """W' as fp32 (M, K)."""
+    _need_gpu(w.data)
+    if out is None:
+        out = torch.empty((w.M, w.K), dtype=torch.float32, device=w.data.device)
+    src, dst = w.desc(), _dense_desc(out, F32)
+    _check(lib().qmm_dequantize(ctypes.byref(src), ctypes.byref(dst), _stream(stream)),
+           "qmm_dequantize")
+    return out
+
+
+def f16_weight(w16: torch.Tensor) -> Weight:
+    """Wrap float16 rows (M, K) as an F16 weight."""
+    _need_gpu(w16)
+    assert w16.dtype == torch.float16
+    return Weight(w16, F16, w16.shape[1], w16.shape[0])
+
+
+def gemv(w: Weight, x: torch.Tensor, *, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y (N, M) fp32 = x (N, K) fp32 times W'^T; 1 <= N <= 8."""
+    _need_gpu(w.data, x)
+    if out is None:
+        out = torch.empty((x.shape[0], w.M), dtype=torch.float32, device=x.device)
+    wd, xd, yd = w.desc(), _dense_desc(x, F32), _dense_desc(out, F32)
+    _check(lib().qmm_gemv(ctypes.byref(wd), ctypes.byref(xd), ctypes.byref(yd), _stream(stream)),
+           "qmm_gemv")
+    return out
+
+
+def gemm(w: Weight, x: torch.Tensor, *, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y (N, M) fp32 = x (N, K) bf16 times W'^T on the bf16 matrix cores."""
+    _need_gpu(w.data, x)
+    if out is None:
+        out = torch.empty((x.shape[0], w.M), dtype=torch.float32, device=x.device)
+    wd, xd, yd = w.desc(), _dense_desc(x, BF16), _dense_desc(out, F32)
+    _check(lib().qmm_gemm(ctypes.byref(wd), ctypes.byref(xd), ctypes.byref(yd), _stream(stream)),
+           "qmm_gemm")
+    return out
+
+
+def call_raw(name: str, *descs: QmmTensor, stream: int = 0) -> int:
+    """Call an entry point with hand-made descriptors; returns the status."""
+    fn = getattr(lib(), name)
+    return fn(*[ctypes.byref(d) if d is not None else None for d in descs], ctypes.c_void_p(stream))

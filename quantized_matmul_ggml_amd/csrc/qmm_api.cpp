@@ -1,0 +1,209 @@
+// qmm_api.cpp -- the C entry points of libqmm: descriptor validation and
+// kernel dispatch.  Everything here runs on the host and touches no device
+// memory; a call either enqueues its kernels on the caller's stream and
+// returns QMM_OK, or returns a negative qmm_status with nothing enqueued.
+//
+// Descriptor convention: No Python! Building an AI Inference Engine
+// Exclusively in C++, §4 (ne = elements per dimension, nb = byte strides,
+// ne[0] contiguous).  Operand roles of MUL_MAT: same page, §5 (the result
+// takes ne = {a.ne[0], b.ne[1]} with b "transposed") read together with the
+// stride definition: W ne = [K, M], x ne = [K, N], y ne = [M, N].
+#include "../../include/qmm.h"
+#include "qmm_internal.h"
+
+namespace {
+
+using qmm::W_BF16;
+using qmm::W_F16;
+using qmm::W_F32;
+using qmm::W_Q4_0;
+using qmm::W_Q8_0;
+
+bool is_quant(int t) { return t == QMM_TYPE_Q8_0 || t == QMM_TYPE_Q4_0; }
+
+int64_t elem_size(int t)
+{
+    switch (t) {
+    case QMM_TYPE_F32: return 4;
+    case QMM_TYPE_F16: return 2;
+    case QMM_TYPE_BF16: return 2;
+    default: return 0;
+    }
+}
+
+// Shape / layout rules shared by every operand.  `align` is the byte
+// alignment required of data and nb[1].
+int check_tensor(const qmm_tensor *t, uint64_t align)
+{
+    if (!t) return QMM_ERR_NULL;
+    if (t->type < QMM_TYPE_F32 || t->type > QMM_TYPE_Q4_0) return QMM_ERR_TYPE;
+    if (t->n_dims < 1 || t->n_dims > 4) return QMM_ERR_UNSUPPORTED;
+    if (t->n_dims > 2 || t->ne[2] != 1 || t->ne[3] != 1) return QMM_ERR_UNSUPPORTED;
+    if (t->ne[0] < 0 || t->ne[1] < 0) return QMM_ERR_SHAPE;
+    if (t->n_dims == 1 && t->ne[1] != 1) return QMM_ERR_SHAPE;
+    if (is_quant(t->type)) {
+        if (t->ne[0] % 32 != 0) return QMM_ERR_SHAPE;
+        if (t->nb[0] != 0) return QMM_ERR_LAYOUT;
+    } else if ((int64_t)t->nb[0] != elem_size(t->type)) {
+        return QMM_ERR_LAYOUT;
+    }
+    const uint64_t rs = qmm_row_size(t->type, t->ne[0]);
+    if (t->ne[1] > 1 && t->nb[1] < rs) return QMM_ERR_LAYOUT;
+    if (t->ne[1] > 1 && t->nb[1] % align != 0) return QMM_ERR_LAYOUT;
+    const bool empty = t->ne[0] == 0 || t->ne[1] == 0;
+    if (!t->data && !empty) return QMM_ERR_NULL;
+    if ((uintptr_t)t->data % align != 0) return QMM_ERR_LAYOUT;
+    return QMM_OK;
+}
+
+// Byte range [lo, hi) a 2-D tensor touches.
+void extent(const qmm_tensor *t, uintptr_t *lo, uintptr_t *hi)
+{
+    const uint64_t rs = qmm_row_size(t->type, t->ne[0]);
+    *lo = (uintptr_t)t->data;
+    *hi = *lo + (t->ne[1] > 0 ? (uint64_t)(t->ne[1] - 1) * t->nb[1] + rs : 0);
+}
+
+bool overlaps(const qmm_tensor *a, const qmm_tensor *b)
+{
+    uintptr_t alo, ahi, blo, bhi;
+    extent(a, &alo, &ahi);
+    extent(b, &blo, &bhi);
+    if (alo == ahi || blo == bhi) return false;
+    return alo < bhi && blo < ahi;
+}
+
+qmm::WeightView weight_view(const qmm_tensor *w)
+{
+    qmm::WeightView v;
+    v.base = static_cast<const uint8_t *>(w->data);
+    v.pitch = w->ne[1] > 1 ? w->nb[1] : qmm_row_size(w->type, w->ne[0]);
+    v.K = w->ne[0];
+    v.M = w->ne[1];
+    v.type = w->type;
+    return v;
+}
+
+uint64_t pitch_elems(const qmm_tensor *t)
+{
+    const int64_t es = elem_size(t->type);
+    return t->ne[1] > 1 ? t->nb[1] / (uint64_t)es : (uint64_t)t->ne[0];
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_DEVICE; }
+
+// Common checks of MUL_MAT operands.
+int check_mul_mat(const qmm_tensor *w, const qmm_tensor *x, const qmm_tensor *y,
+                  int x_type, uint64_t x_align)
+{
+    if (!w || !x || !y) return QMM_ERR_NULL;
+    int rc = check_tensor(w, 16);
+    if (rc) return rc;
+    rc = check_tensor(x, x_align);
+    if (rc) return rc;
+    rc = check_tensor(y, 4);
+    if (rc) return rc;
+    if (x->type != x_type || y->type != QMM_TYPE_F32) return QMM_ERR_TYPE;
+    if (x->ne[0] != w->ne[0]) return QMM_ERR_SHAPE;
+    if (y->ne[0] != w->ne[1] || y->ne[1] != x->ne[1]) return QMM_ERR_SHAPE;
+    if (overlaps(y, w) || overlaps(y, x)) return QMM_ERR_ALIAS;
+    return QMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qmm_row_size(int32_t type, int64_t ne0)
+{
+    if (ne0 < 0) return 0;
+    const uint64_t k = (uint64_t)ne0;
+    auto a16 = [](uint64_t v) { return (v + 15) / 16 * 16; };
+    switch (type) {
+    case QMM_TYPE_F32: return k * 4;
+    case QMM_TYPE_F16: return k * 2;
+    case QMM_TYPE_BF16: return k * 2;
+    case QMM_TYPE_Q8_0: return (k % 32) ? 0 : a16(k / 16) + a16(k);
+    case QMM_TYPE_Q4_0: return (k % 32) ? 0 : a16(k / 16) + a16(k / 2);
+    default: return 0;
+    }
+}
+
+int qmm_quantize(const qmm_tensor *src, qmm_tensor *dst, void *stream)
+{
+    if (!src || !dst) return QMM_ERR_NULL;
+    int rc = check_tensor(src, 4);
+    if (rc) return rc;
+    rc = check_tensor(dst, 16);
+    if (rc) return rc;
+    if (src->type != QMM_TYPE_F32 || !is_quant(dst->type)) return QMM_ERR_TYPE;
+    if (src->ne[0] != dst->ne[0] || src->ne[1] != dst->ne[1]) return QMM_ERR_SHAPE;
+    if (src->ne[0] % 32 != 0) return QMM_ERR_SHAPE;
+    if (overlaps(dst, src)) return QMM_ERR_ALIAS;
+    const qmm::WeightView d = weight_view(dst);
+    return status_of(qmm::launch_quantize(static_cast<const float *>(src->data), pitch_elems(src),
+                                          src->ne[0], src->ne[1],
+                                          static_cast<uint8_t *>(dst->data), d.pitch, dst->type,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int qmm_dequantize(const qmm_tensor *src, qmm_tensor *dst, void *stream)
+{
+    if (!src || !dst) return QMM_ERR_NULL;
+    int rc = check_tensor(src, 16);
+    if (rc) return rc;
+    rc = check_tensor(dst, 4);
+    if (rc) return rc;
+    if (!(is_quant(src->type) || src->type == QMM_TYPE_F16) || dst->type != QMM_TYPE_F32)
+        return QMM_ERR_TYPE;
+    if (src->ne[0] != dst->ne[0] || src->ne[1] != dst->ne[1]) return QMM_ERR_SHAPE;
+    if (overlaps(dst, src)) return QMM_ERR_ALIAS;
+    const qmm::WeightView s = weight_view(src);
+    return status_of(qmm::launch_dequantize(s.base, s.pitch, s.K, s.M, s.type,
+                                            static_cast<float *>(dst->data), pitch_elems(dst),
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int qmm_gemv(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *stream)
+{
+    int rc = check_mul_mat(w, x, y, QMM_TYPE_F32, 4);
+    if (rc) return rc;
+    if (!(is_quant(w->type) || w->type == QMM_TYPE_F16)) return QMM_ERR_TYPE;
+    if (x->ne[1] > 8) return QMM_ERR_SHAPE;
+    if (x->ne[1] == 0 || w->ne[1] == 0) return QMM_OK;
+    // The activation slice of every lane lives in registers (at most 128
+    // floats per lane), which bounds K * N.
+    qmm::GemvConfig cfg;
+    if (!qmm::gemv_config(w->type, w->ne[0], w->ne[1], x->ne[1], &cfg)) return QMM_ERR_UNSUPPORTED;
+    qmm::ActView xv{x->data, pitch_elems(x), x->ne[1]};
+    qmm::OutView yv{static_cast<float *>(y->data), pitch_elems(y)};
+    return status_of(qmm::launch_gemv(weight_view(w), xv, yv, static_cast<hipStream_t>(stream)));
+}
+
+int qmm_gemm(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *stream)
+{
+    int rc = check_mul_mat(w, x, y, QMM_TYPE_BF16, 16);
+    if (rc) return rc;
+    if (!is_quant(w->type)) return QMM_ERR_TYPE;
+    qmm::ActView xv{x->data, pitch_elems(x), x->ne[1]};
+    qmm::OutView yv{static_cast<float *>(y->data), pitch_elems(y)};
+    if (w->ne[1] == 0 || x->ne[1] == 0) return QMM_OK;
+    return status_of(qmm::launch_gemm(weight_view(w), xv, yv, static_cast<hipStream_t>(stream)));
+}
+
+const char *qmm_strerror(int status)
+{
+    switch (status) {
+    case QMM_OK: return "success";
+    case QMM_ERR_NULL: return "a descriptor or data pointer is NULL";
+    case QMM_ERR_TYPE: return "operand type not accepted by this entry point";
+    case QMM_ERR_SHAPE: return "operand shapes do not match (or K % 32 != 0, or N out of range)";
+    case QMM_ERR_LAYOUT: return "unsupported strides or alignment";
+    case QMM_ERR_ALIAS: return "the output overlaps an input";
+    case QMM_ERR_UNSUPPORTED: return "unsupported tensor rank or size";
+    case QMM_ERR_DEVICE: return "the HIP runtime refused the launch";
+    default: return "unknown qmm status";
+    }
+}
+
+}  // extern "C"

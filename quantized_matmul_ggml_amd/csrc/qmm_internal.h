@@ -1,0 +1,64 @@
+// qmm_internal.h -- declarations shared by the host entry points (qmm_api.cpp)
+// and the kernel translation units (*.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmm {
+
+// Weight encodings the kernels understand (same values as qmm_type).
+enum WType : int { W_F32 = 0, W_F16 = 1, W_BF16 = 2, W_Q8_0 = 3, W_Q4_0 = 4 };
+
+// Byte offset of the codes inside a quantized row: the K/32 fp16 scales come
+// first, padded to 16 bytes.
+__host__ __device__ inline int64_t quant_offset(int64_t K) { return ((K / 16) + 15) / 16 * 16; }
+
+// One weight matrix as the kernels see it: M rows of K weights, row r at
+// base + r * pitch (bytes).
+struct WeightView {
+    const uint8_t *base;
+    uint64_t pitch;
+    int64_t K;
+    int64_t M;
+    int type;
+};
+
+// Activations: N rows of K values, row n at data + n * pitch_elems elements.
+struct ActView {
+    const void *data;
+    uint64_t pitch_elems;
+    int64_t N;
+};
+
+// Output: N rows of M floats, row n at data + n * pitch_elems.
+struct OutView {
+    float *data;
+    uint64_t pitch_elems;
+};
+
+// Launch shape of the GEMV kernel, a pure function of (type, K, M, N).
+struct GemvConfig {
+    int nt;    // tokens per kernel instance (N rounded up to 1, 2, 4 or 8)
+    int ks;    // waves sharing one row (1, 2 or 4)
+    int cpl;   // 16-byte code chunks per lane (1, 2, 4 or 8)
+    int u;     // rows per wave group per iteration
+};
+
+// Fills cfg and returns true when the register-resident GEMV supports the
+// shape (each lane keeps at most 128 activation floats); false otherwise.
+bool gemv_config(int type, int64_t K, int64_t M, int64_t N, GemvConfig *cfg);
+
+// Launchers (return hipSuccess or the launch error).  Shapes are validated by
+// the caller; every launcher accepts M == 0 / N == 0 as a no-op.
+hipError_t launch_quantize(const float *src, uint64_t src_pitch_elems, int64_t K, int64_t M,
+                           uint8_t *dst, uint64_t dst_pitch, int type, hipStream_t stream);
+hipError_t launch_dequantize(const uint8_t *src, uint64_t src_pitch, int64_t K, int64_t M,
+                             int type, float *dst, uint64_t dst_pitch_elems, hipStream_t stream);
+hipError_t launch_gemv(const WeightView &w, const ActView &x, const OutView &y,
+                       hipStream_t stream);
+hipError_t launch_gemm(const WeightView &w, const ActView &x, const OutView &y,
+                       hipStream_t stream);
+
+}  // namespace qmm

@@ -25,3 +25,12 @@ def orc():
     import oracle
     oracle.lib()
     return oracle
+
+
+@pytest.fixture(scope="session")
+def qmm_lib():
+    """libqmm.so, built in-tree with hipcc if it is not there yet."""
+    from quantized_matmul_ggml_amd import binding, build
+    if not os.path.exists(binding.LIB_PATH):
+        build.build()
+    return binding

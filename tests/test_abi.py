@@ -1,0 +1,166 @@
+"""The C-ABI boundary on the CPU (no compute calls): libqmm.so loads, exports
+every entry point include/qmm.h declares, sizes rows as the header states, and
+rejects malformed descriptors before enqueueing anything.
+
+Validation runs on the host before any HIP call, so the rejected calls below
+never reach the GPU.  They use fake device addresses, so they only run where
+no GPU is visible (the GPU tests exercise the accepted paths with real
+memory)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+from quantized_matmul_ggml_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmm.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"QMM_API\s+[^;(]*?\b(qmm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(qmm_lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", qmm_lib.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (qmm_\w+)", out))
+    assert set(_declared()) <= exported
+    assert exported == set(_declared()), "only the C ABI is exported"
+    for name in _declared():
+        assert getattr(qmm_lib.lib(), name) is not None
+
+
+def test_row_size_closed_forms(qmm_lib):
+    rs = qmm_lib.row_size
+    for K in (256, 512, 2048, 5632, 32768):
+        assert rs(B.Q8_0, K) == 17 * K // 16     # 34 bytes per 32 weights
+        assert rs(B.Q4_0, K) == 9 * K // 16      # 18 bytes per 32 weights
+    assert rs(B.Q4_0, 32) == 32 and rs(B.Q8_0, 32) == 48
+    assert rs(B.Q4_0, 96) == 64 and rs(B.Q8_0, 96) == 112
+    assert rs(B.F16, 7) == 14 and rs(B.F32, 7) == 28 and rs(B.BF16, 3) == 6
+    assert rs(B.Q4_0, 33) == 0 and rs(B.Q8_0, -32) == 0 and rs(99, 32) == 0
+    assert rs(B.Q4_0, 0) == 0
+
+
+def test_row_size_matches_oracle(qmm_lib, orc):
+    for K in (32, 64, 96, 160, 512, 2048, 5632, 4096 + 32):
+        assert qmm_lib.row_size(B.Q8_0, K) == orc.row_size(orc.Q8_0, K)
+        assert qmm_lib.row_size(B.Q4_0, K) == orc.row_size(orc.Q4_0, K)
+
+
+def test_strerror_covers_every_status(qmm_lib):
+    seen = set()
+    for s in range(-7, 1):
+        t = qmm_lib.strerror(s)
+        assert t and t not in seen
+        seen.add(t)
+    assert "unknown" in qmm_lib.strerror(-99)
+
+
+no_gpu = pytest.mark.skipif(
+    __import__("torch").cuda.device_count() > 0,
+    reason="fake device addresses: host-only validation checks run where no GPU is visible")
+
+BASE = 0x7F0000000000        # fake, 4 KiB aligned device addresses
+W_ADDR, X_ADDR, Y_ADDR = BASE, BASE + (1 << 32), BASE + (2 << 32)
+
+
+def _w(type_=B.Q4_0, K=2048, M=64, addr=W_ADDR, pitch=None):
+    return B.make_desc(type_, K, M, pitch if pitch is not None else B.row_size(type_, K), addr)
+
+
+def _x(type_=B.F32, K=2048, N=1, addr=X_ADDR):
+    es = 4 if type_ == B.F32 else 2
+    return B.make_desc(type_, K, N, K * es, addr)
+
+
+def _y(M=64, N=1, addr=Y_ADDR):
+    return B.make_desc(B.F32, M, N, M * 4, addr)
+
+
+@no_gpu
+@pytest.mark.parametrize("case,expect", [
+    ("null_w", B.ERR_NULL), ("null_data", B.ERR_NULL), ("w_f32", B.ERR_TYPE),
+    ("x_bf16", B.ERR_TYPE), ("y_f16", B.ERR_TYPE), ("k_mismatch", B.ERR_SHAPE),
+    ("k_not_32", B.ERR_SHAPE), ("n_over_8", B.ERR_SHAPE), ("y_rows", B.ERR_SHAPE),
+    ("y_tokens", B.ERR_SHAPE), ("w_misaligned", B.ERR_LAYOUT), ("pitch_small", B.ERR_LAYOUT),
+    ("pitch_unaligned", B.ERR_LAYOUT), ("nb0_quant", B.ERR_LAYOUT), ("nb0_dense", B.ERR_LAYOUT),
+    ("x_misaligned", B.ERR_LAYOUT), ("three_dims", B.ERR_UNSUPPORTED),
+    ("ne2", B.ERR_UNSUPPORTED), ("alias_y_w", B.ERR_ALIAS), ("alias_y_x", B.ERR_ALIAS),
+    ("too_large", B.ERR_UNSUPPORTED), ("bad_type", B.ERR_TYPE), ("neg_ne", B.ERR_SHAPE),
+])
+def test_gemv_rejects(qmm_lib, case, expect):
+    w, x, y = _w(), _x(), _y()
+    if case == "null_w": w = None
+    elif case == "null_data": x.data = None
+    elif case == "w_f32": w = B.make_desc(B.F32, 2048, 64, 8192, W_ADDR)
+    elif case == "x_bf16": x = _x(B.BF16)
+    elif case == "y_f16": y = B.make_desc(B.F16, 64, 1, 128, Y_ADDR)
+    elif case == "k_mismatch": x = _x(K=1024)
+    elif case == "k_not_32": w = B.make_desc(B.Q4_0, 2040, 64, 1152, W_ADDR); x = _x(K=2040)
+    elif case == "n_over_8": x = _x(N=9); y = _y(N=9)
+    elif case == "y_rows": y = _y(M=63)
+    elif case == "y_tokens": y = _y(N=2)
+    elif case == "w_misaligned": w = _w(addr=W_ADDR + 8)
+    elif case == "pitch_small": w = _w(pitch=1136)
+    elif case == "pitch_unaligned": w = _w(pitch=1160)
+    elif case == "nb0_quant": w.nb[0] = 18
+    elif case == "nb0_dense": x.nb[0] = 8
+    elif case == "x_misaligned": x.data = X_ADDR + 2
+    elif case == "three_dims": w.n_dims = 3
+    elif case == "ne2": w.ne[2] = 2
+    elif case == "alias_y_w": y.data = W_ADDR + 1152 * 10
+    elif case == "alias_y_x": y.data = X_ADDR + 4 * 100
+    elif case == "too_large": w = _w(K=65536, M=4); x = _x(K=65536); y = _y(M=4)
+    elif case == "bad_type": w.type = 9
+    elif case == "neg_ne": w.ne[1] = -1
+    assert B.call_raw("qmm_gemv", w, x, y) == expect
+
+
+@no_gpu
+@pytest.mark.parametrize("case,expect", [
+    ("x_f32", B.ERR_TYPE), ("w_f16", B.ERR_TYPE), ("x_unaligned_pitch", B.ERR_LAYOUT),
+    ("x_misaligned", B.ERR_LAYOUT), ("alias", B.ERR_ALIAS), ("k_mismatch", B.ERR_SHAPE),
+])
+def test_gemm_rejects(qmm_lib, case, expect):
+    w, x, y = _w(), _x(B.BF16, N=512), _y(N=512)
+    if case == "x_f32": x = _x(B.F32, N=512)
+    elif case == "w_f16": w = B.make_desc(B.F16, 2048, 64, 4096, W_ADDR)
+    elif case == "x_unaligned_pitch": x.nb[1] = 2048 * 2 + 2
+    elif case == "x_misaligned": x.data = X_ADDR + 8
+    elif case == "alias": y.data = X_ADDR
+    elif case == "k_mismatch": x = _x(B.BF16, K=2080, N=512)
+    assert B.call_raw("qmm_gemm", w, x, y) == expect
+
+
+@no_gpu
+def test_quantize_and_dequantize_reject(qmm_lib):
+    src = B.make_desc(B.F32, 2048, 64, 8192, X_ADDR)
+    dst = _w()
+    assert B.call_raw("qmm_quantize", None, dst) == B.ERR_NULL
+    assert B.call_raw("qmm_quantize", src, B.make_desc(B.F16, 2048, 64, 4096, W_ADDR)) == B.ERR_TYPE
+    assert B.call_raw("qmm_quantize", B.make_desc(B.F32, 2048, 63, 8192, X_ADDR), dst) == B.ERR_SHAPE
+    assert B.call_raw("qmm_quantize", B.make_desc(B.F32, 2040, 64, 8192, X_ADDR),
+                      B.make_desc(B.Q4_0, 2040, 64, 1152, W_ADDR)) == B.ERR_SHAPE
+    assert B.call_raw("qmm_quantize", B.make_desc(B.F32, 2048, 64, 8192, W_ADDR + 64), dst) == B.ERR_ALIAS
+    assert B.call_raw("qmm_dequantize", dst, B.make_desc(B.F16, 2048, 64, 4096, Y_ADDR)) == B.ERR_TYPE
+    assert B.call_raw("qmm_dequantize", B.make_desc(B.F32, 2048, 64, 8192, X_ADDR),
+                      B.make_desc(B.F32, 2048, 64, 8192, Y_ADDR)) == B.ERR_TYPE
+
+
+@no_gpu
+def test_empty_operands_enqueue_nothing(qmm_lib):
+    # zero rows / zero tokens are valid and launch no kernel (so they are safe
+    # without a GPU); NULL data is allowed for empty tensors
+    assert B.call_raw("qmm_gemv", _w(M=0, addr=0), _x(), _y(M=0, addr=0)) == B.OK
+    assert B.call_raw("qmm_gemm", _w(), B.make_desc(B.BF16, 2048, 0, 4096, 0),
+                      B.make_desc(B.F32, 64, 0, 256, 0)) == B.OK
+    assert B.call_raw("qmm_quantize", B.make_desc(B.F32, 2048, 0, 8192, 0),
+                      B.make_desc(B.Q4_0, 2048, 0, 1152, 0)) == B.OK
