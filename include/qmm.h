@@ -128,13 +128,35 @@ QMM_API int qmm_dequantize(const qmm_tensor *src, qmm_tensor *dst_f32, void *str
  * token per step makes every projection a GEMV).
  * w: Q8_0, Q4_0 or F16, ne = [K, M];  x: F32 ne = [K, N], 1 <= N <= 8
  * (N > 8: QMM_ERR_SHAPE);  y: F32 ne = [M, N], must not overlap w or x.
- * Each lane keeps its slice of x in registers, which bounds the size: the
- * call returns QMM_ERR_UNSUPPORTED when K * N exceeds 32768 (Q4_0), 16384
- * (Q8_0) or 8192 (F16), counting N rounded up to 1, 2, 4 or 8.
+ * Each lane keeps its slice of x in registers, which bounds K: the call
+ * returns QMM_ERR_UNSUPPORTED when K exceeds 32768 (Q4_0, Q8_0) or 16384
+ * (F16).  Tokens are processed in groups that fit the registers (one pass
+ * over the weights per group).
  * Weights are read once from HBM and dequantized in registers; binary32
  * multiply-add; the accumulation order is unspecified (results agree with
  * the exact sum within 1e-4 * sum_k |W'[m][k] x[n][k]| + 1e-6). */
 QMM_API int qmm_gemv(const qmm_tensor *w, const qmm_tensor *x_f32, qmm_tensor *y_f32, void *stream);
+
+/* Most GEMVs one qmm_gemv_batch call takes. */
+#define QMM_GEMV_BATCH_MAX 8
+
+/* One GEMV of a batch: the operands of a qmm_gemv call. */
+typedef struct qmm_gemv_item {
+    const qmm_tensor *w;
+    const qmm_tensor *x_f32;
+    qmm_tensor *y_f32;
+} qmm_gemv_item;
+
+/* Several independent decode GEMVs in one launch ("A Complete Guide to
+ * llama.cpp ...", §2.1: at one token per step the Q, K and V projections are
+ * three GEMVs of the same input; "Development Guide ...", §4.4: so are the
+ * gate and up projections of the feed-forward block).  Each item follows the
+ * rules of qmm_gemv; all items must share the weight type, K and N, and no
+ * output may overlap any operand of any item.  1 <= count <=
+ * QMM_GEMV_BATCH_MAX (else QMM_ERR_SHAPE).  Equivalent to count qmm_gemv
+ * calls, without the fixed cost of count - 1 kernel launches; the workgroups
+ * of the launch are shared among the items in proportion to their rows. */
+QMM_API int qmm_gemv_batch(const qmm_gemv_item *items, int32_t count, void *stream);
 
 /* Prefill GEMM ("No Python! ...", §6: C_ij = sum_k A_ik B_kj, with many tokens
  * per step).  w: Q4_0 or Q8_0, ne = [K, M];  x: BF16 ne = [K, N], any N >= 0;

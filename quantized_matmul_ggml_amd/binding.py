@@ -25,8 +25,9 @@ TYPE_NAMES = {F32: "F32", F16: "F16", BF16: "BF16", Q8_0: "Q8_0", Q4_0: "Q4_0"}
 OK, ERR_NULL, ERR_TYPE, ERR_SHAPE, ERR_LAYOUT, ERR_ALIAS, ERR_UNSUPPORTED, ERR_DEVICE = \
     0, -1, -2, -3, -4, -5, -6, -7
 
-EXPORTS = ("qmm_row_size", "qmm_quantize", "qmm_dequantize", "qmm_gemv", "qmm_gemm",
-           "qmm_strerror")
+EXPORTS = ("qmm_row_size", "qmm_quantize", "qmm_dequantize", "qmm_gemv", "qmm_gemv_batch",
+           "qmm_gemm", "qmm_strerror")
+GEMV_BATCH_MAX = 8
 
 
 class QmmTensor(ctypes.Structure):
@@ -34,6 +35,12 @@ class QmmTensor(ctypes.Structure):
     _fields_ = [("type", ctypes.c_int32), ("n_dims", ctypes.c_int32),
                 ("ne", ctypes.c_int64 * 4), ("nb", ctypes.c_uint64 * 4),
                 ("data", ctypes.c_void_p)]
+
+
+class QmmGemvItem(ctypes.Structure):
+    """Mirror of ``qmm_gemv_item``."""
+    _fields_ = [("w", ctypes.POINTER(QmmTensor)), ("x_f32", ctypes.POINTER(QmmTensor)),
+                ("y_f32", ctypes.POINTER(QmmTensor))]
 
 
 class QmmError(RuntimeError):
@@ -61,6 +68,8 @@ def lib() -> ctypes.CDLL:
         h.qmm_dequantize.argtypes = [P, P, ctypes.c_void_p]
         h.qmm_gemv.argtypes = [P, P, P, ctypes.c_void_p]
         h.qmm_gemm.argtypes = [P, P, P, ctypes.c_void_p]
+        h.qmm_gemv_batch.argtypes = [ctypes.POINTER(QmmGemvItem), ctypes.c_int32, ctypes.c_void_p]
+        h.qmm_gemv_batch.restype = ctypes.c_int
         for f in ("qmm_quantize", "qmm_dequantize", "qmm_gemv", "qmm_gemm"):
             getattr(h, f).restype = ctypes.c_int
         h.qmm_strerror.argtypes = [ctypes.c_int]
@@ -123,8 +132,13 @@ def _need_gpu(*ts: torch.Tensor):
 
 def _dense_desc(t: torch.Tensor, type_: int) -> QmmTensor:
     """2-D row-major torch tensor (rows, cols) -> ne = [cols, rows]."""
-    assert t.dim() == 2 and t.stride(1) == 1
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
     es = t.element_size()
+    if t.numel() == 0:                  # empty: strides are meaningless
+        return make_desc(type_, t.shape[1], t.shape[0], t.shape[1] * es, t.data_ptr())
+    if t.stride(1) != 1:
+        raise ValueError("rows must be contiguous (stride 1 along the last dimension)")
     return make_desc(type_, t.shape[1], t.shape[0], t.stride(0) * es, t.data_ptr())
 
 
@@ -182,6 +196,23 @@ def gemv(w: Weight, x: torch.Tensor, *, out: torch.Tensor | None = None, stream=
     return out
 
 
+def gemv_batch(items, *, stream=None) -> list:
+    """Several GEMVs in one launch: items = [(Weight, x (N, K) f32, out or None), ...]
+    sharing the weight type, K and N.  Returns the outputs."""
+    descs, keep, outs = [], [], []
+    for w, x, out in items:
+        _need_gpu(w.data, x)
+        if out is None:
+            out = torch.empty((x.shape[0], w.M), dtype=torch.float32, device=x.device)
+        wd, xd, yd = w.desc(), _dense_desc(x, F32), _dense_desc(out, F32)
+        keep += [wd, xd, yd]
+        descs.append(QmmGemvItem(ctypes.pointer(wd), ctypes.pointer(xd), ctypes.pointer(yd)))
+        outs.append(out)
+    arr = (QmmGemvItem * max(1, len(descs)))(*descs)
+    _check(lib().qmm_gemv_batch(arr, len(descs), _stream(stream)), "qmm_gemv_batch")
+    return outs
+
+
 def gemm(w: Weight, x: torch.Tensor, *, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """y (N, M) fp32 = x (N, K) bf16 times W'^T on the bf16 matrix cores."""
     _need_gpu(w.data, x)
@@ -191,6 +222,14 @@ def gemm(w: Weight, x: torch.Tensor, *, out: torch.Tensor | None = None, stream=
     _check(lib().qmm_gemm(ctypes.byref(wd), ctypes.byref(xd), ctypes.byref(yd), _stream(stream)),
            "qmm_gemm")
     return out
+
+
+def call_batch_raw(triples, count=None, stream: int = 0) -> int:
+    """qmm_gemv_batch with hand-made descriptors [(w, x, y), ...]; returns the status."""
+    items = [QmmGemvItem(*(ctypes.pointer(d) if d is not None else None for d in t)) for t in triples]
+    arr = (QmmGemvItem * max(1, len(items)))(*items)
+    n = len(items) if count is None else count
+    return lib().qmm_gemv_batch(arr, n, ctypes.c_void_p(stream))
 
 
 def call_raw(name: str, *descs: QmmTensor, stream: int = 0) -> int:

@@ -35,37 +35,66 @@
 namespace qmm {
 namespace {
 
-constexpr int kThreads = 256;  // four wave64 per workgroup
+constexpr int kThreads = 256;         // four wave64 per workgroup
+constexpr int kMaxWorkgroups = 1024;  // persistent grid: 4 workgroups per CU
+constexpr int kMaxItems = QMM_GEMV_BATCH_MAX;
 
-template <int WT> struct Fmt;
-template <> struct Fmt<W_Q4_0> { static constexpr int wpc = 32; static constexpr float offset = 8.0f; };
-template <> struct Fmt<W_Q8_0> { static constexpr int wpc = 16; static constexpr float offset = 128.0f; };
-template <> struct Fmt<W_F16>  { static constexpr int wpc = 8;  static constexpr float offset = 0.0f; };
-
-struct GemvArgs {
+// One GEMV of a launch: its weights, activations and outputs.  All items of
+// a launch share the weight type, K and the token count.
+struct GemvItem {
     const uint8_t *w;
     uint64_t pitch;       // bytes between weight rows
     int64_t M;
-    int64_t K;
-    int64_t qoff;         // byte offset of the codes inside a row (0 for F16)
-    int64_t nchunk;       // 16-byte chunks of codes per row
     const float *x;
     uint64_t x_pitch;     // elements between token rows of x
-    int32_t N;            // real tokens (<= NT)
     float *y;
     uint64_t y_pitch;     // elements between token rows of y
     int64_t n_groups;     // row groups of U rows
+    int32_t wg_begin;     // first workgroup of this item
+    int32_t wg_count;     // workgroups of this item
 };
 
-// Weight index of element i (0..wpc-1) of chunk c, in the order the kernel
-// unpacks a chunk: Q4_0 low nibbles of the 16 bytes are elements 0..15 of the
-// block, high nibbles elements 16..31 (the packing order of the row layout).
+struct GemvArgs {
+    GemvItem item[kMaxItems];
+    int32_t n_items;
+    int32_t N;            // real tokens (<= NT)
+    int64_t K;
+    int64_t qoff;         // byte offset of the codes inside a row (0 for F16)
+    int64_t nchunk;       // 16-byte chunks of codes per row
+};
+
+// (a & m) | c in one VALU op (the compiler would split it: gfx9 VOP3 takes no
+// literal operands, so c has to sit in a register).
+__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t c)
+{
+    uint32_t d;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(c));
+    return d;
+}
+
+__device__ inline float lo_half(uint32_t p)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xFFFFu));
+}
+__device__ inline float hi_half(uint32_t p)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16));
+}
+
+// Per-format constants.  A chunk is 16 bytes of codes.  The chunk's dot
+// product is accumulated with biased codes (see chunk_dot) and the bias is
+// removed with a per-chunk term -offset * sum(x) computed once per lane.
+template <int WT> struct Fmt;
+template <> struct Fmt<W_Q4_0> { static constexpr int wpc = 32; static constexpr float offset = 24.0f; };
+template <> struct Fmt<W_Q8_0> { static constexpr int wpc = 16; static constexpr float offset = 128.0f; };
+template <> struct Fmt<W_F16>  { static constexpr int wpc = 8;  static constexpr float offset = 0.0f; };
+
+// Weight index (within the row) of element i of chunk c, in the order the
+// kernel keeps activations: natural k order.
 template <int WT>
 __device__ inline int64_t chunk_k(int64_t c, int i)
 {
-    if (WT == W_Q4_0) return c * 32 + i;
-    if (WT == W_Q8_0) return c * 16 + i;
-    return c * 8 + i;
+    return c * Fmt<WT>::wpc + i;
 }
 
 template <int WT>
@@ -74,21 +103,36 @@ __device__ inline int64_t chunk_block(int64_t c)
     return WT == W_Q4_0 ? c : c / 2;   // Q8_0: two chunks per 32-block
 }
 
-// sum_i code_i * x_i for one chunk, starting from the folded bias.
+// sum_i code_i * x_i over one chunk, starting from acc (the folded bias).
+//  Q4_0: byte j of a block holds element j (low nibble) and j+16 (high
+//        nibble).  A nibble n placed at bits 6..9 of a binary16 word with
+//        exponent field 19 (0x4C00) reads as 16 + n, so one shift and one
+//        and-or give two weights; v_fma_mix_f32 widens the half on the fly.
+//        The chunk sum is then sum (16 + n) x = sum (n - 8) x + 24 sum x.
+//  Q8_0: flipping the sign bit of each byte gives code + 128 as an unsigned
+//        byte, which v_cvt_f32_ubyte{0..3} widens exactly.
+//  F16:  the halves of each dword feed v_fma_mix_f32 directly.
 template <int WT>
-__device__ inline float chunk_dot(const uint4 q, const float *xv, float acc)
+__device__ inline float chunk_dot(const uint4 q, const float *xv, float acc, uint32_t magic)
 {
     const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
     if (WT == W_Q4_0) {
+        const uint32_t m = 0x03C003C0u;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            const uint32_t lo = wd[d] & 0x0F0F0F0Fu;
-            const uint32_t hi = (wd[d] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc = fmaf((float)((lo >> (8 * e)) & 0xFFu), xv[4 * d + e], acc);
-                acc = fmaf((float)((hi >> (8 * e)) & 0xFFu), xv[16 + 4 * d + e], acc);
-            }
+            const uint32_t w = wd[d];
+            const uint32_t p0 = and_or(w << 6, m, magic);   // elems 4d,      4d+2
+            const uint32_t p1 = and_or(w << 2, m, magic);   // elems 16+4d,   16+4d+2
+            const uint32_t p2 = and_or(w >> 2, m, magic);   // elems 4d+1,    4d+3
+            const uint32_t p3 = and_or(w >> 6, m, magic);   // elems 16+4d+1, 16+4d+3
+            acc = fmaf(lo_half(p0), xv[4 * d], acc);
+            acc = fmaf(hi_half(p0), xv[4 * d + 2], acc);
+            acc = fmaf(lo_half(p1), xv[16 + 4 * d], acc);
+            acc = fmaf(hi_half(p1), xv[16 + 4 * d + 2], acc);
+            acc = fmaf(lo_half(p2), xv[4 * d + 1], acc);
+            acc = fmaf(hi_half(p2), xv[4 * d + 3], acc);
+            acc = fmaf(lo_half(p3), xv[16 + 4 * d + 1], acc);
+            acc = fmaf(hi_half(p3), xv[16 + 4 * d + 3], acc);
         }
     } else if (WT == W_Q8_0) {
 #pragma unroll
@@ -101,55 +145,99 @@ __device__ inline float chunk_dot(const uint4 q, const float *xv, float acc)
     } else {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            const float h0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd[d] & 0xFFFFu));
-            const float h1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd[d] >> 16));
-            acc = fmaf(h0, xv[2 * d], acc);
-            acc = fmaf(h1, xv[2 * d + 1], acc);
+            acc = fmaf(lo_half(wd[d]), xv[2 * d], acc);
+            acc = fmaf(hi_half(wd[d]), xv[2 * d + 1], acc);
         }
     }
     return acc;
 }
 
-// Transposed butterfly over the 64 lanes of a wave.  On entry every lane holds
-// V partial values; on exit lane L holds the full wave sum of value
-// L >> (6 - log2 V) (and so do the 64/V - 1 lanes that follow it).
-template <int V>
+// Value of the lane whose index differs from this lane's in bit B (a
+// butterfly partner): DPP quad permutations for bits 0 and 1, ds_swizzle
+// (xor mode, within 32 lanes) for bits 2..4, ds_bpermute for bit 5.
+template <int B>
+__device__ inline float partner(float v)
+{
+    const int iv = __builtin_bit_cast(int, v);
+    if constexpr (B == 0) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true));
+    } else if constexpr (B == 1) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true));
+    } else if constexpr (B <= 4) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(iv, 0x1F | ((1 << B) << 10)));
+    } else {
+        return __shfl_xor(v, 32, 64);
+    }
+}
+
+// Transposed butterfly over the 64 lanes of a wave.  Every lane enters with
+// V partial values; each exchange on lane bit B (from bit 0 up) halves the
+// set a lane carries, then the single remaining value is all-reduced over
+// the higher bits.  On exit every lane holds the full wave sum of value
+// value_index<V>(lane), so lanes 0 .. V-1 together hold all V sums.
+template <int V, int B>
 struct WaveReduce {
-    static __device__ inline float run(const float *v, int lane, int mask)
+    static __device__ inline float run(const float *v, int lane)
     {
         constexpr int H = V / 2;
-        const bool upper = (lane & mask) != 0;
+        const bool upper = ((lane >> B) & 1) != 0;
         float keep[H];
 #pragma unroll
         for (int i = 0; i < H; ++i) {
             const float send = upper ? v[i] : v[i + H];
             const float mine = upper ? v[i + H] : v[i];
-            keep[i] = mine + __shfl_xor(send, mask, 64);
+            keep[i] = mine + partner<B>(send);
         }
-        return WaveReduce<H>::run(keep, lane, mask >> 1);
+        return WaveReduce<H, B + 1>::run(keep, lane);
     }
 };
-template <>
-struct WaveReduce<1> {
-    static __device__ inline float run(const float *v, int, int mask)
+template <int B>
+struct WaveReduce<1, B> {
+    static __device__ inline float run(const float *v, int)
     {
         float s = v[0];
-        for (int m = mask; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
+        if constexpr (B <= 0) s += partner<0>(s);
+        if constexpr (B <= 1) s += partner<1>(s);
+        if constexpr (B <= 2) s += partner<2>(s);
+        if constexpr (B <= 3) s += partner<3>(s);
+        if constexpr (B <= 4) s += partner<4>(s);
+        s += partner<5>(s);
         return s;
     }
 };
 
+// Index of the value a lane holds after WaveReduce<V, 0>: the halving on bit
+// b picks the upper half of the remaining indices, so lane bit b is index
+// bit log2(V) - 1 - b.
+template <int V>
+__device__ inline int value_index(int lane)
+{
+    int idx = 0;
+#pragma unroll
+    for (int b = 0; (1 << b) < V; ++b) idx = (idx << 1) | ((lane >> b) & 1);
+    return idx;
+}
+
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 constexpr int pow2_ceil(int v) { return v <= 1 ? 1 : 2 * pow2_ceil((v + 1) / 2); }
+
+// LDS image of one round of activation chunks: lane-local chunk c holds its
+// wpc floats at c * (wpc + 4); the 16-byte pad per chunk spreads the
+// lane-strided 128-bit reads of the lanes over all banks.
+template <int WT>
+__host__ __device__ constexpr int lds_chunk_stride() { return Fmt<WT>::wpc + 4; }
 
 template <int WT, int NT, int KS, int CPL, int U>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
 {
     constexpr int WPC = Fmt<WT>::wpc;
+    constexpr int SC = lds_chunk_stride<WT>();
     constexpr int G = 4 / KS;                 // wave groups per workgroup
     constexpr int VL = 64 * KS;               // lanes per wave group
     constexpr int V = pow2_ceil(U * NT);      // values per lane to reduce
     static_assert(V <= 64, "too many partial sums per lane");
+    extern __shared__ __attribute__((aligned(16))) float xs[];
+    __shared__ float red[2][4][64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -157,36 +245,29 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
     const int grp = wave / KS;
     const int ks = wave % KS;
     const int v = ks * 64 + lane;
+    const int nt_real = a.N < NT ? a.N : NT;
 
-    // ---- activations for this lane's chunks, and the folded code offset ----
-    float xr[NT][CPL][WPC];
-    float xb[NT][CPL];
+    // ---- which item this workgroup serves (uniform scalar search) ----
+    int item = 0;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const int64_t c = v + (int64_t)j * VL;
-        const bool ok = c < a.nchunk;
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            float s = 0.0f;
-            const bool tok = ok && n < a.N;
-            const float *xn = a.x + (uint64_t)n * a.x_pitch;
-#pragma unroll
-            for (int i = 0; i < WPC; ++i) {
-                const int64_t k = chunk_k<WT>(c, i);
-                const float val = (tok && k < a.K) ? xn[k] : 0.0f;
-                xr[n][j][i] = val;
-                s += val;
-            }
-            xb[n][j] = -Fmt<WT>::offset * s;
-        }
-    }
+    for (int i = 1; i < kMaxItems; ++i)
+        if (i < a.n_items && (int)blockIdx.x >= a.item[i].wg_begin) item = i;
+    const uint8_t *const W = a.item[item].w;
+    const uint64_t pitch = a.item[item].pitch;
+    const int64_t M = a.item[item].M;
+    const float *const X = a.item[item].x;
+    const uint64_t x_pitch = a.item[item].x_pitch;
+    float *const Y = a.item[item].y;
+    const uint64_t y_pitch = a.item[item].y_pitch;
+    const int64_t n_groups = a.item[item].n_groups;
+    const int64_t wg = (int64_t)blockIdx.x - a.item[item].wg_begin;
+    const int64_t n_wg = a.item[item].wg_count;
 
-    __shared__ float red[2][4][64];
-
-    // ---- row loop: every wave of the workgroup runs the same trip count ----
-    const int64_t iters = (a.n_groups + (int64_t)G * gridDim.x - 1) / ((int64_t)G * gridDim.x);
-    int64_t g = (int64_t)blockIdx.x * G + grp;
-    const int64_t gstep = (int64_t)gridDim.x * G;
+    // ---- row loop bookkeeping: every wave of the workgroup runs the same
+    // trip count (the KS > 1 reduction uses workgroup barriers) ----
+    const int64_t iters = (n_groups + (int64_t)G * n_wg - 1) / ((int64_t)G * n_wg);
+    int64_t g = wg * G + grp;
+    const int64_t gstep = n_wg * G;
 
     uint4 q[U][CPL];
     uint16_t sc[U][CPL];
@@ -194,8 +275,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             int64_t r = grp_idx * U + u;
-            r = r < a.M ? r : a.M - 1;          // tail rows re-read the last row
-            const uint8_t *row = a.w + (uint64_t)r * a.pitch;
+            r = r < M ? r : M - 1;              // tail rows re-read the last row
+            const uint8_t *row = W + (uint64_t)r * pitch;
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 const int64_t c = v + (int64_t)j * VL;
@@ -220,7 +301,56 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
         }
     };
 
-    if (iters > 0) load_group(g < a.n_groups ? g : a.n_groups - 1);
+    // First weight loads go out before the activations are staged, so the
+    // two memory latencies overlap.
+    if (iters > 0) load_group(g < n_groups ? g : n_groups - 1);
+
+    // ---- activations for this lane's chunks, staged through LDS one (token,
+    // chunk round) at a time with coalesced global reads; the folded code
+    // offset -offset * sum(x) per chunk ----
+    float xr[NT][CPL][WPC];
+    float xb[NT][CPL];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            if (n < nt_real) {                       // uniform over the workgroup
+                const int64_t k0 = (int64_t)j * VL * WPC;
+                const float *xn = X + (uint64_t)n * x_pitch;
+                for (int e = tid; e < VL * WPC; e += kThreads) {
+                    const int64_t k = k0 + e;
+                    const int cl = e / WPC;
+                    xs[cl * SC + (e - cl * WPC)] = k < a.K ? xn[k] : 0.0f;
+                }
+                __syncthreads();
+                const int64_t c = v + (int64_t)j * VL;
+                if (c < a.nchunk) {
+                    const float4 *src = reinterpret_cast<const float4 *>(&xs[v * SC]);
+#pragma unroll
+                    for (int i = 0; i < WPC / 4; ++i) {
+                        const float4 t = src[i];
+                        xr[n][j][4 * i] = t.x;
+                        xr[n][j][4 * i + 1] = t.y;
+                        xr[n][j][4 * i + 2] = t.z;
+                        xr[n][j][4 * i + 3] = t.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < WPC; ++i) xr[n][j][i] = 0.0f;
+                }
+                __syncthreads();
+            } else {
+#pragma unroll
+                for (int i = 0; i < WPC; ++i) xr[n][j][i] = 0.0f;
+            }
+            float s = 0.0f;
+#pragma unroll
+            for (int i = 0; i < WPC; ++i) s += xr[n][j][i];
+            xb[n][j] = -Fmt<WT>::offset * s;
+        }
+    }
+    const uint32_t magic = 0x4C004C00u;   // binary16 exponent field of 16.0 in both halves
+
     for (int64_t it = 0; it < iters; ++it, g += gstep) {
         uint4 qc[U][CPL];
         uint16_t scc[U][CPL];
@@ -230,7 +360,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
             for (int j = 0; j < CPL; ++j) { qc[u][j] = q[u][j]; scc[u][j] = sc[u][j]; }
         if (it + 1 < iters) {
             const int64_t gn = g + gstep;
-            load_group(gn < a.n_groups ? gn : a.n_groups - 1);
+            load_group(gn < n_groups ? gn : n_groups - 1);
         }
 
         float part[V];
@@ -245,25 +375,24 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
                                     : (float)__builtin_bit_cast(_Float16, scc[u][j]);
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
-                    const float s = chunk_dot<WT>(qc[u][j], xr[n][j], xb[n][j]);
+                    const float s = chunk_dot<WT>(qc[u][j], xr[n][j], xb[n][j], magic);
                     part[u * NT + n] = fmaf(d, s, part[u * NT + n]);
                 }
             }
         }
-        const float tot = WaveReduce<V>::run(part, lane, 32);
-        const int idx = lane >> (6 - ilog2(V));
-        const bool owner = (lane & ((64 / V) - 1)) == 0;
-        const bool in_range = g < a.n_groups;
+        const float tot = WaveReduce<V, 0>::run(part, lane);
+        const int idx = value_index<V>(lane);
+        const bool in_range = g < n_groups;
 
         if (KS == 1) {
-            if (owner && idx < U * NT && in_range) {
+            if (lane < V && idx < U * NT && in_range) {
                 const int u = idx / NT, n = idx % NT;
                 const int64_t r = g * U + u;
-                if (r < a.M && n < a.N) a.y[(uint64_t)n * a.y_pitch + r] = tot;
+                if (r < M && n < a.N) Y[(uint64_t)n * y_pitch + r] = tot;
             }
         } else {
             float *buf = red[it & 1][wave];
-            if (owner) buf[idx] = tot;
+            if (lane < V) buf[idx] = tot;
             __syncthreads();
             if (ks == 0 && lane < U * NT && in_range) {
                 float s = 0.0f;
@@ -271,7 +400,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
                 for (int w2 = 0; w2 < KS; ++w2) s += red[it & 1][grp * KS + w2][lane];
                 const int u = lane / NT, n = lane % NT;
                 const int64_t r = g * U + u;
-                if (r < a.M && n < a.N) a.y[(uint64_t)n * a.y_pitch + r] = s;
+                if (r < M && n < a.N) Y[(uint64_t)n * y_pitch + r] = s;
             }
         }
     }
@@ -382,12 +511,12 @@ bool gemv_config(int type, int64_t K, int64_t M, int64_t N, GemvConfig *cfg)
     }
     if (c.ks == 0) return false;
     // ... widened while the rows alone cannot fill 256 CUs with 8 waves each,
-    // as long as at least half of the added lanes get a chunk.
+    // as long as no more than a quarter of the lanes is left without a chunk.
     while (c.ks < 4) {
         const int64_t waves = ((M + c.u - 1) / c.u) * c.ks;
         const int nks = c.ks * 2;
         const int64_t need = (nchunk + 64 * nks - 1) / (64 * nks);
-        if (waves >= 2048 || need * 64 * nks > 2 * nchunk) break;
+        if (waves >= 2048 || 3 * need * 64 * nks > 4 * nchunk) break;
         const int cp = round_cpl(need);
         if (cp == 0 || cp * wpc * c.nt > 128) break;
         c.ks = nks;
@@ -399,32 +528,76 @@ bool gemv_config(int type, int64_t K, int64_t M, int64_t N, GemvConfig *cfg)
     return true;
 }
 
+hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t stream)
+{
+    if (count < 1 || count > kMaxItems) return hipErrorInvalidValue;
+    const int type = tasks[0].w.type;
+    const int64_t K = tasks[0].w.K;
+    const int64_t N = tasks[0].x.N;
+    int64_t m_total = 0;
+    for (int i = 0; i < count; ++i) m_total += tasks[i].w.M;
+    if (m_total == 0 || N == 0) return hipSuccess;
+
+    // Tokens are processed in chunks of at most 8; a chunk shrinks (halving)
+    // until a register-resident configuration exists for it.
+    for (int64_t n0 = 0; n0 < N;) {
+        int64_t nb = N - n0 < 8 ? N - n0 : 8;
+        GemvConfig c;
+        while (!gemv_config(type, K, m_total, nb, &c)) {
+            if (nb == 1) return hipErrorInvalidValue;
+            nb = nb > 4 ? 4 : nb > 2 ? 2 : 1;
+        }
+        const Kernel k = pick(type, c);
+        const int groups_per_wg = 4 / c.ks;
+        GemvArgs a;
+        a.n_items = 0;
+        a.N = (int32_t)nb;
+        a.K = K;
+        a.qoff = (type == W_F16) ? 0 : quant_offset(K);
+        a.nchunk = chunks_per_row(type, K);
+        int64_t need_total = 0;
+        int64_t need[kMaxItems];
+        for (int i = 0; i < count; ++i) {
+            const int64_t groups = (tasks[i].w.M + c.u - 1) / c.u;
+            need[i] = (groups + groups_per_wg - 1) / groups_per_wg;
+            need_total += need[i];
+        }
+        int32_t wg_next = 0;
+        for (int i = 0; i < count; ++i) {
+            if (tasks[i].w.M == 0) continue;
+            int64_t wgs = need[i];
+            if (need_total > kMaxWorkgroups) {
+                wgs = need[i] * kMaxWorkgroups / need_total;   // share of the persistent grid
+                if (wgs < 1) wgs = 1;
+            }
+            GemvItem &it = a.item[a.n_items++];
+            it.w = tasks[i].w.base;
+            it.pitch = tasks[i].w.pitch;
+            it.M = tasks[i].w.M;
+            it.x = static_cast<const float *>(tasks[i].x.data) + (uint64_t)n0 * tasks[i].x.pitch_elems;
+            it.x_pitch = tasks[i].x.pitch_elems;
+            it.y = tasks[i].y.data + (uint64_t)n0 * tasks[i].y.pitch_elems;
+            it.y_pitch = tasks[i].y.pitch_elems;
+            it.n_groups = (tasks[i].w.M + c.u - 1) / c.u;
+            it.wg_begin = wg_next;
+            it.wg_count = (int32_t)wgs;
+            wg_next += (int32_t)wgs;
+        }
+        const int wpc = weights_per_chunk(type);
+        const size_t lds = (size_t)64 * c.ks * (wpc + 4) * sizeof(float);
+        hipLaunchKernelGGL(k, dim3((unsigned)wg_next), dim3(kThreads), lds, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        n0 += nb;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_gemv(const WeightView &w, const ActView &x, const OutView &y,
                        hipStream_t stream)
 {
-    if (w.M == 0 || x.N == 0) return hipSuccess;
-    GemvConfig c;
-    if (!gemv_config(w.type, w.K, w.M, x.N, &c)) return hipErrorInvalidValue;
-    Kernel k = pick(w.type, c);
-
-    GemvArgs a;
-    a.w = w.base;
-    a.pitch = w.pitch;
-    a.M = w.M;
-    a.K = w.K;
-    a.qoff = (w.type == W_F16) ? 0 : quant_offset(w.K);
-    a.nchunk = chunks_per_row(w.type, w.K);
-    a.x = static_cast<const float *>(x.data);
-    a.x_pitch = x.pitch_elems;
-    a.N = (int32_t)x.N;
-    a.y = y.data;
-    a.y_pitch = y.pitch_elems;
-    a.n_groups = (w.M + c.u - 1) / c.u;
-    const int groups_per_wg = 4 / c.ks;
-    int64_t wgs = (a.n_groups + groups_per_wg - 1) / groups_per_wg;
-    if (wgs > 2048) wgs = 2048;
-    hipLaunchKernelGGL(k, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
-    return hipGetLastError();
+    const GemvTask t{w, x, y};
+    return launch_gemv_batch(&t, 1, stream);
 }
 
 }  // namespace qmm

@@ -172,12 +172,49 @@ int qmm_gemv(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *stre
     if (x->ne[1] > 8) return QMM_ERR_SHAPE;
     if (x->ne[1] == 0 || w->ne[1] == 0) return QMM_OK;
     // The activation slice of every lane lives in registers (at most 128
-    // floats per lane), which bounds K * N.
+    // floats per lane), which bounds K; tokens are split into chunks that fit.
     qmm::GemvConfig cfg;
-    if (!qmm::gemv_config(w->type, w->ne[0], w->ne[1], x->ne[1], &cfg)) return QMM_ERR_UNSUPPORTED;
+    if (!qmm::gemv_config(w->type, w->ne[0], w->ne[1], 1, &cfg)) return QMM_ERR_UNSUPPORTED;
     qmm::ActView xv{x->data, pitch_elems(x), x->ne[1]};
     qmm::OutView yv{static_cast<float *>(y->data), pitch_elems(y)};
     return status_of(qmm::launch_gemv(weight_view(w), xv, yv, static_cast<hipStream_t>(stream)));
+}
+
+int qmm_gemv_batch(const qmm_gemv_item *items, int32_t count, void *stream)
+{
+    if (!items) return QMM_ERR_NULL;
+    if (count < 1 || count > QMM_GEMV_BATCH_MAX) return QMM_ERR_SHAPE;
+    qmm::GemvTask tasks[QMM_GEMV_BATCH_MAX];
+    for (int i = 0; i < count; ++i) {           // every item on its own first
+        const qmm_tensor *w = items[i].w, *x = items[i].x_f32, *y = items[i].y_f32;
+        int rc = check_mul_mat(w, x, y, QMM_TYPE_F32, 4);
+        if (rc) return rc;
+        if (!(is_quant(w->type) || w->type == QMM_TYPE_F16)) return QMM_ERR_TYPE;
+        if (x->ne[1] > 8) return QMM_ERR_SHAPE;
+        if (i > 0) {
+            const qmm_tensor *w0 = items[0].w, *x0 = items[0].x_f32;
+            if (w->type != w0->type) return QMM_ERR_TYPE;
+            if (w->ne[0] != w0->ne[0] || x->ne[1] != x0->ne[1]) return QMM_ERR_SHAPE;
+        }
+    }
+    for (int i = 0; i < count; ++i) {           // then outputs against every operand
+        const qmm_tensor *w = items[i].w, *x = items[i].x_f32, *y = items[i].y_f32;
+        for (int j = 0; j < count; ++j) {
+            if (j == i) continue;
+            if (overlaps(y, items[j].w) || overlaps(y, items[j].x_f32) || overlaps(y, items[j].y_f32))
+                return QMM_ERR_ALIAS;
+        }
+        tasks[i].w = weight_view(w);
+        tasks[i].x = qmm::ActView{x->data, pitch_elems(x), x->ne[1]};
+        tasks[i].y = qmm::OutView{static_cast<float *>(y->data), pitch_elems(y)};
+    }
+    int64_t m_total = 0;
+    for (int i = 0; i < count; ++i) m_total += items[i].w->ne[1];
+    if (m_total == 0 || items[0].x_f32->ne[1] == 0) return QMM_OK;
+    qmm::GemvConfig cfg;
+    if (!qmm::gemv_config(items[0].w->type, items[0].w->ne[0], m_total, 1, &cfg))
+        return QMM_ERR_UNSUPPORTED;
+    return status_of(qmm::launch_gemv_batch(tasks, count, static_cast<hipStream_t>(stream)));
 }
 
 int qmm_gemm(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *stream)

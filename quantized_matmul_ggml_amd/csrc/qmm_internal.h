@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include "../../include/qmm.h"
 #include <stddef.h>
 #include <stdint.h>
 
@@ -58,6 +60,15 @@ hipError_t launch_dequantize(const uint8_t *src, uint64_t src_pitch, int64_t K, 
                              int type, float *dst, uint64_t dst_pitch_elems, hipStream_t stream);
 hipError_t launch_gemv(const WeightView &w, const ActView &x, const OutView &y,
                        hipStream_t stream);
+
+// Several GEMVs (same weight type, K and token count) in one launch; each
+// workgroup serves one of them.  count <= QMM_GEMV_BATCH_MAX.
+struct GemvTask {
+    WeightView w;
+    ActView x;
+    OutView y;
+};
+hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t stream);
 hipError_t launch_gemm(const WeightView &w, const ActView &x, const OutView &y,
                        hipStream_t stream);
 

@@ -156,6 +156,28 @@ def test_quantize_and_dequantize_reject(qmm_lib):
 
 
 @no_gpu
+def test_gemv_batch_rejects(qmm_lib):
+    item = lambda **kw: (_w(**{k: v for k, v in kw.items() if k in ("type_", "K", "M", "addr")}), _x(K=kw.get("K", 2048), addr=kw.get("xaddr", X_ADDR)), _y(M=kw.get("M", 64), addr=kw.get("yaddr", Y_ADDR)))
+    a = item()
+    b = item(addr=W_ADDR + (1 << 28), xaddr=X_ADDR + (1 << 28), yaddr=Y_ADDR + (1 << 28))
+    assert B.call_batch_raw([a, b], count=0) == B.ERR_SHAPE
+    assert B.call_batch_raw([a] * 9) == B.ERR_SHAPE
+    assert B.call_batch_raw([a, (b[0], None, b[2])]) == B.ERR_NULL
+    c = (B.make_desc(B.Q8_0, 2048, 64, 2176, W_ADDR + (1 << 28)), b[1], b[2])
+    assert B.call_batch_raw([a, c]) == B.ERR_TYPE                     # mixed weight types
+    d = (B.make_desc(B.Q4_0, 1024, 64, 576, W_ADDR + (1 << 28)), _x(K=1024, addr=b[1].data), b[2])
+    assert B.call_batch_raw([a, d]) == B.ERR_SHAPE                    # mixed K
+    e = (b[0], _x(N=2, addr=b[1].data), _y(N=2, addr=b[2].data))
+    assert B.call_batch_raw([a, e]) == B.ERR_SHAPE                    # mixed N
+    f = (b[0], b[1], _y(addr=a[1].data))                              # output over another item's x
+    assert B.call_batch_raw([a, f]) == B.ERR_ALIAS
+    g = (b[0], b[1], _y(addr=Y_ADDR + 16))                            # two outputs overlap
+    assert B.call_batch_raw([a, g]) == B.ERR_ALIAS
+    h = (b[0], _x(K=2048, addr=b[1].data), _y(M=63, addr=b[2].data))
+    assert B.call_batch_raw([a, h]) == B.ERR_SHAPE
+
+
+@no_gpu
 def test_empty_operands_enqueue_nothing(qmm_lib):
     # zero rows / zero tokens are valid and launch no kernel (so they are safe
     # without a GPU); NULL data is allowed for empty tensors

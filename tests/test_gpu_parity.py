@@ -60,7 +60,7 @@ def _assert_tol(y, yref, a, rel, abs_, what):
 def _oracle_weight(orc, tname, w32):
     """Oracle-side packed rows (or fp16 rows as bytes) of fp32 weights."""
     if tname == "F16":
-        return WL.round_f16(w32).view(np.uint8).reshape(w32.shape[0], -1)
+        return WL.round_f16(w32).view(np.uint8).reshape(w32.shape[0], 2 * w32.shape[1])
     return orc.quantize(TYPES[tname][1], w32)
 
 
@@ -381,3 +381,67 @@ def test_gemm_deterministic_and_token_columns(orc):
     for n in (0, 129, 199):
         yn = Q.gemm(wt, xt[n:n + 1]).cpu().numpy()
         assert np.array_equal(yn[0].view(np.uint32), y1[n].view(np.uint32))
+
+
+# ---------------------------------------------------------------- GEMV batch
+
+def test_gemv_batch_decoder_layer(orc):
+    """The K = 2048 projections of a layer (Q, K, V, O, gate, up, each with its
+    own input as the layer workload gives them) in one batched launch, and
+    the down projection alone; every output checked against the oracle."""
+    _banner("gemv batch: one decoder layer")
+    xs = [WL.activations(WL.seed(3, 7 + s), 1, k) for s, k in enumerate(WL.LAYER_X_K)]
+    xt = [torch.from_numpy(x).to(DEV) for x in xs]
+    items, refs = [], []
+    for t, (name, M, K, slot) in enumerate(WL.LAYER):
+        w = WL.weights(WL.seed(3, t, 5), M, K)
+        packed = orc.quantize(orc.Q4_0, w)
+        refs.append(orc.mul_mat(orc.Q4_0, packed, K, xs[slot]))
+        items.append((B.Weight(torch.from_numpy(packed).to(DEV), B.Q4_0, K, M), xt[slot], None))
+    outs = Q.gemv_batch(items[:6]) + Q.gemv_batch(items[6:])
+    for (name, *_), y, (yref, a) in zip(WL.LAYER, outs, refs):
+        _assert_tol(y.cpu().numpy(), yref, a, 1e-4, 1e-6, f"batch {name}")
+
+
+@pytest.mark.parametrize("tname", ["Q8_0", "Q4_0", "F16"])
+def test_gemv_batch_ragged_items(orc, tname):
+    """Items of 1, 0, 300 and 4100 rows sharing one x, N = 5 (split into
+    token chunks), outputs in guard-banded buffers."""
+    K, N = 2048, 5
+    _banner(f"gemv batch ragged {tname}")
+    x = WL.activations(31, N, K)
+    xt = torch.from_numpy(x).to(DEV)
+    items, refs, bufs = [], [], []
+    for i, M in enumerate((1, 0, 300, 4100)):
+        w = WL.weights(40 + i, M, K)
+        packed = _oracle_weight(orc, tname, w)
+        refs.append(orc.mul_mat(TYPES[tname][1], packed, K, x) if M else None)
+        buf, yv = _guarded_out(N, M)
+        bufs.append(buf)
+        items.append((_gpu_weight(tname, w), xt, yv))
+    outs = Q.gemv_batch(items)
+    torch.cuda.synchronize()
+    for buf in bufs:
+        _check_guard(buf)
+    for y, ref in zip(outs, refs):
+        if ref is not None:
+            _assert_tol(y.cpu().numpy(), ref[0], ref[1], 1e-4, 1e-6, f"ragged {tname}")
+
+
+def test_gemv_batch_matches_single_calls(orc):
+    """A batch of eight equals eight single calls within the bar (same kernel,
+    possibly a different share of the grid)."""
+    K = 2048
+    _banner("gemv batch of eight vs single calls")
+    items, singles = [], []
+    for i in range(8):
+        w = WL.weights(60 + i, 256 + 100 * i, K)
+        x = torch.from_numpy(WL.activations(70 + i, 2, K)).to(DEV)
+        wt = _gpu_weight("Q4_0", w)
+        items.append((wt, x, None))
+        singles.append(Q.gemv(wt, x).cpu().numpy())
+    outs = Q.gemv_batch(items)
+    for i, (y, y1) in enumerate(zip(outs, singles)):
+        w = WL.weights(60 + i, 256 + 100 * i, K)
+        _, a = orc.mul_mat(orc.Q4_0, orc.quantize(orc.Q4_0, w), K, WL.activations(70 + i, 2, K))
+        assert np.all(np.abs(y.cpu().numpy() - y1) <= 2e-4 * a + 2e-6)
