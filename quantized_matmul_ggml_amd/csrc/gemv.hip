@@ -154,7 +154,8 @@ __device__ inline float chunk_dot(const uint4 q, const float *xv, float acc, uin
 
 // Value of the lane whose index differs from this lane's in bit B (a
 // butterfly partner): DPP quad permutations for bits 0 and 1, ds_swizzle
-// (xor mode, within 32 lanes) for bits 2..4, ds_bpermute for bit 5.
+// (xor mode, within 32 lanes) for bits 2..4, ds_bpermute for bit 5.  The
+// last all-reduce stage uses lower_half_to_upper() instead (see WaveReduce).
 template <int B>
 __device__ inline float partner(float v)
 {
@@ -173,8 +174,9 @@ __device__ inline float partner(float v)
 // Transposed butterfly over the 64 lanes of a wave.  Every lane enters with
 // V partial values; each exchange on lane bit B (from bit 0 up) halves the
 // set a lane carries, then the single remaining value is all-reduced over
-// the higher bits.  On exit every lane holds the full wave sum of value
-// value_index<V>(lane), so lanes 0 .. V-1 together hold all V sums.
+// the higher bits.  On exit every lane of the upper half (lanes 32..63)
+// holds the full wave sum of value value_index<V>(lane), so lanes
+// 32 .. 32+V-1 together hold all V sums.
 template <int V, int B>
 struct WaveReduce {
     static __device__ inline float run(const float *v, int lane)
@@ -191,6 +193,14 @@ struct WaveReduce {
         return WaveReduce<H, B + 1>::run(keep, lane);
     }
 };
+// v_permlane32_swap: lanes 32..63 receive the values of lanes 0..31 (a
+// VALU exchange, no LDS crossbar).
+__device__ inline float lower_half_to_upper(float v)
+{
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    return __builtin_bit_cast(float, __builtin_amdgcn_permlane32_swap(u, u, false, false)[0]);
+}
+
 template <int B>
 struct WaveReduce<1, B> {
     static __device__ inline float run(const float *v, int)
@@ -201,7 +211,7 @@ struct WaveReduce<1, B> {
         if constexpr (B <= 2) s += partner<2>(s);
         if constexpr (B <= 3) s += partner<3>(s);
         if constexpr (B <= 4) s += partner<4>(s);
-        s += partner<5>(s);
+        s += lower_half_to_upper(s);      // complete in lanes 32..63 only
         return s;
     }
 };
@@ -301,8 +311,19 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
         }
     };
 
-    // First weight loads go out before the activations are staged, so the
-    // two memory latencies overlap.
+    // The first staging round's activations are loaded before the first
+    // weight loads are issued: staging then waits only for them (they come
+    // from L2) while the weights stream in.
+    constexpr int PER = VL * WPC / kThreads;    // activations per thread per round
+    float x0[PER];
+    {
+        const bool on = nt_real > 0;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int64_t k = tid + i * kThreads;
+            x0[i] = (on && k < a.K) ? X[k] : 0.0f;
+        }
+    }
     if (iters > 0) load_group(g < n_groups ? g : n_groups - 1);
 
     // ---- activations for this lane's chunks, staged through LDS one (token,
@@ -317,10 +338,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
             if (n < nt_real) {                       // uniform over the workgroup
                 const int64_t k0 = (int64_t)j * VL * WPC;
                 const float *xn = X + (uint64_t)n * x_pitch;
-                for (int e = tid; e < VL * WPC; e += kThreads) {
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const int e = tid + i * kThreads;
                     const int64_t k = k0 + e;
                     const int cl = e / WPC;
-                    xs[cl * SC + (e - cl * WPC)] = k < a.K ? xn[k] : 0.0f;
+                    xs[cl * SC + (e - cl * WPC)] = (n == 0 && j == 0) ? x0[i] : (k < a.K ? xn[k] : 0.0f);
                 }
                 __syncthreads();
                 const int64_t c = v + (int64_t)j * VL;
@@ -384,15 +407,16 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
         const int idx = value_index<V>(lane);
         const bool in_range = g < n_groups;
 
+        const bool owner = lane >= 32 && lane < 32 + V;
         if (KS == 1) {
-            if (lane < V && idx < U * NT && in_range) {
+            if (owner && idx < U * NT && in_range) {
                 const int u = idx / NT, n = idx % NT;
                 const int64_t r = g * U + u;
                 if (r < M && n < a.N) Y[(uint64_t)n * y_pitch + r] = tot;
             }
         } else {
             float *buf = red[it & 1][wave];
-            if (lane < V) buf[idx] = tot;
+            if (owner) buf[idx] = tot;
             __syncthreads();
             if (ks == 0 && lane < U * NT && in_range) {
                 float s = 0.0f;
@@ -537,6 +561,9 @@ hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t strea
     int64_t m_total = 0;
     for (int i = 0; i < count; ++i) m_total += tasks[i].w.M;
     if (m_total == 0 || N == 0) return hipSuccess;
+    // The matrix-core kernel's cost does not grow with the token count; it is
+    // the faster one from 5 tokens up (measured), the VALU kernel below that.
+    if (N >= 5 && gemv_mfma_supported(type, K, N)) return launch_gemv_mfma(tasks, count, stream);
 
     // Tokens are processed in chunks of at most 8; a chunk shrinks (halving)
     // until a register-resident configuration exists for it.

@@ -69,6 +69,11 @@ struct GemvTask {
     OutView y;
 };
 hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t stream);
+
+// The matrix-core GEMV for Q4_0 / Q8_0 weights (gemv_mfma.hip): whether its
+// LDS image of the activations fits for (K, N), and its launcher.
+bool gemv_mfma_supported(int type, int64_t K, int64_t N);
+hipError_t launch_gemv_mfma(const GemvTask *tasks, int count, hipStream_t stream);
 hipError_t launch_gemm(const WeightView &w, const ActView &x, const OutView &y,
                        hipStream_t stream);
 
