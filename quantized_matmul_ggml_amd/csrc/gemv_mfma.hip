@@ -409,6 +409,9 @@ int dynamic_lds_limit()
 
 // Raise a kernel's dynamic-LDS limit once (the attribute persists for the
 // process); later launches, including those recorded into graphs, reuse it.
+
+}  // namespace
+
 hipError_t allow_dynamic_lds(const void *fn, int bytes)
 {
     static std::mutex mu;
@@ -425,8 +428,6 @@ hipError_t allow_dynamic_lds(const void *fn, int bytes)
     if (n < 64) { fns[n] = fn; granted[n] = bytes; ++n; }
     return hipSuccess;
 }
-
-}  // namespace
 
 bool gemv_mfma_supported(int type, int64_t K, int64_t N)
 {

@@ -225,6 +225,7 @@ int qmm_gemm(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *stre
     qmm::ActView xv{x->data, pitch_elems(x), x->ne[1]};
     qmm::OutView yv{static_cast<float *>(y->data), pitch_elems(y)};
     if (w->ne[1] == 0 || x->ne[1] == 0) return QMM_OK;
+    if (!qmm::gemm_supported(weight_view(w), xv)) return QMM_ERR_UNSUPPORTED;
     return status_of(qmm::launch_gemm(weight_view(w), xv, yv, static_cast<hipStream_t>(stream)));
 }
 

@@ -74,6 +74,12 @@ hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t strea
 // LDS image of the activations fits for (K, N), and its launcher.
 bool gemv_mfma_supported(int type, int64_t K, int64_t N);
 hipError_t launch_gemv_mfma(const GemvTask *tasks, int count, hipStream_t stream);
+// Grant a kernel more than the default dynamic LDS (once per size).
+hipError_t allow_dynamic_lds(const void *fn, int bytes);
+
+// The prefill GEMM (gemm.hip): whether the operand strides fit its 32-bit
+// per-tile offsets, and its launcher.
+bool gemm_supported(const WeightView &w, const ActView &x);
 hipError_t launch_gemm(const WeightView &w, const ActView &x, const OutView &y,
                        hipStream_t stream);
 

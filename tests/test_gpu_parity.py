@@ -342,6 +342,30 @@ def test_gemm_parity(orc, case):
     _assert_tol(y, ydiag, a, 1.1 * K * 2.0 ** -24, 1e-7, f"gemm bf16-weight diagnostic {case}")
 
 
+@pytest.mark.parametrize("tname", ["Q4_0", "Q8_0"])
+def test_gemm_strided_operands(orc, tname):
+    """Padded weight pitch (padding filled with 0xFF bytes, which as scales or
+    codes would poison the result if read), x rows with a larger pitch, y rows
+    with a larger pitch; K/32 odd so the last K-step is half empty."""
+    M, K, N = 150, 2048 + 32, 140
+    _banner(f"gemm strided {tname}")
+    w = WL.weights(31, M, K)
+    xbits = WL.round_bf16_bits(WL.activations(32, N, K))
+    packed = orc.quantize(TYPES[tname][1], w)
+    yref, a = orc.mul_mat(TYPES[tname][1], packed, K, xbits, x_bf16_bits=True)
+    rs = packed.shape[1]
+    padded = np.full((M, rs + 80), 0xFF, np.uint8)
+    padded[:, :rs] = packed
+    wt = B.Weight(torch.from_numpy(padded).to(DEV), TYPES[tname][0], K, M)
+    xfull = torch.full((N, K + 24), -3.0e38, dtype=torch.bfloat16, device=DEV)
+    xfull[:, :K] = WL.bf16_bits_to_torch(xbits, DEV)
+    buf, yv = _guarded_out(N, M, pad_cols=5)
+    Q.gemm(wt, xfull[:, :K], out=yv)
+    torch.cuda.synchronize()
+    _check_guard(buf, pad_cols=5)
+    _assert_tol(yv.cpu().numpy(), yref, a, 1e-2, 1e-5, f"gemm strided {tname}")
+
+
 def test_gemm_prefill_full_size_sampled(orc):
     """The 5632 x 2048 Q4_0 weight times 512 bf16 tokens, checked on 4096
     sampled outputs plus every output of the first and last 128 x 128 tiles."""
