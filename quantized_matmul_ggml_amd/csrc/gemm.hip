@@ -6,24 +6,27 @@
 // data, and feed the multiply-add units).  On gfx950 the multiply-add units are
 // the bf16 matrix cores: each weight tile is dequantized once per workgroup
 // (Development Guide for Small AI Models (TinyLLaMA, etc.) Using C++, §6.2:
-// unpack, multiply by the block scale) into LDS as bf16, the activation tile
-// is copied to LDS, and v_mfma_f32_32x32x16_bf16 accumulates in fp32.
+// unpack, multiply by the block scale) into LDS as bf16, and
+// v_mfma_f32_32x32x16_bf16 accumulates in fp32.
 //
 // The workgroup is split by role.  Of its eight waves, four (one per SIMD)
-// only read LDS and issue matrix-core instructions; the other four (again one
-// per SIMD) only load from memory, dequantize and write LDS.  Each SIMD thus
-// holds one wave of each kind, so the dequantization arithmetic of one wave
-// issues while the other wave's matrix instructions run.  The producers keep
-// DEPTH steps of global loads in flight in registers, and LDS holds a ring of
-// three K-steps: while the consumers work on step t (and read the first
-// fragments of step t+1), the producers fill step t+2.  One barrier per step.
+// load the weight and token tiles, dequantize the weights and write both into
+// a four-stage LDS ring, two K-steps ahead of use; the other four (again one per SIMD) read operand
+// fragments from LDS and issue the matrix instructions.  Each SIMD thus holds
+// one wave of each kind, so the dequantization arithmetic of one issues while
+// the matrix instructions of the other run.
 //
 // Tile: 128 weight rows x 128 tokens, K advancing 64 (two 32-blocks) per step;
 // each consumer wave owns 64 x 64 of the output (2 x 2 MFMA tiles of 32 x 32).
 // Tokens sit on the MFMA row side so that each lane's results run along the
-// contiguous m dimension of Y.  Loads go through buffer resources based at
-// the tile's first row, so rows and tokens past the end read as zero.
+// contiguous m dimension of Y.
+//
+// Loads go through buffer resources based at the tile's first row and sized
+// to the bytes the operands span, so rows and tokens past the end read as
+// zero; blocks past the end of K get a zero scale and zero tokens.
 #include "qmm_internal.h"
+
+#include <type_traits>
 
 namespace qmm {
 namespace {
@@ -31,16 +34,23 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 128;                   // weight rows per tile
 constexpr int BN = 128;                   // tokens per tile
 constexpr int BK = 64;                    // K per step (two 32-blocks)
 constexpr int LDS_STRIDE = BK + 8;        // bf16 elements per LDS row (+16 B pad)
 constexpr int OPERAND_ELEMS = 128 * LDS_STRIDE;
-constexpr int STAGES = 3;
-constexpr int DEPTH = 4;                  // K-steps of global loads in flight
+constexpr int STAGE_ELEMS = 2 * OPERAND_ELEMS;   // weights, then tokens
+constexpr int STAGES = 4;
+constexpr int X_DEPTH = 4;                // K-steps of token loads in flight
+static_assert(X_DEPTH == STAGES, "the consumer loop unrolls over both with one index");
+constexpr int SCALE_GROUP_STEPS = 8;      // steps whose scales are staged together
+constexpr int SCALE_GROUP_BLOCKS = 2 * SCALE_GROUP_STEPS;
 constexpr int THREADS = 512;
 constexpr int BUFFER_FLAGS = 0x00020000;  // raw buffer, 32-bit data format
+constexpr uint32_t OUT_OF_RANGE = 0x80000000u;   // above every buffer size
 
 struct GemmArgs {
     const uint8_t *w;
@@ -53,13 +63,8 @@ struct GemmArgs {
     int64_t N;
     float *y;
     uint64_t y_pitch;
-    int m_tiles;
     int n_tiles;
-    int xcd_chunk;          // tiles per XCD when the tile count divides by 8, else 0
 };
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Round two floats to bf16 (nearest even) in one v_cvt_pk_bf16_f32.
 __device__ inline uint32_t pack_bf16(float lo, float hi)
@@ -81,21 +86,19 @@ __device__ inline float ubyte(uint32_t w)
     return r;
 }
 
-// One producer lane's share of a K-step: one 32-block of one weight row
-// (codes and scale) and 32 activations of one token.
+// One producer lane's share of a K-step: one 32-block of one weight row.
 template <int WT>
-struct Stage {
+struct WBlock {
     static constexpr int QV = (WT == W_Q4_0) ? 1 : 2;
     u32x4 q[QV];
     uint16_t s;
-    u32x4 x[4];
 };
 
 // Dequantize one 32-block to 32 bf16 values in k order, two per dword.
 // (code - offset) * d is exact in fp32 (at most 19 significant bits), so each
 // value is the bf16 rounding of the exact product.
 template <int WT>
-__device__ inline void dequant_block(const Stage<WT> &st, uint32_t out[16])
+__device__ inline void dequant_block(const WBlock<WT> &st, uint32_t out[16])
 {
     const float d = (float)__builtin_bit_cast(_Float16, st.s);
     if constexpr (WT == W_Q4_0) {
@@ -120,21 +123,43 @@ __device__ inline void dequant_block(const Stage<WT> &st, uint32_t out[16])
     }
 }
 
+// Calls f(std::integral_constant<int, 0>{}) .. f(std::integral_constant<int, N-1>{}).
+template <int N, int I = 0, class F>
+__device__ inline void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
+// The fp16 scale of a producer lane's block of step S of a scale group:
+// block 2S + h of the group, which lane S / 2 of the lane's quad (the four
+// lanes sharing a pair of rows) holds in dword S % 2 of row use0 ? 0 : 1,
+// half h.  The quad broadcast is a DPP move.
+template <int S>
+__device__ inline uint16_t group_scale(const uint32_t (&sreg)[2][2], bool use0, int h)
+{
+    constexpr int ctrl = (S / 2) * 0x55;     // quad_perm [S/2, S/2, S/2, S/2]
+    const uint32_t v0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)sreg[0][S % 2], ctrl, 0xF, 0xF, false);
+    const uint32_t v1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)sreg[1][S % 2], ctrl, 0xF, 0xF, false);
+    return (uint16_t)((use0 ? v0 : v1) >> (16 * h));
+}
+
 template <int WT>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
 {
     constexpr int QB = (WT == W_Q4_0) ? 16 : 32;     // code bytes per block
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-    // stage s: weights at lds + s * 2 * OPERAND_ELEMS, tokens right after
+    // STAGES x [weights BM x LDS_STRIDE | tokens BN x LDS_STRIDE] bf16
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    int tile = blockIdx.x;
-    if (a.xcd_chunk) tile = (tile % 8) * a.xcd_chunk + tile / 8;
     // the division runs on the vector unit; the tile is uniform, so move it
     // back to scalar registers (buffer resources must live there)
+    const int tile = blockIdx.x;
     const int mt = __builtin_amdgcn_readfirstlane(tile / a.n_tiles);
     const int nt = __builtin_amdgcn_readfirstlane(tile - mt * a.n_tiles);
     const int64_t m0 = (int64_t)mt * BM;
@@ -142,87 +167,168 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
     const int64_t nblk = a.K / 32;
     const int steps = (int)((a.K + BK - 1) / BK);
 
+    // Step p of K sits in LDS stage p % STAGES and is complete at barrier p.
+    // It is written between barriers p-2 and p-1 (weights by the producers,
+    // tokens by the consumers), two steps ahead of its use: between barriers
+    // t and t+1 the consumers read step t into registers and multiply step
+    // t-1.  The stage written then, that of step t-2, was read in window t-2
+    // and those reads were consumed by the matrix instructions of window
+    // t-1.  A wave's wait before barrier t+1 leaves its LDS operations of
+    // window t in flight and only requires those of window t-1 to have
+    // landed.
+    //
+    // Every global load covers whole row segments with several lanes per
+    // row, so that one instruction touches few cache lines: the vector L1
+    // serves about one line per two cycles whatever part of it is used.
+
     if (wave >= 4) {
-        // ---------------- producers ----------------
-        const int p = tid - 256;
-        const int prow = p >> 1;           // weight row / token of this lane
-        const int phalf = p & 1;           // which 32-block of the step
+        // ---------------- producers: weights ----------------
+        //  * codes: 4 lanes per row covering two steps (four blocks), 16 rows
+        //    per load; of the two loads a lane makes per pair of steps, one
+        //    holds a block of the first step and one of the second (the
+        //    16-byte chunk order is rotated between them);
+        //  * scales: 4 lanes per row pair covering eight steps, handed to the
+        //    lane that needs each one with a quad broadcast.
+        const int pw = wave - 4;
+        const int q4 = lane & 3;
         const int64_t rows = a.M - m0 < BM ? a.M - m0 : BM;
-        const int64_t toks = a.N - n0 < BN ? a.N - n0 : BN;
-        // Buffer sizes are the bytes the operands really span, so an offset
-        // past them reads zeros without touching memory.  All offsets go in
-        // the VGPR operand, which the range check covers.
         const uint32_t row_bytes = (uint32_t)(a.qoff + (WT == W_Q4_0 ? a.K / 2 : a.K));
         const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(a.w + (uint64_t)m0 * a.pitch), 0,
             (int)(uint32_t)((rows - 1) * a.pitch + row_bytes), BUFFER_FLAGS);
-        const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(a.x + (uint64_t)n0 * a.x_pitch), 0,
-            (int)(uint32_t)(((toks - 1) * a.x_pitch + a.K) * 2), BUFFER_FLAGS);
-        constexpr uint32_t OUT_OF_RANGE = 0x80000000u;   // above every buffer size
-        const uint32_t qoff = (uint32_t)(prow * a.pitch + a.qoff) + phalf * QB;
-        const uint32_t soff = (uint32_t)(prow * a.pitch) + phalf * 2;
-        const uint32_t xoff = (uint32_t)(prow * a.x_pitch * 2) + phalf * 64;
 
-        Stage<WT> ring[DEPTH];
-        // Blocks past the end of K (the second block of the last step when
-        // K/32 is odd) are loaded from an out-of-range offset and so are zero:
-        // zero scale, zero activations.
-        auto load = [&](Stage<WT> &st, int t) {
-            const bool in_k = 2 * t + phalf < nblk;
-            const uint32_t oq = in_k ? qoff + (uint32_t)t * (2 * QB) : OUT_OF_RANGE;
-            const uint32_t os = in_k ? soff + (uint32_t)t * 4 : OUT_OF_RANGE;
-            const uint32_t ox = in_k ? xoff + (uint32_t)t * 128 : OUT_OF_RANGE;
+        // code load i of a pair covers rows 32 pw + 2 m + i (m = lane / 4)
+        // with chunk (q4 + 2 i) % 4 of the pair's four blocks
+        const int wrow0 = 32 * pw + 2 * (lane >> 2);
+        uint32_t qoff[2];
 #pragma unroll
-            for (int v = 0; v < Stage<WT>::QV; ++v)
-                st.q[v] = __builtin_amdgcn_raw_buffer_load_b128(wres, oq + 16 * v, 0, 0);
-            st.s = __builtin_amdgcn_raw_buffer_load_b16(wres, os, 0, 0);
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                st.x[v] = __builtin_amdgcn_raw_buffer_load_b128(xres, ox + 16 * v, 0, 0);
-        };
-        auto store = [&](const Stage<WT> &st, int t) {
-            uint32_t deq[16];
-            dequant_block<WT>(st, deq);
-            uint16_t *ws = lds + (t % STAGES) * 2 * OPERAND_ELEMS;
-            u32x4 *wdst = reinterpret_cast<u32x4 *>(ws + prow * LDS_STRIDE + 32 * phalf);
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-                wdst[v] = u32x4{deq[4 * v], deq[4 * v + 1], deq[4 * v + 2], deq[4 * v + 3]};
-            u32x4 *xdst = reinterpret_cast<u32x4 *>(ws + OPERAND_ELEMS + prow * LDS_STRIDE + 32 * phalf);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) xdst[v] = st.x[v];
-        };
+        for (int i = 0; i < 2; ++i)
+            qoff[i] = (uint32_t)((wrow0 + i) * a.pitch + a.qoff) + ((q4 + 2 * i) & 3) * QB;
+        // step s of a pair uses load i_s = (q4 / 2 == s) ? 0 : 1; within its
+        // step the block is half h = q4 % 2
+        const int h = q4 & 1;
+        const bool first_is_0 = (q4 >> 1) == 0;
+        // scale load i covers rows wrow0 + i, blocks 4 q4 .. 4 q4 + 3 of a group
+        const uint32_t soff[2] = {(uint32_t)(wrow0 * a.pitch) + 8 * q4,
+                                  (uint32_t)((wrow0 + 1) * a.pitch) + 8 * q4};
+        uint16_t *wdst0 = lds + wrow0 * LDS_STRIDE + 32 * h;
 
-        // Loads are unconditional (those past the last step read zeros) so
-        // that the number in flight is the same on every path and each wait
-        // is for one step's loads only.  Step p lives in ring slot p % DEPTH
-        // and LDS stage p % STAGES; producing step p (p >= 1) ends with the
-        // barrier that releases step p - 1 to the consumers.
+        struct WPair { u32x4 q[2][WBlock<WT>::QV]; };
+        WPair wr[2];
+        uint32_t sreg[2][2], snext[2][2];   // [row wrow0 + i][dword] of a scale group
+
+        auto load_w = [&](WPair &wp, int pair) {
 #pragma unroll
-        for (int j = 0; j < DEPTH; ++j) load(ring[j], j);
-        for (int p0 = 0; p0 < steps; p0 += DEPTH) {
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int u = 0; u < DEPTH; ++u) {
-                const int p = p0 + u;
-                if (p < steps) store(ring[u], p);
-                load(ring[u], p + DEPTH);
-                if (p >= 1 && p < steps) __syncthreads();
+                for (int v = 0; v < WBlock<WT>::QV; ++v)
+                    wp.q[i][v] = __builtin_amdgcn_raw_buffer_load_b128(
+                        wres, qoff[i] + (uint32_t)pair * (4 * QB) + 16 * v, 0, 0);
+        };
+        auto load_scales = [&](uint32_t (&dst)[2][2], int group) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b64(
+                    wres, soff[i] + (uint32_t)group * (2 * SCALE_GROUP_BLOCKS), 0, 0);
+                dst[i][0] = v[0];
+                dst[i][1] = v[1];
             }
+        };
+        auto produce = [&](auto S_, int p, const WPair &wp) {
+            constexpr int S = decltype(S_)::value;   // p % SCALE_GROUP_STEPS
+            const bool use0 = ((S & 1) == 0) == first_is_0;
+            const int blk = 2 * p + h;
+            WBlock<WT> b;
+#pragma unroll
+            for (int v = 0; v < WBlock<WT>::QV; ++v) b.q[v] = use0 ? wp.q[0][v] : wp.q[1][v];
+            const uint16_t s16 = group_scale<S>(sreg, use0, h);
+            b.s = blk < nblk ? s16 : (uint16_t)0;   // past K: zero scale (the codes may be anything)
+            uint32_t deq[16];
+            dequant_block<WT>(b, deq);
+            u32x4 *dst = reinterpret_cast<u32x4 *>(wdst0 + (p % STAGES) * STAGE_ELEMS + (use0 ? 0 : LDS_STRIDE));
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                dst[v] = u32x4{deq[4 * v], deq[4 * v + 1], deq[4 * v + 2], deq[4 * v + 3]};
+        };
+
+        // Loads are unconditional (those past the end read zeros or unused
+        // bytes) so that the number in flight is the same on every path; the
+        // scheduling fences keep the initial loads in slot order, which the
+        // wait counts inside the loop rely on.
+        load_scales(sreg, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            load_w(wr[j], j);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // the consumers' last two barriers
-        __syncthreads();
-        __syncthreads();
+        // Step p: code pair slot (p / 2) % 2, scale group p / SCALE_GROUP_STEPS
+        // (loaded at its group's first step one group ahead).  Iteration p
+        // writes step p and ends with barrier p - 1, before which only this
+        // iteration's four LDS writes may still be in flight.
+        for (int p0 = 0; p0 < steps; p0 += SCALE_GROUP_STEPS) {
+            static_for<SCALE_GROUP_STEPS>([&](auto U) {
+                constexpr int u = decltype(U)::value;
+                const int p = p0 + u;
+                if (u == 0) load_scales(snext, p / SCALE_GROUP_STEPS + 1);
+                if (p < steps) produce(U, p, wr[(u / 2) % 2]);
+                if (u % 2 == 1) load_w(wr[(u / 2) % 2], p / 2 + 2);
+                if (u == SCALE_GROUP_STEPS - 1) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        sreg[i][0] = snext[i][0];
+                        sreg[i][1] = snext[i][1];
+                    }
+                }
+                if (p >= 1 && p < steps) asm volatile("s_waitcnt lgkmcnt(4)\n\ts_barrier" ::: "memory");
+            });
+        }
+        if (steps > 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // barrier steps - 1
         return;
     }
 
-    // ---------------- consumers ----------------
-    const int wm = wave & 1;     // weight-row half of the tile
-    const int wn = wave >> 1;    // token half of the tile
-    const int frow = lane & 31;         // row of the MFMA operand this lane feeds
-    const int fk = (lane >> 5) * 8;     // its 8-element k group
-    const int a_off = OPERAND_ELEMS + (wn * 64 + frow) * LDS_STRIDE + fk;
-    const int b_off = (wm * 64 + frow) * LDS_STRIDE + fk;
+    // ---------------- consumers: tokens + matrix cores ----------------
+    const int c = wave;
+    const int wm = c & 1;        // weight-row half of the tile
+    const int wn = c >> 1;       // token half of the tile
+
+    // Token staging: wave c loads rows 32 c .. 32 c + 31 of the token tile,
+    // 8 lanes per row (a step's 128 bytes), 8 rows per load.
+    const int q8 = lane & 7;
+    const int64_t toks = a.N - n0 < BN ? a.N - n0 : BN;
+    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.x + (uint64_t)n0 * a.x_pitch), 0,
+        (int)(uint32_t)(((toks - 1) * a.x_pitch + a.K) * 2), BUFFER_FLAGS);
+    const int xrow = 32 * c + (lane >> 3);
+    const uint32_t xoff = (uint32_t)(xrow * a.x_pitch * 2) + 16 * q8;
+    const uint32_t xrow_step = (uint32_t)(8 * a.x_pitch * 2);
+    const int64_t xlim = a.K - 8 * q8;     // chunk q8 of step t is in K iff 64 t < xlim
+    uint16_t *xdst0 = lds + OPERAND_ELEMS + xrow * LDS_STRIDE + 8 * q8;
+    struct XStep { u32x4 v[4]; };
+    XStep xr[X_DEPTH];
+    auto load_x = [&](XStep &xs, int t) {
+        const bool in_k = (int64_t)64 * t < xlim;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            xs.v[i] = __builtin_amdgcn_raw_buffer_load_b128(
+                xres, in_k ? xoff + i * xrow_step + (uint32_t)t * 128 : OUT_OF_RANGE, 0, 0);
+    };
+    auto store_x = [&](const XStep &xs, int t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<u32x4 *>(xdst0 + (t % STAGES) * STAGE_ELEMS + i * 8 * LDS_STRIDE) = xs.v[i];
+    };
+
+    // Fragments: lane (frow, fk) feeds MFMA row frow, k group fk of each
+    // 16-deep k chunk.
+    const int frow = lane & 31;
+    const int fk = (lane >> 5) * 8;
+    const int a_off = OPERAND_ELEMS + (wn * 64 + frow) * LDS_STRIDE + fk;   // tokens
+    const int b_off = (wm * 64 + frow) * LDS_STRIDE + fk;                   // weights
+    auto frag = [&](int stage, int off, int i, int kk) {
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
+            lds + stage * STAGE_ELEMS + off + i * 32 * LDS_STRIDE + kk * 16));
+    };
 
     f32x16 acc[2][2];
 #pragma unroll
@@ -232,37 +338,87 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    auto read_frags = [&](int stage, int kk, bf16x8 af[2], bf16x8 bf[2]) {
-        const uint16_t *base = lds + stage * 2 * OPERAND_ELEMS + kk * 16;
+    // One set of fragment registers: each is refilled with the next step's
+    // fragment right after the last matrix instruction that uses it, so reads
+    // and matrix instructions alternate (a burst of reads would fill the LDS
+    // command queue and stall the in-order issue of the matrix instructions
+    // behind it) and every read has a whole step to land.
+    bf16x8 fa[BK / 16][2], fb[BK / 16][2];
+    auto read_all = [&](int stage) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            af[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(base + a_off + i * 32 * LDS_STRIDE));
-            bf[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(base + b_off + i * 32 * LDS_STRIDE));
-        }
+        for (int kk = 0; kk < BK / 16; ++kk)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                fa[kk][i] = frag(stage, a_off, i, kk);
+                fb[kk][i] = frag(stage, b_off, i, kk);
+            }
     };
-
-    __syncthreads();
-    bf16x8 af[2][2], bf[2][2];          // [parity of kk][sub-tile]
-    if (steps > 0) read_frags(0, 0, af[0], bf[0]);
-    int stage = 0;
-    for (int t = 0; t < steps; ++t) {
-        const int next = stage + 1 == STAGES ? 0 : stage + 1;
+    auto mma = [&](int kk, int i, int j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j], acc[i][j], 0, 0, 0);
+    };
+    auto mma_and_read = [&](int stage) {
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
-            const int cur = kk & 1;
-            if (kk + 1 < BK / 16)
-                read_frags(stage, kk + 1, af[cur ^ 1], bf[cur ^ 1]);
-            else if (t + 1 < steps)
-                read_frags(next, 0, af[cur ^ 1], bf[cur ^ 1]);
+            mma(kk, 0, 0);
+            mma(kk, 0, 1);
+            fa[kk][0] = frag(stage, a_off, 0, kk);
+            mma(kk, 1, 0);
+            fb[kk][0] = frag(stage, b_off, 0, kk);
+            mma(kk, 1, 1);
+            fa[kk][1] = frag(stage, a_off, 1, kk);
+            fb[kk][1] = frag(stage, b_off, 1, kk);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two matrix instructions
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+    };
+    auto mma_all = [&]() {
+#pragma unroll
+        for (int kk = 0; kk < BK / 16; ++kk)
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bf[cur][j], acc[i][j], 0, 0, 0);
-        }
-        stage = next;
-        __syncthreads();
+                for (int j = 0; j < 2; ++j) mma(kk, i, j);
+    };
+
+    // Tokens of step s are stored in window s-2 from ring slot s % X_DEPTH,
+    // which is then refilled with step s + X_DEPTH; steps 0 and 1 are stored
+    // before barrier 0.  (The scheduling fences keep the initial loads in
+    // slot order.)
+#pragma unroll
+    for (int j = 0; j < X_DEPTH; ++j) {
+        load_x(xr[j], j);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    // (unconditional, like the loop's loads, so that the wait counts at the
+    // loop head see one history; with no steps nothing reads the stages)
+    store_x(xr[0], 0);
+    load_x(xr[0], X_DEPTH);
+    store_x(xr[1], 1);
+    load_x(xr[1], X_DEPTH + 1);
+    if (steps > 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // barrier 0
+    store_x(xr[2], 2);
+    load_x(xr[2], X_DEPTH + 2);
+    read_all(0);
+    // Window t >= 1: store the tokens of step t+2, read step t, multiply step
+    // t-1.  Before barrier t the stores of window t-2 (tokens of step t) must
+    // have landed; the twenty LDS operations of window t-1 may not.
+    for (int t0 = 1; t0 < steps; t0 += X_DEPTH) {
+        static_for<X_DEPTH>([&](auto U) {
+            constexpr int u = decltype(U)::value;
+            const int t = t0 + u;                 // t0 % X_DEPTH == 1
+            if (t < steps) {
+                asm volatile("s_waitcnt lgkmcnt(15)\n\ts_barrier" ::: "memory");
+                store_x(xr[(u + 3) % X_DEPTH], t + 2);
+                load_x(xr[(u + 3) % X_DEPTH], t + 2 + X_DEPTH);
+                mma_and_read((u + 1) % STAGES);
+            }
+        });
+    }
+    if (steps > 0) mma_all();
 
     // Epilogue: acc[i][j] register r holds token 8*(r/4) + 4*(lane/32) + r%4
     // of sub-tile i and weight row lane%32 of sub-tile j.
@@ -281,7 +437,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
     }
 }
 
-constexpr size_t LDS_BYTES = (size_t)STAGES * 2 * OPERAND_ELEMS * sizeof(uint16_t);
+constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_ELEMS * sizeof(uint16_t);
 
 template <int WT>
 hipError_t launch_typed(const GemmArgs &a, unsigned tiles, hipStream_t stream)
@@ -315,13 +471,8 @@ hipError_t launch_gemm(const WeightView &w, const ActView &x, const OutView &y,
     a.N = x.N;
     a.y = y.data;
     a.y_pitch = y.pitch_elems;
-    a.m_tiles = (int)((w.M + BM - 1) / BM);
     a.n_tiles = (int)((x.N + BN - 1) / BN);
-    const unsigned tiles = (unsigned)a.m_tiles * (unsigned)a.n_tiles;
-    // Consecutive tiles share a weight row band; handing each XCD (which
-    // receives every eighth workgroup) a contiguous run keeps a band's
-    // weights in one L2.
-    a.xcd_chunk = tiles % 8 == 0 ? (int)(tiles / 8) : 0;
+    const unsigned tiles = (unsigned)((w.M + BM - 1) / BM) * (unsigned)a.n_tiles;
     if (w.type == W_Q4_0) return launch_typed<W_Q4_0>(a, tiles, stream);
     if (w.type == W_Q8_0) return launch_typed<W_Q8_0>(a, tiles, stream);
     return hipErrorInvalidValue;
