@@ -48,6 +48,8 @@ constexpr int X_DEPTH = 4;                // K-steps of token loads in flight
 static_assert(X_DEPTH == STAGES, "the consumer loop unrolls over both with one index");
 constexpr int SCALE_GROUP_STEPS = 8;      // steps whose scales are staged together
 constexpr int SCALE_GROUP_BLOCKS = 2 * SCALE_GROUP_STEPS;
+constexpr int W_PAIRS = 4;                // pairs of K-steps of weight codes in flight
+static_assert(2 * W_PAIRS == SCALE_GROUP_STEPS, "the producer loop unrolls over both with one index");
 constexpr int THREADS = 512;
 constexpr int BUFFER_FLAGS = 0x00020000;  // raw buffer, 32-bit data format
 constexpr uint32_t OUT_OF_RANGE = 0x80000000u;   // above every buffer size
@@ -214,7 +216,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
         uint16_t *wdst0 = lds + wrow0 * LDS_STRIDE + 32 * h;
 
         struct WPair { u32x4 q[2][WBlock<WT>::QV]; };
-        WPair wr[2];
+        WPair wr[W_PAIRS];
         uint32_t sreg[2][2], snext[2][2];   // [row wrow0 + i][dword] of a scale group
 
         auto load_w = [&](WPair &wp, int pair) {
@@ -258,11 +260,11 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
         load_scales(sreg, 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < W_PAIRS; ++j) {
             load_w(wr[j], j);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // Step p: code pair slot (p / 2) % 2, scale group p / SCALE_GROUP_STEPS
+        // Step p: code pair slot (p / 2) % W_PAIRS, scale group p / SCALE_GROUP_STEPS
         // (loaded at its group's first step one group ahead).  Iteration p
         // writes step p and ends with barrier p - 1, before which only this
         // iteration's four LDS writes may still be in flight.
@@ -271,8 +273,8 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
                 constexpr int u = decltype(U)::value;
                 const int p = p0 + u;
                 if (u == 0) load_scales(snext, p / SCALE_GROUP_STEPS + 1);
-                if (p < steps) produce(U, p, wr[(u / 2) % 2]);
-                if (u % 2 == 1) load_w(wr[(u / 2) % 2], p / 2 + 2);
+                if (p < steps) produce(U, p, wr[(u / 2) % W_PAIRS]);
+                if (u % 2 == 1) load_w(wr[(u / 2) % W_PAIRS], p / 2 + W_PAIRS);
                 if (u == SCALE_GROUP_STEPS - 1) {
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {

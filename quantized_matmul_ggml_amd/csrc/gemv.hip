@@ -520,20 +520,33 @@ bool gemv_config(int type, int64_t K, int64_t M, int64_t N, GemvConfig *cfg)
     c.nt = N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : 8;
     const int wpc = weights_per_chunk(type);
     const int64_t nchunk = chunks_per_row(type, K);
-    // Short matrices stream one row per wave group so that more waves run.
-    const int u_wide = c.nt <= 1 ? 4 : (c.nt == 2 ? 2 : 1);
-    c.u = (M < 4096) ? 1 : u_wide;
     c.cpl = 0;
-    // Smallest wave group whose activation slice fits in registers ...
     c.ks = 0;
+    // One chunk per lane when a wave group of up to four waves covers the
+    // row: the activation slice, and the rounds that stage it through LDS,
+    // are then smallest (measured faster for long rows, e.g. K = 5632) ...
     for (int ks : {1, 2, 4}) {
-        const int cp = round_cpl((nchunk + 64 * ks - 1) / (64 * ks));
-        if (cp == 0 || cp * wpc * c.nt > 128) continue;
-        c.ks = ks;
-        c.cpl = cp;
-        break;
+        if (nchunk <= 64 * ks && wpc * c.nt <= 128) {
+            c.ks = ks;
+            c.cpl = 1;
+            break;
+        }
+    }
+    // ... otherwise the smallest wave group whose slice fits in registers.
+    if (c.ks == 0) {
+        for (int ks : {1, 2, 4}) {
+            const int cp = round_cpl((nchunk + 64 * ks - 1) / (64 * ks));
+            if (cp == 0 || cp * wpc * c.nt > 128) continue;
+            c.ks = ks;
+            c.cpl = cp;
+            break;
+        }
     }
     if (c.ks == 0) return false;
+    // Short matrices stream one row per wave group so that more waves run,
+    // unless the row already takes several waves.
+    const int u_wide = c.nt <= 1 ? 4 : (c.nt == 2 ? 2 : 1);
+    c.u = (M < 4096 && c.ks == 1) ? 1 : u_wide;
     // ... widened while the rows alone cannot fill 256 CUs with 8 waves each,
     // as long as no more than a quarter of the lanes is left without a chunk.
     while (c.ks < 4) {
