@@ -31,6 +31,11 @@ import time
 METRIC = "quantized mul_mat GB/s (decode GEMV) & TFLOP/s (prefill), % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
+HERE = os.path.dirname(os.path.abspath(__file__))
+# HBM traffic of the dominant kernel, from hardware counters (see traffic_probe)
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "gemv_q4_0_gate_up_hbm_traffic.md")
+GEMV_SOURCE = os.path.join(HERE, "quantized_matmul_ggml_amd", "csrc", "gemv.hip")
+COPY_PROBE_BYTES = 256 << 20   # calibration copy: 256 MiB read + 256 MiB written
 
 
 def log(msg):
@@ -46,6 +51,9 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip prefill/breakdown legs")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only launch the copy calibration kernel and the dominant GEMV, for "
+                         "hardware-counter runs (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
     return ap.parse_args()
 
 
@@ -113,8 +121,12 @@ def main():
               "(the library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
+    if args.traffic_probe:
+        traffic_probe()
+        return
+
     import torch
-    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, HERE)
     import quantized_matmul_ggml_amd as Q
     from quantized_matmul_ggml_amd import workloads as WL
 
@@ -230,7 +242,7 @@ def main():
         "roofline": {
             "kernel": "Q4_0 batched GEMV [Wgate, Wup] 2 x 5632 x 2048, batch 1",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(),
             "avg_launch_us": round(kern_ms * 1e3, 3), "bytes_per_launch": kern_bytes,
         },
     }
@@ -243,6 +255,63 @@ def main():
         result["cpu_baseline"] = cpu_baseline_leg(WL, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+def gemv_source_hash():
+    import hashlib
+    with open(GEMV_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per launch of the dominant kernel as the hardware counters
+    measured them (FETCH_SIZE + WRITE_SIZE, each scaled by what the same
+    counter reads for a copy of known size), or None when no measurement is
+    stored or the GEMV source has changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = [l for l in f if l.startswith("traffic-record: ")]
+    except OSError:
+        return None
+    if not lines:
+        return None
+    rec = json.loads(lines[-1][len("traffic-record: "):])
+    if rec.get("gemv_source_sha256") != gemv_source_hash():
+        log("stored HBM traffic is stale (GEMV source changed): reporting null")
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
+def traffic_probe():
+    """Launches for the hardware-counter runs: three copies of COPY_PROBE_BYTES
+    (a plain device-to-device copy, the counters' calibration), then the
+    dominant kernel, the batched Q4_0 [Wgate, Wup] GEMV, over 22 layers' weights
+    twice (each launch reads weights that are not in L2)."""
+    import torch
+    sys.path.insert(0, HERE)
+    import quantized_matmul_ggml_amd as Q
+    from quantized_matmul_ggml_amd import workloads as WL
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    src = torch.ones(COPY_PROBE_BYTES // 4, device=dev)
+    dst = torch.empty_like(src)
+    gate_up = [(n, M, K) for t, (n, M, K, _) in enumerate(WL.LAYER) if n in ("wgate", "wup")]
+    layers = []
+    for l in range(WL.LAYERS):
+        layers.append([Q.quantize(WL.weights_device(WL.seed(3, t, l), M, K, dev), Q.Q4_0)
+                       for t, (n, M, K, _) in enumerate(WL.LAYER) if n in ("wgate", "wup")])
+    x = WL.activations_device(WL.seed(3, 9), 1, WL.HIDDEN, dev)
+    ys = [torch.empty((1, M), device=dev) for _, M, _ in gate_up]
+    torch.cuda.synchronize()
+    log(f"traffic probe: gemv source sha256 {gemv_source_hash()}")
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        for L in layers:
+            Q.gemv_batch([(w, x, y) for w, y in zip(L, ys)])
+    torch.cuda.synchronize()
+    log(f"traffic probe done: 3 copies of {COPY_PROBE_BYTES} B, {2 * WL.LAYERS} gate/up launches")
 
 
 def prefill_leg(Q, WL, dev, args):
