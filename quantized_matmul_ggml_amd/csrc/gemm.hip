@@ -51,8 +51,6 @@ constexpr int SCALE_GROUP_BLOCKS = 2 * SCALE_GROUP_STEPS;
 constexpr int W_PAIRS = 4;                // pairs of K-steps of weight codes in flight
 static_assert(2 * W_PAIRS == SCALE_GROUP_STEPS, "the producer loop unrolls over both with one index");
 constexpr int THREADS = 512;
-constexpr int BUFFER_FLAGS = 0x00020000;  // raw buffer, 32-bit data format
-constexpr uint32_t OUT_OF_RANGE = 0x80000000u;   // above every buffer size
 
 struct GemmArgs {
     const uint8_t *w;

@@ -50,8 +50,8 @@ struct GemvItem {
     float *y;
     uint64_t y_pitch;     // elements between token rows of y
     int64_t n_groups;     // row groups of U rows
-    int32_t wg_begin;     // first workgroup of this item
-    int32_t wg_count;     // workgroups of this item
+    int32_t wg_count;     // workgroups of this item (grid x; grid y indexes the item)
+    int32_t pad;
 };
 
 struct GemvArgs {
@@ -152,22 +152,32 @@ __device__ inline float chunk_dot(const uint4 q, const float *xv, float acc, uin
     return acc;
 }
 
-// Value of the lane whose index differs from this lane's in bit B (a
-// butterfly partner): DPP quad permutations for bits 0 and 1, ds_swizzle
-// (xor mode, within 32 lanes) for bits 2..4, ds_bpermute for bit 5.  The
-// last all-reduce stage uses lower_half_to_upper() instead (see WaveReduce).
+// The value of a partner lane for the exchange on lane bit B: a lane whose
+// index has the same lower bits 0..B-1 and the other value of bit B.  The
+// pairing is a bijection, not necessarily an involution, which is all the
+// butterfly below needs (every partial value is received exactly once).
+// Every exchange stays on the VALU: DPP quad permutations for bits 0 and 1,
+// DPP rotations by 4 and 8 lanes within a 16-lane row for bits 2 and 3,
+// v_permlane16_swap / v_permlane32_swap for bits 4 and 5.
 template <int B>
-__device__ inline float partner(float v)
+__device__ inline float partner(float v, int lane)
 {
     const int iv = __builtin_bit_cast(int, v);
     if constexpr (B == 0) {
         return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0xB1, 0xF, 0xF, true));
     } else if constexpr (B == 1) {
         return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0x4E, 0xF, 0xF, true));
-    } else if constexpr (B <= 4) {
-        return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(iv, 0x1F | ((1 << B) << 10)));
+    } else if constexpr (B == 2) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0x124, 0xF, 0xF, true));  // row_ror:4
+    } else if constexpr (B == 3) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0x128, 0xF, 0xF, true));  // row_ror:8
+    } else if constexpr (B == 4) {
+        // [0]: odd rows receive the even rows' values; [1]: even rows the odd rows'
+        const auto p = __builtin_amdgcn_permlane16_swap((unsigned)iv, (unsigned)iv, false, false);
+        return __builtin_bit_cast(float, (lane & 16) ? p[0] : p[1]);
     } else {
-        return __shfl_xor(v, 32, 64);
+        const auto p = __builtin_amdgcn_permlane32_swap((unsigned)iv, (unsigned)iv, false, false);
+        return __builtin_bit_cast(float, (lane & 32) ? p[0] : p[1]);
     }
 }
 
@@ -188,7 +198,7 @@ struct WaveReduce {
         for (int i = 0; i < H; ++i) {
             const float send = upper ? v[i] : v[i + H];
             const float mine = upper ? v[i + H] : v[i];
-            keep[i] = mine + partner<B>(send);
+            keep[i] = mine + partner<B>(send, lane);
         }
         return WaveReduce<H, B + 1>::run(keep, lane);
     }
@@ -203,14 +213,16 @@ __device__ inline float lower_half_to_upper(float v)
 
 template <int B>
 struct WaveReduce<1, B> {
-    static __device__ inline float run(const float *v, int)
+    static __device__ inline float run(const float *v, int lane)
     {
+        // all-reduce over bits B..4 (the rotations of bits 2 and 3 add the
+        // next quad, then the next two, so every lane ends with its row sum)
         float s = v[0];
-        if constexpr (B <= 0) s += partner<0>(s);
-        if constexpr (B <= 1) s += partner<1>(s);
-        if constexpr (B <= 2) s += partner<2>(s);
-        if constexpr (B <= 3) s += partner<3>(s);
-        if constexpr (B <= 4) s += partner<4>(s);
+        if constexpr (B <= 0) s += partner<0>(s, lane);
+        if constexpr (B <= 1) s += partner<1>(s, lane);
+        if constexpr (B <= 2) s += partner<2>(s, lane);
+        if constexpr (B <= 3) s += partner<3>(s, lane);
+        if constexpr (B <= 4) s += partner<4>(s, lane);
         s += lower_half_to_upper(s);      // complete in lanes 32..63 only
         return s;
     }
@@ -251,17 +263,19 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: keeps group indices scalar
     const int grp = wave / KS;
     const int ks = wave % KS;
     const int v = ks * 64 + lane;
     const int nt_real = a.N < NT ? a.N : NT;
 
-    // ---- which item this workgroup serves (uniform scalar search) ----
-    int item = 0;
-#pragma unroll
-    for (int i = 1; i < kMaxItems; ++i)
-        if (i < a.n_items && (int)blockIdx.x >= a.item[i].wg_begin) item = i;
+    // ---- this workgroup's item: grid y.  The address of its descriptor is
+    // known at wave start, so its fields arrive in the first round trip to
+    // the kernel arguments (a search over the items' first workgroups would
+    // take a second, dependent one).  Items have their own workgroup counts;
+    // the surplus of a short item's row of the grid exits at once. ----
+    const int item = blockIdx.y;
+    if ((int)blockIdx.x >= a.item[item].wg_count) return;
     const uint8_t *const W = a.item[item].w;
     const uint64_t pitch = a.item[item].pitch;
     const int64_t M = a.item[item].M;
@@ -270,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
     float *const Y = a.item[item].y;
     const uint64_t y_pitch = a.item[item].y_pitch;
     const int64_t n_groups = a.item[item].n_groups;
-    const int64_t wg = (int64_t)blockIdx.x - a.item[item].wg_begin;
+    const int64_t wg = blockIdx.x;
     const int64_t n_wg = a.item[item].wg_count;
 
     // ---- row loop bookkeeping: every wave of the workgroup runs the same
@@ -279,56 +293,102 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
     int64_t g = wg * G + grp;
     const int64_t gstep = n_wg * G;
 
+    // ---- weight loads.  Every load is unconditional: a buffer resource
+    // spans the rows of one group, and a lane without a chunk (row tail) or a
+    // group past the end reads zeros from an out-of-range offset, so the
+    // compiler's wait counts follow one fixed sequence of loads and the
+    // activation staging below waits for its own loads only. ----
+    const int64_t code_bytes = (WT == W_Q4_0) ? a.K / 2 : (WT == W_Q8_0 ? a.K : 2 * a.K);
+    const uint32_t row_bytes = (uint32_t)(a.qoff + code_bytes);
+    // F16 rows whose K is not a multiple of 8 end in a partial chunk: its
+    // halves inside the row are loaded one by one (the bytes after them may
+    // hold anything), the full chunks as usual.
+    const bool f16_tail = WT == W_F16 && (a.K & 7) != 0;
+    uint32_t qoffs[CPL], soffs[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int64_t c = v + (int64_t)j * VL;
+        const bool full = (WT == W_F16) ? c * 8 + 8 <= a.K : c < a.nchunk;
+        qoffs[j] = full ? (uint32_t)(a.qoff + c * 16) : OUT_OF_RANGE;
+        soffs[j] = full ? (uint32_t)(2 * chunk_block<WT>(c)) : OUT_OF_RANGE;
+    }
+    auto group_rsrc = [&](int64_t gi) {
+        const int64_t r0 = gi * U;
+        const int64_t rows = gi < n_groups ? (M - r0 < U ? M - r0 : U) : 0;
+        const uint8_t *base = W + (uint64_t)(rows > 0 ? r0 : 0) * pitch;
+        const uint32_t nrec = rows > 0 ? (uint32_t)((rows - 1) * pitch + row_bytes) : 0u;
+        return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, (int)nrec, BUFFER_FLAGS);
+    };
     uint4 q[U][CPL];
     uint16_t sc[U][CPL];
-    auto load_group = [&](int64_t grp_idx) {
+    auto load_group = [&](int64_t gi) {
+        const __amdgpu_buffer_rsrc_t res = group_rsrc(gi);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            int64_t r = grp_idx * U + u;
-            r = r < M ? r : M - 1;              // tail rows re-read the last row
-            const uint8_t *row = W + (uint64_t)r * pitch;
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
-                const int64_t c = v + (int64_t)j * VL;
-                if (c < a.nchunk) {
-                    q[u][j] = *reinterpret_cast<const uint4 *>(row + a.qoff + c * 16);
-                    if (WT != W_F16) {
-                        sc[u][j] = *reinterpret_cast<const uint16_t *>(row + 2 * chunk_block<WT>(c));
-                    } else if (c * 8 + 8 > a.K) {
-                        // F16 row tail: the 16-byte chunk runs past K; zero the
-                        // halves beyond the row (they may hold anything).
-                        const int valid = (int)(a.K - c * 8);
-                        uint32_t *wd = reinterpret_cast<uint32_t *>(&q[u][j]);
+                const uint32_t ro = (uint32_t)(u * pitch);
+                q[u][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res, qoffs[j] + ro, 0, 0));
+                if (WT != W_F16)
+                    sc[u][j] = __builtin_amdgcn_raw_buffer_load_b16(res, soffs[j] + ro, 0, 0);
+            }
+        }
+        if (f16_tail) {                // uniform; rare: waits for the loads here
 #pragma unroll
-                        for (int h = 0; h < 8; ++h)
-                            if (h >= valid) wd[h / 2] &= (h & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+            for (int u = 0; u < U; ++u) {
+#pragma unroll
+                for (int j = 0; j < CPL; ++j) {
+                    const uint32_t ro = (uint32_t)(u * pitch);
+                    const int64_t c = v + (int64_t)j * VL;
+                    const bool partial = c * 8 < a.K && c * 8 + 8 > a.K;
+                    uint32_t hv[8];
+#pragma unroll
+                    for (int h = 0; h < 8; ++h) {
+                        const uint32_t off = (partial && c * 8 + h < a.K) ? (uint32_t)(c * 16 + 2 * h) + ro
+                                                                          : OUT_OF_RANGE;
+                        hv[h] = __builtin_amdgcn_raw_buffer_load_b16(res, off, 0, 0);
                     }
-                } else {
-                    q[u][j] = make_uint4(0, 0, 0, 0);
-                    sc[u][j] = 0;
+                    q[u][j].x |= hv[0] | (hv[1] << 16);
+                    q[u][j].y |= hv[2] | (hv[3] << 16);
+                    q[u][j].z |= hv[4] | (hv[5] << 16);
+                    q[u][j].w |= hv[6] | (hv[7] << 16);
                 }
             }
         }
     };
-
     // The first staging round's activations are loaded before the first
-    // weight loads are issued: staging then waits only for them (they come
-    // from L2) while the weights stream in.
+    // weight loads are issued: staging then waits only for them while the
+    // weights stream in.  A thread loads LV consecutive activations at a time
+    // (four for quantized rows, whose K is a multiple of 32; one for F16
+    // rows, whose K is arbitrary); those at or past K read zeros.
     constexpr int PER = VL * WPC / kThreads;    // activations per thread per round
-    float x0[PER];
-    {
-        const bool on = nt_real > 0;
+    constexpr int LV = (WT == W_F16) ? 1 : 4;
+    constexpr int NV = PER / LV;
+    static_assert(PER % LV == 0, "activation rounds are whole vectors");
+    struct XVec { float v[LV]; };
+    const uint32_t x_bytes = (uint32_t)(a.K * 4);
+    auto load_x_round = [&](XVec (&dst)[NV], int n, int j) {
+        const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(X + (uint64_t)n * x_pitch), 0, (int)x_bytes, BUFFER_FLAGS);
 #pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int64_t k = tid + i * kThreads;
-            x0[i] = (on && k < a.K) ? X[k] : 0.0f;
+        for (int i = 0; i < NV; ++i) {
+            const int64_t k = (int64_t)j * VL * WPC + LV * (tid + i * kThreads);
+            const uint32_t off = k < a.K ? (uint32_t)(k * 4) : OUT_OF_RANGE;
+            if constexpr (LV == 4)
+                dst[i] = __builtin_bit_cast(XVec, __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0));
+            else
+                dst[i] = __builtin_bit_cast(XVec, __builtin_amdgcn_raw_buffer_load_b32(xres, off, 0, 0));
         }
-    }
-    if (iters > 0) load_group(g < n_groups ? g : n_groups - 1);
+    };
+    XVec x0[NV];
+    load_x_round(x0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_group(g);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- activations for this lane's chunks, staged through LDS one (token,
-    // chunk round) at a time with coalesced global reads; the folded code
-    // offset -offset * sum(x) per chunk ----
+    // chunk round) at a time; the folded code offset -offset * sum(x) per
+    // chunk ----
     float xr[NT][CPL][WPC];
     float xb[NT][CPL];
 #pragma unroll
@@ -336,30 +396,28 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
 #pragma unroll
         for (int j = 0; j < CPL; ++j) {
             if (n < nt_real) {                       // uniform over the workgroup
-                const int64_t k0 = (int64_t)j * VL * WPC;
-                const float *xn = X + (uint64_t)n * x_pitch;
+                XVec xv[NV];
+                if (n == 0 && j == 0) {
 #pragma unroll
-                for (int i = 0; i < PER; ++i) {
-                    const int e = tid + i * kThreads;
-                    const int64_t k = k0 + e;
+                    for (int i = 0; i < NV; ++i) xv[i] = x0[i];
+                } else {
+                    load_x_round(xv, n, j);
+                }
+#pragma unroll
+                for (int i = 0; i < NV; ++i) {
+                    const int e = LV * (tid + i * kThreads);   // element within the round
                     const int cl = e / WPC;
-                    xs[cl * SC + (e - cl * WPC)] = (n == 0 && j == 0) ? x0[i] : (k < a.K ? xn[k] : 0.0f);
+                    *reinterpret_cast<XVec *>(&xs[cl * SC + (e - cl * WPC)]) = xv[i];
                 }
                 __syncthreads();
-                const int64_t c = v + (int64_t)j * VL;
-                if (c < a.nchunk) {
-                    const float4 *src = reinterpret_cast<const float4 *>(&xs[v * SC]);
+                const float4 *src = reinterpret_cast<const float4 *>(&xs[v * SC]);
 #pragma unroll
-                    for (int i = 0; i < WPC / 4; ++i) {
-                        const float4 t = src[i];
-                        xr[n][j][4 * i] = t.x;
-                        xr[n][j][4 * i + 1] = t.y;
-                        xr[n][j][4 * i + 2] = t.z;
-                        xr[n][j][4 * i + 3] = t.w;
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < WPC; ++i) xr[n][j][i] = 0.0f;
+                for (int i = 0; i < WPC / 4; ++i) {
+                    const float4 t = src[i];
+                    xr[n][j][4 * i] = t.x;
+                    xr[n][j][4 * i + 1] = t.y;
+                    xr[n][j][4 * i + 2] = t.z;
+                    xr[n][j][4 * i + 3] = t.w;
                 }
                 __syncthreads();
             } else {
@@ -381,10 +439,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int j = 0; j < CPL; ++j) { qc[u][j] = q[u][j]; scc[u][j] = sc[u][j]; }
-        if (it + 1 < iters) {
-            const int64_t gn = g + gstep;
-            load_group(gn < n_groups ? gn : n_groups - 1);
-        }
+        load_group(g + gstep);     // past the last group: reads nothing
 
         float part[V];
 #pragma unroll
@@ -602,7 +657,7 @@ hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t strea
             need[i] = (groups + groups_per_wg - 1) / groups_per_wg;
             need_total += need[i];
         }
-        int32_t wg_next = 0;
+        int32_t wg_max = 0;
         for (int i = 0; i < count; ++i) {
             if (tasks[i].w.M == 0) continue;
             int64_t wgs = need[i];
@@ -619,13 +674,13 @@ hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t strea
             it.y = tasks[i].y.data + (uint64_t)n0 * tasks[i].y.pitch_elems;
             it.y_pitch = tasks[i].y.pitch_elems;
             it.n_groups = (tasks[i].w.M + c.u - 1) / c.u;
-            it.wg_begin = wg_next;
             it.wg_count = (int32_t)wgs;
-            wg_next += (int32_t)wgs;
+            it.pad = 0;
+            if (wgs > wg_max) wg_max = (int32_t)wgs;
         }
         const int wpc = weights_per_chunk(type);
         const size_t lds = (size_t)64 * c.ks * (wpc + 4) * sizeof(float);
-        hipLaunchKernelGGL(k, dim3((unsigned)wg_next), dim3(kThreads), lds, stream, a);
+        hipLaunchKernelGGL(k, dim3((unsigned)wg_max, (unsigned)a.n_items), dim3(kThreads), lds, stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         n0 += nb;

@@ -51,8 +51,8 @@ struct MItem {
     float *y;
     uint64_t y_pitch;
     int64_t n_tiles;      // 16-row tiles
-    int32_t wg_begin;
-    int32_t wg_count;
+    int32_t wg_count;     // workgroups of this item (grid x; grid y indexes the item)
+    int32_t pad;
 };
 
 struct MArgs {
@@ -163,10 +163,10 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(const MArgs a)
     const int j = lane & 15;               // row within the tile / A channel
     const int g = lane >> 4;               // block within the quad / k-group
 
-    int item = 0;
-#pragma unroll
-    for (int i = 1; i < QMM_GEMV_BATCH_MAX; ++i)
-        if (i < a.n_items && (int)blockIdx.x >= a.item[i].wg_begin) item = i;
+    // The item is grid y, so its descriptor is read in the first round trip
+    // to the kernel arguments; a short item's surplus workgroups exit.
+    const int item = blockIdx.y;
+    if ((int)blockIdx.x >= a.item[item].wg_count) return;
     const uint8_t *const W = a.item[item].w;
     const uint64_t pitch = a.item[item].pitch;
     const int64_t M = a.item[item].M;
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mfma_kernel(const MArgs a)
     float *const Y = a.item[item].y;
     const uint64_t y_pitch = a.item[item].y_pitch;
     const int64_t n_tiles = a.item[item].n_tiles;
-    const int64_t wg = (int64_t)blockIdx.x - a.item[item].wg_begin;
+    const int64_t wg = blockIdx.x;
     const int64_t n_wg = a.item[item].wg_count;
 
     // LDS: A fragments [quad][t][pair][channel][8] bf16, a 16-byte zero
@@ -474,7 +474,7 @@ hipError_t launch_gemv_mfma(const GemvTask *tasks, int count, hipStream_t stream
             need[i] = (t + groups_per_wg - 1) / groups_per_wg;
             need_total += need[i];
         }
-        int32_t wg_next = 0;
+        int32_t wg_max = 0;
         for (int i = 0; i < count; ++i) {
             if (tasks[i].w.M == 0) continue;
             int64_t wgs = need[i];
@@ -491,16 +491,16 @@ hipError_t launch_gemv_mfma(const GemvTask *tasks, int count, hipStream_t stream
             it.y = tasks[i].y.data + (uint64_t)n0 * tasks[i].y.pitch_elems;
             it.y_pitch = tasks[i].y.pitch_elems;
             it.n_tiles = (tasks[i].w.M + 15) / 16;
-            it.wg_begin = wg_next;
             it.wg_count = (int32_t)wgs;
-            wg_next += (int32_t)wgs;
+            it.pad = 0;
+            if (wgs > wg_max) wg_max = (int32_t)wgs;
         }
         const size_t lds = mfma_lds_bytes(K, np);
         if (lds > 65536 - sizeof(float) * 2 * 4 * 16 * 8) {
             const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(k), (int)lds);
             if (e != hipSuccess) return e;
         }
-        hipLaunchKernelGGL(k, dim3((unsigned)wg_next), dim3(kThreads), lds, stream, a);
+        hipLaunchKernelGGL(k, dim3((unsigned)wg_max, (unsigned)a.n_items), dim3(kThreads), lds, stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         n0 += nb;

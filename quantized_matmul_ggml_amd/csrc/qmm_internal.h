@@ -17,6 +17,12 @@ enum WType : int { W_F32 = 0, W_F16 = 1, W_BF16 = 2, W_Q8_0 = 3, W_Q4_0 = 4 };
 // first, padded to 16 bytes.
 __host__ __device__ inline int64_t quant_offset(int64_t K) { return ((K / 16) + 15) / 16 * 16; }
 
+// Raw buffer resources (kernels): word 3 of the descriptor (32-bit data
+// format, no swizzle), and an offset above every buffer size the kernels
+// build, whose loads return zeros without touching memory.
+constexpr int BUFFER_FLAGS = 0x00020000;
+constexpr uint32_t OUT_OF_RANGE = 0x80000000u;
+
 // One weight matrix as the kernels see it: M rows of K weights, row r at
 // base + r * pitch (bytes).
 struct WeightView {
@@ -51,6 +57,9 @@ struct GemvConfig {
 // Fills cfg and returns true when the register-resident GEMV supports the
 // shape (each lane keeps at most 128 activation floats); false otherwise.
 bool gemv_config(int type, int64_t K, int64_t M, int64_t N, GemvConfig *cfg);
+// Whether the GEMV kernels can address w: loads span a few rows with 32-bit
+// buffer offsets, so the row pitch is bounded (2^28 bytes).
+inline bool gemv_pitch_supported(const WeightView &w) { return w.pitch <= (1ull << 28); }
 
 // Launchers (return hipSuccess or the launch error).  Shapes are validated by
 // the caller; every launcher accepts M == 0 / N == 0 as a no-op.

@@ -211,6 +211,23 @@ def test_gemv_strided_operands(orc):
         _assert_tol(y, yref, a, 1e-4, 1e-6, f"gemv strided {tname}")
 
 
+@pytest.mark.parametrize("K", [7, 1003, 2051])
+def test_gemv_f16_tail_with_nan_padding(orc, K):
+    """F16 rows whose K is not a multiple of 8, stored with a row pitch whose
+    padding holds NaN: only the halves inside each row may contribute."""
+    M, N = 37, 3
+    _banner(f"gemv f16 tail K={K} nan padding")
+    w = WL.weights(900 + K, M, K)
+    x = WL.activations(901 + K, N, K)
+    pitch = (K + 7) // 8 * 8 + 8            # halves; the pitch is 16-byte aligned
+    buf = torch.full((M, pitch), float("nan"), dtype=torch.float16, device=DEV)
+    buf[:, :K] = torch.from_numpy(WL.round_f16(w)).to(DEV)
+    wt = B.Weight(buf, B.F16, K, M)
+    y = Q.gemv(wt, torch.from_numpy(x).to(DEV)).cpu().numpy()
+    yref, a = orc.mul_mat(TYPES["F16"][1], _oracle_weight(orc, "F16", w), K, x)
+    _assert_tol(y, yref, a, 1e-4, 1e-6, f"gemv f16 tail K={K}")
+
+
 def test_gemv_decoder_layer_full_size(orc):
     """The seven projections of one TinyLLaMA-shaped layer, Q4_0, one token."""
     xs = [WL.activations(WL.seed(3, 7 + s), 1, k) for s, k in enumerate(WL.LAYER_X_K)]
