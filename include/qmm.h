@@ -130,8 +130,9 @@ QMM_API int qmm_dequantize(const qmm_tensor *src, qmm_tensor *dst_f32, void *str
  * (N > 8: QMM_ERR_SHAPE);  y: F32 ne = [M, N], must not overlap w or x.
  * Each lane keeps its slice of x in registers, which bounds K: the call
  * returns QMM_ERR_UNSUPPORTED when K exceeds 32768 (Q4_0, Q8_0) or 16384
- * (F16), or when the row pitch nb[1] of w exceeds 2^28 bytes (loads address
- * a few rows with 32-bit offsets).  Tokens are processed in groups that fit
+ * (F16), when the row pitch nb[1] of w exceeds 2^28 bytes (loads address
+ * a few rows with 32-bit offsets), or when M or the row pitch of x or y (in
+ * elements) reaches 2^31.  Tokens are processed in groups that fit
  * the registers (one pass over the weights per group).
  * Weights are read once from HBM and dequantized in registers; binary32
  * multiply-add; the accumulation order is unspecified (results agree with

@@ -40,27 +40,33 @@ constexpr int kMaxWorkgroups = 1024;  // persistent grid: 4 workgroups per CU
 constexpr int kMaxItems = QMM_GEMV_BATCH_MAX;
 
 // One GEMV of a launch: its weights, activations and outputs.  All items of
-// a launch share the weight type, K and the token count.
-struct GemvItem {
+// a launch share the weight type, K and the token count.  An item is one
+// 64-byte record, and the fields shared by all items sit in the first 64
+// bytes of the arguments, so a wave fetches everything it needs in one round
+// trip to the kernel arguments (each trip costs a few hundred nanoseconds).
+struct alignas(64) GemvItem {
     const uint8_t *w;
-    uint64_t pitch;       // bytes between weight rows
-    int64_t M;
     const float *x;
-    uint64_t x_pitch;     // elements between token rows of x
     float *y;
-    uint64_t y_pitch;     // elements between token rows of y
-    int64_t n_groups;     // row groups of U rows
+    uint32_t pitch;       // bytes between weight rows (<= 2^28)
+    uint32_t x_pitch;     // elements between token rows of x
+    uint32_t y_pitch;     // elements between token rows of y
+    int32_t M;
+    int32_t n_groups;     // row groups of U rows
     int32_t wg_count;     // workgroups of this item (grid x; grid y indexes the item)
-    int32_t pad;
+    int32_t iters;        // row-group iterations of each wave group
+    int32_t pad[3];
 };
+static_assert(sizeof(GemvItem) == 64, "one 64-byte record per item");
 
 struct GemvArgs {
-    GemvItem item[kMaxItems];
-    int32_t n_items;
     int32_t N;            // real tokens (<= NT)
-    int64_t K;
-    int64_t qoff;         // byte offset of the codes inside a row (0 for F16)
-    int64_t nchunk;       // 16-byte chunks of codes per row
+    int32_t K;
+    int32_t qoff;         // byte offset of the codes inside a row (0 for F16)
+    int32_t nchunk;       // 16-byte chunks of codes per row
+    int32_t n_items;
+    int32_t pad[11];
+    GemvItem item[kMaxItems];
 };
 
 // (a & m) | c in one VALU op (the compiler would split it: gfx9 VOP3 takes no
@@ -267,61 +273,66 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
     const int grp = wave / KS;
     const int ks = wave % KS;
     const int v = ks * 64 + lane;
-    const int nt_real = a.N < NT ? a.N : NT;
 
-    // ---- this workgroup's item: grid y.  The address of its descriptor is
-    // known at wave start, so its fields arrive in the first round trip to
-    // the kernel arguments (a search over the items' first workgroups would
-    // take a second, dependent one).  Items have their own workgroup counts;
-    // the surplus of a short item's row of the grid exits at once. ----
+    // ---- this workgroup's item: grid y, so the address of its record is
+    // known at wave start.  Every field is fetched before the early exit of
+    // a short item's surplus workgroups (the empty asm makes them needed
+    // there), so the fetches go out together: one round trip. ----
     const int item = blockIdx.y;
-    if ((int)blockIdx.x >= a.item[item].wg_count) return;
-    const uint8_t *const W = a.item[item].w;
-    const uint64_t pitch = a.item[item].pitch;
-    const int64_t M = a.item[item].M;
-    const float *const X = a.item[item].x;
-    const uint64_t x_pitch = a.item[item].x_pitch;
-    float *const Y = a.item[item].y;
-    const uint64_t y_pitch = a.item[item].y_pitch;
-    const int64_t n_groups = a.item[item].n_groups;
-    const int64_t wg = blockIdx.x;
-    const int64_t n_wg = a.item[item].wg_count;
+    const GemvItem &itm = a.item[item];
+    const uint8_t *const W = itm.w;
+    const float *const X = itm.x;
+    float *const Y = itm.y;
+    const uint32_t pitch = itm.pitch;
+    const uint32_t x_pitch = itm.x_pitch;
+    const uint32_t y_pitch = itm.y_pitch;
+    const int M = itm.M;
+    const int n_groups = itm.n_groups;
+    const int n_wg = itm.wg_count;
+    const int iters = itm.iters;
+    const int N = a.N;
+    const int K = a.K;
+    const int qoff = a.qoff;
+    const int nchunk = a.nchunk;
+    asm volatile("" ::"s"(W), "s"(X), "s"(Y), "s"(pitch), "s"(x_pitch), "s"(y_pitch), "s"(M),
+                 "s"(n_groups), "s"(n_wg), "s"(iters), "s"(N), "s"(K), "s"(qoff), "s"(nchunk));
+    if ((int)blockIdx.x >= n_wg) return;
+    const int nt_real = N < NT ? N : NT;
 
     // ---- row loop bookkeeping: every wave of the workgroup runs the same
     // trip count (the KS > 1 reduction uses workgroup barriers) ----
-    const int64_t iters = (n_groups + (int64_t)G * n_wg - 1) / ((int64_t)G * n_wg);
-    int64_t g = wg * G + grp;
-    const int64_t gstep = n_wg * G;
+    int g = (int)blockIdx.x * G + grp;
+    const int gstep = n_wg * G;
 
     // ---- weight loads.  Every load is unconditional: a buffer resource
     // spans the rows of one group, and a lane without a chunk (row tail) or a
     // group past the end reads zeros from an out-of-range offset, so the
     // compiler's wait counts follow one fixed sequence of loads and the
     // activation staging below waits for its own loads only. ----
-    const int64_t code_bytes = (WT == W_Q4_0) ? a.K / 2 : (WT == W_Q8_0 ? a.K : 2 * a.K);
-    const uint32_t row_bytes = (uint32_t)(a.qoff + code_bytes);
+    const int code_bytes = (WT == W_Q4_0) ? K / 2 : (WT == W_Q8_0 ? K : 2 * K);
+    const uint32_t row_bytes = (uint32_t)(qoff + code_bytes);
     // F16 rows whose K is not a multiple of 8 end in a partial chunk: its
     // halves inside the row are loaded one by one (the bytes after them may
     // hold anything), the full chunks as usual.
-    const bool f16_tail = WT == W_F16 && (a.K & 7) != 0;
+    const bool f16_tail = WT == W_F16 && (K & 7) != 0;
     uint32_t qoffs[CPL], soffs[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
-        const int64_t c = v + (int64_t)j * VL;
-        const bool full = (WT == W_F16) ? c * 8 + 8 <= a.K : c < a.nchunk;
-        qoffs[j] = full ? (uint32_t)(a.qoff + c * 16) : OUT_OF_RANGE;
+        const int c = v + j * VL;
+        const bool full = (WT == W_F16) ? c * 8 + 8 <= K : c < nchunk;
+        qoffs[j] = full ? (uint32_t)(qoff + c * 16) : OUT_OF_RANGE;
         soffs[j] = full ? (uint32_t)(2 * chunk_block<WT>(c)) : OUT_OF_RANGE;
     }
-    auto group_rsrc = [&](int64_t gi) {
-        const int64_t r0 = gi * U;
-        const int64_t rows = gi < n_groups ? (M - r0 < U ? M - r0 : U) : 0;
+    auto group_rsrc = [&](int gi) {
+        const int r0 = gi * U;
+        const int rows = gi < n_groups ? (M - r0 < U ? M - r0 : U) : 0;
         const uint8_t *base = W + (uint64_t)(rows > 0 ? r0 : 0) * pitch;
-        const uint32_t nrec = rows > 0 ? (uint32_t)((rows - 1) * pitch + row_bytes) : 0u;
+        const uint32_t nrec = rows > 0 ? (uint32_t)(rows - 1) * pitch + row_bytes : 0u;
         return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, (int)nrec, BUFFER_FLAGS);
     };
     uint4 q[U][CPL];
     uint16_t sc[U][CPL];
-    auto load_group = [&](int64_t gi) {
+    auto load_group = [&](int gi) {
         const __amdgpu_buffer_rsrc_t res = group_rsrc(gi);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -339,12 +350,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
 #pragma unroll
                 for (int j = 0; j < CPL; ++j) {
                     const uint32_t ro = (uint32_t)(u * pitch);
-                    const int64_t c = v + (int64_t)j * VL;
-                    const bool partial = c * 8 < a.K && c * 8 + 8 > a.K;
+                    const int c = v + j * VL;
+                    const bool partial = c * 8 < K && c * 8 + 8 > K;
                     uint32_t hv[8];
 #pragma unroll
                     for (int h = 0; h < 8; ++h) {
-                        const uint32_t off = (partial && c * 8 + h < a.K) ? (uint32_t)(c * 16 + 2 * h) + ro
+                        const uint32_t off = (partial && c * 8 + h < K) ? (uint32_t)(c * 16 + 2 * h) + ro
                                                                           : OUT_OF_RANGE;
                         hv[h] = __builtin_amdgcn_raw_buffer_load_b16(res, off, 0, 0);
                     }
@@ -366,14 +377,14 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
     constexpr int NV = PER / LV;
     static_assert(PER % LV == 0, "activation rounds are whole vectors");
     struct XVec { float v[LV]; };
-    const uint32_t x_bytes = (uint32_t)(a.K * 4);
+    const uint32_t x_bytes = (uint32_t)K * 4;
     auto load_x_round = [&](XVec (&dst)[NV], int n, int j) {
         const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(X + (uint64_t)n * x_pitch), 0, (int)x_bytes, BUFFER_FLAGS);
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int64_t k = (int64_t)j * VL * WPC + LV * (tid + i * kThreads);
-            const uint32_t off = k < a.K ? (uint32_t)(k * 4) : OUT_OF_RANGE;
+            const int k = j * VL * WPC + LV * (tid + i * kThreads);
+            const uint32_t off = k < K ? (uint32_t)k * 4 : OUT_OF_RANGE;
             if constexpr (LV == 4)
                 dst[i] = __builtin_bit_cast(XVec, __builtin_amdgcn_raw_buffer_load_b128(xres, off, 0, 0));
             else
@@ -432,7 +443,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
     }
     const uint32_t magic = 0x4C004C00u;   // binary16 exponent field of 16.0 in both halves
 
-    for (int64_t it = 0; it < iters; ++it, g += gstep) {
+    for (int it = 0; it < iters; ++it, g += gstep) {
         uint4 qc[U][CPL];
         uint16_t scc[U][CPL];
 #pragma unroll
@@ -466,8 +477,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
         if (KS == 1) {
             if (owner && idx < U * NT && in_range) {
                 const int u = idx / NT, n = idx % NT;
-                const int64_t r = g * U + u;
-                if (r < M && n < a.N) Y[(uint64_t)n * y_pitch + r] = tot;
+                const int r = g * U + u;
+                if (r < M && n < N) Y[(uint64_t)n * y_pitch + r] = tot;
             }
         } else {
             float *buf = red[it & 1][wave];
@@ -478,8 +489,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
 #pragma unroll
                 for (int w2 = 0; w2 < KS; ++w2) s += red[it & 1][grp * KS + w2][lane];
                 const int u = lane / NT, n = lane % NT;
-                const int64_t r = g * U + u;
-                if (r < M && n < a.N) Y[(uint64_t)n * y_pitch + r] = s;
+                const int r = g * U + u;
+                if (r < M && n < N) Y[(uint64_t)n * y_pitch + r] = s;
             }
         }
     }
@@ -644,12 +655,12 @@ hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t strea
         }
         const Kernel k = pick(type, c);
         const int groups_per_wg = 4 / c.ks;
-        GemvArgs a;
+        GemvArgs a = {};
         a.n_items = 0;
         a.N = (int32_t)nb;
-        a.K = K;
-        a.qoff = (type == W_F16) ? 0 : quant_offset(K);
-        a.nchunk = chunks_per_row(type, K);
+        a.K = (int32_t)K;
+        a.qoff = (type == W_F16) ? 0 : (int32_t)quant_offset(K);
+        a.nchunk = (int32_t)chunks_per_row(type, K);
         int64_t need_total = 0;
         int64_t need[kMaxItems];
         for (int i = 0; i < count; ++i) {
@@ -667,15 +678,16 @@ hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t strea
             }
             GemvItem &it = a.item[a.n_items++];
             it.w = tasks[i].w.base;
-            it.pitch = tasks[i].w.pitch;
-            it.M = tasks[i].w.M;
+            it.pitch = (uint32_t)tasks[i].w.pitch;
+            it.M = (int32_t)tasks[i].w.M;
             it.x = static_cast<const float *>(tasks[i].x.data) + (uint64_t)n0 * tasks[i].x.pitch_elems;
-            it.x_pitch = tasks[i].x.pitch_elems;
+            it.x_pitch = (uint32_t)tasks[i].x.pitch_elems;
             it.y = tasks[i].y.data + (uint64_t)n0 * tasks[i].y.pitch_elems;
-            it.y_pitch = tasks[i].y.pitch_elems;
-            it.n_groups = (tasks[i].w.M + c.u - 1) / c.u;
+            it.y_pitch = (uint32_t)tasks[i].y.pitch_elems;
+            it.n_groups = (int32_t)((tasks[i].w.M + c.u - 1) / c.u);
             it.wg_count = (int32_t)wgs;
-            it.pad = 0;
+            const int64_t per_pass = (int64_t)groups_per_wg * wgs;   // groups one pass of the grid covers
+            it.iters = (int32_t)((it.n_groups + per_pass - 1) / per_pass);
             if (wgs > wg_max) wg_max = (int32_t)wgs;
         }
         const int wpc = weights_per_chunk(type);

@@ -175,9 +175,9 @@ int qmm_gemv(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *stre
     // floats per lane), which bounds K; tokens are split into chunks that fit.
     qmm::GemvConfig cfg;
     if (!qmm::gemv_config(w->type, w->ne[0], w->ne[1], 1, &cfg)) return QMM_ERR_UNSUPPORTED;
-    if (!qmm::gemv_pitch_supported(weight_view(w))) return QMM_ERR_UNSUPPORTED;
     qmm::ActView xv{x->data, pitch_elems(x), x->ne[1]};
     qmm::OutView yv{static_cast<float *>(y->data), pitch_elems(y)};
+    if (!qmm::gemv_supported(weight_view(w), xv, yv)) return QMM_ERR_UNSUPPORTED;
     return status_of(qmm::launch_gemv(weight_view(w), xv, yv, static_cast<hipStream_t>(stream)));
 }
 
@@ -206,9 +206,9 @@ int qmm_gemv_batch(const qmm_gemv_item *items, int32_t count, void *stream)
                 return QMM_ERR_ALIAS;
         }
         tasks[i].w = weight_view(w);
-        if (!qmm::gemv_pitch_supported(tasks[i].w)) return QMM_ERR_UNSUPPORTED;
         tasks[i].x = qmm::ActView{x->data, pitch_elems(x), x->ne[1]};
         tasks[i].y = qmm::OutView{static_cast<float *>(y->data), pitch_elems(y)};
+        if (!qmm::gemv_supported(tasks[i].w, tasks[i].x, tasks[i].y)) return QMM_ERR_UNSUPPORTED;
     }
     int64_t m_total = 0;
     for (int i = 0; i < count; ++i) m_total += items[i].w->ne[1];

@@ -57,9 +57,14 @@ struct GemvConfig {
 // Fills cfg and returns true when the register-resident GEMV supports the
 // shape (each lane keeps at most 128 activation floats); false otherwise.
 bool gemv_config(int type, int64_t K, int64_t M, int64_t N, GemvConfig *cfg);
-// Whether the GEMV kernels can address w: loads span a few rows with 32-bit
-// buffer offsets, so the row pitch is bounded (2^28 bytes).
-inline bool gemv_pitch_supported(const WeightView &w) { return w.pitch <= (1ull << 28); }
+// Whether the GEMV kernels can address the operands: loads span a few rows
+// with 32-bit buffer offsets, so the weight row pitch is bounded (2^28
+// bytes), and row counts and activation / output pitches are 32-bit.
+inline bool gemv_supported(const WeightView &w, const ActView &x, const OutView &y)
+{
+    return w.pitch <= (1ull << 28) && w.M < (1ll << 31) && x.pitch_elems < (1ull << 31) &&
+           y.pitch_elems < (1ull << 31);
+}
 
 // Launchers (return hipSuccess or the launch error).  Shapes are validated by
 // the caller; every launcher accepts M == 0 / N == 0 as a no-op.
