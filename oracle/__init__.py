@@ -11,7 +11,8 @@ What it computes (the pages it follows are cited in ``qmm_oracle.h``):
   * Q8_0 / Q4_0 block quantization of fp32 rows and the row-planar packing;
   * the exact dequantized weights W';
   * MUL_MAT y[n][m] = sum_k W'[m][k] x[n][k] accumulated in binary64, with
-    the magnitude sum a[n][m] = sum_k |W'[m][k] x[n][k]| used by tolerances.
+    the magnitude sum a[n][m] = sum_k |W'[m][k] x[n][k]| used by tolerances;
+  * the SwiGLU epilogue h = Swish(g) * u of the fused gate/up projection.
 """
 from __future__ import annotations
 
@@ -81,6 +82,10 @@ def lib() -> ctypes.CDLL:
         h.orc_mul_mat_pairs.argtypes = [ci, u8p, sz, i64, i64, vp, ci, i64, ci,
                                         i64p, i64p, i64, f64p, f64p]
         h.orc_mul_mat_pairs.restype = ci
+        h.orc_swish.argtypes = [ctypes.c_double]
+        h.orc_swish.restype = ctypes.c_double
+        h.orc_swiglu_n.argtypes = [f64p, f64p, f64p, sz]
+        h.orc_swiglu_n.restype = None
         _lib_handle = h
     return _lib_handle
 
@@ -223,3 +228,21 @@ def mul_mat_pairs(type_: int, packed, K: int, x, ms, ns, *, x_bf16_bits: bool = 
     if rc != 0:
         raise ValueError("orc_mul_mat_pairs rejected its arguments")
     return y, a
+
+
+# ---- SwiGLU ---------------------------------------------------------------
+
+def swish(z: float) -> float:
+    """Swish(z) = z * sigma(z) in binary64."""
+    return float(lib().orc_swish(float(z)))
+
+
+def swiglu(g, u) -> np.ndarray:
+    """h = Swish(g) * u elementwise in binary64 (g, u of the same shape)."""
+    g = _c(g, np.float64)
+    u = _c(u, np.float64)
+    assert g.shape == u.shape
+    h = np.empty(g.shape, np.float64)
+    lib().orc_swiglu_n(_ptr(g, ctypes.c_double), _ptr(u, ctypes.c_double),
+                       _ptr(h, ctypes.c_double), g.size)
+    return h

@@ -347,3 +347,17 @@ int orc_mul_mat_pairs(int type, const uint8_t *w, size_t pitch, int64_t K, int64
     free(wrow);
     return 0;
 }
+
+/* ---- SwiGLU ------------------------------------------------------------- */
+
+double orc_swish(double z)
+{
+    /* z * sigma(z); for z far below zero e^{-z} overflows to +inf and the
+     * quotient is the correct limit (-0). */
+    return z / (1.0 + exp(-z));
+}
+
+void orc_swiglu_n(const double *g, const double *u, double *h, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) h[i] = orc_swish(g[i]) * u[i];
+}

@@ -92,6 +92,14 @@ int orc_mul_mat_pairs(int type, const uint8_t *w, size_t pitch, int64_t K, int64
                       const int64_t *ms, const int64_t *ns, int64_t count,
                       double *y, double *a);
 
+/* ---- SwiGLU epilogue of the fused gate/up projection ------------------
+ * "Development Guide for Small AI Models (TinyLLaMA, etc.) Using C++", §4.4:
+ * SwiGLU(x) = Swish(x W_gate) (elementwise *) (x W_up), with
+ * Swish(z) = z * sigma(z) and sigma(z) = 1 / (1 + e^{-z}).  Binary64.       */
+double orc_swish(double z);
+/* h[i] = Swish(g[i]) * u[i] for i < n.                                      */
+void orc_swiglu_n(const double *g, const double *u, double *h, size_t n);
+
 #ifdef __cplusplus
 }
 #endif

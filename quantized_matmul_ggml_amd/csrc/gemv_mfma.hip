@@ -453,9 +453,10 @@ hipError_t launch_gemv_mfma(const GemvTask *tasks, int count, hipStream_t stream
             np /= 2;
             nb = 2 * np;
         }
-        // Split the quads of a tile over more waves while the tiles alone
-        // cannot keep 8 waves per CU busy.
-        int ks = tiles_total >= 2048 ? 1 : tiles_total >= 1024 ? 2 : 4;
+        // Split the quads of a tile over more waves only while the tiles
+        // alone leave CUs short of waves (the LM head's 2000 tiles run 1.4x
+        // faster with one wave per tile than with two, measured).
+        int ks = tiles_total >= 1024 ? 1 : tiles_total >= 512 ? 2 : 4;
         const int64_t nquad = (K / 32 + 3) / 4;
         while (ks > 1 && ks > nquad) ks /= 2;
         const int groups_per_wg = 4 / ks;
