@@ -186,15 +186,31 @@ def main():
             Q.gemv(L["wdown"], xs[3], out=ys["wdown"])
         Q.gemv(lm, x_lm, out=y_lm)
 
+    # dependent, with the gate/up pair fused with its SwiGLU epilogue (one
+    # 5632-vector written instead of two)
+    h_ffn = torch.empty((1, WL.FFN), device=dev)
+
+    def step_fused():
+        for L in layers:
+            Q.gemv_batch([(L[n], xs[0], ys[n]) for n in ("wq", "wk", "wv")])
+            Q.gemv(L["wo"], xs[1], out=ys["wo"])
+            Q.gemv_swiglu(L["wgate"], L["wup"], xs[2], out=h_ffn)
+            Q.gemv(L["wdown"], xs[3], out=ys["wdown"])
+        Q.gemv(lm, x_lm, out=y_lm)
+
+    fused_bytes = step_bytes - WL.LAYERS * (4 * WL.HIDDEN + 4 * WL.FFN)
+
     variants = {}
-    for vname, fn, launches in (("per_matrix", step_per_matrix, 7 * WL.LAYERS + 1),
-                                ("dependent", step_dependent, 4 * WL.LAYERS + 1),
-                                ("grouped", step_grouped, 2 * WL.LAYERS + 1)):
+    for vname, fn, launches, nbytes in (
+            ("per_matrix", step_per_matrix, 7 * WL.LAYERS + 1, step_bytes),
+            ("dependent", step_dependent, 4 * WL.LAYERS + 1, step_bytes),
+            ("grouped", step_grouped, 2 * WL.LAYERS + 1, step_bytes),
+            ("dependent_swiglu_fused", step_fused, 4 * WL.LAYERS + 1, fused_bytes)):
         log(f"decode step [{vname}]: capturing {launches} launches into a HIP graph")
         graph = Graph(fn)
         ms_v, wall_v = timed(graph, args.steps, args.warmup)
         variants[vname] = {"ms": ms_v, "wall": wall_v, "launches": launches,
-                           "gbs": step_bytes / (ms_v * 1e-3) / 1e9}
+                           "gbs": nbytes / (ms_v * 1e-3) / 1e9}
         log(f"decode step [{vname}] {ms_v * 1e3:.1f} us  {variants[vname]['gbs']:.0f} GB/s  "
             f"{1e3 / ms_v:.0f} tokens/s")
     head = "dependent"
@@ -212,6 +228,16 @@ def main():
     kern_bytes = gemv_bytes(layers[0]["wgate"], 1) + gemv_bytes(layers[0]["wup"], 1)
     achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     log(f"gate/up batched GEMV {kern_ms * 1e3:.2f} us/launch  {achieved:.0f} GB/s")
+
+    # the same pair fused with its SwiGLU epilogue, per launch
+    swiglu_launches = [lambda L=L: Q.gemv_swiglu(L["wgate"], L["wup"], xs[2], out=h_ffn) for L in layers]
+    durs = []
+    for _ in range(max(1, args.steps // 4)):
+        durs += per_launch_ms(swiglu_launches)
+    sw_ms = sum(durs) / len(durs)
+    sw_bytes = kern_bytes - 4 * WL.HIDDEN - 4 * WL.FFN
+    sw_gbs = sw_bytes / (sw_ms * 1e-3) / 1e9
+    log(f"gate/up SwiGLU fused GEMV {sw_ms * 1e3:.2f} us/launch  {sw_gbs:.0f} GB/s")
 
     result = {
         "metric": METRIC,
@@ -238,6 +264,10 @@ def main():
             "variants": {k: {"us": round(v["ms"] * 1e3, 1), "gbs": round(v["gbs"], 1),
                              "launches": v["launches"], "tokens_per_s": round(1e3 / v["ms"], 1)}
                          for k, v in variants.items()},
+            "swiglu_fused_gate_up": {"kernel": "Q4_0 gate/up 2 x 5632 x 2048 + SwiGLU, batch 1",
+                                     "avg_launch_us": round(sw_ms * 1e3, 3), "bytes_per_launch": sw_bytes,
+                                     "gbs": round(sw_gbs, 1),
+                                     "frac_of_hbm_peak": round(sw_gbs / HBM_PEAK_GBS, 4)},
         },
         "roofline": {
             "kernel": "Q4_0 batched GEMV [Wgate, Wup] 2 x 5632 x 2048, batch 1",

@@ -160,6 +160,23 @@ typedef struct qmm_gemv_item {
  * of the launch are shared among the items in proportion to their rows. */
 QMM_API int qmm_gemv_batch(const qmm_gemv_item *items, int32_t count, void *stream);
 
+/* The fused gate/up projection of the feed-forward block with its SwiGLU
+ * epilogue ("Development Guide for Small AI Models (TinyLLaMA, etc.) Using
+ * C++", §4.4: SwiGLU(x) = Swish(x W_gate) * (x W_up) elementwise, with
+ * Swish(z) = z sigma(z) = z / (1 + e^{-z})):
+ *   h[n][m] = Swish(sum_k Wg'[m][k] x[n][k]) * sum_k Wu'[m][k] x[n][k].
+ * w_gate, w_up: the same type (Q8_0, Q4_0 or F16) and ne = [K, M], each with
+ * its own row pitch under the rules of qmm_gemv;  x: F32 ne = [K, N],
+ * 1 <= N <= 8;  h: F32 ne = [M, N], overlapping none of w_gate, w_up, x
+ * (QMM_ERR_ALIAS).  Different types: QMM_ERR_TYPE; different ne: QMM_ERR_SHAPE.
+ * One launch streams both matrices once and writes h only (the two
+ * projections are never stored).  The two sums carry the accuracy of
+ * qmm_gemv; the epilogue runs in binary32 (expf, one division, two
+ * products), so |h - h_exact| <= 1.1 e_g (|u| + e_u) + |Swish(g)| e_u
+ * + 2^-20 |h| with e_g, e_u the qmm_gemv bounds of the two sums. */
+QMM_API int qmm_gemv_swiglu(const qmm_tensor *w_gate, const qmm_tensor *w_up,
+                            const qmm_tensor *x_f32, qmm_tensor *h_f32, void *stream);
+
 /* Prefill GEMM ("No Python! ...", §6: C_ij = sum_k A_ik B_kj, with many tokens
  * per step).  w: Q4_0 or Q8_0, ne = [K, M];  x: BF16 ne = [K, N], any N >= 0;
  * y: F32 ne = [M, N], must not overlap w or x.  Weight tiles are dequantized

@@ -26,7 +26,7 @@ OK, ERR_NULL, ERR_TYPE, ERR_SHAPE, ERR_LAYOUT, ERR_ALIAS, ERR_UNSUPPORTED, ERR_D
     0, -1, -2, -3, -4, -5, -6, -7
 
 EXPORTS = ("qmm_row_size", "qmm_quantize", "qmm_dequantize", "qmm_gemv", "qmm_gemv_batch",
-           "qmm_gemm", "qmm_strerror")
+           "qmm_gemv_swiglu", "qmm_gemm", "qmm_strerror")
 GEMV_BATCH_MAX = 8
 
 
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         h.qmm_dequantize.argtypes = [P, P, ctypes.c_void_p]
         h.qmm_gemv.argtypes = [P, P, P, ctypes.c_void_p]
         h.qmm_gemm.argtypes = [P, P, P, ctypes.c_void_p]
+        h.qmm_gemv_swiglu.argtypes = [P, P, P, P, ctypes.c_void_p]
+        h.qmm_gemv_swiglu.restype = ctypes.c_int
         h.qmm_gemv_batch.argtypes = [ctypes.POINTER(QmmGemvItem), ctypes.c_int32, ctypes.c_void_p]
         h.qmm_gemv_batch.restype = ctypes.c_int
         for f in ("qmm_quantize", "qmm_dequantize", "qmm_gemv", "qmm_gemm"):
@@ -211,6 +213,18 @@ def gemv_batch(items, *, stream=None) -> list:
     arr = (QmmGemvItem * max(1, len(descs)))(*descs)
     _check(lib().qmm_gemv_batch(arr, len(descs), _stream(stream)), "qmm_gemv_batch")
     return outs
+
+
+def gemv_swiglu(w_gate: Weight, w_up: Weight, x: torch.Tensor, *, out: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """h (N, M) fp32 = Swish(x W_gate'^T) * (x W_up'^T), one fused launch; 1 <= N <= 8."""
+    _need_gpu(w_gate.data, w_up.data, x)
+    if out is None:
+        out = torch.empty((x.shape[0], w_gate.M), dtype=torch.float32, device=x.device)
+    gd, ud, xd, hd = w_gate.desc(), w_up.desc(), _dense_desc(x, F32), _dense_desc(out, F32)
+    _check(lib().qmm_gemv_swiglu(ctypes.byref(gd), ctypes.byref(ud), ctypes.byref(xd), ctypes.byref(hd),
+                                 _stream(stream)), "qmm_gemv_swiglu")
+    return out
 
 
 def gemm(w: Weight, x: torch.Tensor, *, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:

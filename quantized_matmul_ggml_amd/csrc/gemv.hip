@@ -48,14 +48,15 @@ struct alignas(64) GemvItem {
     const uint8_t *w;
     const float *x;
     float *y;
+    const uint8_t *w2;    // fused SwiGLU launches: the up projection (w is the gate)
     uint32_t pitch;       // bytes between weight rows (<= 2^28)
+    uint32_t pitch2;      // the same for w2
     uint32_t x_pitch;     // elements between token rows of x
     uint32_t y_pitch;     // elements between token rows of y
     int32_t M;
-    int32_t n_groups;     // row groups of U rows
+    int32_t n_groups;     // row groups (U rows, or U/2 row indices of each matrix when fused)
     int32_t wg_count;     // workgroups of this item (grid x; grid y indexes the item)
     int32_t iters;        // row-group iterations of each wave group
-    int32_t pad[3];
 };
 static_assert(sizeof(GemvItem) == 64, "one 64-byte record per item");
 
@@ -249,15 +250,30 @@ __device__ inline int value_index(int lane)
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 constexpr int pow2_ceil(int v) { return v <= 1 ? 1 : 2 * pow2_ceil((v + 1) / 2); }
 
+// Swish(z) = z * sigma(z) = z / (1 + e^{-z}) in binary32; for z far below
+// zero e^{-z} overflows and the quotient is the limit -0.
+__device__ inline float swish(float z)
+{
+    return z / (1.0f + expf(-z));
+}
+
 // LDS image of one round of activation chunks: lane-local chunk c holds its
 // wpc floats at c * (wpc + 4); the 16-byte pad per chunk spreads the
 // lane-strided 128-bit reads of the lanes over all banks.
 template <int WT>
 __host__ __device__ constexpr int lds_chunk_stride() { return Fmt<WT>::wpc + 4; }
 
-template <int WT, int NT, int KS, int CPL, int U>
+// SWIGLU: the fused gate/up projection with the SwiGLU epilogue
+// ("Development Guide for Small AI Models (TinyLLaMA, etc.) Using C++",
+// §4.4: h = Swish(x W_gate) * (x W_up), Swish(z) = z sigma(z)).  A group then
+// covers U/2 row indices of both matrices: group rows u < U/2 come from the
+// gate, rows u >= U/2 from the up projection at the same indices, and after
+// the reduction each gate sum meets its up sum in a neighbouring lane.
+template <int WT, int NT, int KS, int CPL, int U, bool SWIGLU>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
 {
+    static_assert(!SWIGLU || U % 2 == 0, "a fused group pairs gate and up rows");
+    constexpr int RU = SWIGLU ? U / 2 : U;    // row indices per group
     constexpr int WPC = Fmt<WT>::wpc;
     constexpr int SC = lds_chunk_stride<WT>();
     constexpr int G = 4 / KS;                 // wave groups per workgroup
@@ -283,7 +299,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
     const uint8_t *const W = itm.w;
     const float *const X = itm.x;
     float *const Y = itm.y;
+    const uint8_t *const W2 = itm.w2;
     const uint32_t pitch = itm.pitch;
+    const uint32_t pitch2 = itm.pitch2;
     const uint32_t x_pitch = itm.x_pitch;
     const uint32_t y_pitch = itm.y_pitch;
     const int M = itm.M;
@@ -296,6 +314,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
     const int nchunk = a.nchunk;
     asm volatile("" ::"s"(W), "s"(X), "s"(Y), "s"(pitch), "s"(x_pitch), "s"(y_pitch), "s"(M),
                  "s"(n_groups), "s"(n_wg), "s"(iters), "s"(N), "s"(K), "s"(qoff), "s"(nchunk));
+    if constexpr (SWIGLU) asm volatile("" ::"s"(W2), "s"(pitch2));
     if ((int)blockIdx.x >= n_wg) return;
     const int nt_real = N < NT ? N : NT;
 
@@ -323,22 +342,26 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
         qoffs[j] = full ? (uint32_t)(qoff + c * 16) : OUT_OF_RANGE;
         soffs[j] = full ? (uint32_t)(2 * chunk_block<WT>(c)) : OUT_OF_RANGE;
     }
-    auto group_rsrc = [&](int gi) {
-        const int r0 = gi * U;
-        const int rows = gi < n_groups ? (M - r0 < U ? M - r0 : U) : 0;
-        const uint8_t *base = W + (uint64_t)(rows > 0 ? r0 : 0) * pitch;
-        const uint32_t nrec = rows > 0 ? (uint32_t)(rows - 1) * pitch + row_bytes : 0u;
+    auto group_rsrc = [&](int gi, const uint8_t *Wm, uint32_t pm) {
+        const int r0 = gi * RU;
+        const int rows = gi < n_groups ? (M - r0 < RU ? M - r0 : RU) : 0;
+        const uint8_t *base = Wm + (uint64_t)(rows > 0 ? r0 : 0) * pm;
+        const uint32_t nrec = rows > 0 ? (uint32_t)(rows - 1) * pm + row_bytes : 0u;
         return __builtin_amdgcn_make_buffer_rsrc((void *)base, 0, (int)nrec, BUFFER_FLAGS);
     };
     uint4 q[U][CPL];
     uint16_t sc[U][CPL];
     auto load_group = [&](int gi) {
-        const __amdgpu_buffer_rsrc_t res = group_rsrc(gi);
+        const __amdgpu_buffer_rsrc_t res1 = group_rsrc(gi, W, pitch);
+        const __amdgpu_buffer_rsrc_t res2 = SWIGLU ? group_rsrc(gi, W2, pitch2) : res1;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            const bool second = SWIGLU && u >= RU;
+            const __amdgpu_buffer_rsrc_t res = second ? res2 : res1;
+            const uint32_t pu = second ? pitch2 : pitch;
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
-                const uint32_t ro = (uint32_t)(u * pitch);
+                const uint32_t ro = (uint32_t)(u % RU) * pu;
                 q[u][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res, qoffs[j] + ro, 0, 0));
                 if (WT != W_F16)
                     sc[u][j] = __builtin_amdgcn_raw_buffer_load_b16(res, soffs[j] + ro, 0, 0);
@@ -347,9 +370,12 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
         if (f16_tail) {                // uniform; rare: waits for the loads here
 #pragma unroll
             for (int u = 0; u < U; ++u) {
+                const bool second = SWIGLU && u >= RU;
+                const __amdgpu_buffer_rsrc_t res = second ? res2 : res1;
+                const uint32_t pu = second ? pitch2 : pitch;
 #pragma unroll
                 for (int j = 0; j < CPL; ++j) {
-                    const uint32_t ro = (uint32_t)(u * pitch);
+                    const uint32_t ro = (uint32_t)(u % RU) * pu;
                     const int c = v + j * VL;
                     const bool partial = c * 8 < K && c * 8 + 8 > K;
                     uint32_t hv[8];
@@ -475,21 +501,38 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
 
         const bool owner = lane >= 32 && lane < 32 + V;
         if (KS == 1) {
-            if (owner && idx < U * NT && in_range) {
-                const int u = idx / NT, n = idx % NT;
-                const int r = g * U + u;
-                if (r < M && n < N) Y[(uint64_t)n * y_pitch + r] = tot;
+            if constexpr (SWIGLU) {
+                // value idx + V/2 (the up row of gate value idx) sits in the
+                // lane whose bit 0 differs: the top index bit is lane bit 0
+                const float up = partner<0>(tot, lane);
+                if (owner && idx < RU * NT && in_range) {
+                    const int u = idx / NT, n = idx % NT;
+                    const int r = g * RU + u;
+                    if (r < M && n < N) Y[(uint64_t)n * y_pitch + r] = swish(tot) * up;
+                }
+            } else {
+                if (owner && idx < U * NT && in_range) {
+                    const int u = idx / NT, n = idx % NT;
+                    const int r = g * U + u;
+                    if (r < M && n < N) Y[(uint64_t)n * y_pitch + r] = tot;
+                }
             }
         } else {
             float *buf = red[it & 1][wave];
             if (owner) buf[idx] = tot;
             __syncthreads();
-            if (ks == 0 && lane < U * NT && in_range) {
+            if (ks == 0 && lane < RU * NT && in_range) {
                 float s = 0.0f;
 #pragma unroll
                 for (int w2 = 0; w2 < KS; ++w2) s += red[it & 1][grp * KS + w2][lane];
+                if constexpr (SWIGLU) {
+                    float su = 0.0f;
+#pragma unroll
+                    for (int w2 = 0; w2 < KS; ++w2) su += red[it & 1][grp * KS + w2][lane + RU * NT];
+                    s = swish(s) * su;
+                }
                 const int u = lane / NT, n = lane % NT;
-                const int r = g * U + u;
+                const int r = g * RU + u;
                 if (r < M && n < N) Y[(uint64_t)n * y_pitch + r] = s;
             }
         }
@@ -507,7 +550,7 @@ constexpr bool fits()
 }
 
 template <int WT, int NT, int KS, int CPL>
-Kernel pick_u(int u)
+Kernel pick_u(int u, bool swiglu)
 {
     if constexpr (!fits<WT, NT, KS, CPL>()) {
         return nullptr;
@@ -515,53 +558,60 @@ Kernel pick_u(int u)
         // Several rows per wave group only while a lane holds few chunks;
         // otherwise the in-flight code registers would spill.
         constexpr int UW = (CPL > 2) ? 1 : (NT <= 1) ? 4 : (NT == 2 ? 2 : 1);
-        if (u == 1) return gemv_kernel<WT, NT, KS, CPL, 1>;
-        if (u == UW) return gemv_kernel<WT, NT, KS, CPL, UW>;
+        if (swiglu) {
+            // a fused group holds a gate row and an up row per row index
+            if (u == 2) return gemv_kernel<WT, NT, KS, CPL, 2, true>;
+            if constexpr (UW == 4)
+                if (u == 4) return gemv_kernel<WT, NT, KS, CPL, 4, true>;
+            return nullptr;
+        }
+        if (u == 1) return gemv_kernel<WT, NT, KS, CPL, 1, false>;
+        if (u == UW) return gemv_kernel<WT, NT, KS, CPL, UW, false>;
         return nullptr;
     }
 }
 
 template <int WT, int NT, int KS>
-Kernel pick_cpl(int cpl, int u)
+Kernel pick_cpl(int cpl, int u, bool swiglu)
 {
     switch (cpl) {
-    case 1: return pick_u<WT, NT, KS, 1>(u);
-    case 2: return pick_u<WT, NT, KS, 2>(u);
-    case 4: return pick_u<WT, NT, KS, 4>(u);
-    case 8: return pick_u<WT, NT, KS, 8>(u);
+    case 1: return pick_u<WT, NT, KS, 1>(u, swiglu);
+    case 2: return pick_u<WT, NT, KS, 2>(u, swiglu);
+    case 4: return pick_u<WT, NT, KS, 4>(u, swiglu);
+    case 8: return pick_u<WT, NT, KS, 8>(u, swiglu);
     default: return nullptr;
     }
 }
 
 template <int WT, int NT>
-Kernel pick_ks(int ks, int cpl, int u)
+Kernel pick_ks(int ks, int cpl, int u, bool swiglu)
 {
     switch (ks) {
-    case 1: return pick_cpl<WT, NT, 1>(cpl, u);
-    case 2: return pick_cpl<WT, NT, 2>(cpl, u);
-    case 4: return pick_cpl<WT, NT, 4>(cpl, u);
+    case 1: return pick_cpl<WT, NT, 1>(cpl, u, swiglu);
+    case 2: return pick_cpl<WT, NT, 2>(cpl, u, swiglu);
+    case 4: return pick_cpl<WT, NT, 4>(cpl, u, swiglu);
     default: return nullptr;
     }
 }
 
 template <int WT>
-Kernel pick_nt(int nt, int ks, int cpl, int u)
+Kernel pick_nt(int nt, int ks, int cpl, int u, bool swiglu)
 {
     switch (nt) {
-    case 1: return pick_ks<WT, 1>(ks, cpl, u);
-    case 2: return pick_ks<WT, 2>(ks, cpl, u);
-    case 4: return pick_ks<WT, 4>(ks, cpl, u);
-    case 8: return pick_ks<WT, 8>(ks, cpl, u);
+    case 1: return pick_ks<WT, 1>(ks, cpl, u, swiglu);
+    case 2: return pick_ks<WT, 2>(ks, cpl, u, swiglu);
+    case 4: return pick_ks<WT, 4>(ks, cpl, u, swiglu);
+    case 8: return pick_ks<WT, 8>(ks, cpl, u, swiglu);
     default: return nullptr;
     }
 }
 
-Kernel pick(int wt, const GemvConfig &c)
+Kernel pick(int wt, const GemvConfig &c, bool swiglu = false)
 {
     switch (wt) {
-    case W_Q4_0: return pick_nt<W_Q4_0>(c.nt, c.ks, c.cpl, c.u);
-    case W_Q8_0: return pick_nt<W_Q8_0>(c.nt, c.ks, c.cpl, c.u);
-    case W_F16:  return pick_nt<W_F16>(c.nt, c.ks, c.cpl, c.u);
+    case W_Q4_0: return pick_nt<W_Q4_0>(c.nt, c.ks, c.cpl, c.u, swiglu);
+    case W_Q8_0: return pick_nt<W_Q8_0>(c.nt, c.ks, c.cpl, c.u, swiglu);
+    case W_F16:  return pick_nt<W_F16>(c.nt, c.ks, c.cpl, c.u, swiglu);
     default: return nullptr;
     }
 }
@@ -693,6 +743,58 @@ hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t strea
         const int wpc = weights_per_chunk(type);
         const size_t lds = (size_t)64 * c.ks * (wpc + 4) * sizeof(float);
         hipLaunchKernelGGL(k, dim3((unsigned)wg_max, (unsigned)a.n_items), dim3(kThreads), lds, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        n0 += nb;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_gemv_swiglu(const WeightView &wg, const WeightView &wu, const ActView &x,
+                              const OutView &h, hipStream_t stream)
+{
+    const int type = wg.type;
+    const int64_t K = wg.K, M = wg.M, N = x.N;
+    if (M == 0 || N == 0) return hipSuccess;
+    for (int64_t n0 = 0; n0 < N;) {
+        int64_t nb = N - n0 < 8 ? N - n0 : 8;
+        GemvConfig c;
+        while (!gemv_config(type, K, 2 * M, nb, &c)) {
+            if (nb == 1) return hipErrorInvalidValue;
+            nb = nb > 4 ? 4 : nb > 2 ? 2 : 1;
+        }
+        // The plain configuration for the 2M rows of both matrices; a fused
+        // group holds at least one row index of each.
+        if (c.u < 2) c.u = 2;
+        const Kernel k = pick(type, c, true);
+        if (!k) return hipErrorInvalidValue;
+        const int groups_per_wg = 4 / c.ks;
+        const int ru = c.u / 2;
+        GemvArgs a = {};
+        a.n_items = 1;
+        a.N = (int32_t)nb;
+        a.K = (int32_t)K;
+        a.qoff = (type == W_F16) ? 0 : (int32_t)quant_offset(K);
+        a.nchunk = (int32_t)chunks_per_row(type, K);
+        GemvItem &it = a.item[0];
+        it.w = wg.base;
+        it.w2 = wu.base;
+        it.pitch = (uint32_t)wg.pitch;
+        it.pitch2 = (uint32_t)wu.pitch;
+        it.M = (int32_t)M;
+        it.x = static_cast<const float *>(x.data) + (uint64_t)n0 * x.pitch_elems;
+        it.x_pitch = (uint32_t)x.pitch_elems;
+        it.y = h.data + (uint64_t)n0 * h.pitch_elems;
+        it.y_pitch = (uint32_t)h.pitch_elems;
+        it.n_groups = (int32_t)((M + ru - 1) / ru);
+        int64_t wgs = (it.n_groups + groups_per_wg - 1) / groups_per_wg;
+        if (wgs > kMaxWorkgroups) wgs = kMaxWorkgroups;
+        it.wg_count = (int32_t)wgs;
+        const int64_t per_pass = (int64_t)groups_per_wg * wgs;
+        it.iters = (int32_t)((it.n_groups + per_pass - 1) / per_pass);
+        const int wpc = weights_per_chunk(type);
+        const size_t lds = (size_t)64 * c.ks * (wpc + 4) * sizeof(float);
+        hipLaunchKernelGGL(k, dim3((unsigned)wgs, 1u), dim3(kThreads), lds, stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         n0 += nb;

@@ -219,6 +219,27 @@ int qmm_gemv_batch(const qmm_gemv_item *items, int32_t count, void *stream)
     return status_of(qmm::launch_gemv_batch(tasks, count, static_cast<hipStream_t>(stream)));
 }
 
+int qmm_gemv_swiglu(const qmm_tensor *w_gate, const qmm_tensor *w_up, const qmm_tensor *x,
+                    qmm_tensor *h, void *stream)
+{
+    int rc = check_mul_mat(w_gate, x, h, QMM_TYPE_F32, 4);
+    if (rc) return rc;
+    rc = check_mul_mat(w_up, x, h, QMM_TYPE_F32, 4);
+    if (rc) return rc;
+    if (!(is_quant(w_gate->type) || w_gate->type == QMM_TYPE_F16)) return QMM_ERR_TYPE;
+    if (w_up->type != w_gate->type) return QMM_ERR_TYPE;
+    if (w_up->ne[0] != w_gate->ne[0] || w_up->ne[1] != w_gate->ne[1]) return QMM_ERR_SHAPE;
+    if (x->ne[1] > 8) return QMM_ERR_SHAPE;
+    if (x->ne[1] == 0 || w_gate->ne[1] == 0) return QMM_OK;
+    qmm::GemvConfig cfg;
+    if (!qmm::gemv_config(w_gate->type, w_gate->ne[0], 2 * w_gate->ne[1], 1, &cfg)) return QMM_ERR_UNSUPPORTED;
+    qmm::ActView xv{x->data, pitch_elems(x), x->ne[1]};
+    qmm::OutView hv{static_cast<float *>(h->data), pitch_elems(h)};
+    const qmm::WeightView gv = weight_view(w_gate), uv = weight_view(w_up);
+    if (!qmm::gemv_supported(gv, xv, hv) || !qmm::gemv_supported(uv, xv, hv)) return QMM_ERR_UNSUPPORTED;
+    return status_of(qmm::launch_gemv_swiglu(gv, uv, xv, hv, static_cast<hipStream_t>(stream)));
+}
+
 int qmm_gemm(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *stream)
 {
     int rc = check_mul_mat(w, x, y, QMM_TYPE_BF16, 16);

@@ -84,6 +84,12 @@ struct GemvTask {
 };
 hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t stream);
 
+// The fused gate/up projection with the SwiGLU epilogue:
+// h[n][m] = Swish(sum_k Wg'[m][k] x[n][k]) * sum_k Wu'[m][k] x[n][k].
+// wg and wu share the type, K and M.
+hipError_t launch_gemv_swiglu(const WeightView &wg, const WeightView &wu, const ActView &x,
+                              const OutView &h, hipStream_t stream);
+
 // The matrix-core GEMV for Q4_0 / Q8_0 weights (gemv_mfma.hip): whether its
 // LDS image of the activations fits for (K, N), and its launcher.
 bool gemv_mfma_supported(int type, int64_t K, int64_t N);

@@ -178,6 +178,23 @@ def test_gemv_batch_rejects(qmm_lib):
 
 
 @no_gpu
+def test_gemv_swiglu_rejects(qmm_lib):
+    U_ADDR = BASE + (3 << 32)
+    g, u, x, h = _w(), _w(addr=U_ADDR), _x(), _y()
+    call = lambda *d: B.call_raw("qmm_gemv_swiglu", *d)
+    assert call(None, u, x, h) == B.ERR_NULL
+    assert call(g, B.make_desc(B.Q8_0, 2048, 64, 2176, U_ADDR), x, h) == B.ERR_TYPE   # mixed types
+    assert call(g, _w(M=65, addr=U_ADDR), x, h) == B.ERR_SHAPE                       # mixed M
+    assert call(g, u, _x(N=9), _y(N=9)) == B.ERR_SHAPE                               # N > 8
+    assert call(g, u, _x(K=1024), h) == B.ERR_SHAPE                                  # K mismatch
+    assert call(g, u, x, _y(addr=U_ADDR + 64)) == B.ERR_ALIAS                        # h over w_up
+    assert call(g, u, x, _y(addr=W_ADDR)) == B.ERR_ALIAS                             # h over w_gate
+    assert call(g, u, x, _y(addr=X_ADDR)) == B.ERR_ALIAS                             # h over x
+    assert call(B.make_desc(B.F32, 2048, 64, 8192, W_ADDR), u, x, h) == B.ERR_TYPE
+    assert call(_w(M=0, addr=0), _w(M=0, addr=0), x, _y(M=0, addr=0)) == B.OK        # empty: no launch
+
+
+@no_gpu
 def test_empty_operands_enqueue_nothing(qmm_lib):
     # zero rows / zero tokens are valid and launch no kernel (so they are safe
     # without a GPU); NULL data is allowed for empty tensors

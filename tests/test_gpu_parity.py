@@ -228,6 +228,64 @@ def test_gemv_f16_tail_with_nan_padding(orc, K):
     _assert_tol(y, yref, a, 1e-4, 1e-6, f"gemv f16 tail K={K}")
 
 
+def _swiglu_tol(orc, gref, ga, uref, ua, h):
+    """Bound of the fused gate/up SwiGLU: the GEMV bound of each sum carried
+    through Swish (|Swish'| <= 1.1) and the product, plus binary32 rounding of
+    the epilogue (a few ulps of h)."""
+    eg = 1e-4 * ga + 1e-6
+    eu = 1e-4 * ua + 1e-6
+    sg = np.array([orc.swish(v) for v in gref.ravel()]).reshape(gref.shape)
+    return 1.1 * eg * (np.abs(uref) + eu) + np.abs(sg) * eu + 2.0 ** -20 * np.abs(h)
+
+
+SWIGLU_CASES = [
+    ("Q4_0", 5632, 2048, 1),       # the TinyLLaMA feed-forward gate/up pair
+    ("Q4_0", 37, 96, 1), ("Q4_0", 300, 1024, 2), ("Q4_0", 129, 2048, 3),
+    ("Q8_0", 513, 512, 8), ("Q8_0", 64, 4096, 5), ("Q8_0", 1, 32, 1),
+    ("F16", 77, 1003, 2), ("F16", 260, 2048, 4),
+]
+
+
+@pytest.mark.parametrize("case", SWIGLU_CASES, ids=lambda c: "%s-%dx%d-n%d" % c)
+def test_gemv_swiglu_parity(orc, case):
+    tname, M, K, N = case
+    _banner(f"gemv swiglu {tname} M={M} K={K} N={N}")
+    seed = 7 * M + K + N
+    wg, wu = WL.weights(seed, M, K), WL.weights(seed + 1, M, K)
+    x = WL.activations(seed + 2, N, K)
+    gref, ga = orc.mul_mat(TYPES[tname][1], _oracle_weight(orc, tname, wg), K, x)
+    uref, ua = orc.mul_mat(TYPES[tname][1], _oracle_weight(orc, tname, wu), K, x)
+    href = orc.swiglu(gref, uref)
+    pitch = (2 * K + 15) // 16 * 16 if tname == "F16" else None   # F16 rows 16-byte aligned
+    h = Q.gemv_swiglu(_gpu_weight(tname, wg, pitch), _gpu_weight(tname, wu, pitch),
+                      torch.from_numpy(x).to(DEV))
+    h = h.cpu().numpy().astype(np.float64)
+    tol = _swiglu_tol(orc, gref, ga, uref, ua, href)
+    err = np.abs(h - href)
+    assert np.isfinite(h).all()
+    assert (err <= tol).all(), f"worst err/tol {(err / tol).max():.3g}"
+
+
+def test_gemv_swiglu_saturated_and_separate_pitches(orc):
+    """|gate| in the hundreds (e^{-z} overflows for the negative ones), the
+    up matrix stored with a padded pitch, and rows and tokens that fill no
+    whole group."""
+    M, K, N = 203, 256, 3
+    _banner("gemv swiglu saturated, separate pitches")
+    wg, wu = WL.weights(41, M, K), WL.weights(42, M, K)
+    x = (WL.activations(43, N, K) * np.float32(400.0)).astype(np.float32)
+    gref, ga = orc.mul_mat(orc.Q8_0, orc.quantize(orc.Q8_0, wg), K, x)
+    uref, ua = orc.mul_mat(orc.Q8_0, orc.quantize(orc.Q8_0, wu), K, x)
+    assert np.abs(gref).max() > 100.0 and gref.min() < -88.0
+    href = orc.swiglu(gref, uref)
+    gw = Q.quantize(torch.from_numpy(wg).to(DEV), B.Q8_0)
+    uw = Q.quantize(torch.from_numpy(wu).to(DEV), B.Q8_0, pitch=B.row_size(B.Q8_0, K) + 48)
+    h = Q.gemv_swiglu(gw, uw, torch.from_numpy(x).to(DEV)).cpu().numpy().astype(np.float64)
+    tol = _swiglu_tol(orc, gref, ga, uref, ua, href)
+    assert np.isfinite(h).all()
+    assert (np.abs(h - href) <= tol).all()
+
+
 def test_gemv_decoder_layer_full_size(orc):
     """The seven projections of one TinyLLaMA-shaped layer, Q4_0, one token."""
     xs = [WL.activations(WL.seed(3, 7 + s), 1, k) for s, k in enumerate(WL.LAYER_X_K)]
