@@ -12,7 +12,8 @@ What it computes (the pages it follows are cited in ``qmm_oracle.h``):
   * the exact dequantized weights W';
   * MUL_MAT y[n][m] = sum_k W'[m][k] x[n][k] accumulated in binary64, with
     the magnitude sum a[n][m] = sum_k |W'[m][k] x[n][k]| used by tolerances;
-  * the SwiGLU epilogue h = Swish(g) * u of the fused gate/up projection.
+  * the SwiGLU epilogue h = Swish(g) * u of the fused gate/up projection;
+  * the GGUF-style block records (scale, then codes) <-> packed rows.
 """
 from __future__ import annotations
 
@@ -82,6 +83,12 @@ def lib() -> ctypes.CDLL:
         h.orc_mul_mat_pairs.argtypes = [ci, u8p, sz, i64, i64, vp, ci, i64, ci,
                                         i64p, i64p, i64, f64p, f64p]
         h.orc_mul_mat_pairs.restype = ci
+        h.orc_record_size.argtypes = [ci]
+        h.orc_record_size.restype = sz
+        h.orc_rows_to_records.argtypes = [ci, u8p, sz, i64, i64, u8p]
+        h.orc_rows_to_records.restype = ci
+        h.orc_records_to_rows.argtypes = [ci, u8p, i64, i64, u8p, sz]
+        h.orc_records_to_rows.restype = ci
         h.orc_swish.argtypes = [ctypes.c_double]
         h.orc_swish.restype = ctypes.c_double
         h.orc_swiglu_n.argtypes = [f64p, f64p, f64p, sz]
@@ -246,3 +253,34 @@ def swiglu(g, u) -> np.ndarray:
     lib().orc_swiglu_n(_ptr(g, ctypes.c_double), _ptr(u, ctypes.c_double),
                        _ptr(h, ctypes.c_double), g.size)
     return h
+
+
+# ---- block-record interchange --------------------------------------------
+
+def record_size(type_: int) -> int:
+    return int(lib().orc_record_size(type_))
+
+
+def rows_to_records(type_: int, rows, K: int) -> np.ndarray:
+    """Packed rows (M, pitch) uint8 -> records, uint8 (M * K/32 * record_size,)."""
+    rows = _c(rows, np.uint8)
+    M, pitch = rows.shape
+    out = np.zeros(M * (K // 32) * record_size(type_), np.uint8)
+    rc = lib().orc_rows_to_records(type_, _ptr(rows, ctypes.c_uint8), pitch, K, M,
+                                   _ptr(out, ctypes.c_uint8))
+    if rc != 0:
+        raise ValueError("orc_rows_to_records rejected its arguments")
+    return out
+
+
+def records_to_rows(type_: int, records, K: int, M: int, pitch: int | None = None) -> np.ndarray:
+    """Records -> packed rows (M, pitch) uint8, padding zero."""
+    records = _c(records, np.uint8).ravel()
+    pitch = row_size(type_, K) if pitch is None else pitch
+    assert records.size == M * (K // 32) * record_size(type_)
+    out = np.empty((M, pitch), np.uint8)
+    rc = lib().orc_records_to_rows(type_, _ptr(records, ctypes.c_uint8), K, M,
+                                   _ptr(out, ctypes.c_uint8), pitch)
+    if rc != 0:
+        raise ValueError("orc_records_to_rows rejected its arguments")
+    return out

@@ -361,3 +361,53 @@ void orc_swiglu_n(const double *g, const double *u, double *h, size_t n)
 {
     for (size_t i = 0; i < n; ++i) h[i] = orc_swish(g[i]) * u[i];
 }
+
+/* ---- block-record interchange ---------------------------------------------- */
+
+size_t orc_record_size(int type)
+{
+    if (type == ORC_Q4_0) return 2 + 16;
+    if (type == ORC_Q8_0) return 2 + 32;
+    return 0;
+}
+
+/* Offset of the codes inside a packed row and the code bytes of one block. */
+static int64_t code_offset(int64_t K) { return (K / 16 + 15) / 16 * 16; }
+static int64_t block_code_bytes(int type) { return type == ORC_Q4_0 ? 16 : 32; }
+
+int orc_rows_to_records(int type, const uint8_t *rows, size_t pitch, int64_t K, int64_t M,
+                        uint8_t *records)
+{
+    const size_t rec = orc_record_size(type);
+    if (rec == 0 || K <= 0 || K % 32 != 0 || M < 0 || pitch < orc_row_size(type, K)) return -1;
+    const int64_t nblk = K / 32, cb = block_code_bytes(type), qoff = code_offset(K);
+    for (int64_t m = 0; m < M; ++m) {
+        const uint8_t *row = rows + (size_t)m * pitch;
+        for (int64_t b = 0; b < nblk; ++b) {
+            uint8_t *out = records + ((size_t)m * nblk + b) * rec;
+            out[0] = row[2 * b];               /* scale, little endian */
+            out[1] = row[2 * b + 1];
+            for (int64_t i = 0; i < cb; ++i) out[2 + i] = row[qoff + b * cb + i];
+        }
+    }
+    return 0;
+}
+
+int orc_records_to_rows(int type, const uint8_t *records, int64_t K, int64_t M,
+                        uint8_t *rows, size_t pitch)
+{
+    const size_t rec = orc_record_size(type);
+    if (rec == 0 || K <= 0 || K % 32 != 0 || M < 0 || pitch < orc_row_size(type, K)) return -1;
+    const int64_t nblk = K / 32, cb = block_code_bytes(type), qoff = code_offset(K);
+    for (int64_t m = 0; m < M; ++m) {
+        uint8_t *row = rows + (size_t)m * pitch;
+        memset(row, 0, pitch);
+        for (int64_t b = 0; b < nblk; ++b) {
+            const uint8_t *in = records + ((size_t)m * nblk + b) * rec;
+            row[2 * b] = in[0];
+            row[2 * b + 1] = in[1];
+            for (int64_t i = 0; i < cb; ++i) row[qoff + b * cb + i] = in[2 + i];
+        }
+    }
+    return 0;
+}

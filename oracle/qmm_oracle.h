@@ -92,6 +92,23 @@ int orc_mul_mat_pairs(int type, const uint8_t *w, size_t pitch, int64_t K, int64
                       const int64_t *ms, const int64_t *ns, int64_t count,
                       double *y, double *a);
 
+/* ---- block-record interchange ------------------------------------------
+ * GGUF-style tensor data: the blocks of a quantized tensor as back-to-back
+ * records in row-major order (row 0's K/32 blocks, then row 1's, ...), each
+ * record the block's fp16 scale (2 bytes, little endian) followed by its
+ * codes: 16 bytes for Q4_0 (byte j = nib_j | nib_{j+16} << 4) or 32 int8
+ * bytes for Q8_0.  "Development Guide for Small AI Models (TinyLLaMA, etc.)
+ * Using C++", §6.1: one FP16 scale (2 bytes) then 32 4-bit values (16
+ * bytes); §3.2: tensor data is an aligned array after the tensor info.      */
+size_t orc_record_size(int type);        /* 18 (Q4_0), 34 (Q8_0), else 0 */
+/* Packed rows (row m at rows + m*pitch) -> M*K/32 records.  0 or -1.        */
+int orc_rows_to_records(int type, const uint8_t *rows, size_t pitch, int64_t K, int64_t M,
+                        uint8_t *records);
+/* Records -> packed rows, every byte of each row's pitch written (the
+ * padding with zeros).  0 or -1.                                            */
+int orc_records_to_rows(int type, const uint8_t *records, int64_t K, int64_t M,
+                        uint8_t *rows, size_t pitch);
+
 /* ---- SwiGLU epilogue of the fused gate/up projection ------------------
  * "Development Guide for Small AI Models (TinyLLaMA, etc.) Using C++", §4.4:
  * SwiGLU(x) = Swish(x W_gate) (elementwise *) (x W_up), with
