@@ -365,8 +365,13 @@ def prefill_leg(Q, WL, dev, args):
 
 
 def breakdown_leg(Q, WL, dev, args, gemv_bytes):
+    import ctypes
     import torch
+    from quantized_matmul_ggml_amd import binding as B
     out = {}
+
+    def stream_ptr():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
     def rotate(ws, x, y, n_per_graph):
         calls = [ws[i % len(ws)] for i in range(n_per_graph)]
@@ -407,7 +412,26 @@ def breakdown_leg(Q, WL, dev, args, gemv_bytes):
         out[f"q8_0_lm_head_32000x2048_n{n}"] = {
             "us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1),
             "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
-    del w4
+    # block-record interchange of the LM head (GGUF-style records <-> rows),
+    # 4 copies so the 139 MB each call moves is not cache-resident
+    recs = [Q.rows_to_records(w) for w in w4[:4]]
+    rows = [Q.Weight(torch.empty_like(w.data), w.type, w.K, w.M) for w in w4[:4]]
+    for name, fn in (("q8_0_records_to_rows_32000x2048",
+                      lambda i: B.lib().qmm_records_to_rows(ctypes.c_void_p(recs[i].data_ptr()),
+                                                            ctypes.byref(descs[i]), stream_ptr())),
+                     ("q8_0_rows_to_records_32000x2048",
+                      lambda i: B.lib().qmm_rows_to_records(ctypes.byref(srcs[i]),
+                                                            ctypes.c_void_p(recs[i].data_ptr()), stream_ptr()))):
+        descs = [r.desc() for r in rows]
+        srcs = [w.desc() for w in w4[:4]]
+        g = Graph(lambda: [fn(i) for i in range(4)])
+        ms, _ = timed(g, max(2, args.steps // 2), 2)
+        per = ms / 4
+        b = 2 * recs[0].numel()                 # record bytes read + row bytes written (equal)
+        out[name] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1),
+                     "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
+    assert torch.equal(rows[0].data, w4[0].data), "records -> rows must restore the packed rows"
+    del w4, recs, rows
     for k, v in out.items():
         log(f"{k}: {v}")
     return out

@@ -185,6 +185,36 @@ QMM_API int qmm_gemv_swiglu(const qmm_tensor *w_gate, const qmm_tensor *w_up,
  * dequantized weights within 1e-2 * sum_k |W'[m][k] x[n][k]| + 1e-5). */
 QMM_API int qmm_gemm(const qmm_tensor *w, const qmm_tensor *x_bf16, qmm_tensor *y_f32, void *stream);
 
+/* GGUF-style block records ("Development Guide for Small AI Models (TinyLLaMA,
+ * etc.) Using C++", §3.2: a GGUF file's tensor data is an aligned array;
+ * §6.1: a Q4_0 block is one FP16 scale (2 bytes) followed by 32 4-bit
+ * values (16 bytes)).  A record is the block's fp16 scale (little endian)
+ * followed by its codes: 16 bytes for Q4_0 (byte j holds element j in its
+ * low nibble and element j + 16 in its high nibble, offset binary: value =
+ * scale * (nibble - 8)) or 32 int8 bytes for Q8_0 (value = scale * code).
+ * The M * K/32 records of a tensor run back to back in row-major order:
+ * row 0's blocks 0 .. K/32 - 1, then row 1's, and so on.
+ *
+ * qmm_record_size: bytes of one record, 18 (Q4_0) or 34 (Q8_0); 0 for any
+ * other type.
+ *
+ * qmm_records_to_rows: fills the packed rows of dst_q (Q8_0 or Q4_0, ne =
+ * [K, M], the layout rules of qmm_quantize) from M * K/32 records at
+ * `records` (device memory, 16-byte aligned, caller-owned, not overlapping
+ * dst_q).  Every byte of each row's qmm_row_size bytes is written (the gap
+ * between the scales and the codes with zeros); bytes past it up to nb[1]
+ * are left as they are.  qmm_rows_to_records is the inverse: it writes the
+ * M * K/32 records of src_q to `records`.  Both are bit-exact and
+ * asynchronous on `stream`.
+ * Errors: QMM_ERR_NULL (no tensor, or NULL records for a non-empty tensor),
+ * QMM_ERR_TYPE (not Q8_0 / Q4_0), QMM_ERR_SHAPE / QMM_ERR_LAYOUT (the tensor
+ * rules), QMM_ERR_LAYOUT (records not 16-byte aligned), QMM_ERR_ALIAS
+ * (records overlap the rows), QMM_ERR_UNSUPPORTED (M * K/32 >= 2^31).
+ * An empty tensor enqueues nothing. */
+QMM_API size_t qmm_record_size(int32_t type);
+QMM_API int qmm_records_to_rows(const void *records, qmm_tensor *dst_q, void *stream);
+QMM_API int qmm_rows_to_records(const qmm_tensor *src_q, void *records, void *stream);
+
 /* Static text for a qmm_status value (never NULL). */
 QMM_API const char *qmm_strerror(int status);
 

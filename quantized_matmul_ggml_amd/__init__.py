@@ -6,8 +6,9 @@ layer over the C ABI of include/qmm.h, with torch supplying device memory and
 streams.
 """
 from .binding import (BF16, F16, F32, Q4_0, Q8_0, QmmError, Weight, dequantize, f16_weight,
-                      gemm, gemv, gemv_batch, gemv_swiglu, quantize, row_size, strerror)
+                      gemm, gemv, gemv_batch, gemv_swiglu, quantize, record_size, records_to_rows,
+                      row_size, rows_to_records, strerror)
 
 __all__ = ["BF16", "F16", "F32", "Q4_0", "Q8_0", "QmmError", "Weight", "dequantize",
-           "f16_weight", "gemm", "gemv", "gemv_batch", "gemv_swiglu", "quantize", "row_size",
-           "strerror"]
+           "f16_weight", "gemm", "gemv", "gemv_batch", "gemv_swiglu", "quantize", "record_size",
+           "records_to_rows", "row_size", "rows_to_records", "strerror"]

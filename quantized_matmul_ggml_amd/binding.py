@@ -26,7 +26,8 @@ OK, ERR_NULL, ERR_TYPE, ERR_SHAPE, ERR_LAYOUT, ERR_ALIAS, ERR_UNSUPPORTED, ERR_D
     0, -1, -2, -3, -4, -5, -6, -7
 
 EXPORTS = ("qmm_row_size", "qmm_quantize", "qmm_dequantize", "qmm_gemv", "qmm_gemv_batch",
-           "qmm_gemv_swiglu", "qmm_gemm", "qmm_strerror")
+           "qmm_gemv_swiglu", "qmm_gemm", "qmm_record_size", "qmm_records_to_rows",
+           "qmm_rows_to_records", "qmm_strerror")
 GEMV_BATCH_MAX = 8
 
 
@@ -70,6 +71,12 @@ def lib() -> ctypes.CDLL:
         h.qmm_gemm.argtypes = [P, P, P, ctypes.c_void_p]
         h.qmm_gemv_swiglu.argtypes = [P, P, P, P, ctypes.c_void_p]
         h.qmm_gemv_swiglu.restype = ctypes.c_int
+        h.qmm_record_size.argtypes = [ctypes.c_int32]
+        h.qmm_record_size.restype = ctypes.c_size_t
+        h.qmm_records_to_rows.argtypes = [ctypes.c_void_p, P, ctypes.c_void_p]
+        h.qmm_records_to_rows.restype = ctypes.c_int
+        h.qmm_rows_to_records.argtypes = [P, ctypes.c_void_p, ctypes.c_void_p]
+        h.qmm_rows_to_records.restype = ctypes.c_int
         h.qmm_gemv_batch.argtypes = [ctypes.POINTER(QmmGemvItem), ctypes.c_int32, ctypes.c_void_p]
         h.qmm_gemv_batch.restype = ctypes.c_int
         for f in ("qmm_quantize", "qmm_dequantize", "qmm_gemv", "qmm_gemm"):
@@ -224,6 +231,37 @@ def gemv_swiglu(w_gate: Weight, w_up: Weight, x: torch.Tensor, *, out: torch.Ten
     gd, ud, xd, hd = w_gate.desc(), w_up.desc(), _dense_desc(x, F32), _dense_desc(out, F32)
     _check(lib().qmm_gemv_swiglu(ctypes.byref(gd), ctypes.byref(ud), ctypes.byref(xd), ctypes.byref(hd),
                                  _stream(stream)), "qmm_gemv_swiglu")
+    return out
+
+
+def record_size(type_: int) -> int:
+    """Bytes of one GGUF-style block record (18 for Q4_0, 34 for Q8_0, else 0)."""
+    return int(lib().qmm_record_size(type_))
+
+
+def records_to_rows(records: torch.Tensor, type_: int, K: int, M: int, *, pitch: int | None = None,
+                    stream=None) -> Weight:
+    """Packed rows (a Weight) from M * K/32 block records (uint8 device tensor)."""
+    _need_gpu(records)
+    rs = row_size(type_, K)
+    pitch = rs if pitch is None else pitch
+    out = torch.zeros((M, pitch), dtype=torch.uint8, device=records.device)
+    wt = Weight(out, type_, K, M)
+    d = wt.desc()
+    _check(lib().qmm_records_to_rows(ctypes.c_void_p(records.data_ptr()), ctypes.byref(d), _stream(stream)),
+           "qmm_records_to_rows")
+    return wt
+
+
+def rows_to_records(w: Weight, *, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The M * K/32 block records of a quantized Weight (uint8 device tensor)."""
+    _need_gpu(w.data)
+    n = w.M * (w.K // 32) * record_size(w.type)
+    if out is None:
+        out = torch.empty(n, dtype=torch.uint8, device=w.data.device)
+    d = w.desc()
+    _check(lib().qmm_rows_to_records(ctypes.byref(d), ctypes.c_void_p(out.data_ptr()), _stream(stream)),
+           "qmm_rows_to_records")
     return out
 
 

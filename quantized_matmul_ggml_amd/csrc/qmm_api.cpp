@@ -240,6 +240,53 @@ int qmm_gemv_swiglu(const qmm_tensor *w_gate, const qmm_tensor *w_up, const qmm_
     return status_of(qmm::launch_gemv_swiglu(gv, uv, xv, hv, static_cast<hipStream_t>(stream)));
 }
 
+size_t qmm_record_size(int32_t type)
+{
+    return (size_t)qmm::record_size(type);
+}
+
+namespace {
+
+// Shared validation of the record conversions; on success *bytes is the
+// size of the record array.
+int check_records(const qmm_tensor *q, const void *records, uint64_t *bytes)
+{
+    int rc = check_tensor(q, 16);
+    if (rc) return rc;
+    if (!is_quant(q->type)) return QMM_ERR_TYPE;
+    const int64_t blocks = q->ne[1] * (q->ne[0] / 32);
+    if (blocks >= (1ll << 31)) return QMM_ERR_UNSUPPORTED;
+    *bytes = (uint64_t)blocks * (uint64_t)qmm::record_size(q->type);
+    if (*bytes == 0) return QMM_OK;
+    if (!records) return QMM_ERR_NULL;
+    if ((uintptr_t)records % 16 != 0) return QMM_ERR_LAYOUT;
+    uintptr_t lo, hi;
+    extent(q, &lo, &hi);
+    const uintptr_t r = (uintptr_t)records;
+    if (r < hi && lo < r + *bytes) return QMM_ERR_ALIAS;
+    return QMM_OK;
+}
+
+}  // namespace
+
+int qmm_records_to_rows(const void *records, qmm_tensor *dst, void *stream)
+{
+    uint64_t bytes = 0;
+    const int rc = check_records(dst, records, &bytes);
+    if (rc || bytes == 0) return rc;
+    return status_of(qmm::launch_records(weight_view(dst), static_cast<uint8_t *>(const_cast<void *>(records)),
+                                         true, static_cast<hipStream_t>(stream)));
+}
+
+int qmm_rows_to_records(const qmm_tensor *src, void *records, void *stream)
+{
+    uint64_t bytes = 0;
+    const int rc = check_records(src, records, &bytes);
+    if (rc || bytes == 0) return rc;
+    return status_of(qmm::launch_records(weight_view(src), static_cast<uint8_t *>(records), false,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int qmm_gemm(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *stream)
 {
     int rc = check_mul_mat(w, x, y, QMM_TYPE_BF16, 16);

@@ -97,6 +97,15 @@ hipError_t launch_gemv_mfma(const GemvTask *tasks, int count, hipStream_t stream
 // Grant a kernel more than the default dynamic LDS (once per size).
 hipError_t allow_dynamic_lds(const void *fn, int bytes);
 
+// GGUF-style block records (records.hip): bytes of one record (18 for
+// Q4_0, 34 for Q8_0, else 0), and the conversion between w's packed rows and
+// M * K/32 back-to-back records at `records` (16-byte aligned device memory):
+// records -> rows when to_rows (every byte of each row's row size is
+// written, the gap before the codes with zeros), rows -> records otherwise.
+// M * K/32 < 2^31.
+int record_size(int type);
+hipError_t launch_records(const WeightView &w, uint8_t *records, bool to_rows, hipStream_t stream);
+
 // The prefill GEMM (gemm.hip): whether the operand strides fit its 32-bit
 // per-tile offsets, and its launcher.
 bool gemm_supported(const WeightView &w, const ActView &x);

@@ -6,6 +6,7 @@ Validation runs on the host before any HIP call, so the rejected calls below
 never reach the GPU.  They use fake device addresses, so they only run where
 no GPU is visible (the GPU tests exercise the accepted paths with real
 memory)."""
+import ctypes
 import os
 import re
 import subprocess
@@ -192,6 +193,34 @@ def test_gemv_swiglu_rejects(qmm_lib):
     assert call(g, u, x, _y(addr=X_ADDR)) == B.ERR_ALIAS                             # h over x
     assert call(B.make_desc(B.F32, 2048, 64, 8192, W_ADDR), u, x, h) == B.ERR_TYPE
     assert call(_w(M=0, addr=0), _w(M=0, addr=0), x, _y(M=0, addr=0)) == B.OK        # empty: no launch
+
+
+def test_record_size_closed_forms(qmm_lib):
+    # one fp16 scale (2 bytes) plus the codes of 32 weights
+    assert qmm_lib.record_size(B.Q4_0) == 2 + 16
+    assert qmm_lib.record_size(B.Q8_0) == 2 + 32
+    for t in (B.F32, B.F16, B.BF16, 99, -1):
+        assert qmm_lib.record_size(t) == 0
+
+
+@no_gpu
+def test_record_conversions_reject(qmm_lib):
+    R_ADDR = BASE + (4 << 32)
+    q = _w()                                             # Q4_0 2048 x 64
+    for name, args in (("qmm_records_to_rows", lambda r, t: (r, t)),
+                       ("qmm_rows_to_records", lambda r, t: (t, r))):
+        call = lambda r, t: getattr(qmm_lib.lib(), name)(*[
+            ctypes.c_void_p(r) if isinstance(r, int) else (ctypes.byref(r) if r is not None else None)
+            for r in args(r, t)], None)
+        assert call(R_ADDR, None) == B.ERR_NULL
+        assert call(0, q) == B.ERR_NULL                  # NULL records, non-empty tensor
+        assert call(R_ADDR + 8, q) == B.ERR_LAYOUT       # records not 16-byte aligned
+        assert call(R_ADDR, B.make_desc(B.F16, 2048, 64, 4096, W_ADDR)) == B.ERR_TYPE
+        assert call(R_ADDR, _w(pitch=1160)) == B.ERR_LAYOUT
+        assert call(W_ADDR + 1152 * 63, q) == B.ERR_ALIAS   # records start inside the last row
+        assert call(W_ADDR - 1024, q) == B.ERR_ALIAS        # records run into the first row
+        assert call(R_ADDR, _w(M=0, addr=0)) == B.OK        # empty: nothing enqueued
+        assert call(0, _w(M=0, addr=0)) == B.OK
 
 
 @no_gpu
