@@ -29,6 +29,8 @@ _SO = os.environ.get("QMM_ORACLE_LIB") or os.path.join(_HERE, "libqmm_oracle.so"
 
 # Own type numbering (mirrors qmm_oracle.h, not the GPU library's enum).
 F32, F16, BF16, Q8_0, Q4_0 = 0, 1, 2, 3, 4
+# Quantization rules: the default ones, and the pages' symmetric Q4 rule.
+RULE_DEFAULT, RULE_Q4_SYM7 = 0, 1
 
 CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
           "-fPIC", "-shared", "-Wall", "-Wextra"]
@@ -75,6 +77,10 @@ def lib() -> ctypes.CDLL:
         h.orc_row_size.restype = sz
         h.orc_quantize_rows.argtypes = [ci, f32p, i64, i64, u8p, sz]
         h.orc_quantize_rows.restype = ci
+        h.orc_quantize_rows_rule.argtypes = [ci, ci, f32p, i64, i64, u8p, sz]
+        h.orc_quantize_rows_rule.restype = ci
+        h.orc_quantize_block_q4_sym7.argtypes = [f32p, u16p, u8p]
+        h.orc_quantize_block_q4_sym7.restype = None
         h.orc_dequantize_rows.argtypes = [ci, u8p, sz, i64, i64, f32p]
         h.orc_dequantize_rows.restype = ci
         h.orc_mul_mat_rows.argtypes = [ci, u8p, sz, i64, i64, vp, ci, i64, ci,
@@ -150,6 +156,10 @@ def quantize_block(type_: int, w32) -> tuple[int, np.ndarray]:
         q = np.zeros(32, np.uint8)
         lib().orc_quantize_block_q4_0(_ptr(w, ctypes.c_float), _ptr(sb, ctypes.c_uint16),
                                       _ptr(q, ctypes.c_uint8))
+    elif type_ == "q4_sym7":
+        q = np.zeros(32, np.uint8)
+        lib().orc_quantize_block_q4_sym7(_ptr(w, ctypes.c_float), _ptr(sb, ctypes.c_uint16),
+                                         _ptr(q, ctypes.c_uint8))
     else:
         raise ValueError("quantize_block: type must be Q8_0 or Q4_0")
     return int(sb[0]), q
@@ -159,14 +169,14 @@ def row_size(type_: int, K: int) -> int:
     return int(lib().orc_row_size(type_, K))
 
 
-def quantize(type_: int, w, pitch: int | None = None) -> np.ndarray:
+def quantize(type_: int, w, pitch: int | None = None, rule: int = RULE_DEFAULT) -> np.ndarray:
     """Quantize fp32 rows w (M x K) into packed rows: uint8 array (M, pitch)."""
     w = _c(w, np.float32)
     M, K = w.shape
     pitch = row_size(type_, K) if pitch is None else pitch
     out = np.zeros((M, pitch), np.uint8)
-    rc = lib().orc_quantize_rows(type_, _ptr(w, ctypes.c_float), K, M,
-                                 _ptr(out, ctypes.c_uint8), pitch)
+    rc = lib().orc_quantize_rows_rule(type_, rule, _ptr(w, ctypes.c_float), K, M,
+                                      _ptr(out, ctypes.c_uint8), pitch)
     if rc != 0:
         raise ValueError("orc_quantize_rows rejected its arguments")
     return out

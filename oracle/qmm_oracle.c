@@ -173,6 +173,24 @@ void orc_quantize_block_q4_0(const float w[32], uint16_t *scale_bits, uint8_t ni
     }
 }
 
+/* The pages' own Q4 rule ("A Complete Guide to llama.cpp and Customization
+ * with C++", §2.2): Delta = max|w| / 7, q in [-8, 7]; stored, like Q4_0, as
+ * the offset-binary nibble q + 8 with the fp16 Delta. */
+void orc_quantize_block_q4_sym7(const float w[32], uint16_t *scale_bits, uint8_t nib[32])
+{
+    const float s = block_amax(w) / 7.0f;
+    const uint16_t h = orc_f32_to_f16(s);
+    const float d = orc_f16_to_f32(h);
+    *scale_bits = h;
+    for (int i = 0; i < 32; ++i) {
+        if (d == 0.0f) { nib[i] = 8; continue; }
+        float q = roundf(w[i] / d);
+        if (q > 7.0f) q = 7.0f;
+        if (q < -8.0f) q = -8.0f;
+        nib[i] = (uint8_t)(q + 8.0f);
+    }
+}
+
 /* ------------------------------------------------------------------------
  * Row-planar packing (see qmm_oracle.h).
  * ------------------------------------------------------------------------ */
@@ -197,7 +215,14 @@ static int is_quant(int type) { return type == ORC_Q8_0 || type == ORC_Q4_0; }
 int orc_quantize_rows(int type, const float *w, int64_t K, int64_t M,
                       uint8_t *dst, size_t pitch)
 {
+    return orc_quantize_rows_rule(type, ORC_RULE_DEFAULT, w, K, M, dst, pitch);
+}
+
+int orc_quantize_rows_rule(int type, int rule, const float *w, int64_t K, int64_t M,
+                           uint8_t *dst, size_t pitch)
+{
     if (!is_quant(type) || K < 0 || M < 0 || (K % 32) != 0) return -1;
+    if (rule != ORC_RULE_DEFAULT && !(rule == ORC_RULE_Q4_SYM7 && type == ORC_Q4_0)) return -1;
     if (pitch < orc_row_size(type, K)) return -1;
     const int64_t nblk = K / 32;
     const size_t qoff = align16((size_t)K / 16u);
@@ -213,7 +238,10 @@ int orc_quantize_rows(int type, const float *w, int64_t K, int64_t M,
                 memcpy(row + qoff + (size_t)b * 32u, q, 32);
             } else {
                 uint8_t nib[32];
-                orc_quantize_block_q4_0(blk, &sb, nib);
+                if (rule == ORC_RULE_Q4_SYM7)
+                    orc_quantize_block_q4_sym7(blk, &sb, nib);
+                else
+                    orc_quantize_block_q4_0(blk, &sb, nib);
                 uint8_t *qb = row + qoff + (size_t)b * 16u;
                 for (int j = 0; j < 16; ++j)
                     qb[j] = (uint8_t)(nib[j] | (nib[j + 16] << 4));

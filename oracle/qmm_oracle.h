@@ -56,6 +56,16 @@ void orc_quantize_block_q8_0(const float w[32], uint16_t *scale_bits, int8_t q[3
 /* Q4_0: scale_bits = fp16(amax/8); nib_i = clamp(roundf(w_i/scale) + 8, 0, 15). */
 void orc_quantize_block_q4_0(const float w[32], uint16_t *scale_bits, uint8_t nib[32]);
 
+/* The pages' symmetric Q4 rule ("A Complete Guide to llama.cpp and
+ * Customization with C++", §2.2: Delta = max|w| / 7, q in [-8, 7]):
+ * scale_bits = fp16(amax/7); nib_i = clamp(roundf(w_i/scale), -8, 7) + 8.
+ * Same storage (and dequantization) as Q4_0.                               */
+void orc_quantize_block_q4_sym7(const float w[32], uint16_t *scale_bits, uint8_t nib[32]);
+
+/* Quantization rules of orc_quantize_rows_rule.                            */
+enum { ORC_RULE_DEFAULT = 0,   /* Q8_0: amax/127; Q4_0: amax/8 (offset 8) */
+       ORC_RULE_Q4_SYM7 = 1 }; /* Q4_0 storage, the pages' amax/7 rule    */
+
 /* ---- packed rows ------------------------------------------------------
  * Row-planar packing of one row of K weights (K % 32 == 0):
  *   bytes [0, 2*K/32)            fp16 scale of block b at offset 2b (little endian)
@@ -70,6 +80,10 @@ size_t orc_row_size(int type, int64_t K);
  * dst + m*pitch, pitch >= orc_row_size).  Returns 0, or -1 on bad args.     */
 int orc_quantize_rows(int type, const float *w, int64_t K, int64_t M,
                       uint8_t *dst, size_t pitch);
+
+/* The same with an explicit rule (ORC_RULE_Q4_SYM7 only with ORC_Q4_0).   */
+int orc_quantize_rows_rule(int type, int rule, const float *w, int64_t K, int64_t M,
+                           uint8_t *dst, size_t pitch);
 
 /* Expand rows of any weight type to exact binary32 values (M x K, dense).  */
 int orc_dequantize_rows(int type, const uint8_t *src, size_t pitch,
