@@ -119,6 +119,23 @@ QMM_API size_t qmm_row_size(int32_t type, int64_t ne0);
  * be finite with amax / 127 (Q8_0) or amax / 8 (Q4_0) below 65520. */
 QMM_API int qmm_quantize(const qmm_tensor *src_f32, qmm_tensor *dst_q, void *stream);
 
+/* Quantization rules of qmm_quantize_rule. */
+typedef enum {
+    QMM_QUANT_DEFAULT = 0,   /* the rules of qmm_quantize                          */
+    QMM_QUANT_Q4_AMAX7 = 1   /* Q4_0 storage, the pages' symmetric rule (below)    */
+} qmm_quant_rule;
+
+/* qmm_quantize with an explicit rule.  QMM_QUANT_Q4_AMAX7 is the rule of
+ * "A Complete Guide to llama.cpp and Customization with C++", §2.2
+ * (Delta = max|w| / 7, q in [-8, 7]): Delta = fp16(amax / 7) (RNE);
+ * q = round(w / Delta) half away from zero by one binary32 division by the
+ * stored Delta, clamped to [-8, 7]; stored as the Q4_0 nibble q + 8, so the
+ * result is an ordinary Q4_0 tensor (every kernel reads it unchanged) and
+ * |W' - w| <= Delta / 2 holds for every weight (no code clamps).  Only for
+ * dst type Q4_0 (else QMM_ERR_TYPE); an unknown rule returns
+ * QMM_ERR_UNSUPPORTED.  Inputs must be finite with amax / 7 below 65520. */
+QMM_API int qmm_quantize_rule(const qmm_tensor *src_f32, qmm_tensor *dst_q, int32_t rule, void *stream);
+
 /* Expand Q8_0 / Q4_0 / F16 rows to F32 (W' = Delta * code, exact in binary32;
  * "Development Guide ...", §6.2 step "Dequantization").
  * src ne = [K, M];  dst: F32 ne = [K, M].  Bit-exact. */

@@ -25,7 +25,7 @@ TYPE_NAMES = {F32: "F32", F16: "F16", BF16: "BF16", Q8_0: "Q8_0", Q4_0: "Q4_0"}
 OK, ERR_NULL, ERR_TYPE, ERR_SHAPE, ERR_LAYOUT, ERR_ALIAS, ERR_UNSUPPORTED, ERR_DEVICE = \
     0, -1, -2, -3, -4, -5, -6, -7
 
-EXPORTS = ("qmm_row_size", "qmm_quantize", "qmm_dequantize", "qmm_gemv", "qmm_gemv_batch",
+EXPORTS = ("qmm_row_size", "qmm_quantize", "qmm_quantize_rule", "qmm_dequantize", "qmm_gemv", "qmm_gemv_batch",
            "qmm_gemv_swiglu", "qmm_gemm", "qmm_record_size", "qmm_records_to_rows",
            "qmm_rows_to_records", "qmm_strerror")
 GEMV_BATCH_MAX = 8
@@ -66,6 +66,8 @@ def lib() -> ctypes.CDLL:
         h.qmm_row_size.argtypes = [ctypes.c_int32, ctypes.c_int64]
         h.qmm_row_size.restype = ctypes.c_size_t
         h.qmm_quantize.argtypes = [P, P, ctypes.c_void_p]
+        h.qmm_quantize_rule.argtypes = [P, P, ctypes.c_int32, ctypes.c_void_p]
+        h.qmm_quantize_rule.restype = ctypes.c_int
         h.qmm_dequantize.argtypes = [P, P, ctypes.c_void_p]
         h.qmm_gemv.argtypes = [P, P, P, ctypes.c_void_p]
         h.qmm_gemm.argtypes = [P, P, P, ctypes.c_void_p]
@@ -161,8 +163,13 @@ def _check(status: int, where: str):
         raise QmmError(status, where)
 
 
-def quantize(w: torch.Tensor, type_: int, *, pitch: int | None = None, stream=None) -> Weight:
-    """Quantize fp32 rows w (M, K) on the GPU into Q8_0 / Q4_0 rows."""
+QUANT_DEFAULT, QUANT_Q4_AMAX7 = 0, 1
+
+
+def quantize(w: torch.Tensor, type_: int, *, pitch: int | None = None, rule: int = QUANT_DEFAULT,
+             stream=None) -> Weight:
+    """Quantize fp32 rows w (M, K) on the GPU into Q8_0 / Q4_0 rows (rule:
+    QUANT_DEFAULT, or QUANT_Q4_AMAX7 for the symmetric amax/7 Q4 rule)."""
     _need_gpu(w)
     M, K = w.shape
     rs = row_size(type_, K)
@@ -172,7 +179,8 @@ def quantize(w: torch.Tensor, type_: int, *, pitch: int | None = None, stream=No
         out[:, rs:].zero_()
     wt = Weight(out, type_, K, M)
     src, dst = _dense_desc(w, F32), wt.desc()
-    _check(lib().qmm_quantize(ctypes.byref(src), ctypes.byref(dst), _stream(stream)), "qmm_quantize")
+    _check(lib().qmm_quantize_rule(ctypes.byref(src), ctypes.byref(dst), rule, _stream(stream)),
+           "qmm_quantize_rule")
     return wt
 
 

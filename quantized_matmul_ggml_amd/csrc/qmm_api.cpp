@@ -131,6 +131,12 @@ size_t qmm_row_size(int32_t type, int64_t ne0)
 
 int qmm_quantize(const qmm_tensor *src, qmm_tensor *dst, void *stream)
 {
+    return qmm_quantize_rule(src, dst, QMM_QUANT_DEFAULT, stream);
+}
+
+int qmm_quantize_rule(const qmm_tensor *src, qmm_tensor *dst, int32_t rule, void *stream)
+{
+    if (rule != QMM_QUANT_DEFAULT && rule != QMM_QUANT_Q4_AMAX7) return QMM_ERR_UNSUPPORTED;
     if (!src || !dst) return QMM_ERR_NULL;
     int rc = check_tensor(src, 4);
     if (rc) return rc;
@@ -140,11 +146,13 @@ int qmm_quantize(const qmm_tensor *src, qmm_tensor *dst, void *stream)
     if (src->ne[0] != dst->ne[0] || src->ne[1] != dst->ne[1]) return QMM_ERR_SHAPE;
     if (src->ne[0] % 32 != 0) return QMM_ERR_SHAPE;
     if (overlaps(dst, src)) return QMM_ERR_ALIAS;
+    if (rule == QMM_QUANT_Q4_AMAX7 && dst->type != QMM_TYPE_Q4_0) return QMM_ERR_TYPE;
     const qmm::WeightView d = weight_view(dst);
     return status_of(qmm::launch_quantize(static_cast<const float *>(src->data), pitch_elems(src),
                                           src->ne[0], src->ne[1],
                                           static_cast<uint8_t *>(dst->data), d.pitch, dst->type,
-                                          static_cast<hipStream_t>(stream)));
+                                          static_cast<hipStream_t>(stream),
+                                          rule == QMM_QUANT_Q4_AMAX7));
 }
 
 int qmm_dequantize(const qmm_tensor *src, qmm_tensor *dst, void *stream)

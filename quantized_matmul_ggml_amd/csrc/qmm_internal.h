@@ -68,8 +68,10 @@ inline bool gemv_supported(const WeightView &w, const ActView &x, const OutView 
 
 // Launchers (return hipSuccess or the launch error).  Shapes are validated by
 // the caller; every launcher accepts M == 0 / N == 0 as a no-op.
+// q4_amax7: the pages' symmetric Q4 rule (Delta = amax / 7) instead of amax / 8.
 hipError_t launch_quantize(const float *src, uint64_t src_pitch_elems, int64_t K, int64_t M,
-                           uint8_t *dst, uint64_t dst_pitch, int type, hipStream_t stream);
+                           uint8_t *dst, uint64_t dst_pitch, int type, hipStream_t stream,
+                           bool q4_amax7 = false);
 hipError_t launch_dequantize(const uint8_t *src, uint64_t src_pitch, int64_t K, int64_t M,
                              int type, float *dst, uint64_t dst_pitch_elems, hipStream_t stream);
 hipError_t launch_gemv(const WeightView &w, const ActView &x, const OutView &y,

@@ -11,6 +11,10 @@
 // The library is built without fast-math, so '/' is the IEEE division and
 // the fp16 / bf16 conversions round to nearest even: the codes are bit-exact.
 //
+// A second Q4 rule is the pages' own (A Complete Guide to llama.cpp ...,
+// §2.2: Delta = max|w| / 7, q_i in [-8, 7]): the same steps with 7 as the
+// divisor, stored the same way (clamp(q + 8, 0, 15) = clamp(q, -8, 7) + 8).
+//
 // These kernels run once per weight at load time, so they favour clarity:
 // one thread per 32-weight block.
 #include "qmm_internal.h"
@@ -28,7 +32,7 @@ __device__ inline float f16_bits_to_f32(uint16_t h)
     return static_cast<float>(__builtin_bit_cast(_Float16, h));
 }
 
-template <int TYPE>
+template <int TYPE, int DIV>
 __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__ src,
                                                        uint64_t src_pitch, int64_t K, int64_t M,
                                                        uint8_t *__restrict__ dst, uint64_t dst_pitch)
@@ -50,7 +54,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const float *__restrict__
             v[j] = w[j];
             amax = fmaxf(amax, fabsf(v[j]));
         }
-        const float s = amax / (TYPE == W_Q8_0 ? 127.0f : 8.0f);
+        const float s = amax / (float)DIV;
         const uint16_t sb = f32_to_f16_bits(s);
         const float d = f16_bits_to_f32(sb);
         uint8_t *row = dst + r * dst_pitch;
@@ -143,15 +147,19 @@ unsigned grid_for(int64_t items)
 }  // namespace
 
 hipError_t launch_quantize(const float *src, uint64_t src_pitch_elems, int64_t K, int64_t M,
-                           uint8_t *dst, uint64_t dst_pitch, int type, hipStream_t stream)
+                           uint8_t *dst, uint64_t dst_pitch, int type, hipStream_t stream,
+                           bool q4_amax7)
 {
     const int64_t items = M * (K / 32);
     if (items == 0) return hipSuccess;
     if (type == W_Q8_0)
-        hipLaunchKernelGGL(quantize_kernel<W_Q8_0>, dim3(grid_for(items)), dim3(256), 0, stream,
+        hipLaunchKernelGGL((quantize_kernel<W_Q8_0, 127>), dim3(grid_for(items)), dim3(256), 0, stream,
+                           src, src_pitch_elems, K, M, dst, dst_pitch);
+    else if (q4_amax7)
+        hipLaunchKernelGGL((quantize_kernel<W_Q4_0, 7>), dim3(grid_for(items)), dim3(256), 0, stream,
                            src, src_pitch_elems, K, M, dst, dst_pitch);
     else
-        hipLaunchKernelGGL(quantize_kernel<W_Q4_0>, dim3(grid_for(items)), dim3(256), 0, stream,
+        hipLaunchKernelGGL((quantize_kernel<W_Q4_0, 8>), dim3(grid_for(items)), dim3(256), 0, stream,
                            src, src_pitch_elems, K, M, dst, dst_pitch);
     return hipGetLastError();
 }

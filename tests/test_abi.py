@@ -157,6 +157,18 @@ def test_quantize_and_dequantize_reject(qmm_lib):
 
 
 @no_gpu
+def test_quantize_rule_rejects(qmm_lib):
+    src = B.make_desc(B.F32, 2048, 64, 8192, X_ADDR)
+    call = lambda s, d, r: qmm_lib.lib().qmm_quantize_rule(
+        ctypes.byref(s) if s is not None else None, ctypes.byref(d) if d is not None else None, r, None)
+    assert call(src, _w(), 2) == B.ERR_UNSUPPORTED                       # unknown rule
+    assert call(src, _w(), -1) == B.ERR_UNSUPPORTED
+    assert call(src, _w(type_=B.Q8_0), 1) == B.ERR_TYPE                  # amax/7 is a Q4 rule
+    assert call(None, _w(), 1) == B.ERR_NULL
+    assert call(B.make_desc(B.F32, 2048, 0, 8192, 0), _w(M=0, addr=0), 1) == B.OK
+
+
+@no_gpu
 def test_gemv_batch_rejects(qmm_lib):
     item = lambda **kw: (_w(**{k: v for k, v in kw.items() if k in ("type_", "K", "M", "addr")}), _x(K=kw.get("K", 2048), addr=kw.get("xaddr", X_ADDR)), _y(M=kw.get("M", 64), addr=kw.get("yaddr", Y_ADDR)))
     a = item()

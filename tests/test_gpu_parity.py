@@ -139,6 +139,49 @@ def test_quantize_hand_worked_blocks(tname, fixture):
             assert np.array_equal(got[i, 16:48].view(np.int8).astype(np.int64), c["codes"]), c["name"]
 
 
+@pytest.mark.parametrize("shape", QUANT_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_quantize_q4_amax7_bit_exact(orc, shape):
+    """The pages' symmetric rule (amax / 7) against the oracle, byte for byte."""
+    M, K = shape
+    _banner(f"quantize q4 amax7 {M}x{K}")
+    w = _adversarial(M, K, 500 + M + K)
+    ref = orc.quantize(orc.Q4_0, w, rule=orc.RULE_Q4_SYM7)
+    got = Q.quantize(torch.from_numpy(w).to(DEV), B.Q4_0, rule=B.QUANT_Q4_AMAX7)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.data.cpu().numpy(), ref)
+
+
+def test_quantize_q4_amax7_hand_worked():
+    _banner("quantize q4 amax7 hand-worked")
+    cases = read_blocks("q4_sym7_blocks.txt")
+    w = np.stack([c["w"] for c in cases])
+    got = Q.quantize(torch.from_numpy(w).to(DEV), B.Q4_0, rule=B.QUANT_Q4_AMAX7).data.cpu().numpy()
+    for i, c in enumerate(cases):
+        assert int(got[i, 0]) | (int(got[i, 1]) << 8) == c["scale"], c["name"]
+        assert got[i, 16:32].tobytes() == c["bytes"], c["name"]
+
+
+def test_q4_amax7_weights_through_gemv_and_gemm(orc):
+    """amax/7 rows are ordinary Q4_0 rows: the GEMV and the GEMM read them
+    unchanged (the Wdown shape, one token and 300 tokens)."""
+    M, K = 2048, 5632
+    _banner("q4 amax7 weights: gemv + gemm")
+    w = WL.weights(WL.seed(3, 6), M, K)
+    packed = orc.quantize(orc.Q4_0, w, rule=orc.RULE_Q4_SYM7)
+    wt = Q.quantize(torch.from_numpy(w).to(DEV), B.Q4_0, rule=B.QUANT_Q4_AMAX7)
+    assert np.array_equal(wt.data.cpu().numpy(), packed)
+    x = WL.activations(WL.seed(3, 10), 1, K)
+    yref, a = orc.mul_mat(orc.Q4_0, packed, K, x)
+    y = Q.gemv(wt, torch.from_numpy(x).to(DEV)).cpu().numpy()
+    _assert_tol(y, yref, a, 1e-4, 1e-6, "gemv amax7")
+    xb = WL.round_bf16_bits(WL.activations(WL.seed(3, 11), 300, K))
+    ms = np.repeat(np.arange(0, M, 37), 4)            # sampled rows ...
+    ns = np.tile(np.array([0, 1, 150, 299]), ms.size // 4)   # ... and tokens
+    yr, ar = orc.mul_mat_pairs(orc.Q4_0, packed, K, xb, ms, ns, x_bf16_bits=True)
+    yg = Q.gemm(wt, WL.bf16_bits_to_torch(xb, DEV)).cpu().numpy()
+    assert (np.abs(yg[ns, ms] - yr) <= 1e-2 * ar + 1e-5).all()
+
+
 def test_quantize_full_size_weights(orc):
     _banner("quantize full-size LM head (Q8_0) and decoder layer (Q4_0)")
     w = WL.weights(WL.seed(4, 0), WL.VOCAB, WL.HIDDEN)
