@@ -218,23 +218,22 @@ def main():
     value = variants[head]["gbs"]
 
     # dominant kernel of the step: the batched gate/up GEMV (2 x 5632 x 2048,
-    # 52 % of a layer's bytes), timed per launch
-    gate_launches = [lambda L=L: Q.gemv_batch([(L[n], xs[2], ys[n]) for n in ("wgate", "wup")])
-                     for L in layers]
-    durs = []
-    for _ in range(max(1, args.steps // 4)):
-        durs += per_launch_ms(gate_launches)
-    kern_ms = sum(durs) / len(durs)
+    # 52 % of a layer's bytes).  Its average launch duration: HIP events on
+    # the launch stream around replays of a graph of the 22 layers' launches
+    # back to back (each launch reads weights no other launch has touched
+    # since the previous replay), divided by the launches.
+    gate_graph = Graph(lambda: [Q.gemv_batch([(L[n], xs[2], ys[n]) for n in ("wgate", "wup")])
+                                for L in layers])
+    g_ms, _ = timed(gate_graph, args.steps, args.warmup)
+    kern_ms = g_ms / len(layers)
     kern_bytes = gemv_bytes(layers[0]["wgate"], 1) + gemv_bytes(layers[0]["wup"], 1)
     achieved = kern_bytes / (kern_ms * 1e-3) / 1e9
     log(f"gate/up batched GEMV {kern_ms * 1e3:.2f} us/launch  {achieved:.0f} GB/s")
 
-    # the same pair fused with its SwiGLU epilogue, per launch
-    swiglu_launches = [lambda L=L: Q.gemv_swiglu(L["wgate"], L["wup"], xs[2], out=h_ffn) for L in layers]
-    durs = []
-    for _ in range(max(1, args.steps // 4)):
-        durs += per_launch_ms(swiglu_launches)
-    sw_ms = sum(durs) / len(durs)
+    # the same pair fused with its SwiGLU epilogue, timed the same way
+    sw_graph = Graph(lambda: [Q.gemv_swiglu(L["wgate"], L["wup"], xs[2], out=h_ffn) for L in layers])
+    s_ms, _ = timed(sw_graph, args.steps, args.warmup)
+    sw_ms = s_ms / len(layers)
     sw_bytes = kern_bytes - 4 * WL.HIDDEN - 4 * WL.FFN
     sw_gbs = sw_bytes / (sw_ms * 1e-3) / 1e9
     log(f"gate/up SwiGLU fused GEMV {sw_ms * 1e3:.2f} us/launch  {sw_gbs:.0f} GB/s")
