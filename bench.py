@@ -358,9 +358,17 @@ def prefill_leg(Q, WL, dev, args):
     durs = per_launch_ms([lambda: Q.gemm(w, x, out=y)] * 20)
     kern = sum(durs) / len(durs)
     log(f"prefill GEMM {per * 1e3:.1f} us  {tf:.0f} TFLOP/s (per-launch events {kern * 1e3:.1f} us)")
+    # the same product with F16 weights (converted, not dequantized, to bf16)
+    wf = Q.f16_weight(WL.weights_device(WL.seed(5, 0), M, K, dev).to(torch.float16))
+    gf = Graph(lambda: [Q.gemm(wf, x, out=y) for _ in range(reps)])
+    ms_f, _ = timed(gf, max(2, args.steps // 2), 2)
+    tf_f = flops / (ms_f / reps * 1e-3) / 1e12
+    log(f"prefill GEMM, F16 weights {ms_f / reps * 1e3:.1f} us  {tf_f:.0f} TFLOP/s")
     return {"workload": "Q4_0 5632 x 2048 x bf16 2048 x 512 -> f32", "us": round(per * 1e3, 2),
             "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
-            "avg_launch_us": round(kern * 1e3, 2), "flops": flops}
+            "avg_launch_us": round(kern * 1e3, 2), "flops": flops,
+            "f16_weights": {"us": round(ms_f / reps * 1e3, 2), "tflops": round(tf_f, 1),
+                            "frac_of_bf16_peak": round(tf_f / BF16_PEAK_TFLOPS, 4)}}
 
 
 def breakdown_leg(Q, WL, dev, args, gemv_bytes):

@@ -195,11 +195,12 @@ QMM_API int qmm_gemv_swiglu(const qmm_tensor *w_gate, const qmm_tensor *w_up,
                             const qmm_tensor *x_f32, qmm_tensor *h_f32, void *stream);
 
 /* Prefill GEMM ("No Python! ...", §6: C_ij = sum_k A_ik B_kj, with many tokens
- * per step).  w: Q4_0 or Q8_0, ne = [K, M];  x: BF16 ne = [K, N], any N >= 0;
+ * per step).  w: Q4_0, Q8_0 or F16 (F16 with K % 32 == 0, else
+ * QMM_ERR_UNSUPPORTED), ne = [K, M];  x: BF16 ne = [K, N], any N >= 0;
  * y: F32 ne = [M, N], must not overlap w or x.  Weight tiles are dequantized
- * to bfloat16 (round to nearest even) and multiplied on the bf16 matrix cores
- * with binary32 accumulation (results agree with the exact sum of the
- * dequantized weights within 1e-2 * sum_k |W'[m][k] x[n][k]| + 1e-5). */
+ * (F16: converted) to bfloat16 (round to nearest even) and multiplied on the
+ * bf16 matrix cores with binary32 accumulation (results agree with the exact
+ * sum of the weights within 1e-2 * sum_k |W'[m][k] x[n][k]| + 1e-5). */
 QMM_API int qmm_gemm(const qmm_tensor *w, const qmm_tensor *x_bf16, qmm_tensor *y_f32, void *stream);
 
 /* GGUF-style block records ("Development Guide for Small AI Models (TinyLLaMA,

@@ -50,6 +50,7 @@ constexpr int SCALE_GROUP_STEPS = 8;      // steps whose scales are staged toget
 constexpr int SCALE_GROUP_BLOCKS = 2 * SCALE_GROUP_STEPS;
 constexpr int W_PAIRS = 4;                // pairs of K-steps of weight codes in flight
 static_assert(2 * W_PAIRS == SCALE_GROUP_STEPS, "the producer loop unrolls over both with one index");
+constexpr int F16_PAIRS = 2;              // pairs of K-steps of F16 weights in flight (4x the bytes of Q4_0)
 constexpr int THREADS = 512;
 
 struct GemmArgs {
@@ -146,10 +147,19 @@ __device__ inline uint16_t group_scale(const uint32_t (&sreg)[2][2], bool use0, 
     return (uint16_t)((use0 ? v0 : v1) >> (16 * h));
 }
 
+// Two fp16 weights (one dword) to two bf16 (nearest even): each half widens
+// exactly to fp32, then one v_cvt_pk_bf16_f32.
+__device__ inline uint32_t f16x2_to_bf16x2(uint32_t w)
+{
+    const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+    const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    return pack_bf16(lo, hi);
+}
+
 template <int WT>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
 {
-    constexpr int QB = (WT == W_Q4_0) ? 16 : 32;     // code bytes per block
+    constexpr int QB = (WT == W_Q4_0) ? 16 : 32;     // code bytes per block (quantized rows)
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     // STAGES x [weights BM x LDS_STRIDE | tokens BN x LDS_STRIDE] bf16
 
@@ -181,8 +191,72 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
     // row, so that one instruction touches few cache lines: the vector L1
     // serves about one line per two cycles whatever part of it is used.
 
-    if (wave >= 4) {
-        // ---------------- producers: weights ----------------
+    if constexpr (WT == W_F16) {
+      if (wave >= 4) {
+        // ---------------- producers: F16 weights ----------------
+        // Same ring protocol as the quantized producers below; the weights
+        // are converted to bf16 instead of dequantized.  A pair of K-steps
+        // spans 256 bytes of a row (four 32-blocks); load v of a row covers
+        // block v of the pair with 4 lanes of 16 bytes (lane q4 holds
+        // k = 8 q4 .. 8 q4 + 7 of the block), so an instruction touches 64
+        // contiguous bytes of each of 16 rows.  Each lane serves two rows.
+        const int pw = wave - 4;
+        const int q4 = lane & 3;
+        const int64_t rows = a.M - m0 < BM ? a.M - m0 : BM;
+        const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(a.w + (uint64_t)m0 * a.pitch), 0,
+            (int)(uint32_t)((rows - 1) * a.pitch + 2 * a.K), BUFFER_FLAGS);
+        const int wrow0 = 32 * pw + 2 * (lane >> 2);
+        const uint32_t roff[2] = {(uint32_t)(wrow0 * a.pitch) + 16 * q4,
+                                  (uint32_t)((wrow0 + 1) * a.pitch) + 16 * q4};
+        uint16_t *fdst0 = lds + wrow0 * LDS_STRIDE + 8 * q4;
+        struct FPair { u32x4 q[2][4]; };   // [row wrow0 + i][block v of the pair]
+        FPair fr[F16_PAIRS];
+        auto load_f = [&](FPair &fp, int pair) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    fp.q[i][v] = __builtin_amdgcn_raw_buffer_load_b128(
+                        wres, roff[i] + (uint32_t)pair * 256 + 64 * v, 0, 0);
+        };
+        // step p = 2 pair + s holds blocks 2 s and 2 s + 1 of the pair, i.e.
+        // K-blocks 2 p and 2 p + 1; a block past K is written as zeros (its
+        // bytes belong to the next row or to the padding)
+        auto produce_f = [&](int p, const FPair &fp) {
+            const int s = p & 1;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int bb = 0; bb < 2; ++bb) {
+                    const bool live = 2 * p + bb < nblk;
+                    const u32x4 q = fp.q[i][2 * s + bb];
+                    u32x4 o;
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) o[d] = live ? f16x2_to_bf16x2(q[d]) : 0u;
+                    *reinterpret_cast<u32x4 *>(fdst0 + (p % STAGES) * STAGE_ELEMS + i * LDS_STRIDE + 32 * bb) = o;
+                }
+        };
+#pragma unroll
+        for (int j = 0; j < F16_PAIRS; ++j) {
+            load_f(fr[j], j);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int p0 = 0; p0 < steps; p0 += 2 * F16_PAIRS) {
+            static_for<2 * F16_PAIRS>([&](auto U) {
+                constexpr int u = decltype(U)::value;
+                const int p = p0 + u;
+                if (p < steps) produce_f(p, fr[(u / 2) % F16_PAIRS]);
+                if (u % 2 == 1) load_f(fr[(u / 2) % F16_PAIRS], p / 2 + F16_PAIRS);
+                if (p >= 1 && p < steps) asm volatile("s_waitcnt lgkmcnt(4)\n\ts_barrier" ::: "memory");
+            });
+        }
+        if (steps > 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // barrier steps - 1
+        return;
+      }
+    } else {
+      if (wave >= 4) {
+        // ---------------- producers: quantized weights ----------------
         //  * codes: 4 lanes per row covering two steps (four blocks), 16 rows
         //    per load; of the two loads a lane makes per pair of steps, one
         //    holds a block of the first step and one of the second (the
@@ -285,6 +359,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
         }
         if (steps > 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // barrier steps - 1
         return;
+      }
     }
 
     // ---------------- consumers: tokens + matrix cores ----------------
@@ -475,6 +550,7 @@ hipError_t launch_gemm(const WeightView &w, const ActView &x, const OutView &y,
     const unsigned tiles = (unsigned)((w.M + BM - 1) / BM) * (unsigned)a.n_tiles;
     if (w.type == W_Q4_0) return launch_typed<W_Q4_0>(a, tiles, stream);
     if (w.type == W_Q8_0) return launch_typed<W_Q8_0>(a, tiles, stream);
+    if (w.type == W_F16) return launch_typed<W_F16>(a, tiles, stream);
     return hipErrorInvalidValue;
 }
 

@@ -127,13 +127,16 @@ def test_gemv_rejects(qmm_lib, case, expect):
 
 @no_gpu
 @pytest.mark.parametrize("case,expect", [
-    ("x_f32", B.ERR_TYPE), ("w_f16", B.ERR_TYPE), ("x_unaligned_pitch", B.ERR_LAYOUT),
+    ("x_f32", B.ERR_TYPE), ("w_f32", B.ERR_TYPE), ("w_f16_k_not_32", B.ERR_UNSUPPORTED),
+    ("x_unaligned_pitch", B.ERR_LAYOUT),
     ("x_misaligned", B.ERR_LAYOUT), ("alias", B.ERR_ALIAS), ("k_mismatch", B.ERR_SHAPE),
 ])
 def test_gemm_rejects(qmm_lib, case, expect):
     w, x, y = _w(), _x(B.BF16, N=512), _y(N=512)
     if case == "x_f32": x = _x(B.F32, N=512)
-    elif case == "w_f16": w = B.make_desc(B.F16, 2048, 64, 4096, W_ADDR)
+    elif case == "w_f32": w = B.make_desc(B.F32, 2048, 64, 8192, W_ADDR)
+    elif case == "w_f16_k_not_32":
+        w = B.make_desc(B.F16, 2056, 64, 4112 + 16 - 4112 % 16, W_ADDR); x = _x(B.BF16, K=2056, N=512)
     elif case == "x_unaligned_pitch": x.nb[1] = 2048 * 2 + 2
     elif case == "x_misaligned": x.data = X_ADDR + 8
     elif case == "alias": y.data = X_ADDR

@@ -435,14 +435,18 @@ GEMM_CASES = [
     ("Q4_0", 1, 32, 1), ("Q4_0", 130, 96, 7), ("Q4_0", 128, 64, 128), ("Q4_0", 257, 2048, 129),
     ("Q4_0", 200, 5632, 300), ("Q4_0", 64, 2048 + 32, 64), ("Q8_0", 130, 2048, 65),
     ("Q8_0", 33, 96, 257),
+    ("F16", 130, 2048, 65), ("F16", 33, 96, 257), ("F16", 200, 2048 + 32, 300), ("F16", 1, 32, 1),
 ]
 
 
 def _gemm_inputs(orc, tname, M, K, N, seed):
     w = WL.weights(seed, M, K)
     xbits = WL.round_bf16_bits(WL.activations(seed + 1, N, K))
-    packed = orc.quantize(TYPES[tname][1], w)
-    wt = B.Weight(torch.from_numpy(packed).to(DEV), TYPES[tname][0], K, M)
+    packed = _oracle_weight(orc, tname, w)
+    if tname == "F16":
+        wt = B.Weight(torch.from_numpy(packed.view(np.float16)).to(DEV), B.F16, K, M)
+    else:
+        wt = B.Weight(torch.from_numpy(packed).to(DEV), TYPES[tname][0], K, M)
     return packed, xbits, wt
 
 
@@ -462,7 +466,7 @@ def test_gemm_parity(orc, case):
     _assert_tol(y, ydiag, a, 1.1 * K * 2.0 ** -24, 1e-7, f"gemm bf16-weight diagnostic {case}")
 
 
-@pytest.mark.parametrize("tname", ["Q4_0", "Q8_0"])
+@pytest.mark.parametrize("tname", ["Q4_0", "Q8_0", "F16"])
 def test_gemm_strided_operands(orc, tname):
     """Padded weight pitch (padding filled with 0xFF bytes, which as scales or
     codes would poison the result if read), x rows with a larger pitch, y rows
@@ -471,12 +475,15 @@ def test_gemm_strided_operands(orc, tname):
     _banner(f"gemm strided {tname}")
     w = WL.weights(31, M, K)
     xbits = WL.round_bf16_bits(WL.activations(32, N, K))
-    packed = orc.quantize(TYPES[tname][1], w)
+    packed = _oracle_weight(orc, tname, w)
     yref, a = orc.mul_mat(TYPES[tname][1], packed, K, xbits, x_bf16_bits=True)
     rs = packed.shape[1]
-    padded = np.full((M, rs + 80), 0xFF, np.uint8)
+    padded = np.full((M, rs + 80), 0xFF, np.uint8)      # F16: 0xFFFF halves are NaN
     padded[:, :rs] = packed
-    wt = B.Weight(torch.from_numpy(padded).to(DEV), TYPES[tname][0], K, M)
+    if tname == "F16":
+        wt = B.Weight(torch.from_numpy(padded.view(np.float16)).to(DEV), B.F16, K, M)
+    else:
+        wt = B.Weight(torch.from_numpy(padded).to(DEV), TYPES[tname][0], K, M)
     xfull = torch.full((N, K + 24), -3.0e38, dtype=torch.bfloat16, device=DEV)
     xfull[:, :K] = WL.bf16_bits_to_torch(xbits, DEV)
     buf, yv = _guarded_out(N, M, pad_cols=5)
