@@ -13,7 +13,9 @@ What it computes (the pages it follows are cited in ``qmm_oracle.h``):
   * MUL_MAT y[n][m] = sum_k W'[m][k] x[n][k] accumulated in binary64, with
     the magnitude sum a[n][m] = sum_k |W'[m][k] x[n][k]| used by tolerances;
   * the SwiGLU epilogue h = Swish(g) * u of the fused gate/up projection;
-  * the GGUF-style block records (scale, then codes) <-> packed rows.
+  * the GGUF-style block records (scale, then codes) <-> packed rows;
+  * the integer-activation MUL_MAT (activations quantized to Q8_0 blocks,
+    block dot products in integers).
 """
 from __future__ import annotations
 
@@ -89,6 +91,9 @@ def lib() -> ctypes.CDLL:
         h.orc_mul_mat_pairs.argtypes = [ci, u8p, sz, i64, i64, vp, ci, i64, ci,
                                         i64p, i64p, i64, f64p, f64p]
         h.orc_mul_mat_pairs.restype = ci
+        h.orc_mul_mat_q8act_rows.argtypes = [ci, u8p, sz, i64, i64, u8p, sz, i64, i64, i64,
+                                             f64p, f64p]
+        h.orc_mul_mat_q8act_rows.restype = ci
         h.orc_record_size.argtypes = [ci]
         h.orc_record_size.restype = sz
         h.orc_rows_to_records.argtypes = [ci, u8p, sz, i64, i64, u8p]
@@ -294,3 +299,24 @@ def records_to_rows(type_: int, records, K: int, M: int, pitch: int | None = Non
     if rc != 0:
         raise ValueError("orc_records_to_rows rejected its arguments")
     return out
+
+
+# ---- integer-activation MUL_MAT --------------------------------------------
+
+def mul_mat_q8act(type_: int, packed, K: int, xq, rows: tuple[int, int] | None = None):
+    """y[n][m] = sum_b Delta_w Delta_x sum_i q_i qx_i (integer block sums,
+    binary64 over blocks) and a = sum_b |block term|; xq: (N, pitch) Q8_0 rows
+    of the activations.  Returns (y, a), each (N, M) float64."""
+    packed = _c(packed, np.uint8)
+    xq = _c(xq, np.uint8)
+    M, pitch = packed.shape
+    N, x_pitch = xq.shape
+    m0, m1 = (0, M) if rows is None else rows
+    y = np.zeros((N, M), np.float64)
+    a = np.zeros((N, M), np.float64)
+    rc = lib().orc_mul_mat_q8act_rows(type_, _ptr(packed, ctypes.c_uint8), pitch, K, M,
+                                      _ptr(xq, ctypes.c_uint8), x_pitch, N, m0, m1,
+                                      _ptr(y, ctypes.c_double), _ptr(a, ctypes.c_double))
+    if rc != 0:
+        raise ValueError("orc_mul_mat_q8act_rows rejected its arguments")
+    return y, a

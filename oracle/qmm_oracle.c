@@ -439,3 +439,47 @@ int orc_records_to_rows(int type, const uint8_t *records, int64_t K, int64_t M,
     }
     return 0;
 }
+
+/* ---- integer-activation MUL_MAT ------------------------------------------- */
+
+/* Integer code i of block b of a packed row: Q8_0 the int8 code, Q4_0 the
+ * nibble minus 8 (the pages' q in [-8, 7]). */
+static int block_code(int type, const uint8_t *row, int64_t K, int64_t b, int i)
+{
+    const size_t qoff = align16((size_t)K / 16u);
+    if (type == ORC_Q8_0) return (int8_t)row[qoff + (size_t)b * 32u + (size_t)i];
+    const uint8_t byte = row[qoff + (size_t)b * 16u + (size_t)(i & 15)];
+    return ((i < 16) ? (byte & 0x0F) : (byte >> 4)) - 8;
+}
+
+static double block_scale(const uint8_t *row, int64_t b)
+{
+    return (double)orc_f16_to_f32((uint16_t)(row[2 * b] | (row[2 * b + 1] << 8)));
+}
+
+int orc_mul_mat_q8act_rows(int type, const uint8_t *w, size_t pitch, int64_t K, int64_t M,
+                           const uint8_t *xq, size_t x_pitch, int64_t N,
+                           int64_t m0, int64_t m1, double *y, double *a)
+{
+    if (!is_quant(type) || K < 0 || K % 32 != 0 || M < 0 || N < 0) return -1;
+    if (pitch < orc_row_size(type, K) || x_pitch < orc_row_size(ORC_Q8_0, K)) return -1;
+    if (m0 < 0 || m1 > M || m0 > m1) return -1;
+    for (int64_t m = m0; m < m1; ++m) {
+        const uint8_t *wr = w + (size_t)m * pitch;
+        for (int64_t n = 0; n < N; ++n) {
+            const uint8_t *xr = xq + (size_t)n * x_pitch;
+            double acc = 0.0, aacc = 0.0;
+            for (int64_t b = 0; b < K / 32; ++b) {
+                int64_t s = 0;
+                for (int i = 0; i < 32; ++i)
+                    s += (int64_t)block_code(type, wr, K, b, i) * block_code(ORC_Q8_0, xr, K, b, i);
+                const double t = block_scale(wr, b) * block_scale(xr, b) * (double)s;
+                acc += t;
+                aacc += fabs(t);
+            }
+            y[n * M + m] = acc;
+            a[n * M + m] = aacc;
+        }
+    }
+    return 0;
+}

@@ -106,6 +106,20 @@ int orc_mul_mat_pairs(int type, const uint8_t *w, size_t pitch, int64_t K, int64
                       const int64_t *ms, const int64_t *ns, int64_t count,
                       double *y, double *a);
 
+/* ---- integer-activation MUL_MAT ----------------------------------------
+ * "A Complete Guide to llama.cpp and Customization with C++", §2.2: with the
+ * activations quantized per block as well, x_i ~= Delta_x * qx_i, the block
+ * dot product is y ~= Delta * Delta_x * sum_i q_i qx_i, whose sum is pure
+ * integer arithmetic.  Weights: Q8_0 (q = code) or Q4_0 (q = nibble - 8);
+ * activations: Q8_0 rows of the same K (quantized by orc_quantize_rows, the
+ * Q8_0 rule).  y[n][m] = sum_b Delta_w(m,b) Delta_x(n,b) S_b with the
+ * integer S_b = sum_i q_i qx_i exact in int64 and the block terms summed in
+ * binary64 (every term is exact there: at most 11 + 11 + 20 bits);
+ * a[n][m] = sum_b |Delta_w Delta_x S_b|.  Rows [m0, m1) only.             */
+int orc_mul_mat_q8act_rows(int type, const uint8_t *w, size_t pitch, int64_t K, int64_t M,
+                           const uint8_t *xq, size_t x_pitch, int64_t N,
+                           int64_t m0, int64_t m1, double *y, double *a);
+
 /* ---- block-record interchange ------------------------------------------
  * GGUF-style tensor data: the blocks of a quantized tensor as back-to-back
  * records in row-major order (row 0's K/32 blocks, then row 1's, ...), each
