@@ -395,6 +395,20 @@ def breakdown_leg(Q, WL, dev, args, gemv_bytes):
     out["q8_0_gemv_512x512_n1"] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1)}
     del w1
 
+    # Q4_0 5632 x 2048 (the FFN gate / up shape), one token: fp32 activations
+    # against Q8_0 activations (the integer path), 48 copies (311 MB)
+    w3 = [Q.quantize(WL.weights_device(WL.seed(3, 4, r), WL.FFN, WL.HIDDEN, dev), Q.Q4_0) for r in range(48)]
+    x3 = WL.activations_device(WL.seed(3, 9), 1, WL.HIDDEN, dev)
+    xq3 = Q.quantize(x3, Q.Q8_0)
+    y3 = torch.empty((1, WL.FFN), device=dev)
+    for name, xx, xbytes in (("q4_0_gemv_5632x2048_n1", x3, 4 * WL.HIDDEN),
+                             ("q4_0_gemv_5632x2048_n1_int8_activations", xq3, xq3.data.numel())):
+        per = rotate(w3, xx, y3, 96)
+        b = WL.FFN * Q.row_size(Q.Q4_0, WL.HIDDEN) + xbytes + 4 * WL.FFN
+        out[name] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1),
+                     "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
+    del w3
+
     # fp16 5632 x 2048, one token: 48 copies (1.1 GB) so HBM is read
     w2 = []
     for r in range(48):
@@ -417,6 +431,16 @@ def breakdown_leg(Q, WL, dev, args, gemv_bytes):
         per = rotate(w4, x4, y4, 32)
         b = gemv_bytes(w4[0], n)
         out[f"q8_0_lm_head_32000x2048_n{n}"] = {
+            "us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1),
+            "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
+    # the integer-activation path: activations quantized to Q8_0 blocks, block
+    # dot products in int8 (bytes: weights + Q8_0 activations + fp32 outputs)
+    for n in (1, 8):
+        xq4 = Q.quantize(WL.activations_device(WL.seed(4, 1), n, WL.HIDDEN, dev), Q.Q8_0)
+        y4 = torch.empty((n, WL.VOCAB), device=dev)
+        per = rotate(w4, xq4, y4, 32)
+        b = w4[0].M * Q.row_size(Q.Q8_0, WL.HIDDEN) + xq4.data.numel() + 4 * n * WL.VOCAB
+        out[f"q8_0_lm_head_32000x2048_n{n}_int8_activations"] = {
             "us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1),
             "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
     # block-record interchange of the LM head (GGUF-style records <-> rows),

@@ -154,6 +154,18 @@ QMM_API int qmm_dequantize(const qmm_tensor *src, qmm_tensor *dst_f32, void *str
  * Weights are read once from HBM and dequantized in registers; binary32
  * multiply-add; the accumulation order is unspecified (results agree with
  * the exact sum within 1e-4 * sum_k |W'[m][k] x[n][k]| + 1e-6). */
+/* Integer activations ("A Complete Guide to llama.cpp ...", §2.2: with x
+ * quantized per block too, x_i ~= Delta_x qx_i, the block dot product is
+ * Delta Delta_x sum_i q_i qx_i, an integer sum): when x is Q8_0 (ne = [K, N],
+ * the activations quantized with qmm_quantize, 1 <= N <= 8), w must be Q8_0
+ * or Q4_0 (else QMM_ERR_TYPE) and
+ *   y[n][m] = sum_b Delta_w(m,b) Delta_x(n,b) sum_i q_i qx_i
+ * with each block's integer sum exact (int8 dot products into int32) and
+ * the block terms summed in binary32 (|y - exact| <= (K/16 + 16) 2^-24
+ * sum_b |block term|).  This approximates the fp32-activation product by the
+ * quantization of x: |y - sum_k W' x| <= sum_k |W'_k| Delta_x / 2.  K up to
+ * 16384 (Q8_0) or 32768 (Q4_0), else QMM_ERR_UNSUPPORTED; tokens go in
+ * passes over the weights of up to 8 (fewer for long rows). */
 QMM_API int qmm_gemv(const qmm_tensor *w, const qmm_tensor *x_f32, qmm_tensor *y_f32, void *stream);
 
 /* Most GEMVs one qmm_gemv_batch call takes. */

@@ -202,12 +202,19 @@ def f16_weight(w16: torch.Tensor) -> Weight:
     return Weight(w16, F16, w16.shape[1], w16.shape[0])
 
 
-def gemv(w: Weight, x: torch.Tensor, *, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """y (N, M) fp32 = x (N, K) fp32 times W'^T; 1 <= N <= 8."""
-    _need_gpu(w.data, x)
+def gemv(w: Weight, x, *, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y (N, M) fp32 = x (N, K) times W'^T; 1 <= N <= 8.  x is fp32 (N, K), or
+    a Q8_0 Weight of N rows (activations quantized with quantize()) for the
+    integer-activation path."""
+    if isinstance(x, Weight):
+        _need_gpu(w.data, x.data)
+        n, dev, xd = x.M, x.data.device, x.desc()
+    else:
+        _need_gpu(w.data, x)
+        n, dev, xd = x.shape[0], x.device, _dense_desc(x, F32)
     if out is None:
-        out = torch.empty((x.shape[0], w.M), dtype=torch.float32, device=x.device)
-    wd, xd, yd = w.desc(), _dense_desc(x, F32), _dense_desc(out, F32)
+        out = torch.empty((n, w.M), dtype=torch.float32, device=dev)
+    wd, yd = w.desc(), _dense_desc(out, F32)
     _check(lib().qmm_gemv(ctypes.byref(wd), ctypes.byref(xd), ctypes.byref(yd), _stream(stream)),
            "qmm_gemv")
     return out

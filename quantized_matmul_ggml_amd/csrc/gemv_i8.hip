@@ -1,0 +1,342 @@
+// gemv_i8.hip -- the integer-activation decode GEMV.
+//
+// A Complete Guide to llama.cpp and Customization with C++, §2.2: when the
+// activations are quantized per block as well, x_i ~= Delta_x * qx_i, the
+// dot product of a block is y ~= Delta * Delta_x * sum_i q_i qx_i, and the
+// sum is integer arithmetic.  Here the activations are Q8_0 rows (quantized
+// by qmm_quantize, the weights' Q8_0 rule), the weights Q4_0 (q = nibble - 8)
+// or Q8_0, and each block's integer sum is four-way int8 dot products
+// (v_dot4c_i32_i8) accumulated exactly in int32; only the per-block term
+// Delta * Delta_x * S (Delta * Delta_x is exact in binary32: two 11-bit
+// significands) and the sum over blocks round.
+//
+// The mapping is the one of gemv.hip (16-byte weight chunks, KS waves per
+// row, U rows per wave group, the same wave reduction), with two changes:
+//  * a lane's activations are its blocks' int8 codes and scales, loaded
+//    straight from the Q8_0 rows (32 bytes per Q4_0 block, coalesced across
+//    the lanes), with no LDS staging;
+//  * a Q4_0 nibble n enters the dot product as the int8 value n (it is below
+//    128) and the block sum is corrected by -8 * sum_i qx_i, an integer
+//    computed once per activation block.
+#include "qmm_internal.h"
+#include "wave_reduce.h"
+
+namespace qmm {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxWorkgroups = 1024;
+
+struct I8Args {
+    const uint8_t *w;
+    const uint8_t *xq;     // Q8_0 rows of the activations
+    float *y;
+    uint32_t pitch;        // bytes between weight rows
+    uint32_t x_pitch;      // bytes between activation rows
+    uint32_t y_pitch;      // elements between output rows
+    int32_t M;
+    int32_t N;
+    int32_t K;
+    int32_t qoff;          // code offset inside a row (the same for both operands: same K)
+    int32_t nchunk;        // 16-byte chunks of weight codes per row
+    int32_t n_groups;
+    int32_t wg_count;
+    int32_t iters;
+};
+
+// Per 16-byte chunk of weight codes: Q4_0 one block (32 weights, 8 dwords of
+// activation codes), Q8_0 half a block (16 weights, 4 dwords).
+template <int WT> struct I8Fmt;
+template <> struct I8Fmt<W_Q4_0> { static constexpr int xd = 8; };
+template <> struct I8Fmt<W_Q8_0> { static constexpr int xd = 4; };
+
+template <int WT>
+__device__ inline int chunk_block(int c) { return WT == W_Q4_0 ? c : c / 2; }
+
+// sum_i w_i qx_i over one chunk, w_i the stored code (Q4_0: nibble 0..15).
+// Q4_0 byte j holds elements j (low nibble) and j + 16 (high nibble), so
+// dword d of the chunk pairs with activation dwords d and 4 + d.
+template <int WT>
+__device__ inline int chunk_idot(const uint4 q, const uint32_t *xv)
+{
+    const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+    int s = 0;
+    if constexpr (WT == W_Q4_0) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            s = __builtin_amdgcn_sdot4((int)(wd[d] & 0x0F0F0F0Fu), (int)xv[d], s, false);
+            s = __builtin_amdgcn_sdot4((int)((wd[d] >> 4) & 0x0F0F0F0Fu), (int)xv[4 + d], s, false);
+        }
+    } else {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) s = __builtin_amdgcn_sdot4((int)wd[d], (int)xv[d], s, false);
+    }
+    return s;
+}
+
+template <int WT, int NT, int KS, int CPL, int U>
+__global__ __launch_bounds__(kThreads) void gemv_i8_kernel(const I8Args a)
+{
+    constexpr int XD = I8Fmt<WT>::xd;
+    constexpr int G = 4 / KS;
+    constexpr int VL = 64 * KS;
+    constexpr int V = pow2_ceil(U * NT);
+    static_assert(V <= 64, "too many partial sums per lane");
+    __shared__ float red[2][4][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave / KS;
+    const int ks = wave % KS;
+    const int v = ks * 64 + lane;
+
+    const uint8_t *const W = a.w;
+    const uint8_t *const XQ = a.xq;
+    float *const Y = a.y;
+    const uint32_t pitch = a.pitch, x_pitch = a.x_pitch, y_pitch = a.y_pitch;
+    const int M = a.M, N = a.N, K = a.K, qoff = a.qoff, nchunk = a.nchunk;
+    const int n_groups = a.n_groups, n_wg = a.wg_count, iters = a.iters;
+    const int nt_real = N < NT ? N : NT;
+
+    int g = (int)blockIdx.x * G + grp;
+    const int gstep = n_wg * G;
+
+    // ---- activations: this lane's blocks, codes and scales, from the Q8_0
+    // rows; chunks past the row (and tokens past N) read zeros ----
+    const uint32_t x_row_bytes = (uint32_t)(qoff + K);
+    uint32_t xc[NT][CPL][XD];
+    uint16_t xs[NT][CPL];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(XQ + (uint64_t)(n < nt_real ? n : 0) * x_pitch), 0,
+            (int)(n < nt_real ? x_row_bytes : 0u), BUFFER_FLAGS);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            const int c = v + j * VL;
+            const bool in_row = c < nchunk;
+            const int b = chunk_block<WT>(c);
+            const uint32_t coff = in_row ? (uint32_t)(qoff + 32 * b + (WT == W_Q8_0 ? 16 * (c & 1) : 0))
+                                         : OUT_OF_RANGE;
+#pragma unroll
+            for (int h = 0; h < XD / 4; ++h) {
+                const auto t = __builtin_amdgcn_raw_buffer_load_b128(xr, coff + 16 * h, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xc[n][j][4 * h + e] = t[e];
+            }
+            xs[n][j] = __builtin_amdgcn_raw_buffer_load_b16(xr, in_row ? (uint32_t)(2 * b) : OUT_OF_RANGE, 0, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- weights: as gemv.hip (buffer resource per row group, unconditional loads) ----
+    const int code_bytes = (WT == W_Q4_0) ? K / 2 : K;
+    const uint32_t row_bytes = (uint32_t)(qoff + code_bytes);
+    uint32_t qoffs[CPL], soffs[CPL];
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int c = v + j * VL;
+        const bool in_row = c < nchunk;
+        qoffs[j] = in_row ? (uint32_t)(qoff + 16 * c) : OUT_OF_RANGE;
+        soffs[j] = in_row ? (uint32_t)(2 * chunk_block<WT>(c)) : OUT_OF_RANGE;
+    }
+    uint4 q[U][CPL];
+    uint16_t sc[U][CPL];
+    auto load_group = [&](int gi) {
+        const int r0 = gi * U;
+        const int rows = gi < n_groups ? (M - r0 < U ? M - r0 : U) : 0;
+        const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(W + (uint64_t)(rows > 0 ? r0 : 0) * pitch), 0,
+            (int)(rows > 0 ? (uint32_t)(rows - 1) * pitch + row_bytes : 0u), BUFFER_FLAGS);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const uint32_t ro = (uint32_t)u * pitch;
+                q[u][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res, qoffs[j] + ro, 0, 0));
+                sc[u][j] = __builtin_amdgcn_raw_buffer_load_b16(res, soffs[j] + ro, 0, 0);
+            }
+    };
+    load_group(g);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // per activation block: its scale as a float and (Q4_0) -8 * sum of its codes
+    float dx[NT][CPL];
+    int xb[NT][CPL];
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            dx[n][j] = (float)__builtin_bit_cast(_Float16, xs[n][j]);
+            int s = 0;
+            if constexpr (WT == W_Q4_0) {
+#pragma unroll
+                for (int d = 0; d < XD; ++d) s = __builtin_amdgcn_sdot4((int)xc[n][j][d], 0x01010101, s, false);
+            }
+            xb[n][j] = -8 * s;
+        }
+
+    for (int it = 0; it < iters; ++it, g += gstep) {
+        uint4 qc[U][CPL];
+        uint16_t scc[U][CPL];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) { qc[u][j] = q[u][j]; scc[u][j] = sc[u][j]; }
+        load_group(g + gstep);     // past the last group: reads nothing
+
+        float part[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) part[i] = 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < CPL; ++j) {
+                const float dw = (float)__builtin_bit_cast(_Float16, scc[u][j]);
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    const int s = chunk_idot<WT>(qc[u][j], xc[n][j]) + xb[n][j];
+                    part[u * NT + n] = fmaf(dw * dx[n][j], (float)s, part[u * NT + n]);
+                }
+            }
+        const float tot = WaveReduce<V, 0>::run(part, lane);
+        const int idx = value_index<V>(lane);
+        const bool in_range = g < n_groups;
+        const bool owner = lane >= 32 && lane < 32 + V;
+        if (KS == 1) {
+            if (owner && idx < U * NT && in_range) {
+                const int u = idx / NT, n = idx % NT;
+                const int r = g * U + u;
+                if (r < M && n < N) Y[(uint64_t)n * y_pitch + r] = tot;
+            }
+        } else {
+            float *buf = red[it & 1][wave];
+            if (owner) buf[idx] = tot;
+            __syncthreads();
+            if (ks == 0 && lane < U * NT && in_range) {
+                float s = 0.0f;
+#pragma unroll
+                for (int w2 = 0; w2 < KS; ++w2) s += red[it & 1][grp * KS + w2][lane];
+                const int u = lane / NT, n = lane % NT;
+                const int r = g * U + u;
+                if (r < M && n < N) Y[(uint64_t)n * y_pitch + r] = s;
+            }
+        }
+    }
+}
+
+using I8Kernel = void (*)(const I8Args);
+
+template <int WT, int NT, int KS, int CPL>
+I8Kernel pick_i8_u(int u)
+{
+    constexpr int UW = (CPL > 2) ? 1 : (NT <= 1) ? 4 : (NT == 2 ? 2 : 1);
+    if (u == 1) return gemv_i8_kernel<WT, NT, KS, CPL, 1>;
+    if (u == UW) return gemv_i8_kernel<WT, NT, KS, CPL, UW>;
+    return nullptr;
+}
+
+template <int WT, int NT, int KS>
+I8Kernel pick_i8_cpl(int cpl, int u)
+{
+    switch (cpl) {
+    case 1: return pick_i8_u<WT, NT, KS, 1>(u);
+    case 2: return pick_i8_u<WT, NT, KS, 2>(u);
+    case 4: return pick_i8_u<WT, NT, KS, 4>(u);
+    default: return nullptr;
+    }
+}
+
+template <int WT, int NT>
+I8Kernel pick_i8_ks(int ks, int cpl, int u)
+{
+    switch (ks) {
+    case 1: return pick_i8_cpl<WT, NT, 1>(cpl, u);
+    case 2: return pick_i8_cpl<WT, NT, 2>(cpl, u);
+    case 4: return pick_i8_cpl<WT, NT, 4>(cpl, u);
+    default: return nullptr;
+    }
+}
+
+template <int WT>
+I8Kernel pick_i8_nt(int nt, int ks, int cpl, int u)
+{
+    switch (nt) {
+    case 1: return pick_i8_ks<WT, 1>(ks, cpl, u);
+    case 2: return pick_i8_ks<WT, 2>(ks, cpl, u);
+    case 4: return pick_i8_ks<WT, 4>(ks, cpl, u);
+    case 8: return pick_i8_ks<WT, 8>(ks, cpl, u);
+    default: return nullptr;
+    }
+}
+
+}  // namespace
+
+namespace {
+
+// Launch shape: the wave split and chunks per lane of the fp32-activation
+// GEMV at one token (a function of the row length only), then as many
+// tokens per pass as the activation registers allow (NT * CPL * XD <= 64).
+bool i8_config(int wtype, int64_t K, int64_t M, int64_t N, GemvConfig *cfg)
+{
+    GemvConfig c;
+    if (!gemv_config(wtype, K, M, 1, &c) || c.cpl > 4) return false;
+    const int xd = (wtype == W_Q4_0) ? 8 : 4;
+    int nt = N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : 8;
+    while (nt > 1 && nt * c.cpl * xd > 64) nt /= 2;
+    if (nt * c.cpl * xd > 64) return false;
+    c.nt = nt;
+    if (nt >= 4 || c.cpl > 2) c.u = 1;
+    else if (nt == 2 && c.u > 2) c.u = 2;
+    *cfg = c;
+    return true;
+}
+
+}  // namespace
+
+hipError_t launch_gemv_i8(const WeightView &w, const WeightView &xq, const OutView &y, int64_t N,
+                          hipStream_t stream)
+{
+    if (w.M == 0 || N == 0) return hipSuccess;
+    GemvConfig c;
+    if (!i8_config(w.type, w.K, w.M, N, &c)) return hipErrorInvalidValue;
+    const I8Kernel k = (w.type == W_Q4_0) ? pick_i8_nt<W_Q4_0>(c.nt, c.ks, c.cpl, c.u)
+                                          : pick_i8_nt<W_Q8_0>(c.nt, c.ks, c.cpl, c.u);
+    if (!k) return hipErrorInvalidValue;
+    const int groups_per_wg = 4 / c.ks;
+    I8Args a;
+    a.w = w.base;
+    a.pitch = (uint32_t)w.pitch;
+    a.x_pitch = (uint32_t)xq.pitch;
+    a.y_pitch = (uint32_t)y.pitch_elems;
+    a.M = (int32_t)w.M;
+    a.K = (int32_t)w.K;
+    a.qoff = (int32_t)quant_offset(w.K);
+    a.nchunk = (int32_t)((w.type == W_Q4_0 ? w.K / 2 : w.K) / 16);
+    a.n_groups = (int32_t)((w.M + c.u - 1) / c.u);
+    int64_t wgs = (a.n_groups + groups_per_wg - 1) / groups_per_wg;
+    if (wgs > kMaxWorkgroups) wgs = kMaxWorkgroups;
+    a.wg_count = (int32_t)wgs;
+    const int64_t per_pass = (int64_t)groups_per_wg * wgs;
+    a.iters = (int32_t)((a.n_groups + per_pass - 1) / per_pass);
+    // tokens in passes of up to NT (one pass over the weights each)
+    for (int64_t n0 = 0; n0 < N; n0 += c.nt) {
+        a.xq = xq.base + (uint64_t)n0 * xq.pitch;
+        a.y = y.data + (uint64_t)n0 * y.pitch_elems;
+        a.N = (int32_t)(N - n0 < c.nt ? N - n0 : c.nt);
+        hipLaunchKernelGGL(k, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+bool gemv_i8_supported(int wtype, int64_t K, int64_t M, int64_t N)
+{
+    if (wtype != W_Q4_0 && wtype != W_Q8_0) return false;
+    GemvConfig c;
+    return i8_config(wtype, K, M, N, &c);
+}
+
+}  // namespace qmm

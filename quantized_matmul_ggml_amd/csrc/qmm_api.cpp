@@ -174,6 +174,21 @@ int qmm_dequantize(const qmm_tensor *src, qmm_tensor *dst, void *stream)
 
 int qmm_gemv(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *stream)
 {
+    if (x && x->type == QMM_TYPE_Q8_0) {
+        // the integer-activation path ("A Complete Guide to llama.cpp ...", §2.2)
+        int rc = check_mul_mat(w, x, y, QMM_TYPE_Q8_0, 16);
+        if (rc) return rc;
+        if (!is_quant(w->type)) return QMM_ERR_TYPE;
+        if (x->ne[1] > 8) return QMM_ERR_SHAPE;
+        if (x->ne[1] == 0 || w->ne[1] == 0) return QMM_OK;
+        if (!qmm::gemv_i8_supported(w->type, w->ne[0], w->ne[1], x->ne[1])) return QMM_ERR_UNSUPPORTED;
+        const qmm::WeightView wv = weight_view(w), xv = weight_view(x);
+        qmm::OutView yv{static_cast<float *>(y->data), pitch_elems(y)};
+        if (wv.pitch > (1ull << 28) || xv.pitch > (1ull << 28) || wv.M >= (1ll << 31) ||
+            yv.pitch_elems >= (1ull << 31))
+            return QMM_ERR_UNSUPPORTED;
+        return status_of(qmm::launch_gemv_i8(wv, xv, yv, x->ne[1], static_cast<hipStream_t>(stream)));
+    }
     int rc = check_mul_mat(w, x, y, QMM_TYPE_F32, 4);
     if (rc) return rc;
     if (!(is_quant(w->type) || w->type == QMM_TYPE_F16)) return QMM_ERR_TYPE;

@@ -86,6 +86,13 @@ struct GemvTask {
 };
 hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t stream);
 
+// The integer-activation GEMV (gemv_i8.hip): w Q4_0 / Q8_0, the N
+// activation rows xq Q8_0 of the same K (xq.M = N), y F32.  Supported when
+// the plain configuration for (type, K, M, N) uses at most 4 chunks per lane.
+bool gemv_i8_supported(int wtype, int64_t K, int64_t M, int64_t N);
+hipError_t launch_gemv_i8(const WeightView &w, const WeightView &xq, const OutView &y, int64_t N,
+                          hipStream_t stream);
+
 // The fused gate/up projection with the SwiGLU epilogue:
 // h[n][m] = Swish(sum_k Wg'[m][k] x[n][k]) * sum_k Wu'[m][k] x[n][k].
 // wg and wu share the type, K and M.

@@ -239,6 +239,18 @@ def test_record_conversions_reject(qmm_lib):
 
 
 @no_gpu
+def test_gemv_q8_activations_reject(qmm_lib):
+    xq = B.make_desc(B.Q8_0, 2048, 1, 2176, X_ADDR)
+    assert B.call_raw("qmm_gemv", B.make_desc(B.F16, 2048, 64, 4096, W_ADDR), xq, _y()) == B.ERR_TYPE
+    assert B.call_raw("qmm_gemv", _w(), B.make_desc(B.Q8_0, 2048, 9, 2176, X_ADDR), _y(N=9)) == B.ERR_SHAPE
+    assert B.call_raw("qmm_gemv", _w(), B.make_desc(B.Q8_0, 2048, 2, 2184, X_ADDR), _y(N=2)) == B.ERR_LAYOUT
+    assert B.call_raw("qmm_gemv", _w(), B.make_desc(B.Q8_0, 1024, 1, 1088, X_ADDR), _y()) == B.ERR_SHAPE
+    assert B.call_raw("qmm_gemv", _w(), xq, _y(addr=X_ADDR + 64)) == B.ERR_ALIAS
+    assert B.call_raw("qmm_gemv", _w(K=65536, M=4), B.make_desc(B.Q8_0, 65536, 1, 69632, X_ADDR),
+                      _y(M=4)) == B.ERR_UNSUPPORTED
+
+
+@no_gpu
 def test_empty_operands_enqueue_nothing(qmm_lib):
     # zero rows / zero tokens are valid and launch no kernel (so they are safe
     # without a GPU); NULL data is allowed for empty tensors

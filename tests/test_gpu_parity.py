@@ -646,3 +646,59 @@ def test_records_feed_the_gemv(orc):
     y1 = Q.gemv(q, x)
     y2 = Q.gemv(back, x)
     assert torch.equal(y1, y2)
+
+
+# ------------------------------------------------- integer activations (Q8_0 x)
+
+I8_CASES = [
+    ("Q4_0", 2048, 2048, 1), ("Q4_0", 5632, 2048, 1), ("Q4_0", 2048, 5632, 1),
+    ("Q8_0", 32000, 2048, 8), ("Q8_0", 32000, 2048, 1), ("Q4_0", 300, 1024, 3),
+    ("Q8_0", 37, 96, 5), ("Q4_0", 1, 32, 1), ("Q8_0", 513, 512, 2), ("Q4_0", 64, 16384, 2),
+    ("Q4_0", 130, 8192, 8),
+]
+
+
+@pytest.mark.parametrize("case", I8_CASES, ids=lambda c: "%s-%dx%d-n%d" % c)
+def test_gemv_q8_activations(orc, case):
+    """The integer-activation GEMV against the oracle's integer path: x is
+    quantized on the GPU (bit-exact with the oracle), then y must agree
+    within the binary32 summation bound of its block terms."""
+    tname, M, K, N = case
+    _banner(f"gemv q8 activations {tname} M={M} K={K} N={N}")
+    seed = 13 * M + K + N
+    w = WL.weights(seed, M, K)
+    x = WL.activations(seed + 1, N, K)
+    packed = orc.quantize(TYPES[tname][1], w)
+    xq_ref = orc.quantize(orc.Q8_0, x)
+    wt = B.Weight(torch.from_numpy(packed).to(DEV), TYPES[tname][0], K, M)
+    xq = Q.quantize(torch.from_numpy(x).to(DEV), B.Q8_0)
+    assert np.array_equal(xq.data.cpu().numpy(), xq_ref)
+    yref, _ = orc.mul_mat_q8act(TYPES[tname][1], packed, K, xq_ref)
+    _, a_exact = orc.mul_mat(TYPES[tname][1], packed, K, orc.dequantize(orc.Q8_0, xq_ref, K))
+    y = Q.gemv(wt, xq).cpu().numpy().astype(np.float64)
+    nchunk = K // 32 if tname == "Q4_0" else K // 16
+    tol = (nchunk + 16) * 2.0 ** -24 * a_exact + 1e-30
+    err = np.abs(y - yref)
+    assert (err <= tol).all(), f"worst err/tol {(err / tol).max():.3g}"
+
+
+def test_gemv_q8_activations_zero_and_strided(orc):
+    """Zero activation blocks (scale 0) and padded pitches on both operands."""
+    M, K, N = 90, 2048, 4
+    _banner("gemv q8 activations zero blocks, strided")
+    w = WL.weights(61, M, K)
+    x = WL.activations(62, N, K)
+    x[1, 64:512] = 0.0
+    x[3] = 0.0
+    packed = orc.quantize(orc.Q4_0, w)
+    rs = packed.shape[1]
+    padded = np.full((M, rs + 32), 0xFF, np.uint8)
+    padded[:, :rs] = packed
+    wt = B.Weight(torch.from_numpy(padded).to(DEV), B.Q4_0, K, M)
+    xq_ref = orc.quantize(orc.Q8_0, x)
+    xq = Q.quantize(torch.from_numpy(x).to(DEV), B.Q8_0, pitch=B.row_size(B.Q8_0, K) + 64)
+    yref, _ = orc.mul_mat_q8act(orc.Q4_0, packed, K, xq_ref)
+    _, a_exact = orc.mul_mat(orc.Q4_0, packed, K, orc.dequantize(orc.Q8_0, xq_ref, K))
+    y = Q.gemv(wt, xq).cpu().numpy().astype(np.float64)
+    assert (y[3] == 0).all()
+    assert (np.abs(y - yref) <= (K // 32 + 16) * 2.0 ** -24 * a_exact + 1e-30).all()
