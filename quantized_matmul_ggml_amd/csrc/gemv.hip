@@ -37,7 +37,10 @@ namespace qmm {
 namespace {
 
 constexpr int kThreads = 256;         // four wave64 per workgroup
-constexpr int kMaxWorkgroups = 1024;  // persistent grid: 4 workgroups per CU
+// Persistent grid: at most 8 workgroups per CU when a wave owns whole rows,
+// 4 when rows span several waves (measured: the larger grid helps the
+// former and costs the Q8_0 LM head at 2 and 4 tokens 5-7 %).
+inline int max_workgroups(int ks) { return ks == 1 ? 2048 : 1024; }
 constexpr int kMaxItems = QMM_GEMV_BATCH_MAX;
 
 // One GEMV of a launch: its weights, activations and outputs.  All items of
@@ -477,6 +480,8 @@ Kernel pick_u(int u, bool swiglu)
         }
         if (u == 1) return gemv_kernel<WT, NT, KS, CPL, 1, false>;
         if (u == UW) return gemv_kernel<WT, NT, KS, CPL, UW, false>;
+        if constexpr (UW == 4)
+            if (u == 2) return gemv_kernel<WT, NT, KS, CPL, 2, false>;
         return nullptr;
     }
 }
@@ -569,10 +574,15 @@ bool gemv_config(int type, int64_t K, int64_t M, int64_t N, GemvConfig *cfg)
         }
     }
     if (c.ks == 0) return false;
-    // Short matrices stream one row per wave group so that more waves run,
-    // unless the row already takes several waves.
+    // Rows per wave group: with one wave per row, two rows from 2048 rows up
+    // and one below (measured on 256 .. 11264 rows of K = 2048: four rows
+    // leave too few waves, one row too little in flight per wave); rows
+    // split over several waves take the widest group.
     const int u_wide = c.nt <= 1 ? 4 : (c.nt == 2 ? 2 : 1);
-    c.u = (M < 4096 && c.ks == 1) ? 1 : u_wide;
+    if (c.ks == 1)
+        c.u = c.nt <= 2 ? (M >= 2048 ? 2 : 1) : 1;
+    else
+        c.u = u_wide;
     // ... widened while the rows alone cannot fill 256 CUs with 8 waves each,
     // as long as no more than a quarter of the lanes is left without a chunk.
     while (c.ks < 4) {
@@ -632,8 +642,8 @@ hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t strea
         for (int i = 0; i < count; ++i) {
             if (tasks[i].w.M == 0) continue;
             int64_t wgs = need[i];
-            if (need_total > kMaxWorkgroups) {
-                wgs = need[i] * kMaxWorkgroups / need_total;   // share of the persistent grid
+            if (need_total > max_workgroups(c.ks)) {
+                wgs = need[i] * max_workgroups(c.ks) / need_total;   // share of the persistent grid
                 if (wgs < 1) wgs = 1;
             }
             GemvItem &it = a.item[a.n_items++];
@@ -698,7 +708,7 @@ hipError_t launch_gemv_swiglu(const WeightView &wg, const WeightView &wu, const 
         it.y_pitch = (uint32_t)h.pitch_elems;
         it.n_groups = (int32_t)((M + ru - 1) / ru);
         int64_t wgs = (it.n_groups + groups_per_wg - 1) / groups_per_wg;
-        if (wgs > kMaxWorkgroups) wgs = kMaxWorkgroups;
+        if (wgs > max_workgroups(c.ks)) wgs = max_workgroups(c.ks);
         it.wg_count = (int32_t)wgs;
         const int64_t per_pass = (int64_t)groups_per_wg * wgs;
         it.iters = (int32_t)((it.n_groups + per_pass - 1) / per_pass);

@@ -234,6 +234,8 @@ I8Kernel pick_i8_u(int u)
     constexpr int UW = (CPL > 2) ? 1 : (NT <= 1) ? 4 : (NT == 2 ? 2 : 1);
     if (u == 1) return gemv_i8_kernel<WT, NT, KS, CPL, 1>;
     if (u == UW) return gemv_i8_kernel<WT, NT, KS, CPL, UW>;
+    if constexpr (UW == 4)
+        if (u == 2) return gemv_i8_kernel<WT, NT, KS, CPL, 2>;
     return nullptr;
 }
 
@@ -336,7 +338,9 @@ bool gemv_i8_supported(int wtype, int64_t K, int64_t M, int64_t N)
 {
     if (wtype != W_Q4_0 && wtype != W_Q8_0) return false;
     GemvConfig c;
-    return i8_config(wtype, K, M, N, &c);
+    if (!i8_config(wtype, K, M, N, &c)) return false;
+    return (wtype == W_Q4_0 ? pick_i8_nt<W_Q4_0>(c.nt, c.ks, c.cpl, c.u)
+                            : pick_i8_nt<W_Q8_0>(c.nt, c.ks, c.cpl, c.u)) != nullptr;
 }
 
 }  // namespace qmm
