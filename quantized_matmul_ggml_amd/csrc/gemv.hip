@@ -42,6 +42,8 @@ constexpr int kThreads = 256;         // four wave64 per workgroup
 // former and costs the Q8_0 LM head at 2 and 4 tokens 5-7 %).
 inline int max_workgroups(int ks) { return ks == 1 ? 2048 : 1024; }
 constexpr int kMaxItems = QMM_GEMV_BATCH_MAX;
+// From this many tokens on the matrix-core kernels take a batch (measured).
+constexpr int kMfMinTokens = 5;
 
 // One GEMV of a launch: its weights, activations and outputs.  All items of
 // a launch share the weight type, K and the token count.  An item is one
@@ -612,6 +614,7 @@ hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t strea
     if (m_total == 0 || N == 0) return hipSuccess;
     // The matrix-core kernel's cost does not grow with the token count; it is
     // the faster one from 5 tokens up (measured), the VALU kernel below that.
+    if (N >= kMfMinTokens && gemv_mf_supported(tasks, count)) return launch_gemv_mf(tasks, count, stream);
     if (N >= 5 && gemv_mfma_supported(type, K, N)) return launch_gemv_mfma(tasks, count, stream);
 
     // Tokens are processed in chunks of at most 8; a chunk shrinks (halving)

@@ -1,0 +1,432 @@
+// gemv_mf.hip -- decode GEMV / skinny GEMM for Q4_0 and Q8_0 weights and up
+// to 8 fp32 tokens on the bf16 matrix cores.
+//
+// Same operation as gemv.hip (y[n][m] = sum_k W'[m][k] x[n][k]), with the
+// multiply-adds moved to v_mfma_f32_16x16x32_bf16 (D 16 x 16 += A 16 x 32 *
+// B 32 x 16), so that the vector ALUs only unpack codes and apply block scales
+// and the cost per weight does not grow with the token count (Development
+// Guide for Small AI Models (TinyLLaMA, etc.) Using C++, §6.2: unpack, scale,
+// multiply-add; A Complete Guide to llama.cpp and Customization with C++,
+// §2.2: the scale factors out of each block's dot product).
+//
+//  * A (16 x 32): channel i = 2 n + h is token n, h = 0 the bf16 high part of
+//    the activations and h = 1 the bf16 low part (x = hi + lo to 2^-17
+//    relative, so the products keep the fp32 GEMV's accuracy).  A wave owns
+//    a fixed range of NBW blocks of K and keeps their fragments in registers
+//    for every row tile it streams: no LDS traffic per matrix instruction.
+//  * B (32 x 16): column j is weight row j of a 16-row tile.  Each lane loads
+//    16 contiguous bytes of its row (Q4_0: one block of the four a group of
+//    lanes covers; Q8_0: half a block of two), 64 bytes per row per
+//    instruction, and two cross-lane swaps (v_permlane32_swap, then
+//    v_permlane16_swap for Q4_0) regroup them so that the four lane groups of
+//    one matrix instruction hold four disjoint 8-code sets of the SAME block.
+//    Codes enter as exact biased bf16 integers (Q4_0: 128 + nibble by one
+//    and-or per two codes; Q8_0: code + 128 by byte conversion).
+//  * D (16 x 16): lane (row j, group g) gets channels 4 g .. 4 g + 3, i.e.
+//    tokens 2 g and 2 g + 1, of its row for one block; it removes the code
+//    bias (-bias * sum of the block's activations, precomputed per wave) and
+//    applies the block scale in two fused multiply-adds per token.
+//  * The KW waves of a workgroup split K; their partial sums meet in LDS at
+//    the end of each tile.
+#include "qmm_internal.h"
+#include "wave_reduce.h"
+
+namespace qmm {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTileRows = 16;
+constexpr int kMaxMfItems = QMM_GEMV_BATCH_MAX;
+
+template <int WT> struct MfFmt;
+template <> struct MfFmt<W_Q4_0> { static constexpr int bpg = 4, block_bytes = 16; static constexpr float bias = 136.0f; };
+template <> struct MfFmt<W_Q8_0> { static constexpr int bpg = 2, block_bytes = 32; static constexpr float bias = 128.0f; };
+
+struct alignas(64) MfItem {
+    const uint8_t *w;
+    const float *x;
+    float *y;
+    uint32_t pitch;       // bytes between weight rows
+    uint32_t x_pitch;     // elements between token rows of x
+    uint32_t y_pitch;     // elements between token rows of y
+    int32_t M;
+    int32_t n_tiles;      // 16-row tiles
+    int32_t wg_count;     // workgroups of this item (grid x; grid y indexes the item)
+    int32_t pad[2];
+};
+static_assert(sizeof(MfItem) == 64, "one 64-byte record per item");
+
+struct MfArgs {
+    int32_t N;            // tokens of this launch (<= 8)
+    int32_t K;
+    int32_t qoff;
+    int32_t nb;           // 32-blocks per row
+    int32_t n_items;
+    int32_t pad[11];
+    MfItem item[kMaxMfItems];
+};
+
+__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t c)
+{
+    uint32_t d;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(c));
+    return d;
+}
+
+// Round two floats to bf16 (nearest even) in one v_cvt_pk_bf16_f32.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack_bf16(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+__device__ inline float bf16_lo(uint32_t p) { return __builtin_bit_cast(float, p << 16); }
+__device__ inline float bf16_hi(uint32_t p) { return __builtin_bit_cast(float, p & 0xFFFF0000u); }
+
+// Byte E of w as a float (v_cvt_f32_ubyteE).
+template <int E>
+__device__ inline float ubyte(uint32_t w)
+{
+    float r;
+    if constexpr (E == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(w));
+    else if constexpr (E == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(w));
+    else if constexpr (E == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(w));
+    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(w));
+    return r;
+}
+
+// The k positions (within a block) of the 8 values lane group g feeds to
+// one matrix instruction, in register order; A and B use the same list.
+//  Q4_0: group g holds dword g of the block (bytes 4g..4g+3; byte s has
+//        element 4g+s in its low nibble and 16+4g+s in its high nibble),
+//        unpacked as lo(s0) lo(s2) hi(s0) hi(s2) lo(s1) lo(s3) hi(s1) hi(s3).
+//  Q8_0: group g holds codes k0(g) .. k0(g)+7 with k0 = 0, 16, 8, 24.
+
+// Swap helpers: [0] is the new first operand, [1] the new second.
+__device__ inline void swap32(uint32_t &a, uint32_t &b)
+{
+    const auto p = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    a = p[0];
+    b = p[1];
+}
+__device__ inline void swap16(uint32_t &a, uint32_t &b)
+{
+    const auto p = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = p[0];
+    b = p[1];
+}
+
+template <int WT, int KW, int NBW>
+__global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
+{
+    constexpr int BPG = MfFmt<WT>::bpg;
+    constexpr int BB = MfFmt<WT>::block_bytes;
+    constexpr int NG = NBW / BPG;          // load groups per tile per wave
+    static_assert(NBW % BPG == 0, "whole load groups");
+    __shared__ float red[2][KW][64][2];
+    __shared__ float ssum[KW][NBW][16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15;               // A channel / B and D column (weight row)
+    const int g = lane >> 4;               // k group / D channel group
+
+    const int item = blockIdx.y;
+    const MfItem &itm = a.item[item];
+    const uint8_t *const W = itm.w;
+    const float *const X = itm.x;
+    float *const Y = itm.y;
+    const uint32_t pitch = itm.pitch, x_pitch = itm.x_pitch, y_pitch = itm.y_pitch;
+    const int M = itm.M, n_tiles = itm.n_tiles, n_wg = itm.wg_count;
+    const int N = a.N, K = a.K, qoff = a.qoff, nb = a.nb;
+    asm volatile("" ::"s"(W), "s"(X), "s"(Y), "s"(pitch), "s"(x_pitch), "s"(y_pitch), "s"(M),
+                 "s"(n_tiles), "s"(n_wg), "s"(N), "s"(K), "s"(qoff), "s"(nb));
+    if ((int)blockIdx.x >= n_wg) return;
+    const int b_begin = wave * NBW;
+
+    // ---- weight loads of one tile: per load group, 16 bytes of codes and
+    // the group's scales; rows past M and blocks past the row read zeros ----
+    const uint32_t row_bytes = (uint32_t)(qoff + nb * BB);
+    struct Grp { uint32_t q[4]; uint32_t s[BPG / 2]; };
+    auto load_tile = [&](Grp (&dst)[NG], int tile) {
+        const int r0 = tile * kTileRows;
+        const int rows = tile < n_tiles ? (M - r0 < kTileRows ? M - r0 : kTileRows) : 0;
+        const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(W + (uint64_t)(rows > 0 ? r0 : 0) * pitch), 0,
+            (int)(rows > 0 ? (uint32_t)(rows - 1) * pitch + row_bytes : 0u), BUFFER_FLAGS);
+        const uint32_t ro = (uint32_t)j * pitch;
+#pragma unroll
+        for (int p = 0; p < NG; ++p) {
+            const int b0 = b_begin + p * BPG;
+            const int mine = (WT == W_Q4_0) ? b0 + g : b0 + (g >> 1);      // block of this lane's 16 bytes
+            const uint32_t qo = mine < nb ? ro + (uint32_t)(qoff + BB * b0 + 16 * g) : OUT_OF_RANGE;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(wres, qo, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[p].q[e] = v[e];
+            const uint32_t so = b0 < nb ? ro + (uint32_t)(2 * b0) : OUT_OF_RANGE;
+            if constexpr (BPG == 4) {
+                const auto s2 = __builtin_amdgcn_raw_buffer_load_b64(wres, so, 0, 0);
+                dst[p].s[0] = s2[0];
+                dst[p].s[1] = s2[1];
+            } else {
+                dst[p].s[0] = __builtin_amdgcn_raw_buffer_load_b32(wres, so, 0, 0);
+            }
+        }
+    };
+
+    // the first tile's weights are in flight while the activations are set up
+    Grp cur[NG];
+    int tile = blockIdx.x;
+    load_tile(cur, tile);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- activation fragments of this wave's blocks; channel j = token
+    // j / 2, part j % 2; blocks past the row and tokens past N read zeros ----
+    const int tok = j >> 1;
+    const bool lo_part = (j & 1) != 0;
+    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)X, 0, (int)(((uint32_t)(N - 1) * x_pitch + (uint32_t)K) * 4u), BUFFER_FLAGS);
+    const uint32_t xrow = (uint32_t)tok * x_pitch * 4u;
+    // all loads first, then the conversions: one round trip, not NBW
+    uint32_t raw[NBW][8];
+#pragma unroll
+    for (int t = 0; t < NBW; ++t) {
+        const int b = b_begin + t;
+        // the 8 k positions of group g come in two runs of 4 (Q4_0: 4g.. and
+        // 16+4g..; Q8_0: k0.. and k0+4..)
+        const uint32_t base = (uint32_t)(32 * b) * 4;
+        uint32_t o0, o1;
+        if constexpr (WT == W_Q4_0) { o0 = base + 16 * g; o1 = base + 64 + 16 * g; }
+        else { const int k0 = (g == 0) ? 0 : (g == 1) ? 16 : (g == 2) ? 8 : 24; o0 = base + 4 * k0; o1 = o0 + 16; }
+        const bool in = b < nb && tok < N;
+        const auto p0 = __builtin_amdgcn_raw_buffer_load_b128(xres, in ? xrow + o0 : OUT_OF_RANGE, 0, 0);
+        const auto p1 = __builtin_amdgcn_raw_buffer_load_b128(xres, in ? xrow + o1 : OUT_OF_RANGE, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { raw[t][e] = p0[e]; raw[t][4 + e] = p1[e]; }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 xf[NBW];
+#pragma unroll
+    for (int t = 0; t < NBW; ++t) {
+        float v[8];
+        float r0[4], r1[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            r0[e] = __builtin_bit_cast(float, raw[t][e]);
+            r1[e] = __builtin_bit_cast(float, raw[t][4 + e]);
+        }
+        if constexpr (WT == W_Q4_0) {
+            // order lo(s0) lo(s2) hi(s0) hi(s2) lo(s1) lo(s3) hi(s1) hi(s3)
+            v[0] = r0[0]; v[1] = r0[2]; v[2] = r1[0]; v[3] = r1[2];
+            v[4] = r0[1]; v[5] = r0[3]; v[6] = r1[1]; v[7] = r1[3];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { v[e] = r0[e]; v[4 + e] = r1[e]; }
+        }
+        uint32_t w4[4];
+        float s = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t hi = pack_bf16(v[2 * e], v[2 * e + 1]);
+            const uint32_t lo = pack_bf16(v[2 * e] - bf16_lo(hi), v[2 * e + 1] - bf16_hi(hi));
+            const uint32_t part = lo_part ? lo : hi;
+            w4[e] = part;
+            s += bf16_lo(part) + bf16_hi(part);
+        }
+        xf[t] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+        // sum over the four k groups (lanes 16 apart): channel j's block sum
+        s += partner<4>(s, lane);
+        s += partner<5>(s, lane);
+        if (g == 0) ssum[wave][t][j] = s;
+    }
+    __syncthreads();
+    // the code bias of tokens 2g and 2g+1 per block: -bias * (hi sum + lo sum)
+    float cb[NBW][2];
+#pragma unroll
+    for (int t = 0; t < NBW; ++t) {
+        const float4 s4 = *reinterpret_cast<const float4 *>(&ssum[wave][t][4 * g]);
+        cb[t][0] = -MfFmt<WT>::bias * (s4.x + s4.y);
+        cb[t][1] = -MfFmt<WT>::bias * (s4.z + s4.w);
+    }
+
+    const uint32_t magic = 0x43004300u;    // bf16 128.0 in both halves
+    // one tile: unpack, matrix products, bias and scales; then the partial
+    // sums of the KW waves (K ranges) meet in LDS and wave 0 stores the rows
+    auto consume = [&](const Grp (&c)[NG], int tl, int it) {
+        float yp0 = 0.0f, yp1 = 0.0f;
+#pragma unroll
+        for (int p = 0; p < NG; ++p) {
+            uint32_t d0 = c[p].q[0], d1 = c[p].q[1], d2 = c[p].q[2], d3 = c[p].q[3];
+            // regroup: the four lane groups of each matrix instruction hold
+            // disjoint code sets of one block
+            swap32(d0, d2);
+            swap32(d1, d3);
+            if constexpr (WT == W_Q4_0) {
+                swap16(d0, d1);
+                swap16(d2, d3);
+            }
+#pragma unroll
+            for (int t = 0; t < BPG; ++t) {
+                uint32_t r[4];
+                if constexpr (WT == W_Q4_0) {
+                    const uint32_t w = (t == 0) ? d0 : (t == 1) ? d1 : (t == 2) ? d2 : d3;
+                    const uint32_t m = 0x000F000Fu;
+                    r[0] = and_or(w, m, magic);
+                    r[1] = and_or(w >> 4, m, magic);
+                    r[2] = and_or(w >> 8, m, magic);
+                    r[3] = and_or(w >> 12, m, magic);
+                } else {
+                    const uint32_t wa = ((t == 0) ? d0 : d2) ^ 0x80808080u;   // code + 128
+                    const uint32_t wb = ((t == 0) ? d1 : d3) ^ 0x80808080u;
+                    r[0] = pack_bf16(ubyte<0>(wa), ubyte<1>(wa));
+                    r[1] = pack_bf16(ubyte<2>(wa), ubyte<3>(wa));
+                    r[2] = pack_bf16(ubyte<0>(wb), ubyte<1>(wb));
+                    r[3] = pack_bf16(ubyte<2>(wb), ubyte<3>(wb));
+                }
+                const bf16x8 wf = __builtin_bit_cast(bf16x8, make_uint4(r[0], r[1], r[2], r[3]));
+                const f32x4 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[p * BPG + t], wf,
+                                                                       f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                // a block past the row (its codes and activations read as
+                // zeros) may pick up a scale from the bytes after the row's
+                // scales: weight it by 0
+                const uint32_t sw = c[p].s[t / 2];
+                const float ds = (float)__builtin_bit_cast(_Float16, (uint16_t)((t & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+                const float d = (b_begin + p * BPG + t < nb) ? ds : 0.0f;
+                yp0 = fmaf(d, D[0] + D[1] + cb[p * BPG + t][0], yp0);
+                yp1 = fmaf(d, D[2] + D[3] + cb[p * BPG + t][1], yp1);
+            }
+        }
+        float *mine = red[it & 1][wave][lane];
+        mine[0] = yp0;
+        mine[1] = yp1;
+        __syncthreads();
+        if (wave == 0) {
+            float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+            for (int w2 = 0; w2 < KW; ++w2) {
+                s0 += red[it & 1][w2][lane][0];
+                s1 += red[it & 1][w2][lane][1];
+            }
+            const int m = tl * kTileRows + j;
+            if (m < M) {
+                if (2 * g < N) Y[(uint64_t)(2 * g) * y_pitch + m] = s0;
+                if (2 * g + 1 < N) Y[(uint64_t)(2 * g + 1) * y_pitch + m] = s1;
+            }
+        }
+    };
+
+    // two tile buffers in turn (no register copies between iterations, so
+    // the wait before a tile's use covers only that tile's loads); the tile
+    // after the last one reads nothing.  The loop bounds are uniform over
+    // the workgroup.
+    Grp alt[NG];
+    for (int it = 0;; it += 2) {
+        if (tile >= n_tiles) break;
+        load_tile(alt, tile + n_wg);
+        __builtin_amdgcn_sched_barrier(0);     // issue the prefetch first
+        consume(cur, tile, it);
+        tile += n_wg;
+        if (tile >= n_tiles) break;
+        load_tile(cur, tile + n_wg);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(alt, tile, it + 1);
+        tile += n_wg;
+    }
+}
+
+using MfKernel = void (*)(const MfArgs);
+
+template <int WT, int KW>
+MfKernel pick_mf_nbw(int nbw)
+{
+    switch (nbw) {
+    case 4: return gemv_mf_kernel<WT, KW, 4>;
+    case 8: return gemv_mf_kernel<WT, KW, 8>;
+    case 16: return gemv_mf_kernel<WT, KW, 16>;
+    default: return nullptr;
+    }
+}
+
+// Waves per workgroup (each a K range) and blocks per wave for a row of nb
+// blocks: 4 waves up to 64 blocks (K = 2048), 8 waves up to 128 (K = 4096).
+bool mf_shape(int64_t nb, int *kw, int *nbw)
+{
+    if (nb <= 0 || nb > 128) return false;
+    *kw = nb <= 64 ? 4 : 8;
+    const int64_t per = (nb + *kw - 1) / *kw;
+    *nbw = per <= 4 ? 4 : per <= 8 ? 8 : 16;
+    return true;
+}
+
+}  // namespace
+
+bool gemv_mf_supported(const GemvTask *tasks, int count)
+{
+    int kw, nbw;
+    const int type = tasks[0].w.type;
+    const int64_t K = tasks[0].w.K;
+    if (!(type == W_Q4_0 || type == W_Q8_0) || K % 32 != 0 || !mf_shape(K / 32, &kw, &nbw)) return false;
+    // a 16-row tile is one buffer resource with 32-bit offsets
+    // and the activations of up to 8 tokens another (byte offsets < 2^31)
+    for (int i = 0; i < count; ++i) {
+        const int64_t nt = tasks[i].x.N < 8 ? tasks[i].x.N : 8;
+        if (tasks[i].w.pitch > (1ull << 27) ||
+            (nt - 1) * (int64_t)tasks[i].x.pitch_elems + K > (int64_t)1 << 29)
+            return false;
+    }
+    return true;
+}
+
+hipError_t launch_gemv_mf(const GemvTask *tasks, int count, hipStream_t stream)
+{
+    if (count < 1 || count > kMaxMfItems) return hipErrorInvalidValue;
+    const int type = tasks[0].w.type;
+    const int64_t K = tasks[0].w.K;
+    const int64_t N = tasks[0].x.N;
+    int kw, nbw;
+    if (!mf_shape(K / 32, &kw, &nbw)) return hipErrorInvalidValue;
+    MfKernel k = nullptr;
+    if (type == W_Q4_0) k = (kw == 4) ? pick_mf_nbw<W_Q4_0, 4>(nbw) : pick_mf_nbw<W_Q4_0, 8>(nbw);
+    else if (type == W_Q8_0) k = (kw == 4) ? pick_mf_nbw<W_Q8_0, 4>(nbw) : pick_mf_nbw<W_Q8_0, 8>(nbw);
+    if (!k) return hipErrorInvalidValue;
+    int64_t tiles_total = 0;
+    for (int i = 0; i < count; ++i) tiles_total += (tasks[i].w.M + kTileRows - 1) / kTileRows;
+    if (tiles_total == 0 || N == 0) return hipSuccess;
+    // a workgroup streams several tiles with its activation fragments
+    // resident: at most 2 workgroups of 4 waves (1 of 8) per CU
+    const int64_t cap = kw == 4 ? 512 : 256;
+    for (int64_t n0 = 0; n0 < N; n0 += 8) {
+        MfArgs a = {};
+        a.N = (int32_t)(N - n0 < 8 ? N - n0 : 8);
+        a.K = (int32_t)K;
+        a.qoff = (int32_t)quant_offset(K);
+        a.nb = (int32_t)(K / 32);
+        int32_t wg_max = 0;
+        for (int i = 0; i < count; ++i) {
+            if (tasks[i].w.M == 0) continue;
+            MfItem &it = a.item[a.n_items++];
+            it.w = tasks[i].w.base;
+            it.pitch = (uint32_t)tasks[i].w.pitch;
+            it.M = (int32_t)tasks[i].w.M;
+            it.x = static_cast<const float *>(tasks[i].x.data) + (uint64_t)n0 * tasks[i].x.pitch_elems;
+            it.x_pitch = (uint32_t)tasks[i].x.pitch_elems;
+            it.y = tasks[i].y.data + (uint64_t)n0 * tasks[i].y.pitch_elems;
+            it.y_pitch = (uint32_t)tasks[i].y.pitch_elems;
+            it.n_tiles = (int32_t)((tasks[i].w.M + kTileRows - 1) / kTileRows);
+            int64_t wgs = (int64_t)it.n_tiles * cap / tiles_total;
+            if (wgs < 1) wgs = 1;
+            if (wgs > it.n_tiles) wgs = it.n_tiles;
+            it.wg_count = (int32_t)wgs;
+            if (wgs > wg_max) wg_max = (int32_t)wgs;
+        }
+        hipLaunchKernelGGL(k, dim3((unsigned)wg_max, (unsigned)a.n_items), dim3(64 * kw), 0, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace qmm

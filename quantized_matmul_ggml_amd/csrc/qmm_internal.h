@@ -103,6 +103,10 @@ hipError_t launch_gemv_swiglu(const WeightView &wg, const WeightView &wu, const 
 // LDS image of the activations fits for (K, N), and its launcher.
 bool gemv_mfma_supported(int type, int64_t K, int64_t N);
 hipError_t launch_gemv_mfma(const GemvTask *tasks, int count, hipStream_t stream);
+// The matrix-core GEMV with register-resident activation fragments
+// (gemv_mf.hip): Q4_0 / Q8_0 weights, K <= 4096, weight pitch <= 2^27.
+bool gemv_mf_supported(const GemvTask *tasks, int count);
+hipError_t launch_gemv_mf(const GemvTask *tasks, int count, hipStream_t stream);
 // Grant a kernel more than the default dynamic LDS (once per size).
 hipError_t allow_dynamic_lds(const void *fn, int bytes);
 

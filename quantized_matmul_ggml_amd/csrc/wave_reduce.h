@@ -18,6 +18,18 @@ namespace {
 // Every exchange stays on the VALU: DPP quad permutations for bits 0 and 1,
 // DPP rotations by 4 and 8 lanes within a 16-lane row for bits 2 and 3,
 // v_permlane16_swap / v_permlane32_swap for bits 4 and 5.
+// A copy of v that the compiler cannot prove equal to v.  A swap whose two
+// operands are provably the same value has had the lane-dependent choice
+// between its two results folded into one of them (observed with the ROCm
+// 7.2 compiler), which is wrong for half of the lanes; distinct operands keep
+// the choice.
+__device__ inline unsigned opaque_copy(unsigned v)
+{
+    unsigned r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+    return r;
+}
+
 template <int B>
 __device__ inline float partner(float v, int lane)
 {
@@ -32,10 +44,10 @@ __device__ inline float partner(float v, int lane)
         return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(iv, 0x128, 0xF, 0xF, true));  // row_ror:8
     } else if constexpr (B == 4) {
         // [0]: odd rows receive the even rows' values; [1]: even rows the odd rows'
-        const auto p = __builtin_amdgcn_permlane16_swap((unsigned)iv, (unsigned)iv, false, false);
+        const auto p = __builtin_amdgcn_permlane16_swap((unsigned)iv, opaque_copy((unsigned)iv), false, false);
         return __builtin_bit_cast(float, (lane & 16) ? p[0] : p[1]);
     } else {
-        const auto p = __builtin_amdgcn_permlane32_swap((unsigned)iv, (unsigned)iv, false, false);
+        const auto p = __builtin_amdgcn_permlane32_swap((unsigned)iv, opaque_copy((unsigned)iv), false, false);
         return __builtin_bit_cast(float, (lane & 32) ? p[0] : p[1]);
     }
 }
@@ -67,7 +79,7 @@ struct WaveReduce {
 __device__ inline float lower_half_to_upper(float v)
 {
     const unsigned u = __builtin_bit_cast(unsigned, v);
-    return __builtin_bit_cast(float, __builtin_amdgcn_permlane32_swap(u, u, false, false)[0]);
+    return __builtin_bit_cast(float, __builtin_amdgcn_permlane32_swap(u, opaque_copy(u), false, false)[0]);
 }
 
 template <int B>

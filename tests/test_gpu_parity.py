@@ -220,6 +220,11 @@ GEMV_CASES = [
     ("F16", 5632, 2048, 1),         # the fp16 FFN up-projection GEMV
     ("F16", 1, 7, 1), ("F16", 65, 1000, 2), ("F16", 4101, 2048, 1), ("F16", 10, 8192, 1),
     ("F16", 77, 520, 8),
+    # 5+ tokens with K <= 4096 run on the matrix cores: partial block groups
+    # (K = 96, 160, 1056, 2080), 4 and 8 waves per row range, and K just
+    # past that kernel's range
+    ("Q4_0", 40, 96, 5), ("Q4_0", 257, 160, 6), ("Q4_0", 17, 1056, 5), ("Q4_0", 1000, 4096, 6),
+    ("Q8_0", 31, 2080, 6), ("Q8_0", 1001, 4096, 5), ("Q8_0", 64, 4128, 8),
 ]
 
 
@@ -252,8 +257,9 @@ def test_gemv_strided_operands(orc):
         K = 2048
         _banner(f"gemv strided {tname}")
         pitch = B.row_size(TYPES[tname][0], K) + 64 if tname != "F16" else 2 * K + 64
-        y, yref, a = _run_gemv(orc, tname, 70, K, 3, seed=5, w_pitch=pitch, x_pad=12, y_pad=5)
-        _assert_tol(y, yref, a, 1e-4, 1e-6, f"gemv strided {tname}")
+        for N in (3, 6):
+            y, yref, a = _run_gemv(orc, tname, 70, K, N, seed=5, w_pitch=pitch, x_pad=12, y_pad=5)
+            _assert_tol(y, yref, a, 1e-4, 1e-6, f"gemv strided {tname} N={N}")
 
 
 @pytest.mark.parametrize("K", [7, 1003, 2051])
