@@ -42,8 +42,12 @@ constexpr int kThreads = 256;         // four wave64 per workgroup
 // former and costs the Q8_0 LM head at 2 and 4 tokens 5-7 %).
 inline int max_workgroups(int ks) { return ks == 1 ? 2048 : 1024; }
 constexpr int kMaxItems = QMM_GEMV_BATCH_MAX;
-// From this many tokens on the matrix-core kernels take a batch (measured).
-constexpr int kMfMinTokens = 5;
+// Which launches the matrix-core kernels take (measured on the decoder's
+// shapes): from 5 tokens every one; from 3 tokens those of at least 8192 rows
+// (LM head, gate/up), whose 16-row tiles occupy every CU; below that the
+// VALU kernel, whose cost per weight grows with the tokens but whose grid
+// fills the chip at any row count.
+inline bool use_matrix_cores(int64_t N, int64_t m_total) { return N >= 5 || (N >= 3 && m_total >= 8192); }
 
 // One GEMV of a launch: its weights, activations and outputs.  All items of
 // a launch share the weight type, K and the token count.  An item is one
@@ -612,9 +616,8 @@ hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t strea
     int64_t m_total = 0;
     for (int i = 0; i < count; ++i) m_total += tasks[i].w.M;
     if (m_total == 0 || N == 0) return hipSuccess;
-    // The matrix-core kernel's cost does not grow with the token count; it is
-    // the faster one from 5 tokens up (measured), the VALU kernel below that.
-    if (N >= kMfMinTokens && gemv_mf_supported(tasks, count)) return launch_gemv_mf(tasks, count, stream);
+    // The matrix-core kernels' cost does not grow with the token count.
+    if (use_matrix_cores(N, m_total) && gemv_mf_supported(tasks, count)) return launch_gemv_mf(tasks, count, stream);
     if (N >= 5 && gemv_mfma_supported(type, K, N)) return launch_gemv_mfma(tasks, count, stream);
 
     // Tokens are processed in chunks of at most 8; a chunk shrinks (halving)

@@ -118,15 +118,103 @@ __device__ inline void swap16(uint32_t &a, uint32_t &b)
     b = p[1];
 }
 
+// A wave's share of one 16-row tile in LDS: the code bytes of its NBW
+// blocks of each row (SB = 16 U bytes, U 16-byte units) and their scales
+// (SR bytes), as the direct-to-LDS loads deliver them: one load instruction
+// moves 64 lanes x 16 contiguous bytes of RPI whole rows; the scales come
+// with 4-byte lanes.
+template <int WT, int NBW>
+struct MfStage {
+    static constexpr int SB = NBW * MfFmt<WT>::block_bytes;
+    static constexpr int U = SB / 16;
+    static constexpr int RPI = 64 / U;
+    static constexpr int NI = kTileRows / RPI;                 // code load instructions
+    static constexpr int SR = 2 * NBW;
+    static constexpr int NS = (kTileRows * SR + 255) / 256;    // scale load instructions
+    static constexpr int CODE_BYTES = NI * 1024;
+    static constexpr int BYTES = CODE_BYTES + NS * 256;
+    static_assert(U >= 4 && U <= 64, "2..16 rows per load instruction");
+};
+
+// Position (16-byte unit) of unit u of row r inside its row's LDS span: the
+// units of 8 rows that lanes read together land in 8 different 128-byte bank
+// windows (rows of 128 bytes or more start in the same window; rows of 64
+// bytes alternate halves).
+template <int U>
+__device__ inline int swz(int r, int u)
+{
+    if constexpr (U >= 8) return u ^ (r & 7);
+    else return u ^ ((r >> 1) & 3);
+}
+
+// Direct-to-LDS buffer loads, issued as instructions the compiler does not
+// see (so it neither reorders LDS reads around them nor adds waits of its
+// own); the consumer waits with an explicit vmcnt.  Lane i of one load writes
+// its SIZE bytes at lds + SIZE * i.  rsrc is the 4-word buffer resource.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ inline i32x4 buffer_words(const void *base, uint32_t bytes)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, BUFFER_FLAGS};
+}
+// m0 is the loads' LDS base; no other code in this file uses it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int SIZE>
+__device__ inline void load_to_lds(const i32x4 &rsrc, uint32_t lds, uint32_t voff)
+{
+    static_assert(SIZE == 4 || SIZE == 16, "dword or dwordx4");
+    if constexpr (SIZE == 16)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                     :: "s"(lds), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// Wait until at most N vector memory operations of this wave are pending.
+template <int N>
+__device__ inline void wait_vm()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// LDS of a workgroup with KW waves and NSTG stages, and the most stages (up
+// to MAXD, at least 2) that fit the CU's 160 KiB.
+constexpr int kLdsBytes = 160 * 1024;
 template <int WT, int KW, int NBW>
+constexpr int mf_lds_bytes(int nstg)
+{
+    return nstg * KW * MfStage<WT, NBW>::BYTES + (2 * KW * 64 * 2 + KW * NBW * 16) * 4;
+}
+template <int WT, int KW, int NBW, int MAXD>
+constexpr int mf_stages()
+{
+    int d = MAXD;
+    while (d > 2 && mf_lds_bytes<WT, KW, NBW>(d) > kLdsBytes) --d;
+    return d;
+}
+
+template <int WT, int KW, int NBW, int MAXD>
 __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
 {
+    constexpr int NSTG = mf_stages<WT, KW, NBW, MAXD>();
+    static_assert(mf_lds_bytes<WT, KW, NBW>(NSTG) <= kLdsBytes, "LDS of one workgroup");
     constexpr int BPG = MfFmt<WT>::bpg;
     constexpr int BB = MfFmt<WT>::block_bytes;
-    constexpr int NG = NBW / BPG;          // load groups per tile per wave
+    constexpr int NG = NBW / BPG;          // 64-byte groups per row per wave
     static_assert(NBW % BPG == 0, "whole load groups");
+    using St = MfStage<WT, NBW>;
+    static_assert(NSTG >= 2 && NSTG <= 4, "2 to 4 stages");
     __shared__ float red[2][KW][64][2];
     __shared__ float ssum[KW][NBW][16];
+    // one array per stage, so that each wait for a stage's loads counts only
+    // the loads issued before them
+    __shared__ __attribute__((aligned(16))) uint8_t st0[KW][St::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[KW][St::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[KW][NSTG > 2 ? St::BYTES : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t st3[KW][NSTG > 3 ? St::BYTES : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -147,40 +235,40 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
     if ((int)blockIdx.x >= n_wg) return;
     const int b_begin = wave * NBW;
 
-    // ---- weight loads of one tile: per load group, 16 bytes of codes and
-    // the group's scales; rows past M and blocks past the row read zeros ----
+    // ---- a tile's share of this wave into one stage: rows past M, and
+    // units and scales of blocks past the row, read as zeros ----
     const uint32_t row_bytes = (uint32_t)(qoff + nb * BB);
-    struct Grp { uint32_t q[4]; uint32_t s[BPG / 2]; };
-    auto load_tile = [&](Grp (&dst)[NG], int tile) {
-        const int r0 = tile * kTileRows;
-        const int rows = tile < n_tiles ? (M - r0 < kTileRows ? M - r0 : kTileRows) : 0;
-        const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(W + (uint64_t)(rows > 0 ? r0 : 0) * pitch), 0,
-            (int)(rows > 0 ? (uint32_t)(rows - 1) * pitch + row_bytes : 0u), BUFFER_FLAGS);
-        const uint32_t ro = (uint32_t)j * pitch;
+    auto issue = [&](auto &stg, int tl) {
+        const int r0 = tl * kTileRows;
+        const int rows = tl < n_tiles ? (M - r0 < kTileRows ? M - r0 : kTileRows) : 0;
+        const i32x4 wres = buffer_words(W + (uint64_t)(rows > 0 ? r0 : 0) * pitch,
+                                        rows > 0 ? (uint32_t)(rows - 1) * pitch + row_bytes : 0u);
+        const uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(&stg[wave][0]);
 #pragma unroll
-        for (int p = 0; p < NG; ++p) {
-            const int b0 = b_begin + p * BPG;
-            const int mine = (WT == W_Q4_0) ? b0 + g : b0 + (g >> 1);      // block of this lane's 16 bytes
-            const uint32_t qo = mine < nb ? ro + (uint32_t)(qoff + BB * b0 + 16 * g) : OUT_OF_RANGE;
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(wres, qo, 0, 0);
+        for (int i = 0; i < St::NI; ++i) {
+            const int r = i * St::RPI + lane / St::U;
+            const int u = swz<St::U>(r, lane % St::U);
+            const int blk = b_begin + (16 * u) / BB;
+            const uint32_t off = blk < nb ? (uint32_t)r * pitch + (uint32_t)(qoff + BB * b_begin + 16 * u)
+                                          : OUT_OF_RANGE;
+            load_to_lds<16>(wres, base + 1024 * i, off);
+        }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dst[p].q[e] = v[e];
-            const uint32_t so = b0 < nb ? ro + (uint32_t)(2 * b0) : OUT_OF_RANGE;
-            if constexpr (BPG == 4) {
-                const auto s2 = __builtin_amdgcn_raw_buffer_load_b64(wres, so, 0, 0);
-                dst[p].s[0] = s2[0];
-                dst[p].s[1] = s2[1];
-            } else {
-                dst[p].s[0] = __builtin_amdgcn_raw_buffer_load_b32(wres, so, 0, 0);
-            }
+        for (int i = 0; i < St::NS; ++i) {
+            const int byte = 256 * i + 4 * lane;
+            const int r = byte / St::SR, rb = byte % St::SR;
+            const uint32_t off = (r < kTileRows && b_begin + rb / 2 < nb)
+                                     ? (uint32_t)r * pitch + (uint32_t)(2 * b_begin + rb)
+                                     : OUT_OF_RANGE;
+            load_to_lds<4>(wres, base + St::CODE_BYTES + 256 * i, off);
         }
     };
 
-    // the first tile's weights are in flight while the activations are set up
-    Grp cur[NG];
+    // the first NSTG-1 tiles are in flight while the activations are set up
     int tile = blockIdx.x;
-    load_tile(cur, tile);
+    issue(st0, tile);
+    if constexpr (NSTG > 2) issue(st1, tile + n_wg);
+    if constexpr (NSTG > 3) issue(st2, tile + 2 * n_wg);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- activation fragments of this wave's blocks; channel j = token
@@ -255,11 +343,30 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
     const uint32_t magic = 0x43004300u;    // bf16 128.0 in both halves
     // one tile: unpack, matrix products, bias and scales; then the partial
     // sums of the KW waves (K ranges) meet in LDS and wave 0 stores the rows
-    auto consume = [&](const Grp (&c)[NG], int tl, int it) {
+    auto consume = [&](auto &stg, int tl, int it) {
+        const uint8_t *base = stg[wave];
+        // row j's scales, then its units 4p + g
+        uint32_t sc[St::SR / 4];
+        if constexpr (St::SR == 8) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(base + St::CODE_BYTES + St::SR * j);
+            sc[0] = v.x;
+            sc[1] = v.y;
+        } else {
+#pragma unroll
+            for (int h = 0; h < St::SR / 16; ++h) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(base + St::CODE_BYTES + St::SR * j + 16 * h);
+                sc[4 * h] = v.x;
+                sc[4 * h + 1] = v.y;
+                sc[4 * h + 2] = v.z;
+                sc[4 * h + 3] = v.w;
+            }
+        }
+        const uint8_t *rowp = base + (j / St::RPI) * 1024 + (j % St::RPI) * St::SB;
         float yp0 = 0.0f, yp1 = 0.0f;
 #pragma unroll
         for (int p = 0; p < NG; ++p) {
-            uint32_t d0 = c[p].q[0], d1 = c[p].q[1], d2 = c[p].q[2], d3 = c[p].q[3];
+            const uint4 cv = *reinterpret_cast<const uint4 *>(rowp + 16 * swz<St::U>(j, 4 * p + g));
+            uint32_t d0 = cv.x, d1 = cv.y, d2 = cv.z, d3 = cv.w;
             // regroup: the four lane groups of each matrix instruction hold
             // disjoint code sets of one block
             swap32(d0, d2);
@@ -292,7 +399,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
                 // a block past the row (its codes and activations read as
                 // zeros) may pick up a scale from the bytes after the row's
                 // scales: weight it by 0
-                const uint32_t sw = c[p].s[t / 2];
+                const uint32_t sw = sc[(p * BPG + t) / 2];
                 const float ds = (float)__builtin_bit_cast(_Float16, (uint16_t)((t & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
                 const float d = (b_begin + p * BPG + t < nb) ? ds : 0.0f;
                 yp0 = fmaf(d, D[0] + D[1] + cb[p * BPG + t][0], yp0);
@@ -318,57 +425,79 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
         }
     };
 
-    // two tile buffers in turn (no register copies between iterations, so
-    // the wait before a tile's use covers only that tile's loads); the tile
-    // after the last one reads nothing.  The loop bounds are uniform over
-    // the workgroup.
-    Grp alt[NG];
-    for (int it = 0;; it += 2) {
+    // stage s holds tiles it = s (mod NSTG); before a tile is consumed the
+    // tile NSTG-1 steps ahead is issued into the stage the previous step freed.  The
+    // steps past the last tile issue loads that read nothing.  The loop bounds
+    // are uniform over the workgroup.
+    for (int it = 0;; it += NSTG) {
         if (tile >= n_tiles) break;
-        load_tile(alt, tile + n_wg);
-        __builtin_amdgcn_sched_barrier(0);     // issue the prefetch first
-        consume(cur, tile, it);
+        if constexpr (NSTG == 2) issue(st1, tile + n_wg);
+        else if constexpr (NSTG == 3) issue(st2, tile + 2 * n_wg);
+        else issue(st3, tile + 3 * n_wg);
+        wait_vm<(NSTG - 1) * (St::NI + St::NS)>();     // this tile's loads have landed
+        consume(st0, tile, it);
         tile += n_wg;
         if (tile >= n_tiles) break;
-        load_tile(cur, tile + n_wg);
-        __builtin_amdgcn_sched_barrier(0);
-        consume(alt, tile, it + 1);
+        issue(st0, tile + (NSTG - 1) * n_wg);
+        wait_vm<(NSTG - 1) * (St::NI + St::NS)>();     // this tile's loads have landed
+        consume(st1, tile, it + 1);
         tile += n_wg;
+        if constexpr (NSTG > 2) {
+            if (tile >= n_tiles) break;
+            issue(st1, tile + (NSTG - 1) * n_wg);
+            wait_vm<(NSTG - 1) * (St::NI + St::NS)>();
+            consume(st2, tile, it + 2);
+            tile += n_wg;
+        }
+        if constexpr (NSTG > 3) {
+            if (tile >= n_tiles) break;
+            issue(st2, tile + (NSTG - 1) * n_wg);
+            wait_vm<(NSTG - 1) * (St::NI + St::NS)>();
+            consume(st3, tile, it + 3);
+            tile += n_wg;
+        }
     }
+    // no load may still write this workgroup's LDS after it ends
+    wait_vm<0>();
 }
 
 using MfKernel = void (*)(const MfArgs);
 
-template <int WT, int KW>
-MfKernel pick_mf_nbw(int nbw)
+// Eight waves share a tile (each one eighth of K, so that two waves per SIMD
+// hide each other's latencies), with NBW = 4, 8 or 16 blocks per wave (K up
+// to 4096).  Q4_0 tiles are half the bytes of Q8_0 ones, so they get a
+// stage more (measured: 4 for Q4_0, 3 for Q8_0 at K = 2048).
+constexpr int kWaves = 8;
+template <int WT> constexpr int max_stages() { return WT == W_Q4_0 ? 4 : 3; }
+
+// The kernel for (type, NBW) and its LDS bytes.
+template <int WT>
+MfKernel pick_mf(int nbw, int *lds)
 {
+    constexpr int D = max_stages<WT>();
     switch (nbw) {
-    case 4: return gemv_mf_kernel<WT, KW, 4>;
-    case 8: return gemv_mf_kernel<WT, KW, 8>;
-    case 16: return gemv_mf_kernel<WT, KW, 16>;
+    case 4: *lds = mf_lds_bytes<WT, kWaves, 4>(mf_stages<WT, kWaves, 4, D>()); return gemv_mf_kernel<WT, kWaves, 4, D>;
+    case 8: *lds = mf_lds_bytes<WT, kWaves, 8>(mf_stages<WT, kWaves, 8, D>()); return gemv_mf_kernel<WT, kWaves, 8, D>;
+    case 16: *lds = mf_lds_bytes<WT, kWaves, 16>(mf_stages<WT, kWaves, 16, D>()); return gemv_mf_kernel<WT, kWaves, 16, D>;
     default: return nullptr;
     }
 }
 
-// Waves per workgroup (each a K range) and blocks per wave for a row of nb
-// blocks: 4 waves up to 64 blocks (K = 2048), 8 waves up to 128 (K = 4096).
-bool mf_shape(int64_t nb, int *kw, int *nbw)
+// Blocks per wave for a row of nb blocks (0 if unsupported).
+int mf_nbw(int64_t nb)
 {
-    if (nb <= 0 || nb > 128) return false;
-    *kw = nb <= 64 ? 4 : 8;
-    const int64_t per = (nb + *kw - 1) / *kw;
-    *nbw = per <= 4 ? 4 : per <= 8 ? 8 : 16;
-    return true;
+    if (nb <= 0 || nb > 16 * kWaves) return 0;
+    const int64_t per = (nb + kWaves - 1) / kWaves;
+    return per <= 4 ? 4 : per <= 8 ? 8 : 16;
 }
 
 }  // namespace
 
 bool gemv_mf_supported(const GemvTask *tasks, int count)
 {
-    int kw, nbw;
     const int type = tasks[0].w.type;
     const int64_t K = tasks[0].w.K;
-    if (!(type == W_Q4_0 || type == W_Q8_0) || K % 32 != 0 || !mf_shape(K / 32, &kw, &nbw)) return false;
+    if (!(type == W_Q4_0 || type == W_Q8_0) || K % 32 != 0 || mf_nbw(K / 32) == 0) return false;
     // a 16-row tile is one buffer resource with 32-bit offsets
     // and the activations of up to 8 tokens another (byte offsets < 2^31)
     for (int i = 0; i < count; ++i) {
@@ -386,18 +515,18 @@ hipError_t launch_gemv_mf(const GemvTask *tasks, int count, hipStream_t stream)
     const int type = tasks[0].w.type;
     const int64_t K = tasks[0].w.K;
     const int64_t N = tasks[0].x.N;
-    int kw, nbw;
-    if (!mf_shape(K / 32, &kw, &nbw)) return hipErrorInvalidValue;
+    const int nbw = mf_nbw(K / 32);
     MfKernel k = nullptr;
-    if (type == W_Q4_0) k = (kw == 4) ? pick_mf_nbw<W_Q4_0, 4>(nbw) : pick_mf_nbw<W_Q4_0, 8>(nbw);
-    else if (type == W_Q8_0) k = (kw == 4) ? pick_mf_nbw<W_Q8_0, 4>(nbw) : pick_mf_nbw<W_Q8_0, 8>(nbw);
+    int lds = kLdsBytes;
+    if (type == W_Q4_0) k = pick_mf<W_Q4_0>(nbw, &lds);
+    else if (type == W_Q8_0) k = pick_mf<W_Q8_0>(nbw, &lds);
     if (!k) return hipErrorInvalidValue;
     int64_t tiles_total = 0;
     for (int i = 0; i < count; ++i) tiles_total += (tasks[i].w.M + kTileRows - 1) / kTileRows;
     if (tiles_total == 0 || N == 0) return hipSuccess;
     // a workgroup streams several tiles with its activation fragments
-    // resident: at most 2 workgroups of 4 waves (1 of 8) per CU
-    const int64_t cap = kw == 4 ? 512 : 256;
+    // resident: as many workgroups as the LDS of the 256 CUs holds at once
+    const int64_t cap = 256 * (int64_t)(kLdsBytes / lds);
     for (int64_t n0 = 0; n0 < N; n0 += 8) {
         MfArgs a = {};
         a.N = (int32_t)(N - n0 < 8 ? N - n0 : 8);
@@ -422,7 +551,7 @@ hipError_t launch_gemv_mf(const GemvTask *tasks, int count, hipStream_t stream)
             it.wg_count = (int32_t)wgs;
             if (wgs > wg_max) wg_max = (int32_t)wgs;
         }
-        hipLaunchKernelGGL(k, dim3((unsigned)wg_max, (unsigned)a.n_items), dim3(64 * kw), 0, stream, a);
+        hipLaunchKernelGGL(k, dim3((unsigned)wg_max, (unsigned)a.n_items), dim3(64 * kWaves), 0, stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -225,6 +225,8 @@ GEMV_CASES = [
     # past that kernel's range
     ("Q4_0", 40, 96, 5), ("Q4_0", 257, 160, 6), ("Q4_0", 17, 1056, 5), ("Q4_0", 1000, 4096, 6),
     ("Q8_0", 31, 2080, 6), ("Q8_0", 1001, 4096, 5), ("Q8_0", 64, 4128, 8),
+    # 3 and 4 tokens over 8192 rows or more take the matrix cores too
+    ("Q4_0", 8200, 2048, 3), ("Q8_0", 8195, 1024, 4),
 ]
 
 
