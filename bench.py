@@ -34,7 +34,8 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
 HERE = os.path.dirname(os.path.abspath(__file__))
 # HBM traffic of the dominant kernel, from hardware counters (see traffic_probe)
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "gemv_q4_0_gate_up_hbm_traffic.md")
-GEMV_SOURCE = os.path.join(HERE, "quantized_matmul_ggml_amd", "csrc", "gemv.hip")
+# the dominant kernel's device code: its source file and the header it includes
+GEMV_SOURCES = [os.path.join(HERE, "quantized_matmul_ggml_amd", "csrc", f) for f in ("gemv.hip", "wave_reduce.h")]
 COPY_PROBE_BYTES = 256 << 20   # calibration copy: 256 MiB read + 256 MiB written
 
 
@@ -288,8 +289,11 @@ def main():
 
 def gemv_source_hash():
     import hashlib
-    with open(GEMV_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in GEMV_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def stored_traffic():
