@@ -15,7 +15,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqmm.so")
-SOURCES = ["qmm_api.cpp", "quant.hip", "gemv.hip", "gemv_i8.hip", "gemv_mfma.hip", "gemv_mf.hip",
+SOURCES = ["qmm_api.cpp", "quant.hip", "gemv.hip", "gemv_i8.hip", "gemv_mf.hip",
            "gemm.hip", "records.hip"]
 ARCH = os.environ.get("QMM_OFFLOAD_ARCH", "gfx950")
 

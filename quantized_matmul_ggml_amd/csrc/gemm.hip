@@ -26,6 +26,7 @@
 // zero; blocks past the end of K get a zero scale and zero tokens.
 #include "qmm_internal.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace qmm {
@@ -552,6 +553,25 @@ hipError_t launch_gemm(const WeightView &w, const ActView &x, const OutView &y,
     if (w.type == W_Q8_0) return launch_typed<W_Q8_0>(a, tiles, stream);
     if (w.type == W_F16) return launch_typed<W_F16>(a, tiles, stream);
     return hipErrorInvalidValue;
+}
+
+// Raise a kernel's dynamic-LDS limit once (the attribute persists for the
+// process); later launches, including those recorded into graphs, reuse it.
+hipError_t allow_dynamic_lds(const void *fn, int bytes)
+{
+    static std::mutex mu;
+    static const void *fns[64];
+    static int granted[64];
+    static int n = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < n; ++i)
+        if (fns[i] == fn && granted[i] >= bytes) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    for (int i = 0; i < n; ++i)
+        if (fns[i] == fn) { granted[i] = bytes; return hipSuccess; }
+    if (n < 64) { fns[n] = fn; granted[n] = bytes; ++n; }
+    return hipSuccess;
 }
 
 }  // namespace qmm

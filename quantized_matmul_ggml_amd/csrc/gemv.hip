@@ -618,7 +618,6 @@ hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t strea
     if (m_total == 0 || N == 0) return hipSuccess;
     // The matrix-core kernels' cost does not grow with the token count.
     if (use_matrix_cores(N, m_total) && gemv_mf_supported(tasks, count)) return launch_gemv_mf(tasks, count, stream);
-    if (N >= 5 && gemv_mfma_supported(type, K, N)) return launch_gemv_mfma(tasks, count, stream);
 
     // Tokens are processed in chunks of at most 8; a chunk shrinks (halving)
     // until a register-resident configuration exists for it.

@@ -60,11 +60,14 @@ static_assert(sizeof(MfItem) == 64, "one 64-byte record per item");
 
 struct MfArgs {
     int32_t N;            // tokens of this launch (<= 8)
-    int32_t K;
-    int32_t qoff;
-    int32_t nb;           // 32-blocks per row
+    int32_t K;            // K of this pass (32 nb); x points at its first element
+    int32_t qoff;         // byte offset of the codes in a row
+    int32_t nb;           // 32-blocks of this pass (<= 128)
     int32_t n_items;
-    int32_t pad[11];
+    int32_t kb0;          // first block of this pass within the row
+    int32_t nb_row;       // 32-blocks per row
+    int32_t accumulate;   // add to y (a later pass over K) instead of storing
+    int32_t pad[8];
     MfItem item[kMaxMfItems];
 };
 
@@ -229,15 +232,15 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
     float *const Y = itm.y;
     const uint32_t pitch = itm.pitch, x_pitch = itm.x_pitch, y_pitch = itm.y_pitch;
     const int M = itm.M, n_tiles = itm.n_tiles, n_wg = itm.wg_count;
-    const int N = a.N, K = a.K, qoff = a.qoff, nb = a.nb;
+    const int N = a.N, K = a.K, qoff = a.qoff, nb = a.nb, kb0 = a.kb0, nb_row = a.nb_row, acc = a.accumulate;
     asm volatile("" ::"s"(W), "s"(X), "s"(Y), "s"(pitch), "s"(x_pitch), "s"(y_pitch), "s"(M),
-                 "s"(n_tiles), "s"(n_wg), "s"(N), "s"(K), "s"(qoff), "s"(nb));
+                 "s"(n_tiles), "s"(n_wg), "s"(N), "s"(K), "s"(qoff), "s"(nb), "s"(kb0), "s"(nb_row), "s"(acc));
     if ((int)blockIdx.x >= n_wg) return;
     const int b_begin = wave * NBW;
 
     // ---- a tile's share of this wave into one stage: rows past M, and
     // units and scales of blocks past the row, read as zeros ----
-    const uint32_t row_bytes = (uint32_t)(qoff + nb * BB);
+    const uint32_t row_bytes = (uint32_t)(qoff + nb_row * BB);
     auto issue = [&](auto &stg, int tl) {
         const int r0 = tl * kTileRows;
         const int rows = tl < n_tiles ? (M - r0 < kTileRows ? M - r0 : kTileRows) : 0;
@@ -249,7 +252,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
             const int r = i * St::RPI + lane / St::U;
             const int u = swz<St::U>(r, lane % St::U);
             const int blk = b_begin + (16 * u) / BB;
-            const uint32_t off = blk < nb ? (uint32_t)r * pitch + (uint32_t)(qoff + BB * b_begin + 16 * u)
+            const uint32_t off = blk < nb ? (uint32_t)r * pitch + (uint32_t)(qoff + BB * (kb0 + b_begin) + 16 * u)
                                           : OUT_OF_RANGE;
             load_to_lds<16>(wres, base + 1024 * i, off);
         }
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
             const int byte = 256 * i + 4 * lane;
             const int r = byte / St::SR, rb = byte % St::SR;
             const uint32_t off = (r < kTileRows && b_begin + rb / 2 < nb)
-                                     ? (uint32_t)r * pitch + (uint32_t)(2 * b_begin + rb)
+                                     ? (uint32_t)r * pitch + (uint32_t)(2 * (kb0 + b_begin) + rb)
                                      : OUT_OF_RANGE;
             load_to_lds<4>(wres, base + St::CODE_BYTES + 256 * i, off);
         }
@@ -419,8 +422,10 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
             }
             const int m = tl * kTileRows + j;
             if (m < M) {
-                if (2 * g < N) Y[(uint64_t)(2 * g) * y_pitch + m] = s0;
-                if (2 * g + 1 < N) Y[(uint64_t)(2 * g + 1) * y_pitch + m] = s1;
+                float *y0 = Y + (uint64_t)(2 * g) * y_pitch + m;
+                float *y1 = y0 + y_pitch;
+                if (2 * g < N) *y0 = acc ? *y0 + s0 : s0;
+                if (2 * g + 1 < N) *y1 = acc ? *y1 + s1 : s1;
             }
         }
     };
@@ -463,11 +468,14 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
 
 using MfKernel = void (*)(const MfArgs);
 
-// Eight waves share a tile (each one eighth of K, so that two waves per SIMD
-// hide each other's latencies), with NBW = 4, 8 or 16 blocks per wave (K up
-// to 4096).  Q4_0 tiles are half the bytes of Q8_0 ones, so they get a
+// Eight waves share a tile (each one eighth of the pass's K, so that two
+// waves per SIMD hide each other's latencies), with NBW = 4, 8 or 16 blocks
+// per wave.  Q4_0 tiles are half the bytes of Q8_0 ones, so they get a
 // stage more (measured: 4 for Q4_0, 3 for Q8_0 at K = 2048).
 constexpr int kWaves = 8;
+// Blocks of K one launch covers (16 per wave); longer rows take several
+// launches, the later ones adding to y.
+constexpr int kPassBlocks = 16 * kWaves;
 template <int WT> constexpr int max_stages() { return WT == W_Q4_0 ? 4 : 3; }
 
 // The kernel for (type, NBW) and its LDS bytes.
@@ -483,10 +491,10 @@ MfKernel pick_mf(int nbw, int *lds)
     }
 }
 
-// Blocks per wave for a row of nb blocks (0 if unsupported).
+// Blocks per wave for a pass of nb blocks (0 if out of range).
 int mf_nbw(int64_t nb)
 {
-    if (nb <= 0 || nb > 16 * kWaves) return 0;
+    if (nb <= 0 || nb > kPassBlocks) return 0;
     const int64_t per = (nb + kWaves - 1) / kWaves;
     return per <= 4 ? 4 : per <= 8 ? 8 : 16;
 }
@@ -497,7 +505,7 @@ bool gemv_mf_supported(const GemvTask *tasks, int count)
 {
     const int type = tasks[0].w.type;
     const int64_t K = tasks[0].w.K;
-    if (!(type == W_Q4_0 || type == W_Q8_0) || K % 32 != 0 || mf_nbw(K / 32) == 0) return false;
+    if (!(type == W_Q4_0 || type == W_Q8_0) || K % 32 != 0 || K == 0) return false;
     // a 16-row tile is one buffer resource with 32-bit offsets
     // and the activations of up to 8 tokens another (byte offsets < 2^31)
     for (int i = 0; i < count; ++i) {
@@ -515,45 +523,53 @@ hipError_t launch_gemv_mf(const GemvTask *tasks, int count, hipStream_t stream)
     const int type = tasks[0].w.type;
     const int64_t K = tasks[0].w.K;
     const int64_t N = tasks[0].x.N;
-    const int nbw = mf_nbw(K / 32);
-    MfKernel k = nullptr;
-    int lds = kLdsBytes;
-    if (type == W_Q4_0) k = pick_mf<W_Q4_0>(nbw, &lds);
-    else if (type == W_Q8_0) k = pick_mf<W_Q8_0>(nbw, &lds);
-    if (!k) return hipErrorInvalidValue;
+    const int64_t nb_row = K / 32;
     int64_t tiles_total = 0;
     for (int i = 0; i < count; ++i) tiles_total += (tasks[i].w.M + kTileRows - 1) / kTileRows;
-    if (tiles_total == 0 || N == 0) return hipSuccess;
-    // a workgroup streams several tiles with its activation fragments
-    // resident: as many workgroups as the LDS of the 256 CUs holds at once
-    const int64_t cap = 256 * (int64_t)(kLdsBytes / lds);
+    if (tiles_total == 0 || N == 0 || nb_row == 0) return hipSuccess;
     for (int64_t n0 = 0; n0 < N; n0 += 8) {
-        MfArgs a = {};
-        a.N = (int32_t)(N - n0 < 8 ? N - n0 : 8);
-        a.K = (int32_t)K;
-        a.qoff = (int32_t)quant_offset(K);
-        a.nb = (int32_t)(K / 32);
-        int32_t wg_max = 0;
-        for (int i = 0; i < count; ++i) {
-            if (tasks[i].w.M == 0) continue;
-            MfItem &it = a.item[a.n_items++];
-            it.w = tasks[i].w.base;
-            it.pitch = (uint32_t)tasks[i].w.pitch;
-            it.M = (int32_t)tasks[i].w.M;
-            it.x = static_cast<const float *>(tasks[i].x.data) + (uint64_t)n0 * tasks[i].x.pitch_elems;
-            it.x_pitch = (uint32_t)tasks[i].x.pitch_elems;
-            it.y = tasks[i].y.data + (uint64_t)n0 * tasks[i].y.pitch_elems;
-            it.y_pitch = (uint32_t)tasks[i].y.pitch_elems;
-            it.n_tiles = (int32_t)((tasks[i].w.M + kTileRows - 1) / kTileRows);
-            int64_t wgs = (int64_t)it.n_tiles * cap / tiles_total;
-            if (wgs < 1) wgs = 1;
-            if (wgs > it.n_tiles) wgs = it.n_tiles;
-            it.wg_count = (int32_t)wgs;
-            if (wgs > wg_max) wg_max = (int32_t)wgs;
+        // passes over K in stream order: the first stores y, the others add
+        for (int64_t kb0 = 0; kb0 < nb_row; kb0 += kPassBlocks) {
+            const int64_t nb = nb_row - kb0 < kPassBlocks ? nb_row - kb0 : kPassBlocks;
+            MfKernel k = nullptr;
+            int lds = kLdsBytes;
+            if (type == W_Q4_0) k = pick_mf<W_Q4_0>(mf_nbw(nb), &lds);
+            else if (type == W_Q8_0) k = pick_mf<W_Q8_0>(mf_nbw(nb), &lds);
+            if (!k) return hipErrorInvalidValue;
+            // a workgroup streams several tiles with its activation fragments
+            // resident: as many workgroups as the LDS of the 256 CUs holds
+            const int64_t cap = 256 * (int64_t)(kLdsBytes / lds);
+            MfArgs a = {};
+            a.N = (int32_t)(N - n0 < 8 ? N - n0 : 8);
+            a.K = (int32_t)(32 * nb);
+            a.qoff = (int32_t)quant_offset(K);
+            a.nb = (int32_t)nb;
+            a.kb0 = (int32_t)kb0;
+            a.nb_row = (int32_t)nb_row;
+            a.accumulate = kb0 > 0;
+            int32_t wg_max = 0;
+            for (int i = 0; i < count; ++i) {
+                if (tasks[i].w.M == 0) continue;
+                MfItem &it = a.item[a.n_items++];
+                it.w = tasks[i].w.base;
+                it.pitch = (uint32_t)tasks[i].w.pitch;
+                it.M = (int32_t)tasks[i].w.M;
+                it.x = static_cast<const float *>(tasks[i].x.data) + (uint64_t)n0 * tasks[i].x.pitch_elems +
+                       (uint64_t)32 * kb0;
+                it.x_pitch = (uint32_t)tasks[i].x.pitch_elems;
+                it.y = tasks[i].y.data + (uint64_t)n0 * tasks[i].y.pitch_elems;
+                it.y_pitch = (uint32_t)tasks[i].y.pitch_elems;
+                it.n_tiles = (int32_t)((tasks[i].w.M + kTileRows - 1) / kTileRows);
+                int64_t wgs = (int64_t)it.n_tiles * cap / tiles_total;
+                if (wgs < 1) wgs = 1;
+                if (wgs > it.n_tiles) wgs = it.n_tiles;
+                it.wg_count = (int32_t)wgs;
+                if (wgs > wg_max) wg_max = (int32_t)wgs;
+            }
+            hipLaunchKernelGGL(k, dim3((unsigned)wg_max, (unsigned)a.n_items), dim3(64 * kWaves), 0, stream, a);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
         }
-        hipLaunchKernelGGL(k, dim3((unsigned)wg_max, (unsigned)a.n_items), dim3(64 * kWaves), 0, stream, a);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }

@@ -99,15 +99,12 @@ hipError_t launch_gemv_i8(const WeightView &w, const WeightView &xq, const OutVi
 hipError_t launch_gemv_swiglu(const WeightView &wg, const WeightView &wu, const ActView &x,
                               const OutView &h, hipStream_t stream);
 
-// The matrix-core GEMV for Q4_0 / Q8_0 weights (gemv_mfma.hip): whether its
-// LDS image of the activations fits for (K, N), and its launcher.
-bool gemv_mfma_supported(int type, int64_t K, int64_t N);
-hipError_t launch_gemv_mfma(const GemvTask *tasks, int count, hipStream_t stream);
 // The matrix-core GEMV with register-resident activation fragments
-// (gemv_mf.hip): Q4_0 / Q8_0 weights, K <= 4096, weight pitch <= 2^27.
+// (gemv_mf.hip): Q4_0 / Q8_0 weights, weight pitch <= 2^27; K beyond 4096 in
+// passes that add to y.
 bool gemv_mf_supported(const GemvTask *tasks, int count);
 hipError_t launch_gemv_mf(const GemvTask *tasks, int count, hipStream_t stream);
-// Grant a kernel more than the default dynamic LDS (once per size).
+// Grant a kernel more than the default dynamic LDS (once per size; gemm.hip).
 hipError_t allow_dynamic_lds(const void *fn, int bytes);
 
 // GGUF-style block records (records.hip): bytes of one record (18 for

@@ -227,6 +227,8 @@ GEMV_CASES = [
     ("Q8_0", 31, 2080, 6), ("Q8_0", 1001, 4096, 5), ("Q8_0", 64, 4128, 8),
     # 3 and 4 tokens over 8192 rows or more take the matrix cores too
     ("Q4_0", 8200, 2048, 3), ("Q8_0", 8195, 1024, 4),
+    # K beyond 128 blocks: passes that add to y (Wdown's K = 5632; four passes)
+    ("Q4_0", 300, 5632, 6), ("Q8_0", 77, 16384, 5),
 ]
 
 
