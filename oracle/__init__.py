@@ -8,7 +8,8 @@ marshals numpy arrays.
 
 What it computes (the pages it follows are cited in ``qmm_oracle.h``):
   * IEEE binary16 / bfloat16 conversions written from the format definitions;
-  * Q8_0 / Q4_0 block quantization of fp32 rows and the row-planar packing;
+  * Q8_0 / Q4_0 block quantization of fp32 rows (32-weight blocks, and the
+    64-weight variants Q8_B64 / Q4_B64) and the row-planar packing;
   * the exact dequantized weights W';
   * MUL_MAT y[n][m] = sum_k W'[m][k] x[n][k] accumulated in binary64, with
     the magnitude sum a[n][m] = sum_k |W'[m][k] x[n][k]| used by tolerances;
@@ -30,7 +31,7 @@ _SRC = os.path.join(_HERE, "qmm_oracle.c")
 _SO = os.environ.get("QMM_ORACLE_LIB") or os.path.join(_HERE, "libqmm_oracle.so")
 
 # Own type numbering (mirrors qmm_oracle.h, not the GPU library's enum).
-F32, F16, BF16, Q8_0, Q4_0 = 0, 1, 2, 3, 4
+F32, F16, BF16, Q8_0, Q4_0, Q8_B64, Q4_B64 = 0, 1, 2, 3, 4, 5, 6
 # Quantization rules: the default ones, and the pages' symmetric Q4 rule.
 RULE_DEFAULT, RULE_Q4_SYM7 = 0, 1
 
@@ -83,6 +84,10 @@ def lib() -> ctypes.CDLL:
         h.orc_quantize_rows_rule.restype = ci
         h.orc_quantize_block_q4_sym7.argtypes = [f32p, u16p, u8p]
         h.orc_quantize_block_q4_sym7.restype = None
+        h.orc_quantize_block_q8_b64.argtypes = [f32p, u16p, ctypes.POINTER(ctypes.c_int8)]
+        h.orc_quantize_block_q8_b64.restype = None
+        h.orc_quantize_block_q4_b64.argtypes = [f32p, ci, u16p, u8p]
+        h.orc_quantize_block_q4_b64.restype = None
         h.orc_dequantize_rows.argtypes = [ci, u8p, sz, i64, i64, f32p]
         h.orc_dequantize_rows.restype = ci
         h.orc_mul_mat_rows.argtypes = [ci, u8p, sz, i64, i64, vp, ci, i64, ci,
@@ -167,6 +172,24 @@ def quantize_block(type_: int, w32) -> tuple[int, np.ndarray]:
                                          _ptr(q, ctypes.c_uint8))
     else:
         raise ValueError("quantize_block: type must be Q8_0 or Q4_0")
+    return int(sb[0]), q
+
+
+def quantize_block64(type_: int, w64, rule: int = RULE_DEFAULT) -> tuple[int, np.ndarray]:
+    """One 64-weight block -> (fp16 scale bits, codes): Q8_B64 int8 codes, or
+    Q4_B64 nibbles in [0, 15] (rule RULE_Q4_SYM7: the amax/7 scale)."""
+    w = _c(w64, np.float32).reshape(64)
+    sb = np.zeros(1, np.uint16)
+    if type_ == Q8_B64:
+        q = np.zeros(64, np.int8)
+        lib().orc_quantize_block_q8_b64(_ptr(w, ctypes.c_float), _ptr(sb, ctypes.c_uint16),
+                                        _ptr(q, ctypes.c_int8))
+    elif type_ == Q4_B64:
+        q = np.zeros(64, np.uint8)
+        lib().orc_quantize_block_q4_b64(_ptr(w, ctypes.c_float), 7 if rule == RULE_Q4_SYM7 else 8,
+                                        _ptr(sb, ctypes.c_uint16), _ptr(q, ctypes.c_uint8))
+    else:
+        raise ValueError("quantize_block64: type must be Q8_B64 or Q4_B64")
     return int(sb[0]), q
 
 

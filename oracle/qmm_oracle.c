@@ -133,23 +133,24 @@ void orc_bf16_to_f32_n(const uint16_t *src, float *dst, size_t n)
  *           to [0, 15] (offset binary for q in [-8, 7]).
  * ------------------------------------------------------------------------ */
 
-static float block_amax(const float w[32])
+static float block_amax(const float *w, int n)
 {
     float amax = 0.0f;
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < n; ++i) {
         const float v = fabsf(w[i]);
         if (v > amax) amax = v;
     }
     return amax;
 }
 
-void orc_quantize_block_q8_0(const float w[32], uint16_t *scale_bits, int8_t q[32])
+/* The Q8 steps over a block of n values (scale divisor 127). */
+static void quantize_q8(const float *w, int n, uint16_t *scale_bits, int8_t *q)
 {
-    const float s = block_amax(w) / 127.0f;
+    const float s = block_amax(w, n) / 127.0f;
     const uint16_t h = orc_f32_to_f16(s);
     const float d = orc_f16_to_f32(h);
     *scale_bits = h;
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < n; ++i) {
         if (d == 0.0f) { q[i] = 0; continue; }
         float r = roundf(w[i] / d);
         if (r > 127.0f) r = 127.0f;
@@ -158,31 +159,16 @@ void orc_quantize_block_q8_0(const float w[32], uint16_t *scale_bits, int8_t q[3
     }
 }
 
-void orc_quantize_block_q4_0(const float w[32], uint16_t *scale_bits, uint8_t nib[32])
+/* The Q4 steps over a block of n values with scale divisor div (8: the
+ * offset-binary Q4_0 rule, nibble = clamp(q + 8, 0, 15); 7: the pages'
+ * symmetric rule, q clamped to [-8, 7], stored as q + 8 -- the same thing). */
+static void quantize_q4(const float *w, int n, float div, uint16_t *scale_bits, uint8_t *nib)
 {
-    const float s = block_amax(w) / 8.0f;
+    const float s = block_amax(w, n) / div;
     const uint16_t h = orc_f32_to_f16(s);
     const float d = orc_f16_to_f32(h);
     *scale_bits = h;
-    for (int i = 0; i < 32; ++i) {
-        if (d == 0.0f) { nib[i] = 8; continue; }
-        float r = roundf(w[i] / d) + 8.0f;
-        if (r > 15.0f) r = 15.0f;
-        if (r < 0.0f) r = 0.0f;
-        nib[i] = (uint8_t)r;
-    }
-}
-
-/* The pages' own Q4 rule ("A Complete Guide to llama.cpp and Customization
- * with C++", §2.2): Delta = max|w| / 7, q in [-8, 7]; stored, like Q4_0, as
- * the offset-binary nibble q + 8 with the fp16 Delta. */
-void orc_quantize_block_q4_sym7(const float w[32], uint16_t *scale_bits, uint8_t nib[32])
-{
-    const float s = block_amax(w) / 7.0f;
-    const uint16_t h = orc_f32_to_f16(s);
-    const float d = orc_f16_to_f32(h);
-    *scale_bits = h;
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < n; ++i) {
         if (d == 0.0f) { nib[i] = 8; continue; }
         float q = roundf(w[i] / d);
         if (q > 7.0f) q = 7.0f;
@@ -191,11 +177,51 @@ void orc_quantize_block_q4_sym7(const float w[32], uint16_t *scale_bits, uint8_t
     }
 }
 
+void orc_quantize_block_q8_0(const float w[32], uint16_t *scale_bits, int8_t q[32])
+{
+    quantize_q8(w, 32, scale_bits, q);
+}
+
+void orc_quantize_block_q4_0(const float w[32], uint16_t *scale_bits, uint8_t nib[32])
+{
+    quantize_q4(w, 32, 8.0f, scale_bits, nib);
+}
+
+/* The pages' own Q4 rule ("A Complete Guide to llama.cpp and Customization
+ * with C++", §2.2): Delta = max|w| / 7, q in [-8, 7]; stored, like Q4_0, as
+ * the offset-binary nibble q + 8 with the fp16 Delta. */
+void orc_quantize_block_q4_sym7(const float w[32], uint16_t *scale_bits, uint8_t nib[32])
+{
+    quantize_q4(w, 32, 7.0f, scale_bits, nib);
+}
+
+/* 64-weight blocks (same page and section: the block length is usually 32
+ * or 64): the same steps over 64 values sharing one fp16 scale. */
+void orc_quantize_block_q8_b64(const float w[64], uint16_t *scale_bits, int8_t q[64])
+{
+    quantize_q8(w, 64, scale_bits, q);
+}
+
+void orc_quantize_block_q4_b64(const float w[64], int divisor, uint16_t *scale_bits, uint8_t nib[64])
+{
+    quantize_q4(w, 64, (float)divisor, scale_bits, nib);
+}
+
 /* ------------------------------------------------------------------------
  * Row-planar packing (see qmm_oracle.h).
  * ------------------------------------------------------------------------ */
 
 static size_t align16(size_t v) { return (v + 15u) & ~(size_t)15u; }
+
+static int is_quant(int type)
+{
+    return type == ORC_Q8_0 || type == ORC_Q4_0 || type == ORC_Q8_B64 || type == ORC_Q4_B64;
+}
+static int is_q8(int type) { return type == ORC_Q8_0 || type == ORC_Q8_B64; }
+/* Weights per block (one fp16 scale each). */
+static int64_t block_len(int type) { return (type == ORC_Q8_B64 || type == ORC_Q4_B64) ? 64 : 32; }
+/* Bytes of scales before the codes: 2 per block, padded to 16. */
+static size_t scale_bytes(int type, int64_t K) { return align16((size_t)(2 * (K / block_len(type)))); }
 
 size_t orc_row_size(int type, int64_t K)
 {
@@ -204,13 +230,13 @@ size_t orc_row_size(int type, int64_t K)
     case ORC_F32:  return (size_t)K * 4u;
     case ORC_F16:  return (size_t)K * 2u;
     case ORC_BF16: return (size_t)K * 2u;
-    case ORC_Q8_0: return align16((size_t)K / 16u) + align16((size_t)K);
-    case ORC_Q4_0: return align16((size_t)K / 16u) + align16((size_t)K / 2u);
+    case ORC_Q8_0:
+    case ORC_Q8_B64: return scale_bytes(type, K) + align16((size_t)K);
+    case ORC_Q4_0:
+    case ORC_Q4_B64: return scale_bytes(type, K) + align16((size_t)K / 2u);
     default:       return 0;
     }
 }
-
-static int is_quant(int type) { return type == ORC_Q8_0 || type == ORC_Q4_0; }
 
 int orc_quantize_rows(int type, const float *w, int64_t K, int64_t M,
                       uint8_t *dst, size_t pitch)
@@ -221,30 +247,32 @@ int orc_quantize_rows(int type, const float *w, int64_t K, int64_t M,
 int orc_quantize_rows_rule(int type, int rule, const float *w, int64_t K, int64_t M,
                            uint8_t *dst, size_t pitch)
 {
-    if (!is_quant(type) || K < 0 || M < 0 || (K % 32) != 0) return -1;
-    if (rule != ORC_RULE_DEFAULT && !(rule == ORC_RULE_Q4_SYM7 && type == ORC_Q4_0)) return -1;
+    if (!is_quant(type) || K < 0 || M < 0 || (K % block_len(type)) != 0) return -1;
+    if (rule != ORC_RULE_DEFAULT && !(rule == ORC_RULE_Q4_SYM7 && !is_q8(type))) return -1;
     if (pitch < orc_row_size(type, K)) return -1;
-    const int64_t nblk = K / 32;
-    const size_t qoff = align16((size_t)K / 16u);
+    const int64_t bl = block_len(type);
+    const int64_t nblk = K / bl;
+    const size_t qoff = scale_bytes(type, K);
     for (int64_t m = 0; m < M; ++m) {
         uint8_t *row = dst + (size_t)m * pitch;
         memset(row, 0, orc_row_size(type, K));
         for (int64_t b = 0; b < nblk; ++b) {
-            const float *blk = w + (size_t)m * (size_t)K + (size_t)b * 32u;
+            const float *blk = w + (size_t)m * (size_t)K + (size_t)(b * bl);
             uint16_t sb;
-            if (type == ORC_Q8_0) {
-                int8_t q[32];
-                orc_quantize_block_q8_0(blk, &sb, q);
-                memcpy(row + qoff + (size_t)b * 32u, q, 32);
+            if (is_q8(type)) {
+                int8_t q[64];
+                quantize_q8(blk, (int)bl, &sb, q);
+                memcpy(row + qoff + (size_t)(b * bl), q, (size_t)bl);   /* code k at qoff + k */
             } else {
-                uint8_t nib[32];
-                if (rule == ORC_RULE_Q4_SYM7)
-                    orc_quantize_block_q4_sym7(blk, &sb, nib);
-                else
-                    orc_quantize_block_q4_0(blk, &sb, nib);
-                uint8_t *qb = row + qoff + (size_t)b * 16u;
-                for (int j = 0; j < 16; ++j)
-                    qb[j] = (uint8_t)(nib[j] | (nib[j + 16] << 4));
+                uint8_t nib[64];
+                quantize_q4(blk, (int)bl, rule == ORC_RULE_Q4_SYM7 ? 7.0f : 8.0f, &sb, nib);
+                /* each run of 32 codes packs like a Q4_0 block: byte j of the
+                 * run holds code j (low nibble) and code j + 16 (high) */
+                for (int64_t h = 0; h < bl / 32; ++h) {
+                    uint8_t *qb = row + qoff + (size_t)((b * bl + 32 * h) / 2);
+                    for (int j = 0; j < 16; ++j)
+                        qb[j] = (uint8_t)(nib[32 * h + j] | (nib[32 * h + j + 16] << 4));
+                }
             }
             row[2 * b] = (uint8_t)(sb & 0xFF);
             row[2 * b + 1] = (uint8_t)(sb >> 8);
@@ -269,21 +297,22 @@ static void dequantize_row(int type, const uint8_t *row, int64_t K, float *out)
         }
         return;
     }
-    const size_t qoff = align16((size_t)K / 16u);
-    for (int64_t b = 0; b < K / 32; ++b) {
+    const size_t qoff = scale_bytes(type, K);
+    const int64_t bl = block_len(type);
+    for (int64_t k = 0; k < K; ++k) {
+        const int64_t b = k / bl;                       /* the scale's block */
         const uint16_t sb = (uint16_t)(row[2 * b] | (row[2 * b + 1] << 8));
         const float d = orc_f16_to_f32(sb);
-        for (int i = 0; i < 32; ++i) {
-            int code;
-            if (type == ORC_Q8_0) {
-                code = (int8_t)row[qoff + (size_t)b * 32u + (size_t)i];
-            } else {
-                const uint8_t byte = row[qoff + (size_t)b * 16u + (size_t)(i & 15)];
-                const int nib = (i < 16) ? (byte & 0x0F) : (byte >> 4);
-                code = nib - 8;
-            }
-            out[b * 32 + i] = d * (float)code;
+        int code;
+        if (is_q8(type)) {
+            code = (int8_t)row[qoff + (size_t)k];
+        } else {
+            const int64_t run = k / 32, i = k % 32;     /* 32-code run, position */
+            const uint8_t byte = row[qoff + (size_t)run * 16u + (size_t)(i & 15)];
+            const int nib = (i < 16) ? (byte & 0x0F) : (byte >> 4);
+            code = nib - 8;
         }
+        out[k] = d * (float)code;
     }
 }
 
@@ -291,7 +320,7 @@ static int valid_weight(int type, int64_t K, size_t pitch)
 {
     if (K < 0) return 0;
     if (type != ORC_F32 && type != ORC_F16 && type != ORC_BF16 && !is_quant(type)) return 0;
-    if (is_quant(type) && (K % 32) != 0) return 0;
+    if (is_quant(type) && (K % block_len(type)) != 0) return 0;
     return pitch >= orc_row_size(type, K);
 }
 
@@ -461,7 +490,7 @@ int orc_mul_mat_q8act_rows(int type, const uint8_t *w, size_t pitch, int64_t K, 
                            const uint8_t *xq, size_t x_pitch, int64_t N,
                            int64_t m0, int64_t m1, double *y, double *a)
 {
-    if (!is_quant(type) || K < 0 || K % 32 != 0 || M < 0 || N < 0) return -1;
+    if ((type != ORC_Q8_0 && type != ORC_Q4_0) || K < 0 || K % 32 != 0 || M < 0 || N < 0) return -1;
     if (pitch < orc_row_size(type, K) || x_pitch < orc_row_size(ORC_Q8_0, K)) return -1;
     if (m0 < 0 || m1 > M || m0 > m1) return -1;
     for (int64_t m = m0; m < m1; ++m) {

@@ -36,7 +36,9 @@ enum {
     ORC_F16 = 1,   /* dense binary16 rows (bits)                            */
     ORC_BF16 = 2,  /* dense bfloat16 rows (bits)                            */
     ORC_Q8_0 = 3,  /* 32-blocks: fp16 scale + 32 int8 codes                 */
-    ORC_Q4_0 = 4   /* 32-blocks: fp16 scale + 32 offset-binary 4-bit codes  */
+    ORC_Q4_0 = 4,  /* 32-blocks: fp16 scale + 32 offset-binary 4-bit codes  */
+    ORC_Q8_B64 = 5,/* 64-blocks: fp16 scale + 64 int8 codes                 */
+    ORC_Q4_B64 = 6 /* 64-blocks: fp16 scale + 64 offset-binary 4-bit codes  */
 };
 
 /* ---- IEEE conversions, written from the format definitions ---------- */
@@ -62,16 +64,25 @@ void orc_quantize_block_q4_0(const float w[32], uint16_t *scale_bits, uint8_t ni
  * Same storage (and dequantization) as Q4_0.                               */
 void orc_quantize_block_q4_sym7(const float w[32], uint16_t *scale_bits, uint8_t nib[32]);
 
+/* 64-weight blocks ("A Complete Guide to llama.cpp ...", §2.2: the block
+ * length is usually 32 or 64): the same steps over 64 values, one fp16
+ * scale.  divisor 8 (offset-binary rule) or 7 (the pages' symmetric rule).  */
+void orc_quantize_block_q8_b64(const float w[64], uint16_t *scale_bits, int8_t q[64]);
+void orc_quantize_block_q4_b64(const float w[64], int divisor, uint16_t *scale_bits, uint8_t nib[64]);
+
 /* Quantization rules of orc_quantize_rows_rule.                            */
 enum { ORC_RULE_DEFAULT = 0,   /* Q8_0: amax/127; Q4_0: amax/8 (offset 8) */
        ORC_RULE_Q4_SYM7 = 1 }; /* Q4_0 storage, the pages' amax/7 rule    */
 
 /* ---- packed rows ------------------------------------------------------
- * Row-planar packing of one row of K weights (K % 32 == 0):
- *   bytes [0, 2*K/32)            fp16 scale of block b at offset 2b (little endian)
- *   zero padding up to qoff = align16(K/16)
- *   Q8_0: bytes [qoff + 32b, +32) the int8 codes of block b
- *   Q4_0: bytes [qoff + 16b, +16) block b, byte j = nib_j | nib_{j+16} << 4
+ * Row-planar packing of one row of K weights in blocks of B = 32 (Q8_0,
+ * Q4_0) or 64 (Q8_B64, Q4_B64) weights (K % B == 0):
+ *   bytes [0, 2*K/B)             fp16 scale of block b at offset 2b (little endian)
+ *   zero padding up to qoff = align16(2*K/B)
+ *   Q8:  byte qoff + k           the int8 code of weight k
+ *   Q4:  bytes [qoff + 16r, +16) the r-th run of 32 codes (weights 32r ..
+ *        32r+31), byte j = nib_{32r+j} | nib_{32r+j+16} << 4 (a 64-block is
+ *        two such runs under one scale)
  *   zero padding up to the row size (a multiple of 16).
  * orc_row_size returns that size (dense types: K * element size).          */
 size_t orc_row_size(int type, int64_t K);
@@ -81,7 +92,7 @@ size_t orc_row_size(int type, int64_t K);
 int orc_quantize_rows(int type, const float *w, int64_t K, int64_t M,
                       uint8_t *dst, size_t pitch);
 
-/* The same with an explicit rule (ORC_RULE_Q4_SYM7 only with ORC_Q4_0).   */
+/* The same with an explicit rule (ORC_RULE_Q4_SYM7 only with the Q4 types). */
 int orc_quantize_rows_rule(int type, int rule, const float *w, int64_t K, int64_t M,
                            uint8_t *dst, size_t pitch);
 
