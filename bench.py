@@ -368,11 +368,19 @@ def prefill_leg(Q, WL, dev, args):
     ms_f, _ = timed(gf, max(2, args.steps // 2), 2)
     tf_f = flops / (ms_f / reps * 1e-3) / 1e12
     log(f"prefill GEMM, F16 weights {ms_f / reps * 1e3:.1f} us  {tf_f:.0f} TFLOP/s")
+    # and with 64-weight blocks
+    w64 = Q.quantize(WL.weights_device(WL.seed(5, 0), M, K, dev), Q.Q4_B64)
+    g64 = Graph(lambda: [Q.gemm(w64, x, out=y) for _ in range(reps)])
+    ms_b, _ = timed(g64, max(2, args.steps // 2), 2)
+    tf_b = flops / (ms_b / reps * 1e-3) / 1e12
+    log(f"prefill GEMM, Q4_B64 weights {ms_b / reps * 1e3:.1f} us  {tf_b:.0f} TFLOP/s")
     return {"workload": "Q4_0 5632 x 2048 x bf16 2048 x 512 -> f32", "us": round(per * 1e3, 2),
             "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
             "avg_launch_us": round(kern * 1e3, 2), "flops": flops,
             "f16_weights": {"us": round(ms_f / reps * 1e3, 2), "tflops": round(tf_f, 1),
-                            "frac_of_bf16_peak": round(tf_f / BF16_PEAK_TFLOPS, 4)}}
+                            "frac_of_bf16_peak": round(tf_f / BF16_PEAK_TFLOPS, 4)},
+            "q4_b64_weights": {"us": round(ms_b / reps * 1e3, 2), "tflops": round(tf_b, 1),
+                               "frac_of_bf16_peak": round(tf_b / BF16_PEAK_TFLOPS, 4)}}
 
 
 def breakdown_leg(Q, WL, dev, args, gemv_bytes):
@@ -412,6 +420,14 @@ def breakdown_leg(Q, WL, dev, args, gemv_bytes):
         out[name] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1),
                      "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
     del w3
+
+    # the same shape with 64-weight blocks (one fp16 scale per 64 weights)
+    w5 = [Q.quantize(WL.weights_device(WL.seed(3, 4, r), WL.FFN, WL.HIDDEN, dev), Q.Q4_B64) for r in range(48)]
+    per = rotate(w5, x3, y3, 96)
+    b = WL.FFN * Q.row_size(Q.Q4_B64, WL.HIDDEN) + 4 * WL.HIDDEN + 4 * WL.FFN
+    out["q4_b64_gemv_5632x2048_n1"] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1),
+                                       "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
+    del w5
 
     # fp16 5632 x 2048, one token: 48 copies (1.1 GB) so HBM is read
     w2 = []

@@ -21,8 +21,8 @@
  *     x  ne = [K, N]   activations, one row of K per token
  *     y  ne = [M, N]   F32 result, one row of M per token
  *     y[n][m] = sum_k W'[m][k] * x[n][k]
- * where W' is the dequantized weight: Delta_b * code for the 32-weight block b
- * that holds k.  The contraction runs over ne[0] of both operands (the second
+ * where W' is the dequantized weight: Delta_b * code for the block b that
+ * holds k (32 weights per block; 64 for the _B64 types).  The contraction runs over ne[0] of both operands (the second
  * operand is the "transposed" one of the pages' tensor_mul_mat, §5 of
  * "No Python! ...").
  *
@@ -36,6 +36,11 @@
  *     zero padding up to qmm_row_size() (a multiple of 16 bytes).
  * The row keeps the 34 (Q8_0) or 18 (Q4_0) bytes per 32 weights of the block
  * records; when K is a multiple of 256 there is no padding at all.
+ * 64-weight blocks ("A Complete Guide to llama.cpp ...", §2.2: the block
+ * length is usually 32 or 64), types Q8_B64 / Q4_B64, K % 64 == 0: the same
+ * row with one fp16 Delta per 64 weights (bytes [0, 2*K/64), codes from
+ * qoff = align16(K/32)); the codes are laid out exactly as above, so a
+ * 64-block is two consecutive 32-code runs under one Delta.
  *
  * Ownership and errors (all entry points):
  *  - Every buffer is caller-owned DEVICE memory; the library allocates
@@ -72,14 +77,16 @@ typedef enum {
     QMM_TYPE_F16  = 1,
     QMM_TYPE_BF16 = 2,
     QMM_TYPE_Q8_0 = 3,  /* 32-blocks: fp16 Delta + 32 int8 codes in [-127, 127]   */
-    QMM_TYPE_Q4_0 = 4   /* 32-blocks: fp16 Delta + 32 four-bit codes (value - 8)  */
+    QMM_TYPE_Q4_0 = 4,  /* 32-blocks: fp16 Delta + 32 four-bit codes (value - 8)  */
+    QMM_TYPE_Q8_B64 = 5,/* 64-blocks: fp16 Delta + 64 int8 codes in [-127, 127]   */
+    QMM_TYPE_Q4_B64 = 6 /* 64-blocks: fp16 Delta + 64 four-bit codes (value - 8)  */
 } qmm_type;
 
 typedef enum {
     QMM_OK              = 0,
     QMM_ERR_NULL        = -1,  /* a descriptor or a needed data pointer is NULL      */
     QMM_ERR_TYPE        = -2,  /* type not accepted by this entry point              */
-    QMM_ERR_SHAPE       = -3,  /* ne mismatch between operands, K % 32 != 0, N range */
+    QMM_ERR_SHAPE       = -3,  /* ne mismatch between operands, K % block, N range   */
     QMM_ERR_LAYOUT      = -4,  /* nb / alignment not supported                       */
     QMM_ERR_ALIAS       = -5,  /* the output overlaps an input                       */
     QMM_ERR_UNSUPPORTED = -6,  /* n_dims > 2, ne[2] or ne[3] != 1, or K*N too large */
@@ -94,7 +101,8 @@ typedef enum {
  *    and data % 16 == 0; F16 weights need nb[1] % 16 == 0 and data % 16 == 0;
  *    F32 activations and outputs need 4-byte alignment of data and nb[1];
  *    BF16 activations of qmm_gemm need 16-byte alignment of data and nb[1];
- *  - quantized ne[0] must be a multiple of 32 (else QMM_ERR_SHAPE). */
+ *  - quantized ne[0] must be a multiple of 32 (64 for the _B64 types; else
+ *    QMM_ERR_SHAPE). */
 typedef struct qmm_tensor {
     int32_t  type;     /* qmm_type                          */
     int32_t  n_dims;   /* 1 or 2                            */
@@ -104,15 +112,17 @@ typedef struct qmm_tensor {
 } qmm_tensor;
 
 /* Bytes of one packed (or dense) row of ne0 elements; 0 for an unknown type
- * or an invalid ne0 (negative, or not a multiple of 32 for Q8_0 / Q4_0).
- * Q8_0: align16(ne0/16) + align16(ne0);  Q4_0: align16(ne0/16) + align16(ne0/2). */
+ * or an invalid ne0 (negative, or not a multiple of the block length).
+ * Q8_0: align16(ne0/16) + align16(ne0);  Q4_0: align16(ne0/16) + align16(ne0/2);
+ * Q8_B64: align16(ne0/32) + align16(ne0);  Q4_B64: align16(ne0/32) + align16(ne0/2). */
 QMM_API size_t qmm_row_size(int32_t type, int64_t ne0);
 
-/* Quantize F32 rows into Q8_0 or Q4_0 rows (load time, once per weight).
- * src: F32 ne = [K, M];  dst: Q8_0 or Q4_0 ne = [K, M], K % 32 == 0.
- * Per block of 32 ("A Complete Guide to llama.cpp ...", §2.2; Development
- * Guide §6.1): amax = max|w|; Delta = fp16(amax / 127) for Q8_0 or
- * fp16(amax / 8) for Q4_0 (round to nearest even); code = round(w / Delta)
+/* Quantize F32 rows into Q8_0, Q4_0, Q8_B64 or Q4_B64 rows (load time, once
+ * per weight).  src: F32 ne = [K, M];  dst: ne = [K, M], K a multiple of the
+ * block length.
+ * Per block of 32 (or 64) ("A Complete Guide to llama.cpp ...", §2.2; Development
+ * Guide §6.1): amax = max|w|; Delta = fp16(amax / 127) for Q8 or
+ * fp16(amax / 8) for Q4 (round to nearest even); code = round(w / Delta)
  * half away from zero, one IEEE binary32 division by the stored Delta;
  * Q8_0 clamps to [-127, 127], Q4_0 stores code + 8 clamped to [0, 15];
  * Delta = 0 gives all-zero codes.  Bit-exact and deterministic.  Inputs must
@@ -130,20 +140,22 @@ typedef enum {
  * (Delta = max|w| / 7, q in [-8, 7]): Delta = fp16(amax / 7) (RNE);
  * q = round(w / Delta) half away from zero by one binary32 division by the
  * stored Delta, clamped to [-8, 7]; stored as the Q4_0 nibble q + 8, so the
- * result is an ordinary Q4_0 tensor (every kernel reads it unchanged) and
- * |W' - w| <= Delta / 2 holds for every weight (no code clamps).  Only for
- * dst type Q4_0 (else QMM_ERR_TYPE); an unknown rule returns
+ * result is an ordinary Q4_0 (or Q4_B64) tensor (every kernel reads it
+ * unchanged) and |W' - w| <= Delta / 2 holds for every weight (no code
+ * clamps).  Only for dst type Q4_0 or Q4_B64 (else QMM_ERR_TYPE); an unknown
+ * rule returns
  * QMM_ERR_UNSUPPORTED.  Inputs must be finite with amax / 7 below 65520. */
 QMM_API int qmm_quantize_rule(const qmm_tensor *src_f32, qmm_tensor *dst_q, int32_t rule, void *stream);
 
-/* Expand Q8_0 / Q4_0 / F16 rows to F32 (W' = Delta * code, exact in binary32;
+/* Expand Q8_0 / Q4_0 / Q8_B64 / Q4_B64 / F16 rows to F32 (W' = Delta * code, exact in binary32;
  * "Development Guide ...", §6.2 step "Dequantization").
  * src ne = [K, M];  dst: F32 ne = [K, M].  Bit-exact. */
 QMM_API int qmm_dequantize(const qmm_tensor *src, qmm_tensor *dst_f32, void *stream);
 
 /* Decode GEMV / skinny GEMM ("A Complete Guide to llama.cpp ...", §2.1: one
  * token per step makes every projection a GEMV).
- * w: Q8_0, Q4_0 or F16, ne = [K, M];  x: F32 ne = [K, N], 1 <= N <= 8
+ * w: Q8_0, Q4_0, Q8_B64, Q4_B64 or F16, ne = [K, M];  x: F32 ne = [K, N],
+ * 1 <= N <= 8
  * (N > 8: QMM_ERR_SHAPE);  y: F32 ne = [M, N], must not overlap w or x.
  * Each lane keeps its slice of x in registers, which bounds K: the call
  * returns QMM_ERR_UNSUPPORTED when K exceeds 32768 (Q4_0, Q8_0) or 16384
@@ -158,7 +170,7 @@ QMM_API int qmm_dequantize(const qmm_tensor *src, qmm_tensor *dst_f32, void *str
  * quantized per block too, x_i ~= Delta_x qx_i, the block dot product is
  * Delta Delta_x sum_i q_i qx_i, an integer sum): when x is Q8_0 (ne = [K, N],
  * the activations quantized with qmm_quantize, 1 <= N <= 8), w must be Q8_0
- * or Q4_0 (else QMM_ERR_TYPE) and
+ * or Q4_0 (32-blocks like x; else QMM_ERR_TYPE) and
  *   y[n][m] = sum_b Delta_w(m,b) Delta_x(n,b) sum_i q_i qx_i
  * with each block's integer sum exact (int8 dot products into int32) and
  * the block terms summed in binary32 (|y - exact| <= (K/16 + 16) 2^-24
@@ -194,7 +206,7 @@ QMM_API int qmm_gemv_batch(const qmm_gemv_item *items, int32_t count, void *stre
  * C++", §4.4: SwiGLU(x) = Swish(x W_gate) * (x W_up) elementwise, with
  * Swish(z) = z sigma(z) = z / (1 + e^{-z})):
  *   h[n][m] = Swish(sum_k Wg'[m][k] x[n][k]) * sum_k Wu'[m][k] x[n][k].
- * w_gate, w_up: the same type (Q8_0, Q4_0 or F16) and ne = [K, M], each with
+ * w_gate, w_up: the same type (any qmm_gemv weight type) and ne = [K, M], each with
  * its own row pitch under the rules of qmm_gemv;  x: F32 ne = [K, N],
  * 1 <= N <= 8;  h: F32 ne = [M, N], overlapping none of w_gate, w_up, x
  * (QMM_ERR_ALIAS).  Different types: QMM_ERR_TYPE; different ne: QMM_ERR_SHAPE.
@@ -207,7 +219,7 @@ QMM_API int qmm_gemv_swiglu(const qmm_tensor *w_gate, const qmm_tensor *w_up,
                             const qmm_tensor *x_f32, qmm_tensor *h_f32, void *stream);
 
 /* Prefill GEMM ("No Python! ...", §6: C_ij = sum_k A_ik B_kj, with many tokens
- * per step).  w: Q4_0, Q8_0 or F16 (F16 with K % 32 == 0, else
+ * per step).  w: Q4_0, Q8_0, Q4_B64, Q8_B64 or F16 (F16 with K % 32 == 0, else
  * QMM_ERR_UNSUPPORTED), ne = [K, M];  x: BF16 ne = [K, N], any N >= 0;
  * y: F32 ne = [M, N], must not overlap w or x.  Weight tiles are dequantized
  * (F16: converted) to bfloat16 (round to nearest even) and multiplied on the
@@ -237,7 +249,7 @@ QMM_API int qmm_gemm(const qmm_tensor *w, const qmm_tensor *x_bf16, qmm_tensor *
  * M * K/32 records of src_q to `records`.  Both are bit-exact and
  * asynchronous on `stream`.
  * Errors: QMM_ERR_NULL (no tensor, or NULL records for a non-empty tensor),
- * QMM_ERR_TYPE (not Q8_0 / Q4_0), QMM_ERR_SHAPE / QMM_ERR_LAYOUT (the tensor
+ * QMM_ERR_TYPE (not Q8_0 / Q4_0: the _B64 types have no GGUF record), QMM_ERR_SHAPE / QMM_ERR_LAYOUT (the tensor
  * rules), QMM_ERR_LAYOUT (records not 16-byte aligned), QMM_ERR_ALIAS
  * (records overlap the rows), QMM_ERR_UNSUPPORTED (M * K/32 >= 2^31).
  * An empty tensor enqueues nothing. */

@@ -5,12 +5,12 @@ The compute lives in hand-written HIP kernels (csrc/, built into libqmm.so by
 layer over the C ABI of include/qmm.h, with torch supplying device memory and
 streams.
 """
-from .binding import (BF16, F16, F32, Q4_0, Q8_0, QUANT_DEFAULT, QUANT_Q4_AMAX7, QmmError, Weight,
+from .binding import (BF16, F16, F32, Q4_0, Q4_B64, Q8_0, Q8_B64, QUANT_DEFAULT, QUANT_Q4_AMAX7, QmmError, Weight,
                       dequantize, f16_weight,
                       gemm, gemv, gemv_batch, gemv_swiglu, quantize, record_size, records_to_rows,
                       row_size, rows_to_records, strerror)
 
-__all__ = ["BF16", "F16", "F32", "Q4_0", "Q8_0", "QUANT_DEFAULT", "QUANT_Q4_AMAX7", "QmmError",
+__all__ = ["BF16", "F16", "F32", "Q4_0", "Q4_B64", "Q8_0", "Q8_B64", "QUANT_DEFAULT", "QUANT_Q4_AMAX7", "QmmError",
            "Weight", "dequantize",
            "f16_weight", "gemm", "gemv", "gemv_batch", "gemv_swiglu", "quantize", "record_size",
            "records_to_rows", "row_size", "rows_to_records", "strerror"]

@@ -18,8 +18,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqmm.so")
 
 # qmm_type
-F32, F16, BF16, Q8_0, Q4_0 = 0, 1, 2, 3, 4
-TYPE_NAMES = {F32: "F32", F16: "F16", BF16: "BF16", Q8_0: "Q8_0", Q4_0: "Q4_0"}
+F32, F16, BF16, Q8_0, Q4_0, Q8_B64, Q4_B64 = 0, 1, 2, 3, 4, 5, 6
+TYPE_NAMES = {F32: "F32", F16: "F16", BF16: "BF16", Q8_0: "Q8_0", Q4_0: "Q4_0",
+              Q8_B64: "Q8_B64", Q4_B64: "Q4_B64"}
 
 # qmm_status
 OK, ERR_NULL, ERR_TYPE, ERR_SHAPE, ERR_LAYOUT, ERR_ALIAS, ERR_UNSUPPORTED, ERR_DEVICE = \
@@ -116,7 +117,7 @@ def make_desc(type_: int, ne0: int, ne1: int, nb1: int, data_ptr: int, n_dims: i
 class Weight:
     """A weight matrix W (ne = [K, M]): M rows of K weights on the GPU.
 
-    data is uint8 (M, pitch) for Q8_0 / Q4_0 rows in the row-planar layout of
+    data is uint8 (M, pitch) for quantized rows (Q8_0, Q4_0, Q8_B64, Q4_B64) in the row-planar layout of
     include/qmm.h, or float16 (M, >= K) for F16 rows."""
     data: torch.Tensor
     type: int
@@ -168,8 +169,9 @@ QUANT_DEFAULT, QUANT_Q4_AMAX7 = 0, 1
 
 def quantize(w: torch.Tensor, type_: int, *, pitch: int | None = None, rule: int = QUANT_DEFAULT,
              stream=None) -> Weight:
-    """Quantize fp32 rows w (M, K) on the GPU into Q8_0 / Q4_0 rows (rule:
-    QUANT_DEFAULT, or QUANT_Q4_AMAX7 for the symmetric amax/7 Q4 rule)."""
+    """Quantize fp32 rows w (M, K) on the GPU into Q8_0 / Q4_0 rows, or their
+    64-weight-block variants Q8_B64 / Q4_B64 (rule: QUANT_DEFAULT, or
+    QUANT_Q4_AMAX7 for the symmetric amax/7 Q4 rule)."""
     _need_gpu(w)
     M, K = w.shape
     rs = row_size(type_, K)

@@ -136,16 +136,19 @@ __device__ inline void static_for(F &&f)
 }
 
 // The fp16 scale of a producer lane's block of step S of a scale group:
-// block 2S + h of the group, which lane S / 2 of the lane's quad (the four
-// lanes sharing a pair of rows) holds in dword S % 2 of row use0 ? 0 : 1,
-// half h.  The quad broadcast is a DPP move.
-template <int S>
+// 32-weight block 2S + h of the group, which lane S / 2 of the lane's quad
+// (the four lanes sharing a pair of rows) holds in dword S % 2 of row
+// use0 ? 0 : 1, half h.  With 64-weight blocks (SS = 1) both halves of step
+// S share 64-block S: dword 0 of lane S / 2, half S % 2.  The quad broadcast
+// is a DPP move.
+template <int S, int SS>
 __device__ inline uint16_t group_scale(const uint32_t (&sreg)[2][2], bool use0, int h)
 {
     constexpr int ctrl = (S / 2) * 0x55;     // quad_perm [S/2, S/2, S/2, S/2]
-    const uint32_t v0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)sreg[0][S % 2], ctrl, 0xF, 0xF, false);
-    const uint32_t v1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)sreg[1][S % 2], ctrl, 0xF, 0xF, false);
-    return (uint16_t)((use0 ? v0 : v1) >> (16 * h));
+    constexpr int dw = SS ? 0 : S % 2;
+    const uint32_t v0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)sreg[0][dw], ctrl, 0xF, 0xF, false);
+    const uint32_t v1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)sreg[1][dw], ctrl, 0xF, 0xF, false);
+    return (uint16_t)((use0 ? v0 : v1) >> (16 * (SS ? S % 2 : h)));
 }
 
 // Two fp16 weights (one dword) to two bf16 (nearest even): each half widens
@@ -157,9 +160,10 @@ __device__ inline uint32_t f16x2_to_bf16x2(uint32_t w)
     return pack_bf16(lo, hi);
 }
 
-template <int WT>
+template <int WT, int SS>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
 {
+    static_assert(SS == 0 || WT != W_F16, "64-weight blocks are quantized");
     constexpr int QB = (WT == W_Q4_0) ? 16 : 32;     // code bytes per block (quantized rows)
     extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
     // STAGES x [weights BM x LDS_STRIDE | tokens BN x LDS_STRIDE] bf16
@@ -284,8 +288,10 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
         const int h = q4 & 1;
         const bool first_is_0 = (q4 >> 1) == 0;
         // scale load i covers rows wrow0 + i, blocks 4 q4 .. 4 q4 + 3 of a group
-        const uint32_t soff[2] = {(uint32_t)(wrow0 * a.pitch) + 8 * q4,
-                                  (uint32_t)((wrow0 + 1) * a.pitch) + 8 * q4};
+        // (64-blocks: blocks 2 q4, 2 q4 + 1, the group's 8 scales)
+        constexpr uint32_t SLANE = SS ? 4 : 8;                  // scale bytes per lane and row
+        const uint32_t soff[2] = {(uint32_t)(wrow0 * a.pitch) + SLANE * q4,
+                                  (uint32_t)((wrow0 + 1) * a.pitch) + SLANE * q4};
         uint16_t *wdst0 = lds + wrow0 * LDS_STRIDE + 32 * h;
 
         struct WPair { u32x4 q[2][WBlock<WT>::QV]; };
@@ -303,10 +309,16 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
         auto load_scales = [&](uint32_t (&dst)[2][2], int group) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                const auto v = __builtin_amdgcn_raw_buffer_load_b64(
-                    wres, soff[i] + (uint32_t)group * (2 * SCALE_GROUP_BLOCKS), 0, 0);
-                dst[i][0] = v[0];
-                dst[i][1] = v[1];
+                if constexpr (SS) {
+                    dst[i][0] = __builtin_amdgcn_raw_buffer_load_b32(
+                        wres, soff[i] + (uint32_t)group * SCALE_GROUP_BLOCKS, 0, 0);
+                    dst[i][1] = 0;
+                } else {
+                    const auto v = __builtin_amdgcn_raw_buffer_load_b64(
+                        wres, soff[i] + (uint32_t)group * (2 * SCALE_GROUP_BLOCKS), 0, 0);
+                    dst[i][0] = v[0];
+                    dst[i][1] = v[1];
+                }
             }
         };
         auto produce = [&](auto S_, int p, const WPair &wp) {
@@ -316,7 +328,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
             WBlock<WT> b;
 #pragma unroll
             for (int v = 0; v < WBlock<WT>::QV; ++v) b.q[v] = use0 ? wp.q[0][v] : wp.q[1][v];
-            const uint16_t s16 = group_scale<S>(sreg, use0, h);
+            const uint16_t s16 = group_scale<S, SS>(sreg, use0, h);
             b.s = blk < nblk ? s16 : (uint16_t)0;   // past K: zero scale (the codes may be anything)
             uint32_t deq[16];
             dequant_block<WT>(b, deq);
@@ -515,12 +527,12 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
 
 constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_ELEMS * sizeof(uint16_t);
 
-template <int WT>
+template <int WT, int SS>
 hipError_t launch_typed(const GemmArgs &a, unsigned tiles, hipStream_t stream)
 {
-    const hipError_t attr = allow_dynamic_lds(reinterpret_cast<const void *>(&gemm_kernel<WT>), (int)LDS_BYTES);
+    const hipError_t attr = allow_dynamic_lds(reinterpret_cast<const void *>(&gemm_kernel<WT, SS>), (int)LDS_BYTES);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL(gemm_kernel<WT>, dim3(tiles), dim3(THREADS), LDS_BYTES, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<WT, SS>), dim3(tiles), dim3(THREADS), LDS_BYTES, stream, a);
     return hipGetLastError();
 }
 
@@ -541,7 +553,7 @@ hipError_t launch_gemm(const WeightView &w, const ActView &x, const OutView &y,
     a.pitch = w.pitch;
     a.M = w.M;
     a.K = w.K;
-    a.qoff = quant_offset(w.K);
+    a.qoff = quant_offset(w.K, w.scale_shift);
     a.x = static_cast<const uint16_t *>(x.data);
     a.x_pitch = x.pitch_elems;
     a.N = x.N;
@@ -549,9 +561,14 @@ hipError_t launch_gemm(const WeightView &w, const ActView &x, const OutView &y,
     a.y_pitch = y.pitch_elems;
     a.n_tiles = (int)((x.N + BN - 1) / BN);
     const unsigned tiles = (unsigned)((w.M + BM - 1) / BM) * (unsigned)a.n_tiles;
-    if (w.type == W_Q4_0) return launch_typed<W_Q4_0>(a, tiles, stream);
-    if (w.type == W_Q8_0) return launch_typed<W_Q8_0>(a, tiles, stream);
-    if (w.type == W_F16) return launch_typed<W_F16>(a, tiles, stream);
+    if (w.scale_shift) {
+        if (w.type == W_Q4_0) return launch_typed<W_Q4_0, 1>(a, tiles, stream);
+        if (w.type == W_Q8_0) return launch_typed<W_Q8_0, 1>(a, tiles, stream);
+        return hipErrorInvalidValue;
+    }
+    if (w.type == W_Q4_0) return launch_typed<W_Q4_0, 0>(a, tiles, stream);
+    if (w.type == W_Q8_0) return launch_typed<W_Q8_0, 0>(a, tiles, stream);
+    if (w.type == W_F16) return launch_typed<W_F16, 0>(a, tiles, stream);
     return hipErrorInvalidValue;
 }
 

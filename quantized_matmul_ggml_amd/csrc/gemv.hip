@@ -76,7 +76,8 @@ struct GemvArgs {
     int32_t qoff;         // byte offset of the codes inside a row (0 for F16)
     int32_t nchunk;       // 16-byte chunks of codes per row
     int32_t n_items;
-    int32_t pad[11];
+    int32_t scale_shift;  // 1: one scale per two 32-weight runs (64-blocks)
+    int32_t pad[10];
     GemvItem item[kMaxItems];
 };
 
@@ -231,8 +232,9 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
     const int K = a.K;
     const int qoff = a.qoff;
     const int nchunk = a.nchunk;
+    const int sshift = a.scale_shift;
     asm volatile("" ::"s"(W), "s"(X), "s"(Y), "s"(pitch), "s"(x_pitch), "s"(y_pitch), "s"(M),
-                 "s"(n_groups), "s"(n_wg), "s"(iters), "s"(N), "s"(K), "s"(qoff), "s"(nchunk));
+                 "s"(n_groups), "s"(n_wg), "s"(iters), "s"(N), "s"(K), "s"(qoff), "s"(nchunk), "s"(sshift));
     if constexpr (SWIGLU) asm volatile("" ::"s"(W2), "s"(pitch2));
     if ((int)blockIdx.x >= n_wg) return;
     const int nt_real = N < NT ? N : NT;
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
         const int c = v + j * VL;
         const bool full = (WT == W_F16) ? c * 8 + 8 <= K : c < nchunk;
         qoffs[j] = full ? (uint32_t)(qoff + c * 16) : OUT_OF_RANGE;
-        soffs[j] = full ? (uint32_t)(2 * chunk_block<WT>(c)) : OUT_OF_RANGE;
+        soffs[j] = full ? (uint32_t)(2 * (chunk_block<WT>(c) >> sshift)) : OUT_OF_RANGE;
     }
     auto group_rsrc = [&](int gi, const uint8_t *Wm, uint32_t pm) {
         const int r0 = gi * RU;
@@ -634,8 +636,9 @@ hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t strea
         a.n_items = 0;
         a.N = (int32_t)nb;
         a.K = (int32_t)K;
-        a.qoff = (type == W_F16) ? 0 : (int32_t)quant_offset(K);
+        a.qoff = (type == W_F16) ? 0 : (int32_t)quant_offset(K, tasks[0].w.scale_shift);
         a.nchunk = (int32_t)chunks_per_row(type, K);
+        a.scale_shift = tasks[0].w.scale_shift;
         int64_t need_total = 0;
         int64_t need[kMaxItems];
         for (int i = 0; i < count; ++i) {
@@ -699,8 +702,9 @@ hipError_t launch_gemv_swiglu(const WeightView &wg, const WeightView &wu, const 
         a.n_items = 1;
         a.N = (int32_t)nb;
         a.K = (int32_t)K;
-        a.qoff = (type == W_F16) ? 0 : (int32_t)quant_offset(K);
+        a.qoff = (type == W_F16) ? 0 : (int32_t)quant_offset(K, wg.scale_shift);
         a.nchunk = (int32_t)chunks_per_row(type, K);
+        a.scale_shift = wg.scale_shift;
         GemvItem &it = a.item[0];
         it.w = wg.base;
         it.w2 = wu.base;

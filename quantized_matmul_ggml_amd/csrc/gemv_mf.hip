@@ -506,6 +506,7 @@ bool gemv_mf_supported(const GemvTask *tasks, int count)
     const int type = tasks[0].w.type;
     const int64_t K = tasks[0].w.K;
     if (!(type == W_Q4_0 || type == W_Q8_0) || K % 32 != 0 || K == 0) return false;
+    if (tasks[0].w.scale_shift != 0) return false;   // 64-blocks: the VALU kernel
     // a 16-row tile is one buffer resource with 32-bit offsets
     // and the activations of up to 8 tokens another (byte offsets < 2^31)
     for (int i = 0; i < count; ++i) {

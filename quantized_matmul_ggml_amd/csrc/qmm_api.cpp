@@ -19,7 +19,13 @@ using qmm::W_F32;
 using qmm::W_Q4_0;
 using qmm::W_Q8_0;
 
-bool is_quant(int t) { return t == QMM_TYPE_Q8_0 || t == QMM_TYPE_Q4_0; }
+bool is_quant(int t)
+{
+    return t == QMM_TYPE_Q8_0 || t == QMM_TYPE_Q4_0 || t == QMM_TYPE_Q8_B64 || t == QMM_TYPE_Q4_B64;
+}
+bool is_b64(int t) { return t == QMM_TYPE_Q8_B64 || t == QMM_TYPE_Q4_B64; }
+// Weights per fp16 scale of a quantized type.
+int64_t block_len(int t) { return is_b64(t) ? 64 : 32; }
 
 int64_t elem_size(int t)
 {
@@ -36,13 +42,13 @@ int64_t elem_size(int t)
 int check_tensor(const qmm_tensor *t, uint64_t align)
 {
     if (!t) return QMM_ERR_NULL;
-    if (t->type < QMM_TYPE_F32 || t->type > QMM_TYPE_Q4_0) return QMM_ERR_TYPE;
+    if (t->type < QMM_TYPE_F32 || t->type > QMM_TYPE_Q4_B64) return QMM_ERR_TYPE;
     if (t->n_dims < 1 || t->n_dims > 4) return QMM_ERR_UNSUPPORTED;
     if (t->n_dims > 2 || t->ne[2] != 1 || t->ne[3] != 1) return QMM_ERR_UNSUPPORTED;
     if (t->ne[0] < 0 || t->ne[1] < 0) return QMM_ERR_SHAPE;
     if (t->n_dims == 1 && t->ne[1] != 1) return QMM_ERR_SHAPE;
     if (is_quant(t->type)) {
-        if (t->ne[0] % 32 != 0) return QMM_ERR_SHAPE;
+        if (t->ne[0] % block_len(t->type) != 0) return QMM_ERR_SHAPE;
         if (t->nb[0] != 0) return QMM_ERR_LAYOUT;
     } else if ((int64_t)t->nb[0] != elem_size(t->type)) {
         return QMM_ERR_LAYOUT;
@@ -80,7 +86,9 @@ qmm::WeightView weight_view(const qmm_tensor *w)
     v.pitch = w->ne[1] > 1 ? w->nb[1] : qmm_row_size(w->type, w->ne[0]);
     v.K = w->ne[0];
     v.M = w->ne[1];
-    v.type = w->type;
+    // the 64-block types are their code format with one scale per two runs
+    v.type = w->type == QMM_TYPE_Q8_B64 ? W_Q8_0 : w->type == QMM_TYPE_Q4_B64 ? W_Q4_0 : w->type;
+    v.scale_shift = is_b64(w->type) ? 1 : 0;
     return v;
 }
 
@@ -125,6 +133,8 @@ size_t qmm_row_size(int32_t type, int64_t ne0)
     case QMM_TYPE_BF16: return k * 2;
     case QMM_TYPE_Q8_0: return (k % 32) ? 0 : a16(k / 16) + a16(k);
     case QMM_TYPE_Q4_0: return (k % 32) ? 0 : a16(k / 16) + a16(k / 2);
+    case QMM_TYPE_Q8_B64: return (k % 64) ? 0 : a16(k / 32) + a16(k);
+    case QMM_TYPE_Q4_B64: return (k % 64) ? 0 : a16(k / 32) + a16(k / 2);
     default: return 0;
     }
 }
@@ -144,15 +154,16 @@ int qmm_quantize_rule(const qmm_tensor *src, qmm_tensor *dst, int32_t rule, void
     if (rc) return rc;
     if (src->type != QMM_TYPE_F32 || !is_quant(dst->type)) return QMM_ERR_TYPE;
     if (src->ne[0] != dst->ne[0] || src->ne[1] != dst->ne[1]) return QMM_ERR_SHAPE;
-    if (src->ne[0] % 32 != 0) return QMM_ERR_SHAPE;
+    if (src->ne[0] % block_len(dst->type) != 0) return QMM_ERR_SHAPE;
     if (overlaps(dst, src)) return QMM_ERR_ALIAS;
-    if (rule == QMM_QUANT_Q4_AMAX7 && dst->type != QMM_TYPE_Q4_0) return QMM_ERR_TYPE;
+    if (rule == QMM_QUANT_Q4_AMAX7 && dst->type != QMM_TYPE_Q4_0 && dst->type != QMM_TYPE_Q4_B64)
+        return QMM_ERR_TYPE;
     const qmm::WeightView d = weight_view(dst);
     return status_of(qmm::launch_quantize(static_cast<const float *>(src->data), pitch_elems(src),
                                           src->ne[0], src->ne[1],
-                                          static_cast<uint8_t *>(dst->data), d.pitch, dst->type,
+                                          static_cast<uint8_t *>(dst->data), d.pitch, d.type,
                                           static_cast<hipStream_t>(stream),
-                                          rule == QMM_QUANT_Q4_AMAX7));
+                                          rule == QMM_QUANT_Q4_AMAX7, d.scale_shift));
 }
 
 int qmm_dequantize(const qmm_tensor *src, qmm_tensor *dst, void *stream)
@@ -169,7 +180,7 @@ int qmm_dequantize(const qmm_tensor *src, qmm_tensor *dst, void *stream)
     const qmm::WeightView s = weight_view(src);
     return status_of(qmm::launch_dequantize(s.base, s.pitch, s.K, s.M, s.type,
                                             static_cast<float *>(dst->data), pitch_elems(dst),
-                                            static_cast<hipStream_t>(stream)));
+                                            static_cast<hipStream_t>(stream), s.scale_shift));
 }
 
 int qmm_gemv(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *stream)
@@ -178,7 +189,7 @@ int qmm_gemv(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *stre
         // the integer-activation path ("A Complete Guide to llama.cpp ...", §2.2)
         int rc = check_mul_mat(w, x, y, QMM_TYPE_Q8_0, 16);
         if (rc) return rc;
-        if (!is_quant(w->type)) return QMM_ERR_TYPE;
+        if (w->type != QMM_TYPE_Q8_0 && w->type != QMM_TYPE_Q4_0) return QMM_ERR_TYPE;   // 32-blocks like x
         if (x->ne[1] > 8) return QMM_ERR_SHAPE;
         if (x->ne[1] == 0 || w->ne[1] == 0) return QMM_OK;
         if (!qmm::gemv_i8_supported(w->type, w->ne[0], w->ne[1], x->ne[1])) return QMM_ERR_UNSUPPORTED;
@@ -197,7 +208,7 @@ int qmm_gemv(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *stre
     // The activation slice of every lane lives in registers (at most 128
     // floats per lane), which bounds K; tokens are split into chunks that fit.
     qmm::GemvConfig cfg;
-    if (!qmm::gemv_config(w->type, w->ne[0], w->ne[1], 1, &cfg)) return QMM_ERR_UNSUPPORTED;
+    if (!qmm::gemv_config(weight_view(w).type, w->ne[0], w->ne[1], 1, &cfg)) return QMM_ERR_UNSUPPORTED;
     qmm::ActView xv{x->data, pitch_elems(x), x->ne[1]};
     qmm::OutView yv{static_cast<float *>(y->data), pitch_elems(y)};
     if (!qmm::gemv_supported(weight_view(w), xv, yv)) return QMM_ERR_UNSUPPORTED;
@@ -237,7 +248,7 @@ int qmm_gemv_batch(const qmm_gemv_item *items, int32_t count, void *stream)
     for (int i = 0; i < count; ++i) m_total += items[i].w->ne[1];
     if (m_total == 0 || items[0].x_f32->ne[1] == 0) return QMM_OK;
     qmm::GemvConfig cfg;
-    if (!qmm::gemv_config(items[0].w->type, items[0].w->ne[0], m_total, 1, &cfg))
+    if (!qmm::gemv_config(tasks[0].w.type, items[0].w->ne[0], m_total, 1, &cfg))
         return QMM_ERR_UNSUPPORTED;
     return status_of(qmm::launch_gemv_batch(tasks, count, static_cast<hipStream_t>(stream)));
 }
@@ -255,7 +266,8 @@ int qmm_gemv_swiglu(const qmm_tensor *w_gate, const qmm_tensor *w_up, const qmm_
     if (x->ne[1] > 8) return QMM_ERR_SHAPE;
     if (x->ne[1] == 0 || w_gate->ne[1] == 0) return QMM_OK;
     qmm::GemvConfig cfg;
-    if (!qmm::gemv_config(w_gate->type, w_gate->ne[0], 2 * w_gate->ne[1], 1, &cfg)) return QMM_ERR_UNSUPPORTED;
+    if (!qmm::gemv_config(weight_view(w_gate).type, w_gate->ne[0], 2 * w_gate->ne[1], 1, &cfg))
+        return QMM_ERR_UNSUPPORTED;
     qmm::ActView xv{x->data, pitch_elems(x), x->ne[1]};
     qmm::OutView hv{static_cast<float *>(h->data), pitch_elems(h)};
     const qmm::WeightView gv = weight_view(w_gate), uv = weight_view(w_up);
@@ -276,7 +288,7 @@ int check_records(const qmm_tensor *q, const void *records, uint64_t *bytes)
 {
     int rc = check_tensor(q, 16);
     if (rc) return rc;
-    if (!is_quant(q->type)) return QMM_ERR_TYPE;
+    if (q->type != QMM_TYPE_Q8_0 && q->type != QMM_TYPE_Q4_0) return QMM_ERR_TYPE;
     const int64_t blocks = q->ne[1] * (q->ne[0] / 32);
     if (blocks >= (1ll << 31)) return QMM_ERR_UNSUPPORTED;
     *bytes = (uint64_t)blocks * (uint64_t)qmm::record_size(q->type);
@@ -330,7 +342,7 @@ const char *qmm_strerror(int status)
     case QMM_OK: return "success";
     case QMM_ERR_NULL: return "a descriptor or data pointer is NULL";
     case QMM_ERR_TYPE: return "operand type not accepted by this entry point";
-    case QMM_ERR_SHAPE: return "operand shapes do not match (or K % 32 != 0, or N out of range)";
+    case QMM_ERR_SHAPE: return "operand shapes do not match (or K not a multiple of the block length, or N out of range)";
     case QMM_ERR_LAYOUT: return "unsupported strides or alignment";
     case QMM_ERR_ALIAS: return "the output overlaps an input";
     case QMM_ERR_UNSUPPORTED: return "unsupported tensor rank or size";

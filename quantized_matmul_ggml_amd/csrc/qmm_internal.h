@@ -11,11 +11,14 @@
 namespace qmm {
 
 // Weight encodings the kernels understand (same values as qmm_type).
-enum WType : int { W_F32 = 0, W_F16 = 1, W_BF16 = 2, W_Q8_0 = 3, W_Q4_0 = 4 };
+enum WType : int { W_F32 = 0, W_F16 = 1, W_BF16 = 2, W_Q8_0 = 3, W_Q4_0 = 4, W_Q8_B64 = 5, W_Q4_B64 = 6 };
 
-// Byte offset of the codes inside a quantized row: the K/32 fp16 scales come
-// first, padded to 16 bytes.
-__host__ __device__ inline int64_t quant_offset(int64_t K) { return ((K / 16) + 15) / 16 * 16; }
+// Byte offset of the codes inside a quantized row: the fp16 scales come
+// first (K/32 of them, or K/64 with scale_shift 1), padded to 16 bytes.
+__host__ __device__ inline int64_t quant_offset(int64_t K, int scale_shift = 0)
+{
+    return ((K >> (4 + scale_shift)) + 15) / 16 * 16;
+}
 
 // Raw buffer resources (kernels): word 3 of the descriptor (32-bit data
 // format, no swizzle), and an offset above every buffer size the kernels
@@ -24,13 +27,16 @@ constexpr int BUFFER_FLAGS = 0x00020000;
 constexpr uint32_t OUT_OF_RANGE = 0x80000000u;
 
 // One weight matrix as the kernels see it: M rows of K weights, row r at
-// base + r * pitch (bytes).
+// base + r * pitch (bytes).  type is the code format (W_Q8_0, W_Q4_0 or
+// W_F16); the 64-block types arrive as their code format with scale_shift 1
+// (one scale per two 32-weight runs: the scale of run c is scale c >> 1).
 struct WeightView {
     const uint8_t *base;
     uint64_t pitch;
     int64_t K;
     int64_t M;
     int type;
+    int scale_shift = 0;
 };
 
 // Activations: N rows of K values, row n at data + n * pitch_elems elements.
@@ -69,11 +75,13 @@ inline bool gemv_supported(const WeightView &w, const ActView &x, const OutView 
 // Launchers (return hipSuccess or the launch error).  Shapes are validated by
 // the caller; every launcher accepts M == 0 / N == 0 as a no-op.
 // q4_amax7: the pages' symmetric Q4 rule (Delta = amax / 7) instead of amax / 8.
+// scale_shift 1: 64-weight blocks (one scale per two 32-code runs).
 hipError_t launch_quantize(const float *src, uint64_t src_pitch_elems, int64_t K, int64_t M,
                            uint8_t *dst, uint64_t dst_pitch, int type, hipStream_t stream,
-                           bool q4_amax7 = false);
+                           bool q4_amax7 = false, int scale_shift = 0);
 hipError_t launch_dequantize(const uint8_t *src, uint64_t src_pitch, int64_t K, int64_t M,
-                             int type, float *dst, uint64_t dst_pitch_elems, hipStream_t stream);
+                             int type, float *dst, uint64_t dst_pitch_elems, hipStream_t stream,
+                             int scale_shift = 0);
 hipError_t launch_gemv(const WeightView &w, const ActView &x, const OutView &y,
                        hipStream_t stream);
 

@@ -259,3 +259,37 @@ def test_empty_operands_enqueue_nothing(qmm_lib):
                       B.make_desc(B.F32, 64, 0, 256, 0)) == B.OK
     assert B.call_raw("qmm_quantize", B.make_desc(B.F32, 2048, 0, 8192, 0),
                       B.make_desc(B.Q4_0, 2048, 0, 1152, 0)) == B.OK
+
+
+def test_row_size_64_blocks(qmm_lib, orc):
+    rs = qmm_lib.row_size
+    for K in (64, 128, 2048, 5632, 4096 + 64):
+        assert rs(B.Q8_B64, K) == orc.row_size(orc.Q8_B64, K)
+        assert rs(B.Q4_B64, K) == orc.row_size(orc.Q4_B64, K)
+    for K in (512, 2048, 32768):                   # no padding when K % 512 == 0
+        assert rs(B.Q8_B64, K) == K // 32 + K      # 66 bytes per 64 weights
+        assert rs(B.Q4_B64, K) == K // 32 + K // 2   # 34 bytes per 64 weights
+    assert rs(B.Q4_B64, 96) == 0 and rs(B.Q8_B64, 32) == 0   # K % 64 != 0
+    assert qmm_lib.record_size(B.Q4_B64) == 0 and qmm_lib.record_size(B.Q8_B64) == 0
+
+
+@no_gpu
+def test_64_block_types_reject(qmm_lib):
+    w = B.make_desc(B.Q4_B64, 2048, 64, 1088, W_ADDR)
+    # K not a multiple of 64
+    assert B.call_raw("qmm_gemv", B.make_desc(B.Q4_B64, 2080, 64, 1104, W_ADDR), _x(K=2080), _y()) == B.ERR_SHAPE
+    assert B.call_raw("qmm_quantize", B.make_desc(B.F32, 2080, 64, 8320, X_ADDR),
+                      B.make_desc(B.Q8_B64, 2080, 64, 2176, W_ADDR)) == B.ERR_SHAPE
+    # the integer-activation path needs 32-blocks like x
+    xq = B.make_desc(B.Q8_0, 2048, 1, 2176, X_ADDR)
+    assert B.call_raw("qmm_gemv", w, xq, _y()) == B.ERR_TYPE
+    # no GGUF record for 64-blocks
+    R_ADDR = BASE + (4 << 32)
+    assert qmm_lib.lib().qmm_rows_to_records(ctypes.byref(w), ctypes.c_void_p(R_ADDR), None) == B.ERR_TYPE
+    # the amax/7 rule is a Q4 rule: accepted for Q4_B64 (nothing enqueued for
+    # an empty tensor), rejected for Q8_B64
+    call = lambda s, d, r: qmm_lib.lib().qmm_quantize_rule(ctypes.byref(s), ctypes.byref(d), r, None)
+    assert call(B.make_desc(B.F32, 2048, 0, 8192, 0), B.make_desc(B.Q4_B64, 2048, 0, 1088, 0), 1) == B.OK
+    assert call(B.make_desc(B.F32, 2048, 64, 8192, X_ADDR), B.make_desc(B.Q8_B64, 2048, 64, 2112, W_ADDR), 1) == B.ERR_TYPE
+    # a pitch below the 64-block row size
+    assert B.call_raw("qmm_gemv", B.make_desc(B.Q4_B64, 2048, 64, 1072, W_ADDR), _x(), _y()) == B.ERR_LAYOUT

@@ -25,7 +25,8 @@ from golden_io import read_blocks
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-TYPES = {"Q8_0": (B.Q8_0, 3), "Q4_0": (B.Q4_0, 4), "F16": (B.F16, 1)}   # (qmm, oracle) ids
+TYPES = {"Q8_0": (B.Q8_0, 3), "Q4_0": (B.Q4_0, 4), "F16": (B.F16, 1),   # (qmm, oracle) ids
+         "Q8_B64": (B.Q8_B64, 5), "Q4_B64": (B.Q4_B64, 6)}
 CANARY = np.float32(np.array([0x7FC0DEAD], np.uint32).view(np.float32)[0])
 
 
@@ -208,6 +209,37 @@ def test_dequantize_bit_exact(orc, tname):
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
 
 
+QUANT_SHAPES_B64 = [(1, 64), (3, 128), (257, 192), (64, 2048), (129, 5632), (5, 32768)]
+
+
+@pytest.mark.parametrize("tname,rule", [("Q8_B64", 0),
+                                        ("Q4_B64", 0), ("Q4_B64", 1)])
+@pytest.mark.parametrize("shape", QUANT_SHAPES_B64, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_quantize_64_blocks_bit_exact(orc, tname, rule, shape):
+    """64-weight blocks, both Q4 rules (rule 1: the pages' amax/7)."""
+    M, K = shape
+    _banner(f"quantize {tname} rule {rule} {M}x{K}")
+    w = _adversarial(M, K, 300 + M + K)
+    ref = orc.quantize(TYPES[tname][1], w, rule=rule)
+    got = Q.quantize(torch.from_numpy(w).to(DEV), TYPES[tname][0], rule=rule)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.data.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("tname", ["Q8_B64", "Q4_B64"])
+def test_dequantize_64_blocks_bit_exact(orc, tname):
+    M, K = 67, 2048 + 192
+    _banner(f"dequantize {tname}")
+    w = _adversarial(M, K, 5)
+    packed = orc.quantize(TYPES[tname][1], w)
+    ref = orc.dequantize(TYPES[tname][1], packed, K)
+    rs = B.row_size(TYPES[tname][0], K)
+    buf = torch.full((M, rs + 32), 0x7F, dtype=torch.uint8, device=DEV)   # padded pitch, junk padding
+    buf[:, :rs] = torch.from_numpy(packed).to(DEV)
+    got = Q.dequantize(B.Weight(buf, TYPES[tname][0], K, M)).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
 # ---------------------------------------------------------------- GEMV
 
 GEMV_CASES = [
@@ -229,6 +261,9 @@ GEMV_CASES = [
     ("Q4_0", 8200, 2048, 3), ("Q8_0", 8195, 1024, 4),
     # K beyond 128 blocks: passes that add to y (Wdown's K = 5632; four passes)
     ("Q4_0", 300, 5632, 6), ("Q8_0", 77, 16384, 5),
+    # 64-weight blocks (one scale per two 32-code runs)
+    ("Q4_B64", 5632, 2048, 1), ("Q8_B64", 300, 5632, 3), ("Q4_B64", 100, 192, 8), ("Q8_B64", 4099, 2048, 2),
+    ("Q4_B64", 64, 16384, 5), ("Q8_B64", 1, 64, 1), ("Q4_B64", 8200, 2048, 4),
 ]
 
 
@@ -298,6 +333,7 @@ SWIGLU_CASES = [
     ("Q4_0", 37, 96, 1), ("Q4_0", 300, 1024, 2), ("Q4_0", 129, 2048, 3),
     ("Q8_0", 513, 512, 8), ("Q8_0", 64, 4096, 5), ("Q8_0", 1, 32, 1),
     ("F16", 77, 1003, 2), ("F16", 260, 2048, 4),
+    ("Q4_B64", 300, 2048, 2), ("Q8_B64", 65, 192, 1),
 ]
 
 
@@ -446,6 +482,7 @@ GEMM_CASES = [
     ("Q4_0", 200, 5632, 300), ("Q4_0", 64, 2048 + 32, 64), ("Q8_0", 130, 2048, 65),
     ("Q8_0", 33, 96, 257),
     ("F16", 130, 2048, 65), ("F16", 33, 96, 257), ("F16", 200, 2048 + 32, 300), ("F16", 1, 32, 1),
+    ("Q4_B64", 257, 2048, 129), ("Q4_B64", 130, 64, 7), ("Q8_B64", 200, 5632, 300), ("Q8_B64", 33, 192, 65),
 ]
 
 
