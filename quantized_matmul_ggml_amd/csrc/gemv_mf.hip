@@ -125,14 +125,14 @@ __device__ inline void swap16(uint32_t &a, uint32_t &b)
 // blocks of each row (SB = 16 U bytes, U 16-byte units) and their scales
 // (SR bytes), as the direct-to-LDS loads deliver them: one load instruction
 // moves 64 lanes x 16 contiguous bytes of RPI whole rows; the scales come
-// with 4-byte lanes.
-template <int WT, int NBW>
+// with 4-byte lanes (one fp16 scale per 32 weights, or per 64 with SS = 1).
+template <int WT, int NBW, int SS>
 struct MfStage {
     static constexpr int SB = NBW * MfFmt<WT>::block_bytes;
     static constexpr int U = SB / 16;
     static constexpr int RPI = 64 / U;
     static constexpr int NI = kTileRows / RPI;                 // code load instructions
-    static constexpr int SR = 2 * NBW;
+    static constexpr int SR = (2 * NBW) >> SS;
     static constexpr int NS = (kTileRows * SR + 255) / 256;    // scale load instructions
     static constexpr int CODE_BYTES = NI * 1024;
     static constexpr int BYTES = CODE_BYTES + NS * 256;
@@ -186,29 +186,29 @@ __device__ inline void wait_vm()
 // LDS of a workgroup with KW waves and NSTG stages, and the most stages (up
 // to MAXD, at least 2) that fit the CU's 160 KiB.
 constexpr int kLdsBytes = 160 * 1024;
-template <int WT, int KW, int NBW>
+template <int WT, int KW, int NBW, int SS>
 constexpr int mf_lds_bytes(int nstg)
 {
-    return nstg * KW * MfStage<WT, NBW>::BYTES + (2 * KW * 64 * 2 + KW * NBW * 16) * 4;
+    return nstg * KW * MfStage<WT, NBW, SS>::BYTES + (2 * KW * 64 * 2 + KW * NBW * 16) * 4;
 }
-template <int WT, int KW, int NBW, int MAXD>
+template <int WT, int KW, int NBW, int SS, int MAXD>
 constexpr int mf_stages()
 {
     int d = MAXD;
-    while (d > 2 && mf_lds_bytes<WT, KW, NBW>(d) > kLdsBytes) --d;
+    while (d > 2 && mf_lds_bytes<WT, KW, NBW, SS>(d) > kLdsBytes) --d;
     return d;
 }
 
-template <int WT, int KW, int NBW, int MAXD>
+template <int WT, int KW, int NBW, int SS, int MAXD>
 __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
 {
-    constexpr int NSTG = mf_stages<WT, KW, NBW, MAXD>();
-    static_assert(mf_lds_bytes<WT, KW, NBW>(NSTG) <= kLdsBytes, "LDS of one workgroup");
+    constexpr int NSTG = mf_stages<WT, KW, NBW, SS, MAXD>();
+    static_assert(mf_lds_bytes<WT, KW, NBW, SS>(NSTG) <= kLdsBytes, "LDS of one workgroup");
     constexpr int BPG = MfFmt<WT>::bpg;
     constexpr int BB = MfFmt<WT>::block_bytes;
     constexpr int NG = NBW / BPG;          // 64-byte groups per row per wave
     static_assert(NBW % BPG == 0, "whole load groups");
-    using St = MfStage<WT, NBW>;
+    using St = MfStage<WT, NBW, SS>;
     static_assert(NSTG >= 2 && NSTG <= 4, "2 to 4 stages");
     __shared__ float red[2][KW][64][2];
     __shared__ float ssum[KW][NBW][16];
@@ -260,8 +260,10 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
         for (int i = 0; i < St::NS; ++i) {
             const int byte = 256 * i + 4 * lane;
             const int r = byte / St::SR, rb = byte % St::SR;
-            const uint32_t off = (r < kTileRows && b_begin + rb / 2 < nb)
-                                     ? (uint32_t)r * pitch + (uint32_t)(2 * (kb0 + b_begin) + rb)
+            // scale rb / 2 of the wave's slice is that of 32-block
+            // b_begin + (rb / 2 << SS) (kb0 and b_begin are even)
+            const uint32_t off = (r < kTileRows && (b_begin >> SS) + rb / 2 < (nb >> SS))
+                                     ? (uint32_t)r * pitch + (uint32_t)(2 * ((kb0 + b_begin) >> SS) + rb)
                                      : OUT_OF_RANGE;
             load_to_lds<4>(wres, base + St::CODE_BYTES + 256 * i, off);
         }
@@ -350,7 +352,9 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
         const uint8_t *base = stg[wave];
         // row j's scales, then its units 4p + g
         uint32_t sc[St::SR / 4];
-        if constexpr (St::SR == 8) {
+        if constexpr (St::SR == 4) {
+            sc[0] = *reinterpret_cast<const uint32_t *>(base + St::CODE_BYTES + St::SR * j);
+        } else if constexpr (St::SR == 8) {
             const uint2 v = *reinterpret_cast<const uint2 *>(base + St::CODE_BYTES + St::SR * j);
             sc[0] = v.x;
             sc[1] = v.y;
@@ -402,8 +406,9 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
                 // a block past the row (its codes and activations read as
                 // zeros) may pick up a scale from the bytes after the row's
                 // scales: weight it by 0
-                const uint32_t sw = sc[(p * BPG + t) / 2];
-                const float ds = (float)__builtin_bit_cast(_Float16, (uint16_t)((t & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+                const int hw = (p * BPG + t) >> SS;             // the block's scale in the slice
+                const uint32_t sw = sc[hw / 2];
+                const float ds = (float)__builtin_bit_cast(_Float16, (uint16_t)((hw & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
                 const float d = (b_begin + p * BPG + t < nb) ? ds : 0.0f;
                 yp0 = fmaf(d, D[0] + D[1] + cb[p * BPG + t][0], yp0);
                 yp1 = fmaf(d, D[2] + D[3] + cb[p * BPG + t][1], yp1);
@@ -478,15 +483,15 @@ constexpr int kWaves = 8;
 constexpr int kPassBlocks = 16 * kWaves;
 template <int WT> constexpr int max_stages() { return WT == W_Q4_0 ? 4 : 3; }
 
-// The kernel for (type, NBW) and its LDS bytes.
-template <int WT>
+// The kernel for (type, NBW, scale shift) and its LDS bytes.
+template <int WT, int SS>
 MfKernel pick_mf(int nbw, int *lds)
 {
     constexpr int D = max_stages<WT>();
     switch (nbw) {
-    case 4: *lds = mf_lds_bytes<WT, kWaves, 4>(mf_stages<WT, kWaves, 4, D>()); return gemv_mf_kernel<WT, kWaves, 4, D>;
-    case 8: *lds = mf_lds_bytes<WT, kWaves, 8>(mf_stages<WT, kWaves, 8, D>()); return gemv_mf_kernel<WT, kWaves, 8, D>;
-    case 16: *lds = mf_lds_bytes<WT, kWaves, 16>(mf_stages<WT, kWaves, 16, D>()); return gemv_mf_kernel<WT, kWaves, 16, D>;
+    case 4: *lds = mf_lds_bytes<WT, kWaves, 4, SS>(mf_stages<WT, kWaves, 4, SS, D>()); return gemv_mf_kernel<WT, kWaves, 4, SS, D>;
+    case 8: *lds = mf_lds_bytes<WT, kWaves, 8, SS>(mf_stages<WT, kWaves, 8, SS, D>()); return gemv_mf_kernel<WT, kWaves, 8, SS, D>;
+    case 16: *lds = mf_lds_bytes<WT, kWaves, 16, SS>(mf_stages<WT, kWaves, 16, SS, D>()); return gemv_mf_kernel<WT, kWaves, 16, SS, D>;
     default: return nullptr;
     }
 }
@@ -506,7 +511,6 @@ bool gemv_mf_supported(const GemvTask *tasks, int count)
     const int type = tasks[0].w.type;
     const int64_t K = tasks[0].w.K;
     if (!(type == W_Q4_0 || type == W_Q8_0) || K % 32 != 0 || K == 0) return false;
-    if (tasks[0].w.scale_shift != 0) return false;   // 64-blocks: the VALU kernel
     // a 16-row tile is one buffer resource with 32-bit offsets
     // and the activations of up to 8 tokens another (byte offsets < 2^31)
     for (int i = 0; i < count; ++i) {
@@ -534,8 +538,9 @@ hipError_t launch_gemv_mf(const GemvTask *tasks, int count, hipStream_t stream)
             const int64_t nb = nb_row - kb0 < kPassBlocks ? nb_row - kb0 : kPassBlocks;
             MfKernel k = nullptr;
             int lds = kLdsBytes;
-            if (type == W_Q4_0) k = pick_mf<W_Q4_0>(mf_nbw(nb), &lds);
-            else if (type == W_Q8_0) k = pick_mf<W_Q8_0>(mf_nbw(nb), &lds);
+            const int ss = tasks[0].w.scale_shift;
+            if (type == W_Q4_0) k = ss ? pick_mf<W_Q4_0, 1>(mf_nbw(nb), &lds) : pick_mf<W_Q4_0, 0>(mf_nbw(nb), &lds);
+            else if (type == W_Q8_0) k = ss ? pick_mf<W_Q8_0, 1>(mf_nbw(nb), &lds) : pick_mf<W_Q8_0, 0>(mf_nbw(nb), &lds);
             if (!k) return hipErrorInvalidValue;
             // a workgroup streams several tiles with its activation fragments
             // resident: as many workgroups as the LDS of the 256 CUs holds
@@ -543,7 +548,7 @@ hipError_t launch_gemv_mf(const GemvTask *tasks, int count, hipStream_t stream)
             MfArgs a = {};
             a.N = (int32_t)(N - n0 < 8 ? N - n0 : 8);
             a.K = (int32_t)(32 * nb);
-            a.qoff = (int32_t)quant_offset(K);
+            a.qoff = (int32_t)quant_offset(K, tasks[0].w.scale_shift);
             a.nb = (int32_t)nb;
             a.kb0 = (int32_t)kb0;
             a.nb_row = (int32_t)nb_row;
