@@ -471,26 +471,28 @@ int orc_records_to_rows(int type, const uint8_t *records, int64_t K, int64_t M,
 
 /* ---- integer-activation MUL_MAT ------------------------------------------- */
 
-/* Integer code i of block b of a packed row: Q8_0 the int8 code, Q4_0 the
- * nibble minus 8 (the pages' q in [-8, 7]). */
+/* Integer code i of the b-th run of 32 codes of a packed row: Q8 the int8
+ * code, Q4 the nibble minus 8 (the pages' q in [-8, 7]). */
 static int block_code(int type, const uint8_t *row, int64_t K, int64_t b, int i)
 {
-    const size_t qoff = align16((size_t)K / 16u);
-    if (type == ORC_Q8_0) return (int8_t)row[qoff + (size_t)b * 32u + (size_t)i];
+    const size_t qoff = scale_bytes(type, K);
+    if (is_q8(type)) return (int8_t)row[qoff + (size_t)b * 32u + (size_t)i];
     const uint8_t byte = row[qoff + (size_t)b * 16u + (size_t)(i & 15)];
     return ((i < 16) ? (byte & 0x0F) : (byte >> 4)) - 8;
 }
 
-static double block_scale(const uint8_t *row, int64_t b)
+/* The scale of the b-th run of 32 codes: that of the block holding it. */
+static double block_scale(int type, const uint8_t *row, int64_t b)
 {
-    return (double)orc_f16_to_f32((uint16_t)(row[2 * b] | (row[2 * b + 1] << 8)));
+    const int64_t s = b / (block_len(type) / 32);
+    return (double)orc_f16_to_f32((uint16_t)(row[2 * s] | (row[2 * s + 1] << 8)));
 }
 
 int orc_mul_mat_q8act_rows(int type, const uint8_t *w, size_t pitch, int64_t K, int64_t M,
                            const uint8_t *xq, size_t x_pitch, int64_t N,
                            int64_t m0, int64_t m1, double *y, double *a)
 {
-    if ((type != ORC_Q8_0 && type != ORC_Q4_0) || K < 0 || K % 32 != 0 || M < 0 || N < 0) return -1;
+    if (!is_quant(type) || K < 0 || K % block_len(type) != 0 || M < 0 || N < 0) return -1;
     if (pitch < orc_row_size(type, K) || x_pitch < orc_row_size(ORC_Q8_0, K)) return -1;
     if (m0 < 0 || m1 > M || m0 > m1) return -1;
     for (int64_t m = m0; m < m1; ++m) {
@@ -502,7 +504,7 @@ int orc_mul_mat_q8act_rows(int type, const uint8_t *w, size_t pitch, int64_t K, 
                 int64_t s = 0;
                 for (int i = 0; i < 32; ++i)
                     s += (int64_t)block_code(type, wr, K, b, i) * block_code(ORC_Q8_0, xr, K, b, i);
-                const double t = block_scale(wr, b) * block_scale(xr, b) * (double)s;
+                const double t = block_scale(type, wr, b) * block_scale(ORC_Q8_0, xr, b) * (double)s;
                 acc += t;
                 aacc += fabs(t);
             }

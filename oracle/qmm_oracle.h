@@ -121,9 +121,11 @@ int orc_mul_mat_pairs(int type, const uint8_t *w, size_t pitch, int64_t K, int64
  * "A Complete Guide to llama.cpp and Customization with C++", §2.2: with the
  * activations quantized per block as well, x_i ~= Delta_x * qx_i, the block
  * dot product is y ~= Delta * Delta_x * sum_i q_i qx_i, whose sum is pure
- * integer arithmetic.  Weights: Q8_0 (q = code) or Q4_0 (q = nibble - 8);
- * activations: Q8_0 rows of the same K (quantized by orc_quantize_rows, the
- * Q8_0 rule).  y[n][m] = sum_b Delta_w(m,b) Delta_x(n,b) S_b with the
+ * integer arithmetic.  Weights: Q8_0 (q = code) or Q4_0 (q = nibble - 8),
+ * or their 64-block forms (b then runs over 32-code runs and Delta_w(m,b) is
+ * the scale of the 64-block holding run b); activations: Q8_0 rows of the
+ * same K (quantized by orc_quantize_rows, the Q8_0 rule).
+ * y[n][m] = sum_b Delta_w(m,b) Delta_x(n,b) S_b with the
  * integer S_b = sum_i q_i qx_i exact in int64 and the block terms summed in
  * binary64 (every term is exact there: at most 11 + 11 + 20 bits);
  * a[n][m] = sum_b |Delta_w Delta_x S_b|.  Rows [m0, m1) only.             */

@@ -10,7 +10,8 @@ Pinned by: a hand-worked block; the identity with the exact MUL_MAT over
 the dequantized activations (every block term Delta_w q Delta_x qx is exact,
 so the two differ only by binary64 summation order); the quantization
 bound |y_int - y(x)| <= sum_k |W'_k| Delta_x(k) / 2 against the float
-activations; and the factored form with all-ones codes.
+activations; the factored form with all-ones codes; and, for 64-block
+weights, the same identity plus the reduction to 32-block weights.
 """
 import numpy as np
 
@@ -48,8 +49,8 @@ def test_hand_worked_block(orc):
 
 def test_equals_exact_mul_mat_on_dequantized_activations(orc):
     rng = np.random.default_rng(3)
-    for type_ in (orc.Q4_0, orc.Q8_0):
-        for M, K, N in ((7, 96, 3), (33, 2048, 2), (5, 5632, 1)):
+    for type_ in (orc.Q4_0, orc.Q8_0, orc.Q4_B64, orc.Q8_B64):
+        for M, K, N in ((7, 128, 3), (33, 2048, 2), (5, 5632, 1)):
             w = (rng.standard_normal((M, K)) * 0.02).astype(np.float32)
             x = rng.standard_normal((N, K)).astype(np.float32)
             packed = orc.quantize(type_, w)
@@ -94,3 +95,19 @@ def test_factored_form_all_ones(orc):
     xq[0, qoff:qoff + K] = 1
     y, _ = orc.mul_mat_q8act(orc.Q8_0, w, K, xq)
     assert y[0, 0] == 32 * sum(a * b for a, b in zip(dw, dxs))
+
+
+def test_64_block_weights_reduce_to_32_blocks(orc):
+    """Weights whose 64-block halves share amax quantize to the same codes
+    and scales in both forms (pinned in test_oracle_b64), so the integer path
+    gives bit-identical results for the two."""
+    rng = np.random.default_rng(5)
+    M, K, N = 9, 2048, 3
+    w = (rng.standard_normal((M, K)) * 0.02).astype(np.float32)
+    b = w.reshape(M, K // 64, 2, 32)
+    b[:, :, 1, :] = -b[:, :, 0, ::-1]
+    xq = orc.quantize(orc.Q8_0, rng.standard_normal((N, K)).astype(np.float32))
+    for t64, t32 in ((orc.Q4_B64, orc.Q4_0), (orc.Q8_B64, orc.Q8_0)):
+        y64, a64 = orc.mul_mat_q8act(t64, orc.quantize(t64, w), K, xq)
+        y32, a32 = orc.mul_mat_q8act(t32, orc.quantize(t32, w), K, xq)
+        assert np.array_equal(y64, y32) and np.array_equal(a64, a32)
