@@ -169,8 +169,9 @@ QMM_API int qmm_dequantize(const qmm_tensor *src, qmm_tensor *dst_f32, void *str
 /* Integer activations ("A Complete Guide to llama.cpp ...", §2.2: with x
  * quantized per block too, x_i ~= Delta_x qx_i, the block dot product is
  * Delta Delta_x sum_i q_i qx_i, an integer sum): when x is Q8_0 (ne = [K, N],
- * the activations quantized with qmm_quantize, 1 <= N <= 8), w must be Q8_0
- * or Q4_0 (32-blocks like x; else QMM_ERR_TYPE) and
+ * the activations quantized with qmm_quantize, 1 <= N <= 8), w must be
+ * quantized (else QMM_ERR_TYPE; with 64-blocks, Delta_w(m,b) below is the
+ * scale of the 64-block holding the 32-block b) and
  *   y[n][m] = sum_b Delta_w(m,b) Delta_x(n,b) sum_i q_i qx_i
  * with each block's integer sum exact (int8 dot products into int32) and
  * the block terms summed in binary32 (|y - exact| <= (K/16 + 16) 2^-24

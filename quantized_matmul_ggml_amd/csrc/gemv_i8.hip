@@ -37,11 +37,13 @@ struct I8Args {
     int32_t M;
     int32_t N;
     int32_t K;
-    int32_t qoff;          // code offset inside a row (the same for both operands: same K)
+    int32_t qoff;          // code offset inside an activation row (Q8_0, 32-blocks)
     int32_t nchunk;        // 16-byte chunks of weight codes per row
     int32_t n_groups;
     int32_t wg_count;
     int32_t iters;
+    int32_t wqoff;         // code offset inside a weight row (qoff for 32-blocks)
+    int32_t scale_shift;   // 1: the weights have one scale per two 32-code runs
 };
 
 // Per 16-byte chunk of weight codes: Q4_0 one block (32 weights, 8 dwords of
@@ -132,14 +134,15 @@ __global__ __launch_bounds__(kThreads) void gemv_i8_kernel(const I8Args a)
 
     // ---- weights: as gemv.hip (buffer resource per row group, unconditional loads) ----
     const int code_bytes = (WT == W_Q4_0) ? K / 2 : K;
-    const uint32_t row_bytes = (uint32_t)(qoff + code_bytes);
+    const int wqoff = a.wqoff, sshift = a.scale_shift;
+    const uint32_t row_bytes = (uint32_t)(wqoff + code_bytes);
     uint32_t qoffs[CPL], soffs[CPL];
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
         const int c = v + j * VL;
         const bool in_row = c < nchunk;
-        qoffs[j] = in_row ? (uint32_t)(qoff + 16 * c) : OUT_OF_RANGE;
-        soffs[j] = in_row ? (uint32_t)(2 * chunk_block<WT>(c)) : OUT_OF_RANGE;
+        qoffs[j] = in_row ? (uint32_t)(wqoff + 16 * c) : OUT_OF_RANGE;
+        soffs[j] = in_row ? (uint32_t)(2 * (chunk_block<WT>(c) >> sshift)) : OUT_OF_RANGE;
     }
     uint4 q[U][CPL];
     uint16_t sc[U][CPL];
@@ -315,6 +318,8 @@ hipError_t launch_gemv_i8(const WeightView &w, const WeightView &xq, const OutVi
     a.M = (int32_t)w.M;
     a.K = (int32_t)w.K;
     a.qoff = (int32_t)quant_offset(w.K);
+    a.wqoff = (int32_t)quant_offset(w.K, w.scale_shift);
+    a.scale_shift = w.scale_shift;
     a.nchunk = (int32_t)((w.type == W_Q4_0 ? w.K / 2 : w.K) / 16);
     a.n_groups = (int32_t)((w.M + c.u - 1) / c.u);
     int64_t wgs = (a.n_groups + groups_per_wg - 1) / groups_per_wg;

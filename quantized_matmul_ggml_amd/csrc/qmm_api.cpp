@@ -189,11 +189,11 @@ int qmm_gemv(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *stre
         // the integer-activation path ("A Complete Guide to llama.cpp ...", §2.2)
         int rc = check_mul_mat(w, x, y, QMM_TYPE_Q8_0, 16);
         if (rc) return rc;
-        if (w->type != QMM_TYPE_Q8_0 && w->type != QMM_TYPE_Q4_0) return QMM_ERR_TYPE;   // 32-blocks like x
+        if (!is_quant(w->type)) return QMM_ERR_TYPE;
         if (x->ne[1] > 8) return QMM_ERR_SHAPE;
         if (x->ne[1] == 0 || w->ne[1] == 0) return QMM_OK;
-        if (!qmm::gemv_i8_supported(w->type, w->ne[0], w->ne[1], x->ne[1])) return QMM_ERR_UNSUPPORTED;
         const qmm::WeightView wv = weight_view(w), xv = weight_view(x);
+        if (!qmm::gemv_i8_supported(wv.type, w->ne[0], w->ne[1], x->ne[1])) return QMM_ERR_UNSUPPORTED;
         qmm::OutView yv{static_cast<float *>(y->data), pitch_elems(y)};
         if (wv.pitch > (1ull << 28) || xv.pitch > (1ull << 28) || wv.M >= (1ll << 31) ||
             yv.pitch_elems >= (1ull << 31))

@@ -280,8 +280,8 @@ def test_64_block_types_reject(qmm_lib):
     assert B.call_raw("qmm_gemv", B.make_desc(B.Q4_B64, 2080, 64, 1104, W_ADDR), _x(K=2080), _y()) == B.ERR_SHAPE
     assert B.call_raw("qmm_quantize", B.make_desc(B.F32, 2080, 64, 8320, X_ADDR),
                       B.make_desc(B.Q8_B64, 2080, 64, 2176, W_ADDR)) == B.ERR_SHAPE
-    # the integer-activation path needs 32-blocks like x
-    xq = B.make_desc(B.Q8_0, 2048, 1, 2176, X_ADDR)
+    # the integer-activation path takes them too, but its activations stay Q8_0
+    xq = B.make_desc(B.Q8_B64, 2048, 1, 2112, X_ADDR)
     assert B.call_raw("qmm_gemv", w, xq, _y()) == B.ERR_TYPE
     # no GGUF record for 64-blocks
     R_ADDR = BASE + (4 << 32)

@@ -702,6 +702,8 @@ I8_CASES = [
     ("Q8_0", 32000, 2048, 8), ("Q8_0", 32000, 2048, 1), ("Q4_0", 300, 1024, 3),
     ("Q8_0", 37, 96, 5), ("Q4_0", 1, 32, 1), ("Q8_0", 513, 512, 2), ("Q4_0", 64, 16384, 2),
     ("Q4_0", 130, 8192, 8),
+    # 64-block weights: each 32-block term takes its 64-block's scale
+    ("Q4_B64", 5632, 2048, 1), ("Q8_B64", 300, 5632, 3), ("Q4_B64", 37, 128, 8), ("Q8_B64", 513, 512, 2),
 ]
 
 
@@ -723,7 +725,7 @@ def test_gemv_q8_activations(orc, case):
     yref, _ = orc.mul_mat_q8act(TYPES[tname][1], packed, K, xq_ref)
     _, a_exact = orc.mul_mat(TYPES[tname][1], packed, K, orc.dequantize(orc.Q8_0, xq_ref, K))
     y = Q.gemv(wt, xq).cpu().numpy().astype(np.float64)
-    nchunk = K // 32 if tname == "Q4_0" else K // 16
+    nchunk = K // 32 if tname.startswith("Q4") else K // 16
     tol = (nchunk + 16) * 2.0 ** -24 * a_exact + 1e-30
     err = np.abs(y - yref)
     assert (err <= tol).all(), f"worst err/tol {(err / tol).max():.3g}"
