@@ -165,7 +165,11 @@ QMM_API int qmm_dequantize(const qmm_tensor *src, qmm_tensor *dst_f32, void *str
  * the registers (one pass over the weights per group).
  * Weights are read once from HBM and dequantized in registers; binary32
  * multiply-add; the accumulation order is unspecified (results agree with
- * the exact sum within 1e-4 * sum_k |W'[m][k] x[n][k]| + 1e-6). */
+ * the exact sum within 1e-4 * sum_k |W'[m][k] x[n][k]| + 1e-6).  From 5
+ * tokens (3 when the call has at least 8192 rows), quantized weights go to
+ * the bf16 matrix cores instead: codes enter exactly, x as two bfloat16
+ * parts (x = hi + lo to 2^-17 relative), products accumulated in binary32,
+ * within the same bound. */
 /* Integer activations ("A Complete Guide to llama.cpp ...", §2.2: with x
  * quantized per block too, x_i ~= Delta_x qx_i, the block dot product is
  * Delta Delta_x sum_i q_i qx_i, an integer sum): when x is Q8_0 (ne = [K, N],
