@@ -374,13 +374,32 @@ def prefill_leg(Q, WL, dev, args):
     ms_b, _ = timed(g64, max(2, args.steps // 2), 2)
     tf_b = flops / (ms_b / reps * 1e-3) / 1e12
     log(f"prefill GEMM, Q4_B64 weights {ms_b / reps * 1e3:.1f} us  {tf_b:.0f} TFLOP/s")
+    # the layer's other prefill shapes, which leave compute units idle at 128 x 128
+    # tiles: K split over a workspace (two launches) against one launch without
+    shapes = {}
+    for name, Ms, Ks in (("wdown", WL.HIDDEN, WL.FFN), ("wq", WL.HIDDEN, WL.HIDDEN), ("wk", 256, WL.HIDDEN)):
+        ws_w = Q.quantize(WL.weights_device(WL.seed(5, 4), Ms, Ks, dev), Q.Q4_0)
+        ws_x = WL.activations_device(WL.seed(5, 5), N, Ks, dev).to(torch.bfloat16)
+        ws_y = torch.empty((N, Ms), device=dev)
+        nbytes = Q.gemm_workspace_size(ws_w, ws_x)
+        buf = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)[:nbytes]
+        row = {"workspace_bytes": nbytes}
+        for mode, wsarg in (("split", buf), ("unsplit", None)):
+            gs = Graph(lambda: [Q.gemm(ws_w, ws_x, out=ws_y, workspace=wsarg) for _ in range(reps)])
+            ms_s, _ = timed(gs, max(2, args.steps // 2), 2)
+            us = ms_s / reps * 1e3
+            row[mode] = {"us": round(us, 2), "tflops": round(2.0 * Ms * Ks * N / (us * 1e-6) / 1e12, 1)}
+        log(f"prefill {name} {Ms}x{Ks}x{N}: split {row['split']['us']:.1f} us, unsplit {row['unsplit']['us']:.1f} us")
+        shapes[f"{name}_{Ms}x{Ks}x{N}"] = row
+        del ws_w, ws_x, ws_y, buf
     return {"workload": "Q4_0 5632 x 2048 x bf16 2048 x 512 -> f32", "us": round(per * 1e3, 2),
             "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
             "avg_launch_us": round(kern * 1e3, 2), "flops": flops,
             "f16_weights": {"us": round(ms_f / reps * 1e3, 2), "tflops": round(tf_f, 1),
                             "frac_of_bf16_peak": round(tf_f / BF16_PEAK_TFLOPS, 4)},
             "q4_b64_weights": {"us": round(ms_b / reps * 1e3, 2), "tflops": round(tf_b, 1),
-                               "frac_of_bf16_peak": round(tf_b / BF16_PEAK_TFLOPS, 4)}}
+                               "frac_of_bf16_peak": round(tf_b / BF16_PEAK_TFLOPS, 4)},
+            "split_k_shapes": shapes}
 
 
 def breakdown_leg(Q, WL, dev, args, gemv_bytes):

@@ -232,6 +232,30 @@ QMM_API int qmm_gemv_swiglu(const qmm_tensor *w_gate, const qmm_tensor *w_up,
  * sum of the weights within 1e-2 * sum_k |W'[m][k] x[n][k]| + 1e-5). */
 QMM_API int qmm_gemm(const qmm_tensor *w, const qmm_tensor *x_bf16, qmm_tensor *y_f32, void *stream);
 
+/* qmm_gemm with a caller-owned workspace that lets a product with too few
+ * output tiles to occupy every compute unit split K ("No Python! ...", §6:
+ * C_ij = sum_k A_ik B_kj is a sum over k, so it can be cut into k ranges
+ * whose partial sums are added afterwards).  Each range's partial sums go to
+ * the workspace; a second kernel on the same stream adds them in range order,
+ * so results are deterministic (the same for every call with the same
+ * workspace size) and agree with the exact sum within the qmm_gemm bound.
+ *
+ * qmm_gemm_workspace_size(w, x_bf16): bytes the split that the current
+ * device's compute-unit count calls for uses (0 when K is not split, or for
+ * NULL descriptors); it depends only on the shapes and the device.
+ *
+ * qmm_gemm_ws: operands and errors as qmm_gemm.  workspace: device memory,
+ * 16-byte aligned (else QMM_ERR_LAYOUT), overlapping none of w, x, y in the
+ * bytes the call uses (QMM_ERR_ALIAS); workspace_bytes: its size.  A NULL
+ * workspace or a size below the planned one makes the call choose a smaller
+ * split that fits, down to none (then it is qmm_gemm).  The workspace is
+ * scratch: its contents on entry do not matter, it is written and read by
+ * the enqueued kernels, and it must stay allocated, and unused by other
+ * work, until they have run.  qmm_gemm is qmm_gemm_ws with no workspace. */
+QMM_API size_t qmm_gemm_workspace_size(const qmm_tensor *w, const qmm_tensor *x_bf16);
+QMM_API int qmm_gemm_ws(const qmm_tensor *w, const qmm_tensor *x_bf16, qmm_tensor *y_f32, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
 /* GGUF-style block records ("Development Guide for Small AI Models (TinyLLaMA,
  * etc.) Using C++", §3.2: a GGUF file's tensor data is an aligned array;
  * §6.1: a Q4_0 block is one FP16 scale (2 bytes) followed by 32 4-bit

@@ -27,7 +27,7 @@ OK, ERR_NULL, ERR_TYPE, ERR_SHAPE, ERR_LAYOUT, ERR_ALIAS, ERR_UNSUPPORTED, ERR_D
     0, -1, -2, -3, -4, -5, -6, -7
 
 EXPORTS = ("qmm_row_size", "qmm_quantize", "qmm_quantize_rule", "qmm_dequantize", "qmm_gemv", "qmm_gemv_batch",
-           "qmm_gemv_swiglu", "qmm_gemm", "qmm_record_size", "qmm_records_to_rows",
+           "qmm_gemv_swiglu", "qmm_gemm", "qmm_gemm_ws", "qmm_gemm_workspace_size", "qmm_record_size", "qmm_records_to_rows",
            "qmm_rows_to_records", "qmm_strerror")
 GEMV_BATCH_MAX = 8
 
@@ -72,6 +72,10 @@ def lib() -> ctypes.CDLL:
         h.qmm_dequantize.argtypes = [P, P, ctypes.c_void_p]
         h.qmm_gemv.argtypes = [P, P, P, ctypes.c_void_p]
         h.qmm_gemm.argtypes = [P, P, P, ctypes.c_void_p]
+        h.qmm_gemm_ws.argtypes = [P, P, P, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        h.qmm_gemm_ws.restype = ctypes.c_int
+        h.qmm_gemm_workspace_size.argtypes = [P, P]
+        h.qmm_gemm_workspace_size.restype = ctypes.c_size_t
         h.qmm_gemv_swiglu.argtypes = [P, P, P, P, ctypes.c_void_p]
         h.qmm_gemv_swiglu.restype = ctypes.c_int
         h.qmm_record_size.argtypes = [ctypes.c_int32]
@@ -282,14 +286,37 @@ def rows_to_records(w: Weight, *, out: torch.Tensor | None = None, stream=None) 
     return out
 
 
-def gemm(w: Weight, x: torch.Tensor, *, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """y (N, M) fp32 = x (N, K) bf16 times W'^T on the bf16 matrix cores."""
+def gemm_workspace_size(w: Weight, x: torch.Tensor) -> int:
+    """Bytes of workspace qmm_gemm_ws uses to split K for these shapes (0: no split)."""
+    wd, xd = w.desc(), _dense_desc(x, BF16)
+    return int(lib().qmm_gemm_workspace_size(ctypes.byref(wd), ctypes.byref(xd)))
+
+
+def gemm(w: Weight, x: torch.Tensor, *, out: torch.Tensor | None = None, workspace="auto",
+         stream=None) -> torch.Tensor:
+    """y (N, M) fp32 = x (N, K) bf16 times W'^T on the bf16 matrix cores.
+
+    workspace: "auto" allocates the split-K workspace the shapes call for (a
+    torch allocation, so it is graph-capture safe), None runs without one
+    (qmm_gemm), or a uint8 device tensor to use as is."""
     _need_gpu(w.data, x)
     if out is None:
         out = torch.empty((x.shape[0], w.M), dtype=torch.float32, device=x.device)
     wd, xd, yd = w.desc(), _dense_desc(x, BF16), _dense_desc(out, F32)
-    _check(lib().qmm_gemm(ctypes.byref(wd), ctypes.byref(xd), ctypes.byref(yd), _stream(stream)),
-           "qmm_gemm")
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError(f"workspace must be 'auto', None or a tensor, not {workspace!r}")
+        n = int(lib().qmm_gemm_workspace_size(ctypes.byref(wd), ctypes.byref(xd)))
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device) if n else None
+    if workspace is None:
+        _check(lib().qmm_gemm(ctypes.byref(wd), ctypes.byref(xd), ctypes.byref(yd), _stream(stream)),
+               "qmm_gemm")
+    else:
+        _need_gpu(workspace)
+        _check(lib().qmm_gemm_ws(ctypes.byref(wd), ctypes.byref(xd), ctypes.byref(yd),
+                                 ctypes.c_void_p(workspace.data_ptr()),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+               "qmm_gemm_ws")
     return out
 
 

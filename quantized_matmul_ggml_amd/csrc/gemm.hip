@@ -26,6 +26,7 @@
 // zero; blocks past the end of K get a zero scale and zero tokens.
 #include "qmm_internal.h"
 
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -63,9 +64,12 @@ struct GemmArgs {
     const uint16_t *x;      // bf16 bits, row n at x + n * x_pitch
     uint64_t x_pitch;
     int64_t N;
-    float *y;
+    float *y;               // the output, or the first partial-sum slab
     uint64_t y_pitch;
     int n_tiles;
+    int n_splits;           // K ranges per tile (1: the whole K)
+    int split_steps;        // K-steps per range, a multiple of SCALE_GROUP_STEPS
+    uint64_t split_stride;  // floats between the slabs of consecutive ranges
 };
 
 // Round two floats to bf16 (nearest even) in one v_cvt_pk_bf16_f32.
@@ -174,13 +178,20 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
 
     // the division runs on the vector unit; the tile is uniform, so move it
     // back to scalar registers (buffer resources must live there)
-    const int tile = blockIdx.x;
+    // Workgroup b takes K range b % n_splits of tile b / n_splits: steps
+    // s0 .. s0 + steps - 1 of K.  Every offset below is relative to s0, and
+    // nblk counts the 32-blocks of K from block 2 s0 on.
+    const int split = __builtin_amdgcn_readfirstlane((int)blockIdx.x % a.n_splits);
+    const int tile = __builtin_amdgcn_readfirstlane((int)blockIdx.x / a.n_splits);
     const int mt = __builtin_amdgcn_readfirstlane(tile / a.n_tiles);
     const int nt = __builtin_amdgcn_readfirstlane(tile - mt * a.n_tiles);
     const int64_t m0 = (int64_t)mt * BM;
     const int64_t n0 = (int64_t)nt * BN;
-    const int64_t nblk = a.K / 32;
-    const int steps = (int)((a.K + BK - 1) / BK);
+    const int s0 = split * a.split_steps;
+    const int64_t nblk = a.K / 32 - 2 * (int64_t)s0;
+    const int all_steps = (int)((a.K + BK - 1) / BK);
+    const int steps = all_steps - s0 < a.split_steps ? all_steps - s0 : a.split_steps;
+    float *const out = a.y + (uint64_t)split * a.split_stride;
 
     // Step p of K sits in LDS stage p % STAGES and is complete at barrier p.
     // It is written between barriers p-2 and p-1 (weights by the producers,
@@ -212,8 +223,8 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
             (void *)(a.w + (uint64_t)m0 * a.pitch), 0,
             (int)(uint32_t)((rows - 1) * a.pitch + 2 * a.K), BUFFER_FLAGS);
         const int wrow0 = 32 * pw + 2 * (lane >> 2);
-        const uint32_t roff[2] = {(uint32_t)(wrow0 * a.pitch) + 16 * q4,
-                                  (uint32_t)((wrow0 + 1) * a.pitch) + 16 * q4};
+        const uint32_t roff[2] = {(uint32_t)(wrow0 * a.pitch) + 16 * q4 + 128u * s0,
+                                  (uint32_t)((wrow0 + 1) * a.pitch) + 16 * q4 + 128u * s0};
         uint16_t *fdst0 = lds + wrow0 * LDS_STRIDE + 8 * q4;
         struct FPair { u32x4 q[2][4]; };   // [row wrow0 + i][block v of the pair]
         FPair fr[F16_PAIRS];
@@ -282,7 +293,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
         uint32_t qoff[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-            qoff[i] = (uint32_t)((wrow0 + i) * a.pitch + a.qoff) + ((q4 + 2 * i) & 3) * QB;
+            qoff[i] = (uint32_t)((wrow0 + i) * a.pitch + a.qoff) + ((q4 + 2 * i) & 3) * QB + 2u * QB * s0;
         // step s of a pair uses load i_s = (q4 / 2 == s) ? 0 : 1; within its
         // step the block is half h = q4 % 2
         const int h = q4 & 1;
@@ -290,8 +301,10 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
         // scale load i covers rows wrow0 + i, blocks 4 q4 .. 4 q4 + 3 of a group
         // (64-blocks: blocks 2 q4, 2 q4 + 1, the group's 8 scales)
         constexpr uint32_t SLANE = SS ? 4 : 8;                  // scale bytes per lane and row
-        const uint32_t soff[2] = {(uint32_t)(wrow0 * a.pitch) + SLANE * q4,
-                                  (uint32_t)((wrow0 + 1) * a.pitch) + SLANE * q4};
+        // (scale bytes of a step: 4, or 2 with 64-blocks; s0 is a whole number of groups)
+        const uint32_t s0b = (SS ? 2u : 4u) * s0;
+        const uint32_t soff[2] = {(uint32_t)(wrow0 * a.pitch) + SLANE * q4 + s0b,
+                                  (uint32_t)((wrow0 + 1) * a.pitch) + SLANE * q4 + s0b};
         uint16_t *wdst0 = lds + wrow0 * LDS_STRIDE + 32 * h;
 
         struct WPair { u32x4 q[2][WBlock<WT>::QV]; };
@@ -388,9 +401,9 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
         (void *)(a.x + (uint64_t)n0 * a.x_pitch), 0,
         (int)(uint32_t)(((toks - 1) * a.x_pitch + a.K) * 2), BUFFER_FLAGS);
     const int xrow = 32 * c + (lane >> 3);
-    const uint32_t xoff = (uint32_t)(xrow * a.x_pitch * 2) + 16 * q8;
+    const uint32_t xoff = (uint32_t)(xrow * a.x_pitch * 2) + 16 * q8 + 128u * s0;
     const uint32_t xrow_step = (uint32_t)(8 * a.x_pitch * 2);
-    const int64_t xlim = a.K - 8 * q8;     // chunk q8 of step t is in K iff 64 t < xlim
+    const int64_t xlim = a.K - 8 * q8 - 64 * (int64_t)s0;   // chunk q8 of step t is in K iff 64 t < xlim
     uint16_t *xdst0 = lds + OPERAND_ELEMS + xrow * LDS_STRIDE + 8 * q8;
     struct XStep { u32x4 v[4]; };
     XStep xr[X_DEPTH];
@@ -519,7 +532,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t n = n0 + wn * 64 + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-                if (n < a.N) a.y[(uint64_t)n * a.y_pitch + m] = acc[i][j][r];
+                if (n < a.N) out[(uint64_t)n * a.y_pitch + m] = acc[i][j][r];
             }
         }
     }
@@ -528,15 +541,112 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
 constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_ELEMS * sizeof(uint16_t);
 
 template <int WT, int SS>
-hipError_t launch_typed(const GemmArgs &a, unsigned tiles, hipStream_t stream)
+hipError_t launch_typed(const GemmArgs &a, unsigned blocks, hipStream_t stream)
 {
     const hipError_t attr = allow_dynamic_lds(reinterpret_cast<const void *>(&gemm_kernel<WT, SS>), (int)LDS_BYTES);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemm_kernel<WT, SS>), dim3(tiles), dim3(THREADS), LDS_BYTES, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<WT, SS>), dim3(blocks), dim3(THREADS), LDS_BYTES, stream, a);
     return hipGetLastError();
 }
 
+// y[n][m] = sum over s = 0, 1, .., S-1 in that order of slab s's [n][m]:
+// the K ranges' partial sums added in a fixed order, so the result does not
+// depend on which workgroup finished first.  Slab rows are Mp floats (M
+// rounded up to 4), so each thread moves four outputs with 16-byte loads;
+// vec_y says whether y's rows allow 16-byte stores too.
+__global__ __launch_bounds__(256) void split_sum_kernel(const float *ws, uint64_t slab, int S, int64_t Mp,
+                                                        float *y, uint64_t y_pitch, int64_t M, int64_t N,
+                                                        int vec_y)
+{
+    const int64_t quads = Mp / 4;
+    const int64_t total = N * quads;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+        const int64_t n = i / quads;
+        const int64_t m = (i - n * quads) * 4;
+        const float *src = ws + (uint64_t)n * Mp + m;
+        float4 acc = *reinterpret_cast<const float4 *>(src);
+        for (int s = 1; s < S; ++s) {
+            const float4 v = *reinterpret_cast<const float4 *>(src + (uint64_t)s * slab);
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        float *dst = y + (uint64_t)n * y_pitch + m;
+        if (vec_y && m + 4 <= M) {
+            *reinterpret_cast<float4 *>(dst) = acc;
+        } else {
+            if (m < M) dst[0] = acc.x;
+            if (m + 1 < M) dst[1] = acc.y;
+            if (m + 2 < M) dst[2] = acc.z;
+            if (m + 3 < M) dst[3] = acc.w;
+        }
+    }
+}
+
+// Compute units of the current device (queried once per device).
+int device_cus()
+{
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < 64) {
+        const int c = cus[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    if (dev < 64) cus[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+constexpr int kMinSplitSteps = SCALE_GROUP_STEPS;   // K-steps of the shortest range (512 of K)
+
 }  // namespace
+
+GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N, uint64_t ws_bytes)
+{
+    GemmPlan p;
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int64_t steps = (K + BK - 1) / BK;
+    p.mp = (M + 3) / 4 * 4;
+    p.splits = 1;
+    p.split_steps = (int)steps;
+    p.ws_bytes = 0;
+    if (M <= 0 || N <= 0 || steps <= 0) return p;
+    // Estimated time (us) of a launch: a fixed part, the K-steps of one range
+    // at a per-step cost that grows with the workgroups running at once, and
+    // for a split the second launch plus the partial sums written and read
+    // back (fitted to timings of this kernel on MI355X over M = 256..5632,
+    // K = 2048..5632, N = 128..512; e.g. 2048 x 5632 x 512: 44.8 us whole,
+    // 26.7 us in four ranges, while 2048 x 2048 x 512 is fastest whole).
+    const int64_t cus = device_cus();
+    auto cost = [&](int64_t ranges, int64_t len) {
+        const double wgs = (double)(tiles * ranges);
+        const double step_us = 0.29 + 0.2 * wgs / 256.0;
+        double t = 10.0 + (double)len * step_us;
+        if (ranges > 1) t += 2.5 + 0.35e-6 * (double)ranges * (double)N * (double)p.mp * sizeof(float);
+        return t;
+    };
+    double best = cost(1, steps);
+    // Ranges are multiples of SCALE_GROUP_STEPS, at least kMinSplitSteps long,
+    // and one round of workgroups must still fit the chip.
+    for (int64_t s = 2; tiles * s <= cus && steps >= s * kMinSplitSteps; s *= 2) {
+        int64_t len = (steps + s - 1) / s;
+        len = (len + SCALE_GROUP_STEPS - 1) / SCALE_GROUP_STEPS * SCALE_GROUP_STEPS;
+        const int64_t used = (steps + len - 1) / len;
+        const uint64_t bytes = (uint64_t)used * (uint64_t)N * (uint64_t)p.mp * sizeof(float);
+        if (used < 2 || bytes > ws_bytes) continue;
+        const double t = cost(used, len);
+        if (t < best) {
+            best = t;
+            p.splits = (int)used;
+            p.split_steps = (int)len;
+            p.ws_bytes = bytes;
+        }
+    }
+    return p;
+}
 
 bool gemm_supported(const WeightView &w, const ActView &x)
 {
@@ -545,9 +655,10 @@ bool gemm_supported(const WeightView &w, const ActView &x)
 }
 
 hipError_t launch_gemm(const WeightView &w, const ActView &x, const OutView &y,
-                       hipStream_t stream)
+                       float *ws, uint64_t ws_bytes, hipStream_t stream)
 {
     if (w.M == 0 || x.N == 0) return hipSuccess;
+    const GemmPlan plan = gemm_plan(w.M, w.K, x.N, ws ? ws_bytes : 0);
     GemmArgs a;
     a.w = w.base;
     a.pitch = w.pitch;
@@ -557,19 +668,36 @@ hipError_t launch_gemm(const WeightView &w, const ActView &x, const OutView &y,
     a.x = static_cast<const uint16_t *>(x.data);
     a.x_pitch = x.pitch_elems;
     a.N = x.N;
-    a.y = y.data;
-    a.y_pitch = y.pitch_elems;
     a.n_tiles = (int)((x.N + BN - 1) / BN);
-    const unsigned tiles = (unsigned)((w.M + BM - 1) / BM) * (unsigned)a.n_tiles;
-    if (w.scale_shift) {
-        if (w.type == W_Q4_0) return launch_typed<W_Q4_0, 1>(a, tiles, stream);
-        if (w.type == W_Q8_0) return launch_typed<W_Q8_0, 1>(a, tiles, stream);
-        return hipErrorInvalidValue;
+    a.n_splits = plan.splits;
+    a.split_steps = plan.split_steps;
+    if (plan.splits > 1) {          // partial sums into the workspace slabs
+        a.y = ws;
+        a.y_pitch = (uint64_t)plan.mp;
+        a.split_stride = (uint64_t)x.N * (uint64_t)plan.mp;
+    } else {
+        a.y = y.data;
+        a.y_pitch = y.pitch_elems;
+        a.split_stride = 0;
     }
-    if (w.type == W_Q4_0) return launch_typed<W_Q4_0, 0>(a, tiles, stream);
-    if (w.type == W_Q8_0) return launch_typed<W_Q8_0, 0>(a, tiles, stream);
-    if (w.type == W_F16) return launch_typed<W_F16, 0>(a, tiles, stream);
-    return hipErrorInvalidValue;
+    const unsigned blocks = (unsigned)((w.M + BM - 1) / BM) * (unsigned)a.n_tiles * (unsigned)plan.splits;
+    hipError_t e = hipErrorInvalidValue;
+    if (w.scale_shift) {
+        if (w.type == W_Q4_0) e = launch_typed<W_Q4_0, 1>(a, blocks, stream);
+        else if (w.type == W_Q8_0) e = launch_typed<W_Q8_0, 1>(a, blocks, stream);
+    } else {
+        if (w.type == W_Q4_0) e = launch_typed<W_Q4_0, 0>(a, blocks, stream);
+        else if (w.type == W_Q8_0) e = launch_typed<W_Q8_0, 0>(a, blocks, stream);
+        else if (w.type == W_F16) e = launch_typed<W_F16, 0>(a, blocks, stream);
+    }
+    if (e != hipSuccess || plan.splits == 1) return e;
+    const int64_t quads = x.N * (plan.mp / 4);
+    const int64_t want = (quads + 255) / 256;
+    const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
+    const int vec_y = ((uintptr_t)y.data % 16 == 0 && y.pitch_elems % 4 == 0) ? 1 : 0;
+    hipLaunchKernelGGL(split_sum_kernel, dim3(grid), dim3(256), 0, stream, (const float *)ws,
+                       (uint64_t)a.split_stride, plan.splits, plan.mp, y.data, y.pitch_elems, w.M, x.N, vec_y);
+    return hipGetLastError();
 }
 
 // Raise a kernel's dynamic-LDS limit once (the attribute persists for the

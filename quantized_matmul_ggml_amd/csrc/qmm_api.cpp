@@ -322,18 +322,62 @@ int qmm_rows_to_records(const qmm_tensor *src, void *records, void *stream)
                                          static_cast<hipStream_t>(stream)));
 }
 
-int qmm_gemm(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *stream)
+namespace {
+
+int check_gemm(const qmm_tensor *w, const qmm_tensor *x, const qmm_tensor *y)
 {
-    int rc = check_mul_mat(w, x, y, QMM_TYPE_BF16, 16);
+    const int rc = check_mul_mat(w, x, y, QMM_TYPE_BF16, 16);
     if (rc) return rc;
     if (!(is_quant(w->type) || w->type == QMM_TYPE_F16)) return QMM_ERR_TYPE;
     // the F16 producer moves whole 32-weight blocks
     if (w->type == QMM_TYPE_F16 && w->ne[0] % 32 != 0) return QMM_ERR_UNSUPPORTED;
+    if (w->ne[1] == 0 || x->ne[1] == 0) return QMM_OK;
+    qmm::ActView xv{x->data, pitch_elems(x), x->ne[1]};
+    if (!qmm::gemm_supported(weight_view(w), xv)) return QMM_ERR_UNSUPPORTED;
+    return QMM_OK;
+}
+
+bool range_overlaps(uintptr_t lo, uintptr_t hi, const qmm_tensor *t)
+{
+    uintptr_t tlo, thi;
+    extent(t, &tlo, &thi);
+    if (lo == hi || tlo == thi) return false;
+    return lo < thi && tlo < hi;
+}
+
+}  // namespace
+
+int qmm_gemm(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *stream)
+{
+    return qmm_gemm_ws(w, x, y, nullptr, 0, stream);
+}
+
+size_t qmm_gemm_workspace_size(const qmm_tensor *w, const qmm_tensor *x)
+{
+    if (!w || !x) return 0;
+    if (w->n_dims < 1 || x->n_dims < 1) return 0;
+    return (size_t)qmm::gemm_plan(w->ne[1], w->ne[0], x->ne[1], ~0ull).ws_bytes;
+}
+
+int qmm_gemm_ws(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *workspace,
+                size_t workspace_bytes, void *stream)
+{
+    const int rc = check_gemm(w, x, y);
+    if (rc) return rc;
+    if (w->ne[1] == 0 || x->ne[1] == 0) return QMM_OK;
+    if (!workspace) workspace_bytes = 0;
+    if (workspace_bytes) {
+        if ((uintptr_t)workspace % 16 != 0) return QMM_ERR_LAYOUT;
+        const uint64_t used = qmm::gemm_plan(w->ne[1], w->ne[0], x->ne[1], workspace_bytes).ws_bytes;
+        const uintptr_t lo = (uintptr_t)workspace;
+        if (range_overlaps(lo, lo + used, w) || range_overlaps(lo, lo + used, x) ||
+            range_overlaps(lo, lo + used, y))
+            return QMM_ERR_ALIAS;
+    }
     qmm::ActView xv{x->data, pitch_elems(x), x->ne[1]};
     qmm::OutView yv{static_cast<float *>(y->data), pitch_elems(y)};
-    if (w->ne[1] == 0 || x->ne[1] == 0) return QMM_OK;
-    if (!qmm::gemm_supported(weight_view(w), xv)) return QMM_ERR_UNSUPPORTED;
-    return status_of(qmm::launch_gemm(weight_view(w), xv, yv, static_cast<hipStream_t>(stream)));
+    return status_of(qmm::launch_gemm(weight_view(w), xv, yv, static_cast<float *>(workspace),
+                                      workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
 const char *qmm_strerror(int status)

@@ -127,7 +127,20 @@ hipError_t launch_records(const WeightView &w, uint8_t *records, bool to_rows, h
 // The prefill GEMM (gemm.hip): whether the operand strides fit its 32-bit
 // per-tile offsets, and its launcher.
 bool gemm_supported(const WeightView &w, const ActView &x);
+// How the GEMM splits K: `splits` ranges of `split_steps` K-steps (64 of K)
+// each, whose partial sums take ws_bytes of workspace (slab rows of mp = M
+// rounded up to 4 floats).  splits == 1 (no workspace) unless the tiles
+// leave compute units idle and a split fits in ws_bytes.
+struct GemmPlan {
+    int splits;
+    int split_steps;
+    int64_t mp;
+    uint64_t ws_bytes;
+};
+GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N, uint64_t ws_bytes);
+// ws (16-byte aligned, ws_bytes long, or NULL) holds the partial sums when K
+// is split; a second kernel then adds them into y.
 hipError_t launch_gemm(const WeightView &w, const ActView &x, const OutView &y,
-                       hipStream_t stream);
+                       float *ws, uint64_t ws_bytes, hipStream_t stream);
 
 }  // namespace qmm

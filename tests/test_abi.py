@@ -144,6 +144,51 @@ def test_gemm_rejects(qmm_lib, case, expect):
     assert B.call_raw("qmm_gemm", w, x, y) == expect
 
 
+def _ws_call(w, x, y, ws, nbytes):
+    import ctypes
+    return B.lib().qmm_gemm_ws(*(ctypes.byref(d) if d is not None else None for d in (w, x, y)),
+                               ctypes.c_void_p(ws), nbytes, ctypes.c_void_p(0))
+
+
+def _gemm_pair(M, K, N):
+    return _w(B.Q4_0, K=K, M=M), _x(B.BF16, K=K, N=N)
+
+
+@no_gpu
+def test_gemm_workspace_size(qmm_lib):
+    """K is split only where the launch's cost estimate says it pays (few
+    output tiles for 256 compute units, long K): into ranges that are
+    multiples of 512 of K and at least that long, at most one workgroup per
+    compute unit; the workspace is one M x N float slab per range (M rounded
+    up to 4)."""
+    import ctypes
+    size = lambda M, K, N: B.lib().qmm_gemm_workspace_size(*(ctypes.byref(d) for d in _gemm_pair(M, K, N)))
+    assert size(5632, 2048, 512) == 0             # 176 tiles: no split
+    assert size(2048, 2048, 2048) == 0            # 256 tiles
+    assert size(2048, 2048, 512) == 0             # 64 tiles, 32 steps: the partial sums cost more
+    assert size(4096, 2048, 512) == 0             # 128 tiles
+    assert size(100, 512, 5) == 0                 # 8 K-steps: too short to split
+    assert size(2048, 5632, 512) == 4 * 512 * 2048 * 4     # 64 tiles, 88 steps: 24, 24, 24, 16
+    assert size(1024, 4096, 512) == 4 * 512 * 1024 * 4     # 32 tiles, 64 steps: 4 x 16
+    assert size(256, 2048, 512) == 4 * 512 * 256 * 4       # 8 tiles, 32 steps: 4 x 8
+    assert size(300, 4160, 77) == 5 * 77 * 300 * 4         # 65 steps in ranges of 16
+    assert size(1002, 2048, 3) == 4 * 3 * 1004 * 4         # rows rounded up to 4 floats
+    assert B.lib().qmm_gemm_workspace_size(None, None) == 0
+
+
+@no_gpu
+def test_gemm_ws_rejects(qmm_lib):
+    w, x = _gemm_pair(64, 2048, 512)
+    y = _y(M=64, N=512)
+    ws_addr = BASE + (3 << 32)
+    need = 4 * 512 * 64 * 4
+    assert _ws_call(w, x, y, ws_addr + 8, need) == B.ERR_LAYOUT      # misaligned workspace
+    assert _ws_call(w, x, y, Y_ADDR - 4096, need) == B.ERR_ALIAS     # runs into y
+    assert _ws_call(w, x, y, W_ADDR, need) == B.ERR_ALIAS            # w's rows
+    assert _ws_call(w, _x(B.F32, N=512), y, ws_addr, need) == B.ERR_TYPE   # operand checks first
+    assert _ws_call(None, x, y, ws_addr, need) == B.ERR_NULL
+
+
 @no_gpu
 def test_quantize_and_dequantize_reject(qmm_lib):
     src = B.make_desc(B.F32, 2048, 64, 8192, X_ADDR)

@@ -504,13 +504,17 @@ def test_gemm_parity(orc, case):
     packed, xbits, wt = _gemm_inputs(orc, tname, M, K, N, seed=M + K + N)
     yref, a = orc.mul_mat(TYPES[tname][1], packed, K, xbits, x_bf16_bits=True)
     ydiag, _ = orc.mul_mat(TYPES[tname][1], packed, K, xbits, x_bf16_bits=True, w_to_bf16=True)
-    buf, yv = _guarded_out(N, M)
-    Q.gemm(wt, WL.bf16_bits_to_torch(xbits, DEV), out=yv)
-    torch.cuda.synchronize()
-    _check_guard(buf)
-    y = yv.cpu().numpy()
-    _assert_tol(y, yref, a, 1e-2, 1e-5, f"gemm {case}")
-    _assert_tol(y, ydiag, a, 1.1 * K * 2.0 ** -24, 1e-7, f"gemm bf16-weight diagnostic {case}")
+    xt = WL.bf16_bits_to_torch(xbits, DEV)
+    # with the split-K workspace the shapes call for (most of these shapes
+    # leave compute units idle, so K is split), and without one
+    for ws in ("auto", None):
+        buf, yv = _guarded_out(N, M)
+        Q.gemm(wt, xt, out=yv, workspace=ws)
+        torch.cuda.synchronize()
+        _check_guard(buf)
+        y = yv.cpu().numpy()
+        _assert_tol(y, yref, a, 1e-2, 1e-5, f"gemm {case} workspace={ws}")
+        _assert_tol(y, ydiag, a, 1.1 * K * 2.0 ** -24, 1e-7, f"gemm bf16-weight diagnostic {case} workspace={ws}")
 
 
 @pytest.mark.parametrize("tname", ["Q4_0", "Q8_0", "F16"])
@@ -566,18 +570,79 @@ def test_gemm_prefill_full_size_sampled(orc):
     _assert_tol(y[ns, ms], ydiag, a, 1.1 * K * 2.0 ** -24, 1e-7, "prefill sampled diagnostic")
 
 
+def test_gemm_split_k_full_size_sampled(orc):
+    """The 2048 x 5632 down projection times 512 bf16 tokens: 64 output
+    tiles, so K is split over four workspace slabs and the slabs added by the
+    second kernel; checked on 4096 sampled outputs plus every output of the
+    first and last 128 x 128 tiles."""
+    M, K, N = WL.HIDDEN, WL.FFN, 512
+    _banner("gemm split-K 2048x5632x512")
+    w = WL.weights(WL.seed(5, 2), M, K)
+    xbits = WL.round_bf16_bits(WL.activations(WL.seed(5, 3), N, K))
+    packed = orc.quantize(orc.Q4_0, w)
+    wt = B.Weight(torch.from_numpy(packed).to(DEV), B.Q4_0, K, M)
+    xt = WL.bf16_bits_to_torch(xbits, DEV)
+    assert Q.gemm_workspace_size(wt, xt) == 4 * N * M * 4
+    y = Q.gemm(wt, xt).cpu().numpy()
+    rng = np.random.default_rng(98)
+    ms = list(rng.integers(0, M, 4096))
+    ns = list(rng.integers(0, N, 4096))
+    for m0, n0 in ((0, 0), (M - 128, N - 128)):
+        mm, nn = np.meshgrid(np.arange(m0, m0 + 128), np.arange(n0, n0 + 128))
+        ms += list(mm.ravel())
+        ns += list(nn.ravel())
+    ms, ns = np.array(ms), np.array(ns)
+    yref, a = orc.mul_mat_pairs(orc.Q4_0, packed, K, xbits, ms, ns, x_bf16_bits=True)
+    _assert_tol(y[ns, ms], yref, a, 1e-2, 1e-5, "split-K sampled")
+
+
+def test_gemm_split_k_workspace_sizes(orc):
+    """A workspace smaller than planned gives a smaller split (here two K
+    ranges instead of four), a misaligned one is refused, and each split is
+    deterministic: the same workspace size always gives the same bits."""
+    M, K, N = 300, 4096, 100          # 3 tiles, 64 K-steps
+    _banner("gemm split-K workspace sizes")
+    packed, xbits, wt = _gemm_inputs(orc, "Q8_0", M, K, N, seed=23)
+    yref, a = orc.mul_mat(orc.Q8_0, packed, K, xbits, x_bf16_bits=True)
+    xt = WL.bf16_bits_to_torch(xbits, DEV)
+    full = Q.gemm_workspace_size(wt, xt)
+    slab = N * 300 * 4
+    assert full == 8 * slab
+    outs = {}
+    for nbytes in (full, 4 * slab, 2 * slab + 16, slab, 0):
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=DEV)[:nbytes]
+        y1 = Q.gemm(wt, xt, workspace=ws).cpu().numpy()
+        y2 = Q.gemm(wt, xt, workspace=ws).cpu().numpy()
+        assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), nbytes
+        _assert_tol(y1, yref, a, 1e-2, 1e-5, f"split-K workspace {nbytes} B")
+        outs[nbytes] = y1
+    # a workspace of one slab cannot hold a split: the same bits as no workspace
+    assert np.array_equal(outs[slab].view(np.uint32), outs[0].view(np.uint32))
+    bad = torch.empty(full + 64, dtype=torch.uint8, device=DEV)[4:4 + full]
+    with pytest.raises(Q.QmmError) as e:
+        Q.gemm(wt, xt, workspace=bad)
+    assert e.value.status == B.ERR_LAYOUT
+    big = torch.empty(full + slab, dtype=torch.uint8, device=DEV)
+    yv = big[:slab].view(torch.float32).view(N, M)
+    with pytest.raises(Q.QmmError) as e:     # the workspace overlaps y
+        Q.gemm(wt, xt, out=yv, workspace=big)
+    assert e.value.status == B.ERR_ALIAS
+
+
 def test_gemm_deterministic_and_token_columns(orc):
-    """Repeat calls are bitwise identical; each token column equals the GEMM
-    of that token alone (the kernel has no cross-token reduction)."""
+    """Repeat calls are bitwise identical (with K split, each call with its
+    own workspace, and without); without a split each token column equals
+    the GEMM of that token alone (the kernel has no cross-token reduction)."""
     M, K, N = 700, 2048, 200
     _banner("gemm determinism")
     packed, xbits, wt = _gemm_inputs(orc, "Q4_0", M, K, N, seed=21)
     xt = WL.bf16_bits_to_torch(xbits, DEV)
-    y1 = Q.gemm(wt, xt).cpu().numpy()
-    y2 = Q.gemm(wt, xt).cpu().numpy()
-    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    for ws in ("auto", None):
+        y1 = Q.gemm(wt, xt, workspace=ws).cpu().numpy()
+        y2 = Q.gemm(wt, xt, workspace=ws).cpu().numpy()
+        assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32)), ws
     for n in (0, 129, 199):
-        yn = Q.gemm(wt, xt[n:n + 1]).cpu().numpy()
+        yn = Q.gemm(wt, xt[n:n + 1], workspace=None).cpu().numpy()
         assert np.array_equal(yn[0].view(np.uint32), y1[n].view(np.uint32))
 
 
