@@ -392,6 +392,36 @@ def prefill_leg(Q, WL, dev, args):
         log(f"prefill {name} {Ms}x{Ks}x{N}: split {row['split']['us']:.1f} us, unsplit {row['unsplit']['us']:.1f} us")
         shapes[f"{name}_{Ms}x{Ks}x{N}"] = row
         del ws_w, ws_x, ws_y, buf
+    # one decoder layer's seven projections at 512 tokens: one launch each
+    # (K split where it pays), against [Wq Wk Wv] and [Wgate Wup] as one
+    # batched launch each (Wo and Wdown alone)
+    lw = {name: Q.quantize(WL.weights_device(WL.seed(5, 6 + t), Ml, Kl, dev), Q.Q4_0)
+          for t, (name, Ml, Kl, _) in enumerate(WL.LAYER)}
+    lx = {Kl: WL.activations_device(WL.seed(5, 20 + Kl), N, Kl, dev).to(torch.bfloat16)
+          for Kl in {Kl for _, _, Kl, _ in WL.LAYER}}
+    ly = {name: torch.empty((N, Ml), device=dev) for name, Ml, _, _ in WL.LAYER}
+    lws = {name: torch.empty(max(1, Q.gemm_workspace_size(lw[name], lx[Kl])), dtype=torch.uint8, device=dev)
+           [:Q.gemm_workspace_size(lw[name], lx[Kl])] for name, _, Kl, _ in WL.LAYER}
+
+    def layer_separate():
+        for name, _, Kl, _ in WL.LAYER:
+            Q.gemm(lw[name], lx[Kl], out=ly[name], workspace=lws[name])
+
+    def layer_batched():
+        Q.gemm_batch([(lw[n], lx[WL.HIDDEN], ly[n]) for n in ("wq", "wk", "wv")])
+        Q.gemm(lw["wo"], lx[WL.HIDDEN], out=ly["wo"], workspace=lws["wo"])
+        Q.gemm_batch([(lw[n], lx[WL.HIDDEN], ly[n]) for n in ("wgate", "wup")])
+        Q.gemm(lw["wdown"], lx[WL.FFN], out=ly["wdown"], workspace=lws["wdown"])
+
+    layer_flops = sum(2.0 * Ml * Kl * N for _, Ml, Kl, _ in WL.LAYER)
+    layer = {"flops": layer_flops}
+    for mode, fn in (("separate", layer_separate), ("batched", layer_batched)):
+        gl = Graph(lambda: [fn() for _ in range(reps)])
+        ms_l, _ = timed(gl, max(2, args.steps // 2), 2)
+        us = ms_l / reps * 1e3
+        layer[mode] = {"us": round(us, 2), "tflops": round(layer_flops / (us * 1e-6) / 1e12, 1)}
+        log(f"prefill layer (7 projections, 512 tokens) {mode}: {us:.1f} us  {layer[mode]['tflops']:.0f} TFLOP/s")
+    del lw, lx, ly, lws
     return {"workload": "Q4_0 5632 x 2048 x bf16 2048 x 512 -> f32", "us": round(per * 1e3, 2),
             "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
             "avg_launch_us": round(kern * 1e3, 2), "flops": flops,
@@ -399,7 +429,8 @@ def prefill_leg(Q, WL, dev, args):
                             "frac_of_bf16_peak": round(tf_f / BF16_PEAK_TFLOPS, 4)},
             "q4_b64_weights": {"us": round(ms_b / reps * 1e3, 2), "tflops": round(tf_b, 1),
                                "frac_of_bf16_peak": round(tf_b / BF16_PEAK_TFLOPS, 4)},
-            "split_k_shapes": shapes}
+            "split_k_shapes": shapes,
+            "layer_512_tokens": layer}
 
 
 def breakdown_leg(Q, WL, dev, args, gemv_bytes):

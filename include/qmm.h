@@ -256,6 +256,29 @@ QMM_API size_t qmm_gemm_workspace_size(const qmm_tensor *w, const qmm_tensor *x_
 QMM_API int qmm_gemm_ws(const qmm_tensor *w, const qmm_tensor *x_bf16, qmm_tensor *y_f32, void *workspace,
                         size_t workspace_bytes, void *stream);
 
+/* Most products one qmm_gemm_batch call takes. */
+#define QMM_GEMM_BATCH_MAX 8
+
+/* One product of a GEMM batch: the operands of a qmm_gemm call. */
+typedef struct qmm_gemm_item {
+    const qmm_tensor *w;
+    const qmm_tensor *x_bf16;
+    qmm_tensor *y_f32;
+} qmm_gemm_item;
+
+/* Several independent prefill GEMMs in one launch (the query, key and value
+ * projections of a decoder layer multiply the same tokens: "Development
+ * Guide for Small AI Models (TinyLLaMA, etc.) Using C++", §4; so do the gate
+ * and up projections of its feed-forward block, §4.4).  Each item follows
+ * the rules of qmm_gemm; all items must share the weight type, K and N
+ * (else QMM_ERR_TYPE / QMM_ERR_SHAPE), and no output may overlap any operand
+ * of any item (QMM_ERR_ALIAS).  1 <= count <= QMM_GEMM_BATCH_MAX (else
+ * QMM_ERR_SHAPE).  The items' 128 x 128 output tiles form one grid, so
+ * small matrices that would leave most compute units idle on their own
+ * share a launch; each output equals, bit for bit, that of qmm_gemm on the
+ * same item (K is never split in a batch). */
+QMM_API int qmm_gemm_batch(const qmm_gemm_item *items, int32_t count, void *stream);
+
 /* GGUF-style block records ("Development Guide for Small AI Models (TinyLLaMA,
  * etc.) Using C++", §3.2: a GGUF file's tensor data is an aligned array;
  * §6.1: a Q4_0 block is one FP16 scale (2 bytes) followed by 32 4-bit

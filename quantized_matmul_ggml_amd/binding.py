@@ -27,7 +27,7 @@ OK, ERR_NULL, ERR_TYPE, ERR_SHAPE, ERR_LAYOUT, ERR_ALIAS, ERR_UNSUPPORTED, ERR_D
     0, -1, -2, -3, -4, -5, -6, -7
 
 EXPORTS = ("qmm_row_size", "qmm_quantize", "qmm_quantize_rule", "qmm_dequantize", "qmm_gemv", "qmm_gemv_batch",
-           "qmm_gemv_swiglu", "qmm_gemm", "qmm_gemm_ws", "qmm_gemm_workspace_size", "qmm_record_size", "qmm_records_to_rows",
+           "qmm_gemv_swiglu", "qmm_gemm", "qmm_gemm_ws", "qmm_gemm_workspace_size", "qmm_gemm_batch", "qmm_record_size", "qmm_records_to_rows",
            "qmm_rows_to_records", "qmm_strerror")
 GEMV_BATCH_MAX = 8
 
@@ -42,6 +42,12 @@ class QmmTensor(ctypes.Structure):
 class QmmGemvItem(ctypes.Structure):
     """Mirror of ``qmm_gemv_item``."""
     _fields_ = [("w", ctypes.POINTER(QmmTensor)), ("x_f32", ctypes.POINTER(QmmTensor)),
+                ("y_f32", ctypes.POINTER(QmmTensor))]
+
+
+class QmmGemmItem(ctypes.Structure):
+    """Mirror of ``qmm_gemm_item``."""
+    _fields_ = [("w", ctypes.POINTER(QmmTensor)), ("x_bf16", ctypes.POINTER(QmmTensor)),
                 ("y_f32", ctypes.POINTER(QmmTensor))]
 
 
@@ -76,6 +82,8 @@ def lib() -> ctypes.CDLL:
         h.qmm_gemm_ws.restype = ctypes.c_int
         h.qmm_gemm_workspace_size.argtypes = [P, P]
         h.qmm_gemm_workspace_size.restype = ctypes.c_size_t
+        h.qmm_gemm_batch.argtypes = [ctypes.POINTER(QmmGemmItem), ctypes.c_int32, ctypes.c_void_p]
+        h.qmm_gemm_batch.restype = ctypes.c_int
         h.qmm_gemv_swiglu.argtypes = [P, P, P, P, ctypes.c_void_p]
         h.qmm_gemv_swiglu.restype = ctypes.c_int
         h.qmm_record_size.argtypes = [ctypes.c_int32]
@@ -318,6 +326,23 @@ def gemm(w: Weight, x: torch.Tensor, *, out: torch.Tensor | None = None, workspa
                                  workspace.numel() * workspace.element_size(), _stream(stream)),
                "qmm_gemm_ws")
     return out
+
+
+def gemm_batch(items, *, stream=None) -> list:
+    """Several prefill GEMMs in one launch: items = [(Weight, x (N, K) bf16, out or None), ...]
+    sharing the weight type, K and N.  Returns the outputs."""
+    descs, keep, outs = [], [], []
+    for w, x, out in items:
+        _need_gpu(w.data, x)
+        if out is None:
+            out = torch.empty((x.shape[0], w.M), dtype=torch.float32, device=x.device)
+        wd, xd, yd = w.desc(), _dense_desc(x, BF16), _dense_desc(out, F32)
+        keep += [wd, xd, yd]
+        descs.append(QmmGemmItem(ctypes.pointer(wd), ctypes.pointer(xd), ctypes.pointer(yd)))
+        outs.append(out)
+    arr = (QmmGemmItem * max(1, len(descs)))(*descs)
+    _check(lib().qmm_gemm_batch(arr, len(descs), _stream(stream)), "qmm_gemm_batch")
+    return outs
 
 
 def call_batch_raw(triples, count=None, stream: int = 0) -> int:

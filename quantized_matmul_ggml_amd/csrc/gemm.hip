@@ -54,22 +54,32 @@ constexpr int W_PAIRS = 4;                // pairs of K-steps of weight codes in
 static_assert(2 * W_PAIRS == SCALE_GROUP_STEPS, "the producer loop unrolls over both with one index");
 constexpr int F16_PAIRS = 2;              // pairs of K-steps of F16 weights in flight (4x the bytes of Q4_0)
 constexpr int THREADS = 512;
+constexpr int kMaxGemmItems = QMM_GEMM_BATCH_MAX;
 
-struct GemmArgs {
+// One product of a launch (several share one launch in a batch): its
+// weights, tokens and output, and the first tile index it owns.
+struct GemmItem {
     const uint8_t *w;
     uint64_t pitch;
     int64_t M;
-    int64_t K;
-    int64_t qoff;
     const uint16_t *x;      // bf16 bits, row n at x + n * x_pitch
     uint64_t x_pitch;
-    int64_t N;
     float *y;               // the output, or the first partial-sum slab
     uint64_t y_pitch;
-    int n_tiles;
+    int tile_begin;
+    int pad;
+};
+
+struct GemmArgs {
+    int64_t K;              // shared by the items, like the type, N and qoff
+    int64_t qoff;
+    int64_t N;
+    int n_tiles;            // token tiles
     int n_splits;           // K ranges per tile (1: the whole K)
     int split_steps;        // K-steps per range, a multiple of SCALE_GROUP_STEPS
+    int n_items;
     uint64_t split_stride;  // floats between the slabs of consecutive ranges
+    GemmItem item[kMaxGemmItems];
 };
 
 // Round two floats to bf16 (nearest even) in one v_cvt_pk_bf16_f32.
@@ -182,7 +192,19 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
     // s0 .. s0 + steps - 1 of K.  Every offset below is relative to s0, and
     // nblk counts the 32-blocks of K from block 2 s0 on.
     const int split = __builtin_amdgcn_readfirstlane((int)blockIdx.x % a.n_splits);
-    const int tile = __builtin_amdgcn_readfirstlane((int)blockIdx.x / a.n_splits);
+    const int btile = __builtin_amdgcn_readfirstlane((int)blockIdx.x / a.n_splits);
+    // the item owning the tile: the last whose first tile is not past it
+    int item = 0;
+    for (int i = 1; i < a.n_items; ++i)
+        if (btile >= a.item[i].tile_begin) item = i;
+    const GemmItem &itm = a.item[item];
+    const uint8_t *const Wp = itm.w;
+    const uint64_t pitch = itm.pitch;
+    const int64_t M = itm.M;
+    const uint16_t *const Xp = itm.x;
+    const uint64_t x_pitch = itm.x_pitch;
+    const uint64_t y_pitch = itm.y_pitch;
+    const int tile = btile - itm.tile_begin;
     const int mt = __builtin_amdgcn_readfirstlane(tile / a.n_tiles);
     const int nt = __builtin_amdgcn_readfirstlane(tile - mt * a.n_tiles);
     const int64_t m0 = (int64_t)mt * BM;
@@ -191,7 +213,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
     const int64_t nblk = a.K / 32 - 2 * (int64_t)s0;
     const int all_steps = (int)((a.K + BK - 1) / BK);
     const int steps = all_steps - s0 < a.split_steps ? all_steps - s0 : a.split_steps;
-    float *const out = a.y + (uint64_t)split * a.split_stride;
+    float *const out = itm.y + (uint64_t)split * a.split_stride;
 
     // Step p of K sits in LDS stage p % STAGES and is complete at barrier p.
     // It is written between barriers p-2 and p-1 (weights by the producers,
@@ -218,13 +240,13 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
         // contiguous bytes of each of 16 rows.  Each lane serves two rows.
         const int pw = wave - 4;
         const int q4 = lane & 3;
-        const int64_t rows = a.M - m0 < BM ? a.M - m0 : BM;
+        const int64_t rows = M - m0 < BM ? M - m0 : BM;
         const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(a.w + (uint64_t)m0 * a.pitch), 0,
-            (int)(uint32_t)((rows - 1) * a.pitch + 2 * a.K), BUFFER_FLAGS);
+            (void *)(Wp + (uint64_t)m0 * pitch), 0,
+            (int)(uint32_t)((rows - 1) * pitch + 2 * a.K), BUFFER_FLAGS);
         const int wrow0 = 32 * pw + 2 * (lane >> 2);
-        const uint32_t roff[2] = {(uint32_t)(wrow0 * a.pitch) + 16 * q4 + 128u * s0,
-                                  (uint32_t)((wrow0 + 1) * a.pitch) + 16 * q4 + 128u * s0};
+        const uint32_t roff[2] = {(uint32_t)(wrow0 * pitch) + 16 * q4 + 128u * s0,
+                                  (uint32_t)((wrow0 + 1) * pitch) + 16 * q4 + 128u * s0};
         uint16_t *fdst0 = lds + wrow0 * LDS_STRIDE + 8 * q4;
         struct FPair { u32x4 q[2][4]; };   // [row wrow0 + i][block v of the pair]
         FPair fr[F16_PAIRS];
@@ -281,11 +303,11 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
         //    lane that needs each one with a quad broadcast.
         const int pw = wave - 4;
         const int q4 = lane & 3;
-        const int64_t rows = a.M - m0 < BM ? a.M - m0 : BM;
+        const int64_t rows = M - m0 < BM ? M - m0 : BM;
         const uint32_t row_bytes = (uint32_t)(a.qoff + (WT == W_Q4_0 ? a.K / 2 : a.K));
         const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(a.w + (uint64_t)m0 * a.pitch), 0,
-            (int)(uint32_t)((rows - 1) * a.pitch + row_bytes), BUFFER_FLAGS);
+            (void *)(Wp + (uint64_t)m0 * pitch), 0,
+            (int)(uint32_t)((rows - 1) * pitch + row_bytes), BUFFER_FLAGS);
 
         // code load i of a pair covers rows 32 pw + 2 m + i (m = lane / 4)
         // with chunk (q4 + 2 i) % 4 of the pair's four blocks
@@ -293,7 +315,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
         uint32_t qoff[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-            qoff[i] = (uint32_t)((wrow0 + i) * a.pitch + a.qoff) + ((q4 + 2 * i) & 3) * QB + 2u * QB * s0;
+            qoff[i] = (uint32_t)((wrow0 + i) * pitch + a.qoff) + ((q4 + 2 * i) & 3) * QB + 2u * QB * s0;
         // step s of a pair uses load i_s = (q4 / 2 == s) ? 0 : 1; within its
         // step the block is half h = q4 % 2
         const int h = q4 & 1;
@@ -303,8 +325,8 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
         constexpr uint32_t SLANE = SS ? 4 : 8;                  // scale bytes per lane and row
         // (scale bytes of a step: 4, or 2 with 64-blocks; s0 is a whole number of groups)
         const uint32_t s0b = (SS ? 2u : 4u) * s0;
-        const uint32_t soff[2] = {(uint32_t)(wrow0 * a.pitch) + SLANE * q4 + s0b,
-                                  (uint32_t)((wrow0 + 1) * a.pitch) + SLANE * q4 + s0b};
+        const uint32_t soff[2] = {(uint32_t)(wrow0 * pitch) + SLANE * q4 + s0b,
+                                  (uint32_t)((wrow0 + 1) * pitch) + SLANE * q4 + s0b};
         uint16_t *wdst0 = lds + wrow0 * LDS_STRIDE + 32 * h;
 
         struct WPair { u32x4 q[2][WBlock<WT>::QV]; };
@@ -398,11 +420,11 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
     const int q8 = lane & 7;
     const int64_t toks = a.N - n0 < BN ? a.N - n0 : BN;
     const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(a.x + (uint64_t)n0 * a.x_pitch), 0,
-        (int)(uint32_t)(((toks - 1) * a.x_pitch + a.K) * 2), BUFFER_FLAGS);
+        (void *)(Xp + (uint64_t)n0 * x_pitch), 0,
+        (int)(uint32_t)(((toks - 1) * x_pitch + a.K) * 2), BUFFER_FLAGS);
     const int xrow = 32 * c + (lane >> 3);
-    const uint32_t xoff = (uint32_t)(xrow * a.x_pitch * 2) + 16 * q8 + 128u * s0;
-    const uint32_t xrow_step = (uint32_t)(8 * a.x_pitch * 2);
+    const uint32_t xoff = (uint32_t)(xrow * x_pitch * 2) + 16 * q8 + 128u * s0;
+    const uint32_t xrow_step = (uint32_t)(8 * x_pitch * 2);
     const int64_t xlim = a.K - 8 * q8 - 64 * (int64_t)s0;   // chunk q8 of step t is in K iff 64 t < xlim
     uint16_t *xdst0 = lds + OPERAND_ELEMS + xrow * LDS_STRIDE + 8 * q8;
     struct XStep { u32x4 v[4]; };
@@ -528,11 +550,11 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int64_t m = m0 + wm * 64 + j * 32 + (lane & 31);
-            if (m >= a.M) continue;
+            if (m >= M) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t n = n0 + wn * 64 + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-                if (n < a.N) out[(uint64_t)n * a.y_pitch + m] = acc[i][j][r];
+                if (n < a.N) out[(uint64_t)n * y_pitch + m] = acc[i][j][r];
             }
         }
     }
@@ -654,50 +676,81 @@ bool gemm_supported(const WeightView &w, const ActView &x)
     return (uint64_t)BM * w.pitch < (1ull << 31) && (uint64_t)BN * x.pitch_elems * 2 < (1ull << 31);
 }
 
+namespace {
+
+// Launch the GEMM over `count` items (same type, K and N) with `plan`'s K
+// split, then the slab sum when K is split (one item only).
+hipError_t launch_items(const WeightView *w, const ActView *x, const OutView *y, int count,
+                        const GemmPlan &plan, float *ws, hipStream_t stream)
+{
+    GemmArgs a;
+    a.K = w[0].K;
+    a.qoff = quant_offset(w[0].K, w[0].scale_shift);
+    a.N = x[0].N;
+    a.n_tiles = (int)((x[0].N + BN - 1) / BN);
+    a.n_splits = plan.splits;
+    a.split_steps = plan.split_steps;
+    a.n_items = count;
+    a.split_stride = plan.splits > 1 ? (uint64_t)x[0].N * (uint64_t)plan.mp : 0;
+    int tiles = 0;
+    for (int i = 0; i < kMaxGemmItems; ++i) {
+        GemmItem &it = a.item[i];
+        const int k = i < count ? i : count - 1;      // unused slots repeat the last item
+        it.w = w[k].base;
+        it.pitch = w[k].pitch;
+        it.M = w[k].M;
+        it.x = static_cast<const uint16_t *>(x[k].data);
+        it.x_pitch = x[k].pitch_elems;
+        it.y = plan.splits > 1 ? ws : y[k].data;
+        it.y_pitch = plan.splits > 1 ? (uint64_t)plan.mp : y[k].pitch_elems;
+        it.tile_begin = i < count ? tiles : 0x7FFFFFFF;
+        it.pad = 0;
+        if (i < count) tiles += (int)((w[k].M + BM - 1) / BM) * a.n_tiles;
+    }
+    const unsigned blocks = (unsigned)tiles * (unsigned)plan.splits;
+    if (blocks == 0) return hipSuccess;
+    const WeightView &w0 = w[0];
+    hipError_t e = hipErrorInvalidValue;
+    if (w0.scale_shift) {
+        if (w0.type == W_Q4_0) e = launch_typed<W_Q4_0, 1>(a, blocks, stream);
+        else if (w0.type == W_Q8_0) e = launch_typed<W_Q8_0, 1>(a, blocks, stream);
+    } else {
+        if (w0.type == W_Q4_0) e = launch_typed<W_Q4_0, 0>(a, blocks, stream);
+        else if (w0.type == W_Q8_0) e = launch_typed<W_Q8_0, 0>(a, blocks, stream);
+        else if (w0.type == W_F16) e = launch_typed<W_F16, 0>(a, blocks, stream);
+    }
+    if (e != hipSuccess || plan.splits == 1) return e;
+    const int64_t quads = x[0].N * (plan.mp / 4);
+    const int64_t want = (quads + 255) / 256;
+    const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
+    const int vec_y = ((uintptr_t)y[0].data % 16 == 0 && y[0].pitch_elems % 4 == 0) ? 1 : 0;
+    hipLaunchKernelGGL(split_sum_kernel, dim3(grid), dim3(256), 0, stream, (const float *)ws,
+                       (uint64_t)a.split_stride, plan.splits, plan.mp, y[0].data, y[0].pitch_elems, w0.M,
+                       x[0].N, vec_y);
+    return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_gemm(const WeightView &w, const ActView &x, const OutView &y,
                        float *ws, uint64_t ws_bytes, hipStream_t stream)
 {
     if (w.M == 0 || x.N == 0) return hipSuccess;
     const GemmPlan plan = gemm_plan(w.M, w.K, x.N, ws ? ws_bytes : 0);
-    GemmArgs a;
-    a.w = w.base;
-    a.pitch = w.pitch;
-    a.M = w.M;
-    a.K = w.K;
-    a.qoff = quant_offset(w.K, w.scale_shift);
-    a.x = static_cast<const uint16_t *>(x.data);
-    a.x_pitch = x.pitch_elems;
-    a.N = x.N;
-    a.n_tiles = (int)((x.N + BN - 1) / BN);
-    a.n_splits = plan.splits;
-    a.split_steps = plan.split_steps;
-    if (plan.splits > 1) {          // partial sums into the workspace slabs
-        a.y = ws;
-        a.y_pitch = (uint64_t)plan.mp;
-        a.split_stride = (uint64_t)x.N * (uint64_t)plan.mp;
-    } else {
-        a.y = y.data;
-        a.y_pitch = y.pitch_elems;
-        a.split_stride = 0;
-    }
-    const unsigned blocks = (unsigned)((w.M + BM - 1) / BM) * (unsigned)a.n_tiles * (unsigned)plan.splits;
-    hipError_t e = hipErrorInvalidValue;
-    if (w.scale_shift) {
-        if (w.type == W_Q4_0) e = launch_typed<W_Q4_0, 1>(a, blocks, stream);
-        else if (w.type == W_Q8_0) e = launch_typed<W_Q8_0, 1>(a, blocks, stream);
-    } else {
-        if (w.type == W_Q4_0) e = launch_typed<W_Q4_0, 0>(a, blocks, stream);
-        else if (w.type == W_Q8_0) e = launch_typed<W_Q8_0, 0>(a, blocks, stream);
-        else if (w.type == W_F16) e = launch_typed<W_F16, 0>(a, blocks, stream);
-    }
-    if (e != hipSuccess || plan.splits == 1) return e;
-    const int64_t quads = x.N * (plan.mp / 4);
-    const int64_t want = (quads + 255) / 256;
-    const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
-    const int vec_y = ((uintptr_t)y.data % 16 == 0 && y.pitch_elems % 4 == 0) ? 1 : 0;
-    hipLaunchKernelGGL(split_sum_kernel, dim3(grid), dim3(256), 0, stream, (const float *)ws,
-                       (uint64_t)a.split_stride, plan.splits, plan.mp, y.data, y.pitch_elems, w.M, x.N, vec_y);
-    return hipGetLastError();
+    return launch_items(&w, &x, &y, 1, plan, ws, stream);
+}
+
+hipError_t launch_gemm_batch(const WeightView *w, const ActView *x, const OutView *y, int count,
+                             hipStream_t stream)
+{
+    if (count < 1 || count > kMaxGemmItems) return hipErrorInvalidValue;
+    if (x[0].N == 0) return hipSuccess;
+    GemmPlan plan;
+    plan.splits = 1;
+    plan.split_steps = (int)((w[0].K + BK - 1) / BK);
+    plan.mp = 0;
+    plan.ws_bytes = 0;
+    return launch_items(w, x, y, count, plan, nullptr, stream);
 }
 
 // Raise a kernel's dynamic-LDS limit once (the attribute persists for the

@@ -359,6 +359,37 @@ size_t qmm_gemm_workspace_size(const qmm_tensor *w, const qmm_tensor *x)
     return (size_t)qmm::gemm_plan(w->ne[1], w->ne[0], x->ne[1], ~0ull).ws_bytes;
 }
 
+int qmm_gemm_batch(const qmm_gemm_item *items, int32_t count, void *stream)
+{
+    if (!items) return QMM_ERR_NULL;
+    if (count < 1 || count > QMM_GEMM_BATCH_MAX) return QMM_ERR_SHAPE;
+    qmm::WeightView wv[QMM_GEMM_BATCH_MAX];
+    qmm::ActView xv[QMM_GEMM_BATCH_MAX];
+    qmm::OutView yv[QMM_GEMM_BATCH_MAX];
+    for (int i = 0; i < count; ++i) {           // every item on its own first
+        const qmm_tensor *w = items[i].w, *x = items[i].x_bf16, *y = items[i].y_f32;
+        const int rc = check_gemm(w, x, y);
+        if (rc) return rc;
+        if (i > 0) {
+            const qmm_tensor *w0 = items[0].w, *x0 = items[0].x_bf16;
+            if (w->type != w0->type) return QMM_ERR_TYPE;
+            if (w->ne[0] != w0->ne[0] || x->ne[1] != x0->ne[1]) return QMM_ERR_SHAPE;
+        }
+    }
+    for (int i = 0; i < count; ++i) {           // then outputs against every operand
+        const qmm_tensor *w = items[i].w, *x = items[i].x_bf16, *y = items[i].y_f32;
+        for (int j = 0; j < count; ++j) {
+            if (j == i) continue;
+            if (overlaps(y, items[j].w) || overlaps(y, items[j].x_bf16) || overlaps(y, items[j].y_f32))
+                return QMM_ERR_ALIAS;
+        }
+        wv[i] = weight_view(w);
+        xv[i] = qmm::ActView{x->data, pitch_elems(x), x->ne[1]};
+        yv[i] = qmm::OutView{static_cast<float *>(y->data), pitch_elems(y)};
+    }
+    return status_of(qmm::launch_gemm_batch(wv, xv, yv, count, static_cast<hipStream_t>(stream)));
+}
+
 int qmm_gemm_ws(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *workspace,
                 size_t workspace_bytes, void *stream)
 {

@@ -142,5 +142,9 @@ GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N, uint64_t ws_bytes);
 // is split; a second kernel then adds them into y.
 hipError_t launch_gemm(const WeightView &w, const ActView &x, const OutView &y,
                        float *ws, uint64_t ws_bytes, hipStream_t stream);
+// count (1 .. QMM_GEMM_BATCH_MAX) products sharing the type, K and N in one
+// launch, without a K split; items with no rows own no tiles.
+hipError_t launch_gemm_batch(const WeightView *w, const ActView *x, const OutView *y, int count,
+                             hipStream_t stream);
 
 }  // namespace qmm

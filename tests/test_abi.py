@@ -189,6 +189,33 @@ def test_gemm_ws_rejects(qmm_lib):
     assert _ws_call(None, x, y, ws_addr, need) == B.ERR_NULL
 
 
+def _gemm_batch_call(triples, count=None):
+    import ctypes
+    items = [B.QmmGemmItem(*(ctypes.pointer(d) if d is not None else None for d in t)) for t in triples]
+    arr = (B.QmmGemmItem * max(1, len(items)))(*items)
+    n = len(items) if count is None else count
+    return B.lib().qmm_gemm_batch(arr, n, ctypes.c_void_p(0))
+
+
+@no_gpu
+def test_gemm_batch_rejects(qmm_lib):
+    w0, w1 = _w(M=64), _w(M=32, addr=W_ADDR + (1 << 24))
+    x = _x(B.BF16, N=512)
+    y0, y1 = _y(M=64, N=512), _y(M=32, N=512, addr=Y_ADDR + (1 << 24))
+    assert B.lib().qmm_gemm_batch(None, 1, None) == B.ERR_NULL
+    assert _gemm_batch_call([(w0, x, y0)], count=0) == B.ERR_SHAPE
+    assert _gemm_batch_call([(w0, x, y0)] * 9) == B.ERR_SHAPE
+    assert _gemm_batch_call([(w0, x, y0), (_w(B.Q8_0, M=32, addr=W_ADDR + (1 << 24)), x, y1)]) == B.ERR_TYPE
+    wk = _w(K=1024, M=32, addr=W_ADDR + (1 << 24))
+    assert _gemm_batch_call([(w0, x, y0), (wk, _x(B.BF16, K=1024, N=512), y1)]) == B.ERR_SHAPE
+    assert _gemm_batch_call([(w0, x, y0), (w1, _x(B.BF16, N=256), _y(M=32, N=256, addr=y1.data))]) == B.ERR_SHAPE
+    assert _gemm_batch_call([(w0, x, y0), (w1, _x(B.F32, N=512), y1)]) == B.ERR_TYPE
+    # an output overlapping another item's output or weights
+    assert _gemm_batch_call([(w0, x, y0), (w1, x, _y(M=32, N=512, addr=Y_ADDR + 64))]) == B.ERR_ALIAS
+    assert _gemm_batch_call([(w0, x, y0), (w1, x, _y(M=32, N=512, addr=W_ADDR))]) == B.ERR_ALIAS
+    assert _gemm_batch_call([(w0, x, None)]) == B.ERR_NULL
+
+
 @no_gpu
 def test_quantize_and_dequantize_reject(qmm_lib):
     src = B.make_desc(B.F32, 2048, 64, 8192, X_ADDR)

@@ -646,6 +646,52 @@ def test_gemm_deterministic_and_token_columns(orc):
         assert np.array_equal(yn[0].view(np.uint32), y1[n].view(np.uint32))
 
 
+GEMM_BATCH_CASES = [
+    # (type, [M of each item], K, N): query/key/value-like shapes with an
+    # empty item; gate/up-like; a single item; the most items
+    ("Q4_0", [300, 40, 0, 40], 576, 200),
+    ("Q8_0", [130, 130], 1024, 129),
+    ("F16", [70, 33, 128], 2048 + 32, 65),
+    ("Q4_B64", [257], 640, 7),
+    ("Q8_B64", [17, 1, 130, 64, 5, 200, 2, 128], 192, 300),
+]
+
+
+@pytest.mark.parametrize("case", GEMM_BATCH_CASES, ids=lambda c: "%s-%s-k%d-n%d" % (c[0], "_".join(map(str, c[1])), c[2], c[3]))
+def test_gemm_batch_parity(orc, case):
+    """Every output of a batched launch against the oracle, and bit for bit
+    equal to qmm_gemm of the same item without a K split."""
+    tname, Ms, K, N = case
+    _banner(f"gemm batch {tname} M={Ms} K={K} N={N}")
+    xbits = WL.round_bf16_bits(WL.activations(77 + K, N, K))
+    xt = WL.bf16_bits_to_torch(xbits, DEV)
+    items, refs = [], []
+    for i, M in enumerate(Ms):
+        if M == 0:                      # an item with no rows owns no tiles
+            code = TYPES[tname][0]
+            items.append(B.Weight(torch.empty((0, B.row_size(code, K)), dtype=torch.uint8, device=DEV), code, K, 0))
+            refs.append(None)
+            continue
+        w = WL.weights(700 + 10 * i + M, M, K)
+        packed = _oracle_weight(orc, tname, w)
+        if tname == "F16":
+            wt = B.Weight(torch.from_numpy(packed.view(np.float16)).to(DEV), B.F16, K, M)
+        else:
+            wt = B.Weight(torch.from_numpy(packed).to(DEV), TYPES[tname][0], K, M)
+        items.append(wt)
+        refs.append(orc.mul_mat(TYPES[tname][1], packed, K, xbits, x_bf16_bits=True))
+    outs = Q.gemm_batch([(wt, xt, None) for wt in items])
+    torch.cuda.synchronize()
+    for i, (wt, y, ref) in enumerate(zip(items, outs, refs)):
+        assert tuple(y.shape) == (N, Ms[i])
+        if not Ms[i]:
+            continue
+        yn = y.cpu().numpy()
+        _assert_tol(yn, ref[0], ref[1], 1e-2, 1e-5, f"gemm batch {case} item {i}")
+        alone = Q.gemm(wt, xt, workspace=None).cpu().numpy()
+        assert np.array_equal(yn.view(np.uint32), alone.view(np.uint32)), f"item {i} differs from qmm_gemm"
+
+
 # ---------------------------------------------------------------- GEMV batch
 
 def test_gemv_batch_decoder_layer(orc):
