@@ -199,8 +199,10 @@ typedef struct qmm_gemv_item {
  * llama.cpp ...", §2.1: at one token per step the Q, K and V projections are
  * three GEMVs of the same input; "Development Guide ...", §4.4: so are the
  * gate and up projections of the feed-forward block).  Each item follows the
- * rules of qmm_gemv; all items must share the weight type, K and N, and no
- * output may overlap any operand of any item.  1 <= count <=
+ * rules of qmm_gemv; all items must share the weight type, K and N, and the
+ * activation type: F32 for all, or Q8_0 for all (the integer-activation
+ * path of qmm_gemv, with its accuracy; a mix is QMM_ERR_TYPE); no output
+ * may overlap any operand of any item.  1 <= count <=
  * QMM_GEMV_BATCH_MAX (else QMM_ERR_SHAPE).  Equivalent to count qmm_gemv
  * calls, without the fixed cost of count - 1 kernel launches; the workgroups
  * of the launch are shared among the items in proportion to their rows. */

@@ -235,14 +235,21 @@ def gemv(w: Weight, x, *, out: torch.Tensor | None = None, stream=None) -> torch
 
 
 def gemv_batch(items, *, stream=None) -> list:
-    """Several GEMVs in one launch: items = [(Weight, x (N, K) f32, out or None), ...]
-    sharing the weight type, K and N.  Returns the outputs."""
+    """Several GEMVs in one launch: items = [(Weight, x, out or None), ...]
+    sharing the weight type, K and N; x is fp32 (N, K) in every item, or a
+    Q8_0 Weight of N rows in every item (the integer-activation path).
+    Returns the outputs."""
     descs, keep, outs = [], [], []
     for w, x, out in items:
-        _need_gpu(w.data, x)
+        if isinstance(x, Weight):
+            _need_gpu(w.data, x.data)
+            n, dev, xd = x.M, x.data.device, x.desc()
+        else:
+            _need_gpu(w.data, x)
+            n, dev, xd = x.shape[0], x.device, _dense_desc(x, F32)
         if out is None:
-            out = torch.empty((x.shape[0], w.M), dtype=torch.float32, device=x.device)
-        wd, xd, yd = w.desc(), _dense_desc(x, F32), _dense_desc(out, F32)
+            out = torch.empty((n, w.M), dtype=torch.float32, device=dev)
+        wd, yd = w.desc(), _dense_desc(out, F32)
         keep += [wd, xd, yd]
         descs.append(QmmGemvItem(ctypes.pointer(wd), ctypes.pointer(xd), ctypes.pointer(yd)))
         outs.append(out)

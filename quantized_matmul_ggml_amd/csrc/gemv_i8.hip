@@ -27,7 +27,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxWorkgroups = 1024;
 
-struct I8Args {
+constexpr int kMaxItems = QMM_GEMV_BATCH_MAX;
+
+// One GEMV of a launch (grid y indexes the items; a batch shares the weight
+// type, K and the tokens).
+struct alignas(64) I8Item {
     const uint8_t *w;
     const uint8_t *xq;     // Q8_0 rows of the activations
     float *y;
@@ -35,15 +39,20 @@ struct I8Args {
     uint32_t x_pitch;      // bytes between activation rows
     uint32_t y_pitch;      // elements between output rows
     int32_t M;
+    int32_t n_groups;
+    int32_t wg_count;      // workgroups of this item (the rest of grid x exits)
+    int32_t iters;
+};
+
+struct I8Args {
     int32_t N;
     int32_t K;
     int32_t qoff;          // code offset inside an activation row (Q8_0, 32-blocks)
     int32_t nchunk;        // 16-byte chunks of weight codes per row
-    int32_t n_groups;
-    int32_t wg_count;
-    int32_t iters;
     int32_t wqoff;         // code offset inside a weight row (qoff for 32-blocks)
     int32_t scale_shift;   // 1: the weights have one scale per two 32-code runs
+    int32_t pad[10];
+    I8Item item[kMaxItems];
 };
 
 // Per 16-byte chunk of weight codes: Q4_0 one block (32 weights, 8 dwords of
@@ -93,12 +102,14 @@ __global__ __launch_bounds__(kThreads) void gemv_i8_kernel(const I8Args a)
     const int ks = wave % KS;
     const int v = ks * 64 + lane;
 
-    const uint8_t *const W = a.w;
-    const uint8_t *const XQ = a.xq;
-    float *const Y = a.y;
-    const uint32_t pitch = a.pitch, x_pitch = a.x_pitch, y_pitch = a.y_pitch;
-    const int M = a.M, N = a.N, K = a.K, qoff = a.qoff, nchunk = a.nchunk;
-    const int n_groups = a.n_groups, n_wg = a.wg_count, iters = a.iters;
+    const I8Item &itm = a.item[blockIdx.y];
+    const uint8_t *const W = itm.w;
+    const uint8_t *const XQ = itm.xq;
+    float *const Y = itm.y;
+    const uint32_t pitch = itm.pitch, x_pitch = itm.x_pitch, y_pitch = itm.y_pitch;
+    const int M = itm.M, n_groups = itm.n_groups, n_wg = itm.wg_count, iters = itm.iters;
+    const int N = a.N, K = a.K, qoff = a.qoff, nchunk = a.nchunk;
+    if ((int)blockIdx.x >= n_wg) return;     // a shorter item's surplus workgroups
     const int nt_real = N < NT ? N : NT;
 
     int g = (int)blockIdx.x * G + grp;
@@ -300,43 +311,70 @@ bool i8_config(int wtype, int64_t K, int64_t M, int64_t N, GemvConfig *cfg)
 
 }  // namespace
 
-hipError_t launch_gemv_i8(const WeightView &w, const WeightView &xq, const OutView &y, int64_t N,
-                          hipStream_t stream)
+hipError_t launch_gemv_i8_batch(const WeightView *w, const WeightView *xq, const OutView *y, int count,
+                                int64_t N, hipStream_t stream)
 {
-    if (w.M == 0 || N == 0) return hipSuccess;
+    if (count < 1 || count > kMaxItems) return hipErrorInvalidValue;
+    int64_t m_total = 0;
+    for (int i = 0; i < count; ++i) m_total += w[i].M;
+    if (m_total == 0 || N == 0) return hipSuccess;
+    const WeightView &w0 = w[0];
     GemvConfig c;
-    if (!i8_config(w.type, w.K, w.M, N, &c)) return hipErrorInvalidValue;
-    const I8Kernel k = (w.type == W_Q4_0) ? pick_i8_nt<W_Q4_0>(c.nt, c.ks, c.cpl, c.u)
-                                          : pick_i8_nt<W_Q8_0>(c.nt, c.ks, c.cpl, c.u);
+    if (!i8_config(w0.type, w0.K, m_total, N, &c)) return hipErrorInvalidValue;
+    const I8Kernel k = (w0.type == W_Q4_0) ? pick_i8_nt<W_Q4_0>(c.nt, c.ks, c.cpl, c.u)
+                                           : pick_i8_nt<W_Q8_0>(c.nt, c.ks, c.cpl, c.u);
     if (!k) return hipErrorInvalidValue;
     const int groups_per_wg = 4 / c.ks;
-    I8Args a;
-    a.w = w.base;
-    a.pitch = (uint32_t)w.pitch;
-    a.x_pitch = (uint32_t)xq.pitch;
-    a.y_pitch = (uint32_t)y.pitch_elems;
-    a.M = (int32_t)w.M;
-    a.K = (int32_t)w.K;
-    a.qoff = (int32_t)quant_offset(w.K);
-    a.wqoff = (int32_t)quant_offset(w.K, w.scale_shift);
-    a.scale_shift = w.scale_shift;
-    a.nchunk = (int32_t)((w.type == W_Q4_0 ? w.K / 2 : w.K) / 16);
-    a.n_groups = (int32_t)((w.M + c.u - 1) / c.u);
-    int64_t wgs = (a.n_groups + groups_per_wg - 1) / groups_per_wg;
-    if (wgs > kMaxWorkgroups) wgs = kMaxWorkgroups;
-    a.wg_count = (int32_t)wgs;
-    const int64_t per_pass = (int64_t)groups_per_wg * wgs;
-    a.iters = (int32_t)((a.n_groups + per_pass - 1) / per_pass);
+    I8Args a = {};
+    a.K = (int32_t)w0.K;
+    a.qoff = (int32_t)quant_offset(w0.K);
+    a.wqoff = (int32_t)quant_offset(w0.K, w0.scale_shift);
+    a.scale_shift = w0.scale_shift;
+    a.nchunk = (int32_t)((w0.type == W_Q4_0 ? w0.K / 2 : w0.K) / 16);
+    // the persistent grid's workgroups, shared among the items by rows
+    int64_t need[kMaxItems], need_total = 0;
+    for (int i = 0; i < count; ++i) {
+        const int64_t groups = (w[i].M + c.u - 1) / c.u;
+        need[i] = (groups + groups_per_wg - 1) / groups_per_wg;
+        need_total += need[i];
+    }
+    int64_t grid_x = 1;
+    for (int i = 0; i < count; ++i) {
+        I8Item &it = a.item[i];
+        it.w = w[i].base;
+        it.pitch = (uint32_t)w[i].pitch;
+        it.x_pitch = (uint32_t)xq[i].pitch;
+        it.y_pitch = (uint32_t)y[i].pitch_elems;
+        it.M = (int32_t)w[i].M;
+        it.n_groups = (int32_t)((w[i].M + c.u - 1) / c.u);
+        int64_t wgs = need[i];
+        if (need_total > kMaxWorkgroups) {
+            wgs = need[i] * kMaxWorkgroups / need_total;
+            if (wgs < 1 && need[i] > 0) wgs = 1;
+        }
+        it.wg_count = (int32_t)wgs;
+        const int64_t per_pass = (int64_t)groups_per_wg * (wgs > 0 ? wgs : 1);
+        it.iters = (int32_t)((it.n_groups + per_pass - 1) / per_pass);
+        if (wgs > grid_x) grid_x = wgs;
+    }
     // tokens in passes of up to NT (one pass over the weights each)
     for (int64_t n0 = 0; n0 < N; n0 += c.nt) {
-        a.xq = xq.base + (uint64_t)n0 * xq.pitch;
-        a.y = y.data + (uint64_t)n0 * y.pitch_elems;
+        for (int i = 0; i < count; ++i) {
+            a.item[i].xq = xq[i].base + (uint64_t)n0 * xq[i].pitch;
+            a.item[i].y = y[i].data + (uint64_t)n0 * y[i].pitch_elems;
+        }
         a.N = (int32_t)(N - n0 < c.nt ? N - n0 : c.nt);
-        hipLaunchKernelGGL(k, dim3((unsigned)wgs), dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL(k, dim3((unsigned)grid_x, (unsigned)count), dim3(kThreads), 0, stream, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_gemv_i8(const WeightView &w, const WeightView &xq, const OutView &y, int64_t N,
+                          hipStream_t stream)
+{
+    return launch_gemv_i8_batch(&w, &xq, &y, 1, N, stream);
 }
 
 bool gemv_i8_supported(int wtype, int64_t K, int64_t M, int64_t N)

@@ -219,12 +219,16 @@ int qmm_gemv_batch(const qmm_gemv_item *items, int32_t count, void *stream)
 {
     if (!items) return QMM_ERR_NULL;
     if (count < 1 || count > QMM_GEMV_BATCH_MAX) return QMM_ERR_SHAPE;
+    if (!items[0].x_f32) return QMM_ERR_NULL;
+    // Q8_0 activations in the first item select the integer-activation path
+    // for the whole batch ("A Complete Guide to llama.cpp ...", §2.2)
+    const bool i8 = items[0].x_f32->type == QMM_TYPE_Q8_0;
     qmm::GemvTask tasks[QMM_GEMV_BATCH_MAX];
     for (int i = 0; i < count; ++i) {           // every item on its own first
         const qmm_tensor *w = items[i].w, *x = items[i].x_f32, *y = items[i].y_f32;
-        int rc = check_mul_mat(w, x, y, QMM_TYPE_F32, 4);
+        int rc = i8 ? check_mul_mat(w, x, y, QMM_TYPE_Q8_0, 16) : check_mul_mat(w, x, y, QMM_TYPE_F32, 4);
         if (rc) return rc;
-        if (!(is_quant(w->type) || w->type == QMM_TYPE_F16)) return QMM_ERR_TYPE;
+        if (i8 ? !is_quant(w->type) : !(is_quant(w->type) || w->type == QMM_TYPE_F16)) return QMM_ERR_TYPE;
         if (x->ne[1] > 8) return QMM_ERR_SHAPE;
         if (i > 0) {
             const qmm_tensor *w0 = items[0].w, *x0 = items[0].x_f32;
@@ -242,11 +246,26 @@ int qmm_gemv_batch(const qmm_gemv_item *items, int32_t count, void *stream)
         tasks[i].w = weight_view(w);
         tasks[i].x = qmm::ActView{x->data, pitch_elems(x), x->ne[1]};
         tasks[i].y = qmm::OutView{static_cast<float *>(y->data), pitch_elems(y)};
-        if (!qmm::gemv_supported(tasks[i].w, tasks[i].x, tasks[i].y)) return QMM_ERR_UNSUPPORTED;
+        if (!i8 && !qmm::gemv_supported(tasks[i].w, tasks[i].x, tasks[i].y)) return QMM_ERR_UNSUPPORTED;
     }
     int64_t m_total = 0;
     for (int i = 0; i < count; ++i) m_total += items[i].w->ne[1];
-    if (m_total == 0 || items[0].x_f32->ne[1] == 0) return QMM_OK;
+    const int64_t N = items[0].x_f32->ne[1];
+    if (m_total == 0 || N == 0) return QMM_OK;
+    if (i8) {
+        qmm::WeightView wv[QMM_GEMV_BATCH_MAX], xv[QMM_GEMV_BATCH_MAX];
+        qmm::OutView yv[QMM_GEMV_BATCH_MAX];
+        for (int i = 0; i < count; ++i) {
+            wv[i] = tasks[i].w;
+            xv[i] = weight_view(items[i].x_f32);
+            yv[i] = tasks[i].y;
+            if (wv[i].pitch > (1ull << 28) || xv[i].pitch > (1ull << 28) || wv[i].M >= (1ll << 31) ||
+                yv[i].pitch_elems >= (1ull << 31))
+                return QMM_ERR_UNSUPPORTED;
+        }
+        if (!qmm::gemv_i8_supported(wv[0].type, items[0].w->ne[0], m_total, N)) return QMM_ERR_UNSUPPORTED;
+        return status_of(qmm::launch_gemv_i8_batch(wv, xv, yv, count, N, static_cast<hipStream_t>(stream)));
+    }
     qmm::GemvConfig cfg;
     if (!qmm::gemv_config(tasks[0].w.type, items[0].w->ne[0], m_total, 1, &cfg))
         return QMM_ERR_UNSUPPORTED;

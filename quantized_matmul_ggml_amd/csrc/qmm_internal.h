@@ -100,6 +100,10 @@ hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t strea
 bool gemv_i8_supported(int wtype, int64_t K, int64_t M, int64_t N);
 hipError_t launch_gemv_i8(const WeightView &w, const WeightView &xq, const OutView &y, int64_t N,
                           hipStream_t stream);
+// count (1 .. QMM_GEMV_BATCH_MAX) such GEMVs sharing the weight type, K and
+// N in one launch (grid y indexes the items).
+hipError_t launch_gemv_i8_batch(const WeightView *w, const WeightView *xq, const OutView *y, int count,
+                                int64_t N, hipStream_t stream);
 
 // The fused gate/up projection with the SwiGLU epilogue:
 // h[n][m] = Swish(sum_k Wg'[m][k] x[n][k]) * sum_k Wu'[m][k] x[n][k].

@@ -263,6 +263,14 @@ def test_gemv_batch_rejects(qmm_lib):
     assert B.call_batch_raw([a, g]) == B.ERR_ALIAS
     h = (b[0], _x(K=2048, addr=b[1].data), _y(M=63, addr=b[2].data))
     assert B.call_batch_raw([a, h]) == B.ERR_SHAPE
+    # Q8_0 activations: all items or none, and quantized weights only
+    xq = lambda addr: B.make_desc(B.Q8_0, 2048, 1, 2176, addr)
+    qa = (a[0], xq(X_ADDR), a[2])
+    qb = (b[0], xq(X_ADDR + (1 << 28)), b[2])
+    assert B.call_batch_raw([qa, b]) == B.ERR_TYPE
+    assert B.call_batch_raw([a, qb]) == B.ERR_TYPE
+    assert B.call_batch_raw([(B.make_desc(B.F16, 2048, 64, 4096, W_ADDR), xq(X_ADDR), a[2])]) == B.ERR_TYPE
+    assert B.call_batch_raw([qa, (b[0], B.make_desc(B.Q8_0, 2048, 1, 2176, X_ADDR + 8), b[2])]) == B.ERR_LAYOUT
 
 
 @no_gpu

@@ -842,6 +842,57 @@ def test_gemv_q8_activations(orc, case):
     assert (err <= tol).all(), f"worst err/tol {(err / tol).max():.3g}"
 
 
+I8_BATCH_CASES = [
+    # (type, [M of each item], K, N, shared x): a layer's [Wq Wk Wv] on one
+    # token; items with their own activations and an empty item; 64-blocks
+    ("Q4_0", [2048, 256, 256], 2048, 1, True),
+    ("Q8_0", [300, 0, 130, 37], 1024, 5, False),
+    ("Q4_B64", [5632, 5632], 2048, 2, True),
+    ("Q8_0", [64] * 8, 512, 8, False),
+]
+
+
+@pytest.mark.parametrize("case", I8_BATCH_CASES, ids=lambda c: "%s-%s-k%d-n%d" % (c[0], "_".join(map(str, c[1])), c[2], c[3]))
+def test_gemv_batch_q8_activations(orc, case):
+    """qmm_gemv_batch with Q8_0 activations: every item against the
+    oracle's integer path within the bound of qmm_gemv's integer path."""
+    tname, Ms, K, N, shared = case
+    _banner(f"gemv batch q8 activations {tname} M={Ms} K={K} N={N}")
+    code = TYPES[tname][0]
+    items, checks = [], []
+    xs_shared = WL.activations(900 + K, N, K)
+    for i, M in enumerate(Ms):
+        x = xs_shared if shared else WL.activations(910 + i, N, K)
+        xq_ref = orc.quantize(orc.Q8_0, x)
+        xq = Q.quantize(torch.from_numpy(x).to(DEV), B.Q8_0)
+        assert np.array_equal(xq.data.cpu().numpy(), xq_ref)
+        if M == 0:
+            wt = B.Weight(torch.empty((0, B.row_size(code, K)), dtype=torch.uint8, device=DEV), code, K, 0)
+            items.append((wt, xq, None))
+            checks.append(None)
+            continue
+        w = WL.weights(920 + 7 * i + M, M, K)
+        packed = orc.quantize(TYPES[tname][1], w)
+        items.append((B.Weight(torch.from_numpy(packed).to(DEV), code, K, M), xq, None))
+        yref, _ = orc.mul_mat_q8act(TYPES[tname][1], packed, K, xq_ref)
+        _, a_exact = orc.mul_mat(TYPES[tname][1], packed, K, orc.dequantize(orc.Q8_0, xq_ref, K))
+        checks.append((yref, a_exact))
+    outs = Q.gemv_batch(items)
+    nchunk = K // 32 if tname.startswith("Q4") else K // 16
+    for i, (y, chk) in enumerate(zip(outs, checks)):
+        assert tuple(y.shape) == (N, Ms[i])
+        if chk is None:
+            continue
+        err = np.abs(y.cpu().numpy().astype(np.float64) - chk[0])
+        tol = (nchunk + 16) * 2.0 ** -24 * chk[1] + 1e-30
+        assert (err <= tol).all(), f"item {i}: worst err/tol {(err / tol).max():.3g}"
+    # a batch mixing fp32 and Q8_0 activations is refused
+    w0 = items[0][0]
+    with pytest.raises(Q.QmmError) as e:
+        Q.gemv_batch([(w0, items[0][1], None), (w0, torch.zeros((N, K), device=DEV), None)])
+    assert e.value.status == B.ERR_TYPE
+
+
 def test_gemv_q8_activations_zero_and_strided(orc):
     """Zero activation blocks (scale 0) and padded pitches on both operands."""
     M, K, N = 90, 2048, 4
