@@ -215,7 +215,8 @@ QMM_API int qmm_gemv_batch(const qmm_gemv_item *items, int32_t count, void *stre
  *   h[n][m] = Swish(sum_k Wg'[m][k] x[n][k]) * sum_k Wu'[m][k] x[n][k].
  * w_gate, w_up: the same type (any qmm_gemv weight type) and ne = [K, M], each with
  * its own row pitch under the rules of qmm_gemv;  x: F32 ne = [K, N],
- * 1 <= N <= 8;  h: F32 ne = [M, N], overlapping none of w_gate, w_up, x
+ * 1 <= N <= 8, or Q8_0 rows (the integer-activation path of qmm_gemv, then
+ * the two sums carry that path's accuracy and the weights are quantized);  h: F32 ne = [M, N], overlapping none of w_gate, w_up, x
  * (QMM_ERR_ALIAS).  Different types: QMM_ERR_TYPE; different ne: QMM_ERR_SHAPE.
  * One launch streams both matrices once and writes h only (the two
  * projections are never stored).  The two sums carry the accuracy of

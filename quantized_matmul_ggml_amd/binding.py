@@ -258,13 +258,19 @@ def gemv_batch(items, *, stream=None) -> list:
     return outs
 
 
-def gemv_swiglu(w_gate: Weight, w_up: Weight, x: torch.Tensor, *, out: torch.Tensor | None = None,
+def gemv_swiglu(w_gate: Weight, w_up: Weight, x, *, out: torch.Tensor | None = None,
                 stream=None) -> torch.Tensor:
-    """h (N, M) fp32 = Swish(x W_gate'^T) * (x W_up'^T), one fused launch; 1 <= N <= 8."""
-    _need_gpu(w_gate.data, w_up.data, x)
+    """h (N, M) fp32 = Swish(x W_gate'^T) * (x W_up'^T), one fused launch; 1 <= N <= 8.
+    x is fp32 (N, K), or a Q8_0 Weight of N rows for the integer-activation path."""
+    if isinstance(x, Weight):
+        _need_gpu(w_gate.data, w_up.data, x.data)
+        n, dev, xd = x.M, x.data.device, x.desc()
+    else:
+        _need_gpu(w_gate.data, w_up.data, x)
+        n, dev, xd = x.shape[0], x.device, _dense_desc(x, F32)
     if out is None:
-        out = torch.empty((x.shape[0], w_gate.M), dtype=torch.float32, device=x.device)
-    gd, ud, xd, hd = w_gate.desc(), w_up.desc(), _dense_desc(x, F32), _dense_desc(out, F32)
+        out = torch.empty((n, w_gate.M), dtype=torch.float32, device=dev)
+    gd, ud, hd = w_gate.desc(), w_up.desc(), _dense_desc(out, F32)
     _check(lib().qmm_gemv_swiglu(ctypes.byref(gd), ctypes.byref(ud), ctypes.byref(xd), ctypes.byref(hd),
                                  _stream(stream)), "qmm_gemv_swiglu")
     return out

@@ -35,14 +35,17 @@ struct alignas(64) I8Item {
     const uint8_t *w;
     const uint8_t *xq;     // Q8_0 rows of the activations
     float *y;
+    const uint8_t *w2;     // fused SwiGLU launches: the up projection (w is the gate)
     uint32_t pitch;        // bytes between weight rows
     uint32_t x_pitch;      // bytes between activation rows
     uint32_t y_pitch;      // elements between output rows
+    uint32_t pitch2;
     int32_t M;
-    int32_t n_groups;
+    int32_t n_groups;      // row groups (U rows, or U/2 row indices of each matrix when fused)
     int32_t wg_count;      // workgroups of this item (the rest of grid x exits)
     int32_t iters;
 };
+static_assert(sizeof(I8Item) == 64, "one record per item");
 
 struct I8Args {
     int32_t N;
@@ -85,9 +88,22 @@ __device__ inline int chunk_idot(const uint4 q, const uint32_t *xv)
     return s;
 }
 
-template <int WT, int NT, int KS, int CPL, int U>
+// Swish(z) = z * sigma(z) = z / (1 + e^{-z}) in binary32 (for z far below
+// zero e^{-z} overflows and the quotient is the limit -0).
+__device__ inline float swish(float z)
+{
+    return z / (1.0f + expf(-z));
+}
+
+// SWIGLU: the fused gate/up projection with the SwiGLU epilogue ("Development
+// Guide for Small AI Models (TinyLLaMA, etc.) Using C++", §4.4): a group of U
+// rows holds U/2 row indices of the gate matrix (rows u < U/2) and the same
+// indices of the up matrix, and h = Swish(gate sum) * up sum is stored.
+template <int WT, int NT, int KS, int CPL, int U, bool SWIGLU>
 __global__ __launch_bounds__(kThreads) void gemv_i8_kernel(const I8Args a)
 {
+    static_assert(!SWIGLU || U % 2 == 0, "a fused group pairs gate and up rows");
+    constexpr int RU = SWIGLU ? U / 2 : U;    // row indices per group
     constexpr int XD = I8Fmt<WT>::xd;
     constexpr int G = 4 / KS;
     constexpr int VL = 64 * KS;
@@ -104,6 +120,8 @@ __global__ __launch_bounds__(kThreads) void gemv_i8_kernel(const I8Args a)
 
     const I8Item &itm = a.item[blockIdx.y];
     const uint8_t *const W = itm.w;
+    const uint8_t *const W2 = itm.w2;
+    const uint32_t pitch2 = itm.pitch2;
     const uint8_t *const XQ = itm.xq;
     float *const Y = itm.y;
     const uint32_t pitch = itm.pitch, x_pitch = itm.x_pitch, y_pitch = itm.y_pitch;
@@ -157,17 +175,23 @@ __global__ __launch_bounds__(kThreads) void gemv_i8_kernel(const I8Args a)
     }
     uint4 q[U][CPL];
     uint16_t sc[U][CPL];
+    auto group_rsrc = [&](int gi, const uint8_t *Wm, uint32_t pm) {
+        const int r0 = gi * RU;
+        const int rows = gi < n_groups ? (M - r0 < RU ? M - r0 : RU) : 0;
+        return __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(Wm + (uint64_t)(rows > 0 ? r0 : 0) * pm), 0,
+            (int)(rows > 0 ? (uint32_t)(rows - 1) * pm + row_bytes : 0u), BUFFER_FLAGS);
+    };
     auto load_group = [&](int gi) {
-        const int r0 = gi * U;
-        const int rows = gi < n_groups ? (M - r0 < U ? M - r0 : U) : 0;
-        const __amdgpu_buffer_rsrc_t res = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(W + (uint64_t)(rows > 0 ? r0 : 0) * pitch), 0,
-            (int)(rows > 0 ? (uint32_t)(rows - 1) * pitch + row_bytes : 0u), BUFFER_FLAGS);
+        const __amdgpu_buffer_rsrc_t res1 = group_rsrc(gi, W, pitch);
+        const __amdgpu_buffer_rsrc_t res2 = SWIGLU ? group_rsrc(gi, W2, pitch2) : res1;
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
-                const uint32_t ro = (uint32_t)u * pitch;
+                const bool second = SWIGLU && u >= RU;
+                const __amdgpu_buffer_rsrc_t res = second ? res2 : res1;
+                const uint32_t ro = (uint32_t)(u % RU) * (second ? pitch2 : pitch);
                 q[u][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res, qoffs[j] + ro, 0, 0));
                 sc[u][j] = __builtin_amdgcn_raw_buffer_load_b16(res, soffs[j] + ro, 0, 0);
             }
@@ -219,21 +243,38 @@ __global__ __launch_bounds__(kThreads) void gemv_i8_kernel(const I8Args a)
         const bool in_range = g < n_groups;
         const bool owner = lane >= 32 && lane < 32 + V;
         if (KS == 1) {
-            if (owner && idx < U * NT && in_range) {
-                const int u = idx / NT, n = idx % NT;
-                const int r = g * U + u;
-                if (r < M && n < N) Y[(uint64_t)n * y_pitch + r] = tot;
+            if constexpr (SWIGLU) {
+                // value idx + V/2 (the up sum of gate value idx) sits in the
+                // lane whose bit 0 differs: the top index bit is lane bit 0
+                const float up = partner<0>(tot, lane);
+                if (owner && idx < RU * NT && in_range) {
+                    const int u = idx / NT, n = idx % NT;
+                    const int r = g * RU + u;
+                    if (r < M && n < N) Y[(uint64_t)n * y_pitch + r] = swish(tot) * up;
+                }
+            } else {
+                if (owner && idx < U * NT && in_range) {
+                    const int u = idx / NT, n = idx % NT;
+                    const int r = g * U + u;
+                    if (r < M && n < N) Y[(uint64_t)n * y_pitch + r] = tot;
+                }
             }
         } else {
             float *buf = red[it & 1][wave];
             if (owner) buf[idx] = tot;
             __syncthreads();
-            if (ks == 0 && lane < U * NT && in_range) {
+            if (ks == 0 && lane < RU * NT && in_range) {
                 float s = 0.0f;
 #pragma unroll
                 for (int w2 = 0; w2 < KS; ++w2) s += red[it & 1][grp * KS + w2][lane];
+                if constexpr (SWIGLU) {
+                    float su = 0.0f;
+#pragma unroll
+                    for (int w2 = 0; w2 < KS; ++w2) su += red[it & 1][grp * KS + w2][lane + RU * NT];
+                    s = swish(s) * su;
+                }
                 const int u = lane / NT, n = lane % NT;
-                const int r = g * U + u;
+                const int r = g * RU + u;
                 if (r < M && n < N) Y[(uint64_t)n * y_pitch + r] = s;
             }
         }
@@ -246,43 +287,50 @@ template <int WT, int NT, int KS, int CPL>
 I8Kernel pick_i8_u(int u)
 {
     constexpr int UW = (CPL > 2) ? 1 : (NT <= 1) ? 4 : (NT == 2 ? 2 : 1);
-    if (u == 1) return gemv_i8_kernel<WT, NT, KS, CPL, 1>;
-    if (u == UW) return gemv_i8_kernel<WT, NT, KS, CPL, UW>;
+    if (u == 1) return gemv_i8_kernel<WT, NT, KS, CPL, 1, false>;
+    if (u == UW) return gemv_i8_kernel<WT, NT, KS, CPL, UW, false>;
     if constexpr (UW == 4)
-        if (u == 2) return gemv_i8_kernel<WT, NT, KS, CPL, 2>;
+        if (u == 2) return gemv_i8_kernel<WT, NT, KS, CPL, 2, false>;
     return nullptr;
 }
 
+// The fused SwiGLU kernels use two-row groups (one gate, one up row).
+template <int WT, int NT, int KS, int CPL>
+I8Kernel pick_i8_u_sw(int u)
+{
+    return u == 2 ? gemv_i8_kernel<WT, NT, KS, CPL, 2, true> : nullptr;
+}
+
 template <int WT, int NT, int KS>
-I8Kernel pick_i8_cpl(int cpl, int u)
+I8Kernel pick_i8_cpl(int cpl, int u, bool sw)
 {
     switch (cpl) {
-    case 1: return pick_i8_u<WT, NT, KS, 1>(u);
-    case 2: return pick_i8_u<WT, NT, KS, 2>(u);
-    case 4: return pick_i8_u<WT, NT, KS, 4>(u);
+    case 1: return sw ? pick_i8_u_sw<WT, NT, KS, 1>(u) : pick_i8_u<WT, NT, KS, 1>(u);
+    case 2: return sw ? pick_i8_u_sw<WT, NT, KS, 2>(u) : pick_i8_u<WT, NT, KS, 2>(u);
+    case 4: return sw ? pick_i8_u_sw<WT, NT, KS, 4>(u) : pick_i8_u<WT, NT, KS, 4>(u);
     default: return nullptr;
     }
 }
 
 template <int WT, int NT>
-I8Kernel pick_i8_ks(int ks, int cpl, int u)
+I8Kernel pick_i8_ks(int ks, int cpl, int u, bool sw)
 {
     switch (ks) {
-    case 1: return pick_i8_cpl<WT, NT, 1>(cpl, u);
-    case 2: return pick_i8_cpl<WT, NT, 2>(cpl, u);
-    case 4: return pick_i8_cpl<WT, NT, 4>(cpl, u);
+    case 1: return pick_i8_cpl<WT, NT, 1>(cpl, u, sw);
+    case 2: return pick_i8_cpl<WT, NT, 2>(cpl, u, sw);
+    case 4: return pick_i8_cpl<WT, NT, 4>(cpl, u, sw);
     default: return nullptr;
     }
 }
 
 template <int WT>
-I8Kernel pick_i8_nt(int nt, int ks, int cpl, int u)
+I8Kernel pick_i8_nt(int nt, int ks, int cpl, int u, bool sw = false)
 {
     switch (nt) {
-    case 1: return pick_i8_ks<WT, 1>(ks, cpl, u);
-    case 2: return pick_i8_ks<WT, 2>(ks, cpl, u);
-    case 4: return pick_i8_ks<WT, 4>(ks, cpl, u);
-    case 8: return pick_i8_ks<WT, 8>(ks, cpl, u);
+    case 1: return pick_i8_ks<WT, 1>(ks, cpl, u, sw);
+    case 2: return pick_i8_ks<WT, 2>(ks, cpl, u, sw);
+    case 4: return pick_i8_ks<WT, 4>(ks, cpl, u, sw);
+    case 8: return pick_i8_ks<WT, 8>(ks, cpl, u, sw);
     default: return nullptr;
     }
 }
@@ -311,18 +359,25 @@ bool i8_config(int wtype, int64_t K, int64_t M, int64_t N, GemvConfig *cfg)
 
 }  // namespace
 
-hipError_t launch_gemv_i8_batch(const WeightView *w, const WeightView *xq, const OutView *y, int count,
-                                int64_t N, hipStream_t stream)
+namespace {
+
+// count items (or, with w2, one fused gate/up pair: w the gate, w2 the up
+// projection) in one launch per pass of up to NT tokens.
+hipError_t launch_i8(const WeightView *w, const WeightView *w2, const WeightView *xq, const OutView *y,
+                     int count, int64_t N, hipStream_t stream)
 {
-    if (count < 1 || count > kMaxItems) return hipErrorInvalidValue;
+    if (count < 1 || count > kMaxItems || (w2 && count != 1)) return hipErrorInvalidValue;
+    const bool sw = w2 != nullptr;
     int64_t m_total = 0;
     for (int i = 0; i < count; ++i) m_total += w[i].M;
     if (m_total == 0 || N == 0) return hipSuccess;
     const WeightView &w0 = w[0];
     GemvConfig c;
-    if (!i8_config(w0.type, w0.K, m_total, N, &c)) return hipErrorInvalidValue;
-    const I8Kernel k = (w0.type == W_Q4_0) ? pick_i8_nt<W_Q4_0>(c.nt, c.ks, c.cpl, c.u)
-                                           : pick_i8_nt<W_Q8_0>(c.nt, c.ks, c.cpl, c.u);
+    if (!i8_config(w0.type, w0.K, sw ? 2 * m_total : m_total, N, &c)) return hipErrorInvalidValue;
+    if (sw) c.u = 2;                     // one gate and one up row per group
+    const int ru = sw ? 1 : c.u;         // row indices per group
+    const I8Kernel k = (w0.type == W_Q4_0) ? pick_i8_nt<W_Q4_0>(c.nt, c.ks, c.cpl, c.u, sw)
+                                           : pick_i8_nt<W_Q8_0>(c.nt, c.ks, c.cpl, c.u, sw);
     if (!k) return hipErrorInvalidValue;
     const int groups_per_wg = 4 / c.ks;
     I8Args a = {};
@@ -334,7 +389,7 @@ hipError_t launch_gemv_i8_batch(const WeightView *w, const WeightView *xq, const
     // the persistent grid's workgroups, shared among the items by rows
     int64_t need[kMaxItems], need_total = 0;
     for (int i = 0; i < count; ++i) {
-        const int64_t groups = (w[i].M + c.u - 1) / c.u;
+        const int64_t groups = (w[i].M + ru - 1) / ru;
         need[i] = (groups + groups_per_wg - 1) / groups_per_wg;
         need_total += need[i];
     }
@@ -343,10 +398,12 @@ hipError_t launch_gemv_i8_batch(const WeightView *w, const WeightView *xq, const
         I8Item &it = a.item[i];
         it.w = w[i].base;
         it.pitch = (uint32_t)w[i].pitch;
+        it.w2 = sw ? w2->base : w[i].base;
+        it.pitch2 = sw ? (uint32_t)w2->pitch : (uint32_t)w[i].pitch;
         it.x_pitch = (uint32_t)xq[i].pitch;
         it.y_pitch = (uint32_t)y[i].pitch_elems;
         it.M = (int32_t)w[i].M;
-        it.n_groups = (int32_t)((w[i].M + c.u - 1) / c.u);
+        it.n_groups = (int32_t)((w[i].M + ru - 1) / ru);
         int64_t wgs = need[i];
         if (need_total > kMaxWorkgroups) {
             wgs = need[i] * kMaxWorkgroups / need_total;
@@ -371,10 +428,33 @@ hipError_t launch_gemv_i8_batch(const WeightView *w, const WeightView *xq, const
     return hipSuccess;
 }
 
+}  // namespace
+
+hipError_t launch_gemv_i8_batch(const WeightView *w, const WeightView *xq, const OutView *y, int count,
+                                int64_t N, hipStream_t stream)
+{
+    return launch_i8(w, nullptr, xq, y, count, N, stream);
+}
+
 hipError_t launch_gemv_i8(const WeightView &w, const WeightView &xq, const OutView &y, int64_t N,
                           hipStream_t stream)
 {
-    return launch_gemv_i8_batch(&w, &xq, &y, 1, N, stream);
+    return launch_i8(&w, nullptr, &xq, &y, 1, N, stream);
+}
+
+hipError_t launch_gemv_i8_swiglu(const WeightView &wg, const WeightView &wu, const WeightView &xq,
+                                 const OutView &h, int64_t N, hipStream_t stream)
+{
+    return launch_i8(&wg, &wu, &xq, &h, 1, N, stream);
+}
+
+bool gemv_i8_swiglu_supported(int wtype, int64_t K, int64_t M, int64_t N)
+{
+    if (wtype != W_Q4_0 && wtype != W_Q8_0) return false;
+    GemvConfig c;
+    if (!i8_config(wtype, K, 2 * M, N, &c)) return false;
+    return (wtype == W_Q4_0 ? pick_i8_nt<W_Q4_0>(c.nt, c.ks, c.cpl, 2, true)
+                            : pick_i8_nt<W_Q8_0>(c.nt, c.ks, c.cpl, 2, true)) != nullptr;
 }
 
 bool gemv_i8_supported(int wtype, int64_t K, int64_t M, int64_t N)

@@ -275,6 +275,26 @@ int qmm_gemv_batch(const qmm_gemv_item *items, int32_t count, void *stream)
 int qmm_gemv_swiglu(const qmm_tensor *w_gate, const qmm_tensor *w_up, const qmm_tensor *x,
                     qmm_tensor *h, void *stream)
 {
+    if (x && x->type == QMM_TYPE_Q8_0) {
+        // the integer-activation path ("A Complete Guide to llama.cpp ...", §2.2)
+        int rc = check_mul_mat(w_gate, x, h, QMM_TYPE_Q8_0, 16);
+        if (rc) return rc;
+        rc = check_mul_mat(w_up, x, h, QMM_TYPE_Q8_0, 16);
+        if (rc) return rc;
+        if (!is_quant(w_gate->type)) return QMM_ERR_TYPE;
+        if (w_up->type != w_gate->type) return QMM_ERR_TYPE;
+        if (w_up->ne[0] != w_gate->ne[0] || w_up->ne[1] != w_gate->ne[1]) return QMM_ERR_SHAPE;
+        if (x->ne[1] > 8) return QMM_ERR_SHAPE;
+        if (x->ne[1] == 0 || w_gate->ne[1] == 0) return QMM_OK;
+        const qmm::WeightView gv = weight_view(w_gate), uv = weight_view(w_up), xv = weight_view(x);
+        qmm::OutView hv{static_cast<float *>(h->data), pitch_elems(h)};
+        if (!qmm::gemv_i8_swiglu_supported(gv.type, w_gate->ne[0], w_gate->ne[1], x->ne[1]))
+            return QMM_ERR_UNSUPPORTED;
+        if (gv.pitch > (1ull << 28) || uv.pitch > (1ull << 28) || xv.pitch > (1ull << 28) ||
+            gv.M >= (1ll << 31) || hv.pitch_elems >= (1ull << 31))
+            return QMM_ERR_UNSUPPORTED;
+        return status_of(qmm::launch_gemv_i8_swiglu(gv, uv, xv, hv, x->ne[1], static_cast<hipStream_t>(stream)));
+    }
     int rc = check_mul_mat(w_gate, x, h, QMM_TYPE_F32, 4);
     if (rc) return rc;
     rc = check_mul_mat(w_up, x, h, QMM_TYPE_F32, 4);

@@ -104,6 +104,11 @@ hipError_t launch_gemv_i8(const WeightView &w, const WeightView &xq, const OutVi
 // N in one launch (grid y indexes the items).
 hipError_t launch_gemv_i8_batch(const WeightView *w, const WeightView *xq, const OutView *y, int count,
                                 int64_t N, hipStream_t stream);
+// The fused gate/up SwiGLU projection with Q8_0 activations:
+// h[n][m] = Swish(sum of gate block terms) * sum of up block terms.
+bool gemv_i8_swiglu_supported(int wtype, int64_t K, int64_t M, int64_t N);
+hipError_t launch_gemv_i8_swiglu(const WeightView &wg, const WeightView &wu, const WeightView &xq,
+                                 const OutView &h, int64_t N, hipStream_t stream);
 
 // The fused gate/up projection with the SwiGLU epilogue:
 // h[n][m] = Swish(sum_k Wg'[m][k] x[n][k]) * sum_k Wu'[m][k] x[n][k].

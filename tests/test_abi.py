@@ -288,6 +288,14 @@ def test_gemv_swiglu_rejects(qmm_lib):
     assert call(g, u, x, _y(addr=X_ADDR)) == B.ERR_ALIAS                             # h over x
     assert call(B.make_desc(B.F32, 2048, 64, 8192, W_ADDR), u, x, h) == B.ERR_TYPE
     assert call(_w(M=0, addr=0), _w(M=0, addr=0), x, _y(M=0, addr=0)) == B.OK        # empty: no launch
+    # Q8_0 activations: quantized weights only, same rules otherwise
+    xq = B.make_desc(B.Q8_0, 2048, 1, 2176, X_ADDR)
+    f16 = lambda addr: B.make_desc(B.F16, 2048, 64, 4096, addr)
+    assert call(f16(W_ADDR), f16(U_ADDR), xq, h) == B.ERR_TYPE
+    assert call(g, B.make_desc(B.Q8_0, 2048, 64, 2176, U_ADDR), xq, h) == B.ERR_TYPE
+    assert call(g, u, B.make_desc(B.Q8_0, 2048, 9, 2176, X_ADDR), _y(N=9)) == B.ERR_SHAPE
+    assert call(g, u, B.make_desc(B.Q8_0, 2048, 1, 2176, X_ADDR + 8), h) == B.ERR_LAYOUT
+    assert call(g, u, xq, _y(addr=X_ADDR)) == B.ERR_ALIAS
 
 
 def test_record_size_closed_forms(qmm_lib):

@@ -663,10 +663,13 @@ def test_gemm_batch_parity(orc, case):
     equal to qmm_gemm of the same item without a K split."""
     tname, Ms, K, N = case
     _banner(f"gemm batch {tname} M={Ms} K={K} N={N}")
-    xbits = WL.round_bf16_bits(WL.activations(77 + K, N, K))
-    xt = WL.bf16_bits_to_torch(xbits, DEV)
-    items, refs = [], []
+    shared = tname != "Q8_0"           # the Q8_0 case gives every item its own tokens
+    xs = [WL.round_bf16_bits(WL.activations(77 + K + (0 if shared else i), N, K)) for i in range(len(Ms))]
+    items, refs, xts = [], [], []
     for i, M in enumerate(Ms):
+        xbits = xs[i]
+        xt = WL.bf16_bits_to_torch(xbits, DEV)
+        xts.append(xt)
         if M == 0:                      # an item with no rows owns no tiles
             code = TYPES[tname][0]
             items.append(B.Weight(torch.empty((0, B.row_size(code, K)), dtype=torch.uint8, device=DEV), code, K, 0))
@@ -680,9 +683,9 @@ def test_gemm_batch_parity(orc, case):
             wt = B.Weight(torch.from_numpy(packed).to(DEV), TYPES[tname][0], K, M)
         items.append(wt)
         refs.append(orc.mul_mat(TYPES[tname][1], packed, K, xbits, x_bf16_bits=True))
-    outs = Q.gemm_batch([(wt, xt, None) for wt in items])
+    outs = Q.gemm_batch([(wt, xt, None) for wt, xt in zip(items, xts)])
     torch.cuda.synchronize()
-    for i, (wt, y, ref) in enumerate(zip(items, outs, refs)):
+    for i, (wt, y, ref, xt) in enumerate(zip(items, outs, refs, xts)):
         assert tuple(y.shape) == (N, Ms[i])
         if not Ms[i]:
             continue
@@ -891,6 +894,48 @@ def test_gemv_batch_q8_activations(orc, case):
     with pytest.raises(Q.QmmError) as e:
         Q.gemv_batch([(w0, items[0][1], None), (w0, torch.zeros((N, K), device=DEV), None)])
     assert e.value.status == B.ERR_TYPE
+
+
+I8_SWIGLU_CASES = [
+    ("Q4_0", 5632, 2048, 1),       # the TinyLLaMA feed-forward gate/up pair
+    ("Q4_0", 37, 96, 3), ("Q8_0", 513, 512, 8), ("Q8_0", 64, 4096, 5), ("Q4_0", 300, 5632, 2),
+    ("Q4_B64", 300, 2048, 2), ("Q8_B64", 65, 192, 1),
+]
+
+
+@pytest.mark.parametrize("case", I8_SWIGLU_CASES, ids=lambda c: "%s-%dx%d-n%d" % c)
+def test_gemv_swiglu_q8_activations(orc, case):
+    """The fused gate/up SwiGLU with Q8_0 activations: h against Swish(g) * u
+    of the oracle's integer-path sums, within the bound of the fused GEMV
+    with each sum's bound that of the integer path."""
+    tname, M, K, N = case
+    _banner(f"gemv swiglu q8 activations {tname} M={M} K={K} N={N}")
+    seed = 5 * M + K + N
+    wg, wu = WL.weights(seed, M, K), WL.weights(seed + 1, M, K)
+    x = WL.activations(seed + 2, N, K)
+    t = TYPES[tname][1]
+    pg, pu = orc.quantize(t, wg), orc.quantize(t, wu)
+    xq_ref = orc.quantize(orc.Q8_0, x)
+    xq = Q.quantize(torch.from_numpy(x).to(DEV), B.Q8_0)
+    assert np.array_equal(xq.data.cpu().numpy(), xq_ref)
+    gref, _ = orc.mul_mat_q8act(t, pg, K, xq_ref)
+    uref, _ = orc.mul_mat_q8act(t, pu, K, xq_ref)
+    xd = orc.dequantize(orc.Q8_0, xq_ref, K)
+    _, ga = orc.mul_mat(t, pg, K, xd)
+    _, ua = orc.mul_mat(t, pu, K, xd)
+    href = orc.swiglu(gref, uref)
+    code = TYPES[tname][0]
+    h = Q.gemv_swiglu(B.Weight(torch.from_numpy(pg).to(DEV), code, K, M),
+                      B.Weight(torch.from_numpy(pu).to(DEV), code, K, M), xq)
+    h = h.cpu().numpy().astype(np.float64)
+    nchunk = K // 32 if tname.startswith("Q4") else K // 16
+    eg = (nchunk + 16) * 2.0 ** -24 * ga + 1e-30
+    eu = (nchunk + 16) * 2.0 ** -24 * ua + 1e-30
+    sg = np.array([orc.swish(v) for v in gref.ravel()]).reshape(gref.shape)
+    tol = 1.1 * eg * (np.abs(uref) + eu) + np.abs(sg) * eu + 2.0 ** -20 * np.abs(href)
+    assert np.isfinite(h).all()
+    err = np.abs(h - href)
+    assert (err <= tol).all(), f"worst err/tol {(err / tol).max():.3g}"
 
 
 def test_gemv_q8_activations_zero_and_strided(orc):
