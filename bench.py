@@ -52,6 +52,9 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip prefill/breakdown legs")
+    ap.add_argument("--gemm-probe", action="store_true",
+                    help="only launch the prefill GEMM (Q4_0 5632 x 2048 x 512) 20 times, for "
+                         "hardware-counter runs (rocprofv3 --pmc MfmaUtil MfmaFlopsBF16)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch the copy calibration kernel and the dominant GEMV, for "
                          "hardware-counter runs (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
@@ -124,6 +127,9 @@ def main():
 
     if args.traffic_probe:
         traffic_probe()
+        return
+    if args.gemm_probe:
+        gemm_probe()
         return
 
     import torch
@@ -345,6 +351,23 @@ def traffic_probe():
             Q.gemv_batch([(w, x, y) for w, y in zip(L, ys)])
     torch.cuda.synchronize()
     log(f"traffic probe done: 3 copies of {COPY_PROBE_BYTES} B, {2 * WL.LAYERS} gate/up launches")
+
+
+def gemm_probe():
+    """The prefill GEMM alone, 20 launches, for matrix-core counter runs."""
+    import torch
+    sys.path.insert(0, HERE)
+    import quantized_matmul_ggml_amd as Q
+    from quantized_matmul_ggml_amd import workloads as WL
+    dev = torch.device("cuda:0")
+    M, K, N = WL.FFN, WL.HIDDEN, 512
+    w = Q.quantize(WL.weights_device(WL.seed(5, 0), M, K, dev), Q.Q4_0)
+    x = WL.activations_device(WL.seed(5, 1), N, K, dev).to(torch.bfloat16)
+    y = torch.empty((N, M), device=dev)
+    for _ in range(20):
+        Q.gemm(w, x, out=y)
+    torch.cuda.synchronize()
+    log(f"gemm probe: 20 launches of Q4_0 {M} x {K} x bf16 {N}")
 
 
 def prefill_leg(Q, WL, dev, args):
