@@ -393,8 +393,11 @@ int qmm_gemm(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *stre
 
 size_t qmm_gemm_workspace_size(const qmm_tensor *w, const qmm_tensor *x)
 {
+    // 0 for operands qmm_gemm_ws would refuse by type or shape
     if (!w || !x) return 0;
-    if (w->n_dims < 1 || x->n_dims < 1) return 0;
+    if (check_tensor(w, 16) || check_tensor(x, 16)) return 0;
+    if (!(is_quant(w->type) || w->type == QMM_TYPE_F16) || x->type != QMM_TYPE_BF16) return 0;
+    if (w->ne[0] != x->ne[0]) return 0;
     return (size_t)qmm::gemm_plan(w->ne[1], w->ne[0], x->ne[1], ~0ull).ws_bytes;
 }
 

@@ -174,6 +174,12 @@ def test_gemm_workspace_size(qmm_lib):
     assert size(300, 4160, 77) == 5 * 77 * 300 * 4         # 65 steps in ranges of 16
     assert size(1002, 2048, 3) == 4 * 3 * 1004 * 4         # rows rounded up to 4 floats
     assert B.lib().qmm_gemm_workspace_size(None, None) == 0
+    # operands qmm_gemm_ws refuses get no size
+    w, x = _gemm_pair(2048, 5632, 512)
+    for bad_w, bad_x in ((B.make_desc(B.F32, 5632, 2048, 4 * 5632, W_ADDR), x),   # f32 weights
+                         (w, _x(B.F32, K=5632, N=512)),                            # f32 tokens
+                         (w, _x(B.BF16, K=2048, N=512))):                          # K mismatch
+        assert B.lib().qmm_gemm_workspace_size(ctypes.byref(bad_w), ctypes.byref(bad_x)) == 0
 
 
 @no_gpu
