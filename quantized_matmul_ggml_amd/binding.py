@@ -329,6 +329,10 @@ def gemm(w: Weight, x: torch.Tensor, *, out: torch.Tensor | None = None, workspa
             raise ValueError(f"workspace must be 'auto', None or a tensor, not {workspace!r}")
         n = int(lib().qmm_gemm_workspace_size(ctypes.byref(wd), ctypes.byref(xd)))
         workspace = torch.empty(n, dtype=torch.uint8, device=x.device) if n else None
+        if workspace is not None and stream is not None:
+            # freed when this call returns: keep the allocator from handing it
+            # out again before the kernels on `stream` have run
+            workspace.record_stream(stream)
     if workspace is None:
         _check(lib().qmm_gemm(ctypes.byref(wd), ctypes.byref(xd), ctypes.byref(yd), _stream(stream)),
                "qmm_gemm")
