@@ -629,6 +629,27 @@ def test_gemm_split_k_workspace_sizes(orc):
     assert e.value.status == B.ERR_ALIAS
 
 
+def test_gemm_split_k_on_a_side_stream(orc):
+    """K split with the binding's automatic workspace, enqueued on a stream
+    other than torch's current one, several times in a row: the bits equal
+    those of the same call on the current stream."""
+    M, K, N = 256, 4096, 300
+    _banner("gemm split-K on a side stream")
+    packed, xbits, wt = _gemm_inputs(orc, "Q4_0", M, K, N, seed=25)
+    xt = WL.bf16_bits_to_torch(xbits, DEV)
+    assert Q.gemm_workspace_size(wt, xt) > 0
+    ref = Q.gemm(wt, xt).cpu().numpy()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    outs = [torch.empty((N, M), device=DEV) for _ in range(4)]
+    for o in outs:
+        Q.gemm(wt, xt, out=o, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert np.array_equal(o.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
 def test_gemm_deterministic_and_token_columns(orc):
     """Repeat calls are bitwise identical (with K split, each call with its
     own workspace, and without); without a split each token column equals
