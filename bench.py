@@ -436,15 +436,24 @@ def prefill_leg(Q, WL, dev, args):
         Q.gemm_batch([(lw[n], lx[WL.HIDDEN], ly[n]) for n in ("wgate", "wup")])
         Q.gemm(lw["wdown"], lx[WL.FFN], out=ly["wdown"], workspace=lws["wdown"])
 
+    lh = torch.empty((N, WL.FFN), device=dev)
+
+    def layer_fused():          # gate/up as one fused SwiGLU launch writing h only
+        Q.gemm_batch([(lw[n], lx[WL.HIDDEN], ly[n]) for n in ("wq", "wk", "wv")])
+        Q.gemm(lw["wo"], lx[WL.HIDDEN], out=ly["wo"], workspace=lws["wo"])
+        Q.gemm_swiglu(lw["wgate"], lw["wup"], lx[WL.HIDDEN], out=lh)
+        Q.gemm(lw["wdown"], lx[WL.FFN], out=ly["wdown"], workspace=lws["wdown"])
+
     layer_flops = sum(2.0 * Ml * Kl * N for _, Ml, Kl, _ in WL.LAYER)
     layer = {"flops": layer_flops}
-    for mode, fn in (("separate", layer_separate), ("batched", layer_batched)):
+    for mode, fn in (("separate", layer_separate), ("batched", layer_batched),
+                     ("batched_swiglu_fused", layer_fused)):
         gl = Graph(lambda: [fn() for _ in range(reps)])
         ms_l, _ = timed(gl, max(2, args.steps // 2), 2)
         us = ms_l / reps * 1e3
         layer[mode] = {"us": round(us, 2), "tflops": round(layer_flops / (us * 1e-6) / 1e12, 1)}
         log(f"prefill layer (7 projections, 512 tokens) {mode}: {us:.1f} us  {layer[mode]['tflops']:.0f} TFLOP/s")
-    del lw, lx, ly, lws
+    del lw, lx, ly, lws, lh
     return {"workload": "Q4_0 5632 x 2048 x bf16 2048 x 512 -> f32", "us": round(per * 1e3, 2),
             "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
             "avg_launch_us": round(kern * 1e3, 2), "flops": flops,

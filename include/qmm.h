@@ -282,6 +282,20 @@ typedef struct qmm_gemm_item {
  * same item (K is never split in a batch). */
 QMM_API int qmm_gemm_batch(const qmm_gemm_item *items, int32_t count, void *stream);
 
+/* The fused gate/up prefill projection with its SwiGLU epilogue ("Development
+ * Guide for Small AI Models (TinyLLaMA, etc.) Using C++", §4.4: SwiGLU(x) =
+ * Swish(x W_gate) * (x W_up) elementwise, Swish(z) = z / (1 + e^{-z})):
+ *   h[n][m] = Swish(sum_k Wg'[m][k] x[n][k]) * sum_k Wu'[m][k] x[n][k].
+ * w_gate, w_up: the same type (any qmm_gemm weight type) and ne = [K, M], each
+ * under the rules of qmm_gemm with its own row pitch;  x: BF16 ne = [K, N];
+ * h: F32 ne = [M, N], overlapping none of the operands (QMM_ERR_ALIAS).
+ * Different types: QMM_ERR_TYPE; different ne: QMM_ERR_SHAPE.  One launch
+ * computes both products (each workgroup 64 rows of each matrix times 128
+ * tokens) and writes h only.  Each sum carries the accuracy of qmm_gemm; the
+ * epilogue runs in binary32 (expf, one division, two products). */
+QMM_API int qmm_gemm_swiglu(const qmm_tensor *w_gate, const qmm_tensor *w_up, const qmm_tensor *x_bf16,
+                            qmm_tensor *h_f32, void *stream);
+
 /* GGUF-style block records ("Development Guide for Small AI Models (TinyLLaMA,
  * etc.) Using C++", §3.2: a GGUF file's tensor data is an aligned array;
  * §6.1: a Q4_0 block is one FP16 scale (2 bytes) followed by 32 4-bit

@@ -27,7 +27,7 @@ OK, ERR_NULL, ERR_TYPE, ERR_SHAPE, ERR_LAYOUT, ERR_ALIAS, ERR_UNSUPPORTED, ERR_D
     0, -1, -2, -3, -4, -5, -6, -7
 
 EXPORTS = ("qmm_row_size", "qmm_quantize", "qmm_quantize_rule", "qmm_dequantize", "qmm_gemv", "qmm_gemv_batch",
-           "qmm_gemv_swiglu", "qmm_gemm", "qmm_gemm_ws", "qmm_gemm_workspace_size", "qmm_gemm_batch", "qmm_record_size", "qmm_records_to_rows",
+           "qmm_gemv_swiglu", "qmm_gemm", "qmm_gemm_ws", "qmm_gemm_workspace_size", "qmm_gemm_batch", "qmm_gemm_swiglu", "qmm_record_size", "qmm_records_to_rows",
            "qmm_rows_to_records", "qmm_strerror")
 GEMV_BATCH_MAX = 8
 
@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         h.qmm_gemm_workspace_size.restype = ctypes.c_size_t
         h.qmm_gemm_batch.argtypes = [ctypes.POINTER(QmmGemmItem), ctypes.c_int32, ctypes.c_void_p]
         h.qmm_gemm_batch.restype = ctypes.c_int
+        h.qmm_gemm_swiglu.argtypes = [P, P, P, P, ctypes.c_void_p]
+        h.qmm_gemm_swiglu.restype = ctypes.c_int
         h.qmm_gemv_swiglu.argtypes = [P, P, P, P, ctypes.c_void_p]
         h.qmm_gemv_swiglu.restype = ctypes.c_int
         h.qmm_record_size.argtypes = [ctypes.c_int32]
@@ -342,6 +344,18 @@ def gemm(w: Weight, x: torch.Tensor, *, out: torch.Tensor | None = None, workspa
                                  ctypes.c_void_p(workspace.data_ptr()),
                                  workspace.numel() * workspace.element_size(), _stream(stream)),
                "qmm_gemm_ws")
+    return out
+
+
+def gemm_swiglu(w_gate: Weight, w_up: Weight, x: torch.Tensor, *, out: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """h (N, M) fp32 = Swish(x W_gate'^T) * (x W_up'^T) for bf16 x (N, K), one fused launch."""
+    _need_gpu(w_gate.data, w_up.data, x)
+    if out is None:
+        out = torch.empty((x.shape[0], w_gate.M), dtype=torch.float32, device=x.device)
+    gd, ud, xd, hd = w_gate.desc(), w_up.desc(), _dense_desc(x, BF16), _dense_desc(out, F32)
+    _check(lib().qmm_gemm_swiglu(ctypes.byref(gd), ctypes.byref(ud), ctypes.byref(xd), ctypes.byref(hd),
+                                 _stream(stream)), "qmm_gemm_swiglu")
     return out
 
 

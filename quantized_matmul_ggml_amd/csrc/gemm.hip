@@ -66,6 +66,8 @@ struct GemmItem {
     uint64_t x_pitch;
     float *y;               // the output, or the first partial-sum slab
     uint64_t y_pitch;
+    const uint8_t *w2;      // fused SwiGLU launches: the up projection (w is the gate)
+    uint64_t pitch2;
     int tile_begin;
     int pad;
 };
@@ -187,7 +189,19 @@ __device__ inline uint32_t f16x2_to_bf16x2(uint32_t w)
     return pack_bf16(lo, hi);
 }
 
-template <int WT, int SS>
+// Swish(z) = z * sigma(z) = z / (1 + e^{-z}) in binary32 (for z far below
+// zero e^{-z} overflows and the quotient is the limit -0).
+__device__ inline float swish(float z)
+{
+    return z / (1.0f + expf(-z));
+}
+
+// SW: the fused gate/up projection with the SwiGLU epilogue ("Development
+// Guide for Small AI Models (TinyLLaMA, etc.) Using C++", §4.4): a tile is 64
+// rows of the gate matrix (tile rows 0..63) and the same 64 rows of the up
+// matrix (tile rows 64..127) times 128 tokens; the consumer waves of the two
+// halves meet in LDS after the last step, and h = Swish(gate) * up is stored.
+template <int WT, int SS, bool SW>
 __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
 {
     static_assert(SS == 0 || WT != W_F16, "64-weight blocks are quantized");
@@ -220,7 +234,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
     const int tile = btile - itm.tile_begin;
     const int mt = __builtin_amdgcn_readfirstlane(tile / a.n_tiles);
     const int nt = __builtin_amdgcn_readfirstlane(tile - mt * a.n_tiles);
-    const int64_t m0 = (int64_t)mt * BM;
+    const int64_t m0 = (int64_t)mt * (SW ? BM / 2 : BM);   // the tile's first matrix row
     const int64_t n0 = (int64_t)nt * BN;
     const int s0 = split * a.split_steps;
     const int64_t nblk = a.K / 32 - 2 * (int64_t)s0;
@@ -253,13 +267,18 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
         // contiguous bytes of each of 16 rows.  Each lane serves two rows.
         const int pw = wave - 4;
         const int q4 = lane & 3;
-        const int64_t rows = M - m0 < BM ? M - m0 : BM;
+        // fused SwiGLU: producers 2 and 3 serve the up matrix (tile rows 64..127)
+        const bool upper = SW && pw >= 2;
+        const uint8_t *const Wm = upper ? itm.w2 : Wp;
+        const uint64_t pm = upper ? itm.pitch2 : pitch;
+        const int lrow = upper ? 64 : 0;          // tile row of the matrix's row m0
+        const int64_t rows = M - m0 < (SW ? BM / 2 : BM) ? M - m0 : (SW ? BM / 2 : BM);
         const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(Wp + (uint64_t)m0 * pitch), 0,
-            (int)(uint32_t)((rows - 1) * pitch + 2 * a.K), BUFFER_FLAGS);
+            (void *)(Wm + (uint64_t)m0 * pm), 0,
+            (int)(uint32_t)((rows - 1) * pm + 2 * a.K), BUFFER_FLAGS);
         const int wrow0 = 32 * pw + 2 * (lane >> 2);
-        const uint32_t roff[2] = {(uint32_t)(wrow0 * pitch) + 16 * q4 + 128u * s0,
-                                  (uint32_t)((wrow0 + 1) * pitch) + 16 * q4 + 128u * s0};
+        const uint32_t roff[2] = {(uint32_t)((wrow0 - lrow) * pm) + 16 * q4 + 128u * s0,
+                                  (uint32_t)((wrow0 + 1 - lrow) * pm) + 16 * q4 + 128u * s0};
         uint16_t *fdst0 = lds + wrow0 * LDS_STRIDE + 8 * q4;
         struct FPair { u32x4 q[2][4]; };   // [row wrow0 + i][block v of the pair]
         FPair fr[F16_PAIRS];
@@ -303,6 +322,10 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
             });
         }
         if (steps > 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // barrier steps - 1
+        if constexpr (SW) {          // the consumers' exchange of the two halves
+            asm volatile("s_barrier" ::: "memory");
+            asm volatile("s_barrier" ::: "memory");
+        }
         return;
       }
     } else {
@@ -316,11 +339,16 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
         //    lane that needs each one with a quad broadcast.
         const int pw = wave - 4;
         const int q4 = lane & 3;
-        const int64_t rows = M - m0 < BM ? M - m0 : BM;
+        // fused SwiGLU: producers 2 and 3 serve the up matrix (tile rows 64..127)
+        const bool upper = SW && pw >= 2;
+        const uint8_t *const Wm = upper ? itm.w2 : Wp;
+        const uint64_t pm = upper ? itm.pitch2 : pitch;
+        const int lrow = upper ? 64 : 0;          // tile row of the matrix's row m0
+        const int64_t rows = M - m0 < (SW ? BM / 2 : BM) ? M - m0 : (SW ? BM / 2 : BM);
         const uint32_t row_bytes = (uint32_t)(a.qoff + (WT == W_Q4_0 ? a.K / 2 : a.K));
         const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(Wp + (uint64_t)m0 * pitch), 0,
-            (int)(uint32_t)((rows - 1) * pitch + row_bytes), BUFFER_FLAGS);
+            (void *)(Wm + (uint64_t)m0 * pm), 0,
+            (int)(uint32_t)((rows - 1) * pm + row_bytes), BUFFER_FLAGS);
 
         // code load i of a pair covers rows 32 pw + 2 m + i (m = lane / 4)
         // with chunk (q4 + 2 i) % 4 of the pair's four blocks
@@ -328,7 +356,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
         uint32_t qoff[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-            qoff[i] = (uint32_t)((wrow0 + i) * pitch + a.qoff) + ((q4 + 2 * i) & 3) * QB + 2u * QB * s0;
+            qoff[i] = (uint32_t)((wrow0 + i - lrow) * pm + a.qoff) + ((q4 + 2 * i) & 3) * QB + 2u * QB * s0;
         // step s of a pair uses load i_s = (q4 / 2 == s) ? 0 : 1; within its
         // step the block is half h = q4 % 2
         const int h = q4 & 1;
@@ -338,8 +366,8 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
         constexpr uint32_t SLANE = SS ? 4 : 8;                  // scale bytes per lane and row
         // (scale bytes of a step: 4, or 2 with 64-blocks; s0 is a whole number of groups)
         const uint32_t s0b = (SS ? 2u : 4u) * s0;
-        const uint32_t soff[2] = {(uint32_t)(wrow0 * pitch) + SLANE * q4 + s0b,
-                                  (uint32_t)((wrow0 + 1) * pitch) + SLANE * q4 + s0b};
+        const uint32_t soff[2] = {(uint32_t)((wrow0 - lrow) * pm) + SLANE * q4 + s0b,
+                                  (uint32_t)((wrow0 + 1 - lrow) * pm) + SLANE * q4 + s0b};
         uint16_t *wdst0 = lds + wrow0 * LDS_STRIDE + 32 * h;
 
         struct WPair { u32x4 q[2][WBlock<WT>::QV]; };
@@ -419,6 +447,10 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
             });
         }
         if (steps > 0) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // barrier steps - 1
+        if constexpr (SW) {          // the consumers' exchange of the two halves
+            asm volatile("s_barrier" ::: "memory");
+            asm volatile("s_barrier" ::: "memory");
+        }
         return;
       }
     }
@@ -558,6 +590,41 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
 
     // Epilogue: acc[i][j] register r holds token 8*(r/4) + 4*(lane/32) + r%4
     // of sub-tile i and weight row lane%32 of sub-tile j.
+    if constexpr (SW) {
+        // The gate-half (wm = 0) and up-half (wm = 1) consumers of the same
+        // tokens (same wn) each finish one token sub-tile: wm = 0 sub-tile
+        // 0, wm = 1 sub-tile 1.  Each hands the other the sums it needs
+        // through LDS, which no stage uses any more.
+        float *xa = reinterpret_cast<float *>(lds) + wn * (2 * 2 * 16 * 64);   // up sums of sub-tile 0
+        float *xb = xa + 2 * 16 * 64;                                          // gate sums of sub-tile 1
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // every stage read
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                if (wm == 1) xa[(j * 16 + r) * 64 + lane] = acc[0][j][r];
+                else xb[(j * 16 + r) * 64 + lane] = acc[1][j][r];
+            }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        auto finish = [&](auto I_) {
+            constexpr int i = decltype(I_)::value;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int64_t m = m0 + j * 32 + (lane & 31);
+                if (m >= M) continue;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t n = n0 + wn * 64 + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+                    const float g = i == 0 ? acc[0][j][r] : xb[(j * 16 + r) * 64 + lane];
+                    const float u = i == 0 ? xa[(j * 16 + r) * 64 + lane] : acc[1][j][r];
+                    if (n < a.N) out[(uint64_t)n * y_pitch + m] = swish(g) * u;
+                }
+            }
+        };
+        if (wm == 0) finish(std::integral_constant<int, 0>{});
+        else finish(std::integral_constant<int, 1>{});
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
@@ -575,12 +642,12 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
 
 constexpr size_t LDS_BYTES = (size_t)STAGES * STAGE_ELEMS * sizeof(uint16_t);
 
-template <int WT, int SS>
+template <int WT, int SS, bool SW = false>
 hipError_t launch_typed(const GemmArgs &a, unsigned blocks, hipStream_t stream)
 {
-    const hipError_t attr = allow_dynamic_lds(reinterpret_cast<const void *>(&gemm_kernel<WT, SS>), (int)LDS_BYTES);
+    const hipError_t attr = allow_dynamic_lds(reinterpret_cast<const void *>(&gemm_kernel<WT, SS, SW>), (int)LDS_BYTES);
     if (attr != hipSuccess) return attr;
-    hipLaunchKernelGGL((gemm_kernel<WT, SS>), dim3(blocks), dim3(THREADS), LDS_BYTES, stream, a);
+    hipLaunchKernelGGL((gemm_kernel<WT, SS, SW>), dim3(blocks), dim3(THREADS), LDS_BYTES, stream, a);
     return hipGetLastError();
 }
 
@@ -716,6 +783,8 @@ hipError_t launch_items(const WeightView *w, const ActView *x, const OutView *y,
         it.x_pitch = x[k].pitch_elems;
         it.y = plan.splits > 1 ? ws : y[k].data;
         it.y_pitch = plan.splits > 1 ? (uint64_t)plan.mp : y[k].pitch_elems;
+        it.w2 = w[k].base;
+        it.pitch2 = w[k].pitch;
         it.tile_begin = i < count ? tiles : 0x7FFFFFFF;
         it.pad = 0;
         if (i < count) tiles += (int)((w[k].M + BM - 1) / BM) * a.n_tiles;
@@ -751,6 +820,45 @@ hipError_t launch_gemm(const WeightView &w, const ActView &x, const OutView &y,
     if (w.M == 0 || x.N == 0) return hipSuccess;
     const GemmPlan plan = gemm_plan(w.M, w.K, x.N, ws ? ws_bytes : 0);
     return launch_items(&w, &x, &y, 1, plan, ws, stream);
+}
+
+hipError_t launch_gemm_swiglu(const WeightView &wg, const WeightView &wu, const ActView &x, const OutView &h,
+                              hipStream_t stream)
+{
+    if (wg.M == 0 || x.N == 0) return hipSuccess;
+    GemmArgs a;
+    a.K = wg.K;
+    a.qoff = quant_offset(wg.K, wg.scale_shift);
+    a.N = x.N;
+    a.n_tiles = (int)((x.N + BN - 1) / BN);
+    a.n_splits = 1;
+    a.split_steps = (int)((wg.K + BK - 1) / BK);
+    a.n_items = 1;
+    a.split_stride = 0;
+    for (int i = 0; i < kMaxGemmItems; ++i) {
+        GemmItem &it = a.item[i];
+        it.w = wg.base;
+        it.pitch = wg.pitch;
+        it.w2 = wu.base;
+        it.pitch2 = wu.pitch;
+        it.M = wg.M;
+        it.x = static_cast<const uint16_t *>(x.data);
+        it.x_pitch = x.pitch_elems;
+        it.y = h.data;
+        it.y_pitch = h.pitch_elems;
+        it.tile_begin = i == 0 ? 0 : 0x7FFFFFFF;
+        it.pad = 0;
+    }
+    const unsigned blocks = (unsigned)((wg.M + BM / 2 - 1) / (BM / 2)) * (unsigned)a.n_tiles;
+    if (wg.scale_shift) {
+        if (wg.type == W_Q4_0) return launch_typed<W_Q4_0, 1, true>(a, blocks, stream);
+        if (wg.type == W_Q8_0) return launch_typed<W_Q8_0, 1, true>(a, blocks, stream);
+        return hipErrorInvalidValue;
+    }
+    if (wg.type == W_Q4_0) return launch_typed<W_Q4_0, 0, true>(a, blocks, stream);
+    if (wg.type == W_Q8_0) return launch_typed<W_Q8_0, 0, true>(a, blocks, stream);
+    if (wg.type == W_F16) return launch_typed<W_F16, 0, true>(a, blocks, stream);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_batch(const WeightView *w, const ActView *x, const OutView *y, int count,

@@ -432,6 +432,22 @@ int qmm_gemm_batch(const qmm_gemm_item *items, int32_t count, void *stream)
     return status_of(qmm::launch_gemm_batch(wv, xv, yv, count, static_cast<hipStream_t>(stream)));
 }
 
+int qmm_gemm_swiglu(const qmm_tensor *w_gate, const qmm_tensor *w_up, const qmm_tensor *x, qmm_tensor *h,
+                    void *stream)
+{
+    int rc = check_gemm(w_gate, x, h);
+    if (rc) return rc;
+    rc = check_gemm(w_up, x, h);
+    if (rc) return rc;
+    if (w_up->type != w_gate->type) return QMM_ERR_TYPE;
+    if (w_up->ne[0] != w_gate->ne[0] || w_up->ne[1] != w_gate->ne[1]) return QMM_ERR_SHAPE;
+    if (w_gate->ne[1] == 0 || x->ne[1] == 0) return QMM_OK;
+    qmm::ActView xv{x->data, pitch_elems(x), x->ne[1]};
+    qmm::OutView hv{static_cast<float *>(h->data), pitch_elems(h)};
+    return status_of(qmm::launch_gemm_swiglu(weight_view(w_gate), weight_view(w_up), xv, hv,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int qmm_gemm_ws(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *workspace,
                 size_t workspace_bytes, void *stream)
 {

@@ -155,5 +155,10 @@ hipError_t launch_gemm(const WeightView &w, const ActView &x, const OutView &y,
 // launch, without a K split; items with no rows own no tiles.
 hipError_t launch_gemm_batch(const WeightView *w, const ActView *x, const OutView *y, int count,
                              hipStream_t stream);
+// The fused gate/up prefill projection with the SwiGLU epilogue:
+// h[n][m] = Swish(sum_k Wg'[m][k] x[n][k]) * sum_k Wu'[m][k] x[n][k]
+// (wg and wu share the type, K and M; K is never split).
+hipError_t launch_gemm_swiglu(const WeightView &wg, const WeightView &wu, const ActView &x, const OutView &h,
+                              hipStream_t stream);
 
 }  // namespace qmm

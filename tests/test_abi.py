@@ -223,6 +223,21 @@ def test_gemm_batch_rejects(qmm_lib):
 
 
 @no_gpu
+def test_gemm_swiglu_rejects(qmm_lib):
+    U_ADDR = BASE + (3 << 32)
+    g, u, x, h = _w(), _w(addr=U_ADDR), _x(B.BF16, N=512), _y(N=512)
+    call = lambda *d: B.call_raw("qmm_gemm_swiglu", *d)
+    assert call(None, u, x, h) == B.ERR_NULL
+    assert call(g, B.make_desc(B.Q8_0, 2048, 64, 2176, U_ADDR), x, h) == B.ERR_TYPE   # mixed types
+    assert call(g, _w(M=65, addr=U_ADDR), x, h) == B.ERR_SHAPE                       # mixed M
+    assert call(g, u, _x(B.F32, N=512), h) == B.ERR_TYPE                             # f32 tokens
+    assert call(g, u, _x(B.BF16, K=1024, N=512), h) == B.ERR_SHAPE                   # K mismatch
+    assert call(g, u, x, _y(N=512, addr=U_ADDR + 64)) == B.ERR_ALIAS                 # h over w_up
+    assert call(g, u, x, _y(N=512, addr=X_ADDR)) == B.ERR_ALIAS                      # h over x
+    assert call(_w(M=0, addr=0), _w(M=0, addr=0), x, _y(M=0, N=512, addr=0)) == B.OK
+
+
+@no_gpu
 def test_quantize_and_dequantize_reject(qmm_lib):
     src = B.make_desc(B.F32, 2048, 64, 8192, X_ADDR)
     dst = _w()

@@ -5,7 +5,8 @@ and replays them, so every kernel path it times is checked here the same
 way: one graph holds a one-token GEMV, a GEMV batch of eight tokens (the
 matrix-core kernel), the fused gate/up SwiGLU projection, an integer-
 activation GEMV, the prefill GEMM (its K split over a workspace the binding
-allocates during capture), a batched prefill GEMM and a 64-weight-block GEMV.  The graph is
+allocates during capture), a batched prefill GEMM, the fused gate/up SwiGLU
+prefill GEMM and a 64-weight-block GEMV.  The graph is
 replayed several times with new inputs written eagerly (and the device
 synchronized) between replays; every replay must equal, bit for bit, the
 same calls made eagerly on the same inputs (the kernels are deterministic).
@@ -32,6 +33,7 @@ def _calls(ops, ins, outs):
     Q.gemv(wq, ins["xq"], out=outs["yi"])
     Q.gemm(w4, ins["xb"], out=outs["Y"])
     Q.gemm_batch([(w4, ins["xb"], outs["Yb1"]), (wg, ins["xb"], outs["Yb2"])])
+    Q.gemm_swiglu(wg, wu, ins["xb"], out=outs["Hb"])
     Q.gemv(w64, ins["x3"], out=outs["y64"])
 
 
@@ -61,7 +63,7 @@ def test_graph_replays_match_eager_calls():
            "xb": torch.empty((300, K), device=DEV, dtype=torch.bfloat16),
            "xq": Q.quantize(torch.zeros((2, K), device=DEV), Q.Q8_0)}
     shapes = {"y1": (1, M), "g8": (8, MF), "u8": (8, MF), "h": (1, MF), "yi": (2, M),
-              "Y": (300, M), "y64": (3, M), "Yb1": (300, M), "Yb2": (300, MF)}
+              "Y": (300, M), "y64": (3, M), "Yb1": (300, M), "Yb2": (300, MF), "Hb": (300, MF)}
     outs = {k: torch.full(s, float("nan"), device=DEV) for k, s in shapes.items()}
     ref = {k: torch.empty(s, device=DEV) for k, s in shapes.items()}
 

@@ -629,6 +629,78 @@ def test_gemm_split_k_workspace_sizes(orc):
     assert e.value.status == B.ERR_ALIAS
 
 
+GEMM_SWIGLU_CASES = [
+    ("Q4_0", 300, 640, 130), ("Q8_0", 65, 96, 7), ("F16", 130, 2048 + 32, 65),
+    ("Q4_B64", 200, 1024, 129), ("Q8_B64", 64, 192, 300), ("Q4_0", 1, 32, 1),
+]
+
+
+def _gemm_swiglu_tol(orc, gref, ga, uref, ua, h):
+    """The fused SwiGLU bound with each sum's GEMM bound (1e-2 * a + 1e-5)
+    carried through Swish (|Swish'| <= 1.1) and the product, plus binary32
+    rounding of the epilogue."""
+    eg = 1e-2 * ga + 1e-5
+    eu = 1e-2 * ua + 1e-5
+    sg = np.array([orc.swish(v) for v in np.ravel(gref)]).reshape(np.shape(gref))
+    return 1.1 * eg * (np.abs(uref) + eu) + np.abs(sg) * eu + 2.0 ** -20 * np.abs(h)
+
+
+@pytest.mark.parametrize("case", GEMM_SWIGLU_CASES, ids=lambda c: "%s-%dx%d-n%d" % c)
+def test_gemm_swiglu_parity(orc, case):
+    """The fused gate/up prefill projection: h against Swish(g) * u of the
+    oracle's sums, every output, guard bands intact."""
+    tname, M, K, N = case
+    _banner(f"gemm swiglu {tname} M={M} K={K} N={N}")
+    seed = 3 * M + K + N
+    pg = _oracle_weight(orc, tname, WL.weights(seed, M, K))
+    pu = _oracle_weight(orc, tname, WL.weights(seed + 1, M, K))
+    xbits = WL.round_bf16_bits(WL.activations(seed + 2, N, K))
+    t = TYPES[tname][1]
+    gref, ga = orc.mul_mat(t, pg, K, xbits, x_bf16_bits=True)
+    uref, ua = orc.mul_mat(t, pu, K, xbits, x_bf16_bits=True)
+    href = orc.swiglu(gref, uref)
+
+    def wt(packed):
+        if tname == "F16":
+            return B.Weight(torch.from_numpy(packed.view(np.float16)).to(DEV), B.F16, K, M)
+        return B.Weight(torch.from_numpy(packed).to(DEV), TYPES[tname][0], K, M)
+    buf, hv = _guarded_out(N, M)
+    Q.gemm_swiglu(wt(pg), wt(pu), WL.bf16_bits_to_torch(xbits, DEV), out=hv)
+    torch.cuda.synchronize()
+    _check_guard(buf)
+    h = hv.cpu().numpy().astype(np.float64)
+    tol = _gemm_swiglu_tol(orc, gref, ga, uref, ua, href)
+    assert np.isfinite(h).all()
+    err = np.abs(h - href)
+    assert (err <= tol).all(), f"worst err/tol {(err / tol).max():.3g}"
+
+
+def test_gemm_swiglu_full_size_sampled(orc):
+    """The TinyLLaMA gate/up pair (2 x 5632 x 2048, Q4_0) times 512 bf16
+    tokens, on 2048 sampled outputs plus the first and last 64 x 128 tiles."""
+    M, K, N = WL.FFN, WL.HIDDEN, 512
+    _banner("gemm swiglu 5632x2048x512")
+    wg_, wu_ = WL.weights(WL.seed(5, 0), M, K), WL.weights(WL.seed(5, 9), M, K)
+    xbits = WL.round_bf16_bits(WL.activations(WL.seed(5, 1), N, K))
+    pg, pu = orc.quantize(orc.Q4_0, wg_), orc.quantize(orc.Q4_0, wu_)
+    h = Q.gemm_swiglu(B.Weight(torch.from_numpy(pg).to(DEV), B.Q4_0, K, M),
+                      B.Weight(torch.from_numpy(pu).to(DEV), B.Q4_0, K, M),
+                      WL.bf16_bits_to_torch(xbits, DEV)).cpu().numpy().astype(np.float64)
+    rng = np.random.default_rng(97)
+    ms, ns = list(rng.integers(0, M, 2048)), list(rng.integers(0, N, 2048))
+    for m0, n0 in ((0, 0), (M - 64, N - 128)):
+        mm, nn = np.meshgrid(np.arange(m0, m0 + 64), np.arange(n0, n0 + 128))
+        ms += list(mm.ravel())
+        ns += list(nn.ravel())
+    ms, ns = np.array(ms), np.array(ns)
+    gref, ga = orc.mul_mat_pairs(orc.Q4_0, pg, K, xbits, ms, ns, x_bf16_bits=True)
+    uref, ua = orc.mul_mat_pairs(orc.Q4_0, pu, K, xbits, ms, ns, x_bf16_bits=True)
+    href = orc.swiglu(gref, uref)
+    tol = _gemm_swiglu_tol(orc, gref, ga, uref, ua, href)
+    err = np.abs(h[ns, ms] - href)
+    assert (err <= tol).all(), f"worst err/tol {(err / tol).max():.3g}"
+
+
 def test_gemm_split_k_on_a_side_stream(orc):
     """K split with the binding's automatic workspace, enqueued on a stream
     other than torch's current one, several times in a row: the bits equal
