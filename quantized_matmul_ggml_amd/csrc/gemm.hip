@@ -24,6 +24,16 @@
 // Loads go through buffer resources based at the tile's first row and sized
 // to the bytes the operands span, so rows and tokens past the end read as
 // zero; blocks past the end of K get a zero scale and zero tokens.
+//
+// One launch serves three callers:
+//  * one product, with K optionally split into ranges (a workgroup per tile
+//    and range) whose partial sums go to a caller workspace and are added in
+//    range order by split_sum_kernel (products with too few tiles for the
+//    chip; gemm_plan decides);
+//  * a batch of up to QMM_GEMM_BATCH_MAX products sharing type, K and N,
+//    whose tiles form one grid (a workgroup finds its item by tile index);
+//  * the gate/up pair with the SwiGLU epilogue (SW): 64 rows of each matrix
+//    per tile, combined in LDS after the last step.
 #include "qmm_internal.h"
 
 #include <atomic>
