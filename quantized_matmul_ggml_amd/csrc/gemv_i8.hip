@@ -18,6 +18,9 @@
 //  * a Q4_0 nibble n enters the dot product as the int8 value n (it is below
 //    128) and the block sum is corrected by -8 * sum_i qx_i, an integer
 //    computed once per activation block.
+// Like the fp32 GEMV, a launch takes up to QMM_GEMV_BATCH_MAX items (grid y)
+// sharing the persistent grid by rows, or one gate/up pair fused with the
+// SwiGLU epilogue (one gate and one up row per group).
 #include "qmm_internal.h"
 #include "wave_reduce.h"
 
