@@ -113,6 +113,10 @@ typedef struct qmm_tensor {
 
 /* Bytes of one packed (or dense) row of ne0 elements; 0 for an unknown type
  * or an invalid ne0 (negative, or not a multiple of the block length).
+ * A row holds its blocks' contents as the Development Guide for Small AI
+ * Models (TinyLLaMA, etc.) Using C++, §6.1 lists them (one fp16 scale per
+ * block, then the block's codes), 34 bytes per 32 Q8_0 weights and 18 per
+ * 32 Q4_0 weights, with the scales first and each part 16-byte aligned.
  * Q8_0: align16(ne0/16) + align16(ne0);  Q4_0: align16(ne0/16) + align16(ne0/2);
  * Q8_B64: align16(ne0/32) + align16(ne0);  Q4_B64: align16(ne0/32) + align16(ne0/2). */
 QMM_API size_t qmm_row_size(int32_t type, int64_t ne0);
@@ -153,7 +157,9 @@ QMM_API int qmm_quantize_rule(const qmm_tensor *src_f32, qmm_tensor *dst_q, int3
 QMM_API int qmm_dequantize(const qmm_tensor *src, qmm_tensor *dst_f32, void *stream);
 
 /* Decode GEMV / skinny GEMM ("A Complete Guide to llama.cpp ...", §2.1: one
- * token per step makes every projection a GEMV).
+ * token per step makes every projection a GEMV; Development Guide §6.2: the
+ * codes are unpacked to their signed values and scaled before the
+ * multiply-add).
  * w: Q8_0, Q4_0, Q8_B64, Q4_B64 or F16, ne = [K, M];  x: F32 ne = [K, N],
  * 1 <= N <= 8
  * (N > 8: QMM_ERR_SHAPE);  y: F32 ne = [M, N], must not overlap w or x.
@@ -165,11 +171,13 @@ QMM_API int qmm_dequantize(const qmm_tensor *src, qmm_tensor *dst_f32, void *str
  * the registers (one pass over the weights per group).
  * Weights are read once from HBM and dequantized in registers; binary32
  * multiply-add; the accumulation order is unspecified (results agree with
- * the exact sum within 1e-4 * sum_k |W'[m][k] x[n][k]| + 1e-6).  From 5
- * tokens (3 when the call has at least 8192 rows), quantized weights go to
- * the bf16 matrix cores instead: codes enter exactly, x as two bfloat16
- * parts (x = hi + lo to 2^-17 relative), products accumulated in binary32,
- * within the same bound. */
+ * the exact sum within 1e-4 * sum_k |W'[m][k] x[n][k]| + 1e-6 for every
+ * output and every input: each product is a signed code times x, so the
+ * rounding error is relative to sum |W' x|, never to a larger biased sum).
+ * From 5 tokens (3 when the call has at least 8192 rows), quantized weights
+ * go to the bf16 matrix cores instead: signed codes enter exactly, x as two
+ * bfloat16 parts (x = hi + lo to 2^-17 relative), products accumulated in
+ * binary32, within the same bound. */
 /* Integer activations ("A Complete Guide to llama.cpp ...", §2.2: with x
  * quantized per block too, x_i ~= Delta_x qx_i, the block dot product is
  * Delta Delta_x sum_i q_i qx_i, an integer sum): when x is Q8_0 (ne = [K, N],
@@ -326,7 +334,10 @@ QMM_API size_t qmm_record_size(int32_t type);
 QMM_API int qmm_records_to_rows(const void *records, qmm_tensor *dst_q, void *stream);
 QMM_API int qmm_rows_to_records(const qmm_tensor *src_q, void *records, void *stream);
 
-/* Static text for a qmm_status value (never NULL). */
+/* Static text for a qmm_status value (never NULL).  Every call reports
+ * failure as a status code that the caller checks, as the calls of "A
+ * Complete Guide to llama.cpp and Customization with C++", §5.2-§5.4 do;
+ * nothing is thrown across the ABI. */
 QMM_API const char *qmm_strerror(int status);
 
 #ifdef __cplusplus

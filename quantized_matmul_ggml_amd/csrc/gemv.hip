@@ -18,11 +18,11 @@
 //    lane, fully coalesced).
 //  * The activations a lane needs for its chunks are loaded once into VGPRs
 //    and reused for every row the wave streams; only weights come from HBM.
-//  * Codes are turned into floats with byte conversions; the offset of the
-//    codes (8 for Q4_0 nibbles, 128 for Q8_0 bytes after flipping the sign
-//    bit) is folded into a per-chunk bias -offset * sum(x) computed once, so a
-//    weight costs one conversion and one FMA.  The block scale is applied once
-//    per chunk: sum_i d*(c_i - o)*x_i = d*(sum_i c_i*x_i - o*sum_i x_i)
+//  * Codes are unpacked to their signed values (Q4_0: nibble - 8; Q8_0: the
+//    int8 code) before they meet the activations, so every product is an
+//    exact dequantized code times x and the accumulation error is relative to
+//    sum |code * x|, whatever the codes or activations are.  The block scale
+//    is applied once per chunk: sum_i d*q_i*x_i = d*(sum_i q_i*x_i)
 //    (A Complete Guide to llama.cpp ..., §2.2: the scale factors out of the
 //    block's dot product).
 //  * U rows x NT tokens partial sums per lane are reduced across the wave by
@@ -99,13 +99,11 @@ __device__ inline float hi_half(uint32_t p)
     return (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16));
 }
 
-// Per-format constants.  A chunk is 16 bytes of codes.  The chunk's dot
-// product is accumulated with biased codes (see chunk_dot) and the bias is
-// removed with a per-chunk term -offset * sum(x) computed once per lane.
+// Weights per 16-byte chunk of codes.
 template <int WT> struct Fmt;
-template <> struct Fmt<W_Q4_0> { static constexpr int wpc = 32; static constexpr float offset = 24.0f; };
-template <> struct Fmt<W_Q8_0> { static constexpr int wpc = 16; static constexpr float offset = 128.0f; };
-template <> struct Fmt<W_F16>  { static constexpr int wpc = 8;  static constexpr float offset = 0.0f; };
+template <> struct Fmt<W_Q4_0> { static constexpr int wpc = 32; };
+template <> struct Fmt<W_Q8_0> { static constexpr int wpc = 16; };
+template <> struct Fmt<W_F16>  { static constexpr int wpc = 8; };
 
 // Weight index (within the row) of element i of chunk c, in the order the
 // kernel keeps activations: natural k order.
@@ -121,44 +119,46 @@ __device__ inline int64_t chunk_block(int64_t c)
     return WT == W_Q4_0 ? c : c / 2;   // Q8_0: two chunks per 32-block
 }
 
-// sum_i code_i * x_i over one chunk, starting from acc (the folded bias).
+// sum_i q_i * x_i over one chunk with the signed codes q_i.
 //  Q4_0: byte j of a block holds element j (low nibble) and j+16 (high
 //        nibble).  A nibble n placed at bits 6..9 of a binary16 word with
 //        exponent field 19 (0x4C00) reads as 16 + n, so one shift and one
-//        and-or give two weights; v_fma_mix_f32 widens the half on the fly.
-//        The chunk sum is then sum (16 + n) x = sum (n - 8) x + 24 sum x.
-//  Q8_0: flipping the sign bit of each byte gives code + 128 as an unsigned
-//        byte, which v_cvt_f32_ubyte{0..3} widens exactly.
+//        and-or give two weights, and one packed binary16 subtraction of 24
+//        (exact: all values are small integers) turns them into n - 8;
+//        v_fma_mix_f32 widens each half on the fly.
+//  Q8_0: each byte is sign-extended and converted (one SDWA conversion).
 //  F16:  the halves of each dword feed v_fma_mix_f32 directly.
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 template <int WT>
-__device__ inline float chunk_dot(const uint4 q, const float *xv, float acc, uint32_t magic)
+__device__ inline float chunk_dot(const uint4 q, const float *xv, uint32_t magic)
 {
     const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+    float acc = 0.0f;
     if (WT == W_Q4_0) {
         const uint32_t m = 0x03C003C0u;
+        const half2_t off = {(_Float16)-24.0f, (_Float16)-24.0f};
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
             const uint32_t w = wd[d];
-            const uint32_t p0 = and_or(w << 6, m, magic);   // elems 4d,      4d+2
-            const uint32_t p1 = and_or(w << 2, m, magic);   // elems 16+4d,   16+4d+2
-            const uint32_t p2 = and_or(w >> 2, m, magic);   // elems 4d+1,    4d+3
-            const uint32_t p3 = and_or(w >> 6, m, magic);   // elems 16+4d+1, 16+4d+3
-            acc = fmaf(lo_half(p0), xv[4 * d], acc);
-            acc = fmaf(hi_half(p0), xv[4 * d + 2], acc);
-            acc = fmaf(lo_half(p1), xv[16 + 4 * d], acc);
-            acc = fmaf(hi_half(p1), xv[16 + 4 * d + 2], acc);
-            acc = fmaf(lo_half(p2), xv[4 * d + 1], acc);
-            acc = fmaf(hi_half(p2), xv[4 * d + 3], acc);
-            acc = fmaf(lo_half(p3), xv[16 + 4 * d + 1], acc);
-            acc = fmaf(hi_half(p3), xv[16 + 4 * d + 3], acc);
+            const half2_t p0 = __builtin_bit_cast(half2_t, and_or(w << 6, m, magic)) + off;   // elems 4d,      4d+2
+            const half2_t p1 = __builtin_bit_cast(half2_t, and_or(w << 2, m, magic)) + off;   // elems 16+4d,   16+4d+2
+            const half2_t p2 = __builtin_bit_cast(half2_t, and_or(w >> 2, m, magic)) + off;   // elems 4d+1,    4d+3
+            const half2_t p3 = __builtin_bit_cast(half2_t, and_or(w >> 6, m, magic)) + off;   // elems 16+4d+1, 16+4d+3
+            acc = fmaf((float)p0.x, xv[4 * d], acc);
+            acc = fmaf((float)p0.y, xv[4 * d + 2], acc);
+            acc = fmaf((float)p1.x, xv[16 + 4 * d], acc);
+            acc = fmaf((float)p1.y, xv[16 + 4 * d + 2], acc);
+            acc = fmaf((float)p2.x, xv[4 * d + 1], acc);
+            acc = fmaf((float)p2.y, xv[4 * d + 3], acc);
+            acc = fmaf((float)p3.x, xv[16 + 4 * d + 1], acc);
+            acc = fmaf((float)p3.y, xv[16 + 4 * d + 3], acc);
         }
     } else if (WT == W_Q8_0) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            const uint32_t u = wd[d] ^ 0x80808080u;   // code + 128 in each byte
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                acc = fmaf((float)((u >> (8 * e)) & 0xFFu), xv[4 * d + e], acc);
+                acc = fmaf((float)(int8_t)(wd[d] >> (8 * e)), xv[4 * d + e], acc);
         }
     } else {
 #pragma unroll
@@ -345,10 +345,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- activations for this lane's chunks, staged through LDS one (token,
-    // chunk round) at a time; the folded code offset -offset * sum(x) per
-    // chunk ----
+    // chunk round) at a time ----
     float xr[NT][CPL][WPC];
-    float xb[NT][CPL];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
 #pragma unroll
@@ -382,10 +380,6 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
 #pragma unroll
                 for (int i = 0; i < WPC; ++i) xr[n][j][i] = 0.0f;
             }
-            float s = 0.0f;
-#pragma unroll
-            for (int i = 0; i < WPC; ++i) s += xr[n][j][i];
-            xb[n][j] = -Fmt<WT>::offset * s;
         }
     }
     const uint32_t magic = 0x4C004C00u;   // binary16 exponent field of 16.0 in both halves
@@ -411,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(const GemvArgs a)
                                     : (float)__builtin_bit_cast(_Float16, scc[u][j]);
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
-                    const float s = chunk_dot<WT>(qc[u][j], xr[n][j], xb[n][j], magic);
+                    const float s = chunk_dot<WT>(qc[u][j], xr[n][j], magic);
                     part[u * NT + n] = fmaf(d, s, part[u * NT + n]);
                 }
             }

@@ -20,12 +20,14 @@
 //    instruction, and two cross-lane swaps (v_permlane32_swap, then
 //    v_permlane16_swap for Q4_0) regroup them so that the four lane groups of
 //    one matrix instruction hold four disjoint 8-code sets of the SAME block.
-//    Codes enter as exact biased bf16 integers (Q4_0: 128 + nibble by one
-//    and-or per two codes; Q8_0: code + 128 by byte conversion).
+//    Codes enter as exact signed bf16 integers, so each product is the
+//    dequantized code times the activation part and no large biased sum
+//    ever has to cancel: Q8_0 bytes are sign-extended and converted; a Q4_0
+//    nibble n is moved to the top of a byte with its top bit flipped, which
+//    reads as the int8 value 16 (n - 8), and the block scale absorbs the 16.
 //  * D (16 x 16): lane (row j, group g) gets channels 4 g .. 4 g + 3, i.e.
-//    tokens 2 g and 2 g + 1, of its row for one block; it removes the code
-//    bias (-bias * sum of the block's activations, precomputed per wave) and
-//    applies the block scale in two fused multiply-adds per token.
+//    tokens 2 g and 2 g + 1, of its row for one block, and applies the block
+//    scale in one fused multiply-add per token.
 //  * The KW waves of a workgroup split K; their partial sums meet in LDS at
 //    the end of each tile.
 #include "qmm_internal.h"
@@ -41,8 +43,10 @@ constexpr int kTileRows = 16;
 constexpr int kMaxMfItems = QMM_GEMV_BATCH_MAX;
 
 template <int WT> struct MfFmt;
-template <> struct MfFmt<W_Q4_0> { static constexpr int bpg = 4, block_bytes = 16; static constexpr float bias = 136.0f; };
-template <> struct MfFmt<W_Q8_0> { static constexpr int bpg = 2, block_bytes = 32; static constexpr float bias = 128.0f; };
+// code_scale: the factor between the value a code enters the matrix
+// instruction with and its signed code (Q4_0 codes enter as 16 (n - 8)).
+template <> struct MfFmt<W_Q4_0> { static constexpr int bpg = 4, block_bytes = 16; static constexpr float code_scale = 0.0625f; };
+template <> struct MfFmt<W_Q8_0> { static constexpr int bpg = 2, block_bytes = 32; static constexpr float code_scale = 1.0f; };
 
 struct alignas(64) MfItem {
     const uint8_t *w;
@@ -71,13 +75,6 @@ struct MfArgs {
     MfItem item[kMaxMfItems];
 };
 
-__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t c)
-{
-    uint32_t d;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(c));
-    return d;
-}
-
 // Round two floats to bf16 (nearest even) in one v_cvt_pk_bf16_f32.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -88,16 +85,11 @@ __device__ inline uint32_t pack_bf16(float lo, float hi)
 __device__ inline float bf16_lo(uint32_t p) { return __builtin_bit_cast(float, p << 16); }
 __device__ inline float bf16_hi(uint32_t p) { return __builtin_bit_cast(float, p & 0xFFFF0000u); }
 
-// Byte E of w as a float (v_cvt_f32_ubyteE).
+// Byte E of w as a signed int8, converted to float (one SDWA conversion).
 template <int E>
-__device__ inline float ubyte(uint32_t w)
+__device__ inline float sbyte(uint32_t w)
 {
-    float r;
-    if constexpr (E == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(w));
-    else if constexpr (E == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(w));
-    else if constexpr (E == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(w));
-    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(w));
-    return r;
+    return (float)(int8_t)(w >> (8 * E));
 }
 
 // The k positions (within a block) of the 8 values lane group g feeds to
@@ -189,7 +181,7 @@ constexpr int kLdsBytes = 160 * 1024;
 template <int WT, int KW, int NBW, int SS>
 constexpr int mf_lds_bytes(int nstg)
 {
-    return nstg * KW * MfStage<WT, NBW, SS>::BYTES + (2 * KW * 64 * 2 + KW * NBW * 16) * 4;
+    return nstg * KW * MfStage<WT, NBW, SS>::BYTES + 2 * KW * 64 * 2 * 4;
 }
 template <int WT, int KW, int NBW, int SS, int MAXD>
 constexpr int mf_stages()
@@ -211,7 +203,6 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
     using St = MfStage<WT, NBW, SS>;
     static_assert(NSTG >= 2 && NSTG <= 4, "2 to 4 stages");
     __shared__ float red[2][KW][64][2];
-    __shared__ float ssum[KW][NBW][16];
     // one array per stage, so that each wait for a stage's loads counts only
     // the loads issued before them
     __shared__ __attribute__((aligned(16))) uint8_t st0[KW][St::BYTES];
@@ -320,32 +311,15 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
             for (int e = 0; e < 4; ++e) { v[e] = r0[e]; v[4 + e] = r1[e]; }
         }
         uint32_t w4[4];
-        float s = 0.0f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const uint32_t hi = pack_bf16(v[2 * e], v[2 * e + 1]);
             const uint32_t lo = pack_bf16(v[2 * e] - bf16_lo(hi), v[2 * e + 1] - bf16_hi(hi));
-            const uint32_t part = lo_part ? lo : hi;
-            w4[e] = part;
-            s += bf16_lo(part) + bf16_hi(part);
+            w4[e] = lo_part ? lo : hi;
         }
         xf[t] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
-        // sum over the four k groups (lanes 16 apart): channel j's block sum
-        s += partner<4>(s, lane);
-        s += partner<5>(s, lane);
-        if (g == 0) ssum[wave][t][j] = s;
-    }
-    __syncthreads();
-    // the code bias of tokens 2g and 2g+1 per block: -bias * (hi sum + lo sum)
-    float cb[NBW][2];
-#pragma unroll
-    for (int t = 0; t < NBW; ++t) {
-        const float4 s4 = *reinterpret_cast<const float4 *>(&ssum[wave][t][4 * g]);
-        cb[t][0] = -MfFmt<WT>::bias * (s4.x + s4.y);
-        cb[t][1] = -MfFmt<WT>::bias * (s4.z + s4.w);
     }
 
-    const uint32_t magic = 0x43004300u;    // bf16 128.0 in both halves
     // one tile: unpack, matrix products, bias and scales; then the partial
     // sums of the KW waves (K ranges) meet in LDS and wave 0 stores the rows
     auto consume = [&](auto &stg, int tl, int it) {
@@ -386,19 +360,23 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
             for (int t = 0; t < BPG; ++t) {
                 uint32_t r[4];
                 if constexpr (WT == W_Q4_0) {
-                    const uint32_t w = (t == 0) ? d0 : (t == 1) ? d1 : (t == 2) ? d2 : d3;
-                    const uint32_t m = 0x000F000Fu;
-                    r[0] = and_or(w, m, magic);
-                    r[1] = and_or(w >> 4, m, magic);
-                    r[2] = and_or(w >> 8, m, magic);
-                    r[3] = and_or(w >> 12, m, magic);
+                    // byte s of w holds lo(s) and hi(s); with the nibbles'
+                    // top bits flipped, each nibble at the top of a byte is
+                    // the int8 value 16 (n - 8)
+                    const uint32_t w = ((t == 0) ? d0 : (t == 1) ? d1 : (t == 2) ? d2 : d3) ^ 0x88888888u;
+                    const uint32_t hn = w & 0xF0F0F0F0u;            // hi(s) of every byte
+                    const uint32_t ln = (w << 4) & 0xF0F0F0F0u;     // lo(s) of every byte
+                    r[0] = pack_bf16(sbyte<0>(ln), sbyte<2>(ln));   // lo(s0) lo(s2)
+                    r[1] = pack_bf16(sbyte<0>(hn), sbyte<2>(hn));   // hi(s0) hi(s2)
+                    r[2] = pack_bf16(sbyte<1>(ln), sbyte<3>(ln));   // lo(s1) lo(s3)
+                    r[3] = pack_bf16(sbyte<1>(hn), sbyte<3>(hn));   // hi(s1) hi(s3)
                 } else {
-                    const uint32_t wa = ((t == 0) ? d0 : d2) ^ 0x80808080u;   // code + 128
-                    const uint32_t wb = ((t == 0) ? d1 : d3) ^ 0x80808080u;
-                    r[0] = pack_bf16(ubyte<0>(wa), ubyte<1>(wa));
-                    r[1] = pack_bf16(ubyte<2>(wa), ubyte<3>(wa));
-                    r[2] = pack_bf16(ubyte<0>(wb), ubyte<1>(wb));
-                    r[3] = pack_bf16(ubyte<2>(wb), ubyte<3>(wb));
+                    const uint32_t wa = (t == 0) ? d0 : d2;
+                    const uint32_t wb = (t == 0) ? d1 : d3;
+                    r[0] = pack_bf16(sbyte<0>(wa), sbyte<1>(wa));
+                    r[1] = pack_bf16(sbyte<2>(wa), sbyte<3>(wa));
+                    r[2] = pack_bf16(sbyte<0>(wb), sbyte<1>(wb));
+                    r[3] = pack_bf16(sbyte<2>(wb), sbyte<3>(wb));
                 }
                 const bf16x8 wf = __builtin_bit_cast(bf16x8, make_uint4(r[0], r[1], r[2], r[3]));
                 const f32x4 D = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[p * BPG + t], wf,
@@ -410,13 +388,13 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
                 const uint32_t sw = sc[hw / 2];
                 const float ds = (float)__builtin_bit_cast(_Float16, (uint16_t)((hw & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
                 const float d = (b_begin + p * BPG + t < nb) ? ds : 0.0f;
-                yp0 = fmaf(d, D[0] + D[1] + cb[p * BPG + t][0], yp0);
-                yp1 = fmaf(d, D[2] + D[3] + cb[p * BPG + t][1], yp1);
+                yp0 = fmaf(d, D[0] + D[1], yp0);
+                yp1 = fmaf(d, D[2] + D[3], yp1);
             }
         }
         float *mine = red[it & 1][wave][lane];
-        mine[0] = yp0;
-        mine[1] = yp1;
+        mine[0] = yp0 * MfFmt<WT>::code_scale;     // a power of two: exact
+        mine[1] = yp1 * MfFmt<WT>::code_scale;
         __syncthreads();
         if (wave == 0) {
             float s0 = 0.0f, s1 = 0.0f;

@@ -86,3 +86,74 @@ def activations_device(seed_: int, N: int, K: int, device) -> torch.Tensor:
     g = torch.Generator(device=device)
     g.manual_seed(seed_)
     return torch.randn((N, K), generator=g, device=device, dtype=torch.float32)
+
+
+# ---------------------------------------------------------------- edge cases
+#
+# Inputs that reach the corners of the method rather than its typical case:
+# weight blocks at many magnitudes (zero blocks, blocks whose fp16 scale is
+# subnormal, blocks of exact quarter-steps that make rounding ties, blocks
+# scaled by 1000) and blocks holding one large weight among zeros, paired
+# with activations whose mean is far from zero and which are tiny exactly
+# where those lone weights sit.  Only random draws and masks: no method
+# arithmetic.
+
+def adversarial_weights(seed_: int, M: int, K: int, block: int = 32) -> np.ndarray:
+    """Gaussian rows at many magnitudes plus blocks of `block` weights that
+    hit ties, clamps, zero blocks and subnormal fp16 scales."""
+    rng = np.random.default_rng(seed_)
+    w = rng.standard_normal((M, K), dtype=np.float32) * np.float32(0.02)
+    blocks = w.reshape(-1, block)
+    nb = blocks.shape[0]
+    sel = rng.random(nb)
+    blocks[sel < 0.05] = 0.0
+    tiny = (sel >= 0.05) & (sel < 0.10)
+    blocks[tiny] *= np.float32(2.0 ** -18)
+    ties = (sel >= 0.10) & (sel < 0.20)
+    blocks[ties] = (rng.integers(-16, 17, (int(ties.sum()), block)) / np.float32(16)).astype(np.float32)
+    big = (sel >= 0.20) & (sel < 0.25)
+    blocks[big] *= np.float32(1000.0)
+    return blocks.reshape(M, K)
+
+
+def outlier_column(K: int, seed_: int) -> np.ndarray:
+    """For each 32-block of a row of K, the position (0..31) of its lone
+    weight in outlier blocks; shared by every row, so that activations can be
+    made tiny exactly there."""
+    return np.random.default_rng(seed_).integers(0, 32, K // 32)
+
+
+def outlier_weights(seed_: int, M: int, K: int, frac: float = 0.5) -> np.ndarray:
+    """adversarial_weights, with 32-blocks replaced by one weight of
+    magnitude 0.02, 0.2 or 2 (random sign) at the block's outlier_column
+    position and zeros elsewhere: every block of every third row, and a
+    fraction `frac` of the blocks of the other rows."""
+    w = adversarial_weights(seed_, M, K)
+    rng = np.random.default_rng(seed_ + 1)
+    pos = outlier_column(K, seed_ + 2)
+    nbk = K // 32
+    sel = rng.random((M, nbk)) < frac
+    sel[::3] = True
+    mag = (rng.choice(np.array([0.02, 0.2, 2.0], np.float32), (M, nbk)) *
+           rng.choice(np.array([-1.0, 1.0], np.float32), (M, nbk))).astype(np.float32)
+    blocks = w.reshape(M, nbk, 32)
+    blocks[sel] = 0.0
+    rows, cols = np.nonzero(sel)
+    blocks[rows, cols, pos[cols]] = mag[rows, cols]
+    return blocks.reshape(M, K)
+
+
+def shifted_activations(seed_: int, N: int, K: int, outlier_seed: int | None = None,
+                        mean: float = 5.0) -> np.ndarray:
+    """x ~ N(mean, 1) (N, K); where outlier_seed is given, x = 0.01 (random
+    sign) at the outlier_column positions of that seed, and a tenth of the
+    other activations of token 1 (if any) are exact zeros."""
+    rng = np.random.default_rng(seed_)
+    x = (rng.standard_normal((N, K), dtype=np.float32) + np.float32(mean)).astype(np.float32)
+    if outlier_seed is not None:
+        pos = outlier_column(K, outlier_seed + 2)
+        ks = 32 * np.arange(K // 32) + pos
+        x[:, ks] = (np.float32(0.01) * rng.choice(np.array([-1.0, 1.0], np.float32), (N, ks.size))).astype(np.float32)
+    if N > 1:
+        x[1, rng.random(K) < 0.1] = 0.0
+    return x

@@ -86,19 +86,7 @@ QUANT_SHAPES = [(1, 32), (3, 96), (257, 160), (64, 2048), (129, 5632), (5, 32768
 def _adversarial(M, K, seed):
     """Gaussian rows at many magnitudes plus blocks that hit ties, clamps,
     zero blocks and subnormal fp16 scales."""
-    rng = np.random.default_rng(seed)
-    w = rng.standard_normal((M, K), dtype=np.float32) * np.float32(0.02)
-    blocks = w.reshape(-1, 32)
-    nb = blocks.shape[0]
-    sel = rng.random(nb)
-    blocks[sel < 0.05] = 0.0
-    tiny = (sel >= 0.05) & (sel < 0.10)
-    blocks[tiny] *= np.float32(2.0 ** -18)
-    ties = (sel >= 0.10) & (sel < 0.20)
-    blocks[ties] = (rng.integers(-16, 17, (int(ties.sum()), 32)) / np.float32(16)).astype(np.float32)
-    big = (sel >= 0.20) & (sel < 0.25)
-    blocks[big] *= np.float32(1000.0)
-    return blocks.reshape(M, K)
+    return WL.adversarial_weights(seed, M, K)
 
 
 @pytest.mark.parametrize("tname", ["Q8_0", "Q4_0"])
