@@ -90,7 +90,8 @@ typedef enum {
     QMM_ERR_LAYOUT      = -4,  /* nb / alignment not supported                       */
     QMM_ERR_ALIAS       = -5,  /* the output overlaps an input                       */
     QMM_ERR_UNSUPPORTED = -6,  /* n_dims > 2, ne[2] or ne[3] != 1, or K*N too large */
-    QMM_ERR_DEVICE      = -7   /* the HIP runtime refused the launch                 */
+    QMM_ERR_DEVICE      = -7,  /* the HIP runtime refused the launch                 */
+    QMM_ERR_SCRATCH     = -8   /* more scratch than the static array holds           */
 } qmm_status;
 
 /* Tensor descriptor ("No Python! ...", §4: Tensor {n_dims, ne[4], nb[4],
@@ -266,6 +267,24 @@ QMM_API int qmm_gemm(const qmm_tensor *w, const qmm_tensor *x_bf16, qmm_tensor *
 QMM_API size_t qmm_gemm_workspace_size(const qmm_tensor *w, const qmm_tensor *x_bf16);
 QMM_API int qmm_gemm_ws(const qmm_tensor *w, const qmm_tensor *x_bf16, qmm_tensor *y_f32, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/* qmm_gemm_ws for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the split-K workspace is the first workspace_bytes of a static device
+ * array of QMM_NOALLOC_SCRATCH_BYTES that the library owns (one per device,
+ * held until the process ends), so the call neither allocates nor frees.
+ * Same operands, result bits and errors as qmm_gemm_ws with a caller
+ * workspace of workspace_bytes; workspace_bytes above
+ * QMM_NOALLOC_SCRATCH_BYTES returns QMM_ERR_SCRATCH with nothing enqueued.
+ * qmm_gemm_workspace_size(w, x_bf16) gives the full split (at most 16 MiB on
+ * a 256-CU device, so it always fits there); 0 runs without a split.
+ * Every call on one device shares that device's array: calls that overlap in
+ * time on one device (on different streams, or from several host threads
+ * without ordering) race on it and give wrong results.  The array needs no
+ * clearing: each split writes every partial sum it later reads. */
+#define QMM_NOALLOC_SCRATCH_BYTES (16u << 20)
+QMM_API int qmm_gemm_noalloc(const qmm_tensor *w, const qmm_tensor *x_bf16, qmm_tensor *y_f32,
+                             size_t workspace_bytes, void *stream);
 
 /* Most products one qmm_gemm_batch call takes. */
 #define QMM_GEMM_BATCH_MAX 8

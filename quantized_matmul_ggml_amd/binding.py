@@ -23,11 +23,12 @@ TYPE_NAMES = {F32: "F32", F16: "F16", BF16: "BF16", Q8_0: "Q8_0", Q4_0: "Q4_0",
               Q8_B64: "Q8_B64", Q4_B64: "Q4_B64"}
 
 # qmm_status
-OK, ERR_NULL, ERR_TYPE, ERR_SHAPE, ERR_LAYOUT, ERR_ALIAS, ERR_UNSUPPORTED, ERR_DEVICE = \
-    0, -1, -2, -3, -4, -5, -6, -7
+OK, ERR_NULL, ERR_TYPE, ERR_SHAPE, ERR_LAYOUT, ERR_ALIAS, ERR_UNSUPPORTED, ERR_DEVICE, ERR_SCRATCH = \
+    0, -1, -2, -3, -4, -5, -6, -7, -8
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTS = ("qmm_row_size", "qmm_quantize", "qmm_quantize_rule", "qmm_dequantize", "qmm_gemv", "qmm_gemv_batch",
-           "qmm_gemv_swiglu", "qmm_gemm", "qmm_gemm_ws", "qmm_gemm_workspace_size", "qmm_gemm_batch", "qmm_gemm_swiglu", "qmm_record_size", "qmm_records_to_rows",
+           "qmm_gemv_swiglu", "qmm_gemm", "qmm_gemm_ws", "qmm_gemm_noalloc", "qmm_gemm_workspace_size", "qmm_gemm_batch", "qmm_gemm_swiglu", "qmm_record_size", "qmm_records_to_rows",
            "qmm_rows_to_records", "qmm_strerror")
 GEMV_BATCH_MAX = 8
 
@@ -80,6 +81,8 @@ def lib() -> ctypes.CDLL:
         h.qmm_gemm.argtypes = [P, P, P, ctypes.c_void_p]
         h.qmm_gemm_ws.argtypes = [P, P, P, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
         h.qmm_gemm_ws.restype = ctypes.c_int
+        h.qmm_gemm_noalloc.argtypes = [P, P, P, ctypes.c_size_t, ctypes.c_void_p]
+        h.qmm_gemm_noalloc.restype = ctypes.c_int
         h.qmm_gemm_workspace_size.argtypes = [P, P]
         h.qmm_gemm_workspace_size.restype = ctypes.c_size_t
         h.qmm_gemm_batch.argtypes = [ctypes.POINTER(QmmGemmItem), ctypes.c_int32, ctypes.c_void_p]
@@ -344,6 +347,20 @@ def gemm(w: Weight, x: torch.Tensor, *, out: torch.Tensor | None = None, workspa
                                  ctypes.c_void_p(workspace.data_ptr()),
                                  workspace.numel() * workspace.element_size(), _stream(stream)),
                "qmm_gemm_ws")
+    return out
+
+
+def gemm_noalloc(w: Weight, x: torch.Tensor, out: torch.Tensor, *, workspace_bytes: int | None = None,
+                 stream=None) -> torch.Tensor:
+    """qmm_gemm_noalloc: the GEMM with its split-K partial sums in the
+    library's static scratch array (no allocation in the call; `out` is the
+    caller's).  workspace_bytes defaults to the full split of these shapes."""
+    _need_gpu(w.data, x, out)
+    wd, xd, yd = w.desc(), _dense_desc(x, BF16), _dense_desc(out, F32)
+    if workspace_bytes is None:
+        workspace_bytes = int(lib().qmm_gemm_workspace_size(ctypes.byref(wd), ctypes.byref(xd)))
+    _check(lib().qmm_gemm_noalloc(ctypes.byref(wd), ctypes.byref(xd), ctypes.byref(yd),
+                                  ctypes.c_size_t(workspace_bytes), _stream(stream)), "qmm_gemm_noalloc")
     return out
 
 

@@ -904,3 +904,38 @@ hipError_t allow_dynamic_lds(const void *fn, int bytes)
 }
 
 }  // namespace qmm
+
+// ---- scratch memory for callers that cannot allocate ----------------------
+//
+// The split-K partial sums of qmm_gemm_noalloc live in this array instead of
+// a caller workspace.  Every device the library runs on holds its own copy
+// until the process ends.  In host code the name is only a stand-in: the
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current, and only that address is handed to kernels.
+namespace qmm {
+namespace {
+static __device__ __align__(256) uint8_t scratch[QMM_NOALLOC_SCRATCH_BYTES];
+}  // namespace
+
+hipError_t static_scratch(void **ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
+}  // namespace qmm

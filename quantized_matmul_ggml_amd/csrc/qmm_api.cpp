@@ -469,6 +469,21 @@ int qmm_gemm_ws(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, void *w
                                       workspace_bytes, static_cast<hipStream_t>(stream)));
 }
 
+int qmm_gemm_noalloc(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, size_t workspace_bytes,
+                     void *stream)
+{
+    const int rc = check_gemm(w, x, y);
+    if (rc) return rc;
+    if (workspace_bytes > QMM_NOALLOC_SCRATCH_BYTES) return QMM_ERR_SCRATCH;
+    if (w->ne[1] == 0 || x->ne[1] == 0) return QMM_OK;
+    void *ws = nullptr;
+    if (workspace_bytes && qmm::static_scratch(&ws) != hipSuccess) return QMM_ERR_DEVICE;
+    qmm::ActView xv{x->data, pitch_elems(x), x->ne[1]};
+    qmm::OutView yv{static_cast<float *>(y->data), pitch_elems(y)};
+    return status_of(qmm::launch_gemm(weight_view(w), xv, yv, static_cast<float *>(ws), workspace_bytes,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 const char *qmm_strerror(int status)
 {
     switch (status) {
@@ -480,6 +495,7 @@ const char *qmm_strerror(int status)
     case QMM_ERR_ALIAS: return "the output overlaps an input";
     case QMM_ERR_UNSUPPORTED: return "unsupported tensor rank or size";
     case QMM_ERR_DEVICE: return "the HIP runtime refused the launch";
+    case QMM_ERR_SCRATCH: return "the call needs more scratch memory than the library's static array holds";
     default: return "unknown qmm status";
     }
 }

@@ -121,6 +121,10 @@ hipError_t launch_gemv_swiglu(const WeightView &wg, const WeightView &wu, const 
 // passes that add to y.
 bool gemv_mf_supported(const GemvTask *tasks, int count);
 hipError_t launch_gemv_mf(const GemvTask *tasks, int count, hipStream_t stream);
+// Device address of the library's static scratch array on the current
+// device (QMM_NOALLOC_SCRATCH_BYTES, 256-byte aligned; gemm.hip), looked up
+// once per device.
+hipError_t static_scratch(void **ptr);
 // Grant a kernel more than the default dynamic LDS (once per size; gemm.hip).
 hipError_t allow_dynamic_lds(const void *fn, int bytes);
 

@@ -58,7 +58,7 @@ def test_row_size_matches_oracle(qmm_lib, orc):
 
 def test_strerror_covers_every_status(qmm_lib):
     seen = set()
-    for s in range(-7, 1):
+    for s in range(-8, 1):
         t = qmm_lib.strerror(s)
         assert t and t not in seen
         seen.add(t)
