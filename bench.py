@@ -14,8 +14,12 @@ Also reported on the same JSON line:
   * breakdown: the 512 x 512 Q8_0 GEMV, the fp16 5632 x 2048 GEMV and the
     Q8_0 LM head with 1, 2, 4 and 8 tokens (GB/s, rotating weight copies);
   * roofline: the dominant kernel (the Q4_0 FFN gate/up GEMV, 5632 x 2048)
-    timed per launch with HIP events;
-  * cpu_baseline: the CPU oracle on a bounded sample of the same decode step.
+    timed per launch with HIP events, beside the rocprofv3 average of the
+    same kernel and the read ceiling of a launch of the same bytes;
+  * context: the streaming-read ceiling of one launch at each decode size
+    (libqmm's stream_read kernel) and the shader clock under load;
+  * cpu_baseline: the CPU oracle (1 thread and all host threads, median of 3)
+    on each workload, bounded samples of the large ones.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -25,12 +29,12 @@ import argparse
 import json
 import os
 import sys
-import threading
 import time
 
 METRIC = "quantized mul_mat GB/s (decode GEMV) & TFLOP/s (prefill), % of roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix cores, TFLOP/s
+# MI355X dense bf16 matrix cores: 256 CUs x 2.4 GHz x 4096 flop per clock per CU
+BF16_PEAK_TFLOPS = 2516.6
 HERE = os.path.dirname(os.path.abspath(__file__))
 # HBM traffic of the dominant kernel, from hardware counters (see traffic_probe)
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "gemv_q4_0_gate_up_hbm_traffic.md")
@@ -48,8 +52,6 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip prefill/breakdown legs")
     ap.add_argument("--gemm-probe", action="store_true",
@@ -245,6 +247,21 @@ def main():
     sw_gbs = sw_bytes / (sw_ms * 1e-3) / 1e9
     log(f"gate/up SwiGLU fused GEMV {sw_ms * 1e3:.2f} us/launch  {sw_gbs:.0f} GB/s")
 
+    # context: the read ceiling of one launch of the same bytes, the decode
+    # step's ceiling given its launches (each launch at the read ceiling of
+    # its bytes), and the shader clock under load
+    ceiling = ReadCeiling(Q, dev, args)
+    layer_launch_bytes = [
+        sum(gemv_bytes(layers[0][n], 1) for n in ("wq", "wk", "wv")),
+        gemv_bytes(layers[0]["wo"], 1),
+        kern_bytes,
+        gemv_bytes(layers[0]["wdown"], 1)]
+    step_ceiling_us = (WL.LAYERS * sum(ceiling(b)["us"] for b in layer_launch_bytes)
+                       + ceiling(gemv_bytes(lm, 1))["us"])
+    asym = ceiling(1 << 30)
+    clocks = clock_leg(Q)
+    rec = stored_kernel_record()
+
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -266,29 +283,39 @@ def main():
             "driver": "hip graph replay; [Wq Wk Wv] and [Wgate Wup] as one batched launch each",
             "decode_tokens_per_s": round(1e3 / ms, 1),
             "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+            "step_read_ceiling": {
+                "what": "the step's 89 launches each at the read ceiling of its bytes",
+                "us": round(step_ceiling_us, 1),
+                "gbs": round(step_bytes / (step_ceiling_us * 1e-6) / 1e9, 1),
+                "frac_of_it": round(step_ceiling_us / (ms * 1e3), 4)},
+            "read_ceiling_1gib_gbs": asym["gbs"],
+            "sclk_mhz_under_load": clocks,
             "wall_s_timed_region": round(wall, 4),
             "variants": {k: {"us": round(v["ms"] * 1e3, 1), "gbs": round(v["gbs"], 1),
                              "launches": v["launches"], "tokens_per_s": round(1e3 / v["ms"], 1)}
                          for k, v in variants.items()},
-            "swiglu_fused_gate_up": {"kernel": "Q4_0 gate/up 2 x 5632 x 2048 + SwiGLU, batch 1",
+            "swiglu_fused_gate_up": ceiling.attach({"kernel": "Q4_0 gate/up 2 x 5632 x 2048 + SwiGLU, batch 1",
                                      "avg_launch_us": round(sw_ms * 1e3, 3), "bytes_per_launch": sw_bytes,
                                      "gbs": round(sw_gbs, 1),
-                                     "frac_of_hbm_peak": round(sw_gbs / HBM_PEAK_GBS, 4)},
+                                     "frac_of_hbm_peak": round(sw_gbs / HBM_PEAK_GBS, 4)}, sw_bytes, sw_gbs),
         },
-        "roofline": {
+        "roofline": ceiling.attach({
             "kernel": "Q4_0 batched GEMV [Wgate, Wup] 2 x 5632 x 2048, batch 1",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(),
             "avg_launch_us": round(kern_ms * 1e3, 3), "bytes_per_launch": kern_bytes,
-        },
+            "timing": "HIP events around graph replays of the 22 layers' launches, divided by the launches",
+            "rocprof_avg_us": rec and rec["avg_us"],
+            "frac_rocprof": rec and round(kern_bytes / (rec["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        }, kern_bytes, achieved),
     }
 
     if not args.no_extras:
         result["prefill"] = prefill_leg(Q, WL, dev, args)
-        result["breakdown"] = breakdown_leg(Q, WL, dev, args, gemv_bytes)
+        result["breakdown"] = breakdown_leg(Q, WL, dev, args, gemv_bytes, ceiling)
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_leg(WL, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline_leg(WL)
 
     print(json.dumps(result), flush=True)
 
@@ -319,6 +346,27 @@ def stored_traffic():
         log("stored HBM traffic is stale (GEMV source changed): reporting null")
         return None
     return rec["traffic_bytes_per_launch"]
+
+
+KERNEL_STATS_FILE = os.path.join(HERE, "profiles", "gemv_q4_0_decode_step_kernel_stats.md")
+
+
+def stored_kernel_record():
+    """The rocprofv3 average duration of the dominant kernel (the gate/up
+    batch launch) from the committed kernel trace, or None when there is
+    none or the GEMV source changed since it was taken."""
+    try:
+        with open(KERNEL_STATS_FILE) as f:
+            lines = [l for l in f if l.startswith("kernel-record: ")]
+    except OSError:
+        return None
+    if not lines:
+        return None
+    rec = json.loads(lines[-1][len("kernel-record: "):])
+    if rec.get("gemv_source_sha256") != gemv_source_hash():
+        log("stored kernel trace is stale (GEMV source changed): rocprof figure null")
+        return None
+    return rec
 
 
 def traffic_probe():
@@ -368,6 +416,62 @@ def gemm_probe():
         Q.gemm(w, x, out=y)
     torch.cuda.synchronize()
     log(f"gemm probe: 20 launches of Q4_0 {M} x {K} x bf16 {N}")
+
+
+class ReadCeiling:
+    """Streaming-read ceiling of ONE launch of a given size: libqmm's
+    stream_read kernel reading `size` bytes, rotating over distinct slices of
+    a 2 GiB pool (no launch finds its bytes in a cache), graph-replayed and
+    timed with HIP events per launch like the GEMVs; the fastest of a few
+    grid sizes.  Sizes are measured on first request and remembered."""
+
+    POOL = (1 << 31) + (64 << 20)
+
+    def __init__(self, Q, dev, args):
+        import torch
+        self.Q, self.args = Q, args
+        self.pool = torch.empty(self.POOL, dtype=torch.uint8, device=dev)
+        self.pool.fill_(0x5A)
+        self.sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+        self.memo = {}
+
+    def __call__(self, size):
+        n = (int(size) + 15) // 16 * 16
+        if n in self.memo:
+            return self.memo[n]
+        copies = max(2, min(64, self.POOL // n))
+        slices = [self.pool[i * n:(i + 1) * n] for i in range(copies)]
+        best = None
+        for wgs in (512, 1024, 2048, 4096):
+            g = Graph(lambda: [self.Q.stream_read(sl, self.sink, workgroups=wgs) for sl in slices])
+            ms, _ = timed(g, max(3, self.args.steps // 4), 2)
+            per = ms / copies
+            if best is None or per < best[0]:
+                best = (per, wgs)
+        r = {"bytes": n, "us": round(best[0] * 1e3, 3), "gbs": round(n / (best[0] * 1e-3) / 1e9, 1),
+             "workgroups": best[1]}
+        log(f"read ceiling {n} B: {r['us']:.2f} us/launch  {r['gbs']:.0f} GB/s ({best[1]} workgroups)")
+        self.memo[n] = r
+        return r
+
+    def attach(self, entry, nbytes, gbs):
+        """Add the same-size read ceiling and the fraction of it to entry."""
+        c = self(nbytes)
+        entry["read_ceiling_gbs"] = c["gbs"]
+        entry["frac_of_read_ceiling"] = round(gbs / c["gbs"], 4)
+        return entry
+
+
+def clock_leg(Q):
+    """Shader clock (MHz) under a VALU chain and under a matrix-instruction
+    chain on 4 waves of every CU (libqmm's clock probe)."""
+    import torch
+    props = torch.cuda.get_device_properties(torch.cuda.current_device())
+    cus = props.multi_processor_count
+    r = {"valu_mhz": round(Q.clock_probe(workgroups=cus, iters=20000, mode=0), 1),
+         "mfma_mhz": round(Q.clock_probe(workgroups=cus, iters=20000, mode=1), 1)}
+    log(f"shader clock under load: VALU {r['valu_mhz']} MHz, bf16 MFMA {r['mfma_mhz']} MHz")
+    return r
 
 
 def prefill_leg(Q, WL, dev, args):
@@ -465,7 +569,7 @@ def prefill_leg(Q, WL, dev, args):
             "layer_512_tokens": layer}
 
 
-def breakdown_leg(Q, WL, dev, args, gemv_bytes):
+def breakdown_leg(Q, WL, dev, args, gemv_bytes, ceiling):
     import ctypes
     import torch
     from quantized_matmul_ggml_amd import binding as B
@@ -486,7 +590,7 @@ def breakdown_leg(Q, WL, dev, args, gemv_bytes):
     y1 = torch.empty((1, 512), device=dev)
     per = rotate(w1, x1, y1, 256)
     b = gemv_bytes(w1[0], 1)
-    out["q8_0_gemv_512x512_n1"] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1)}
+    out["q8_0_gemv_512x512_n1"] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1), "bytes": b}
     del w1
 
     # Q4_0 5632 x 2048 (the FFN gate / up shape), one token: fp32 activations
@@ -499,7 +603,7 @@ def breakdown_leg(Q, WL, dev, args, gemv_bytes):
                              ("q4_0_gemv_5632x2048_n1_int8_activations", xq3, xq3.data.numel())):
         per = rotate(w3, xx, y3, 96)
         b = WL.FFN * Q.row_size(Q.Q4_0, WL.HIDDEN) + xbytes + 4 * WL.FFN
-        out[name] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1),
+        out[name] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1), "bytes": b,
                      "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
     del w3
 
@@ -507,7 +611,7 @@ def breakdown_leg(Q, WL, dev, args, gemv_bytes):
     w5 = [Q.quantize(WL.weights_device(WL.seed(3, 4, r), WL.FFN, WL.HIDDEN, dev), Q.Q4_B64) for r in range(48)]
     per = rotate(w5, x3, y3, 96)
     b = WL.FFN * Q.row_size(Q.Q4_B64, WL.HIDDEN) + 4 * WL.HIDDEN + 4 * WL.FFN
-    out["q4_b64_gemv_5632x2048_n1"] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1),
+    out["q4_b64_gemv_5632x2048_n1"] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1), "bytes": b,
                                        "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
     del w5
 
@@ -520,7 +624,7 @@ def breakdown_leg(Q, WL, dev, args, gemv_bytes):
     y2 = torch.empty((1, WL.FFN), device=dev)
     per = rotate(w2, x2, y2, 96)
     b = gemv_bytes(w2[0], 1)
-    out["f16_gemv_5632x2048_n1"] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1),
+    out["f16_gemv_5632x2048_n1"] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1), "bytes": b,
                                     "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
     del w2
 
@@ -533,7 +637,7 @@ def breakdown_leg(Q, WL, dev, args, gemv_bytes):
         per = rotate(w4, x4, y4, 32)
         b = gemv_bytes(w4[0], n)
         out[f"q8_0_lm_head_32000x2048_n{n}"] = {
-            "us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1),
+            "us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1), "bytes": b,
             "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
     # the integer-activation path: activations quantized to Q8_0 blocks, block
     # dot products in int8 (bytes: weights + Q8_0 activations + fp32 outputs)
@@ -543,7 +647,7 @@ def breakdown_leg(Q, WL, dev, args, gemv_bytes):
         per = rotate(w4, xq4, y4, 32)
         b = w4[0].M * Q.row_size(Q.Q8_0, WL.HIDDEN) + xq4.data.numel() + 4 * n * WL.VOCAB
         out[f"q8_0_lm_head_32000x2048_n{n}_int8_activations"] = {
-            "us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1),
+            "us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1), "bytes": b,
             "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
     # block-record interchange of the LM head (GGUF-style records <-> rows),
     # 4 copies so the 139 MB each call moves is not cache-resident
@@ -561,58 +665,99 @@ def breakdown_leg(Q, WL, dev, args, gemv_bytes):
         ms, _ = timed(g, max(2, args.steps // 2), 2)
         per = ms / 4
         b = 2 * recs[0].numel()                 # record bytes read + row bytes written (equal)
-        out[name] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1),
+        out[name] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1), "bytes": b,
                      "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
     assert torch.equal(rows[0].data, w4[0].data), "records -> rows must restore the packed rows"
     del w4, recs, rows
     for k, v in out.items():
+        if "records" not in k:                  # a copy, not a read: no read ceiling
+            ceiling.attach(v, v["bytes"], v["gbs"])
         log(f"{k}: {v}")
     return out
 
 
-def cpu_baseline_leg(WL, seconds):
-    """The oracle (plain C, binary64) on the host cores, on a bounded sample
-    of the decode step: whole decoder layers (same shapes, seeded weights
-    quantized by the oracle itself), repeated until about `seconds` of CPU
-    time, rows split evenly over the threads.  Reported in the step's unit:
-    algorithmic bytes of the sample per second."""
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_leg(WL):
+    """The oracle (plain C, binary64; oracle/oracle_timing.c splits the rows
+    over POSIX threads) timed on the host: each workload once on 1 thread
+    and once on the host's threads (capped at 16, the CPU share of one GPU
+    here), median of 3 runs each.  The large workloads are bounded samples of
+    their rows (all of K and of the tokens).  `value` is the decode layer's
+    rate on the host's threads, in the step's unit (algorithmic GB/s)."""
     import numpy as np
     import oracle as orc
-    cores = max(1, min(16, os.cpu_count() or 1))
+    hw = orc.online_cpus()
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = hw
+    threads = max(1, min(16, avail))
+    rs = orc.row_size
+
+    def entry(name, parts, sample):
+        """parts: [(type, packed, K, x, x_bf16)]; times the sum over parts."""
+        nbytes = flops = 0
+        for t, packed, K, x, bf in parts:
+            M = packed.shape[0]
+            N = x.shape[0]
+            nbytes += M * (rs(t, K) if t != orc.F16 else 2 * K) + (2 if bf else 4) * N * K + 4 * N * M
+            flops += 2 * M * K * N
+        r = {"sample": sample, "bytes": nbytes, "flops": flops}
+        for label, th in (("1_thread", 1), (f"{threads}_threads", threads)):
+            sec = sum(orc.time_mul_mat(t, packed, K, x, threads=th, reps=3, x_bf16_bits=bf)
+                      for t, packed, K, x, bf in parts)
+            r[label] = {"s": round(sec, 5), "gbs": round(nbytes / sec / 1e9, 4),
+                        "gflops": round(flops / sec / 1e9, 4)}
+        log(f"cpu oracle {name}: 1 thread {r['1_thread']['gbs']} GB/s, {threads} threads "
+            f"{r[f'{threads}_threads']['gbs']} GB/s ({sample})")
+        return r
+
+    per = {}
+    w = WL.weights(WL.seed(1, 0), 512, 512)
+    per["q8_0_gemv_512x512_n1"] = entry("C1", [(orc.Q8_0, orc.quantize(orc.Q8_0, w), 512,
+                                               WL.activations(WL.seed(1, 1), 1, 512), False)], "whole")
+    w = WL.round_f16(WL.weights(WL.seed(2, 0), WL.FFN, WL.HIDDEN))
+    per["f16_gemv_5632x2048_n1"] = entry("C2", [(orc.F16, w.view(np.uint8).reshape(WL.FFN, -1), WL.HIDDEN,
+                                                WL.activations(WL.seed(2, 1), 1, WL.HIDDEN), False)], "whole")
     xs = [WL.activations(WL.seed(3, 7 + s), 1, k) for s, k in enumerate(WL.LAYER_X_K)]
-    layer = []
-    for t, (name, M, K, slot) in enumerate(WL.LAYER):
-        layer.append((orc.quantize(orc.Q4_0, WL.weights(WL.seed(3, t), M, K)), M, K, slot))
-    layer_bytes = sum(M * orc.row_size(orc.Q4_0, K) + 4 * K + 4 * M for _, M, K, _ in layer)
-
-    def run_layer():
-        jobs = []
-        for packed, M, K, slot in layer:
-            for c in range(cores):
-                jobs.append((packed, K, xs[slot], M * c // cores, M * (c + 1) // cores))
-        chunks = [jobs[i::cores] for i in range(cores)]
-
-        def worker(chunk):
-            for packed, K, x, m0, m1 in chunk:
-                orc.mul_mat(orc.Q4_0, packed, K, x, rows=(m0, m1))
-        th = [threading.Thread(target=worker, args=(c,)) for c in chunks]
-        for t in th:
-            t.start()
-        for t in th:
-            t.join()
-
-    n_layers, t0 = 0, time.perf_counter()
-    while True:
-        run_layer()
-        n_layers += 1
-        el = time.perf_counter() - t0
-        if el * cores >= seconds:
-            break
-    gbs = n_layers * layer_bytes / el / 1e9
-    log(f"cpu oracle: {n_layers} layer(s) in {el:.2f} s on {cores} threads -> {gbs:.3f} GB/s")
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n_layers} Q4_0 decoder layers (7 GEMVs each, batch 1; the step has 22 "
-                      f"plus the LM head), binary64 oracle, {el:.2f} s wall"}
+    layer = [(orc.Q4_0, orc.quantize(orc.Q4_0, WL.weights(WL.seed(3, t), M, K)), K, xs[slot], False)
+             for t, (_, M, K, slot) in enumerate(WL.LAYER)]
+    per["q4_0_decode_layer"] = entry("C3", layer, "one whole layer (7 GEMVs)")
+    rows = 2048
+    wl = orc.quantize(orc.Q8_0, WL.weights(WL.seed(4, 0), rows, WL.HIDDEN))
+    for n in (1, 2, 4, 8):
+        per[f"q8_0_lm_head_32000x2048_n{n}"] = entry(
+            f"C4 N={n}", [(orc.Q8_0, wl, WL.HIDDEN, WL.activations(WL.seed(4, 1), n, WL.HIDDEN), False)],
+            f"{rows} of 32000 rows")
+    rows5 = 64
+    w5 = orc.quantize(orc.Q4_0, WL.weights(WL.seed(5, 0), rows5, WL.HIDDEN))
+    x5 = WL.round_bf16_bits(WL.activations(WL.seed(5, 1), 512, WL.HIDDEN))
+    per["q4_0_prefill_gemm_5632x2048x512"] = entry("C5", [(orc.Q4_0, w5, WL.HIDDEN, x5, True)],
+                                                   f"{rows5} of 5632 rows, all 512 tokens")
+    head = per["q4_0_decode_layer"][f"{threads}_threads"]
+    return {"value": head["gbs"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "one Q4_0 decoder layer (the decode step's unit of work: 7 GEMVs, batch 1), "
+                      f"binary64 oracle, rows split over {threads} POSIX threads, median of 3",
+            "nproc": hw, "affinity_cpus": avail, "cpu_model": cpu_model(), "per_config": per}
 
 
 if __name__ == "__main__":

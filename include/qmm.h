@@ -353,6 +353,38 @@ QMM_API size_t qmm_record_size(int32_t type);
 QMM_API int qmm_records_to_rows(const void *records, qmm_tensor *dst_q, void *stream);
 QMM_API int qmm_rows_to_records(const qmm_tensor *src_q, void *records, void *stream);
 
+/* ---- Measurement helpers: context for the MUL_MAT figures, not part of
+ * the operation.  Inference is bound by memory bandwidth ("No Python!
+ * Building an AI Inference Engine Exclusively in C++", §9), so a decode GEMV
+ * of B bytes is judged against what one launch can stream of B bytes at all;
+ * the matrix-core peak assumes a shader clock, measured here under load. */
+
+/* Streaming read: `workgroups` workgroups of 256 threads read the `bytes`
+ * bytes at device address src with 128-bit loads (grid-stride, two batches
+ * of four loads per thread in flight) and write one 32-bit xor of what each
+ * read to sink[0 .. workgroups-1] (device memory), so that no load can be
+ * elided.  bytes: a multiple of 16 below 2^31 (else QMM_ERR_SHAPE /
+ * QMM_ERR_UNSUPPORTED); src 16-byte aligned (QMM_ERR_LAYOUT);
+ * 1 <= workgroups <= 65536 (QMM_ERR_SHAPE); NULL src (bytes > 0) or sink:
+ * QMM_ERR_NULL.  Asynchronous on `stream`. */
+QMM_API int qmm_stream_read(const void *src, size_t bytes, uint32_t *sink, int32_t workgroups, void *stream);
+
+/* Shader-clock probe: `workgroups` workgroups of four waves each run
+ * `iters` rounds of a dependent chain (mode 0: sixteen binary32 FMA chains
+ * per lane; mode 1: four bf16 32x32x16 matrix-instruction chains per wave)
+ * and write, per wave w, out[2w] = the shader-clock counter's delta
+ * (s_memtime) and out[2w+1] = the constant-rate counter's delta
+ * (s_memrealtime) over the chain.  The shader clock is
+ * out[2w] / out[2w+1] times the constant counter's rate (the device's wall
+ * clock rate).  out: device memory of 8 * workgroups uint64 (QMM_ERR_NULL if
+ * NULL); 1 <= workgroups <= 65536, iters >= 1, mode 0 or 1 (else
+ * QMM_ERR_SHAPE). */
+QMM_API int qmm_clock_probe(uint64_t *out, int32_t workgroups, int32_t iters, int32_t mode, void *stream);
+
+/* Rate of the constant-rate counter of the current device in kHz (the HIP
+ * device attribute WallClockRate), or QMM_ERR_DEVICE if it cannot be read. */
+QMM_API int64_t qmm_wall_clock_khz(void);
+
 /* Static text for a qmm_status value (never NULL).  Every call reports
  * failure as a status code that the caller checks, as the calls of "A
  * Complete Guide to llama.cpp and Customization with C++", §5.2-§5.4 do;

@@ -28,6 +28,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qmm_oracle.c")
+_SRC_TIMING = os.path.join(_HERE, "oracle_timing.c")
 _SO = os.environ.get("QMM_ORACLE_LIB") or os.path.join(_HERE, "libqmm_oracle.so")
 
 # Own type numbering (mirrors qmm_oracle.h, not the GPU library's enum).
@@ -42,7 +43,7 @@ CFLAGS = ["-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
 def build(out: str = _SO) -> str:
     """Compile the oracle with gcc (plain -O2, contraction off, no fast-math)."""
     tmp = out + ".tmp"
-    subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+    subprocess.run(["gcc", *CFLAGS, _SRC, _SRC_TIMING, "-o", tmp, "-lm", "-lpthread"], check=True)
     os.replace(tmp, out)
     return out
 
@@ -105,6 +106,10 @@ def lib() -> ctypes.CDLL:
         h.orc_rows_to_records.restype = ci
         h.orc_records_to_rows.argtypes = [ci, u8p, i64, i64, u8p, sz]
         h.orc_records_to_rows.restype = ci
+        h.orc_time_mul_mat.argtypes = [ci, u8p, sz, i64, i64, vp, ci, i64, ci, ci, f64p, f64p]
+        h.orc_time_mul_mat.restype = ctypes.c_double
+        h.orc_online_cpus.argtypes = []
+        h.orc_online_cpus.restype = ci
         h.orc_swish.argtypes = [ctypes.c_double]
         h.orc_swish.restype = ctypes.c_double
         h.orc_swiglu_n.argtypes = [f64p, f64p, f64p, sz]
@@ -343,3 +348,27 @@ def mul_mat_q8act(type_: int, packed, K: int, xq, rows: tuple[int, int] | None =
     if rc != 0:
         raise ValueError("orc_mul_mat_q8act_rows rejected its arguments")
     return y, a
+
+
+# ---- timing (the CPU baseline) ---------------------------------------------
+
+def online_cpus() -> int:
+    return int(lib().orc_online_cpus())
+
+
+def time_mul_mat(type_: int, packed, K: int, x, *, threads: int, reps: int = 3,
+                 x_bf16_bits: bool = False) -> float:
+    """Median wall seconds of `reps` runs of the oracle's MUL_MAT over all
+    rows of packed, rows split over `threads` POSIX threads."""
+    packed = _c(packed, np.uint8)
+    M, pitch = packed.shape
+    xa, xt = _x_args(x, x_bf16_bits)
+    N = xa.shape[0]
+    y = np.zeros((N, M), np.float64)
+    a = np.zeros((N, M), np.float64)
+    t = lib().orc_time_mul_mat(type_, _ptr(packed, ctypes.c_uint8), pitch, K, M,
+                               xa.ctypes.data_as(ctypes.c_void_p), xt, N, threads, reps,
+                               _ptr(y, ctypes.c_double), _ptr(a, ctypes.c_double))
+    if t < 0:
+        raise ValueError("orc_time_mul_mat rejected its arguments")
+    return float(t)

@@ -158,6 +158,17 @@ double orc_swish(double z);
 /* h[i] = Swish(g[i]) * u[i] for i < n.                                      */
 void orc_swiglu_n(const double *g, const double *u, double *h, size_t n);
 
+/* ---- timing (oracle_timing.c): the CPU baseline ------------------------
+ * Median wall time (seconds) of `reps` runs of orc_mul_mat_rows over all M
+ * rows (x_type as there, w_to_bf16 = 0), the rows split statically into
+ * `threads` contiguous ranges on as many POSIX threads; y and a (N x M) as
+ * orc_mul_mat_rows fills them.  -1 on bad arguments.                        */
+double orc_time_mul_mat(int type, const uint8_t *w, size_t pitch, int64_t K, int64_t M,
+                        const void *x, int x_type, int64_t N, int threads, int reps,
+                        double *y, double *a);
+/* Online CPUs of the host (sysconf), the hardware thread count.            */
+int orc_online_cpus(void);
+
 #ifdef __cplusplus
 }
 #endif

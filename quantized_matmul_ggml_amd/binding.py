@@ -29,7 +29,7 @@ NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTS = ("qmm_row_size", "qmm_quantize", "qmm_quantize_rule", "qmm_dequantize", "qmm_gemv", "qmm_gemv_batch",
            "qmm_gemv_swiglu", "qmm_gemm", "qmm_gemm_ws", "qmm_gemm_noalloc", "qmm_gemm_workspace_size", "qmm_gemm_batch", "qmm_gemm_swiglu", "qmm_record_size", "qmm_records_to_rows",
-           "qmm_rows_to_records", "qmm_strerror")
+           "qmm_rows_to_records", "qmm_stream_read", "qmm_clock_probe", "qmm_wall_clock_khz", "qmm_strerror")
 GEMV_BATCH_MAX = 8
 
 
@@ -101,6 +101,14 @@ def lib() -> ctypes.CDLL:
         h.qmm_gemv_batch.restype = ctypes.c_int
         for f in ("qmm_quantize", "qmm_dequantize", "qmm_gemv", "qmm_gemm"):
             getattr(h, f).restype = ctypes.c_int
+        h.qmm_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32,
+                                      ctypes.c_void_p]
+        h.qmm_stream_read.restype = ctypes.c_int
+        h.qmm_clock_probe.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_void_p]
+        h.qmm_clock_probe.restype = ctypes.c_int
+        h.qmm_wall_clock_khz.argtypes = []
+        h.qmm_wall_clock_khz.restype = ctypes.c_int64
         h.qmm_strerror.argtypes = [ctypes.c_int]
         h.qmm_strerror.restype = ctypes.c_char_p
         _lib = h
@@ -405,3 +413,30 @@ def call_raw(name: str, *descs: QmmTensor, stream: int = 0) -> int:
     """Call an entry point with hand-made descriptors; returns the status."""
     fn = getattr(lib(), name)
     return fn(*[ctypes.byref(d) if d is not None else None for d in descs], ctypes.c_void_p(stream))
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, *, nbytes: int | None = None, workgroups: int = 1024,
+                stream=None) -> None:
+    """qmm_stream_read over the first nbytes (default: all) of the device
+    tensor src; sink: an int32 device tensor of at least `workgroups` words."""
+    _need_gpu(src, sink)
+    n = src.numel() * src.element_size() if nbytes is None else nbytes
+    if sink.numel() * sink.element_size() < 4 * workgroups:
+        raise ValueError("sink holds fewer words than workgroups")
+    _check(lib().qmm_stream_read(ctypes.c_void_p(src.data_ptr()), ctypes.c_size_t(n),
+                                 ctypes.c_void_p(sink.data_ptr()), workgroups, _stream(stream)),
+           "qmm_stream_read")
+
+
+def clock_probe(workgroups: int = 256, iters: int = 20000, mode: int = 0) -> float:
+    """Shader clock in MHz under a dependent chain on every wave (mode 0:
+    binary32 FMAs, mode 1: bf16 matrix instructions), from the device's
+    shader-clock and constant-rate counters; synchronizes."""
+    out = torch.zeros(8 * workgroups, dtype=torch.int64, device="cuda")
+    _check(lib().qmm_clock_probe(ctypes.c_void_p(out.data_ptr()), workgroups, iters, mode, _stream(None)),
+           "qmm_clock_probe")
+    d = out.view(-1, 2).cpu()
+    wall_khz = int(lib().qmm_wall_clock_khz())
+    if wall_khz <= 0:
+        raise QmmError(wall_khz, "qmm_wall_clock_khz")
+    return float(d[:, 0].sum()) / float(d[:, 1].sum()) * wall_khz / 1e3

@@ -696,6 +696,11 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float *ws, uint64_
     }
 }
 
+
+constexpr int kMinSplitSteps = SCALE_GROUP_STEPS;   // K-steps of the shortest range (512 of K)
+
+}  // namespace
+
 // Compute units of the current device (queried once per device).
 int device_cus()
 {
@@ -711,10 +716,6 @@ int device_cus()
     if (dev < 64) cus[dev].store(n, std::memory_order_relaxed);
     return n;
 }
-
-constexpr int kMinSplitSteps = SCALE_GROUP_STEPS;   // K-steps of the shortest range (512 of K)
-
-}  // namespace
 
 GemmPlan gemm_plan(int64_t M, int64_t K, int64_t N, uint64_t ws_bytes)
 {

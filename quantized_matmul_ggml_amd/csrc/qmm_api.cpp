@@ -484,6 +484,31 @@ int qmm_gemm_noalloc(const qmm_tensor *w, const qmm_tensor *x, qmm_tensor *y, si
                                       static_cast<hipStream_t>(stream)));
 }
 
+int qmm_stream_read(const void *src, size_t bytes, uint32_t *sink, int32_t workgroups, void *stream)
+{
+    if (!sink || (bytes > 0 && !src)) return QMM_ERR_NULL;
+    if (bytes % 16 != 0 || workgroups < 1 || workgroups > 65536) return QMM_ERR_SHAPE;
+    if (bytes >= (1ull << 31)) return QMM_ERR_UNSUPPORTED;
+    if ((uintptr_t)src % 16 != 0) return QMM_ERR_LAYOUT;
+    return status_of(qmm::launch_stream_read(src, bytes, sink, workgroups, static_cast<hipStream_t>(stream)));
+}
+
+int qmm_clock_probe(uint64_t *out, int32_t workgroups, int32_t iters, int32_t mode, void *stream)
+{
+    if (!out) return QMM_ERR_NULL;
+    if (workgroups < 1 || workgroups > 65536 || iters < 1 || (mode != 0 && mode != 1)) return QMM_ERR_SHAPE;
+    return status_of(qmm::launch_clock_probe(out, workgroups, iters, mode, static_cast<hipStream_t>(stream)));
+}
+
+int64_t qmm_wall_clock_khz(void)
+{
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return QMM_ERR_DEVICE;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+        return QMM_ERR_DEVICE;
+    return khz;
+}
+
 const char *qmm_strerror(int status)
 {
     switch (status) {

@@ -58,6 +58,7 @@ struct GemvConfig {
     int ks;    // waves sharing one row (1, 2 or 4)
     int cpl;   // 16-byte code chunks per lane (1, 2, 4 or 8)
     int u;     // rows per wave group per iteration
+    int wgw;   // waves per workgroup (4 or 16)
 };
 
 // Fills cfg and returns true when the register-resident GEMV supports the
@@ -121,6 +122,14 @@ hipError_t launch_gemv_swiglu(const WeightView &wg, const WeightView &wu, const 
 // passes that add to y.
 bool gemv_mf_supported(const GemvTask *tasks, int count);
 hipError_t launch_gemv_mf(const GemvTask *tasks, int count, hipStream_t stream);
+// Measurement kernels (probe.hip): a streaming read of `bytes` (multiple of
+// 16, < 2^31) by `workgroups` workgroups of 256 threads, one xor word per
+// workgroup into sink; and the clock probe (workgroups x 4 waves, each
+// writing its shader-clock and constant-counter deltas to out).
+hipError_t launch_stream_read(const void *src, uint64_t bytes, uint32_t *sink, int workgroups, hipStream_t stream);
+hipError_t launch_clock_probe(uint64_t *out, int workgroups, int iters, int mode, hipStream_t stream);
+// Compute units of the current device (queried once per device; gemm.hip).
+int device_cus();
 // Device address of the library's static scratch array on the current
 // device (QMM_NOALLOC_SCRATCH_BYTES, 256-byte aligned; gemm.hip), looked up
 // once per device.

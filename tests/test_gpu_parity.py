@@ -249,6 +249,11 @@ GEMV_CASES = [
     ("Q4_0", 8200, 2048, 3), ("Q8_0", 8195, 1024, 4),
     # K beyond 128 blocks: passes that add to y (Wdown's K = 5632; four passes)
     ("Q4_0", 300, 5632, 6), ("Q8_0", 77, 16384, 5),
+    # the streaming kernel (F16 rows; two tokens; Q8_0 over 8192 rows at one
+    # token) with ragged groups and grids, and shapes past its limits that
+    # stay on the other kernel (more than 8 row groups per wave; wide rows)
+    ("Q8_0", 9001, 2048, 1), ("Q8_0", 70001, 512, 1), ("F16", 4097, 1024, 2), ("F16", 33, 4096, 1),
+    ("Q4_0", 4099, 4096, 2), ("Q8_0", 8193, 2048, 2), ("F16", 70001, 256, 1),
     # 64-weight blocks (one scale per two 32-code runs)
     ("Q4_B64", 5632, 2048, 1), ("Q8_B64", 300, 5632, 3), ("Q4_B64", 100, 192, 8), ("Q8_B64", 4099, 2048, 2),
     ("Q4_B64", 64, 16384, 5), ("Q8_B64", 1, 64, 1), ("Q4_B64", 8200, 2048, 4),
