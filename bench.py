@@ -260,6 +260,7 @@ def main():
                        + ceiling(gemv_bytes(lm, 1))["us"])
     asym = ceiling(1 << 30)
     clocks = clock_leg(Q)
+    inner = block_gemm_probe_leg(Q)
     rec = stored_kernel_record()
 
     result = {
@@ -290,6 +291,7 @@ def main():
                 "frac_of_it": round(step_ceiling_us / (ms * 1e3), 4)},
             "read_ceiling_1gib_gbs": asym["gbs"],
             "sclk_mhz_under_load": clocks,
+            "block_gemm_inner_loop": inner,
             "wall_s_timed_region": round(wall, 4),
             "variants": {k: {"us": round(v["ms"] * 1e3, 1), "gbs": round(v["gbs"], 1),
                              "launches": v["launches"], "tokens_per_s": round(1e3 / v["ms"], 1)}
@@ -472,6 +474,30 @@ def clock_leg(Q):
          "mfma_mhz": round(Q.clock_probe(workgroups=cus, iters=20000, mode=1), 1)}
     log(f"shader clock under load: VALU {r['valu_mhz']} MHz, bf16 MFMA {r['mfma_mhz']} MHz")
     return r
+
+
+def block_gemm_probe_leg(Q):
+    """The inner loop of a block-quantized GEMM on the matrix cores (libqmm's
+    probe, one and two waves per SIMD on every CU): per round four 32 x 32
+    output tiles each advance by one 32-block of K, with bf16 operands
+    (scale already in the weights) or int8 operands whose int32 tiles are
+    rescaled per block on the vector ALUs (by the weight scale, or by the
+    weight and the activation scale).  The int8 route's cap for a prefill
+    GEMM over Q8_0 activations."""
+    import torch
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    out = {}
+    for mode, name in ((2, "bf16"), (3, "int8_weight_scale"), (4, "int8_weight_and_activation_scale")):
+        row = {}
+        for wps in (1, 2):
+            Q.mfma_probe(mode, workgroups=cus * wps, iters=200)
+            r = Q.mfma_probe(mode, workgroups=cus * wps, iters=4000)
+            row[f"{wps}_wave_per_simd"] = {"cycles_per_round_per_wave": round(r["cycles_per_round"], 1),
+                                           "simd_cycles_per_round": round(r["cycles_per_round"] / wps, 1)}
+        row["tflops_1_wave_per_simd"] = round(Q.mfma_probe(mode, workgroups=cus, iters=4000)["tflops"], 1)
+        out[name] = row
+        log(f"block-GEMM inner loop {name}: {row}")
+    return out
 
 
 def prefill_leg(Q, WL, dev, args):

@@ -103,7 +103,10 @@ typedef enum {
  *    F32 activations and outputs need 4-byte alignment of data and nb[1];
  *    BF16 activations of qmm_gemm need 16-byte alignment of data and nb[1];
  *  - quantized ne[0] must be a multiple of 32 (64 for the _B64 types; else
- *    QMM_ERR_SHAPE). */
+ *    QMM_ERR_SHAPE);
+ *  - ne[0] and ne[1] at most 2^48, and the bytes the tensor spans
+ *    ((ne[1] - 1) nb[1] + the row size) at most 2^62 and inside the address
+ *    space from data on (else QMM_ERR_UNSUPPORTED). */
 typedef struct qmm_tensor {
     int32_t  type;     /* qmm_type                          */
     int32_t  n_dims;   /* 1 or 2                            */
@@ -113,7 +116,8 @@ typedef struct qmm_tensor {
 } qmm_tensor;
 
 /* Bytes of one packed (or dense) row of ne0 elements; 0 for an unknown type
- * or an invalid ne0 (negative, or not a multiple of the block length).
+ * or an invalid ne0 (negative, above 2^48, or not a multiple of the block
+ * length).
  * A row holds its blocks' contents as the Development Guide for Small AI
  * Models (TinyLLaMA, etc.) Using C++, §6.1 lists them (one fp16 scale per
  * block, then the block's codes), 34 bytes per 32 Q8_0 weights and 18 per
@@ -369,16 +373,23 @@ QMM_API int qmm_rows_to_records(const qmm_tensor *src_q, void *records, void *st
  * QMM_ERR_NULL.  Asynchronous on `stream`. */
 QMM_API int qmm_stream_read(const void *src, size_t bytes, uint32_t *sink, int32_t workgroups, void *stream);
 
-/* Shader-clock probe: `workgroups` workgroups of four waves each run
- * `iters` rounds of a dependent chain (mode 0: sixteen binary32 FMA chains
- * per lane; mode 1: four bf16 32x32x16 matrix-instruction chains per wave)
- * and write, per wave w, out[2w] = the shader-clock counter's delta
- * (s_memtime) and out[2w+1] = the constant-rate counter's delta
- * (s_memrealtime) over the chain.  The shader clock is
- * out[2w] / out[2w+1] times the constant counter's rate (the device's wall
- * clock rate).  out: device memory of 8 * workgroups uint64 (QMM_ERR_NULL if
- * NULL); 1 <= workgroups <= 65536, iters >= 1, mode 0 or 1 (else
- * QMM_ERR_SHAPE). */
+/* Shader-clock and matrix-core probe: `workgroups` workgroups of four waves
+ * each run `iters` rounds of a chain and write, per wave w, out[2w] = the
+ * shader-clock counter's delta (s_memtime) and out[2w+1] = the
+ * constant-rate counter's delta (s_memrealtime) over the chain.  The shader
+ * clock is out[2w] / out[2w+1] times the constant counter's rate (the
+ * device's wall clock rate).  Chains: mode 0, sixteen binary32 FMA chains
+ * per lane; mode 1, four bf16 32x32x16 matrix-instruction chains per wave;
+ * modes 2-4, the inner loop of a block-quantized GEMM per round: four
+ * 32 x 32 output tiles each advanced by one 32-block of K ("A Complete Guide
+ * to llama.cpp ...", §2.2: each block's integer dot product is scaled by
+ * Delta_w * Delta_x before blocks are added), with bf16 operands and the
+ * scale already in the weights (mode 2), or int8 operands and the block's
+ * int32 tile converted and scaled on the vector ALUs, by the weight scale
+ * only (mode 3) or by the weight and the activation scale (mode 4).  Each
+ * round is 4 * 32 * 32 * 32 multiply-adds per wave.  out: device memory of
+ * 8 * workgroups uint64 (QMM_ERR_NULL if NULL); 1 <= workgroups <= 65536,
+ * iters >= 1, 0 <= mode <= 4 (else QMM_ERR_SHAPE). */
 QMM_API int qmm_clock_probe(uint64_t *out, int32_t workgroups, int32_t iters, int32_t mode, void *stream);
 
 /* Rate of the constant-rate counter of the current device in kHz (the HIP

@@ -8,10 +8,10 @@ streams.
 from .binding import (BF16, F16, F32, Q4_0, Q4_B64, Q8_0, Q8_B64, QUANT_DEFAULT, QUANT_Q4_AMAX7, QmmError, Weight,
                       dequantize, f16_weight,
                       gemm, gemm_batch, gemm_noalloc, gemm_swiglu, gemm_workspace_size, gemv, gemv_batch, gemv_swiglu, quantize, record_size,
-                      records_to_rows, stream_read, clock_probe,
+                      records_to_rows, stream_read, clock_probe, mfma_probe,
                       row_size, rows_to_records, strerror)
 
 __all__ = ["BF16", "F16", "F32", "Q4_0", "Q4_B64", "Q8_0", "Q8_B64", "QUANT_DEFAULT", "QUANT_Q4_AMAX7", "QmmError",
            "Weight", "dequantize",
            "f16_weight", "gemm", "gemm_batch", "gemm_noalloc", "gemm_swiglu", "gemm_workspace_size", "gemv", "gemv_batch", "gemv_swiglu", "quantize", "record_size",
-           "records_to_rows", "stream_read", "clock_probe", "row_size", "rows_to_records", "strerror"]
+           "records_to_rows", "stream_read", "clock_probe", "mfma_probe", "row_size", "rows_to_records", "strerror"]

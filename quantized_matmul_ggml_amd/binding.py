@@ -440,3 +440,19 @@ def clock_probe(workgroups: int = 256, iters: int = 20000, mode: int = 0) -> flo
     if wall_khz <= 0:
         raise QmmError(wall_khz, "qmm_wall_clock_khz")
     return float(d[:, 0].sum()) / float(d[:, 1].sum()) * wall_khz / 1e3
+
+
+def mfma_probe(mode: int, workgroups: int = 256, iters: int = 4000) -> dict:
+    """The block-GEMM inner-loop probe (qmm_clock_probe modes 2-4) on every
+    CU: multiply-add rate in TFLOP/s over the waves' own clocks, and shader
+    clock cycles per round (four 32 x 32 x 32 tile-blocks) per wave."""
+    out = torch.zeros(8 * workgroups, dtype=torch.int64, device="cuda")
+    _check(lib().qmm_clock_probe(ctypes.c_void_p(out.data_ptr()), workgroups, iters, mode, _stream(None)),
+           "qmm_clock_probe")
+    d = out.view(-1, 2).cpu().double()
+    wall_khz = int(lib().qmm_wall_clock_khz())
+    if wall_khz <= 0:
+        raise QmmError(wall_khz, "qmm_wall_clock_khz")
+    seconds = float(d[:, 1].mean()) / (wall_khz * 1e3)
+    flops = 4.0 * workgroups * iters * 4 * 2 * 32 * 32 * 32
+    return {"tflops": flops / seconds / 1e12, "cycles_per_round": float(d[:, 0].mean()) / iters}

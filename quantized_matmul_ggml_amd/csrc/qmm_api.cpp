@@ -37,6 +37,12 @@ int64_t elem_size(int t)
     }
 }
 
+// Largest element count per dimension and byte span of one tensor the
+// library accepts (far beyond any device memory, and small enough that
+// every size computed from them fits 64 bits).
+constexpr int64_t kMaxElems = (int64_t)1 << 48;
+constexpr uint64_t kMaxSpan = 1ull << 62;
+
 // Shape / layout rules shared by every operand.  `align` is the byte
 // alignment required of data and nb[1].
 int check_tensor(const qmm_tensor *t, uint64_t align)
@@ -46,6 +52,7 @@ int check_tensor(const qmm_tensor *t, uint64_t align)
     if (t->n_dims < 1 || t->n_dims > 4) return QMM_ERR_UNSUPPORTED;
     if (t->n_dims > 2 || t->ne[2] != 1 || t->ne[3] != 1) return QMM_ERR_UNSUPPORTED;
     if (t->ne[0] < 0 || t->ne[1] < 0) return QMM_ERR_SHAPE;
+    if (t->ne[0] > kMaxElems || t->ne[1] > kMaxElems) return QMM_ERR_UNSUPPORTED;
     if (t->n_dims == 1 && t->ne[1] != 1) return QMM_ERR_SHAPE;
     if (is_quant(t->type)) {
         if (t->ne[0] % block_len(t->type) != 0) return QMM_ERR_SHAPE;
@@ -56,6 +63,15 @@ int check_tensor(const qmm_tensor *t, uint64_t align)
     const uint64_t rs = qmm_row_size(t->type, t->ne[0]);
     if (t->ne[1] > 1 && t->nb[1] < rs) return QMM_ERR_LAYOUT;
     if (t->ne[1] > 1 && t->nb[1] % align != 0) return QMM_ERR_LAYOUT;
+    // the bytes the tensor spans must be a range of the address space
+    uint64_t span = rs;
+    if (t->ne[1] > 1) {
+        uint64_t rows;
+        if (__builtin_mul_overflow((uint64_t)(t->ne[1] - 1), t->nb[1], &rows) || rows > kMaxSpan)
+            return QMM_ERR_UNSUPPORTED;
+        span = rows + rs;
+    }
+    if (span > kMaxSpan || (uintptr_t)t->data > UINTPTR_MAX - span) return QMM_ERR_UNSUPPORTED;
     const bool empty = t->ne[0] == 0 || t->ne[1] == 0;
     if (!t->data && !empty) return QMM_ERR_NULL;
     if ((uintptr_t)t->data % align != 0) return QMM_ERR_LAYOUT;
@@ -124,7 +140,7 @@ extern "C" {
 
 size_t qmm_row_size(int32_t type, int64_t ne0)
 {
-    if (ne0 < 0) return 0;
+    if (ne0 < 0 || ne0 > kMaxElems) return 0;
     const uint64_t k = (uint64_t)ne0;
     auto a16 = [](uint64_t v) { return (v + 15) / 16 * 16; };
     switch (type) {
@@ -328,8 +344,9 @@ int check_records(const qmm_tensor *q, const void *records, uint64_t *bytes)
     int rc = check_tensor(q, 16);
     if (rc) return rc;
     if (q->type != QMM_TYPE_Q8_0 && q->type != QMM_TYPE_Q4_0) return QMM_ERR_TYPE;
-    const int64_t blocks = q->ne[1] * (q->ne[0] / 32);
-    if (blocks >= (1ll << 31)) return QMM_ERR_UNSUPPORTED;
+    int64_t blocks;
+    if (__builtin_mul_overflow(q->ne[1], q->ne[0] / 32, &blocks) || blocks >= (1ll << 31))
+        return QMM_ERR_UNSUPPORTED;
     *bytes = (uint64_t)blocks * (uint64_t)qmm::record_size(q->type);
     if (*bytes == 0) return QMM_OK;
     if (!records) return QMM_ERR_NULL;
@@ -496,7 +513,7 @@ int qmm_stream_read(const void *src, size_t bytes, uint32_t *sink, int32_t workg
 int qmm_clock_probe(uint64_t *out, int32_t workgroups, int32_t iters, int32_t mode, void *stream)
 {
     if (!out) return QMM_ERR_NULL;
-    if (workgroups < 1 || workgroups > 65536 || iters < 1 || (mode != 0 && mode != 1)) return QMM_ERR_SHAPE;
+    if (workgroups < 1 || workgroups > 65536 || iters < 1 || mode < 0 || mode > 4) return QMM_ERR_SHAPE;
     return status_of(qmm::launch_clock_probe(out, workgroups, iters, mode, static_cast<hipStream_t>(stream)));
 }
 

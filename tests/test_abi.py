@@ -402,3 +402,21 @@ def test_64_block_types_reject(qmm_lib):
     assert call(B.make_desc(B.F32, 2048, 64, 8192, X_ADDR), B.make_desc(B.Q8_B64, 2048, 64, 2112, W_ADDR), 1) == B.ERR_TYPE
     # a pitch below the 64-block row size
     assert B.call_raw("qmm_gemv", B.make_desc(B.Q4_B64, 2048, 64, 1072, W_ADDR), _x(), _y()) == B.ERR_LAYOUT
+
+
+@no_gpu
+def test_sizes_beyond_the_address_space_are_refused(qmm_lib):
+    """Element counts above 2^48, spans that overflow 64 bits or wrap the
+    address space: QMM_ERR_UNSUPPORTED before any arithmetic can overflow."""
+    assert qmm_lib.row_size(B.Q4_0, 1 << 49) == 0 and qmm_lib.row_size(B.F32, 1 << 50) == 0
+    x, y = _x(), _y()
+    huge_rows = _w(M=1 << 50)
+    assert B.call_raw("qmm_gemv", huge_rows, x, y) == B.ERR_UNSUPPORTED
+    wide_pitch = _w(M=1 << 20, pitch=1 << 47)          # (M - 1) * nb[1] beyond 2^62
+    assert B.call_raw("qmm_gemv", wide_pitch, x, y) == B.ERR_UNSUPPORTED
+    wrapping = _w(addr=(1 << 64) - 4096)               # the span runs past the top of the address space
+    assert B.call_raw("qmm_gemv", wrapping, x, y) == B.ERR_UNSUPPORTED
+    # 2^31 blocks: the record count is refused, not overflowed
+    rec = B.lib().qmm_rows_to_records(ctypes.byref(_w(K=1 << 20, M=1 << 16)),
+                                      ctypes.c_void_p(BASE + (1 << 46)), None)
+    assert rec == B.ERR_UNSUPPORTED
