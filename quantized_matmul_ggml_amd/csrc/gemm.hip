@@ -228,8 +228,18 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
     // Workgroup b takes K range b % n_splits of tile b / n_splits: steps
     // s0 .. s0 + steps - 1 of K.  Every offset below is relative to s0, and
     // nblk counts the 32-blocks of K from block 2 s0 on.
-    const int split = __builtin_amdgcn_readfirstlane((int)blockIdx.x % a.n_splits);
-    const int btile = __builtin_amdgcn_readfirstlane((int)blockIdx.x / a.n_splits);
+    // Workgroups are handed to the chip's eight XCDs in turn (workgroup b to
+    // XCD b mod 8), each XCD with its own L2.  Renumber them so that XCD x
+    // runs a contiguous run of the launch's (tile, range) order: the token
+    // tiles of one weight tile, which read the same weight rows, then share
+    // that XCD's L2 instead of fetching the rows once per XCD.
+    int wgi = (int)blockIdx.x;
+    {
+        const int nwg = (int)gridDim.x, x = wgi % 8, i = wgi / 8, q = nwg / 8, r = nwg % 8;
+        wgi = x * q + (x < r ? x : r) + i;
+    }
+    const int split = __builtin_amdgcn_readfirstlane(wgi % a.n_splits);
+    const int btile = __builtin_amdgcn_readfirstlane(wgi / a.n_splits);
     // the item owning the tile: the last whose first tile is not past it
     int item = 0;
     for (int i = 1; i < a.n_items; ++i)
