@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqmm.so")
 SOURCES = ["qmm_api.cpp", "quant.hip", "gemv.hip", "gemv_i8.hip", "gemv_mf.hip",
-           "gemm.hip", "records.hip", "probe.hip"]
+           "gemm.hip", "gemm_rq.hip", "records.hip", "probe.hip"]
 ARCH = os.environ.get("QMM_OFFLOAD_ARCH", "gfx950")
 
 

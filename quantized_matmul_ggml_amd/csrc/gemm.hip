@@ -1,5 +1,10 @@
 // gemm.hip -- prefill GEMM: block-quantized weights x bf16 activations -> fp32.
 //
+// This file holds the launch planning (K split, batches), the split-K slab
+// sum, and the producer/consumer kernel below, which serves F16 weights and
+// the fused gate/up SwiGLU pair; single Q4_0 / Q8_0 products and their
+// batches run on the register-dequantizing kernel of gemm_rq.hip.
+//
 // Y[n][m] = sum_k W'[m][k] * X[n][k] for many tokens at once (No Python!
 // Building an AI Inference Engine Exclusively in C++, §6: C_ij = sum_k A_ik B_kj;
 // §6.1: tile the matrices, repack tiles so the inner loop reads contiguous
@@ -34,7 +39,7 @@
 //    whose tiles form one grid (a workgroup finds its item by tile index);
 //  * the gate/up pair with the SwiGLU epilogue (SW): 64 rows of each matrix
 //    per tile, combined in LDS after the last step.
-#include "qmm_internal.h"
+#include "gemm_common.h"
 
 #include <atomic>
 #include <mutex>
@@ -43,11 +48,6 @@
 namespace qmm {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 128;                   // weight rows per tile
 constexpr int BN = 128;                   // tokens per tile
@@ -64,41 +64,6 @@ constexpr int W_PAIRS = 4;                // pairs of K-steps of weight codes in
 static_assert(2 * W_PAIRS == SCALE_GROUP_STEPS, "the producer loop unrolls over both with one index");
 constexpr int F16_PAIRS = 2;              // pairs of K-steps of F16 weights in flight (4x the bytes of Q4_0)
 constexpr int THREADS = 512;
-constexpr int kMaxGemmItems = QMM_GEMM_BATCH_MAX;
-
-// One product of a launch (several share one launch in a batch): its
-// weights, tokens and output, and the first tile index it owns.
-struct GemmItem {
-    const uint8_t *w;
-    uint64_t pitch;
-    int64_t M;
-    const uint16_t *x;      // bf16 bits, row n at x + n * x_pitch
-    uint64_t x_pitch;
-    float *y;               // the output, or the first partial-sum slab
-    uint64_t y_pitch;
-    const uint8_t *w2;      // fused SwiGLU launches: the up projection (w is the gate)
-    uint64_t pitch2;
-    int tile_begin;
-    int pad;
-};
-
-struct GemmArgs {
-    int64_t K;              // shared by the items, like the type, N and qoff
-    int64_t qoff;
-    int64_t N;
-    int n_tiles;            // token tiles
-    int n_splits;           // K ranges per tile (1: the whole K)
-    int split_steps;        // K-steps per range, a multiple of SCALE_GROUP_STEPS
-    int n_items;
-    uint64_t split_stride;  // floats between the slabs of consecutive ranges
-    GemmItem item[kMaxGemmItems];
-};
-
-// Round two floats to bf16 (nearest even) in one v_cvt_pk_bf16_f32.
-__device__ inline uint32_t pack_bf16(float lo, float hi)
-{
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
-}
 
 // One producer lane's share of a K-step: one 32-block of one weight row.
 template <int WT>
@@ -107,18 +72,6 @@ struct WBlock {
     u32x4 q[QV];
     uint16_t s;
 };
-
-// (a & m) | c in one VALU op (written out: the compiler splits it, since a
-// gfx9 VOP3 takes no literal and c must sit in a register).
-__device__ inline uint32_t and_or(uint32_t a, uint32_t m, uint32_t c)
-{
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(c));
-    return r;
-}
-
-__device__ inline float lo_half(uint32_t p) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(p & 0xFFFFu)); }
-__device__ inline float hi_half(uint32_t p) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(p >> 16)); }
 
 // Dequantize one 32-block to 32 bf16 values in k order, two per dword.
 // (code - offset) * d is exact in fp32 (at most 19 significant bits), so each
@@ -161,16 +114,6 @@ __device__ inline void dequant_block(const WBlock<WT> &st, uint32_t out[16])
             out[2 * i] = pack_bf16(fmaf(lo_half(p0), d, nd), fmaf(lo_half(p1), d, nd));
             out[2 * i + 1] = pack_bf16(fmaf(hi_half(p0), d, nd), fmaf(hi_half(p1), d, nd));
         }
-    }
-}
-
-// Calls f(std::integral_constant<int, 0>{}) .. f(std::integral_constant<int, N-1>{}).
-template <int N, int I = 0, class F>
-__device__ inline void static_for(F &&f)
-{
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<N, I + 1>(f);
     }
 }
 
@@ -228,16 +171,8 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
     // Workgroup b takes K range b % n_splits of tile b / n_splits: steps
     // s0 .. s0 + steps - 1 of K.  Every offset below is relative to s0, and
     // nblk counts the 32-blocks of K from block 2 s0 on.
-    // Workgroups are handed to the chip's eight XCDs in turn (workgroup b to
-    // XCD b mod 8), each XCD with its own L2.  Renumber them so that XCD x
-    // runs a contiguous run of the launch's (tile, range) order: the token
-    // tiles of one weight tile, which read the same weight rows, then share
-    // that XCD's L2 instead of fetching the rows once per XCD.
-    int wgi = (int)blockIdx.x;
-    {
-        const int nwg = (int)gridDim.x, x = wgi % 8, i = wgi / 8, q = nwg / 8, r = nwg % 8;
-        wgi = x * q + (x < r ? x : r) + i;
-    }
+    // (in the XCD-contiguous order of xcd_order_index)
+    const int wgi = xcd_order_index();
     const int split = __builtin_amdgcn_readfirstlane(wgi % a.n_splits);
     const int btile = __builtin_amdgcn_readfirstlane(wgi / a.n_splits);
     // the item owning the tile: the last whose first tile is not past it
@@ -814,14 +749,10 @@ hipError_t launch_items(const WeightView *w, const ActView *x, const OutView *y,
     if (blocks == 0) return hipSuccess;
     const WeightView &w0 = w[0];
     hipError_t e = hipErrorInvalidValue;
-    if (w0.scale_shift) {
-        if (w0.type == W_Q4_0) e = launch_typed<W_Q4_0, 1>(a, blocks, stream);
-        else if (w0.type == W_Q8_0) e = launch_typed<W_Q8_0, 1>(a, blocks, stream);
-    } else {
-        if (w0.type == W_Q4_0) e = launch_typed<W_Q4_0, 0>(a, blocks, stream);
-        else if (w0.type == W_Q8_0) e = launch_typed<W_Q8_0, 0>(a, blocks, stream);
-        else if (w0.type == W_F16) e = launch_typed<W_F16, 0>(a, blocks, stream);
-    }
+    // quantized weights: the register-dequantizing kernel (gemm_rq.hip);
+    // F16 weights: this file's kernel
+    if (gemm_rq_handles(w0.type)) e = launch_gemm_rq(a, blocks, w0.type, w0.scale_shift, stream);
+    else if (w0.type == W_F16 && !w0.scale_shift) e = launch_typed<W_F16, 0>(a, blocks, stream);
     if (e != hipSuccess || plan.splits == 1) return e;
     const int64_t quads = x[0].N * (plan.mp / 4);
     const int64_t want = (quads + 255) / 256;
