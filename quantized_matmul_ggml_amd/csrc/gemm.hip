@@ -751,7 +751,7 @@ hipError_t launch_items(const WeightView *w, const ActView *x, const OutView *y,
     hipError_t e = hipErrorInvalidValue;
     // quantized weights: the register-dequantizing kernel (gemm_rq.hip);
     // F16 weights: this file's kernel
-    if (gemm_rq_handles(w0.type)) e = launch_gemm_rq(a, blocks, w0.type, w0.scale_shift, stream);
+    if (gemm_rq_handles(w0.type)) e = launch_gemm_rq(a, blocks, w0.type, w0.scale_shift, false, stream);
     else if (w0.type == W_F16 && !w0.scale_shift) e = launch_typed<W_F16, 0>(a, blocks, stream);
     if (e != hipSuccess || plan.splits == 1) return e;
     const int64_t quads = x[0].N * (plan.mp / 4);
@@ -802,6 +802,7 @@ hipError_t launch_gemm_swiglu(const WeightView &wg, const WeightView &wu, const 
         it.pad = 0;
     }
     const unsigned blocks = (unsigned)((wg.M + BM / 2 - 1) / (BM / 2)) * (unsigned)a.n_tiles;
+    if (gemm_rq_handles(wg.type)) return launch_gemm_rq(a, blocks, wg.type, wg.scale_shift, true, stream);
     if (wg.scale_shift) {
         if (wg.type == W_Q4_0) return launch_typed<W_Q4_0, 1, true>(a, blocks, stream);
         if (wg.type == W_Q8_0) return launch_typed<W_Q8_0, 1, true>(a, blocks, stream);

@@ -88,8 +88,9 @@ __device__ inline int xcd_order_index()
 }
 
 // Register-dequantizing GEMM (gemm_rq.hip) for Q4_0 / Q8_0 codes, with
-// 32-weight scales (ss 0) or 64-weight scales (ss 1).
-hipError_t launch_gemm_rq(const GemmArgs &a, unsigned blocks, int type, int ss, hipStream_t stream);
+// 32-weight scales (ss 0) or 64-weight scales (ss 1); sw: the fused gate/up
+// pair (w the gate, w2 the up matrix, 64 rows of each per tile).
+hipError_t launch_gemm_rq(const GemmArgs &a, unsigned blocks, int type, int ss, bool sw, hipStream_t stream);
 bool gemm_rq_handles(int type);
 
 }  // namespace qmm

@@ -48,7 +48,7 @@ constexpr int LDS_GROUP_OFF = TS * TOK_BYTES;
 constexpr int LDS_SCALE_OFF = LDS_GROUP_OFF + NB * GROUP_BYTES;
 constexpr int LDS_BYTES = LDS_SCALE_OFF + NB * SGROUP_BYTES;
 static_assert(LDS_BYTES <= 160 * 1024, "one workgroup per CU");
-static_assert(LDS_BYTES >= 8 * 2 * 16 * 64 * 4, "the final exchange reuses the ring");
+static_assert(LDS_BYTES >= (8 * 2 * 16 * 64 + 8 * 16 * 64) * 4, "the final exchanges reuse the ring");
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -204,10 +204,22 @@ struct Deq<W_Q8_0> {
     }
 };
 
+// Swish(z) = z * sigma(z) = z / (1 + e^{-z}) in binary32 (for z far below
+// zero e^{-z} overflows and the quotient is the limit -0).
+__device__ inline float swish(float z)
+{
+    return z / (1.0f + expf(-z));
+}
+
 // BATCH: several products in one launch (a workgroup finds its item by tile
 // index); otherwise item 0 only, so that every argument is read in one round
 // of scalar loads.
-template <int WT, int SS, bool BATCH>
+// SW: the fused gate/up projection with the SwiGLU epilogue ("Development
+// Guide for Small AI Models (TinyLLaMA, etc.) Using C++", §4.4): a tile is
+// 64 rows of the gate matrix (row groups 0, 1) and the same 64 rows of the
+// up matrix (row groups 2, 3) times 128 tokens; only h = Swish(gate) * up is
+// stored.
+template <int WT, int SS, bool BATCH, bool SW>
 __global__ __launch_bounds__(THREADS) void gemm_rq_kernel(const GemmArgs a)
 {
     using Sc = RqSched<WT>;
@@ -248,7 +260,8 @@ __global__ __launch_bounds__(THREADS) void gemm_rq_kernel(const GemmArgs a)
     const int tile = btile - itm.tile_begin;
     const int mt = __builtin_amdgcn_readfirstlane(tile / a.n_tiles);
     const int nt = __builtin_amdgcn_readfirstlane(tile - mt * a.n_tiles);
-    const int64_t m0 = (int64_t)mt * BM;
+    constexpr int MROWS = SW ? BM / 2 : BM;     // matrix rows per tile
+    const int64_t m0 = (int64_t)mt * MROWS;
     const int64_t n0 = (int64_t)nt * BN;
     const int s0 = split * a.split_steps;
     const int64_t nblk = a.K / 32 - 2 * (int64_t)s0;
@@ -292,10 +305,15 @@ __global__ __launch_bounds__(THREADS) void gemm_rq_kernel(const GemmArgs a)
     // zeros), 4 lanes per row, 16 rows per load.  Rows past M read zeros;
     // groups wholly in K and the range take a scalar offset, the last
     // partial one checks each lane, and groups past it read zeros.
-    const int64_t rows = M - m0 < BM ? M - m0 : BM;
+    const int64_t rows = M - m0 < MROWS ? M - m0 : MROWS;
     const uint32_t row_bytes = (uint32_t)(a.qoff + (a.K / 32) * QB);
-    const i32x4 wres = buffer_rsrc(itm.w + (uint64_t)m0 * pitch, (uint32_t)((rows - 1) * pitch + row_bytes));
     const int cw = token_wave ? 0 : wave;
+    // fused SwiGLU: code waves 2, 3 load the up matrix into tile rows 64..127
+    const bool upper = SW && cw >= 2;
+    const uint8_t *const wm = upper ? itm.w2 : itm.w;
+    const uint64_t pm = upper ? itm.pitch2 : pitch;
+    const int lrow = upper ? BM / 2 : 0;        // tile row of the matrix's row m0
+    const i32x4 wres = buffer_rsrc(wm + (uint64_t)m0 * pm, (uint32_t)((rows - 1) * pm + row_bytes));
     const int64_t nblk_r = nblk < 2 * (int64_t)steps ? nblk : 2 * (int64_t)steps;   // blocks of the range
     const int full_groups = (int)(nblk_r / (2 * GS));
     uint32_t coff[CODE_LOADS];
@@ -303,7 +321,7 @@ __global__ __launch_bounds__(THREADS) void gemm_rq_kernel(const GemmArgs a)
     for (int i = 0; i < CODE_LOADS; ++i) {
         const int row = 8 * (CODE_LOADS * cw + i) + (lane >> 3);
         const int unit = (lane & 7) ^ ((row >> 1) & 7);
-        coff[i] = (uint32_t)(row * pitch + a.qoff) + (uint32_t)(2 * s0 * QB) + 16u * unit;
+        coff[i] = (uint32_t)((row - lrow) * pm + a.qoff) + (uint32_t)(2 * s0 * QB) + 16u * unit;
     }
     constexpr int SPG = (2 * GS) >> SS;          // scales per row and group
     uint32_t soff[SCALE_LOADS];
@@ -312,7 +330,7 @@ __global__ __launch_bounds__(THREADS) void gemm_rq_kernel(const GemmArgs a)
     for (int i = 0; i < SCALE_LOADS; ++i) {
         const int row = 16 * (SCALE_LOADS * cw + i) + (lane >> 2);
         // dwords past the group's scales read zeros in every group
-        soff[i] = 2 * sdw < SPG ? (uint32_t)(row * pitch) + 2u * (uint32_t)((2 * s0) >> SS) + 4u * sdw : OUT_OF_RANGE;
+        soff[i] = 2 * sdw < SPG ? (uint32_t)((row - lrow) * pm) + 2u * (uint32_t)((2 * s0) >> SS) + 4u * sdw : OUT_OF_RANGE;
     }
     const int64_t nscales = nblk_r >> SS;        // scales of the range
     // FAST: group g is known to be < full_groups
@@ -503,32 +521,64 @@ __global__ __launch_bounds__(THREADS) void gemm_rq_kernel(const GemmArgs a)
         for (int r = 0; r < 16; ++r) xch[((wave * 2 + jj) * 16 + r) * 64 + lane] = acc[give + jj][r];
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const float *other = xch + (wave ^ 4) * 2 * 16 * 64;
+    float fin[2][16];             // the sums of token sub-tiles keep, keep + 1
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) fin[jj][r] = acc[keep + jj][r] + other[(jj * 16 + r) * 64 + lane];
+    auto token = [&](int jj, int r) { return n0 + 32 * (keep + jj) + 8 * (r / 4) + 4 * h + (r % 4); };
+    if constexpr (SW) {
+        // Gate row group g (0, 1) and up row group g + 2 hold the same matrix
+        // rows and, for the same parity, the same tokens.  Each hands the
+        // other one token sub-tile through LDS and finishes the other one:
+        // the gate wave sub-tile keep, the up wave sub-tile keep + 1.
+        const bool gate = rg < 2;
+        float *sw = reinterpret_cast<float *>(lds) + 8 * 2 * 16 * 64;     // [wave][16][64], after xch
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sw[(wave * 16 + r) * 64 + lane] = fin[gate ? 1 : 0][r];
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const float *mate = sw + (wave ^ 2) * 16 * 64;               // row group rg ^ 2, same parity
+        const int jj = gate ? 0 : 1;
+        const int64_t m = m0 + 32 * (rg & 1) + (lane & 31);
+        if (m < M) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float g = gate ? fin[0][r] : mate[r * 64 + lane];
+                const float u = gate ? mate[r * 64 + lane] : fin[1][r];
+                const int64_t n = token(jj, r);
+                if (n < a.N) out[(uint64_t)n * y_pitch + m] = swish(g) * u;
+            }
+        }
+        return;
+    }
     const int64_t m = m0 + rl;
     if (m < M) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t n = n0 + 32 * (keep + jj) + 8 * (r / 4) + 4 * h + (r % 4);
-                const float v = acc[keep + jj][r] + other[(jj * 16 + r) * 64 + lane];
-                if (n < a.N) out[(uint64_t)n * y_pitch + m] = v;
+                const int64_t n = token(jj, r);
+                if (n < a.N) out[(uint64_t)n * y_pitch + m] = fin[jj][r];
             }
     }
 }
 
-template <int WT, int SS, bool BATCH>
+template <int WT, int SS, bool BATCH, bool SW>
 hipError_t launch_rq(const GemmArgs &a, unsigned blocks, hipStream_t stream)
 {
     constexpr int bytes = LDS_BYTES;
-    const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(&gemm_rq_kernel<WT, SS, BATCH>), bytes);
+    const hipError_t e = allow_dynamic_lds(reinterpret_cast<const void *>(&gemm_rq_kernel<WT, SS, BATCH, SW>), bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_rq_kernel<WT, SS, BATCH>), dim3(blocks), dim3(THREADS), bytes, stream, a);
+    hipLaunchKernelGGL((gemm_rq_kernel<WT, SS, BATCH, SW>), dim3(blocks), dim3(THREADS), bytes, stream, a);
     return hipGetLastError();
 }
 template <int WT, int SS>
-hipError_t launch_rq(const GemmArgs &a, unsigned blocks, hipStream_t stream)
+hipError_t launch_rq(const GemmArgs &a, unsigned blocks, bool sw, hipStream_t stream)
 {
-    return a.n_items > 1 ? launch_rq<WT, SS, true>(a, blocks, stream) : launch_rq<WT, SS, false>(a, blocks, stream);
+    if (sw) return launch_rq<WT, SS, false, true>(a, blocks, stream);
+    return a.n_items > 1 ? launch_rq<WT, SS, true, false>(a, blocks, stream)
+                         : launch_rq<WT, SS, false, false>(a, blocks, stream);
 }
 
 }  // namespace
@@ -538,10 +588,10 @@ bool gemm_rq_handles(int type)
     return type == W_Q4_0 || type == W_Q8_0;
 }
 
-hipError_t launch_gemm_rq(const GemmArgs &a, unsigned blocks, int type, int ss, hipStream_t stream)
+hipError_t launch_gemm_rq(const GemmArgs &a, unsigned blocks, int type, int ss, bool sw, hipStream_t stream)
 {
-    if (type == W_Q4_0) return ss ? launch_rq<W_Q4_0, 1>(a, blocks, stream) : launch_rq<W_Q4_0, 0>(a, blocks, stream);
-    if (type == W_Q8_0) return ss ? launch_rq<W_Q8_0, 1>(a, blocks, stream) : launch_rq<W_Q8_0, 0>(a, blocks, stream);
+    if (type == W_Q4_0) return ss ? launch_rq<W_Q4_0, 1>(a, blocks, sw, stream) : launch_rq<W_Q4_0, 0>(a, blocks, sw, stream);
+    if (type == W_Q8_0) return ss ? launch_rq<W_Q8_0, 1>(a, blocks, sw, stream) : launch_rq<W_Q8_0, 0>(a, blocks, sw, stream);
     return hipErrorInvalidValue;
 }
 
