@@ -43,13 +43,31 @@ namespace {
 // helps the former and costs the Q8_0 LM head at 2 and 4 tokens 5-7 %); the
 // same number of waves with sixteen-wave workgroups.
 inline int max_workgroups(int ks, int wgw) { return (ks == 1 ? 2048 : 1024) * 4 / wgw; }
+// Every workgroup stages all K activations of its tokens, so rows longer than
+// 4096 with two or more tokens take a smaller grid, each workgroup streaming
+// more rows per staging (measured on 2048 x 5632 Q4_0: 3 / 4 tokens 10.2 /
+// 11.2 us with the full grid, 8.2 / 8.8 us with 512 workgroups, slower again
+// with 384 or 256).
+inline int max_workgroups(int ks, int wgw, int64_t K, int nt)
+{
+    const int cap = max_workgroups(ks, wgw);
+    return (K > 4096 && nt >= 2 && cap > 512) ? 512 : cap;
+}
 constexpr int kMaxItems = QMM_GEMV_BATCH_MAX;
 // Which launches the matrix-core kernels take (measured on the decoder's
 // shapes): from 5 tokens every one; from 3 tokens those of at least 8192 rows
 // (LM head, gate/up), whose 16-row tiles occupy every CU; below that the
 // VALU kernel, whose cost per weight grows with the tokens but whose grid
 // fills the chip at any row count.
-inline bool use_matrix_cores(int64_t N, int64_t m_total) { return N >= 5 || (N >= 3 && m_total >= 8192); }
+// Rows longer than the matrix-core kernel's 128-block pass (K > 4096) run as
+// several dependent passes there; the VALU kernel does them in one launch
+// and is faster up to 6 tokens (2048 x 5632 Q4_0: 12.7 / 14.1 us against
+// 14.3 / 14.8 at 5 / 6 tokens; 16.7 against 15.3 at 8).
+inline bool use_matrix_cores(int64_t N, int64_t m_total, int64_t K)
+{
+    if (K > 4096 && N <= 6) return false;
+    return N >= 5 || (N >= 3 && m_total >= 8192);
+}
 
 // One GEMV of a launch: its weights, activations and outputs.  All items of
 // a launch share the weight type, K and the token count.  An item is one
@@ -941,7 +959,7 @@ hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t strea
     for (int i = 0; i < count; ++i) m_total += tasks[i].w.M;
     if (m_total == 0 || N == 0) return hipSuccess;
     // The matrix-core kernels' cost does not grow with the token count.
-    if (use_matrix_cores(N, m_total) && gemv_mf_supported(tasks, count)) return launch_gemv_mf(tasks, count, stream);
+    if (use_matrix_cores(N, m_total, K) && gemv_mf_supported(tasks, count)) return launch_gemv_mf(tasks, count, stream);
     StreamConfig sc;
     if (stream_config(type, K, m_total, N, &sc) && stream_supported(tasks, count))
         return launch_gemv_stream(tasks, count, sc, stream);
@@ -975,8 +993,9 @@ hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t strea
         for (int i = 0; i < count; ++i) {
             if (tasks[i].w.M == 0) continue;
             int64_t wgs = need[i];
-            if (need_total > max_workgroups(c.ks, c.wgw)) {
-                wgs = need[i] * max_workgroups(c.ks, c.wgw) / need_total;   // share of the persistent grid
+            const int wg_cap = max_workgroups(c.ks, c.wgw, K, c.nt);
+            if (need_total > wg_cap) {
+                wgs = need[i] * wg_cap / need_total;   // share of the persistent grid
                 if (wgs < 1) wgs = 1;
             }
             GemvItem &it = a.item[a.n_items++];
