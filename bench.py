@@ -492,8 +492,9 @@ def block_gemm_probe_leg(Q):
         for wps in (1, 2):
             Q.mfma_probe(mode, workgroups=cus * wps, iters=200)
             r = Q.mfma_probe(mode, workgroups=cus * wps, iters=4000)
+            # a SIMD runs wps waves' rounds by the time its slowest wave ends
             row[f"{wps}_wave_per_simd"] = {"cycles_per_round_per_wave": round(r["cycles_per_round"], 1),
-                                           "simd_cycles_per_round": round(r["cycles_per_round"] / wps, 1)}
+                                           "simd_cycles_per_round": round(r["cycles_per_round_max"] / wps, 1)}
         row["tflops_1_wave_per_simd"] = round(Q.mfma_probe(mode, workgroups=cus, iters=4000)["tflops"], 1)
         out[name] = row
         log(f"block-GEMM inner loop {name}: {row}")

@@ -445,7 +445,9 @@ def clock_probe(workgroups: int = 256, iters: int = 20000, mode: int = 0) -> flo
 def mfma_probe(mode: int, workgroups: int = 256, iters: int = 4000) -> dict:
     """The block-GEMM inner-loop probe (qmm_clock_probe modes 2-4) on every
     CU: multiply-add rate in TFLOP/s over the waves' own clocks, and shader
-    clock cycles per round (four 32 x 32 x 32 tile-blocks) per wave."""
+    clock cycles per round (four 32 x 32 x 32 tile-blocks) per wave: the mean
+    over waves and the slowest wave (waves sharing a SIMD do not run in
+    lockstep, so the SIMD's rate is that of its last wave to finish)."""
     out = torch.zeros(8 * workgroups, dtype=torch.int64, device="cuda")
     _check(lib().qmm_clock_probe(ctypes.c_void_p(out.data_ptr()), workgroups, iters, mode, _stream(None)),
            "qmm_clock_probe")
@@ -455,4 +457,5 @@ def mfma_probe(mode: int, workgroups: int = 256, iters: int = 4000) -> dict:
         raise QmmError(wall_khz, "qmm_wall_clock_khz")
     seconds = float(d[:, 1].mean()) / (wall_khz * 1e3)
     flops = 4.0 * workgroups * iters * 4 * 2 * 32 * 32 * 32
-    return {"tflops": flops / seconds / 1e12, "cycles_per_round": float(d[:, 0].mean()) / iters}
+    return {"tflops": flops / seconds / 1e12, "cycles_per_round": float(d[:, 0].mean()) / iters,
+            "cycles_per_round_max": float(d[:, 0].max()) / iters}
