@@ -450,11 +450,14 @@ __global__ __launch_bounds__(THREADS) void gemm_rq_kernel(const GemmArgs a)
     // FAST loads (every load issued wholly in K and the range)
     auto main_loop = [&](auto TW, auto FAST, int t0, int t1) {
         constexpr bool tokw = decltype(TW)::value;
+        // the fast runs are whole multiples of GS iterations: no per-step
+        // bound check (each one a branch between matrix instructions)
+        constexpr bool guard = !decltype(FAST)::value;
         for (; t0 < t1; t0 += GS) {
             static_for<GS>([&](auto U) {
                 constexpr int u = decltype(U)::value;
                 const int t = t0 + u;
-                if (t < t1) {
+                if (!guard || t < t1) {
                     // this wave's loads for the token stage of step t + 1 and
                     // the code group of step t + 2 have landed; after the
                     // barrier, every wave's have, and the token stage of step
