@@ -572,7 +572,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
                     const int64_t n = n0 + wn * 64 + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
                     const float g = i == 0 ? acc[0][j][r] : xb[(j * 16 + r) * 64 + lane];
                     const float u = i == 0 ? xa[(j * 16 + r) * 64 + lane] : acc[1][j][r];
-                    if (n < a.N) out[(uint64_t)n * y_pitch + m] = swish(g) * u;
+                    if (n < a.N) __builtin_nontemporal_store(swish(g) * u, out + (uint64_t)n * y_pitch + m);
                 }
             }
         };
@@ -589,7 +589,7 @@ __global__ __launch_bounds__(THREADS) void gemm_kernel(const GemmArgs a)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t n = n0 + wn * 64 + i * 32 + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-                if (n < a.N) out[(uint64_t)n * y_pitch + m] = acc[i][j][r];
+                if (n < a.N) __builtin_nontemporal_store(acc[i][j][r], out + (uint64_t)n * y_pitch + m);   // streaming store: skips filling the L2
             }
         }
     }
