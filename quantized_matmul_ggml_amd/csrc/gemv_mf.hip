@@ -453,13 +453,15 @@ using MfKernel = void (*)(const MfArgs);
 
 // Eight waves share a tile (each one eighth of the pass's K, so that two
 // waves per SIMD hide each other's latencies), with NBW = 4, 8 or 16 blocks
-// per wave.  Q4_0 tiles are half the bytes of Q8_0 ones, so they get a
-// stage more (measured: 4 for Q4_0, 3 for Q8_0 at K = 2048).
+// per wave.  Three stages for both types (measured at K = 2048 and 5632,
+// 4 and 8 tokens): a Q4_0 workgroup then needs 63 KB of LDS and two share
+// a CU, 2-4 % faster than one with four stages; Q8_0 with two stages (two
+// workgroups per CU) is as fast at 4 tokens and 4 % slower at 8.
 constexpr int kWaves = 8;
 // Blocks of K one launch covers (16 per wave); longer rows take several
 // launches, the later ones adding to y.
 constexpr int kPassBlocks = 16 * kWaves;
-template <int WT> constexpr int max_stages() { return WT == W_Q4_0 ? 4 : 3; }
+template <int WT> constexpr int max_stages() { return 3; }
 
 // The kernel for (type, NBW, scale shift) and its LDS bytes.
 template <int WT, int SS>
