@@ -37,6 +37,16 @@ struct RecArgs {
     int32_t total;         // M * nblk records
 };
 
+// A 16-byte store that streams past the L2 (non-temporal), for the records
+// that rows_to_records_kernel writes in whole contiguous spans (2 % faster
+// on the box; the scattered 16-byte row stores of the other direction were
+// 3 % slower this way and stay ordinary stores).
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+__device__ inline void store16_nt(void *p, uint4 v)
+{
+    __builtin_nontemporal_store(u32x4v{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4v *>(p));
+}
+
 // Records [r0, r0 + n) of the span (n <= 256) staged in LDS: 16-byte pieces
 // while whole, 2-byte pieces for the tail that ends the tensor.
 template <int WT>
@@ -49,7 +59,7 @@ __device__ inline void span_io(uint8_t *lds, uint8_t *rec, int n, bool load)
         if (load)
             *reinterpret_cast<uint4 *>(lds + 16 * i) = *reinterpret_cast<const uint4 *>(rec + 16 * i);
         else
-            *reinterpret_cast<uint4 *>(rec + 16 * i) = *reinterpret_cast<const uint4 *>(lds + 16 * i);
+            store16_nt(rec + 16 * i, *reinterpret_cast<const uint4 *>(lds + 16 * i));
     }
     for (int i = 16 * vec / 2 + threadIdx.x; i < bytes / 2; i += kRecThreads) {
         if (load)
