@@ -60,23 +60,33 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 template <int WT> struct RqFmt;
 template <> struct RqFmt<W_Q4_0> { static constexpr int QB = 16, GS = 4; };
 template <> struct RqFmt<W_Q8_0> { static constexpr int QB = 32, GS = 2; };
+// F16 rows: 64 bytes per 32 weights, no scales; a group is one K-step
+template <> struct RqFmt<W_F16> { static constexpr int QB = 64, GS = 1; };
 template <int WT>
 struct RqSched {
     static constexpr int QB = RqFmt<WT>::QB;
     static constexpr int GS = RqFmt<WT>::GS;
     static_assert(2 * GS * QB == 128, "a group is 128 bytes of a row");
-    // group g is issued DC = 5 steps ahead of its first step (three
-    // iterations before its first codes are read); it is last read (codes two
-    // steps ahead) in iteration GS g + GS - 3
-    static constexpr int DC = 5;
+    static constexpr bool SCALES = WT != W_F16;
+    // loads of one group by one code wave
+    static constexpr int LOADS = CODE_LOADS + (SCALES ? SCALE_LOADS : 0);
+    // group g is issued DC steps ahead of its first step (five for the
+    // quantized types, three iterations before its first codes are read;
+    // four for F16, whose one-step groups would otherwise need five
+    // buffers); it is last read (codes two steps ahead) in iteration
+    // GS g + GS - 3
+    static constexpr int DC = GS == 1 ? 4 : 5;
     static constexpr int PRO = (DC + GS - 1) / GS;       // groups issued before the loop
     static_assert(PRO <= NB, "the prologue's groups fit the buffers");
+    static_assert(NB * GS - DC > GS - 3, "a group buffer is free before the group after next is issued into it");
+    // groups the prologue reads (the raw codes of steps 0 and 1)
+    static constexpr int PRO_READ = 1 + 1 / GS;
     // loads a code wave may still have in flight at the top of iteration t
     // (t mod GS = u) once the group of step t + 2 has landed: those of the
     // later groups issued by then (iteration GS g - DC <= t - 1)
     static constexpr int pending(int u)
     {
-        return (CODE_LOADS + SCALE_LOADS) * ((u - 1 + DC) / GS - (u + 2) / GS);
+        return LOADS * ((u - 1 + DC) / GS - (u + 2) / GS);
     }
     static_assert(pending(0) >= 0 && pending(GS - 1) >= 0, "the group of step t + 2 is issued before iteration t");
 };
@@ -204,6 +214,25 @@ struct Deq<W_Q8_0> {
     }
 };
 
+// F16: the lane's 16 weights are two runs of 8 halves (k = 8 h .. 8 h + 7 of
+// each chunk); each becomes the bf16 rounding (nearest even) of its exact
+// binary32 value.  A block past K reads the next row's bytes, which may be
+// any halves, Inf and NaN included: it is replaced by zeros.
+template <>
+struct Deq<W_F16> {
+    template <int P>
+    __device__ inline void part(u32x4 c0, u32x4 c1, bool live, uint32_t (&b)[8])
+    {
+        const uint32_t w = P < 4 ? c0[P % 4] : c1[P % 4];
+        const uint32_t v = pack_bf16(lo_half(w), hi_half(w));
+        b[P] = live ? v : 0u;
+    }
+};
+
+// A lane's raw weights of one step: codes and scale, or F16 halves.
+template <int WT> struct RawOf { u32x2 c0, c1; uint16_t sbits; };
+template <> struct RawOf<W_F16> { u32x4 c0, c1; };
+
 // Swish(z) = z * sigma(z) = z / (1 + e^{-z}) in binary32 (for z far below
 // zero e^{-z} overflows and the quotient is the limit -0).
 __device__ inline float swish(float z)
@@ -306,7 +335,8 @@ __global__ __launch_bounds__(THREADS) void gemm_rq_kernel(const GemmArgs a)
     // groups wholly in K and the range take a scalar offset, the last
     // partial one checks each lane, and groups past it read zeros.
     const int64_t rows = M - m0 < MROWS ? M - m0 : MROWS;
-    const uint32_t row_bytes = (uint32_t)(a.qoff + (a.K / 32) * QB);
+    const int64_t qoff = WT == W_F16 ? 0 : a.qoff;  // F16 rows hold no scales
+    const uint32_t row_bytes = (uint32_t)(qoff + (a.K / 32) * QB);
     const int cw = token_wave ? 0 : wave;
     // fused SwiGLU: code waves 2, 3 load the up matrix into tile rows 64..127
     const bool upper = SW && cw >= 2;
@@ -321,7 +351,7 @@ __global__ __launch_bounds__(THREADS) void gemm_rq_kernel(const GemmArgs a)
     for (int i = 0; i < CODE_LOADS; ++i) {
         const int row = 8 * (CODE_LOADS * cw + i) + (lane >> 3);
         const int unit = (lane & 7) ^ ((row >> 1) & 7);
-        coff[i] = (uint32_t)((row - lrow) * pm + a.qoff) + (uint32_t)(2 * s0 * QB) + 16u * unit;
+        coff[i] = (uint32_t)((row - lrow) * pm + qoff) + (uint32_t)(2 * s0 * QB) + 16u * unit;
     }
     constexpr int SPG = (2 * GS) >> SS;          // scales per row and group
     uint32_t soff[SCALE_LOADS];
@@ -347,22 +377,28 @@ __global__ __launch_bounds__(THREADS) void gemm_rq_kernel(const GemmArgs a)
     auto issue_group = [&](int g) {
 #pragma unroll
         for (int i = 0; i < CODE_LOADS; ++i) code_load(std::false_type{}, i, g);
+        if constexpr (Sc::SCALES) {
 #pragma unroll
-        for (int i = 0; i < SCALE_LOADS; ++i) scale_load(std::false_type{}, i, g);
+            for (int i = 0; i < SCALE_LOADS; ++i) scale_load(std::false_type{}, i, g);
+        }
     };
 
     // ---- LDS reads ----
     // B fragment lane (row rl, half h); A fragment lane (token 32 j + lane % 32, half h).
     const int rl = 32 * rg + (lane & 31);
-    uint32_t crd[GS][QB / 16];    // code offsets (within a group buffer) of block 2 u + par
+    // The lane's weights of block bi = 2 u + par: Q4_0 8 bytes of unit bi;
+    // Q8_0 8 bytes of each of units 2 bi (chunk 0) and 2 bi + 1 (chunk 1);
+    // F16 units 4 bi + h (chunk 0) and 4 bi + 2 + h (chunk 1), whole.
+    constexpr int CR = QB == 16 ? 1 : 2;
+    uint32_t crd[GS][CR];         // code offsets (within a group buffer) of block 2 u + par
     uint32_t srd[GS];             // scale offsets
 #pragma unroll
     for (int u = 0; u < GS; ++u) {
         const int bi = 2 * u + par;
 #pragma unroll
-        for (int c = 0; c < QB / 16; ++c) {
-            const int unit = (QB / 16) * bi + c;
-            crd[u][c] = (uint32_t)(rl * 128 + 16 * (unit ^ ((rl >> 1) & 7)) + 8 * h);
+        for (int c = 0; c < CR; ++c) {
+            const int unit = WT == W_F16 ? 4 * bi + 2 * c + h : (QB / 16) * bi + c;
+            crd[u][c] = (uint32_t)(rl * 128 + 16 * (unit ^ ((rl >> 1) & 7)) + (WT == W_F16 ? 0 : 8 * h));
         }
         srd[u] = (uint32_t)(rl * 16 + 2 * (bi >> SS));
     }
@@ -383,7 +419,7 @@ __global__ __launch_bounds__(THREADS) void gemm_rq_kernel(const GemmArgs a)
         for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
     bf16x8 A[2][4][2];            // token fragments of steps t and t + 1
     uint32_t B[2][8];             // weight fragments of steps t and t + 1
-    struct Raw { u32x2 c0, c1; uint16_t sbits; };
+    using Raw = RawOf<WT>;
     Raw R[2];                     // raw codes and scale of steps t + 1 and t + 2 (by step parity)
     Deq<WT> dq;
     const int nblk32 = (int)(nblk < 0x40000000 ? nblk : 0x40000000);
@@ -397,9 +433,14 @@ __global__ __launch_bounds__(THREADS) void gemm_rq_kernel(const GemmArgs a)
         const int gb = (s / GS) % NB;
         const uint8_t *cg = lds + LDS_GROUP_OFF + gb * GROUP_BYTES;
         Raw r;
-        r.sbits = *reinterpret_cast<const uint16_t *>(lds + LDS_SCALE_OFF + gb * SGROUP_BYTES + srd[u]);
-        r.c0 = *reinterpret_cast<const u32x2 *>(cg + crd[u][0]);
-        r.c1 = QB == 32 ? *reinterpret_cast<const u32x2 *>(cg + crd[u][QB / 16 - 1]) : r.c0;
+        if constexpr (WT == W_F16) {
+            r.c0 = *reinterpret_cast<const u32x4 *>(cg + crd[u][0]);
+            r.c1 = *reinterpret_cast<const u32x4 *>(cg + crd[u][1]);
+        } else {
+            r.sbits = *reinterpret_cast<const uint16_t *>(lds + LDS_SCALE_OFF + gb * SGROUP_BYTES + srd[u]);
+            r.c0 = *reinterpret_cast<const u32x2 *>(cg + crd[u][0]);
+            r.c1 = QB == 32 ? *reinterpret_cast<const u32x2 *>(cg + crd[u][CR - 1]) : r.c0;
+        }
         return r;
     };
     // part P of the unpacking of step s from r into b (a block past K gets
@@ -408,7 +449,8 @@ __global__ __launch_bounds__(THREADS) void gemm_rq_kernel(const GemmArgs a)
         constexpr int p = decltype(P)::value;
         const bool live = 2 * s + par < nblk32;
         if constexpr (WT == W_Q4_0) dq.template part<p>(r.c0, r.sbits, live, b);
-        else dq.template part<p>(r.c0, r.c1, r.sbits, live, b);
+        else if constexpr (WT == W_Q8_0) dq.template part<p>(r.c0, r.c1, r.sbits, live, b);
+        else dq.template part<p>(r.c0, r.c1, live, b);
     };
     auto bfrag = [](const uint32_t (&b)[8], int c) {
         return __builtin_bit_cast(bf16x8, u32x4{b[4 * c], b[4 * c + 1], b[4 * c + 2], b[4 * c + 3]});
@@ -425,7 +467,7 @@ __global__ __launch_bounds__(THREADS) void gemm_rq_kernel(const GemmArgs a)
     } else {
 #pragma unroll
         for (int g = 0; g < Sc::PRO; ++g) issue_group(g);
-        wait_vm<(CODE_LOADS + SCALE_LOADS) * (Sc::PRO - 1)>();
+        wait_vm<Sc::LOADS * (Sc::PRO - Sc::PRO_READ)>();
     }
     asm volatile("s_barrier" ::: "memory");
 #pragma unroll
@@ -446,15 +488,19 @@ __global__ __launch_bounds__(THREADS) void gemm_rq_kernel(const GemmArgs a)
     // One straight-line copy per load role.
     int rd_stage = 1;             // token stage of step t + 1
     int ld_stage = DT;            // token stage of step t + DT
-    // iterations t0 .. t1 - 1 (t0 a multiple of GS) of one load role, with
+    // A straight-line copy covers UF iterations, a multiple of GS (the
+    // position in the code group is static) and of 2 (so is the register
+    // set of each step).
+    constexpr int UF = GS % 2 == 0 ? GS : 2 * GS;
+    // iterations t0 .. t1 - 1 (t0 a multiple of UF) of one load role, with
     // FAST loads (every load issued wholly in K and the range)
     auto main_loop = [&](auto TW, auto FAST, int t0, int t1) {
         constexpr bool tokw = decltype(TW)::value;
-        // the fast runs are whole multiples of GS iterations: no per-step
+        // the fast runs are whole multiples of UF iterations: no per-step
         // bound check (each one a branch between matrix instructions)
         constexpr bool guard = !decltype(FAST)::value;
-        for (; t0 < t1; t0 += GS) {
-            static_for<GS>([&](auto U) {
+        for (; t0 < t1; t0 += UF) {
+            static_for<UF>([&](auto U) {
                 constexpr int u = decltype(U)::value;
                 const int t = t0 + u;
                 if (!guard || t < t1) {
@@ -464,7 +510,7 @@ __global__ __launch_bounds__(THREADS) void gemm_rq_kernel(const GemmArgs a)
                     // t - 1 and a group buffer last read in iteration t - 1
                     // are free
                     if constexpr (tokw) wait_vm<TOK_LOADS * (DT - 2)>();
-                    else wait_vm<Sc::pending(u)>();
+                    else wait_vm<Sc::pending(u % GS)>();
                     asm volatile("s_barrier" ::: "memory");
                     constexpr bool group_now = (u + DC) % GS == 0;
                     const int g = (t + DC) / GS;
@@ -484,7 +530,8 @@ __global__ __launch_bounds__(THREADS) void gemm_rq_kernel(const GemmArgs a)
                             if constexpr (k < TOK_LOADS) token_load(FAST, k, t + DT, ld_stage);
                         } else if constexpr (group_now) {
                             if constexpr (k < CODE_LOADS) code_load(FAST, k, g);
-                            else if constexpr (k < CODE_LOADS + SCALE_LOADS) scale_load(FAST, k - CODE_LOADS, g);
+                            else if constexpr (Sc::SCALES && k < CODE_LOADS + SCALE_LOADS)
+                                scale_load(FAST, k - CODE_LOADS, g);
                         }
                         dequant_part(K, rc, t + 1, bn);
                         // keep this order: matrix instruction, its fragment
@@ -502,12 +549,12 @@ __global__ __launch_bounds__(THREADS) void gemm_rq_kernel(const GemmArgs a)
     // (t + DC) / GS < full_groups), then the rest with per-lane checks.
     if (token_wave) {
         int tf = full_steps - DT;
-        tf = tf < 0 ? 0 : (tf > steps ? steps : tf) / GS * GS;
+        tf = tf < 0 ? 0 : (tf > steps ? steps : tf) / UF * UF;
         main_loop(std::true_type{}, std::true_type{}, 0, tf);
         main_loop(std::true_type{}, std::false_type{}, tf, steps);
     } else {
         int tf = GS * full_groups - DC;
-        tf = tf < 0 ? 0 : (tf > steps ? steps : tf) / GS * GS;
+        tf = tf < 0 ? 0 : (tf > steps ? steps : tf) / UF * UF;
         main_loop(std::false_type{}, std::true_type{}, 0, tf);
         main_loop(std::false_type{}, std::false_type{}, tf, steps);
     }
@@ -594,13 +641,14 @@ hipError_t launch_rq(const GemmArgs &a, unsigned blocks, bool sw, hipStream_t st
 
 bool gemm_rq_handles(int type)
 {
-    return type == W_Q4_0 || type == W_Q8_0;
+    return type == W_Q4_0 || type == W_Q8_0 || type == W_F16;
 }
 
 hipError_t launch_gemm_rq(const GemmArgs &a, unsigned blocks, int type, int ss, bool sw, hipStream_t stream)
 {
     if (type == W_Q4_0) return ss ? launch_rq<W_Q4_0, 1>(a, blocks, sw, stream) : launch_rq<W_Q4_0, 0>(a, blocks, sw, stream);
     if (type == W_Q8_0) return ss ? launch_rq<W_Q8_0, 1>(a, blocks, sw, stream) : launch_rq<W_Q8_0, 0>(a, blocks, sw, stream);
+    if (type == W_F16 && !ss) return launch_rq<W_F16, 0>(a, blocks, sw, stream);
     return hipErrorInvalidValue;
 }
 

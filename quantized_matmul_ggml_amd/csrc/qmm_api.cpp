@@ -385,7 +385,7 @@ int check_gemm(const qmm_tensor *w, const qmm_tensor *x, const qmm_tensor *y)
     const int rc = check_mul_mat(w, x, y, QMM_TYPE_BF16, 16);
     if (rc) return rc;
     if (!(is_quant(w->type) || w->type == QMM_TYPE_F16)) return QMM_ERR_TYPE;
-    // the F16 producer moves whole 32-weight blocks
+    // the GEMM stages F16 rows in whole 32-weight blocks
     if (w->type == QMM_TYPE_F16 && w->ne[0] % 32 != 0) return QMM_ERR_UNSUPPORTED;
     if (w->ne[1] == 0 || x->ne[1] == 0) return QMM_OK;
     qmm::ActView xv{x->data, pitch_elems(x), x->ne[1]};
