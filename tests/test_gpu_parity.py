@@ -563,6 +563,31 @@ def test_gemm_prefill_full_size_sampled(orc):
     _assert_tol(y[ns, ms], ydiag, a, 1.1 * K * 2.0 ** -24, 1e-7, "prefill sampled diagnostic")
 
 
+def test_gemm_prefill_f16_full_size_sampled(orc):
+    """The same product with the weights in fp16 (converted to bf16 in the
+    multiplying waves, one K-step per staged group), in the launch the bench
+    times: 4096 sampled outputs plus the first and last 128 x 128 tiles."""
+    M, K, N = WL.FFN, WL.HIDDEN, 512
+    _banner("gemm prefill F16 5632x2048x512")
+    packed = _oracle_weight(orc, "F16", WL.weights(WL.seed(5, 0), M, K))
+    xbits = WL.round_bf16_bits(WL.activations(WL.seed(5, 1), N, K))
+    wt = B.Weight(torch.from_numpy(packed.view(np.float16)).to(DEV), B.F16, K, M)
+    y = Q.gemm(wt, WL.bf16_bits_to_torch(xbits, DEV)).cpu().numpy()
+    rng = np.random.default_rng(101)
+    ms = list(rng.integers(0, M, 4096))
+    ns = list(rng.integers(0, N, 4096))
+    for m0, n0 in ((0, 0), (M - 128, N - 128)):
+        mm, nn = np.meshgrid(np.arange(m0, m0 + 128), np.arange(n0, n0 + 128))
+        ms += list(mm.ravel())
+        ns += list(nn.ravel())
+    ms, ns = np.array(ms), np.array(ns)
+    t = TYPES["F16"][1]
+    yref, a = orc.mul_mat_pairs(t, packed, K, xbits, ms, ns, x_bf16_bits=True)
+    ydiag, _ = orc.mul_mat_pairs(t, packed, K, xbits, ms, ns, x_bf16_bits=True, w_to_bf16=True)
+    _assert_tol(y[ns, ms], yref, a, 1e-2, 1e-5, "prefill F16 sampled")
+    _assert_tol(y[ns, ms], ydiag, a, 1.1 * K * 2.0 ** -24, 1e-7, "prefill F16 sampled diagnostic")
+
+
 def test_gemm_split_k_full_size_sampled(orc):
     """The 2048 x 5632 down projection times 512 bf16 tokens: 64 output
     tiles, so K is split over four workspace slabs and the slabs added by the
