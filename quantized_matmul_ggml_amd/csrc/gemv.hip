@@ -310,9 +310,9 @@ __global__ __launch_bounds__(64 * WGW) void gemv_kernel(const GemvArgs a)
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 const uint32_t ro = (uint32_t)(u % RU) * pu;
-                q[u][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res, qoffs[j] + ro, 0, 0));
+                q[u][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res, qoffs[j] + ro, 0, kStreamLoad));
                 if (WT != W_F16)
-                    sc[u][j] = __builtin_amdgcn_raw_buffer_load_b16(res, soffs[j] + ro, 0, 0);
+                    sc[u][j] = __builtin_amdgcn_raw_buffer_load_b16(res, soffs[j] + ro, 0, kStreamLoad);
             }
         }
         if (f16_tail) {                // uniform; rare: waits for the loads here
@@ -584,9 +584,9 @@ __global__ __launch_bounds__(256) void gemv_stream_kernel(const GemvArgs a)
 #pragma unroll
             for (int j = 0; j < CPL; ++j) {
                 const uint32_t ro = (uint32_t)u * pitch;
-                qd[u][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res, qoffs[j] + ro, 0, 0));
+                qd[u][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res, qoffs[j] + ro, 0, kStreamLoad));
                 if (WT != W_F16)
-                    sd[u][j] = __builtin_amdgcn_raw_buffer_load_b16(res, soffs[j] + ro, 0, 0);
+                    sd[u][j] = __builtin_amdgcn_raw_buffer_load_b16(res, soffs[j] + ro, 0, kStreamLoad);
             }
         }
     };

@@ -195,8 +195,8 @@ __global__ __launch_bounds__(kThreads) void gemv_i8_kernel(const I8Args a)
                 const bool second = SWIGLU && u >= RU;
                 const __amdgpu_buffer_rsrc_t res = second ? res2 : res1;
                 const uint32_t ro = (uint32_t)(u % RU) * (second ? pitch2 : pitch);
-                q[u][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res, qoffs[j] + ro, 0, 0));
-                sc[u][j] = __builtin_amdgcn_raw_buffer_load_b16(res, soffs[j] + ro, 0, 0);
+                q[u][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res, qoffs[j] + ro, 0, kStreamLoad));
+                sc[u][j] = __builtin_amdgcn_raw_buffer_load_b16(res, soffs[j] + ro, 0, kStreamLoad);
             }
     };
     load_group(g);

@@ -146,6 +146,9 @@ __device__ inline int swz(int r, int u)
 // see (so it neither reorders LDS reads around them nor adds waits of its
 // own); the consumer waits with an explicit vmcnt.  Lane i of one load writes
 // its SIZE bytes at lds + SIZE * i.  rsrc is the 4-word buffer resource.
+// They keep the default cache policy: with the non-temporal one of the
+// other GEMVs (kStreamLoad) this kernel was 5-7 % slower on the LM head at
+// 4 and 8 tokens.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ inline i32x4 buffer_words(const void *base, uint32_t bytes)
 {

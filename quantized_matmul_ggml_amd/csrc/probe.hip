@@ -8,7 +8,9 @@
 //  * stream_read_kernel: every thread reads 16-byte units with buffer loads,
 //    two batches of U loads in flight (the next batch is issued before the
 //    current one is consumed), grid-stride over the buffer; each workgroup
-//    xor-folds what it read into one word, so no load can be dropped.
+//    xor-folds what it read into one word, so no load can be dropped.  The
+//    loads carry the GEMVs' weight-streaming cache policy (kStreamLoad), so
+//    the ceiling is measured the way the weights are read.
 //  * clock_kernel: each wave times a long dependent chain (binary32 FMAs,
 //    or bf16 matrix instructions) with the shader-clock counter (s_memtime)
 //    and the constant-rate counter (s_memrealtime); the ratio of the two
@@ -35,7 +37,7 @@ __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const uint8_t
         for (int j = 0; j < kReadU; ++j) {
             const uint32_t u = it * batch + (uint32_t)j * stride + first;
             const uint32_t off = u < units ? u * 16u : OUT_OF_RANGE;
-            v[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res, off, 0, 0));
+            v[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(res, off, 0, kStreamLoad));
         }
     };
     uint4 acc = make_uint4(0, 0, 0, 0);
