@@ -642,6 +642,18 @@ def breakdown_leg(Q, WL, dev, args, gemv_bytes, ceiling):
                                        "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
     del w5
 
+    # Q4_0 2048 x 5632 (the FFN down projection) at 4 and 8 tokens: rows of
+    # 176 blocks in one matrix-core launch; 48 copies (311 MB)
+    w6 = [Q.quantize(WL.weights_device(WL.seed(3, 6, r), WL.HIDDEN, WL.FFN, dev), Q.Q4_0) for r in range(48)]
+    for n in (4, 8):
+        x6 = WL.activations_device(WL.seed(3, 10), n, WL.FFN, dev)
+        y6 = torch.empty((n, WL.HIDDEN), device=dev)
+        per = rotate(w6, x6, y6, 96)
+        b = gemv_bytes(w6[0], n)
+        out[f"q4_0_wdown_2048x5632_n{n}"] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1), "bytes": b,
+                                             "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
+    del w6
+
     # fp16 5632 x 2048, one token: 48 copies (1.1 GB) so HBM is read
     w2 = []
     for r in range(48):

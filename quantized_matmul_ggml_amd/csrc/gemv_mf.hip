@@ -29,7 +29,9 @@
 //    tokens 2 g and 2 g + 1, of its row for one block, and applies the block
 //    scale in one fused multiply-add per token.
 //  * The KW waves of a workgroup split K; their partial sums meet in LDS at
-//    the end of each tile.
+//    the end of each tile.  A tile is TR = 16 weight rows, or 8 (columns
+//    8..15 then repeat rows 0..7 and are not stored) where 16-row stages
+//    would not fit the LDS.
 #include "qmm_internal.h"
 #include "wave_reduce.h"
 
@@ -66,7 +68,7 @@ struct MfArgs {
     int32_t N;            // tokens of this launch (<= 8)
     int32_t K;            // K of this pass (32 nb); x points at its first element
     int32_t qoff;         // byte offset of the codes in a row
-    int32_t nb;           // 32-blocks of this pass (<= 128)
+    int32_t nb;           // 32-blocks of this pass (<= 128; <= 192 in the wide launch)
     int32_t n_items;
     int32_t kb0;          // first block of this pass within the row
     int32_t nb_row;       // 32-blocks per row
@@ -113,22 +115,24 @@ __device__ inline void swap16(uint32_t &a, uint32_t &b)
     b = p[1];
 }
 
-// A wave's share of one 16-row tile in LDS: the code bytes of its NBW
+// A wave's share of one TR-row tile in LDS: the code bytes of its NBW
 // blocks of each row (SB = 16 U bytes, U 16-byte units) and their scales
 // (SR bytes), as the direct-to-LDS loads deliver them: one load instruction
 // moves 64 lanes x 16 contiguous bytes of RPI whole rows; the scales come
 // with 4-byte lanes (one fp16 scale per 32 weights, or per 64 with SS = 1).
-template <int WT, int NBW, int SS>
+template <int WT, int NBW, int SS, int TR>
 struct MfStage {
     static constexpr int SB = NBW * MfFmt<WT>::block_bytes;
     static constexpr int U = SB / 16;
     static constexpr int RPI = 64 / U;
-    static constexpr int NI = kTileRows / RPI;                 // code load instructions
+    static constexpr int NI = TR / RPI;                        // code load instructions
     static constexpr int SR = (2 * NBW) >> SS;
-    static constexpr int NS = (kTileRows * SR + 255) / 256;    // scale load instructions
+    static constexpr int NS = (TR * SR + 255) / 256;           // scale load instructions
     static constexpr int CODE_BYTES = NI * 1024;
     static constexpr int BYTES = CODE_BYTES + NS * 256;
     static_assert(U >= 4 && U <= 64, "2..16 rows per load instruction");
+    static_assert(TR == 8 || TR == 16, "8 or 16 rows per tile");
+    static_assert(RPI <= TR, "whole load instructions per tile");
 };
 
 // Position (16-byte unit) of unit u of row r inside its row's LDS span: the
@@ -181,29 +185,29 @@ __device__ inline void wait_vm()
 // LDS of a workgroup with KW waves and NSTG stages, and the most stages (up
 // to MAXD, at least 2) that fit the CU's 160 KiB.
 constexpr int kLdsBytes = 160 * 1024;
-template <int WT, int KW, int NBW, int SS>
+template <int WT, int KW, int NBW, int SS, int TR>
 constexpr int mf_lds_bytes(int nstg)
 {
-    return nstg * KW * MfStage<WT, NBW, SS>::BYTES + 2 * KW * 64 * 2 * 4;
+    return nstg * KW * MfStage<WT, NBW, SS, TR>::BYTES + 2 * KW * 64 * 2 * 4;
 }
-template <int WT, int KW, int NBW, int SS, int MAXD>
+template <int WT, int KW, int NBW, int SS, int MAXD, int TR>
 constexpr int mf_stages()
 {
     int d = MAXD;
-    while (d > 2 && mf_lds_bytes<WT, KW, NBW, SS>(d) > kLdsBytes) --d;
+    while (d > 2 && mf_lds_bytes<WT, KW, NBW, SS, TR>(d) > kLdsBytes) --d;
     return d;
 }
 
-template <int WT, int KW, int NBW, int SS, int MAXD>
+template <int WT, int KW, int NBW, int SS, int MAXD, int TR>
 __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
 {
-    constexpr int NSTG = mf_stages<WT, KW, NBW, SS, MAXD>();
-    static_assert(mf_lds_bytes<WT, KW, NBW, SS>(NSTG) <= kLdsBytes, "LDS of one workgroup");
+    constexpr int NSTG = mf_stages<WT, KW, NBW, SS, MAXD, TR>();
+    static_assert(mf_lds_bytes<WT, KW, NBW, SS, TR>(NSTG) <= kLdsBytes, "LDS of one workgroup");
     constexpr int BPG = MfFmt<WT>::bpg;
     constexpr int BB = MfFmt<WT>::block_bytes;
     constexpr int NG = NBW / BPG;          // 64-byte groups per row per wave
     static_assert(NBW % BPG == 0, "whole load groups");
-    using St = MfStage<WT, NBW, SS>;
+    using St = MfStage<WT, NBW, SS, TR>;
     static_assert(NSTG >= 2 && NSTG <= 4, "2 to 4 stages");
     __shared__ float red[2][KW][64][2];
     // one array per stage, so that each wait for a stage's loads counts only
@@ -236,8 +240,8 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
     // units and scales of blocks past the row, read as zeros ----
     const uint32_t row_bytes = (uint32_t)(qoff + nb_row * BB);
     auto issue = [&](auto &stg, int tl) {
-        const int r0 = tl * kTileRows;
-        const int rows = tl < n_tiles ? (M - r0 < kTileRows ? M - r0 : kTileRows) : 0;
+        const int r0 = tl * TR;
+        const int rows = tl < n_tiles ? (M - r0 < TR ? M - r0 : TR) : 0;
         const i32x4 wres = buffer_words(W + (uint64_t)(rows > 0 ? r0 : 0) * pitch,
                                         rows > 0 ? (uint32_t)(rows - 1) * pitch + row_bytes : 0u);
         const uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(&stg[wave][0]);
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
             const int r = byte / St::SR, rb = byte % St::SR;
             // scale rb / 2 of the wave's slice is that of 32-block
             // b_begin + (rb / 2 << SS) (kb0 and b_begin are even)
-            const uint32_t off = (r < kTileRows && (b_begin >> SS) + rb / 2 < (nb >> SS))
+            const uint32_t off = (r < TR && (b_begin >> SS) + rb / 2 < (nb >> SS))
                                      ? (uint32_t)r * pitch + (uint32_t)(2 * ((kb0 + b_begin) >> SS) + rb)
                                      : OUT_OF_RANGE;
             load_to_lds<4>(wres, base + St::CODE_BYTES + 256 * i, off);
@@ -277,48 +281,56 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
     const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
         (void *)X, 0, (int)(((uint32_t)(N - 1) * x_pitch + (uint32_t)K) * 4u), BUFFER_FLAGS);
     const uint32_t xrow = (uint32_t)tok * x_pitch * 4u;
-    // all loads first, then the conversions: one round trip, not NBW
-    uint32_t raw[NBW][8];
+    // The 8 k positions of group g come in two runs of 4 (Q4_0: 4g.. and
+    // 16+4g..; Q8_0: k0.. and k0+4..).  Lanes 2t and 2t+1 (token t, high and
+    // low part) need the same 8 values: each loads one run (the even lane
+    // run 0), converts it to both parts, and the pair trades the part the
+    // other lane feeds with one DPP swap.  That halves the load instructions:
+    // a CU's vector-memory path returns about 1 KB per 25 cycles, and with
+    // 8 tokens and one tile per workgroup the activations are most of a
+    // workgroup's bytes.  All loads first, then the conversions: one round
+    // trip, not NBW.
+    uint32_t raw[NBW][4];
 #pragma unroll
     for (int t = 0; t < NBW; ++t) {
         const int b = b_begin + t;
-        // the 8 k positions of group g come in two runs of 4 (Q4_0: 4g.. and
-        // 16+4g..; Q8_0: k0.. and k0+4..)
         const uint32_t base = (uint32_t)(32 * b) * 4;
         uint32_t o0, o1;
         if constexpr (WT == W_Q4_0) { o0 = base + 16 * g; o1 = base + 64 + 16 * g; }
         else { const int k0 = (g == 0) ? 0 : (g == 1) ? 16 : (g == 2) ? 8 : 24; o0 = base + 4 * k0; o1 = o0 + 16; }
         const bool in = b < nb && tok < N;
-        const auto p0 = __builtin_amdgcn_raw_buffer_load_b128(xres, in ? xrow + o0 : OUT_OF_RANGE, 0, 0);
-        const auto p1 = __builtin_amdgcn_raw_buffer_load_b128(xres, in ? xrow + o1 : OUT_OF_RANGE, 0, 0);
+        const auto p = __builtin_amdgcn_raw_buffer_load_b128(xres, in ? xrow + (lo_part ? o1 : o0) : OUT_OF_RANGE, 0, 0);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { raw[t][e] = p0[e]; raw[t][4 + e] = p1[e]; }
+        for (int e = 0; e < 4; ++e) raw[t][e] = p[e];
     }
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 xf[NBW];
 #pragma unroll
     for (int t = 0; t < NBW; ++t) {
-        float v[8];
-        float r0[4], r1[4];
+        float r[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            r0[e] = __builtin_bit_cast(float, raw[t][e]);
-            r1[e] = __builtin_bit_cast(float, raw[t][4 + e]);
-        }
-        if constexpr (WT == W_Q4_0) {
-            // order lo(s0) lo(s2) hi(s0) hi(s2) lo(s1) lo(s3) hi(s1) hi(s3)
-            v[0] = r0[0]; v[1] = r0[2]; v[2] = r1[0]; v[3] = r1[2];
-            v[4] = r0[1]; v[5] = r0[3]; v[6] = r1[1]; v[7] = r1[3];
-        } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { v[e] = r0[e]; v[4 + e] = r1[e]; }
-        }
+        for (int e = 0; e < 4; ++e) r[e] = __builtin_bit_cast(float, raw[t][e]);
+        // the run's two register pairs (Q4_0: elements 0, 2 and 1, 3 of the
+        // run, for lo(s0) lo(s2) | hi(s0) hi(s2) ...; Q8_0: 0, 1 and 2, 3)
+        float a0, a1, b0, b1;
+        if constexpr (WT == W_Q4_0) { a0 = r[0]; a1 = r[2]; b0 = r[1]; b1 = r[3]; }
+        else { a0 = r[0]; a1 = r[1]; b0 = r[2]; b1 = r[3]; }
+        const uint32_t hiA = pack_bf16(a0, a1), loA = pack_bf16(a0 - bf16_lo(hiA), a1 - bf16_hi(hiA));
+        const uint32_t hiB = pack_bf16(b0, b1), loB = pack_bf16(b0 - bf16_lo(hiB), b1 - bf16_hi(hiB));
+        const uint32_t keepA = lo_part ? loA : hiA, keepB = lo_part ? loB : hiB;
+        const uint32_t sendA = lo_part ? hiA : loA, sendB = lo_part ? hiB : loB;
+        // quad_perm [1, 0, 3, 2]: swap with the neighbouring lane
+        const uint32_t recvA = (uint32_t)__builtin_amdgcn_mov_dpp((int)sendA, 0xB1, 0xF, 0xF, true);
+        const uint32_t recvB = (uint32_t)__builtin_amdgcn_mov_dpp((int)sendB, 0xB1, 0xF, 0xF, true);
+        // register order: Q4_0 A(run 0) A(run 1) B(run 0) B(run 1);
+        // Q8_0 A(run 0) B(run 0) A(run 1) B(run 1)
         uint32_t w4[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const uint32_t hi = pack_bf16(v[2 * e], v[2 * e + 1]);
-            const uint32_t lo = pack_bf16(v[2 * e] - bf16_lo(hi), v[2 * e + 1] - bf16_hi(hi));
-            w4[e] = lo_part ? lo : hi;
+        if constexpr (WT == W_Q4_0) {
+            w4[0] = lo_part ? recvA : keepA; w4[1] = lo_part ? keepA : recvA;
+            w4[2] = lo_part ? recvB : keepB; w4[3] = lo_part ? keepB : recvB;
+        } else {
+            w4[0] = lo_part ? recvA : keepA; w4[1] = lo_part ? recvB : keepB;
+            w4[2] = lo_part ? keepA : recvA; w4[3] = lo_part ? keepB : recvB;
         }
         xf[t] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
     }
@@ -327,29 +339,30 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
     // sums of the KW waves (K ranges) meet in LDS and wave 0 stores the rows
     auto consume = [&](auto &stg, int tl, int it) {
         const uint8_t *base = stg[wave];
+        const int jr = j & (TR - 1);       // the tile row column j reads
         // row j's scales, then its units 4p + g
         uint32_t sc[St::SR / 4];
         if constexpr (St::SR == 4) {
-            sc[0] = *reinterpret_cast<const uint32_t *>(base + St::CODE_BYTES + St::SR * j);
+            sc[0] = *reinterpret_cast<const uint32_t *>(base + St::CODE_BYTES + St::SR * jr);
         } else if constexpr (St::SR == 8) {
-            const uint2 v = *reinterpret_cast<const uint2 *>(base + St::CODE_BYTES + St::SR * j);
+            const uint2 v = *reinterpret_cast<const uint2 *>(base + St::CODE_BYTES + St::SR * jr);
             sc[0] = v.x;
             sc[1] = v.y;
         } else {
 #pragma unroll
             for (int h = 0; h < St::SR / 16; ++h) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(base + St::CODE_BYTES + St::SR * j + 16 * h);
+                const uint4 v = *reinterpret_cast<const uint4 *>(base + St::CODE_BYTES + St::SR * jr + 16 * h);
                 sc[4 * h] = v.x;
                 sc[4 * h + 1] = v.y;
                 sc[4 * h + 2] = v.z;
                 sc[4 * h + 3] = v.w;
             }
         }
-        const uint8_t *rowp = base + (j / St::RPI) * 1024 + (j % St::RPI) * St::SB;
+        const uint8_t *rowp = base + (jr / St::RPI) * 1024 + (jr % St::RPI) * St::SB;
         float yp0 = 0.0f, yp1 = 0.0f;
 #pragma unroll
         for (int p = 0; p < NG; ++p) {
-            const uint4 cv = *reinterpret_cast<const uint4 *>(rowp + 16 * swz<St::U>(j, 4 * p + g));
+            const uint4 cv = *reinterpret_cast<const uint4 *>(rowp + 16 * swz<St::U>(jr, 4 * p + g));
             uint32_t d0 = cv.x, d1 = cv.y, d2 = cv.z, d3 = cv.w;
             // regroup: the four lane groups of each matrix instruction hold
             // disjoint code sets of one block
@@ -406,8 +419,8 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
                 s0 += red[it & 1][w2][lane][0];
                 s1 += red[it & 1][w2][lane][1];
             }
-            const int m = tl * kTileRows + j;
-            if (m < M) {
+            const int m = tl * TR + j;
+            if (j < TR && m < M) {
                 float *y0 = Y + (uint64_t)(2 * g) * y_pitch + m;
                 float *y1 = y0 + y_pitch;
                 if (2 * g < N) *y0 = acc ? *y0 + s0 : s0;
@@ -459,24 +472,44 @@ using MfKernel = void (*)(const MfArgs);
 // per wave.  Three stages for both types (measured at K = 2048 and 5632,
 // 4 and 8 tokens): a Q4_0 workgroup then needs 63 KB of LDS and two share
 // a CU, 2-4 % faster than one with four stages; Q8_0 with two stages (two
-// workgroups per CU) is as fast at 4 tokens and 4 % slower at 8.
+// workgroups per CU) is as fast at 4 tokens and 4 % slower at 8.  (The
+// stage count drops to what fits 160 KiB, e.g. two for the wide launch.)
 constexpr int kWaves = 8;
 // Blocks of K one launch covers (16 per wave); longer rows take several
 // launches, the later ones adding to y.
 constexpr int kPassBlocks = 16 * kWaves;
-template <int WT> constexpr int max_stages() { return 3; }
+constexpr int kStages = 3;
+
+// Rows of 129 to 192 blocks (K = 4128 .. 6144; a down projection's 5632)
+// run in ONE launch of twelve waves x 16 blocks instead of two passes.
+// Short matrices of such rows give each workgroup one tile, so the passes'
+// fixed costs (launch, activation set-up, the last wave's data) are paid
+// once.  Measured on 2048 x 5632 (graph-replayed, Q4_0, 8 tokens):
+// 7.9 us against 14.2 us in two passes.  A Q4_0 tile keeps 16 rows (two
+// 55 KB stages); Q8_0 takes 8-row tiles, since 16 rows x 512 code bytes x
+// 12 waves would not fit two stages in the LDS.
+constexpr int kWideWaves = 12;
+constexpr int kWideBlocks = 16 * kWideWaves;
+template <int WT> constexpr int wide_tile_rows() { return WT == W_Q4_0 ? 16 : 8; }
 
 // The kernel for (type, NBW, scale shift) and its LDS bytes.
 template <int WT, int SS>
 MfKernel pick_mf(int nbw, int *lds)
 {
-    constexpr int D = max_stages<WT>();
+    constexpr int D = kStages, T = kTileRows;
     switch (nbw) {
-    case 4: *lds = mf_lds_bytes<WT, kWaves, 4, SS>(mf_stages<WT, kWaves, 4, SS, D>()); return gemv_mf_kernel<WT, kWaves, 4, SS, D>;
-    case 8: *lds = mf_lds_bytes<WT, kWaves, 8, SS>(mf_stages<WT, kWaves, 8, SS, D>()); return gemv_mf_kernel<WT, kWaves, 8, SS, D>;
-    case 16: *lds = mf_lds_bytes<WT, kWaves, 16, SS>(mf_stages<WT, kWaves, 16, SS, D>()); return gemv_mf_kernel<WT, kWaves, 16, SS, D>;
+    case 4: *lds = mf_lds_bytes<WT, kWaves, 4, SS, T>(mf_stages<WT, kWaves, 4, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 4, SS, D, T>;
+    case 8: *lds = mf_lds_bytes<WT, kWaves, 8, SS, T>(mf_stages<WT, kWaves, 8, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 8, SS, D, T>;
+    case 16: *lds = mf_lds_bytes<WT, kWaves, 16, SS, T>(mf_stages<WT, kWaves, 16, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 16, SS, D, T>;
     default: return nullptr;
     }
+}
+template <int WT, int SS>
+MfKernel pick_wide(int *lds)
+{
+    constexpr int T = wide_tile_rows<WT>();
+    *lds = mf_lds_bytes<WT, kWideWaves, 16, SS, T>(mf_stages<WT, kWideWaves, 16, SS, kStages, T>());
+    return gemv_mf_kernel<WT, kWideWaves, 16, SS, kStages, T>;
 }
 
 // Blocks per wave for a pass of nb blocks (0 if out of range).
@@ -512,17 +545,23 @@ hipError_t launch_gemv_mf(const GemvTask *tasks, int count, hipStream_t stream)
     const int64_t K = tasks[0].w.K;
     const int64_t N = tasks[0].x.N;
     const int64_t nb_row = K / 32;
+    const int ss = tasks[0].w.scale_shift;
+    const bool wide = nb_row > kPassBlocks && nb_row <= kWideBlocks;
+    const int tr = !wide ? kTileRows : type == W_Q4_0 ? wide_tile_rows<W_Q4_0>() : wide_tile_rows<W_Q8_0>();
+    const int64_t pass = wide ? kWideBlocks : kPassBlocks;
+    const int waves = wide ? kWideWaves : kWaves;
     int64_t tiles_total = 0;
-    for (int i = 0; i < count; ++i) tiles_total += (tasks[i].w.M + kTileRows - 1) / kTileRows;
+    for (int i = 0; i < count; ++i) tiles_total += (tasks[i].w.M + tr - 1) / tr;
     if (tiles_total == 0 || N == 0 || nb_row == 0) return hipSuccess;
     for (int64_t n0 = 0; n0 < N; n0 += 8) {
         // passes over K in stream order: the first stores y, the others add
-        for (int64_t kb0 = 0; kb0 < nb_row; kb0 += kPassBlocks) {
-            const int64_t nb = nb_row - kb0 < kPassBlocks ? nb_row - kb0 : kPassBlocks;
+        for (int64_t kb0 = 0; kb0 < nb_row; kb0 += pass) {
+            const int64_t nb = nb_row - kb0 < pass ? nb_row - kb0 : pass;
             MfKernel k = nullptr;
             int lds = kLdsBytes;
-            const int ss = tasks[0].w.scale_shift;
-            if (type == W_Q4_0) k = ss ? pick_mf<W_Q4_0, 1>(mf_nbw(nb), &lds) : pick_mf<W_Q4_0, 0>(mf_nbw(nb), &lds);
+            if (wide && type == W_Q4_0) k = ss ? pick_wide<W_Q4_0, 1>(&lds) : pick_wide<W_Q4_0, 0>(&lds);
+            else if (wide && type == W_Q8_0) k = ss ? pick_wide<W_Q8_0, 1>(&lds) : pick_wide<W_Q8_0, 0>(&lds);
+            else if (type == W_Q4_0) k = ss ? pick_mf<W_Q4_0, 1>(mf_nbw(nb), &lds) : pick_mf<W_Q4_0, 0>(mf_nbw(nb), &lds);
             else if (type == W_Q8_0) k = ss ? pick_mf<W_Q8_0, 1>(mf_nbw(nb), &lds) : pick_mf<W_Q8_0, 0>(mf_nbw(nb), &lds);
             if (!k) return hipErrorInvalidValue;
             // a workgroup streams several tiles with its activation fragments
@@ -548,14 +587,14 @@ hipError_t launch_gemv_mf(const GemvTask *tasks, int count, hipStream_t stream)
                 it.x_pitch = (uint32_t)tasks[i].x.pitch_elems;
                 it.y = tasks[i].y.data + (uint64_t)n0 * tasks[i].y.pitch_elems;
                 it.y_pitch = (uint32_t)tasks[i].y.pitch_elems;
-                it.n_tiles = (int32_t)((tasks[i].w.M + kTileRows - 1) / kTileRows);
+                it.n_tiles = (int32_t)((tasks[i].w.M + tr - 1) / tr);
                 int64_t wgs = (int64_t)it.n_tiles * cap / tiles_total;
                 if (wgs < 1) wgs = 1;
                 if (wgs > it.n_tiles) wgs = it.n_tiles;
                 it.wg_count = (int32_t)wgs;
                 if (wgs > wg_max) wg_max = (int32_t)wgs;
             }
-            hipLaunchKernelGGL(k, dim3((unsigned)wg_max, (unsigned)a.n_items), dim3(64 * kWaves), 0, stream, a);
+            hipLaunchKernelGGL(k, dim3((unsigned)wg_max, (unsigned)a.n_items), dim3(64 * waves), 0, stream, a);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

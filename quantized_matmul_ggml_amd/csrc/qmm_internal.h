@@ -127,8 +127,8 @@ hipError_t launch_gemv_swiglu(const WeightView &wg, const WeightView &wu, const 
                               const OutView &h, hipStream_t stream);
 
 // The matrix-core GEMV with register-resident activation fragments
-// (gemv_mf.hip): Q4_0 / Q8_0 weights, weight pitch <= 2^27; K beyond 4096 in
-// passes that add to y.
+// (gemv_mf.hip): Q4_0 / Q8_0 weights, weight pitch <= 2^27; K up to 6144 in
+// one launch, longer rows in passes that add to y.
 bool gemv_mf_supported(const GemvTask *tasks, int count);
 hipError_t launch_gemv_mf(const GemvTask *tasks, int count, hipStream_t stream);
 // Measurement kernels (probe.hip): a streaming read of `bytes` (multiple of

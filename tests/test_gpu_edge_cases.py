@@ -80,19 +80,21 @@ def _swiglu_tol(orc, gref, eg, uref, eu, href):
 
 GEMV_EDGE = [
     # (type, M, K, N, mean): the VALU kernel (1 and 2 tokens; 3-4 tokens
-    # below 8192 rows), one and several waves per row
+    # up to 2048 rows of at most 4096), one and several waves per row
     ("Q4_0", 300, 2048, 1, 5.0), ("Q4_0", 257, 5632, 1, 5.0), ("Q4_0", 130, 2048, 2, -5.0),
     ("Q4_0", 99, 32768, 1, 5.0), ("Q4_0", 100, 2048, 3, 5.0),
     ("Q8_0", 300, 2048, 1, 5.0), ("Q8_0", 129, 5632, 2, 5.0), ("Q8_0", 77, 1024, 4, -5.0),
     ("Q8_0", 512, 512, 1, 5.0),
     ("F16", 300, 2048, 1, 5.0), ("F16", 65, 1024, 2, 5.0),
     ("Q4_B64", 300, 2048, 1, 5.0), ("Q8_B64", 130, 2048, 2, 5.0),
-    # the matrix-core kernel: 3-4 tokens over 8192 rows, 5-8 tokens, K over
-    # 4096 in passes that add to y
-    ("Q4_0", 8200, 2048, 4, 5.0), ("Q8_0", 8195, 1024, 3, 5.0),
+    # the matrix-core kernel: 3-4 tokens over 2048 rows, 5-8 tokens, K of
+    # 129..192 blocks in one launch (from 3 tokens), longer K in passes that
+    # add to y (7-8 tokens)
+    ("Q4_0", 8200, 2048, 4, 5.0), ("Q8_0", 8195, 1024, 3, 5.0), ("Q4_0", 2600, 2048, 3, -5.0),
     ("Q4_0", 300, 2048, 5, 5.0), ("Q8_0", 300, 2048, 8, -5.0), ("Q4_0", 257, 160, 6, 5.0),
-    ("Q4_0", 300, 5632, 6, 5.0), ("Q8_0", 77, 16384, 5, 5.0), ("Q8_0", 31, 2080, 7, 5.0),
-    ("Q4_B64", 64, 4096, 7, 5.0), ("Q8_B64", 8200, 2048, 4, 5.0),
+    ("Q4_0", 300, 5632, 6, 5.0), ("Q4_0", 2048, 5632, 3, 5.0), ("Q8_0", 129, 5632, 5, 5.0),
+    ("Q8_0", 77, 16384, 7, 5.0), ("Q8_0", 31, 2080, 7, 5.0),
+    ("Q4_B64", 64, 4096, 7, 5.0), ("Q8_B64", 8200, 2048, 4, 5.0), ("Q8_B64", 100, 5632, 8, -5.0),
 ]
 
 

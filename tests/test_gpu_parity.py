@@ -245,10 +245,17 @@ GEMV_CASES = [
     # past that kernel's range
     ("Q4_0", 40, 96, 5), ("Q4_0", 257, 160, 6), ("Q4_0", 17, 1056, 5), ("Q4_0", 1000, 4096, 6),
     ("Q8_0", 31, 2080, 6), ("Q8_0", 1001, 4096, 5), ("Q8_0", 64, 4128, 8),
-    # 3 and 4 tokens over 8192 rows or more take the matrix cores too
-    ("Q4_0", 8200, 2048, 3), ("Q8_0", 8195, 1024, 4),
-    # K beyond 128 blocks: passes that add to y (Wdown's K = 5632; four passes)
-    ("Q4_0", 300, 5632, 6), ("Q8_0", 77, 16384, 5),
+    # 3 and 4 tokens over more than 2048 rows take the matrix cores too;
+    # 2048 rows stay on the VALU kernel
+    ("Q4_0", 8200, 2048, 3), ("Q8_0", 8195, 1024, 4), ("Q4_0", 2049, 2048, 3), ("Q8_0", 2600, 1024, 4),
+    ("Q4_0", 2048, 2048, 3),
+    # K of 129..192 blocks: one twelve-wave launch (16-row Q4_0 tiles, 8-row
+    # Q8_0 tiles), from 3 tokens; the down projection itself at 8 tokens
+    ("Q4_0", 300, 5632, 6), ("Q4_0", 2048, 5632, 8), ("Q4_0", 37, 4128, 3), ("Q8_0", 300, 5632, 5),
+    ("Q8_0", 45, 6144, 4), ("Q8_0", 2048, 5632, 8),
+    # K beyond 192 blocks: passes of 128 blocks that add to y (7-8 tokens;
+    # fewer stay on the VALU kernel)
+    ("Q4_0", 100, 6176, 7), ("Q8_0", 77, 16384, 8), ("Q8_0", 77, 16384, 5),
     # the streaming kernel (F16 rows; two tokens; Q8_0 over 8192 rows at one
     # token) with ragged groups and grids, and shapes past its limits that
     # stay on the other kernel (more than 8 row groups per wave; wide rows)
@@ -257,6 +264,7 @@ GEMV_CASES = [
     # 64-weight blocks (one scale per two 32-code runs)
     ("Q4_B64", 5632, 2048, 1), ("Q8_B64", 300, 5632, 3), ("Q4_B64", 100, 192, 8), ("Q8_B64", 4099, 2048, 2),
     ("Q4_B64", 64, 16384, 5), ("Q8_B64", 1, 64, 1), ("Q4_B64", 8200, 2048, 4),
+    ("Q4_B64", 129, 5632, 7), ("Q8_B64", 64, 4160, 8), ("Q4_B64", 64, 16384, 8),
 ]
 
 
@@ -826,12 +834,13 @@ def test_gemv_batch_decoder_layer(orc):
         _assert_tol(y.cpu().numpy(), yref, a, 1e-4, 1e-6, f"batch {name}")
 
 
-@pytest.mark.parametrize("tname", ["Q8_0", "Q4_0", "F16"])
-def test_gemv_batch_ragged_items(orc, tname):
-    """Items of 1, 0, 300 and 4100 rows sharing one x, N = 5 (split into
-    token chunks), outputs in guard-banded buffers."""
-    K, N = 2048, 5
-    _banner(f"gemv batch ragged {tname}")
+@pytest.mark.parametrize("tname,K", [("Q8_0", 2048), ("Q4_0", 2048), ("F16", 2048), ("Q4_0", 5632), ("Q8_0", 5632)])
+def test_gemv_batch_ragged_items(orc, tname, K):
+    """Items of 1, 0, 300 and 4100 rows sharing one x, N = 5, outputs in
+    guard-banded buffers; K = 5632 takes the one-launch matrix-core kernel
+    with several items."""
+    N = 5
+    _banner(f"gemv batch ragged {tname} K={K}")
     x = WL.activations(31, N, K)
     xt = torch.from_numpy(x).to(DEV)
     items, refs, bufs = [], [], []
