@@ -179,8 +179,9 @@ QMM_API int qmm_dequantize(const qmm_tensor *src, qmm_tensor *dst_f32, void *str
  * the exact sum within 1e-4 * sum_k |W'[m][k] x[n][k]| + 1e-6 for every
  * output and every input: each product is a signed code times x, so the
  * rounding error is relative to sum |W' x|, never to a larger biased sum).
- * From 5 tokens (3 when the call has at least 8192 rows), quantized weights
- * go to the bf16 matrix cores instead: signed codes enter exactly, x as two
+ * From 5 tokens (from 3 when the call has more than 2048 rows or K above
+ * 4096; from 7 when K is above 6144), quantized weights go to the bf16
+ * matrix cores instead: signed codes enter exactly, x as two
  * bfloat16 parts (x = hi + lo to 2^-17 relative), products accumulated in
  * binary32, within the same bound. */
 /* Integer activations ("A Complete Guide to llama.cpp ...", §2.2: with x
