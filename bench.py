@@ -181,13 +181,28 @@ def main():
                 Q.gemv(L[name], xs[slot], out=ys[name])
         Q.gemv(lm, x_lm, out=y_lm)
 
-    def step_dependent():
-        for L in layers:
-            Q.gemv_batch([(L[n], xs[0], ys[n]) for n in ("wq", "wk", "wv")])
-            Q.gemv(L["wo"], xs[1], out=ys["wo"])
-            Q.gemv_batch([(L[n], xs[2], ys[n]) for n in ("wgate", "wup")])
-            Q.gemv(L["wdown"], xs[3], out=ys["wdown"])
-        Q.gemv(lm, x_lm, out=y_lm)
+    def dependent(xs, ys, x_lm, y_lm):
+        def step():
+            for L in layers:
+                Q.gemv_batch([(L[n], xs[0], ys[n]) for n in ("wq", "wk", "wv")])
+                Q.gemv(L["wo"], xs[1], out=ys["wo"])
+                Q.gemv_batch([(L[n], xs[2], ys[n]) for n in ("wgate", "wup")])
+                Q.gemv(L["wdown"], xs[3], out=ys["wdown"])
+            Q.gemv(lm, x_lm, out=y_lm)
+        return step
+
+    step_dependent = dependent(xs, ys, x_lm, y_lm)
+
+    # the dependent schedule for 8 sequences decoded together: 8 tokens per
+    # launch, every launch on the matrix-core kernels
+    NB = 8
+    xs8 = [WL.activations_device(WL.seed(3, 20 + s), NB, k, dev) for s, k in enumerate(WL.LAYER_X_K)]
+    ys8 = {name: torch.empty((NB, M), device=dev) for name, M, _, _ in WL.LAYER}
+    x_lm8 = WL.activations_device(WL.seed(4, 2), NB, WL.HIDDEN, dev)
+    y_lm8 = torch.empty((NB, WL.VOCAB), device=dev)
+    step_dependent_8 = dependent(xs8, ys8, x_lm8, y_lm8)
+    step_bytes_8 = (WL.LAYERS * sum(gemv_bytes(layers[0][name], NB) for name, *_ in WL.LAYER)
+                    + gemv_bytes(lm, NB))
 
     def step_grouped():
         for L in layers:
@@ -210,18 +225,19 @@ def main():
     fused_bytes = step_bytes - WL.LAYERS * (4 * WL.HIDDEN + 4 * WL.FFN)
 
     variants = {}
-    for vname, fn, launches, nbytes in (
-            ("per_matrix", step_per_matrix, 7 * WL.LAYERS + 1, step_bytes),
-            ("dependent", step_dependent, 4 * WL.LAYERS + 1, step_bytes),
-            ("grouped", step_grouped, 2 * WL.LAYERS + 1, step_bytes),
-            ("dependent_swiglu_fused", step_fused, 4 * WL.LAYERS + 1, fused_bytes)):
+    for vname, fn, launches, nbytes, ntok in (
+            ("per_matrix", step_per_matrix, 7 * WL.LAYERS + 1, step_bytes, 1),
+            ("dependent", step_dependent, 4 * WL.LAYERS + 1, step_bytes, 1),
+            ("grouped", step_grouped, 2 * WL.LAYERS + 1, step_bytes, 1),
+            ("dependent_swiglu_fused", step_fused, 4 * WL.LAYERS + 1, fused_bytes, 1),
+            ("dependent_8_tokens", step_dependent_8, 4 * WL.LAYERS + 1, step_bytes_8, NB)):
         log(f"decode step [{vname}]: capturing {launches} launches into a HIP graph")
         graph = Graph(fn)
         ms_v, wall_v = timed(graph, args.steps, args.warmup)
-        variants[vname] = {"ms": ms_v, "wall": wall_v, "launches": launches,
+        variants[vname] = {"ms": ms_v, "wall": wall_v, "launches": launches, "tokens": ntok,
                            "gbs": nbytes / (ms_v * 1e-3) / 1e9}
         log(f"decode step [{vname}] {ms_v * 1e3:.1f} us  {variants[vname]['gbs']:.0f} GB/s  "
-            f"{1e3 / ms_v:.0f} tokens/s")
+            f"{ntok * 1e3 / ms_v:.0f} tokens/s")
     head = "dependent"
     ms, wall = variants[head]["ms"], variants[head]["wall"]
     value = variants[head]["gbs"]
@@ -294,7 +310,8 @@ def main():
             "block_gemm_inner_loop": inner,
             "wall_s_timed_region": round(wall, 4),
             "variants": {k: {"us": round(v["ms"] * 1e3, 1), "gbs": round(v["gbs"], 1),
-                             "launches": v["launches"], "tokens_per_s": round(1e3 / v["ms"], 1)}
+                             "launches": v["launches"], "tokens_per_launch": v["tokens"],
+                             "tokens_per_s": round(v["tokens"] * 1e3 / v["ms"], 1)}
                          for k, v in variants.items()},
             "swiglu_fused_gate_up": ceiling.attach({"kernel": "Q4_0 gate/up 2 x 5632 x 2048 + SwiGLU, batch 1",
                                      "avg_launch_us": round(sw_ms * 1e3, 3), "bytes_per_launch": sw_bytes,
