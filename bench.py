@@ -545,6 +545,12 @@ def prefill_leg(Q, WL, dev, args):
     ms_b, _ = timed(g64, max(2, args.steps // 2), 2)
     tf_b = flops / (ms_b / reps * 1e-3) / 1e12
     log(f"prefill GEMM, Q4_B64 weights {ms_b / reps * 1e3:.1f} us  {tf_b:.0f} TFLOP/s")
+    # and with Q8_0 weights (twice the code bytes per step)
+    w8 = Q.quantize(WL.weights_device(WL.seed(5, 0), M, K, dev), Q.Q8_0)
+    g8 = Graph(lambda: [Q.gemm(w8, x, out=y) for _ in range(reps)])
+    ms_8, _ = timed(g8, max(2, args.steps // 2), 2)
+    tf_8 = flops / (ms_8 / reps * 1e-3) / 1e12
+    log(f"prefill GEMM, Q8_0 weights {ms_8 / reps * 1e3:.1f} us  {tf_8:.0f} TFLOP/s")
     # the layer's other prefill shapes, which leave compute units idle at 128 x 128
     # tiles: K split over a workspace (two launches) against one launch without
     shapes = {}
@@ -609,6 +615,8 @@ def prefill_leg(Q, WL, dev, args):
                             "frac_of_bf16_peak": round(tf_f / BF16_PEAK_TFLOPS, 4)},
             "q4_b64_weights": {"us": round(ms_b / reps * 1e3, 2), "tflops": round(tf_b, 1),
                                "frac_of_bf16_peak": round(tf_b / BF16_PEAK_TFLOPS, 4)},
+            "q8_0_weights": {"us": round(ms_8 / reps * 1e3, 2), "tflops": round(tf_8, 1),
+                             "frac_of_bf16_peak": round(tf_8 / BF16_PEAK_TFLOPS, 4)},
             "split_k_shapes": shapes,
             "layer_512_tokens": layer}
 
