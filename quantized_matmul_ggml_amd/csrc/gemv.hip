@@ -44,14 +44,16 @@ namespace {
 // same number of waves with sixteen-wave workgroups.
 inline int max_workgroups(int ks, int wgw) { return (ks == 1 ? 2048 : 1024) * 4 / wgw; }
 // Every workgroup stages all K activations of its tokens, so rows longer than
-// 4096 with two or more tokens take a smaller grid, each workgroup streaming
-// more rows per staging (measured on 2048 x 5632 Q4_0: 3 / 4 tokens 10.2 /
-// 11.2 us with the full grid, 8.2 / 8.8 us with 512 workgroups, slower again
-// with 384 or 256).
-inline int max_workgroups(int ks, int wgw, int64_t K, int nt)
+// 4096 take a smaller grid, each workgroup streaming more rows per staging
+// (measured on 2048 x 5632 Q4_0: 3 / 4 tokens 10.2 / 11.2 us with the full
+// grid, 8.2 / 8.8 us with 512 workgroups, slower again with 384 or 256; at
+// one token, graph-replayed: 4096 x 11008 12.5 -> 10.5 us, 4096 x 8192 7.1
+// -> 6.7, 8192 x 8192 10.9 -> 10.4, 11008 x 5632 12.4 -> 12.2, 2048 x 5632
+// unchanged at 4.2).
+inline int max_workgroups(int ks, int wgw, int64_t K)
 {
     const int cap = max_workgroups(ks, wgw);
-    return (K > 4096 && nt >= 2 && cap > 512) ? 512 : cap;
+    return (K > 4096 && cap > 512) ? 512 : cap;
 }
 constexpr int kMaxItems = QMM_GEMV_BATCH_MAX;
 // Which launches the matrix-core kernels take (measured on the decoder's
@@ -996,7 +998,7 @@ hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t strea
         for (int i = 0; i < count; ++i) {
             if (tasks[i].w.M == 0) continue;
             int64_t wgs = need[i];
-            const int wg_cap = max_workgroups(c.ks, c.wgw, K, c.nt);
+            const int wg_cap = max_workgroups(c.ks, c.wgw, K);
             if (need_total > wg_cap) {
                 wgs = need[i] * wg_cap / need_total;   // share of the persistent grid
                 if (wgs < 1) wgs = 1;

@@ -237,6 +237,8 @@ GEMV_CASES = [
     ("Q8_0", 130, 4096, 8), ("Q8_0", 64, 16384, 1), ("Q8_0", 300, 2048, 7),
     ("Q4_0", 1, 32, 1), ("Q4_0", 257, 5632, 1), ("Q4_0", 4100, 2048, 1), ("Q4_0", 100, 2048, 3),
     ("Q4_0", 33, 32768, 1), ("Q4_0", 5, 8192, 4), ("Q4_0", 300, 2048, 8), ("Q4_0", 4099, 2048, 2),
+    # rows over 4096 at one token on more row groups than the 512 workgroups
+    ("Q4_0", 4100, 8192, 1), ("Q8_0", 3000, 5632, 1),
     ("F16", 5632, 2048, 1),         # the fp16 FFN up-projection GEMV
     ("F16", 1, 7, 1), ("F16", 65, 1000, 2), ("F16", 4101, 2048, 1), ("F16", 10, 8192, 1),
     ("F16", 77, 520, 8),
