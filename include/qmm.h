@@ -196,7 +196,10 @@ QMM_API int qmm_dequantize(const qmm_tensor *src, qmm_tensor *dst_f32, void *str
  * sum_b |block term|).  This approximates the fp32-activation product by the
  * quantization of x: |y - sum_k W' x| <= sum_k |W'_k| Delta_x / 2.  K up to
  * 16384 (Q8_0) or 32768 (Q4_0), else QMM_ERR_UNSUPPORTED; tokens go in
- * passes over the weights of up to 8 (fewer for long rows). */
+ * passes over the weights of up to 8 (fewer for long rows).  Q8_0 weights
+ * from 5 tokens with at least 8192 rows or K above 4096 run on the bf16
+ * matrix cores, where the codes enter exactly and the block sums are exact
+ * too (same arithmetic, same bound). */
 QMM_API int qmm_gemv(const qmm_tensor *w, const qmm_tensor *x_f32, qmm_tensor *y_f32, void *stream);
 
 /* Most GEMVs one qmm_gemv_batch call takes. */

@@ -56,23 +56,6 @@ inline int max_workgroups(int ks, int wgw, int64_t K)
     return (K > 4096 && cap > 512) ? 512 : cap;
 }
 constexpr int kMaxItems = QMM_GEMV_BATCH_MAX;
-// Which launches the matrix-core kernels take (measured on the decoder's
-// shapes, graph-replayed): from 5 tokens every one; at 3 and 4 tokens those
-// of more than 2048 rows or of rows over 4096 (5632 x 2048: 5.8 against
-// 7.3 us at 3 tokens; 2048 x 5632: 7.5 against 8.2), while 2048 x 2048
-// stays on the VALU kernel (3.95 against 4.2 us at 3 tokens), whose cost
-// per weight grows with the tokens but whose grid fills the chip at any
-// row count.
-// Rows over 192 blocks (K > 6144) run on the matrix cores as several
-// dependent passes, and the VALU kernel's one launch is faster up to 6
-// tokens (2048 x 5632 Q4_0 in two passes: 12.7 / 14.1 us on the VALU kernel
-// against 14.3 / 14.8 at 5 / 6 tokens; 16.7 against 15.3 at 8).
-inline bool use_matrix_cores(int64_t N, int64_t m_total, int64_t K)
-{
-    if (K > 6144) return N >= 7;
-    if (N >= 5) return true;
-    return N >= 3 && (m_total > 2048 || K > 4096);
-}
 
 // One GEMV of a launch: its weights, activations and outputs.  All items of
 // a launch share the weight type, K and the token count.  An item is one

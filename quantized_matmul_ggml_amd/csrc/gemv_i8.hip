@@ -374,6 +374,17 @@ hipError_t launch_i8(const WeightView *w, const WeightView *w2, const WeightView
     int64_t m_total = 0;
     for (int i = 0; i < count; ++i) m_total += w[i].M;
     if (m_total == 0 || N == 0) return hipSuccess;
+    // Q8_0 weights from 5 tokens over 8192 rows or more, or rows over 4096,
+    // go to the matrix cores, where the codes enter exactly and each block's
+    // sum is exact as well (graph-replayed, µs at 5 / 8 tokens: the
+    // 32000 x 2048 LM head 16.5 / 16.7 against 20.7 / 21.0 here; 2048 x 5632
+    // 8.5 / 8.6 against 13.1 / 13.2; 16384 x 2048 10.2 / 10.3 against 11.8 /
+    // 12.5; 8192 x 2048 equal; 2048 x 2048 4.9 / 5.2 against 4.6 / 4.3).
+    // This kernel keeps Q4_0 weights (e.g. 11264 x 2048 at 8 tokens: 7.9
+    // against 9.6 us) and up to 4 tokens.
+    if (!sw && w[0].type == W_Q8_0 && N >= 5 && (m_total >= 8192 || w[0].K > 4096) &&
+        use_matrix_cores(N, m_total, w[0].K) && gemv_mf_q8x_supported(w, xq, count, N))
+        return launch_gemv_mf_q8x(w, xq, y, count, N, stream);
     const WeightView &w0 = w[0];
     GemvConfig c;
     if (!i8_config(w0.type, w0.K, sw ? 2 * m_total : m_total, N, &c)) return hipErrorInvalidValue;

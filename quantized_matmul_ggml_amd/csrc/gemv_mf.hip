@@ -52,10 +52,10 @@ template <> struct MfFmt<W_Q8_0> { static constexpr int bpg = 2, block_bytes = 3
 
 struct alignas(64) MfItem {
     const uint8_t *w;
-    const float *x;
+    const void *x;        // fp32 rows, or Q8_0 rows (whole rows, whatever the pass)
     float *y;
     uint32_t pitch;       // bytes between weight rows
-    uint32_t x_pitch;     // elements between token rows of x
+    uint32_t x_pitch;     // between token rows of x: elements (fp32) or bytes (Q8_0)
     uint32_t y_pitch;     // elements between token rows of y
     int32_t M;
     int32_t n_tiles;      // 16-row tiles
@@ -66,14 +66,15 @@ static_assert(sizeof(MfItem) == 64, "one 64-byte record per item");
 
 struct MfArgs {
     int32_t N;            // tokens of this launch (<= 8)
-    int32_t K;            // K of this pass (32 nb); x points at its first element
+    int32_t K;            // K of this pass (32 nb); fp32 x points at its first element
     int32_t qoff;         // byte offset of the codes in a row
     int32_t nb;           // 32-blocks of this pass (<= 128; <= 192 in the wide launch)
     int32_t n_items;
     int32_t kb0;          // first block of this pass within the row
     int32_t nb_row;       // 32-blocks per row
     int32_t accumulate;   // add to y (a later pass over K) instead of storing
-    int32_t pad[8];
+    int32_t xqoff;        // Q8_0 activations: byte offset of the codes in an x row
+    int32_t pad[7];
     MfItem item[kMaxMfItems];
 };
 
@@ -198,7 +199,17 @@ constexpr int mf_stages()
     return d;
 }
 
-template <int WT, int KW, int NBW, int SS, int MAXD, int TR>
+// XQ: the activations are Q8_0 rows (A Complete Guide to llama.cpp and
+// Customization with C++, §2.2: with x quantized per block, a block's dot
+// product is Delta * Delta_x * sum_i q_i qx_i), for Q8_0 weights.  Channel
+// 2n then carries token n's int8 codes, exact in bf16, and channel 2n + 1
+// zeros; the matrix instruction's sum over one block is the exact integer
+// sum_i q_i qx_i (|sum| < 2^19), and each block term is one fused
+// multiply-add of the exact product Delta * Delta_x (two 11-bit
+// significands) with it.  (Q4_0 weights with Q8_0 activations stay on the
+// int8 dot-product kernel, measured faster: their 8 codes per lane and block
+// come in two 4-byte runs, two load instructions per block.)
+template <int WT, int KW, int NBW, int SS, int MAXD, int TR, bool XQ>
 __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
 {
     constexpr int NSTG = mf_stages<WT, KW, NBW, SS, MAXD, TR>();
@@ -209,6 +220,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
     static_assert(NBW % BPG == 0, "whole load groups");
     using St = MfStage<WT, NBW, SS, TR>;
     static_assert(NSTG >= 2 && NSTG <= 4, "2 to 4 stages");
+    static_assert(!XQ || WT == W_Q8_0, "Q8_0 activations with Q8_0 weights");
     __shared__ float red[2][KW][64][2];
     // one array per stage, so that each wait for a stage's loads counts only
     // the loads issued before them
@@ -226,13 +238,15 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
     const int item = blockIdx.y;
     const MfItem &itm = a.item[item];
     const uint8_t *const W = itm.w;
-    const float *const X = itm.x;
+    const void *const X = itm.x;
     float *const Y = itm.y;
     const uint32_t pitch = itm.pitch, x_pitch = itm.x_pitch, y_pitch = itm.y_pitch;
     const int M = itm.M, n_tiles = itm.n_tiles, n_wg = itm.wg_count;
     const int N = a.N, K = a.K, qoff = a.qoff, nb = a.nb, kb0 = a.kb0, nb_row = a.nb_row, acc = a.accumulate;
+    const int xqoff = a.xqoff;
     asm volatile("" ::"s"(W), "s"(X), "s"(Y), "s"(pitch), "s"(x_pitch), "s"(y_pitch), "s"(M),
-                 "s"(n_tiles), "s"(n_wg), "s"(N), "s"(K), "s"(qoff), "s"(nb), "s"(kb0), "s"(nb_row), "s"(acc));
+                 "s"(n_tiles), "s"(n_wg), "s"(N), "s"(K), "s"(qoff), "s"(nb), "s"(kb0), "s"(nb_row), "s"(acc),
+                 "s"(xqoff));
     if ((int)blockIdx.x >= n_wg) return;
     const int b_begin = wave * NBW;
 
@@ -278,61 +292,116 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
     // j / 2, part j % 2; blocks past the row and tokens past N read zeros ----
     const int tok = j >> 1;
     const bool lo_part = (j & 1) != 0;
-    const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)X, 0, (int)(((uint32_t)(N - 1) * x_pitch + (uint32_t)K) * 4u), BUFFER_FLAGS);
-    const uint32_t xrow = (uint32_t)tok * x_pitch * 4u;
-    // The 8 k positions of group g come in two runs of 4 (Q4_0: 4g.. and
-    // 16+4g..; Q8_0: k0.. and k0+4..).  Lanes 2t and 2t+1 (token t, high and
-    // low part) need the same 8 values: each loads one run (the even lane
-    // run 0), converts it to both parts, and the pair trades the part the
-    // other lane feeds with one DPP swap.  That halves the load instructions:
-    // a CU's vector-memory path returns about 1 KB per 25 cycles, and with
-    // 8 tokens and one tile per workgroup the activations are most of a
-    // workgroup's bytes.  All loads first, then the conversions: one round
-    // trip, not NBW.
-    uint32_t raw[NBW][4];
-#pragma unroll
-    for (int t = 0; t < NBW; ++t) {
-        const int b = b_begin + t;
-        const uint32_t base = (uint32_t)(32 * b) * 4;
-        uint32_t o0, o1;
-        if constexpr (WT == W_Q4_0) { o0 = base + 16 * g; o1 = base + 64 + 16 * g; }
-        else { const int k0 = (g == 0) ? 0 : (g == 1) ? 16 : (g == 2) ? 8 : 24; o0 = base + 4 * k0; o1 = o0 + 16; }
-        const bool in = b < nb && tok < N;
-        const auto p = __builtin_amdgcn_raw_buffer_load_b128(xres, in ? xrow + (lo_part ? o1 : o0) : OUT_OF_RANGE, 0, 0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) raw[t][e] = p[e];
-    }
-    __builtin_amdgcn_sched_barrier(0);
     bf16x8 xf[NBW];
-#pragma unroll
-    for (int t = 0; t < NBW; ++t) {
-        float r[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = __builtin_bit_cast(float, raw[t][e]);
-        // the run's two register pairs (Q4_0: elements 0, 2 and 1, 3 of the
-        // run, for lo(s0) lo(s2) | hi(s0) hi(s2) ...; Q8_0: 0, 1 and 2, 3)
-        float a0, a1, b0, b1;
-        if constexpr (WT == W_Q4_0) { a0 = r[0]; a1 = r[2]; b0 = r[1]; b1 = r[3]; }
-        else { a0 = r[0]; a1 = r[1]; b0 = r[2]; b1 = r[3]; }
-        const uint32_t hiA = pack_bf16(a0, a1), loA = pack_bf16(a0 - bf16_lo(hiA), a1 - bf16_hi(hiA));
-        const uint32_t hiB = pack_bf16(b0, b1), loB = pack_bf16(b0 - bf16_lo(hiB), b1 - bf16_hi(hiB));
-        const uint32_t keepA = lo_part ? loA : hiA, keepB = lo_part ? loB : hiB;
-        const uint32_t sendA = lo_part ? hiA : loA, sendB = lo_part ? hiB : loB;
-        // quad_perm [1, 0, 3, 2]: swap with the neighbouring lane
-        const uint32_t recvA = (uint32_t)__builtin_amdgcn_mov_dpp((int)sendA, 0xB1, 0xF, 0xF, true);
-        const uint32_t recvB = (uint32_t)__builtin_amdgcn_mov_dpp((int)sendB, 0xB1, 0xF, 0xF, true);
-        // register order: Q4_0 A(run 0) A(run 1) B(run 0) B(run 1);
-        // Q8_0 A(run 0) B(run 0) A(run 1) B(run 1)
-        uint32_t w4[4];
-        if constexpr (WT == W_Q4_0) {
-            w4[0] = lo_part ? recvA : keepA; w4[1] = lo_part ? keepA : recvA;
-            w4[2] = lo_part ? recvB : keepB; w4[3] = lo_part ? keepB : recvB;
-        } else {
-            w4[0] = lo_part ? recvA : keepA; w4[1] = lo_part ? recvB : keepB;
-            w4[2] = lo_part ? keepA : recvA; w4[3] = lo_part ? keepB : recvB;
+    // XQ: the block scales Delta_x of the two tokens whose sums this lane
+    // receives (2g and 2g + 1), one fp16 per block, two per dword
+    uint32_t dxs[2][XQ ? NBW / 2 : 1];
+    if constexpr (!XQ) {
+        const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<void *>(X), 0, (int)(((uint32_t)(N - 1) * x_pitch + (uint32_t)K) * 4u), BUFFER_FLAGS);
+        const uint32_t xrow = (uint32_t)tok * x_pitch * 4u;
+        // The 8 k positions of group g come in two runs of 4 (Q4_0: 4g.. and
+        // 16+4g..; Q8_0: k0.. and k0+4..).  Lanes 2t and 2t+1 (token t, high and
+        // low part) need the same 8 values: each loads one run (the even lane
+        // run 0), converts it to both parts, and the pair trades the part the
+        // other lane feeds with one DPP swap.  That halves the load instructions:
+        // a CU's vector-memory path returns about 1 KB per 25 cycles, and with
+        // 8 tokens and one tile per workgroup the activations are most of a
+        // workgroup's bytes.  All loads first, then the conversions: one round
+        // trip, not NBW.
+        uint32_t raw[NBW][4];
+    #pragma unroll
+        for (int t = 0; t < NBW; ++t) {
+            const int b = b_begin + t;
+            const uint32_t base = (uint32_t)(32 * b) * 4;
+            uint32_t o0, o1;
+            if constexpr (WT == W_Q4_0) { o0 = base + 16 * g; o1 = base + 64 + 16 * g; }
+            else { const int k0 = (g == 0) ? 0 : (g == 1) ? 16 : (g == 2) ? 8 : 24; o0 = base + 4 * k0; o1 = o0 + 16; }
+            const bool in = b < nb && tok < N;
+            const auto p = __builtin_amdgcn_raw_buffer_load_b128(xres, in ? xrow + (lo_part ? o1 : o0) : OUT_OF_RANGE, 0, 0);
+    #pragma unroll
+            for (int e = 0; e < 4; ++e) raw[t][e] = p[e];
         }
-        xf[t] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+        __builtin_amdgcn_sched_barrier(0);
+    #pragma unroll
+        for (int t = 0; t < NBW; ++t) {
+            float r[4];
+    #pragma unroll
+            for (int e = 0; e < 4; ++e) r[e] = __builtin_bit_cast(float, raw[t][e]);
+            // the run's two register pairs (Q4_0: elements 0, 2 and 1, 3 of the
+            // run, for lo(s0) lo(s2) | hi(s0) hi(s2) ...; Q8_0: 0, 1 and 2, 3)
+            float a0, a1, b0, b1;
+            if constexpr (WT == W_Q4_0) { a0 = r[0]; a1 = r[2]; b0 = r[1]; b1 = r[3]; }
+            else { a0 = r[0]; a1 = r[1]; b0 = r[2]; b1 = r[3]; }
+            const uint32_t hiA = pack_bf16(a0, a1), loA = pack_bf16(a0 - bf16_lo(hiA), a1 - bf16_hi(hiA));
+            const uint32_t hiB = pack_bf16(b0, b1), loB = pack_bf16(b0 - bf16_lo(hiB), b1 - bf16_hi(hiB));
+            const uint32_t keepA = lo_part ? loA : hiA, keepB = lo_part ? loB : hiB;
+            const uint32_t sendA = lo_part ? hiA : loA, sendB = lo_part ? hiB : loB;
+            // quad_perm [1, 0, 3, 2]: swap with the neighbouring lane
+            const uint32_t recvA = (uint32_t)__builtin_amdgcn_mov_dpp((int)sendA, 0xB1, 0xF, 0xF, true);
+            const uint32_t recvB = (uint32_t)__builtin_amdgcn_mov_dpp((int)sendB, 0xB1, 0xF, 0xF, true);
+            // register order: Q4_0 A(run 0) A(run 1) B(run 0) B(run 1);
+            // Q8_0 A(run 0) B(run 0) A(run 1) B(run 1)
+            uint32_t w4[4];
+            if constexpr (WT == W_Q4_0) {
+                w4[0] = lo_part ? recvA : keepA; w4[1] = lo_part ? keepA : recvA;
+                w4[2] = lo_part ? recvB : keepB; w4[3] = lo_part ? keepB : recvB;
+            } else {
+                w4[0] = lo_part ? recvA : keepA; w4[1] = lo_part ? recvB : keepB;
+                w4[2] = lo_part ? keepA : recvA; w4[3] = lo_part ? keepB : recvB;
+            }
+            xf[t] = __builtin_bit_cast(bf16x8, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+        }
+    } else {
+        // Q8_0 rows: fp16 scales from byte 0, int8 codes from byte xqoff;
+        // the pass's first block is kb0
+        const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<void *>(X), 0, (int)((uint32_t)(N - 1) * x_pitch + (uint32_t)(xqoff + 32 * nb_row)),
+            BUFFER_FLAGS);
+        const uint32_t xrow = (uint32_t)tok * x_pitch;
+        // the even lane of a token pair loads the 8 codes k0(g) .. k0(g)+7
+        // of each block; the odd lane's channel stays zero
+        const int k0 = (g == 0) ? 0 : (g == 1) ? 16 : (g == 2) ? 8 : 24;
+        uint32_t raw[NBW][2];
+#pragma unroll
+        for (int t = 0; t < NBW; ++t) {
+            const int b = b_begin + t;
+            const uint32_t base = xrow + (uint32_t)(xqoff + 32 * (kb0 + b));
+            const bool in = b < nb && tok < N && !lo_part;
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(xres, in ? base + k0 : OUT_OF_RANGE, 0, 0);
+            raw[t][0] = v[0];
+            raw[t][1] = v[1];
+        }
+        // scales: 2 NBW bytes from block kb0 + b_begin of each token's row
+        // (8- or 16-byte aligned: kb0 and b_begin are multiples of NBW)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int tk = 2 * g + h;
+            const uint32_t off = (uint32_t)tk * x_pitch + 2u * (uint32_t)(kb0 + b_begin);
+            const bool in = tk < N;
+            if constexpr (NBW == 4) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b64(xres, in ? off : OUT_OF_RANGE, 0, 0);
+                dxs[h][0] = v[0];
+                dxs[h][1] = v[1];
+            } else {
+#pragma unroll
+                for (int q = 0; q < NBW / 8; ++q) {
+                    const auto v = __builtin_amdgcn_raw_buffer_load_b128(xres, in ? off + 16 * q : OUT_OF_RANGE, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dxs[h][4 * q + e] = v[e];
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // codes 0..7 of the run in register order, exact in bf16
+#pragma unroll
+        for (int t = 0; t < NBW; ++t) {
+            const uint32_t r0 = raw[t][0], r1 = raw[t][1];
+            xf[t] = __builtin_bit_cast(bf16x8, make_uint4(pack_bf16(sbyte<0>(r0), sbyte<1>(r0)),
+                                                           pack_bf16(sbyte<2>(r0), sbyte<3>(r0)),
+                                                           pack_bf16(sbyte<0>(r1), sbyte<1>(r1)),
+                                                           pack_bf16(sbyte<2>(r1), sbyte<3>(r1))));
+        }
     }
 
     // one tile: unpack, matrix products, bias and scales; then the partial
@@ -403,9 +472,20 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
                 const int hw = (p * BPG + t) >> SS;             // the block's scale in the slice
                 const uint32_t sw = sc[hw / 2];
                 const float ds = (float)__builtin_bit_cast(_Float16, (uint16_t)((hw & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
-                const float d = (b_begin + p * BPG + t < nb) ? ds : 0.0f;
-                yp0 = fmaf(d, D[0] + D[1], yp0);
-                yp1 = fmaf(d, D[2] + D[3], yp1);
+                const bool inb = b_begin + p * BPG + t < nb;
+                if constexpr (XQ) {
+                    // channels 4g + 1 and 4g + 3 are zero: D[0] and D[2] are
+                    // the exact block sums of tokens 2g and 2g + 1
+                    const int blk = p * BPG + t;
+                    const float dx0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(dxs[0][blk / 2] >> (16 * (blk & 1))));
+                    const float dx1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(dxs[1][blk / 2] >> (16 * (blk & 1))));
+                    yp0 = fmaf(inb ? ds * dx0 : 0.0f, D[0], yp0);
+                    yp1 = fmaf(inb ? ds * dx1 : 0.0f, D[2], yp1);
+                } else {
+                    const float d = inb ? ds : 0.0f;
+                    yp0 = fmaf(d, D[0] + D[1], yp0);
+                    yp1 = fmaf(d, D[2] + D[3], yp1);
+                }
             }
         }
         float *mine = red[it & 1][wave][lane];
@@ -492,32 +572,115 @@ constexpr int kWideWaves = 12;
 constexpr int kWideBlocks = 16 * kWideWaves;
 template <int WT> constexpr int wide_tile_rows() { return WT == W_Q4_0 ? 16 : 8; }
 
-// The kernel for (type, NBW, scale shift) and its LDS bytes.
-template <int WT, int SS>
-MfKernel pick_mf(int nbw, int *lds)
-{
-    constexpr int D = kStages, T = kTileRows;
-    switch (nbw) {
-    case 4: *lds = mf_lds_bytes<WT, kWaves, 4, SS, T>(mf_stages<WT, kWaves, 4, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 4, SS, D, T>;
-    case 8: *lds = mf_lds_bytes<WT, kWaves, 8, SS, T>(mf_stages<WT, kWaves, 8, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 8, SS, D, T>;
-    case 16: *lds = mf_lds_bytes<WT, kWaves, 16, SS, T>(mf_stages<WT, kWaves, 16, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 16, SS, D, T>;
-    default: return nullptr;
-    }
-}
-template <int WT, int SS>
-MfKernel pick_wide(int *lds)
-{
-    constexpr int T = wide_tile_rows<WT>();
-    *lds = mf_lds_bytes<WT, kWideWaves, 16, SS, T>(mf_stages<WT, kWideWaves, 16, SS, kStages, T>());
-    return gemv_mf_kernel<WT, kWideWaves, 16, SS, kStages, T>;
-}
-
 // Blocks per wave for a pass of nb blocks (0 if out of range).
 int mf_nbw(int64_t nb)
 {
     if (nb <= 0 || nb > kPassBlocks) return 0;
     const int64_t per = (nb + kWaves - 1) / kWaves;
     return per <= 4 ? 4 : per <= 8 ? 8 : 16;
+}
+
+// The kernel for (type, NBW, scale shift, activation format) and its LDS bytes.
+template <int WT, int SS, bool XQ>
+MfKernel pick_mf(int nbw, int *lds)
+{
+    constexpr int D = kStages, T = kTileRows;
+    switch (nbw) {
+    case 4: *lds = mf_lds_bytes<WT, kWaves, 4, SS, T>(mf_stages<WT, kWaves, 4, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 4, SS, D, T, XQ>;
+    case 8: *lds = mf_lds_bytes<WT, kWaves, 8, SS, T>(mf_stages<WT, kWaves, 8, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 8, SS, D, T, XQ>;
+    case 16: *lds = mf_lds_bytes<WT, kWaves, 16, SS, T>(mf_stages<WT, kWaves, 16, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 16, SS, D, T, XQ>;
+    default: return nullptr;
+    }
+}
+template <int WT, int SS, bool XQ>
+MfKernel pick_wide(int *lds)
+{
+    constexpr int T = wide_tile_rows<WT>();
+    *lds = mf_lds_bytes<WT, kWideWaves, 16, SS, T>(mf_stages<WT, kWideWaves, 16, SS, kStages, T>());
+    return gemv_mf_kernel<WT, kWideWaves, 16, SS, kStages, T, XQ>;
+}
+template <bool XQ>
+MfKernel pick(int type, int ss, bool wide, int64_t nb, int *lds)
+{
+    const int nbw = mf_nbw(nb);
+    if constexpr (!XQ) {
+        if (wide && type == W_Q4_0) return ss ? pick_wide<W_Q4_0, 1, false>(lds) : pick_wide<W_Q4_0, 0, false>(lds);
+        if (type == W_Q4_0) return ss ? pick_mf<W_Q4_0, 1, false>(nbw, lds) : pick_mf<W_Q4_0, 0, false>(nbw, lds);
+    }
+    if (wide && type == W_Q8_0) return ss ? pick_wide<W_Q8_0, 1, XQ>(lds) : pick_wide<W_Q8_0, 0, XQ>(lds);
+    if (type == W_Q8_0) return ss ? pick_mf<W_Q8_0, 1, XQ>(nbw, lds) : pick_mf<W_Q8_0, 0, XQ>(nbw, lds);
+    return nullptr;
+}
+
+// One item's activations: fp32 rows (pitch in elements) or Q8_0 rows of
+// the same K (pitch in bytes).
+struct MfSrc {
+    const void *base;
+    uint64_t pitch;
+};
+
+template <bool XQ>
+hipError_t launch_mf(const WeightView *w, const MfSrc *x, const OutView *y, int count, int64_t N,
+                     hipStream_t stream)
+{
+    if (count < 1 || count > kMaxMfItems) return hipErrorInvalidValue;
+    const int type = w[0].type;
+    const int64_t K = w[0].K;
+    const int64_t nb_row = K / 32;
+    const int ss = w[0].scale_shift;
+    const bool wide = nb_row > kPassBlocks && nb_row <= kWideBlocks;
+    const int tr = !wide ? kTileRows : type == W_Q4_0 ? wide_tile_rows<W_Q4_0>() : wide_tile_rows<W_Q8_0>();
+    const int64_t pass = wide ? kWideBlocks : kPassBlocks;
+    const int waves = wide ? kWideWaves : kWaves;
+    int64_t tiles_total = 0;
+    for (int i = 0; i < count; ++i) tiles_total += (w[i].M + tr - 1) / tr;
+    if (tiles_total == 0 || N == 0 || nb_row == 0) return hipSuccess;
+    for (int64_t n0 = 0; n0 < N; n0 += 8) {
+        // passes over K in stream order: the first stores y, the others add
+        for (int64_t kb0 = 0; kb0 < nb_row; kb0 += pass) {
+            const int64_t nb = nb_row - kb0 < pass ? nb_row - kb0 : pass;
+            int lds = kLdsBytes;
+            const MfKernel k = pick<XQ>(type, ss, wide, nb, &lds);
+            if (!k) return hipErrorInvalidValue;
+            // a workgroup streams several tiles with its activation fragments
+            // resident: as many workgroups as the LDS of the 256 CUs holds
+            const int64_t cap = 256 * (int64_t)(kLdsBytes / lds);
+            MfArgs a = {};
+            a.N = (int32_t)(N - n0 < 8 ? N - n0 : 8);
+            a.K = (int32_t)(32 * nb);
+            a.qoff = (int32_t)quant_offset(K, ss);
+            a.nb = (int32_t)nb;
+            a.kb0 = (int32_t)kb0;
+            a.nb_row = (int32_t)nb_row;
+            a.accumulate = kb0 > 0;
+            a.xqoff = XQ ? (int32_t)quant_offset(K) : 0;
+            int32_t wg_max = 0;
+            for (int i = 0; i < count; ++i) {
+                if (w[i].M == 0) continue;
+                MfItem &it = a.item[a.n_items++];
+                it.w = w[i].base;
+                it.pitch = (uint32_t)w[i].pitch;
+                it.M = (int32_t)w[i].M;
+                if constexpr (XQ)
+                    it.x = static_cast<const uint8_t *>(x[i].base) + (uint64_t)n0 * x[i].pitch;
+                else
+                    it.x = static_cast<const float *>(x[i].base) + (uint64_t)n0 * x[i].pitch + (uint64_t)32 * kb0;
+                it.x_pitch = (uint32_t)x[i].pitch;
+                it.y = y[i].data + (uint64_t)n0 * y[i].pitch_elems;
+                it.y_pitch = (uint32_t)y[i].pitch_elems;
+                it.n_tiles = (int32_t)((w[i].M + tr - 1) / tr);
+                int64_t wgs = (int64_t)it.n_tiles * cap / tiles_total;
+                if (wgs < 1) wgs = 1;
+                if (wgs > it.n_tiles) wgs = it.n_tiles;
+                it.wg_count = (int32_t)wgs;
+                if (wgs > wg_max) wg_max = (int32_t)wgs;
+            }
+            hipLaunchKernelGGL(k, dim3((unsigned)wg_max, (unsigned)a.n_items), dim3(64 * waves), 0, stream, a);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -541,65 +704,38 @@ bool gemv_mf_supported(const GemvTask *tasks, int count)
 hipError_t launch_gemv_mf(const GemvTask *tasks, int count, hipStream_t stream)
 {
     if (count < 1 || count > kMaxMfItems) return hipErrorInvalidValue;
-    const int type = tasks[0].w.type;
-    const int64_t K = tasks[0].w.K;
-    const int64_t N = tasks[0].x.N;
-    const int64_t nb_row = K / 32;
-    const int ss = tasks[0].w.scale_shift;
-    const bool wide = nb_row > kPassBlocks && nb_row <= kWideBlocks;
-    const int tr = !wide ? kTileRows : type == W_Q4_0 ? wide_tile_rows<W_Q4_0>() : wide_tile_rows<W_Q8_0>();
-    const int64_t pass = wide ? kWideBlocks : kPassBlocks;
-    const int waves = wide ? kWideWaves : kWaves;
-    int64_t tiles_total = 0;
-    for (int i = 0; i < count; ++i) tiles_total += (tasks[i].w.M + tr - 1) / tr;
-    if (tiles_total == 0 || N == 0 || nb_row == 0) return hipSuccess;
-    for (int64_t n0 = 0; n0 < N; n0 += 8) {
-        // passes over K in stream order: the first stores y, the others add
-        for (int64_t kb0 = 0; kb0 < nb_row; kb0 += pass) {
-            const int64_t nb = nb_row - kb0 < pass ? nb_row - kb0 : pass;
-            MfKernel k = nullptr;
-            int lds = kLdsBytes;
-            if (wide && type == W_Q4_0) k = ss ? pick_wide<W_Q4_0, 1>(&lds) : pick_wide<W_Q4_0, 0>(&lds);
-            else if (wide && type == W_Q8_0) k = ss ? pick_wide<W_Q8_0, 1>(&lds) : pick_wide<W_Q8_0, 0>(&lds);
-            else if (type == W_Q4_0) k = ss ? pick_mf<W_Q4_0, 1>(mf_nbw(nb), &lds) : pick_mf<W_Q4_0, 0>(mf_nbw(nb), &lds);
-            else if (type == W_Q8_0) k = ss ? pick_mf<W_Q8_0, 1>(mf_nbw(nb), &lds) : pick_mf<W_Q8_0, 0>(mf_nbw(nb), &lds);
-            if (!k) return hipErrorInvalidValue;
-            // a workgroup streams several tiles with its activation fragments
-            // resident: as many workgroups as the LDS of the 256 CUs holds
-            const int64_t cap = 256 * (int64_t)(kLdsBytes / lds);
-            MfArgs a = {};
-            a.N = (int32_t)(N - n0 < 8 ? N - n0 : 8);
-            a.K = (int32_t)(32 * nb);
-            a.qoff = (int32_t)quant_offset(K, tasks[0].w.scale_shift);
-            a.nb = (int32_t)nb;
-            a.kb0 = (int32_t)kb0;
-            a.nb_row = (int32_t)nb_row;
-            a.accumulate = kb0 > 0;
-            int32_t wg_max = 0;
-            for (int i = 0; i < count; ++i) {
-                if (tasks[i].w.M == 0) continue;
-                MfItem &it = a.item[a.n_items++];
-                it.w = tasks[i].w.base;
-                it.pitch = (uint32_t)tasks[i].w.pitch;
-                it.M = (int32_t)tasks[i].w.M;
-                it.x = static_cast<const float *>(tasks[i].x.data) + (uint64_t)n0 * tasks[i].x.pitch_elems +
-                       (uint64_t)32 * kb0;
-                it.x_pitch = (uint32_t)tasks[i].x.pitch_elems;
-                it.y = tasks[i].y.data + (uint64_t)n0 * tasks[i].y.pitch_elems;
-                it.y_pitch = (uint32_t)tasks[i].y.pitch_elems;
-                it.n_tiles = (int32_t)((tasks[i].w.M + tr - 1) / tr);
-                int64_t wgs = (int64_t)it.n_tiles * cap / tiles_total;
-                if (wgs < 1) wgs = 1;
-                if (wgs > it.n_tiles) wgs = it.n_tiles;
-                it.wg_count = (int32_t)wgs;
-                if (wgs > wg_max) wg_max = (int32_t)wgs;
-            }
-            hipLaunchKernelGGL(k, dim3((unsigned)wg_max, (unsigned)a.n_items), dim3(64 * waves), 0, stream, a);
-            const hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
+    WeightView w[kMaxMfItems];
+    MfSrc x[kMaxMfItems];
+    OutView y[kMaxMfItems];
+    for (int i = 0; i < count; ++i) {
+        w[i] = tasks[i].w;
+        x[i] = MfSrc{tasks[i].x.data, tasks[i].x.pitch_elems};
+        y[i] = tasks[i].y;
     }
-    return hipSuccess;
+    return launch_mf<false>(w, x, y, count, tasks[0].x.N, stream);
+}
+
+bool gemv_mf_q8x_supported(const WeightView *w, const WeightView *xq, int count, int64_t N)
+{
+    const int type = w[0].type;
+    const int64_t K = w[0].K;
+    if (type != W_Q8_0 || K % 32 != 0 || K == 0) return false;
+    const int64_t nt = N < 8 ? N : 8;
+    for (int i = 0; i < count; ++i) {
+        if (w[i].pitch > (1ull << 27) || xq[i].pitch % 16 != 0 ||
+            (nt - 1) * (int64_t)xq[i].pitch + quant_offset(K) + K >= (int64_t)1 << 31)
+            return false;
+    }
+    return true;
+}
+
+hipError_t launch_gemv_mf_q8x(const WeightView *w, const WeightView *xq, const OutView *y, int count, int64_t N,
+                              hipStream_t stream)
+{
+    if (count < 1 || count > kMaxMfItems) return hipErrorInvalidValue;
+    MfSrc x[kMaxMfItems];
+    for (int i = 0; i < count; ++i) x[i] = MfSrc{xq[i].base, xq[i].pitch};
+    return launch_mf<true>(w, x, y, count, N, stream);
 }
 
 }  // namespace qmm

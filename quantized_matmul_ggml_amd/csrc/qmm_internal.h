@@ -126,11 +126,35 @@ hipError_t launch_gemv_i8_swiglu(const WeightView &wg, const WeightView &wu, con
 hipError_t launch_gemv_swiglu(const WeightView &wg, const WeightView &wu, const ActView &x,
                               const OutView &h, hipStream_t stream);
 
+// Which launches the matrix-core kernels take (measured on the decoder's
+// shapes, graph-replayed): from 5 tokens every one; at 3 and 4 tokens those
+// of more than 2048 rows or of rows over 4096 (5632 x 2048: 5.8 against
+// 7.3 us at 3 tokens; 2048 x 5632: 7.5 against 8.2), while 2048 x 2048
+// stays on the VALU kernel (3.95 against 4.2 us at 3 tokens), whose cost
+// per weight grows with the tokens but whose grid fills the chip at any
+// row count.
+// Rows over 192 blocks (K > 6144) run on the matrix cores as several
+// dependent passes, and the VALU kernel's one launch is faster up to 6
+// tokens (2048 x 5632 Q4_0 in two passes: 12.7 / 14.1 us on the VALU kernel
+// against 14.3 / 14.8 at 5 / 6 tokens; 16.7 against 15.3 at 8).
+inline bool use_matrix_cores(int64_t N, int64_t m_total, int64_t K)
+{
+    if (K > 6144) return N >= 7;
+    if (N >= 5) return true;
+    return N >= 3 && (m_total > 2048 || K > 4096);
+}
+
 // The matrix-core GEMV with register-resident activation fragments
 // (gemv_mf.hip): Q4_0 / Q8_0 weights, weight pitch <= 2^27; K up to 6144 in
 // one launch, longer rows in passes that add to y.
 bool gemv_mf_supported(const GemvTask *tasks, int count);
 hipError_t launch_gemv_mf(const GemvTask *tasks, int count, hipStream_t stream);
+// The same kernel with Q8_0 weights and Q8_0 activation rows (xq[i]: pitch
+// in bytes, a multiple of 16): each block's integer sum exact on the matrix
+// cores, the block terms Delta_w Delta_x S summed in binary32.
+bool gemv_mf_q8x_supported(const WeightView *w, const WeightView *xq, int count, int64_t N);
+hipError_t launch_gemv_mf_q8x(const WeightView *w, const WeightView *xq, const OutView *y, int count, int64_t N,
+                              hipStream_t stream);
 // Measurement kernels (probe.hip): a streaming read of `bytes` (multiple of
 // 16, < 2^31) by `workgroups` workgroups of 256 threads, one xor word per
 // workgroup into sink; and the clock probe (workgroups x 4 waves, each

@@ -153,7 +153,9 @@ def test_gemv_swiglu_edge_cases(orc, case):
 # ------------------------------------------------- integer activations (Q8_0 x)
 
 I8_EDGE = [("Q4_0", 300, 2048, 1), ("Q4_0", 2048, 5632, 2), ("Q8_0", 1000, 2048, 8),
-           ("Q8_0", 77, 1024, 3), ("Q4_B64", 130, 2048, 4)]
+           ("Q8_0", 77, 1024, 3), ("Q4_B64", 130, 2048, 4),
+           # the matrix-core kernel: K = 2048, one launch at K = 5632, passes
+           ("Q4_0", 300, 2048, 6), ("Q4_0", 2048, 5632, 8), ("Q8_0", 129, 5632, 5), ("Q4_0", 64, 8192, 7)]
 
 
 def _i8_bound(K, tname, a):

@@ -938,8 +938,14 @@ I8_CASES = [
     ("Q8_0", 32000, 2048, 8), ("Q8_0", 32000, 2048, 1), ("Q4_0", 300, 1024, 3),
     ("Q8_0", 37, 96, 5), ("Q4_0", 1, 32, 1), ("Q8_0", 513, 512, 2), ("Q4_0", 64, 16384, 2),
     ("Q4_0", 130, 8192, 8),
+    # Q8_0 weights from 5 tokens over 8192 rows or K over 4096 take the
+    # matrix-core kernel (one twelve-wave launch up to K = 6144, passes
+    # beyond); the rest stays on the int8 dot-product kernel
+    ("Q8_0", 129, 5632, 6), ("Q8_0", 77, 16384, 7), ("Q8_0", 8200, 1024, 5), ("Q8_0", 2048, 2048, 8),
+    ("Q4_0", 2048, 5632, 8), ("Q4_0", 2600, 2048, 4), ("Q4_0", 45, 6144, 5),
     # 64-block weights: each 32-block term takes its 64-block's scale
     ("Q4_B64", 5632, 2048, 1), ("Q8_B64", 300, 5632, 3), ("Q4_B64", 37, 128, 8), ("Q8_B64", 513, 512, 2),
+    ("Q4_B64", 64, 4160, 8), ("Q8_B64", 100, 5632, 8), ("Q8_B64", 8200, 2048, 5),
 ]
 
 
@@ -974,6 +980,8 @@ I8_BATCH_CASES = [
     ("Q8_0", [300, 0, 130, 37], 1024, 5, False),
     ("Q4_B64", [5632, 5632], 2048, 2, True),
     ("Q8_0", [64] * 8, 512, 8, False),
+    ("Q4_0", [2048, 300], 5632, 8, False),
+    ("Q8_0", [4100, 4100, 17], 2048, 6, False),
 ]
 
 
