@@ -212,17 +212,21 @@ def main():
 
     # dependent, with the gate/up pair fused with its SwiGLU epilogue (one
     # 5632-vector written instead of two)
+    def fused(xs, ys, h_ffn, x_lm, y_lm):
+        def step():
+            for L in layers:
+                Q.gemv_batch([(L[n], xs[0], ys[n]) for n in ("wq", "wk", "wv")])
+                Q.gemv(L["wo"], xs[1], out=ys["wo"])
+                Q.gemv_swiglu(L["wgate"], L["wup"], xs[2], out=h_ffn)
+                Q.gemv(L["wdown"], xs[3], out=ys["wdown"])
+            Q.gemv(lm, x_lm, out=y_lm)
+        return step
+
     h_ffn = torch.empty((1, WL.FFN), device=dev)
-
-    def step_fused():
-        for L in layers:
-            Q.gemv_batch([(L[n], xs[0], ys[n]) for n in ("wq", "wk", "wv")])
-            Q.gemv(L["wo"], xs[1], out=ys["wo"])
-            Q.gemv_swiglu(L["wgate"], L["wup"], xs[2], out=h_ffn)
-            Q.gemv(L["wdown"], xs[3], out=ys["wdown"])
-        Q.gemv(lm, x_lm, out=y_lm)
-
+    step_fused = fused(xs, ys, h_ffn, x_lm, y_lm)
+    step_fused_8 = fused(xs8, ys8, torch.empty((NB, WL.FFN), device=dev), x_lm8, y_lm8)
     fused_bytes = step_bytes - WL.LAYERS * (4 * WL.HIDDEN + 4 * WL.FFN)
+    fused_bytes_8 = step_bytes_8 - WL.LAYERS * NB * (4 * WL.HIDDEN + 4 * WL.FFN)
 
     variants = {}
     for vname, fn, launches, nbytes, ntok in (
@@ -230,7 +234,8 @@ def main():
             ("dependent", step_dependent, 4 * WL.LAYERS + 1, step_bytes, 1),
             ("grouped", step_grouped, 2 * WL.LAYERS + 1, step_bytes, 1),
             ("dependent_swiglu_fused", step_fused, 4 * WL.LAYERS + 1, fused_bytes, 1),
-            ("dependent_8_tokens", step_dependent_8, 4 * WL.LAYERS + 1, step_bytes_8, NB)):
+            ("dependent_8_tokens", step_dependent_8, 4 * WL.LAYERS + 1, step_bytes_8, NB),
+            ("dependent_swiglu_fused_8_tokens", step_fused_8, 4 * WL.LAYERS + 1, fused_bytes_8, NB)):
         log(f"decode step [{vname}]: capturing {launches} launches into a HIP graph")
         graph = Graph(fn)
         ms_v, wall_v = timed(graph, args.steps, args.warmup)

@@ -236,7 +236,8 @@ QMM_API int qmm_gemv_batch(const qmm_gemv_item *items, int32_t count, void *stre
  * the two sums carry that path's accuracy and the weights are quantized);  h: F32 ne = [M, N], overlapping none of w_gate, w_up, x
  * (QMM_ERR_ALIAS).  Different types: QMM_ERR_TYPE; different ne: QMM_ERR_SHAPE.
  * One launch streams both matrices once and writes h only (the two
- * projections are never stored).  The two sums carry the accuracy of
+ * projections are never stored); from 3 fp32 tokens, with quantized weights
+ * and K <= 4096, on the bf16 matrix cores.  The two sums carry the accuracy of
  * qmm_gemv; the epilogue runs in binary32 (expf, one division, two
  * products), so |h - h_exact| <= 1.1 e_g (|u| + e_u) + |Swish(g)| e_u
  * + 2^-20 |h| with e_g, e_u the qmm_gemv bounds of the two sums. */

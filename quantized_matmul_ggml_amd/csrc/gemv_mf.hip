@@ -74,9 +74,12 @@ struct MfArgs {
     int32_t nb_row;       // 32-blocks per row
     int32_t accumulate;   // add to y (a later pass over K) instead of storing
     int32_t xqoff;        // Q8_0 activations: byte offset of the codes in an x row
-    int32_t pad[7];
+    uint32_t pitch2;      // fused SwiGLU: bytes between the up matrix's rows
+    const uint8_t *w2;    // fused SwiGLU: the up matrix (item 0's w is the gate)
+    int32_t pad[4];
     MfItem item[kMaxMfItems];
 };
+static_assert(offsetof(MfArgs, item) == 64, "the shared fields fill the first 64 bytes");
 
 // Round two floats to bf16 (nearest even) in one v_cvt_pk_bf16_f32.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -186,17 +189,24 @@ __device__ inline void wait_vm()
 // LDS of a workgroup with KW waves and NSTG stages, and the most stages (up
 // to MAXD, at least 2) that fit the CU's 160 KiB.
 constexpr int kLdsBytes = 160 * 1024;
-template <int WT, int KW, int NBW, int SS, int TR>
+template <int WT, int KW, int NBW, int SS, int TR, bool SW = false>
 constexpr int mf_lds_bytes(int nstg)
 {
-    return nstg * KW * MfStage<WT, NBW, SS, TR>::BYTES + 2 * KW * 64 * 2 * 4;
+    return nstg * KW * (SW ? 2 : 1) * MfStage<WT, NBW, SS, TR>::BYTES + 2 * KW * 64 * 2 * 4;
 }
-template <int WT, int KW, int NBW, int SS, int MAXD, int TR>
+template <int WT, int KW, int NBW, int SS, int MAXD, int TR, bool SW = false>
 constexpr int mf_stages()
 {
     int d = MAXD;
-    while (d > 2 && mf_lds_bytes<WT, KW, NBW, SS, TR>(d) > kLdsBytes) --d;
+    while (d > 2 && mf_lds_bytes<WT, KW, NBW, SS, TR, SW>(d) > kLdsBytes) --d;
     return d;
+}
+
+// Swish(z) = z * sigma(z) = z / (1 + e^{-z}) in binary32; for z far below
+// zero e^{-z} overflows and the quotient is the limit -0.
+__device__ inline float swish(float z)
+{
+    return z / (1.0f + expf(-z));
 }
 
 // XQ: the activations are Q8_0 rows (A Complete Guide to llama.cpp and
@@ -209,11 +219,21 @@ constexpr int mf_stages()
 // significands) with it.  (Q4_0 weights with Q8_0 activations stay on the
 // int8 dot-product kernel, measured faster: their 8 codes per lane and block
 // come in two 4-byte runs, two load instructions per block.)
-template <int WT, int KW, int NBW, int SS, int MAXD, int TR, bool XQ>
+//
+// SW: the gate/up pair fused with the SwiGLU epilogue (Development Guide for
+// Small AI Models (TinyLLaMA, etc.) Using C++, §4.4: h = Swish(x Wg) * (x Wu)).
+// A tile is 8 row indices of both matrices: matrix columns 0..7 are gate
+// rows, 8..15 the up rows of the same indices, each half staged like an
+// 8-row tile.  After the cross-wave sum, lanes j and j + 8 hold the two sums
+// of one output, one DPP rotation apart, and only h is stored.  One pass
+// over K (h is not linear in partial sums).
+template <int WT, int KW, int NBW, int SS, int MAXD, int TR, bool XQ, bool SW>
 __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
 {
-    constexpr int NSTG = mf_stages<WT, KW, NBW, SS, MAXD, TR>();
-    static_assert(mf_lds_bytes<WT, KW, NBW, SS, TR>(NSTG) <= kLdsBytes, "LDS of one workgroup");
+    constexpr int NSTG = mf_stages<WT, KW, NBW, SS, MAXD, TR, SW>();
+    static_assert(mf_lds_bytes<WT, KW, NBW, SS, TR, SW>(NSTG) <= kLdsBytes, "LDS of one workgroup");
+    static_assert(!SW || (TR == 8 && !XQ), "SwiGLU tiles are 8 gate + 8 up rows");
+    constexpr int SWF = SW ? 2 : 1;        // matrices staged per tile
     constexpr int BPG = MfFmt<WT>::bpg;
     constexpr int BB = MfFmt<WT>::block_bytes;
     constexpr int NG = NBW / BPG;          // 64-byte groups per row per wave
@@ -224,10 +244,10 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
     __shared__ float red[2][KW][64][2];
     // one array per stage, so that each wait for a stage's loads counts only
     // the loads issued before them
-    __shared__ __attribute__((aligned(16))) uint8_t st0[KW][St::BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t st1[KW][St::BYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t st2[KW][NSTG > 2 ? St::BYTES : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t st3[KW][NSTG > 3 ? St::BYTES : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t st0[KW][SWF * St::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t st1[KW][SWF * St::BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t st2[KW][NSTG > 2 ? SWF * St::BYTES : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t st3[KW][NSTG > 3 ? SWF * St::BYTES : 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -244,21 +264,23 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
     const int M = itm.M, n_tiles = itm.n_tiles, n_wg = itm.wg_count;
     const int N = a.N, K = a.K, qoff = a.qoff, nb = a.nb, kb0 = a.kb0, nb_row = a.nb_row, acc = a.accumulate;
     const int xqoff = a.xqoff;
+    const uint8_t *const W2 = a.w2;
+    const uint32_t pitch2 = a.pitch2;
     asm volatile("" ::"s"(W), "s"(X), "s"(Y), "s"(pitch), "s"(x_pitch), "s"(y_pitch), "s"(M),
                  "s"(n_tiles), "s"(n_wg), "s"(N), "s"(K), "s"(qoff), "s"(nb), "s"(kb0), "s"(nb_row), "s"(acc),
-                 "s"(xqoff));
+                 "s"(xqoff), "s"(W2), "s"(pitch2));
     if ((int)blockIdx.x >= n_wg) return;
     const int b_begin = wave * NBW;
 
     // ---- a tile's share of this wave into one stage: rows past M, and
     // units and scales of blocks past the row, read as zeros ----
     const uint32_t row_bytes = (uint32_t)(qoff + nb_row * BB);
-    auto issue = [&](auto &stg, int tl) {
+    auto issue_mat = [&](uint32_t base, const uint8_t *Wm, uint32_t pm, int tl) {
+        const uint32_t pitch = pm;
         const int r0 = tl * TR;
         const int rows = tl < n_tiles ? (M - r0 < TR ? M - r0 : TR) : 0;
-        const i32x4 wres = buffer_words(W + (uint64_t)(rows > 0 ? r0 : 0) * pitch,
+        const i32x4 wres = buffer_words(Wm + (uint64_t)(rows > 0 ? r0 : 0) * pitch,
                                         rows > 0 ? (uint32_t)(rows - 1) * pitch + row_bytes : 0u);
-        const uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(&stg[wave][0]);
 #pragma unroll
         for (int i = 0; i < St::NI; ++i) {
             const int r = i * St::RPI + lane / St::U;
@@ -279,6 +301,11 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
                                      : OUT_OF_RANGE;
             load_to_lds<4>(wres, base + St::CODE_BYTES + 256 * i, off);
         }
+    };
+    auto issue = [&](auto &stg, int tl) {
+        const uint32_t base = (uint32_t)reinterpret_cast<uintptr_t>(&stg[wave][0]);
+        issue_mat(base, W, pitch, tl);
+        if constexpr (SW) issue_mat(base + St::BYTES, W2, pitch2, tl);
     };
 
     // the first NSTG-1 tiles are in flight while the activations are set up
@@ -407,7 +434,8 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
     // one tile: unpack, matrix products, bias and scales; then the partial
     // sums of the KW waves (K ranges) meet in LDS and wave 0 stores the rows
     auto consume = [&](auto &stg, int tl, int it) {
-        const uint8_t *base = stg[wave];
+        // SW: columns 8..15 read the up matrix's half of the stage
+        const uint8_t *base = stg[wave] + (SW && j >= 8 ? St::BYTES : 0);
         const int jr = j & (TR - 1);       // the tile row column j reads
         // row j's scales, then its units 4p + g
         uint32_t sc[St::SR / 4];
@@ -500,7 +528,16 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
                 s1 += red[it & 1][w2][lane][1];
             }
             const int m = tl * TR + j;
-            if (j < TR && m < M) {
+            if constexpr (SW) {
+                // row_ror:8 within each 16-lane row: lane j reads lane j ^ 8
+                const float u0 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s0), 0x128, 0xF, 0xF, true));
+                const float u1 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s1), 0x128, 0xF, 0xF, true));
+                if (j < 8 && m < M) {
+                    float *y0 = Y + (uint64_t)(2 * g) * y_pitch + m;
+                    if (2 * g < N) *y0 = swish(s0) * u0;
+                    if (2 * g + 1 < N) *(y0 + y_pitch) = swish(s1) * u1;
+                }
+            } else if (j < TR && m < M) {
                 float *y0 = Y + (uint64_t)(2 * g) * y_pitch + m;
                 float *y1 = y0 + y_pitch;
                 if (2 * g < N) *y0 = acc ? *y0 + s0 : s0;
@@ -518,25 +555,25 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
         if constexpr (NSTG == 2) issue(st1, tile + n_wg);
         else if constexpr (NSTG == 3) issue(st2, tile + 2 * n_wg);
         else issue(st3, tile + 3 * n_wg);
-        wait_vm<(NSTG - 1) * (St::NI + St::NS)>();     // this tile's loads have landed
+        wait_vm<(NSTG - 1) * SWF * (St::NI + St::NS)>();     // this tile's loads have landed
         consume(st0, tile, it);
         tile += n_wg;
         if (tile >= n_tiles) break;
         issue(st0, tile + (NSTG - 1) * n_wg);
-        wait_vm<(NSTG - 1) * (St::NI + St::NS)>();     // this tile's loads have landed
+        wait_vm<(NSTG - 1) * SWF * (St::NI + St::NS)>();     // this tile's loads have landed
         consume(st1, tile, it + 1);
         tile += n_wg;
         if constexpr (NSTG > 2) {
             if (tile >= n_tiles) break;
             issue(st1, tile + (NSTG - 1) * n_wg);
-            wait_vm<(NSTG - 1) * (St::NI + St::NS)>();
+            wait_vm<(NSTG - 1) * SWF * (St::NI + St::NS)>();
             consume(st2, tile, it + 2);
             tile += n_wg;
         }
         if constexpr (NSTG > 3) {
             if (tile >= n_tiles) break;
             issue(st2, tile + (NSTG - 1) * n_wg);
-            wait_vm<(NSTG - 1) * (St::NI + St::NS)>();
+            wait_vm<(NSTG - 1) * SWF * (St::NI + St::NS)>();
             consume(st3, tile, it + 3);
             tile += n_wg;
         }
@@ -586,9 +623,9 @@ MfKernel pick_mf(int nbw, int *lds)
 {
     constexpr int D = kStages, T = kTileRows;
     switch (nbw) {
-    case 4: *lds = mf_lds_bytes<WT, kWaves, 4, SS, T>(mf_stages<WT, kWaves, 4, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 4, SS, D, T, XQ>;
-    case 8: *lds = mf_lds_bytes<WT, kWaves, 8, SS, T>(mf_stages<WT, kWaves, 8, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 8, SS, D, T, XQ>;
-    case 16: *lds = mf_lds_bytes<WT, kWaves, 16, SS, T>(mf_stages<WT, kWaves, 16, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 16, SS, D, T, XQ>;
+    case 4: *lds = mf_lds_bytes<WT, kWaves, 4, SS, T>(mf_stages<WT, kWaves, 4, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 4, SS, D, T, XQ, false>;
+    case 8: *lds = mf_lds_bytes<WT, kWaves, 8, SS, T>(mf_stages<WT, kWaves, 8, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 8, SS, D, T, XQ, false>;
+    case 16: *lds = mf_lds_bytes<WT, kWaves, 16, SS, T>(mf_stages<WT, kWaves, 16, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 16, SS, D, T, XQ, false>;
     default: return nullptr;
     }
 }
@@ -597,7 +634,7 @@ MfKernel pick_wide(int *lds)
 {
     constexpr int T = wide_tile_rows<WT>();
     *lds = mf_lds_bytes<WT, kWideWaves, 16, SS, T>(mf_stages<WT, kWideWaves, 16, SS, kStages, T>());
-    return gemv_mf_kernel<WT, kWideWaves, 16, SS, kStages, T, XQ>;
+    return gemv_mf_kernel<WT, kWideWaves, 16, SS, kStages, T, XQ, false>;
 }
 template <bool XQ>
 MfKernel pick(int type, int ss, bool wide, int64_t nb, int *lds)
@@ -610,6 +647,26 @@ MfKernel pick(int type, int ss, bool wide, int64_t nb, int *lds)
     if (wide && type == W_Q8_0) return ss ? pick_wide<W_Q8_0, 1, XQ>(lds) : pick_wide<W_Q8_0, 0, XQ>(lds);
     if (type == W_Q8_0) return ss ? pick_mf<W_Q8_0, 1, XQ>(nbw, lds) : pick_mf<W_Q8_0, 0, XQ>(nbw, lds);
     return nullptr;
+}
+
+// The fused SwiGLU kernel: 8 + 8 row tiles (8-row stages need at most 8
+// rows per load instruction, so Q4_0 takes at least 8 blocks per wave).
+template <int WT, int SS>
+MfKernel pick_sw(int nbw, int *lds)
+{
+    constexpr int D = kStages;
+    if (WT == W_Q4_0 && nbw < 8) nbw = 8;
+    switch (nbw) {
+    case 4:
+        if constexpr (WT == W_Q8_0) {
+            *lds = mf_lds_bytes<WT, kWaves, 4, SS, 8, true>(mf_stages<WT, kWaves, 4, SS, D, 8, true>());
+            return gemv_mf_kernel<WT, kWaves, 4, SS, D, 8, false, true>;
+        }
+        return nullptr;
+    case 8: *lds = mf_lds_bytes<WT, kWaves, 8, SS, 8, true>(mf_stages<WT, kWaves, 8, SS, D, 8, true>()); return gemv_mf_kernel<WT, kWaves, 8, SS, D, 8, false, true>;
+    case 16: *lds = mf_lds_bytes<WT, kWaves, 16, SS, 8, true>(mf_stages<WT, kWaves, 16, SS, D, 8, true>()); return gemv_mf_kernel<WT, kWaves, 16, SS, D, 8, false, true>;
+    default: return nullptr;
+    }
 }
 
 // One item's activations: fp32 rows (pitch in elements) or Q8_0 rows of
@@ -713,6 +770,64 @@ hipError_t launch_gemv_mf(const GemvTask *tasks, int count, hipStream_t stream)
         y[i] = tasks[i].y;
     }
     return launch_mf<false>(w, x, y, count, tasks[0].x.N, stream);
+}
+
+bool gemv_mf_swiglu_supported(const WeightView &wg, const WeightView &wu, const ActView &x)
+{
+    const int type = wg.type;
+    const int64_t K = wg.K;
+    if (!(type == W_Q4_0 || type == W_Q8_0) || K % 32 != 0 || K == 0 || K / 32 > kPassBlocks) return false;
+    if (wu.type != type || wu.K != K || wu.M != wg.M || wu.scale_shift != wg.scale_shift) return false;
+    const int64_t nt = x.N < 8 ? x.N : 8;
+    return wg.pitch <= (1ull << 27) && wu.pitch <= (1ull << 27) &&
+           (nt - 1) * (int64_t)x.pitch_elems + K <= (int64_t)1 << 29 && wg.M < ((int64_t)1 << 30);
+}
+
+hipError_t launch_gemv_mf_swiglu(const WeightView &wg, const WeightView &wu, const ActView &x, const OutView &h,
+                                 hipStream_t stream)
+{
+    const int type = wg.type;
+    const int64_t K = wg.K, M = wg.M, N = x.N;
+    const int64_t nb_row = K / 32;
+    if (M == 0 || N == 0) return hipSuccess;
+    if (nb_row == 0 || nb_row > kPassBlocks) return hipErrorInvalidValue;
+    const int ss = wg.scale_shift;
+    int lds = kLdsBytes;
+    const int nbw = mf_nbw(nb_row);
+    const MfKernel k = type == W_Q4_0 ? (ss ? pick_sw<W_Q4_0, 1>(nbw, &lds) : pick_sw<W_Q4_0, 0>(nbw, &lds))
+                     : type == W_Q8_0 ? (ss ? pick_sw<W_Q8_0, 1>(nbw, &lds) : pick_sw<W_Q8_0, 0>(nbw, &lds))
+                                      : nullptr;
+    if (!k) return hipErrorInvalidValue;
+    const int64_t n_tiles = (M + 7) / 8;
+    const int64_t cap = 256 * (int64_t)(kLdsBytes / lds);
+    const int64_t wgs = n_tiles < cap ? n_tiles : cap;
+    for (int64_t n0 = 0; n0 < N; n0 += 8) {
+        MfArgs a = {};
+        a.N = (int32_t)(N - n0 < 8 ? N - n0 : 8);
+        a.K = (int32_t)K;
+        a.qoff = (int32_t)quant_offset(K, ss);
+        a.nb = (int32_t)nb_row;
+        a.n_items = 1;
+        a.kb0 = 0;
+        a.nb_row = (int32_t)nb_row;
+        a.accumulate = 0;
+        a.w2 = wu.base;
+        a.pitch2 = (uint32_t)wu.pitch;
+        MfItem &it = a.item[0];
+        it.w = wg.base;
+        it.pitch = (uint32_t)wg.pitch;
+        it.M = (int32_t)M;
+        it.x = static_cast<const float *>(x.data) + (uint64_t)n0 * x.pitch_elems;
+        it.x_pitch = (uint32_t)x.pitch_elems;
+        it.y = h.data + (uint64_t)n0 * h.pitch_elems;
+        it.y_pitch = (uint32_t)h.pitch_elems;
+        it.n_tiles = (int32_t)n_tiles;
+        it.wg_count = (int32_t)wgs;
+        hipLaunchKernelGGL(k, dim3((unsigned)wgs, 1u), dim3(64 * kWaves), 0, stream, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 bool gemv_mf_q8x_supported(const WeightView *w, const WeightView *xq, int count, int64_t N)

@@ -153,6 +153,11 @@ hipError_t launch_gemv_mf(const GemvTask *tasks, int count, hipStream_t stream);
 // in bytes, a multiple of 16): each block's integer sum exact on the matrix
 // cores, the block terms Delta_w Delta_x S summed in binary32.
 bool gemv_mf_q8x_supported(const WeightView *w, const WeightView *xq, int count, int64_t N);
+// The same kernel on a gate/up pair with the SwiGLU epilogue (one pass over
+// K: at most 128 blocks, K <= 4096).
+bool gemv_mf_swiglu_supported(const WeightView &wg, const WeightView &wu, const ActView &x);
+hipError_t launch_gemv_mf_swiglu(const WeightView &wg, const WeightView &wu, const ActView &x, const OutView &h,
+                                 hipStream_t stream);
 hipError_t launch_gemv_mf_q8x(const WeightView *w, const WeightView *xq, const OutView *y, int count, int64_t N,
                               hipStream_t stream);
 // Measurement kernels (probe.hip): a streaming read of `bytes` (multiple of

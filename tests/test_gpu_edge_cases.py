@@ -127,7 +127,8 @@ def test_gemv_batch_edge_cases(orc, N):
 
 
 SWIGLU_EDGE = [("Q4_0", 5632, 2048, 1), ("Q4_0", 300, 1024, 3), ("Q8_0", 513, 512, 2),
-               ("Q8_0", 64, 4096, 8), ("F16", 130, 1024, 1), ("Q4_B64", 300, 2048, 2)]
+               ("Q8_0", 64, 4096, 8), ("F16", 130, 1024, 1), ("Q4_B64", 300, 2048, 2),
+               ("Q4_0", 5632, 2048, 8), ("Q4_B64", 130, 2048, 5)]
 
 
 @pytest.mark.parametrize("case", SWIGLU_EDGE, ids=lambda c: "%s-%dx%d-n%d" % c)

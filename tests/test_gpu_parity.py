@@ -337,6 +337,10 @@ SWIGLU_CASES = [
     ("Q8_0", 513, 512, 8), ("Q8_0", 64, 4096, 5), ("Q8_0", 1, 32, 1),
     ("F16", 77, 1003, 2), ("F16", 260, 2048, 4),
     ("Q4_B64", 300, 2048, 2), ("Q8_B64", 65, 192, 1),
+    # from 3 tokens the matrix-core kernel (8 gate + 8 up rows per tile, K
+    # up to 4096); longer rows stay on the VALU kernel
+    ("Q4_0", 5632, 2048, 8), ("Q4_0", 300, 1024, 5), ("Q4_B64", 130, 4096, 6), ("Q8_B64", 77, 512, 4),
+    ("Q4_0", 37, 4128, 8),
 ]
 
 
