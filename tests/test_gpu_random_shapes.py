@@ -1,0 +1,124 @@
+"""GPU parity over seeded random shapes: the decode GEMV, the fused gate/up
+SwiGLU GEMV and the integer-activation GEMV against the CPU oracle, over
+weight types, ragged row counts, K at and around the kernels' range limits
+(128 and 192 blocks), 1 to 8 tokens and padded activation and output pitches.
+The shapes come from one fixed seed, so the set is the same on every run;
+each case's oracle work is bounded (M K N <= 2.5e7).
+
+Bars (as in test_gpu_parity.py):
+  * fp32 activations: |y - y_ref| <= 1e-4 * a + 1e-6 per output;
+  * SwiGLU: each sum's GEMV bound carried through Swish (|Swish'| <= 1.1)
+    and the product, plus a few ulps of h;
+  * Q8_0 activations: |y - y_q8| <= (nchunk + 16) 2^-24 a, against the
+    oracle's integer path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import quantized_matmul_ggml_amd as Q
+from quantized_matmul_ggml_amd import binding as B
+from quantized_matmul_ggml_amd import workloads as WL
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TYPES = {"Q8_0": (B.Q8_0, 3), "Q4_0": (B.Q4_0, 4), "Q8_B64": (B.Q8_B64, 5), "Q4_B64": (B.Q4_B64, 6)}
+CANARY = 0x7FC0DEAD
+
+
+def _cases(n=42, seed=20261203):
+    rng = np.random.default_rng(seed)
+    edges = [32, 64, 96, 1024, 2048, 4064, 4096, 4128, 5632, 6144, 6176, 8192]
+    out = []
+    for i in range(n):
+        path = ("gemv", "swiglu", "q8x")[i % 3]
+        tname = ("Q4_0", "Q8_0", "Q4_B64", "Q8_B64")[rng.integers(0, 4)]
+        blk = 64 if tname.endswith("B64") else 32
+        if rng.random() < 0.5:
+            K = int(edges[rng.integers(0, len(edges))])
+        else:
+            K = int(rng.integers(1, 8192 // blk + 1)) * blk
+        K = max(blk, K // blk * blk)
+        N = int(rng.integers(1, 9))
+        M = int(rng.integers(1, 3001))
+        M = max(1, min(M, int(2.5e7 // (K * N))))
+        x_pad = int(rng.choice([0, 16, 40]))
+        out.append((path, tname, M, K, N, x_pad))
+    return out
+
+
+CASES = _cases()
+
+
+def _guarded(rows, cols, pad=8):
+    buf = torch.full((rows + 4, cols + 2 * pad), 0.0, dtype=torch.float32, device=DEV)
+    buf.view(torch.int32).fill_(CANARY)
+    return buf, buf[2:2 + rows, pad:pad + cols]
+
+
+def _guard_intact(buf, rows, cols, pad=8):
+    b = buf.cpu().numpy().view(np.uint32)
+    inner = np.zeros(b.shape, bool)
+    inner[2:2 + rows, pad:pad + cols] = True
+    return bool((b[~inner] == CANARY).all())
+
+
+def _x_padded(x, x_pad):
+    buf = torch.zeros((x.shape[0], x.shape[1] + x_pad), dtype=torch.float32, device=DEV)
+    buf[:, : x.shape[1]] = torch.from_numpy(x).to(DEV)
+    return buf[:, : x.shape[1]]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "%s-%s-%dx%d-n%d-pad%d" % c)
+def test_random_shape(orc, case):
+    path, tname, M, K, N, x_pad = case
+    print(f"[case] random {path} {tname} M={M} K={K} N={N} x_pad={x_pad}", flush=True)
+    code, otype = TYPES[tname]
+    seed = 31 * M + 7 * K + N
+    w = WL.outlier_weights(seed, M, K) if seed % 2 else WL.weights(seed, M, K)
+    x = WL.activations(seed + 1, N, K)
+    packed = orc.quantize(otype, w)
+    wt = Q.quantize(torch.from_numpy(w).to(DEV), code)
+    assert np.array_equal(wt.data.cpu().numpy()[:, : packed.shape[1]], packed)
+
+    if path == "gemv":
+        yref, a = orc.mul_mat(otype, packed, K, x)
+        buf, yv = _guarded(N, M)
+        Q.gemv(wt, _x_padded(x, x_pad), out=yv)
+        torch.cuda.synchronize()
+        assert _guard_intact(buf, N, M), "wrote outside the output"
+        y = yv.cpu().numpy().astype(np.float64)
+        err, tol = np.abs(y - yref), 1e-4 * a + 1e-6
+    elif path == "swiglu":
+        w2 = WL.weights(seed + 2, M, K)
+        packed2 = orc.quantize(otype, w2)
+        wt2 = Q.quantize(torch.from_numpy(w2).to(DEV), code)
+        gref, ga = orc.mul_mat(otype, packed, K, x)
+        uref, ua = orc.mul_mat(otype, packed2, K, x)
+        href = orc.swiglu(gref, uref)
+        buf, hv = _guarded(N, M)
+        Q.gemv_swiglu(wt, wt2, _x_padded(x, x_pad), out=hv)
+        torch.cuda.synchronize()
+        assert _guard_intact(buf, N, M), "wrote outside the output"
+        y = hv.cpu().numpy().astype(np.float64)
+        eg, eu = 1e-4 * ga + 1e-6, 1e-4 * ua + 1e-6
+        sg = np.array([orc.swish(v) for v in gref.ravel()]).reshape(gref.shape)
+        err = np.abs(y - href)
+        tol = 1.1 * eg * (np.abs(uref) + eu) + np.abs(sg) * eu + 2.0 ** -20 * np.abs(href)
+    else:
+        xq_ref = orc.quantize(orc.Q8_0, x)
+        xq = Q.quantize(torch.from_numpy(x).to(DEV), B.Q8_0)
+        assert np.array_equal(xq.data.cpu().numpy(), xq_ref)
+        yref, _ = orc.mul_mat_q8act(otype, packed, K, xq_ref)
+        _, a = orc.mul_mat(otype, packed, K, orc.dequantize(orc.Q8_0, xq_ref, K))
+        buf, yv = _guarded(N, M)
+        Q.gemv(wt, xq, out=yv)
+        torch.cuda.synchronize()
+        assert _guard_intact(buf, N, M), "wrote outside the output"
+        y = yv.cpu().numpy().astype(np.float64)
+        nchunk = K // 32 if tname.startswith("Q4") else K // 16
+        err, tol = np.abs(y - yref), (nchunk + 16) * 2.0 ** -24 * a + 1e-30
+    assert np.isfinite(y).all()
+    worst = float((err / tol).max())
+    assert worst <= 1.0, f"worst err/bound {worst:.3g}"
