@@ -1,16 +1,19 @@
 """GPU parity over seeded random shapes: the decode GEMV, the fused gate/up
-SwiGLU GEMV and the integer-activation GEMV against the CPU oracle, over
-weight types, ragged row counts, K at and around the kernels' range limits
-(128 and 192 blocks), 1 to 8 tokens and padded activation and output pitches.
-The shapes come from one fixed seed, so the set is the same on every run;
-each case's oracle work is bounded (M K N <= 2.5e7).
+SwiGLU GEMV, the integer-activation GEMV and the prefill GEMM against the CPU
+oracle, over weight types, ragged row and token counts, K at and around the
+GEMV kernels' range limits (128 and 192 blocks), 1 to 8 decode tokens and
+padded activation and output pitches.  The shapes come from fixed seeds, so
+the set is the same on every run; each case's oracle work is bounded
+(M K N <= 2.5e7 for the GEMV, 8e7 for the GEMM).
 
 Bars (as in test_gpu_parity.py):
   * fp32 activations: |y - y_ref| <= 1e-4 * a + 1e-6 per output;
   * SwiGLU: each sum's GEMV bound carried through Swish (|Swish'| <= 1.1)
     and the product, plus a few ulps of h;
   * Q8_0 activations: |y - y_q8| <= (nchunk + 16) 2^-24 a, against the
-    oracle's integer path.
+    oracle's integer path;
+  * GEMM (bf16 activations): |y - y_ref| <= 1e-2 a + 1e-5, and the binary32
+    summation bound against bf16-rounded weights.
 """
 import numpy as np
 import pytest
@@ -122,3 +125,61 @@ def test_random_shape(orc, case):
     assert np.isfinite(y).all()
     worst = float((err / tol).max())
     assert worst <= 1.0, f"worst err/bound {worst:.3g}"
+
+
+# ------------------------------------------------------------------ GEMM
+
+def _gemm_cases(n=18, seed=20261204):
+    """Prefill GEMM shapes: ragged M, N and K (K a multiple of the block),
+    every weight type; bf16 activations."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        tname = ("Q4_0", "Q8_0", "Q4_B64", "Q8_B64", "F16")[i % 5]
+        blk = 64 if tname.endswith("B64") else 32
+        K = int(rng.integers(1, 6144 // blk + 1)) * blk
+        M = int(rng.integers(1, 1500))
+        N = int(rng.integers(1, 700))
+        while M * K * N > 8e7:                  # halve the larger of M and N
+            if N > M:
+                N = max(1, N // 2)
+            else:
+                M = max(1, M // 2)
+        out.append((tname, M, K, N))
+    return out
+
+
+GEMM_CASES = _gemm_cases()
+GEMM_TYPES = dict(TYPES, F16=(B.F16, 1))
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=lambda c: "%s-%dx%d-n%d" % c)
+def test_random_gemm_shape(orc, case):
+    """|y - y_ref| <= 1e-2 a + 1e-5, and against the oracle's bf16-weight
+    variant within the binary32 summation bound 1.1 K 2^-24 a + 1e-7; with
+    the split-K workspace the shape calls for and without one."""
+    tname, M, K, N = case
+    print(f"[case] random gemm {tname} M={M} K={K} N={N}", flush=True)
+    code, otype = GEMM_TYPES[tname]
+    seed = 17 * M + 5 * K + N
+    w = WL.weights(seed, M, K)
+    xbits = WL.round_bf16_bits(WL.activations(seed + 1, N, K))
+    if tname == "F16":
+        packed = WL.round_f16(w).view(np.uint8).reshape(M, 2 * K)
+        wt = B.Weight(torch.from_numpy(packed.view(np.float16)).to(DEV), B.F16, K, M)
+    else:
+        packed = orc.quantize(otype, w)
+        wt = B.Weight(torch.from_numpy(packed).to(DEV), code, K, M)
+    yref, a = orc.mul_mat(otype, packed, K, xbits, x_bf16_bits=True)
+    ydiag, _ = orc.mul_mat(otype, packed, K, xbits, x_bf16_bits=True, w_to_bf16=True)
+    xt = WL.bf16_bits_to_torch(xbits, DEV)
+    for ws in ("auto", None):
+        buf, yv = _guarded(N, M)
+        Q.gemm(wt, xt, out=yv, workspace=ws)
+        torch.cuda.synchronize()
+        assert _guard_intact(buf, N, M), "wrote outside the output"
+        y = yv.cpu().numpy().astype(np.float64)
+        assert np.isfinite(y).all()
+        r1 = float((np.abs(y - yref) / (1e-2 * a + 1e-5)).max())
+        r2 = float((np.abs(y - ydiag) / (1.1 * K * 2.0 ** -24 * a + 1e-7)).max())
+        assert r1 <= 1.0 and r2 <= 1.0, f"workspace={ws}: worst {r1:.3g} (bar), {r2:.3g} (bf16-weight diagnostic)"
