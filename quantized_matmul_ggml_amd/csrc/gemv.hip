@@ -1028,8 +1028,11 @@ hipError_t launch_gemv_swiglu(const WeightView &wg, const WeightView &wu, const 
             nb = nb > 4 ? 4 : nb > 2 ? 2 : 1;
         }
         // The plain configuration for the 2M rows of both matrices; a fused
-        // group holds at least one row index of each.
+        // group holds at least one row index of each, and two of each where
+        // the plain kernel takes two rows per group (one token, rows that one
+        // wave covers, M >= 2048: 2 x 5632 x 2048 Q4_0 5.2 -> 5.05 us).
         if (c.u < 2) c.u = 2;
+        if (nb == 1 && c.ks == 1 && c.cpl <= 2 && M >= 2048) c.u = 4;
         const Kernel k = pick(type, c, true);
         if (!k) return hipErrorInvalidValue;
         const int groups_per_wg = c.wgw / c.ks;
