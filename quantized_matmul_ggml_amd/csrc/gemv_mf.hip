@@ -1,5 +1,6 @@
 // gemv_mf.hip -- decode GEMV / skinny GEMM for Q4_0 and Q8_0 weights and up
-// to 8 fp32 tokens on the bf16 matrix cores.
+// to 8 tokens on the bf16 matrix cores: fp32 activations, Q8_0 activations
+// (with Q8_0 weights), and the gate/up pair fused with SwiGLU.
 //
 // Same operation as gemv.hip (y[n][m] = sum_k W'[m][k] x[n][k]), with the
 // multiply-adds moved to v_mfma_f32_16x16x32_bf16 (D 16 x 16 += A 16 x 32 *
@@ -31,7 +32,10 @@
 //  * The KW waves of a workgroup split K; their partial sums meet in LDS at
 //    the end of each tile.  A tile is TR = 16 weight rows, or 8 (columns
 //    8..15 then repeat rows 0..7 and are not stored) where 16-row stages
-//    would not fit the LDS.
+//    would not fit the LDS; the fused SwiGLU tile is 8 gate rows and the 8
+//    up rows of the same indices.
+//  * Q8_0 activations (XQ) and the SwiGLU epilogue (SW) are described at the
+//    kernel.
 #include "qmm_internal.h"
 #include "wave_reduce.h"
 
