@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--gemm-probe", action="store_true",
                     help="only launch the prefill GEMM (Q4_0 5632 x 2048 x 512) 20 times, for "
                          "hardware-counter runs (rocprofv3 --pmc MfmaUtil MfmaFlopsBF16)")
+    ap.add_argument("--mf-probe", action="store_true",
+                    help="launch only the matrix-core decode GEMV (for counter runs) and exit")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only launch the copy calibration kernel and the dominant GEMV, for "
                          "hardware-counter runs (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
@@ -129,6 +131,9 @@ def main():
 
     if args.traffic_probe:
         traffic_probe()
+        return
+    if args.mf_probe:
+        mf_probe()
         return
     if args.gemm_probe:
         gemm_probe()
@@ -423,6 +428,35 @@ def traffic_probe():
             Q.gemv_batch([(w, x, y) for w, y in zip(L, ys)])
     torch.cuda.synchronize()
     log(f"traffic probe done: 3 copies of {COPY_PROBE_BYTES} B, {2 * WL.LAYERS} gate/up launches")
+
+
+def mf_probe():
+    """The matrix-core decode GEMV alone, for counter runs: the Q4_0 down
+    projection 2048 x 5632 at 8 tokens (one 12-wave launch per matrix) over
+    22 distinct matrices, twice, then the Q8_0 LM head 32000 x 2048 at 8
+    tokens over 4 copies, twice."""
+    import torch
+    sys.path.insert(0, HERE)
+    import quantized_matmul_ggml_amd as Q
+    from quantized_matmul_ggml_amd import workloads as WL
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wd = [Q.quantize(WL.weights_device(WL.seed(3, 6, l), WL.HIDDEN, WL.FFN, dev), Q.Q4_0) for l in range(WL.LAYERS)]
+    lm = [Q.quantize(WL.weights_device(WL.seed(4, 0, r), WL.VOCAB, WL.HIDDEN, dev), Q.Q8_0) for r in range(4)]
+    xd = WL.activations_device(WL.seed(3, 10), 8, WL.FFN, dev)
+    xl = WL.activations_device(WL.seed(4, 1), 8, WL.HIDDEN, dev)
+    yd = torch.empty((8, WL.HIDDEN), device=dev)
+    yl = torch.empty((8, WL.VOCAB), device=dev)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        for w in wd:
+            Q.gemv(w, xd, out=yd)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        for w in lm:
+            Q.gemv(w, xl, out=yl)
+    torch.cuda.synchronize()
+    log(f"mf probe done: {2 * WL.LAYERS} down-projection launches, 8 LM-head launches, 8 tokens each")
 
 
 def gemm_probe():
