@@ -772,9 +772,15 @@ bool gemv_config(int type, int64_t K, int64_t M, int64_t N, GemvConfig *cfg)
             break;
         }
     }
-    // ... otherwise the smallest wave group whose slice fits in registers.
+    // ... otherwise the smallest wave group whose slice fits in registers;
+    // for F16 rows the widest (measured, graph-replayed, 1 / 2 tokens:
+    // 4096 x 4096 in 7.9 / 9.3 us with four waves of 2 chunks per lane,
+    // against 13.4 / 29.8 with one wave of 8; 11008 x 4096 in 17.1 / 18.5
+    // against 29.8 / 63.9; 2048 x 5632 in 7.9 / 9.2 with four waves of 4,
+    // against 7.7 / 18.2 with two of 8).
     if (c.ks == 0) {
-        for (int ks : {1, 2, 4}) {
+        const int order[2][3] = {{1, 2, 4}, {4, 2, 1}};
+        for (int ks : order[type == W_F16]) {
             const int cp = round_cpl((nchunk + 64 * ks - 1) / (64 * ks));
             if (cp == 0 || cp * wpc * c.nt > 128) continue;
             c.ks = ks;
@@ -805,6 +811,9 @@ bool gemv_config(int type, int64_t K, int64_t M, int64_t N, GemvConfig *cfg)
         c.cpl = cp;
     }
     if (c.cpl > 2) c.u = 1;
+    // F16 rows of two chunks per lane: two rows per group at one token
+    // (4096 x 4096: 7.9 us, against 9.7 with four rows and 8.2 with one)
+    if (type == W_F16 && c.cpl == 2 && c.u > 2) c.u = 2;
     c.wgw = 4;
     if (!pick(type, c)) return false;
     *cfg = c;
@@ -947,7 +956,8 @@ hipError_t launch_gemv_batch(const GemvTask *tasks, int count, hipStream_t strea
     for (int i = 0; i < count; ++i) m_total += tasks[i].w.M;
     if (m_total == 0 || N == 0) return hipSuccess;
     // The matrix-core kernels' cost does not grow with the token count.
-    if (use_matrix_cores(N, m_total, K) && gemv_mf_supported(tasks, count)) return launch_gemv_mf(tasks, count, stream);
+    const bool mf = type == W_F16 ? use_matrix_cores_f16(N, m_total, K) : use_matrix_cores(N, m_total, K);
+    if (mf && gemv_mf_supported(tasks, count)) return launch_gemv_mf(tasks, count, stream);
     StreamConfig sc;
     if (stream_config(type, K, m_total, N, &sc) && stream_supported(tasks, count))
         return launch_gemv_stream(tasks, count, sc, stream);

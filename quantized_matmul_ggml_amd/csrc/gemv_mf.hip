@@ -1,6 +1,7 @@
 // gemv_mf.hip -- decode GEMV / skinny GEMM for Q4_0 and Q8_0 weights and up
 // to 8 tokens on the bf16 matrix cores: fp32 activations, Q8_0 activations
-// (with Q8_0 weights), and the gate/up pair fused with SwiGLU.
+// (with Q8_0 weights), and the gate/up pair fused with SwiGLU; F16 weights
+// with fp32 activations.
 //
 // Same operation as gemv.hip (y[n][m] = sum_k W'[m][k] x[n][k]), with the
 // multiply-adds moved to v_mfma_f32_16x16x32_bf16 (D 16 x 16 += A 16 x 32 *
@@ -26,6 +27,10 @@
 //    ever has to cancel: Q8_0 bytes are sign-extended and converted; a Q4_0
 //    nibble n is moved to the top of a byte with its top bit flipped, which
 //    reads as the int8 value 16 (n - 8), and the block scale absorbs the 16.
+//  * F16 rows: a lane loads 8 halves of its row, in matrix order.  Each half
+//    splits exactly into two bf16 values (the half rounded to bf16, and the
+//    remainder, at most 3 significant bits), which go through two matrix
+//    instructions into one accumulator: there is no scale.
 //  * D (16 x 16): lane (row j, group g) gets channels 4 g .. 4 g + 3, i.e.
 //    tokens 2 g and 2 g + 1, of its row for one block, and applies the block
 //    scale in one fused multiply-add per token.
@@ -51,8 +56,10 @@ constexpr int kMaxMfItems = QMM_GEMV_BATCH_MAX;
 template <int WT> struct MfFmt;
 // code_scale: the factor between the value a code enters the matrix
 // instruction with and its signed code (Q4_0 codes enter as 16 (n - 8)).
-template <> struct MfFmt<W_Q4_0> { static constexpr int bpg = 4, block_bytes = 16; static constexpr float code_scale = 0.0625f; };
-template <> struct MfFmt<W_Q8_0> { static constexpr int bpg = 2, block_bytes = 32; static constexpr float code_scale = 1.0f; };
+// scaled: fp16 block scales follow the codes' section (F16 rows have none).
+template <> struct MfFmt<W_Q4_0> { static constexpr int bpg = 4, block_bytes = 16; static constexpr float code_scale = 0.0625f; static constexpr bool scaled = true; };
+template <> struct MfFmt<W_Q8_0> { static constexpr int bpg = 2, block_bytes = 32; static constexpr float code_scale = 1.0f; static constexpr bool scaled = true; };
+template <> struct MfFmt<W_F16>  { static constexpr int bpg = 1, block_bytes = 64; static constexpr float code_scale = 1.0f; static constexpr bool scaled = false; };
 
 struct alignas(64) MfItem {
     const uint8_t *w;
@@ -108,6 +115,7 @@ __device__ inline float sbyte(uint32_t w)
 //        element 4g+s in its low nibble and 16+4g+s in its high nibble),
 //        unpacked as lo(s0) lo(s2) hi(s0) hi(s2) lo(s1) lo(s3) hi(s1) hi(s3).
 //  Q8_0: group g holds codes k0(g) .. k0(g)+7 with k0 = 0, 16, 8, 24.
+//  F16:  group g holds halves 8g .. 8g+7.
 
 // Swap helpers: [0] is the new first operand, [1] the new second.
 __device__ inline void swap32(uint32_t &a, uint32_t &b)
@@ -134,7 +142,7 @@ struct MfStage {
     static constexpr int U = SB / 16;
     static constexpr int RPI = 64 / U;
     static constexpr int NI = TR / RPI;                        // code load instructions
-    static constexpr int SR = (2 * NBW) >> SS;
+    static constexpr int SR = MfFmt<WT>::scaled ? (2 * NBW) >> SS : 0;
     static constexpr int NS = (TR * SR + 255) / 256;           // scale load instructions
     static constexpr int CODE_BYTES = NI * 1024;
     static constexpr int BYTES = CODE_BYTES + NS * 256;
@@ -294,6 +302,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
                                           : OUT_OF_RANGE;
             load_to_lds<16>(wres, base + 1024 * i, off);
         }
+        if constexpr (St::NS > 0) {
 #pragma unroll
         for (int i = 0; i < St::NS; ++i) {
             const int byte = 256 * i + 4 * lane;
@@ -304,6 +313,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
                                      ? (uint32_t)r * pitch + (uint32_t)(2 * ((kb0 + b_begin) >> SS) + rb)
                                      : OUT_OF_RANGE;
             load_to_lds<4>(wres, base + St::CODE_BYTES + 256 * i, off);
+        }
         }
     };
     auto issue = [&](auto &stg, int tl) {
@@ -332,7 +342,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
             const_cast<void *>(X), 0, (int)(((uint32_t)(N - 1) * x_pitch + (uint32_t)K) * 4u), BUFFER_FLAGS);
         const uint32_t xrow = (uint32_t)tok * x_pitch * 4u;
         // The 8 k positions of group g come in two runs of 4 (Q4_0: 4g.. and
-        // 16+4g..; Q8_0: k0.. and k0+4..).  Lanes 2t and 2t+1 (token t, high and
+        // 16+4g..; Q8_0: k0.. and k0+4..; F16: 8g.. and 8g+4..).  Lanes 2t and 2t+1 (token t, high and
         // low part) need the same 8 values: each loads one run (the even lane
         // run 0), converts it to both parts, and the pair trades the part the
         // other lane feeds with one DPP swap.  That halves the load instructions:
@@ -347,6 +357,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
             const uint32_t base = (uint32_t)(32 * b) * 4;
             uint32_t o0, o1;
             if constexpr (WT == W_Q4_0) { o0 = base + 16 * g; o1 = base + 64 + 16 * g; }
+            else if constexpr (WT == W_F16) { o0 = base + 32 * g; o1 = o0 + 16; }
             else { const int k0 = (g == 0) ? 0 : (g == 1) ? 16 : (g == 2) ? 8 : 24; o0 = base + 4 * k0; o1 = o0 + 16; }
             const bool in = b < nb && tok < N;
             const auto p = __builtin_amdgcn_raw_buffer_load_b128(xres, in ? xrow + (lo_part ? o1 : o0) : OUT_OF_RANGE, 0, 0);
@@ -360,7 +371,8 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
     #pragma unroll
             for (int e = 0; e < 4; ++e) r[e] = __builtin_bit_cast(float, raw[t][e]);
             // the run's two register pairs (Q4_0: elements 0, 2 and 1, 3 of the
-            // run, for lo(s0) lo(s2) | hi(s0) hi(s2) ...; Q8_0: 0, 1 and 2, 3)
+            // run, for lo(s0) lo(s2) | hi(s0) hi(s2) ...; Q8_0 and F16: 0, 1
+            // and 2, 3)
             float a0, a1, b0, b1;
             if constexpr (WT == W_Q4_0) { a0 = r[0]; a1 = r[2]; b0 = r[1]; b1 = r[3]; }
             else { a0 = r[0]; a1 = r[1]; b0 = r[2]; b1 = r[3]; }
@@ -372,7 +384,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
             const uint32_t recvA = (uint32_t)__builtin_amdgcn_mov_dpp((int)sendA, 0xB1, 0xF, 0xF, true);
             const uint32_t recvB = (uint32_t)__builtin_amdgcn_mov_dpp((int)sendB, 0xB1, 0xF, 0xF, true);
             // register order: Q4_0 A(run 0) A(run 1) B(run 0) B(run 1);
-            // Q8_0 A(run 0) B(run 0) A(run 1) B(run 1)
+            // Q8_0 and F16 A(run 0) B(run 0) A(run 1) B(run 1)
             uint32_t w4[4];
             if constexpr (WT == W_Q4_0) {
                 w4[0] = lo_part ? recvA : keepA; w4[1] = lo_part ? keepA : recvA;
@@ -442,7 +454,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
         const uint8_t *base = stg[wave] + (SW && j >= 8 ? St::BYTES : 0);
         const int jr = j & (TR - 1);       // the tile row column j reads
         // row j's scales, then its units 4p + g
-        uint32_t sc[St::SR / 4];
+        uint32_t sc[St::SR >= 4 ? St::SR / 4 : 1];
         if constexpr (St::SR == 4) {
             sc[0] = *reinterpret_cast<const uint32_t *>(base + St::CODE_BYTES + St::SR * jr);
         } else if constexpr (St::SR == 8) {
@@ -461,9 +473,30 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
         }
         const uint8_t *rowp = base + (jr / St::RPI) * 1024 + (jr % St::RPI) * St::SB;
         float yp0 = 0.0f, yp1 = 0.0f;
+        f32x4 Dh = {0.0f, 0.0f, 0.0f, 0.0f};   // F16: all blocks in one accumulator
 #pragma unroll
         for (int p = 0; p < NG; ++p) {
             const uint4 cv = *reinterpret_cast<const uint4 *>(rowp + 16 * swz<St::U>(jr, 4 * p + g));
+            if constexpr (WT == W_F16) {
+                // halves 8g .. 8g + 7 of block p, already in matrix order.
+                // Each finite half f = hi + lo exactly: hi = f rounded to
+                // bf16, lo = f - hi (at most 3 significant bits, so exact in
+                // bf16).  NaN stays NaN; an infinite half gives lo = NaN, so
+                // its row's outputs are NaN (the activations' low parts,
+                // often exactly 0, would turn Inf into NaN anyway).
+                const uint32_t dw[4] = {cv.x, cv.y, cv.z, cv.w};
+                uint32_t hv[4], lv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float f0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(dw[e] & 0xFFFFu));
+                    const float f1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(dw[e] >> 16));
+                    hv[e] = pack_bf16(f0, f1);
+                    lv[e] = pack_bf16(f0 - bf16_lo(hv[e]), f1 - bf16_hi(hv[e]));
+                }
+                Dh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[p], __builtin_bit_cast(bf16x8, make_uint4(hv[0], hv[1], hv[2], hv[3])), Dh, 0, 0, 0);
+                Dh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xf[p], __builtin_bit_cast(bf16x8, make_uint4(lv[0], lv[1], lv[2], lv[3])), Dh, 0, 0, 0);
+                continue;
+            }
             uint32_t d0 = cv.x, d1 = cv.y, d2 = cv.z, d3 = cv.w;
             // regroup: the four lane groups of each matrix instruction hold
             // disjoint code sets of one block
@@ -519,6 +552,10 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
                     yp1 = fmaf(d, D[2] + D[3], yp1);
                 }
             }
+        }
+        if constexpr (WT == W_F16) {
+            yp0 = Dh[0] + Dh[1];
+            yp1 = Dh[2] + Dh[3];
         }
         float *mine = red[it & 1][wave][lane];
         mine[0] = yp0 * MfFmt<WT>::code_scale;     // a power of two: exact
@@ -622,15 +659,33 @@ int mf_nbw(int64_t nb)
 }
 
 // The kernel for (type, NBW, scale shift, activation format) and its LDS bytes.
+// Tile rows of a pass: F16 rows of 16 blocks per wave (1 KB per row and
+// wave) take 8-row tiles, so that two stages fit the LDS.
+int mf_tile_rows(int type, bool wide, int nbw)
+{
+    if (type == W_F16) return nbw == 16 ? 8 : kTileRows;
+    if (!wide) return kTileRows;
+    return type == W_Q4_0 ? wide_tile_rows<W_Q4_0>() : wide_tile_rows<W_Q8_0>();
+}
+
 template <int WT, int SS, bool XQ>
 MfKernel pick_mf(int nbw, int *lds)
 {
     constexpr int D = kStages, T = kTileRows;
-    switch (nbw) {
-    case 4: *lds = mf_lds_bytes<WT, kWaves, 4, SS, T>(mf_stages<WT, kWaves, 4, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 4, SS, D, T, XQ, false>;
-    case 8: *lds = mf_lds_bytes<WT, kWaves, 8, SS, T>(mf_stages<WT, kWaves, 8, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 8, SS, D, T, XQ, false>;
-    case 16: *lds = mf_lds_bytes<WT, kWaves, 16, SS, T>(mf_stages<WT, kWaves, 16, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 16, SS, D, T, XQ, false>;
-    default: return nullptr;
+    if constexpr (WT == W_F16) {
+        switch (nbw) {
+        case 4: *lds = mf_lds_bytes<WT, kWaves, 4, 0, T>(mf_stages<WT, kWaves, 4, 0, D, T>()); return gemv_mf_kernel<WT, kWaves, 4, 0, D, T, false, false>;
+        case 8: *lds = mf_lds_bytes<WT, kWaves, 8, 0, T>(mf_stages<WT, kWaves, 8, 0, D, T>()); return gemv_mf_kernel<WT, kWaves, 8, 0, D, T, false, false>;
+        case 16: *lds = mf_lds_bytes<WT, kWaves, 16, 0, 8>(mf_stages<WT, kWaves, 16, 0, D, 8>()); return gemv_mf_kernel<WT, kWaves, 16, 0, D, 8, false, false>;
+        default: return nullptr;
+        }
+    } else {
+        switch (nbw) {
+        case 4: *lds = mf_lds_bytes<WT, kWaves, 4, SS, T>(mf_stages<WT, kWaves, 4, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 4, SS, D, T, XQ, false>;
+        case 8: *lds = mf_lds_bytes<WT, kWaves, 8, SS, T>(mf_stages<WT, kWaves, 8, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 8, SS, D, T, XQ, false>;
+        case 16: *lds = mf_lds_bytes<WT, kWaves, 16, SS, T>(mf_stages<WT, kWaves, 16, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 16, SS, D, T, XQ, false>;
+        default: return nullptr;
+        }
     }
 }
 template <int WT, int SS, bool XQ>
@@ -647,6 +702,7 @@ MfKernel pick(int type, int ss, bool wide, int64_t nb, int *lds)
     if constexpr (!XQ) {
         if (wide && type == W_Q4_0) return ss ? pick_wide<W_Q4_0, 1, false>(lds) : pick_wide<W_Q4_0, 0, false>(lds);
         if (type == W_Q4_0) return ss ? pick_mf<W_Q4_0, 1, false>(nbw, lds) : pick_mf<W_Q4_0, 0, false>(nbw, lds);
+        if (type == W_F16) return wide ? nullptr : pick_mf<W_F16, 0, false>(nbw, lds);
     }
     if (wide && type == W_Q8_0) return ss ? pick_wide<W_Q8_0, 1, XQ>(lds) : pick_wide<W_Q8_0, 0, XQ>(lds);
     if (type == W_Q8_0) return ss ? pick_mf<W_Q8_0, 1, XQ>(nbw, lds) : pick_mf<W_Q8_0, 0, XQ>(nbw, lds);
@@ -689,17 +745,19 @@ hipError_t launch_mf(const WeightView *w, const MfSrc *x, const OutView *y, int 
     const int64_t K = w[0].K;
     const int64_t nb_row = K / 32;
     const int ss = w[0].scale_shift;
-    const bool wide = nb_row > kPassBlocks && nb_row <= kWideBlocks;
-    const int tr = !wide ? kTileRows : type == W_Q4_0 ? wide_tile_rows<W_Q4_0>() : wide_tile_rows<W_Q8_0>();
+    const bool wide = type != W_F16 && nb_row > kPassBlocks && nb_row <= kWideBlocks;
     const int64_t pass = wide ? kWideBlocks : kPassBlocks;
     const int waves = wide ? kWideWaves : kWaves;
-    int64_t tiles_total = 0;
-    for (int i = 0; i < count; ++i) tiles_total += (w[i].M + tr - 1) / tr;
-    if (tiles_total == 0 || N == 0 || nb_row == 0) return hipSuccess;
+    int64_t m_total = 0;
+    for (int i = 0; i < count; ++i) m_total += w[i].M;
+    if (m_total == 0 || N == 0 || nb_row == 0) return hipSuccess;
     for (int64_t n0 = 0; n0 < N; n0 += 8) {
         // passes over K in stream order: the first stores y, the others add
         for (int64_t kb0 = 0; kb0 < nb_row; kb0 += pass) {
             const int64_t nb = nb_row - kb0 < pass ? nb_row - kb0 : pass;
+            const int tr = mf_tile_rows(type, wide, mf_nbw(nb));
+            int64_t tiles_total = 0;
+            for (int i = 0; i < count; ++i) tiles_total += (w[i].M + tr - 1) / tr;
             int lds = kLdsBytes;
             const MfKernel k = pick<XQ>(type, ss, wide, nb, &lds);
             if (!k) return hipErrorInvalidValue;
@@ -709,7 +767,7 @@ hipError_t launch_mf(const WeightView *w, const MfSrc *x, const OutView *y, int 
             MfArgs a = {};
             a.N = (int32_t)(N - n0 < 8 ? N - n0 : 8);
             a.K = (int32_t)(32 * nb);
-            a.qoff = (int32_t)quant_offset(K, ss);
+            a.qoff = type == W_F16 ? 0 : (int32_t)quant_offset(K, ss);
             a.nb = (int32_t)nb;
             a.kb0 = (int32_t)kb0;
             a.nb_row = (int32_t)nb_row;
@@ -750,11 +808,14 @@ bool gemv_mf_supported(const GemvTask *tasks, int count)
 {
     const int type = tasks[0].w.type;
     const int64_t K = tasks[0].w.K;
-    if (!(type == W_Q4_0 || type == W_Q8_0) || K % 32 != 0 || K == 0) return false;
+    if (!(type == W_Q4_0 || type == W_Q8_0 || type == W_F16) || K % 32 != 0 || K == 0) return false;
     // a 16-row tile is one buffer resource with 32-bit offsets
     // and the activations of up to 8 tokens another (byte offsets < 2^31)
     for (int i = 0; i < count; ++i) {
         const int64_t nt = tasks[i].x.N < 8 ? tasks[i].x.N : 8;
+        // F16 rows are read in 16-byte units (quantized pitches are
+        // multiples of 16 already)
+        if (type == W_F16 && tasks[i].w.pitch % 16 != 0) return false;
         if (tasks[i].w.pitch > (1ull << 27) ||
             (nt - 1) * (int64_t)tasks[i].x.pitch_elems + K > (int64_t)1 << 29)
             return false;

@@ -144,9 +144,24 @@ inline bool use_matrix_cores(int64_t N, int64_t m_total, int64_t K)
     return N >= 3 && (m_total > 2048 || K > 4096);
 }
 
+// F16 rows (K a multiple of 32; graph-replayed, µs per launch, VALU kernel
+// against matrix cores): from 5 tokens every launch (5632 x 2048: 10.3 / 8.9
+// at 5 tokens; 4096 x 4096: 18.0 / 11.5; 4096 x 11008: 80.4 / 38.3); at 3
+// and 4 tokens only very tall matrices (32000 x 2048: 32.9 / 28.0) and rows
+// over 8192, whose 4-token activation slice no VALU configuration holds in
+// registers (4096 x 11008: 50.3 / 37.6); otherwise the VALU kernel
+// (11008 x 4096: 19.5 / 25.5; 2048 x 5632: 11.2 / 14.8), which also takes 1
+// and 2 tokens everywhere.
+inline bool use_matrix_cores_f16(int64_t N, int64_t m_total, int64_t K)
+{
+    if (N >= 5) return true;
+    return N >= 3 && (m_total >= 16384 || K > 8192);
+}
+
 // The matrix-core GEMV with register-resident activation fragments
-// (gemv_mf.hip): Q4_0 / Q8_0 weights, weight pitch <= 2^27; K up to 6144 in
-// one launch, longer rows in passes that add to y.
+// (gemv_mf.hip): Q4_0 / Q8_0 weights, and F16 rows of whole 32-blocks with
+// a pitch that is a multiple of 16; weight pitch <= 2^27; quantized K up to
+// 6144 in one launch (F16: 4096), longer rows in passes that add to y.
 bool gemv_mf_supported(const GemvTask *tasks, int count);
 hipError_t launch_gemv_mf(const GemvTask *tasks, int count, hipStream_t stream);
 // The same kernel with Q8_0 weights and Q8_0 activation rows (xq[i]: pitch

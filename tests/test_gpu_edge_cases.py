@@ -95,6 +95,10 @@ GEMV_EDGE = [
     ("Q4_0", 300, 5632, 6, 5.0), ("Q4_0", 2048, 5632, 3, 5.0), ("Q8_0", 129, 5632, 5, 5.0),
     ("Q8_0", 77, 16384, 7, 5.0), ("Q8_0", 31, 2080, 7, 5.0),
     ("Q4_B64", 64, 4096, 7, 5.0), ("Q8_B64", 8200, 2048, 4, 5.0), ("Q8_B64", 100, 5632, 8, -5.0),
+    # F16 rows on the matrix cores (one, two and three passes over K) and
+    # on the VALU kernel's four-wave rows
+    ("F16", 300, 2048, 6, 5.0), ("F16", 129, 5632, 8, 5.0), ("F16", 40, 8224, 3, -5.0),
+    ("F16", 2100, 1024, 3, -5.0), ("F16", 500, 4096, 2, 5.0),
 ]
 
 

@@ -267,6 +267,17 @@ GEMV_CASES = [
     ("Q4_B64", 5632, 2048, 1), ("Q8_B64", 300, 5632, 3), ("Q4_B64", 100, 192, 8), ("Q8_B64", 4099, 2048, 2),
     ("Q4_B64", 64, 16384, 5), ("Q8_B64", 1, 64, 1), ("Q4_B64", 8200, 2048, 4),
     ("Q4_B64", 129, 5632, 7), ("Q8_B64", 64, 4160, 8), ("Q4_B64", 64, 16384, 8),
+    # F16 rows (K a multiple of 32) on the matrix cores from 5 tokens: the
+    # 5632 x 2048 up-projection at 8, 4 and 16 blocks per wave (8-row
+    # tiles), K past 4096 in two passes (16 then 8 blocks per wave, 8- then
+    # 16-row tiles); from 3 tokens over 16384 rows or K above 8192 (three
+    # passes); K not a multiple of 32 stays on the VALU kernel
+    ("F16", 5632, 2048, 8), ("F16", 37, 96, 6), ("F16", 1001, 4096, 5), ("F16", 300, 5632, 7),
+    ("F16", 16400, 256, 3), ("F16", 64, 8224, 3), ("F16", 129, 1040, 6),
+    # F16 rows past 2048 on the VALU kernel: four waves per row of 2 or 4
+    # chunks per lane (two rows per group at one token)
+    ("F16", 5632, 2048, 3), ("F16", 2049, 1024, 4), ("F16", 1000, 4096, 1), ("F16", 1000, 4096, 2),
+    ("F16", 300, 5632, 2), ("F16", 999, 4096, 4),
 ]
 
 
@@ -304,12 +315,13 @@ def test_gemv_strided_operands(orc):
             _assert_tol(y, yref, a, 1e-4, 1e-6, f"gemv strided {tname} N={N}")
 
 
-@pytest.mark.parametrize("K", [7, 1003, 2051])
-def test_gemv_f16_tail_with_nan_padding(orc, K):
-    """F16 rows whose K is not a multiple of 8, stored with a row pitch whose
-    padding holds NaN: only the halves inside each row may contribute."""
-    M, N = 37, 3
-    _banner(f"gemv f16 tail K={K} nan padding")
+@pytest.mark.parametrize("K,N", [(7, 3), (1003, 3), (2051, 3), (1024, 6)])
+def test_gemv_f16_tail_with_nan_padding(orc, K, N):
+    """F16 rows whose K is not a multiple of 8 (and, at 6 tokens on the
+    matrix cores, whole 32-blocks), stored with a row pitch whose padding
+    holds NaN: only the halves inside each row may contribute."""
+    M = 37
+    _banner(f"gemv f16 tail K={K} N={N} nan padding")
     w = WL.weights(900 + K, M, K)
     x = WL.activations(901 + K, N, K)
     pitch = (K + 7) // 8 * 8 + 8            # halves; the pitch is 16-byte aligned
@@ -319,6 +331,35 @@ def test_gemv_f16_tail_with_nan_padding(orc, K):
     y = Q.gemv(wt, torch.from_numpy(x).to(DEV)).cpu().numpy()
     yref, a = orc.mul_mat(TYPES["F16"][1], _oracle_weight(orc, "F16", w), K, x)
     _assert_tol(y, yref, a, 1e-4, 1e-6, f"gemv f16 tail K={K}")
+
+
+@pytest.mark.parametrize("N", [1, 6])
+def test_gemv_f16_special_weights(orc, N):
+    """F16 weights at the edges of the format: the largest finite half,
+    subnormal halves and signed zeros everywhere else; rows holding an
+    infinite or NaN weight give non-finite outputs (one token on the VALU
+    kernel: IEEE Inf or NaN; six on the matrix cores: NaN), every other row
+    stays within the bound."""
+    M, K = 96, 2048
+    _banner(f"gemv f16 special weights N={N}")
+    w = WL.round_f16(WL.weights(77, M, K))
+    rng = np.random.default_rng(78)
+    w[0:8, rng.integers(0, K, 8)] = np.float16(65504.0)
+    w[8:16, :] = (rng.integers(-1023, 1024, (8, K)) * 2.0 ** -24).astype(np.float16)   # subnormal halves
+    w[16:24, :] = np.where(rng.random((8, K)) < 0.5, np.float16(0.0), np.float16(-0.0))
+    w[24, 5] = np.float16(np.inf)
+    w[25, 900] = -np.float16(np.inf)
+    w[26, 2047] = np.float16(np.nan)
+    x = WL.activations(79, N, K)
+    packed = w.view(np.uint8).reshape(M, 2 * K)
+    wt = B.Weight(torch.from_numpy(w).to(DEV), B.F16, K, M)
+    y = Q.gemv(wt, torch.from_numpy(x).to(DEV)).cpu().numpy().astype(np.float64)
+    bad = [24, 25, 26]
+    assert not np.isfinite(y[:, bad]).any()
+    ok = np.setdiff1d(np.arange(M), bad)
+    yref, a = orc.mul_mat(TYPES["F16"][1], packed[ok], K, x)
+    _assert_tol(y[:, ok], yref, a, 1e-4, 1e-6, f"gemv f16 special N={N}")
+    assert (y[:, 16:24] == 0.0).all()
 
 
 def _swiglu_tol(orc, gref, ga, uref, ua, h):
@@ -411,14 +452,16 @@ def test_gemv_lm_head_full_size(orc, N):
 
 
 @pytest.mark.parametrize("tname", ["Q8_0", "Q4_0", "F16"])
-def test_gemv_one_hot_is_exact(orc, tname):
-    """x = e_j returns column j of W' exactly (one non-zero term)."""
+@pytest.mark.parametrize("n_tok", [4, 6])
+def test_gemv_one_hot_is_exact(orc, tname, n_tok):
+    """x = e_j returns column j of W' exactly (one non-zero term), on the
+    VALU kernel (4 tokens over 1000 rows) and the matrix cores (6)."""
     M, K = 1000, 2048
-    _banner(f"gemv one-hot {tname}")
+    _banner(f"gemv one-hot {tname} N={n_tok}")
     w = WL.weights(11, M, K)
     packed = _oracle_weight(orc, tname, w)
     deq = orc.dequantize(TYPES[tname][1], packed, K)
-    js = [0, 31, 1000, 2047]
+    js = [0, 31, 1000, 2047, 32, 1999][:n_tok]
     x = np.zeros((len(js), K), np.float32)
     for n, j in enumerate(js):
         x[n, j] = 1.0

@@ -1,6 +1,6 @@
-"""GPU parity over seeded random shapes: the decode GEMV, the fused gate/up
-SwiGLU GEMV, the integer-activation GEMV and the prefill GEMM against the CPU
-oracle, over weight types, ragged row and token counts, K at and around the
+"""GPU parity over seeded random shapes: the decode GEMV (quantized and F16
+rows), the fused gate/up SwiGLU GEMV, the integer-activation GEMV and the
+prefill GEMM against the CPU oracle, over weight types, ragged row and token counts, K at and around the
 GEMV kernels' range limits (128 and 192 blocks), 1 to 8 decode tokens and
 padded activation and output pitches.  The shapes come from fixed seeds, so
 the set is the same on every run; each case's oracle work is bounded
@@ -124,6 +124,53 @@ def test_random_shape(orc, case):
         err, tol = np.abs(y - yref), (nchunk + 16) * 2.0 ** -24 * a + 1e-30
     assert np.isfinite(y).all()
     worst = float((err / tol).max())
+    assert worst <= 1.0, f"worst err/bound {worst:.3g}"
+
+
+# ------------------------------------------------------------------ F16 GEMV
+
+def _f16_cases(n=14, seed=20261205):
+    """F16 rows: K on and off the 32-block grid (the matrix cores take whole
+    blocks from 3 or 5 tokens, the VALU kernel the rest), 1 to 8 tokens,
+    row pitches padded to 16 bytes or further."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        K = int(rng.integers(1, 8192 // 32 + 1)) * 32
+        if i % 3 == 2:
+            K = max(1, K - int(rng.integers(1, 32)))
+        N = int(rng.integers(1, 9))
+        M = int(rng.integers(1, 4001))
+        M = max(1, min(M, int(2.5e7 // (K * N))))
+        extra = int(rng.choice([0, 8, 24]))            # halves of padding past 16-byte alignment
+        out.append((M, K, N, extra))
+    return out
+
+
+F16_CASES = _f16_cases()
+
+
+@pytest.mark.parametrize("case", F16_CASES, ids=lambda c: "f16-%dx%d-n%d-pad%d" % c)
+def test_random_f16_shape(orc, case):
+    """|y - y_ref| <= 1e-4 a + 1e-6, the row padding filled with NaN."""
+    M, K, N, extra = case
+    print(f"[case] random f16 M={M} K={K} N={N} pad={extra}", flush=True)
+    seed = 13 * M + 3 * K + N
+    w = WL.weights(seed, M, K)
+    x = WL.activations(seed + 1, N, K)
+    pitch = (K + 7) // 8 * 8 + extra                 # halves, a multiple of 8
+    wbuf = torch.full((M, pitch), float("nan"), dtype=torch.float16, device=DEV)
+    wbuf[:, :K] = torch.from_numpy(WL.round_f16(w)).to(DEV)
+    wt = B.Weight(wbuf, B.F16, K, M)
+    packed = WL.round_f16(w).view(np.uint8).reshape(M, 2 * K)
+    yref, a = orc.mul_mat(orc.F16, packed, K, x)
+    buf, yv = _guarded(N, M)
+    Q.gemv(wt, torch.from_numpy(x).to(DEV), out=yv)
+    torch.cuda.synchronize()
+    assert _guard_intact(buf, N, M), "wrote outside the output"
+    y = yv.cpu().numpy().astype(np.float64)
+    assert np.isfinite(y).all()
+    worst = float((np.abs(y - yref) / (1e-4 * a + 1e-6)).max())
     assert worst <= 1.0, f"worst err/bound {worst:.3g}"
 
 
