@@ -772,15 +772,18 @@ bool gemv_config(int type, int64_t K, int64_t M, int64_t N, GemvConfig *cfg)
             break;
         }
     }
-    // ... otherwise the smallest wave group whose slice fits in registers;
-    // for F16 rows the widest (measured, graph-replayed, 1 / 2 tokens:
-    // 4096 x 4096 in 7.9 / 9.3 us with four waves of 2 chunks per lane,
-    // against 13.4 / 29.8 with one wave of 8; 11008 x 4096 in 17.1 / 18.5
-    // against 29.8 / 63.9; 2048 x 5632 in 7.9 / 9.2 with four waves of 4,
-    // against 7.7 / 18.2 with two of 8).
+    // ... otherwise, for Q4_0 rows, the smallest wave group whose slice fits
+    // in registers; for F16 and Q8_0 rows the widest (measured,
+    // graph-replayed, 1 / 2 tokens: F16 4096 x 4096 in 7.9 / 9.3 us with
+    // four waves of 2 chunks per lane, against 13.4 / 29.8 with one wave of
+    // 8; F16 11008 x 4096 in 17.1 / 18.5 against 29.8 / 63.9; F16 2048 x 5632
+    // in 7.9 / 9.2 with four waves of 4, against 7.7 / 18.2 with two of 8;
+    // Q8_0 4096 x 8192 in 9.7 / 10.8 against 10.8 / 11.8 with one wave of 8
+    // and two of 4; Q8_0 2048 x 5632 in 5.6 / 6.9 against 6.0 / 7.6 with two
+    // waves of 4.  Q4_0 rows gained or lost up to 3 %).
     if (c.ks == 0) {
         const int order[2][3] = {{1, 2, 4}, {4, 2, 1}};
-        for (int ks : order[type == W_F16]) {
+        for (int ks : order[type != W_Q4_0]) {
             const int cp = round_cpl((nchunk + 64 * ks - 1) / (64 * ks));
             if (cp == 0 || cp * wpc * c.nt > 128) continue;
             c.ks = ks;
@@ -811,9 +814,10 @@ bool gemv_config(int type, int64_t K, int64_t M, int64_t N, GemvConfig *cfg)
         c.cpl = cp;
     }
     if (c.cpl > 2) c.u = 1;
-    // F16 rows of two chunks per lane: two rows per group at one token
-    // (4096 x 4096: 7.9 us, against 9.7 with four rows and 8.2 with one)
-    if (type == W_F16 && c.cpl == 2 && c.u > 2) c.u = 2;
+    // F16 and Q8_0 rows of two chunks per lane: two rows per group at one
+    // token (F16 4096 x 4096: 7.9 us, against 9.7 with four rows and 8.2
+    // with one; Q8_0 2048 x 5632: 5.6, against 5.6 and 6.0)
+    if (type != W_Q4_0 && c.cpl == 2 && c.u > 2) c.u = 2;
     c.wgw = 4;
     if (!pick(type, c)) return false;
     *cfg = c;

@@ -278,6 +278,9 @@ GEMV_CASES = [
     # chunks per lane (two rows per group at one token)
     ("F16", 5632, 2048, 3), ("F16", 2049, 1024, 4), ("F16", 1000, 4096, 1), ("F16", 1000, 4096, 2),
     ("F16", 300, 5632, 2), ("F16", 999, 4096, 4),
+    # Q8_0 rows past 4096 at one and two tokens: four waves per row (2 and 4
+    # chunks per lane, two rows per group)
+    ("Q8_0", 1000, 8192, 1), ("Q8_0", 501, 8192, 2), ("Q8_0", 300, 11008, 1), ("Q8_B64", 257, 8192, 2),
 ]
 
 
