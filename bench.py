@@ -11,8 +11,9 @@ activations + outputs) per second.
 
 Also reported on the same JSON line:
   * prefill: the Q4_0 x bf16 GEMM 5632 x 2048 x 512 in TFLOP/s;
-  * breakdown: the 512 x 512 Q8_0 GEMV, the fp16 5632 x 2048 GEMV and the
-    Q8_0 LM head with 1, 2, 4 and 8 tokens (GB/s, rotating weight copies);
+  * breakdown: the 512 x 512 Q8_0 GEMV, the fp16 5632 x 2048 GEMV (1 and 8
+    tokens) and the Q8_0 LM head with 1, 2, 4 and 8 tokens (GB/s, rotating
+    weight copies);
   * roofline: the dominant kernel (the Q4_0 FFN gate/up GEMV, 5632 x 2048)
     timed per launch with HIP events, beside the rocprofv3 average of the
     same kernel and the read ceiling of a launch of the same bytes;
@@ -723,12 +724,14 @@ def breakdown_leg(Q, WL, dev, args, gemv_bytes, ceiling):
     for r in range(48):
         h = WL.weights_device(WL.seed(2, 0, r), WL.FFN, WL.HIDDEN, dev).to(torch.float16)
         w2.append(Q.f16_weight(h))
-    x2 = WL.activations_device(WL.seed(2, 1), 1, WL.HIDDEN, dev)
-    y2 = torch.empty((1, WL.FFN), device=dev)
-    per = rotate(w2, x2, y2, 96)
-    b = gemv_bytes(w2[0], 1)
-    out["f16_gemv_5632x2048_n1"] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1), "bytes": b,
-                                    "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
+    # (and with 8 tokens, on the matrix cores)
+    for n in (1, 8):
+        x2 = WL.activations_device(WL.seed(2, 1), n, WL.HIDDEN, dev)
+        y2 = torch.empty((n, WL.FFN), device=dev)
+        per = rotate(w2, x2, y2, 96)
+        b = gemv_bytes(w2[0], n)
+        out[f"f16_gemv_5632x2048_n{n}"] = {"us": round(per * 1e3, 3), "gbs": round(b / per / 1e6, 1), "bytes": b,
+                                           "frac_of_hbm_peak": round(b / per / 1e6 / HBM_PEAK_GBS, 4)}
     del w2
 
     # Q8_0 LM head, 16 copies (1.1 GB), N = 1, 2, 4, 8
