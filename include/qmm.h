@@ -184,10 +184,10 @@ QMM_API int qmm_dequantize(const qmm_tensor *src, qmm_tensor *dst_f32, void *str
  * matrix cores instead: signed codes enter exactly, x as two
  * bfloat16 parts (x = hi + lo to 2^-17 relative), products accumulated in
  * binary32, within the same bound.  So do F16 rows whose K is a multiple of
- * 32 and whose pitch is a multiple of 16 bytes, from 5 tokens (from 3 with
- * at least 16384 rows or K above 8192): each half enters exactly as two
- * bfloat16 parts, and an infinite weight there gives NaN (not +-Inf) in
- * its row's outputs, since the low part of an activation may be 0. */
+ * 32, from 5 tokens (from 3 with at least 16384 rows or K above 8192): each
+ * half enters exactly as two bfloat16 parts, and an infinite weight there
+ * gives NaN (not +-Inf) in its row's outputs, since the low part of an
+ * activation may be 0. */
 /* Integer activations ("A Complete Guide to llama.cpp ...", §2.2: with x
  * quantized per block too, x_i ~= Delta_x qx_i, the block dot product is
  * Delta Delta_x sum_i q_i qx_i, an integer sum): when x is Q8_0 (ne = [K, N],

@@ -813,8 +813,8 @@ bool gemv_mf_supported(const GemvTask *tasks, int count)
     // and the activations of up to 8 tokens another (byte offsets < 2^31)
     for (int i = 0; i < count; ++i) {
         const int64_t nt = tasks[i].x.N < 8 ? tasks[i].x.N : 8;
-        // F16 rows are read in 16-byte units (quantized pitches are
-        // multiples of 16 already)
+        // rows are read in 16-byte units (the entry points require 16-byte
+        // weight pitches; F16 rows are checked here too)
         if (type == W_F16 && tasks[i].w.pitch % 16 != 0) return false;
         if (tasks[i].w.pitch > (1ull << 27) ||
             (nt - 1) * (int64_t)tasks[i].x.pitch_elems + K > (int64_t)1 << 29)
