@@ -886,11 +886,13 @@ def test_gemv_batch_decoder_layer(orc):
         _assert_tol(y.cpu().numpy(), yref, a, 1e-4, 1e-6, f"batch {name}")
 
 
-@pytest.mark.parametrize("tname,K", [("Q8_0", 2048), ("Q4_0", 2048), ("F16", 2048), ("Q4_0", 5632), ("Q8_0", 5632)])
+@pytest.mark.parametrize("tname,K", [("Q8_0", 2048), ("Q4_0", 2048), ("F16", 2048), ("Q4_0", 5632), ("Q8_0", 5632),
+                                     ("F16", 4096), ("F16", 5632)])
 def test_gemv_batch_ragged_items(orc, tname, K):
     """Items of 1, 0, 300 and 4100 rows sharing one x, N = 5, outputs in
-    guard-banded buffers; K = 5632 takes the one-launch matrix-core kernel
-    with several items."""
+    guard-banded buffers; quantized K = 5632 takes the one-launch
+    matrix-core kernel with several items, F16 K = 4096 its 8-row tiles and
+    F16 K = 5632 two passes of different tile heights."""
     N = 5
     _banner(f"gemv batch ragged {tname} K={K}")
     x = WL.activations(31, N, K)
