@@ -29,7 +29,7 @@
 //    reads as the int8 value 16 (n - 8), and the block scale absorbs the 16.
 //  * F16 rows: a lane loads 8 halves of its row, in matrix order.  Each half
 //    splits exactly into two bf16 values (the half rounded to bf16, and the
-//    remainder, at most 3 significant bits), which go through two matrix
+//    remainder, at most 2 significant bits), which go through two matrix
 //    instructions into one accumulator: there is no scale.
 //  * D (16 x 16): lane (row j, group g) gets channels 4 g .. 4 g + 3, i.e.
 //    tokens 2 g and 2 g + 1, of its row for one block, and applies the block
@@ -480,7 +480,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
             if constexpr (WT == W_F16) {
                 // halves 8g .. 8g + 7 of block p, already in matrix order.
                 // Each finite half f = hi + lo exactly: hi = f rounded to
-                // bf16, lo = f - hi (at most 3 significant bits, so exact in
+                // bf16, lo = f - hi (at most 2 significant bits, so exact in
                 // bf16).  NaN stays NaN; an infinite half gives lo = NaN, so
                 // its row's outputs are NaN (the activations' low parts,
                 // often exactly 0, would turn Inf into NaN anyway).
