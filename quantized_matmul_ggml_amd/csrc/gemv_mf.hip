@@ -638,6 +638,20 @@ constexpr int kWaves = 8;
 constexpr int kPassBlocks = 16 * kWaves;
 constexpr int kStages = 3;
 
+// Q4_0 passes of at most 64 blocks (K <= 2048) with fp32 activations run as
+// ONE workgroup of sixteen waves x 4 blocks per CU instead of two of eight
+// waves x 8: the same waves per CU, but each CU builds the activation
+// fragments once instead of twice (N K 4 bytes per workgroup, which at 8
+// tokens outweigh its share of the weights on the CU's load path).
+// Measured (graph-replayed, us at 4 / 8 tokens): the [Wgate Wup] batch
+// 2 x 5632 x 2048 7.3 / 7.8 against 8.5 / 9.0, [Wq Wk Wv] 4.7 / 4.9
+// against 5.6 / 5.9; two such workgroups per CU 9.0 / 9.4.  Wo 2048 x 2048
+// (128 tiles: one workgroup per CU either way) and the Q8_0 LM head (whose
+// eight-wave workgroup already fills a CU's LDS) were unchanged, and the
+// fused SwiGLU tiles need 8 blocks per wave, so those keep eight waves.
+constexpr int kNarrowWaves = 16;
+constexpr int kNarrowBlocks = 4 * kNarrowWaves;
+
 // Rows of 129 to 192 blocks (K = 4128 .. 6144; a down projection's 5632)
 // run in ONE launch of twelve waves x 16 blocks instead of two passes.
 // Short matrices of such rows give each workgroup one tile, so the passes'
@@ -695,12 +709,25 @@ MfKernel pick_wide(int *lds)
     *lds = mf_lds_bytes<WT, kWideWaves, 16, SS, T>(mf_stages<WT, kWideWaves, 16, SS, kStages, T>());
     return gemv_mf_kernel<WT, kWideWaves, 16, SS, kStages, T, XQ, false>;
 }
+template <int SS>
+MfKernel pick_narrow(int *lds)
+{
+    constexpr int T = kTileRows;
+    *lds = mf_lds_bytes<W_Q4_0, kNarrowWaves, 4, SS, T>(mf_stages<W_Q4_0, kNarrowWaves, 4, SS, kStages, T>());
+    return gemv_mf_kernel<W_Q4_0, kNarrowWaves, 4, SS, kStages, T, false, false>;
+}
+// The kernel of one pass, its LDS bytes and its waves per workgroup.
 template <bool XQ>
-MfKernel pick(int type, int ss, bool wide, int64_t nb, int *lds)
+MfKernel pick(int type, int ss, bool wide, int64_t nb, int *lds, int *waves)
 {
     const int nbw = mf_nbw(nb);
+    *waves = wide ? kWideWaves : kWaves;
     if constexpr (!XQ) {
         if (wide && type == W_Q4_0) return ss ? pick_wide<W_Q4_0, 1, false>(lds) : pick_wide<W_Q4_0, 0, false>(lds);
+        if (type == W_Q4_0 && nb <= kNarrowBlocks) {
+            *waves = kNarrowWaves;
+            return ss ? pick_narrow<1>(lds) : pick_narrow<0>(lds);
+        }
         if (type == W_Q4_0) return ss ? pick_mf<W_Q4_0, 1, false>(nbw, lds) : pick_mf<W_Q4_0, 0, false>(nbw, lds);
         if (type == W_F16) return wide ? nullptr : pick_mf<W_F16, 0, false>(nbw, lds);
     }
@@ -747,7 +774,6 @@ hipError_t launch_mf(const WeightView *w, const MfSrc *x, const OutView *y, int 
     const int ss = w[0].scale_shift;
     const bool wide = type != W_F16 && nb_row > kPassBlocks && nb_row <= kWideBlocks;
     const int64_t pass = wide ? kWideBlocks : kPassBlocks;
-    const int waves = wide ? kWideWaves : kWaves;
     int64_t m_total = 0;
     for (int i = 0; i < count; ++i) m_total += w[i].M;
     if (m_total == 0 || N == 0 || nb_row == 0) return hipSuccess;
@@ -758,12 +784,13 @@ hipError_t launch_mf(const WeightView *w, const MfSrc *x, const OutView *y, int 
             const int tr = mf_tile_rows(type, wide, mf_nbw(nb));
             int64_t tiles_total = 0;
             for (int i = 0; i < count; ++i) tiles_total += (w[i].M + tr - 1) / tr;
-            int lds = kLdsBytes;
-            const MfKernel k = pick<XQ>(type, ss, wide, nb, &lds);
+            int lds = kLdsBytes, waves = 0;
+            const MfKernel k = pick<XQ>(type, ss, wide, nb, &lds, &waves);
             if (!k) return hipErrorInvalidValue;
             // a workgroup streams several tiles with its activation fragments
             // resident: as many workgroups as the LDS of the 256 CUs holds
-            const int64_t cap = 256 * (int64_t)(kLdsBytes / lds);
+            // (one per CU for the sixteen-wave kind)
+            const int64_t cap = 256 * (int64_t)(waves == kNarrowWaves ? 1 : kLdsBytes / lds);
             MfArgs a = {};
             a.N = (int32_t)(N - n0 < 8 ? N - n0 : 8);
             a.K = (int32_t)(32 * nb);
