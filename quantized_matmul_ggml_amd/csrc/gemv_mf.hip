@@ -638,19 +638,23 @@ constexpr int kWaves = 8;
 constexpr int kPassBlocks = 16 * kWaves;
 constexpr int kStages = 3;
 
-// Q4_0 passes of at most 64 blocks (K <= 2048) with fp32 activations run as
-// ONE workgroup of sixteen waves x 4 blocks per CU instead of two of eight
-// waves x 8: the same waves per CU, but each CU builds the activation
-// fragments once instead of twice (N K 4 bytes per workgroup, which at 8
-// tokens outweigh its share of the weights on the CU's load path).
-// Measured (graph-replayed, us at 4 / 8 tokens): the [Wgate Wup] batch
-// 2 x 5632 x 2048 7.3 / 7.8 against 8.5 / 9.0, [Wq Wk Wv] 4.7 / 4.9
-// against 5.6 / 5.9; two such workgroups per CU 9.0 / 9.4.  Wo 2048 x 2048
-// (128 tiles: one workgroup per CU either way) and the Q8_0 LM head (whose
-// eight-wave workgroup already fills a CU's LDS) were unchanged, and the
-// fused SwiGLU tiles need 8 blocks per wave, so those keep eight waves.
+// Q4_0 and Q8_0 passes with fp32 activations (other than the wide launch)
+// run as ONE workgroup of sixteen waves x 4 or 8 blocks per CU instead of
+// eight-wave workgroups: each CU builds the activation fragments of its K
+// once (N K 4 bytes per workgroup, which at 8 tokens outweigh a CU's share
+// of the weights on its load path) and keeps sixteen waves in flight.
+// Measured (graph-replayed, us at 4 / 8 tokens): the Q4_0 [Wgate Wup] batch
+// 2 x 5632 x 2048 7.3 / 7.8 against 8.5 / 9.0 (two eight-wave workgroups
+// per CU), [Wq Wk Wv] 4.7 / 4.9 against 5.6 / 5.9; at 5 / 8 tokens Q4_0
+// 4096 x 4096 6.4 / 6.7 against 7.4 / 7.9, 11008 x 4096 11.0 / 11.3
+// against 12.2 / 12.4, Q8_0 4096 x 4096 7.6 / 7.7 against 8.4 / 8.5, Q8_0
+// 5632 x 2048 6.3 / 6.5 against 6.6 / 6.8; two sixteen-wave workgroups per
+// CU 9.0 / 9.4 on the gate/up batch; Wo 2048 x 2048 unchanged, the Q8_0
+// LM head unchanged at 4 tokens and 1 % slower at 8 (16.6 against 16.5,
+// medians of 7).  The fused SwiGLU tiles need 8 blocks per wave, so they keep
+// eight waves (at one workgroup per CU: 7.8 against 8.2 us at 8 tokens
+// with two).
 constexpr int kNarrowWaves = 16;
-constexpr int kNarrowBlocks = 4 * kNarrowWaves;
 
 // Rows of 129 to 192 blocks (K = 4128 .. 6144; a down projection's 5632)
 // run in ONE launch of twelve waves x 16 blocks instead of two passes.
@@ -709,12 +713,20 @@ MfKernel pick_wide(int *lds)
     *lds = mf_lds_bytes<WT, kWideWaves, 16, SS, T>(mf_stages<WT, kWideWaves, 16, SS, kStages, T>());
     return gemv_mf_kernel<WT, kWideWaves, 16, SS, kStages, T, XQ, false>;
 }
-template <int SS>
-MfKernel pick_narrow(int *lds)
+template <int WT, int SS>
+MfKernel pick_narrow(int64_t nb, int *lds)
 {
-    constexpr int T = kTileRows;
-    *lds = mf_lds_bytes<W_Q4_0, kNarrowWaves, 4, SS, T>(mf_stages<W_Q4_0, kNarrowWaves, 4, SS, kStages, T>());
-    return gemv_mf_kernel<W_Q4_0, kNarrowWaves, 4, SS, kStages, T, false, false>;
+    constexpr int T = kTileRows, D = kStages, KW = kNarrowWaves;
+    const int64_t per = (nb + KW - 1) / KW;
+    if (per <= 4) {
+        *lds = mf_lds_bytes<WT, KW, 4, SS, T>(mf_stages<WT, KW, 4, SS, D, T>());
+        return gemv_mf_kernel<WT, KW, 4, SS, D, T, false, false>;
+    }
+    if (per <= 8) {
+        *lds = mf_lds_bytes<WT, KW, 8, SS, T>(mf_stages<WT, KW, 8, SS, D, T>());
+        return gemv_mf_kernel<WT, KW, 8, SS, D, T, false, false>;
+    }
+    return nullptr;
 }
 // The kernel of one pass, its LDS bytes and its waves per workgroup.
 template <bool XQ>
@@ -724,11 +736,11 @@ MfKernel pick(int type, int ss, bool wide, int64_t nb, int *lds, int *waves)
     *waves = wide ? kWideWaves : kWaves;
     if constexpr (!XQ) {
         if (wide && type == W_Q4_0) return ss ? pick_wide<W_Q4_0, 1, false>(lds) : pick_wide<W_Q4_0, 0, false>(lds);
-        if (type == W_Q4_0 && nb <= kNarrowBlocks) {
+        if (!wide && (type == W_Q4_0 || type == W_Q8_0)) {
             *waves = kNarrowWaves;
-            return ss ? pick_narrow<1>(lds) : pick_narrow<0>(lds);
+            if (type == W_Q4_0) return ss ? pick_narrow<W_Q4_0, 1>(nb, lds) : pick_narrow<W_Q4_0, 0>(nb, lds);
+            return ss ? pick_narrow<W_Q8_0, 1>(nb, lds) : pick_narrow<W_Q8_0, 0>(nb, lds);
         }
-        if (type == W_Q4_0) return ss ? pick_mf<W_Q4_0, 1, false>(nbw, lds) : pick_mf<W_Q4_0, 0, false>(nbw, lds);
         if (type == W_F16) return wide ? nullptr : pick_mf<W_F16, 0, false>(nbw, lds);
     }
     if (wide && type == W_Q8_0) return ss ? pick_wide<W_Q8_0, 1, XQ>(lds) : pick_wide<W_Q8_0, 0, XQ>(lds);
@@ -891,7 +903,7 @@ hipError_t launch_gemv_mf_swiglu(const WeightView &wg, const WeightView &wu, con
                                       : nullptr;
     if (!k) return hipErrorInvalidValue;
     const int64_t n_tiles = (M + 7) / 8;
-    const int64_t cap = 256 * (int64_t)(kLdsBytes / lds);
+    const int64_t cap = 256;     // one workgroup per CU (see kNarrowWaves)
     const int64_t wgs = n_tiles < cap ? n_tiles : cap;
     for (int64_t n0 = 0; n0 < N; n0 += 8) {
         MfArgs a = {};
