@@ -638,8 +638,8 @@ constexpr int kWaves = 8;
 constexpr int kPassBlocks = 16 * kWaves;
 constexpr int kStages = 3;
 
-// Q4_0 and Q8_0 passes with fp32 activations (other than the wide launch)
-// run as ONE workgroup of sixteen waves x 4 or 8 blocks per CU instead of
+// Q4_0, Q8_0 and F16 passes with fp32 activations (other than the wide
+// launch) run as ONE workgroup of sixteen waves x 4 or 8 blocks per CU instead of
 // eight-wave workgroups: each CU builds the activation fragments of its K
 // once (N K 4 bytes per workgroup, which at 8 tokens outweigh a CU's share
 // of the weights on its load path) and keeps sixteen waves in flight.
@@ -651,7 +651,10 @@ constexpr int kStages = 3;
 // 5632 x 2048 6.3 / 6.5 against 6.6 / 6.8; two sixteen-wave workgroups per
 // CU 9.0 / 9.4 on the gate/up batch; Wo 2048 x 2048 unchanged, the Q8_0
 // LM head unchanged at 4 tokens and 1 % slower at 8 (16.6 against 16.5,
-// medians of 7).  The fused SwiGLU tiles need 8 blocks per wave, so they keep
+// medians of 7).  F16 rows too (3-4 %: 5632 x 2048 at 5 / 8 tokens 8.6 /
+// 8.9 against 8.9 / 9.3, 32000 x 2048 27.4 / 27.9 against 28.3 / 28.9); Q8_0
+// activations keep eight waves (within 1 %, 16384 x 2048 2 % slower with
+// sixteen).  The fused SwiGLU tiles need 8 blocks per wave, so they keep
 // eight waves (at one workgroup per CU: 7.8 against 8.2 us at 8 tokens
 // with two).
 constexpr int kNarrowWaves = 16;
@@ -676,34 +679,27 @@ int mf_nbw(int64_t nb)
     return per <= 4 ? 4 : per <= 8 ? 8 : 16;
 }
 
-// The kernel for (type, NBW, scale shift, activation format) and its LDS bytes.
-// Tile rows of a pass: F16 rows of 16 blocks per wave (1 KB per row and
-// wave) take 8-row tiles, so that two stages fit the LDS.
-int mf_tile_rows(int type, bool wide, int nbw)
+// Tile rows of a pass of nb blocks: F16 rows of 8 blocks per wave (512
+// bytes per row and wave, sixteen waves) take 8-row tiles, so that two
+// stages fit the LDS.
+int mf_tile_rows(int type, bool wide, int64_t nb)
 {
-    if (type == W_F16) return nbw == 16 ? 8 : kTileRows;
+    if (type == W_F16) return (nb + kNarrowWaves - 1) / kNarrowWaves <= 4 ? kTileRows : 8;
     if (!wide) return kTileRows;
     return type == W_Q4_0 ? wide_tile_rows<W_Q4_0>() : wide_tile_rows<W_Q8_0>();
 }
 
+// The eight-wave kernel for (type, NBW, scale shift, activation format)
+// and its LDS bytes: Q8_0 weights with Q8_0 activations.
 template <int WT, int SS, bool XQ>
 MfKernel pick_mf(int nbw, int *lds)
 {
     constexpr int D = kStages, T = kTileRows;
-    if constexpr (WT == W_F16) {
-        switch (nbw) {
-        case 4: *lds = mf_lds_bytes<WT, kWaves, 4, 0, T>(mf_stages<WT, kWaves, 4, 0, D, T>()); return gemv_mf_kernel<WT, kWaves, 4, 0, D, T, false, false>;
-        case 8: *lds = mf_lds_bytes<WT, kWaves, 8, 0, T>(mf_stages<WT, kWaves, 8, 0, D, T>()); return gemv_mf_kernel<WT, kWaves, 8, 0, D, T, false, false>;
-        case 16: *lds = mf_lds_bytes<WT, kWaves, 16, 0, 8>(mf_stages<WT, kWaves, 16, 0, D, 8>()); return gemv_mf_kernel<WT, kWaves, 16, 0, D, 8, false, false>;
-        default: return nullptr;
-        }
-    } else {
-        switch (nbw) {
-        case 4: *lds = mf_lds_bytes<WT, kWaves, 4, SS, T>(mf_stages<WT, kWaves, 4, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 4, SS, D, T, XQ, false>;
-        case 8: *lds = mf_lds_bytes<WT, kWaves, 8, SS, T>(mf_stages<WT, kWaves, 8, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 8, SS, D, T, XQ, false>;
-        case 16: *lds = mf_lds_bytes<WT, kWaves, 16, SS, T>(mf_stages<WT, kWaves, 16, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 16, SS, D, T, XQ, false>;
-        default: return nullptr;
-        }
+    switch (nbw) {
+    case 4: *lds = mf_lds_bytes<WT, kWaves, 4, SS, T>(mf_stages<WT, kWaves, 4, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 4, SS, D, T, XQ, false>;
+    case 8: *lds = mf_lds_bytes<WT, kWaves, 8, SS, T>(mf_stages<WT, kWaves, 8, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 8, SS, D, T, XQ, false>;
+    case 16: *lds = mf_lds_bytes<WT, kWaves, 16, SS, T>(mf_stages<WT, kWaves, 16, SS, D, T>()); return gemv_mf_kernel<WT, kWaves, 16, SS, D, T, XQ, false>;
+    default: return nullptr;
     }
 }
 template <int WT, int SS, bool XQ>
@@ -716,15 +712,16 @@ MfKernel pick_wide(int *lds)
 template <int WT, int SS>
 MfKernel pick_narrow(int64_t nb, int *lds)
 {
-    constexpr int T = kTileRows, D = kStages, KW = kNarrowWaves;
+    constexpr int D = kStages, KW = kNarrowWaves;
+    constexpr int T4 = kTileRows, T8 = WT == W_F16 ? 8 : kTileRows;   // as mf_tile_rows
     const int64_t per = (nb + KW - 1) / KW;
     if (per <= 4) {
-        *lds = mf_lds_bytes<WT, KW, 4, SS, T>(mf_stages<WT, KW, 4, SS, D, T>());
-        return gemv_mf_kernel<WT, KW, 4, SS, D, T, false, false>;
+        *lds = mf_lds_bytes<WT, KW, 4, SS, T4>(mf_stages<WT, KW, 4, SS, D, T4>());
+        return gemv_mf_kernel<WT, KW, 4, SS, D, T4, false, false>;
     }
     if (per <= 8) {
-        *lds = mf_lds_bytes<WT, KW, 8, SS, T>(mf_stages<WT, KW, 8, SS, D, T>());
-        return gemv_mf_kernel<WT, KW, 8, SS, D, T, false, false>;
+        *lds = mf_lds_bytes<WT, KW, 8, SS, T8>(mf_stages<WT, KW, 8, SS, D, T8>());
+        return gemv_mf_kernel<WT, KW, 8, SS, D, T8, false, false>;
     }
     return nullptr;
 }
@@ -741,7 +738,11 @@ MfKernel pick(int type, int ss, bool wide, int64_t nb, int *lds, int *waves)
             if (type == W_Q4_0) return ss ? pick_narrow<W_Q4_0, 1>(nb, lds) : pick_narrow<W_Q4_0, 0>(nb, lds);
             return ss ? pick_narrow<W_Q8_0, 1>(nb, lds) : pick_narrow<W_Q8_0, 0>(nb, lds);
         }
-        if (type == W_F16) return wide ? nullptr : pick_mf<W_F16, 0, false>(nbw, lds);
+        if (type == W_F16) {
+            if (wide) return nullptr;
+            *waves = kNarrowWaves;
+            return pick_narrow<W_F16, 0>(nb, lds);
+        }
     }
     if (wide && type == W_Q8_0) return ss ? pick_wide<W_Q8_0, 1, XQ>(lds) : pick_wide<W_Q8_0, 0, XQ>(lds);
     if (type == W_Q8_0) return ss ? pick_mf<W_Q8_0, 1, XQ>(nbw, lds) : pick_mf<W_Q8_0, 0, XQ>(nbw, lds);
@@ -793,7 +794,7 @@ hipError_t launch_mf(const WeightView *w, const MfSrc *x, const OutView *y, int 
         // passes over K in stream order: the first stores y, the others add
         for (int64_t kb0 = 0; kb0 < nb_row; kb0 += pass) {
             const int64_t nb = nb_row - kb0 < pass ? nb_row - kb0 : pass;
-            const int tr = mf_tile_rows(type, wide, mf_nbw(nb));
+            const int tr = mf_tile_rows(type, wide, nb);
             int64_t tiles_total = 0;
             for (int i = 0; i < count; ++i) tiles_total += (w[i].M + tr - 1) / tr;
             int lds = kLdsBytes, waves = 0;
