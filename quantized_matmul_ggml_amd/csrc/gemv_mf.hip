@@ -625,9 +625,10 @@ __global__ __launch_bounds__(64 * KW) void gemv_mf_kernel(const MfArgs a)
 
 using MfKernel = void (*)(const MfArgs);
 
-// Eight waves share a tile (each one eighth of the pass's K, so that two
-// waves per SIMD hide each other's latencies), with NBW = 4, 8 or 16 blocks
-// per wave.  Three stages for both types (measured at K = 2048 and 5632,
+// In the Q8_0-activation and fused SwiGLU kernels eight waves share a tile
+// (each one eighth of the pass's K, so that two waves per SIMD hide each
+// other's latencies), with NBW = 4, 8 or 16 blocks per wave; the other
+// fp32-activation passes take sixteen (kNarrowWaves below).  Three stages for both types (measured at K = 2048 and 5632,
 // 4 and 8 tokens): a Q4_0 workgroup then needs 63 KB of LDS and two share
 // a CU, 2-4 % faster than one with four stages; Q8_0 with two stages (two
 // workgroups per CU) is as fast at 4 tokens and 4 % slower at 8.  (The
@@ -702,6 +703,7 @@ MfKernel pick_mf(int nbw, int *lds)
     default: return nullptr;
     }
 }
+// The twelve-wave kernel of the wide launch.
 template <int WT, int SS, bool XQ>
 MfKernel pick_wide(int *lds)
 {
@@ -709,6 +711,7 @@ MfKernel pick_wide(int *lds)
     *lds = mf_lds_bytes<WT, kWideWaves, 16, SS, T>(mf_stages<WT, kWideWaves, 16, SS, kStages, T>());
     return gemv_mf_kernel<WT, kWideWaves, 16, SS, kStages, T, XQ, false>;
 }
+// The sixteen-wave kernel of a pass of nb blocks (4 or 8 per wave).
 template <int WT, int SS>
 MfKernel pick_narrow(int64_t nb, int *lds)
 {
