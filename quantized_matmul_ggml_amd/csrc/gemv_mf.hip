@@ -628,10 +628,11 @@ using MfKernel = void (*)(const MfArgs);
 // In the Q8_0-activation and fused SwiGLU kernels eight waves share a tile
 // (each one eighth of the pass's K, so that two waves per SIMD hide each
 // other's latencies), with NBW = 4, 8 or 16 blocks per wave; the other
-// fp32-activation passes take sixteen (kNarrowWaves below).  Three stages for both types (measured at K = 2048 and 5632,
-// 4 and 8 tokens): a Q4_0 workgroup then needs 63 KB of LDS and two share
-// a CU, 2-4 % faster than one with four stages; Q8_0 with two stages (two
-// workgroups per CU) is as fast at 4 tokens and 4 % slower at 8.  (The
+// fp32-activation passes take sixteen (kNarrowWaves below).  Three stages
+// (measured on eight-wave workgroups at K = 2048 and 5632, 4 and 8
+// tokens): a Q4_0 workgroup then needed 63 KB of LDS and two shared a CU,
+// 2-4 % faster than one with four stages; Q8_0 with two stages (two
+// workgroups per CU) was as fast at 4 tokens and 4 % slower at 8.  (The
 // stage count drops to what fits 160 KiB, e.g. two for the wide launch.)
 constexpr int kWaves = 8;
 // Blocks of K one launch covers (16 per wave); longer rows take several
